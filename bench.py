@@ -1,0 +1,227 @@
+"""Benchmark of the rotated-basis matrix-optimizer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload qwen3_1p7b]
+
+One step is one pass of the whole hot path over every matrix of the workload:
+momentum EMA, the basis refresh when due (t = 1, K+1, ...), the two-sided
+rotations, the rotated Adam moments, the rotation back and the weight update.
+The gradient of step 1 is drawn once before the timed region and stays
+resident in the gradient buffers (the optimizer reads them each step; the
+values do not change the work done). With the default 2 warm-up steps the 10
+timed steps are t = 3..12 and include exactly one refresh (t = 11), the
+workload's own cadence of one refresh per 10 steps.
+
+Prints one JSON line. `value` is parameters updated per second (sum of m*n
+over the matrices times steps per second). `roofline` is for the rotation
+GEMMs (the dominant kernels), timed with HIP events recorded by the library
+on the step's stream around every launch of each phase inside the timed
+region. `cpu_baseline` times the fp64 oracle on a bounded sample (see
+--cpu-sample-s), on rank 0 only.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MI355X_FP32_MFMA_TFLOPS = 157.3
+MI355X_HBM_GBPS = 8000.0
+
+METRIC = "optimizer steps/s + params updated/s per micro-group; HBM GB/s & MFMA util"
+
+
+def rotation_flops(shapes):
+    return sum(6.0 * m * n * (m + n) for m, n in shapes)
+
+
+def phase_flops(shapes):
+    """Algorithmic flops of each GEMM phase for one step over all matrices."""
+    return {
+        "rot_left": sum(4.0 * m * m * n for m, n in shapes),
+        "rot_right": sum(4.0 * m * n * n for m, n in shapes),
+        "back_left": sum(2.0 * m * m * n for m, n in shapes),
+        "back_right": sum(2.0 * m * n * n for m, n in shapes),
+    }
+
+
+def elementwise_bytes(shapes, m_dtype):
+    mb = 2 if m_dtype == "bf16" else 4
+    mn = sum(m * n for m, n in shapes)
+    return {"momentum": mn * (4 + 2 * mb), "adam": mn * 20.0}
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle as it stands, one non-refresh step on one matrix of each
+    distinct shape, weighted by shape counts, scaled to parameters/s."""
+    import numpy as np
+    import oracle
+    import workloads
+    import threadpoolctl  # noqa: F401  (reports BLAS threads)
+    from collections import Counter
+    counts = Counter((s.m, s.n) for s in wl.matrices)
+    hp = oracle.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, 0, wl.power_iters)
+    total_s = 0.0
+    done = []
+    t_start = time.time()
+    for (m, n), c in sorted(counts.items(), key=lambda kv: kv[0][0] * kv[0][1]):
+        if time.time() - t_start > budget_s:
+            break
+        i = next(k for k, s in enumerate(wl.matrices) if (s.m, s.n) == (m, n))
+        st = oracle.OracleState.fresh(workloads.initial_weight(wl, i).double().numpy(), wl.m_dtype)
+        G = workloads.gradient(wl, i, 1).double().numpy()
+        # basis from an earlier refresh: the identity is as costly for the oracle as any other
+        t0 = time.time()
+        oracle.step(st, G, hp)
+        dt = time.time() - t0
+        total_s += dt * c
+        done.append((m, n, c, dt))
+    covered = sum(m * n * c for m, n, c, _ in done)
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((x.get("num_threads") or 0) for x in threadpool_info()) or None
+    except Exception:
+        pass
+    return {
+        "value": covered / total_s if total_s > 0 else None,
+        "unit": "params/s",
+        "cores": threads or os.cpu_count(),
+        "kind": "oracle",
+        "sample": ("one non-refresh fp64 oracle step on one matrix of each distinct shape "
+                   + ", ".join(f"{m}x{n} ({dt:.2f} s, x{c})" for m, n, c, dt in done)
+                   + "; refresh steps excluded, so this over-states the oracle's rate"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="qwen3_1p7b")
+    ap.add_argument("--cpu-sample-s", type=float, default=30.0,
+                    help="budget for the oracle CPU baseline (0 disables it)")
+    ap.add_argument("--no-timing", action="store_true", help="do not record per-phase HIP events")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the step shards by whole matrix; see the design notes)", file=sys.stderr)
+        return 2
+
+    import torch
+    import matrix_optimizer_step_02_amd as mo
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.get(args.workload)
+    shapes = [(s.m, s.n) for s in wl.matrices]
+    params = sum(m * n for m, n in shapes)
+    print(f"[bench] workload {wl.key}: {len(shapes)} matrices, {params / 1e9:.3f} G params, "
+          f"M {wl.m_dtype}, K={wl.K}, p={wl.power_iters}", flush=True)
+
+    states = []
+    for i, s in enumerate(wl.matrices):
+        W0 = workloads.initial_weight(wl, i, dev)
+        st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0)
+        st["G"].copy_(workloads.gradient(wl, i, 1, dev))
+        states.append(st)
+    hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes)
+    grp = mo.RotatedAdamGroup(states, hp)
+    _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
+    torch.cuda.synchronize()
+    print(f"[bench] state ready, {ngroups} micro-groups, workspace {grp.ws_bytes / 1e9:.2f} GB", flush=True)
+
+    for w in range(args.warmup):
+        grp.step()
+        torch.cuda.synchronize()
+        print(f"[bench] warmup step {w + 1} done", flush=True)
+
+    t_first = grp.t + 1
+    refresh_steps = [t for t in range(t_first, t_first + args.steps)
+                     if wl.K > 0 and (t - 1) % wl.K == 0]
+    if not args.no_timing:
+        grp.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        grp.step()
+        if (k + 1) % 5 == 0 or k + 1 == args.steps:
+            print(f"[bench] timed step {k + 1}/{args.steps} enqueued", flush=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    phases = grp.read_timing() if not args.no_timing else {}
+    grp.set_timing(False)
+
+    ms_per_step = 1e3 * elapsed / args.steps
+    steps_per_s = args.steps / elapsed
+    value = params * steps_per_s
+
+    roofline = None
+    extra = {}
+    if phases:
+        pf = phase_flops(shapes)
+        flops = sum(pf.values()) * args.steps
+        ms = sum(phases[k][0] for k in pf)
+        launches = sum(phases[k][1] for k in pf)
+        achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else None
+        roofline = {
+            "bound": "mfma", "achieved": achieved, "peak": MI355X_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None, "traffic": None,
+            "kernel": "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)",
+            "launches": launches, "avg_launch_ms": ms / max(launches, 1),
+            "flops_per_launch": flops / max(launches, 1),
+        }
+        eb = elementwise_bytes(shapes, wl.m_dtype)
+        extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items()}
+        extra["phase_launches"] = {k: v[1] for k, v in phases.items()}
+        extra["phase_tflops"] = {k: (pf[k] * args.steps / (phases[k][0] * 1e-3) / 1e12 if phases[k][0] else None)
+                                 for k in pf}
+        extra["elementwise_gbps"] = {k: (eb[k] * args.steps / (phases[k][0] * 1e-3) / 1e9 if phases[k][0] else None)
+                                     for k in eb}
+        if refresh_steps:
+            extra["refresh_ms_each"] = phases["refresh"][0] / len(refresh_steps)
+
+    cpu = None
+    if args.cpu_sample_s > 0:
+        print("[bench] timing the oracle on the host (cpu_baseline)", flush=True)
+        cpu = cpu_baseline(wl, args.cpu_sample_s)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.key, "matrices": len(shapes), "params": params,
+                   "momentum_dtype": wl.m_dtype, "K": wl.K, "power_iters": wl.power_iters,
+                   "micro_groups": ngroups, "refresh_steps_timed": refresh_steps},
+        "steps_per_s": steps_per_s,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    out.update(extra)
+    grp.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,179 @@
+/*
+ * matopt.h -- C ABI of the MI355X (gfx950) rotated-basis matrix-optimizer step.
+ *
+ * What the library computes, per whole weight matrix W (m x n) with gradient G
+ * (sources cited by page title and section):
+ *
+ *   t <- t + 1
+ *   M <- beta1 M + (1 - beta1) G                    momentum matrix, original space
+ *        ("Pipeline parallelism and gradient staleness optimisation in
+ *        distributed training", section 2.2: one momentum matrix per weight
+ *        matrix; "Large-model distributed optimisation: three-layer decoupling
+ *        of communication, memory and compute", section 2.2: EMA form)
+ *   if K > 0 and (t - 1) mod K == 0:  refresh U, V  (pipeline-staleness page,
+ *        section 2.2 power iteration + QR, section 4.2 period K)
+ *   G~ = U^T G V,  m~ = U^T M V                     two-sided rotation (section 2.2)
+ *   v  <- beta2 v + (1 - beta2) G~^2                three-layer page, section 2.1;
+ *                                                   G~ squared in fp32 (section 5.2)
+ *   u  =  m~ / (sqrt(v) + eps)                      pipeline-staleness page, 2.1
+ *   W  <- W - lr U u V^T
+ *
+ * Refresh (orthogonal iteration with positive-diagonal QR), r = min(m, n):
+ *   for (X, A) in ((U, M M^T), (V, M^T M)), power_iters times:
+ *       Y = A X[:, :r]  (formed as M (M^T X_r) or M^T (M X_r))
+ *       Z = [Y | X[:, r:]]                          previous-basis completion
+ *       X = Q of Z = QR with diag(R) > 0 (a zero diagonal counts as positive)
+ *
+ * Matrices are packed into micro-groups in longest-processing-time order of
+ * the cost m*n*(m+n), each group's fp32 gradient payload sum(4 m n) capped by
+ * capacity_bytes (Canzona page, section 3.2.2 micro-group scheduling, section
+ * 6.1: 512 MB-class groups). One step runs the groups one after another on the
+ * caller's stream, each phase of a group as one grouped launch.
+ *
+ * Conventions for every call:
+ *  - All matrices are dense row-major with row stride equal to their column
+ *    count (W, G, M, v: stride n; U: stride m; V: stride n).
+ *  - Device pointers are HIP device (or managed) memory of the current device;
+ *    host pointers are ordinary host memory. The library allocates no device
+ *    memory: every tensor and the workspace belong to the caller and must
+ *    outlive the group.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    step/refresh only enqueue work (no host synchronisation, no allocation).
+ *  - A group is not thread-safe. Distinct groups are independent. Pointers of
+ *    different matrices (and the workspace) must not overlap.
+ *  - Errors: a negative opt_status is returned synchronously for argument or
+ *    state errors; opt_last_error() gives a text (thread-local, valid until the
+ *    next call on this thread). Asynchronous device faults surface as OPT_EHIP
+ *    on a later call. NaN/Inf in inputs propagate (no masking).
+ */
+#ifndef MATOPT_H_
+#define MATOPT_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct opt_group_s* opt_group_t;
+
+typedef enum {
+    OPT_OK = 0,
+    OPT_EINVAL = -1,        /* bad argument: null/misshaped/aliased pointer, bad hyper-parameter */
+    OPT_ENOWS = -2,         /* workspace smaller than opt_group_workspace_size() */
+    OPT_EHIP = -3,          /* a HIP runtime call failed (text carries hipGetErrorString) */
+    OPT_EUNSUPPORTED = -4,  /* dtype or size outside what the kernels implement */
+    OPT_ESTATE = -5         /* call on a group in an unusable state */
+} opt_status;
+
+typedef enum { OPT_F32 = 0, OPT_BF16 = 1 } opt_dtype;
+
+/* One whole matrix (the atomicity constraint of the Canzona page, section 2.1:
+ * a matrix optimizer needs the entire matrix, never a shard). */
+typedef struct {
+    int64_t m, n;          /* rows, columns; 1 <= m, n <= OPT_MAX_DIM */
+    float* W;              /* m x n fp32 master weights, updated in place */
+    const float* G;        /* m x n fp32 gradient, read by every step (caller refills it) */
+    void* M;               /* m x n momentum, fp32 or bf16 (M_dtype), updated in place; start at 0 */
+    int32_t M_dtype;       /* opt_dtype */
+    float* v;              /* m x n fp32 second moment in rotated coordinates; start at 0 */
+    float* U;              /* m x m fp32 orthonormal left basis, updated by refreshes; start at I */
+    float* V;              /* n x n fp32 orthonormal right basis, updated by refreshes; start at I */
+} opt_matrix_desc;
+
+typedef struct {
+    float beta1;              /* momentum EMA weight, 0 <= beta1 < 1 */
+    float beta2;              /* second-moment EMA weight, 0 <= beta2 < 1 */
+    float eps;                /* > 0 */
+    float lr;                 /* finite */
+    int32_t K;                /* refresh period in steps; 0 = no automatic refresh */
+    int32_t power_iters;      /* orthogonal-iteration passes per refresh, >= 1 */
+    uint64_t capacity_bytes;  /* micro-group cap on sum(4 m n); 0 selects 1 << 29 (512 MiB) */
+    uint32_t flags;           /* reserved, must be 0 */
+} opt_hparams;
+
+#define OPT_MAX_DIM 16384       /* largest m or n the QR panel kernel supports */
+#define OPT_MAX_MATRICES 65536
+
+/* Bytes of device workspace a group over these matrices needs (host only).
+ * The workspace holds the device-side work lists and the scratch of one
+ * micro-group (reused by every group in turn). */
+opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
+                                    const opt_hparams* hp, uint64_t* bytes);
+
+/* Validate, plan the micro-groups, lay out the workspace and upload the work
+ * lists with an asynchronous copy on `stream`. `workspace` must be device
+ * memory of at least opt_group_workspace_size() bytes, 256-byte aligned.
+ * The step counter starts at t = 0. On success *out receives the group. */
+opt_status opt_group_create(const opt_matrix_desc* descs, int32_t count, const opt_hparams* hp,
+                            void* workspace, uint64_t workspace_bytes, void* stream,
+                            opt_group_t* out);
+
+/* One optimizer step over every matrix (see the top of this file). Enqueues
+ * on `stream`; t is incremented on the host before enqueueing. */
+opt_status opt_group_step(opt_group_t g, void* stream);
+
+/* Refresh U and V of every matrix from the current M with `power_iters`
+ * passes (>= 1); W, M, v and t are untouched. Enqueues on `stream`. */
+opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* stream);
+
+/* Step counter, for checkpoint/resume (all other state is caller-owned). */
+opt_status opt_group_get_step(opt_group_t g, int64_t* t);
+opt_status opt_group_set_step(opt_group_t g, int64_t t);   /* t >= 0 */
+opt_status opt_group_set_lr(opt_group_t g, float lr);      /* finite */
+
+/* Micro-group plan, host only (pointers in descs are not read). order[k] is
+ * the input index of the k-th matrix in LPT order; group_of[i] the micro-group
+ * of input matrix i; *num_groups the number of groups. Arrays have `count`
+ * entries; any output pointer may be NULL. */
+opt_status opt_plan(const opt_matrix_desc* descs, int32_t count, const opt_hparams* hp,
+                    int32_t* order, int32_t* group_of, int32_t* num_groups);
+
+/* Per-phase timing with HIP events recorded on the step's stream around every
+ * launch of the phase. Phases: */
+enum {
+    OPT_PHASE_MOMENTUM = 0,   /* momentum EMA (elementwise) */
+    OPT_PHASE_REFRESH = 1,    /* whole basis refresh (products + QR) */
+    OPT_PHASE_ROT_LEFT = 2,   /* U^T G, U^T M                 (grouped GEMM) */
+    OPT_PHASE_ROT_RIGHT = 3,  /* (U^T G) V, (U^T M) V         (grouped GEMM) */
+    OPT_PHASE_ADAM = 4,       /* v and u in the rotated basis (elementwise) */
+    OPT_PHASE_BACK_LEFT = 5,  /* U u                          (grouped GEMM) */
+    OPT_PHASE_BACK_RIGHT = 6, /* W -= lr (U u) V^T            (grouped GEMM + apply) */
+    OPT_NUM_PHASES = 7
+};
+/* enable != 0 starts recording (and clears the totals); 0 stops. */
+opt_status opt_group_set_timing(opt_group_t g, int32_t enable);
+/* Synchronises with the last recorded event, then writes for each phase the
+ * summed milliseconds and the number of launches recorded since timing was
+ * enabled (arrays of OPT_NUM_PHASES entries; either may be NULL). */
+opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches);
+
+void opt_group_destroy(opt_group_t g);   /* NULL is ignored; does not synchronise */
+
+const char* opt_last_error(void);
+
+/* ---- building blocks, exported for testing and reuse ------------------- */
+
+/* C = alpha * op(A) op(B) + beta * C on device memory, fp32 accumulate.
+ * op(A) is M x K: A is stored row-major as M x K (trans_a = 0, row stride
+ * lda >= K) or as K x M (trans_a = 1, lda >= M). op(B) is K x N: B stored as
+ * K x N (trans_b = 0, ldb >= N) or N x K (trans_b = 1, ldb >= K). A and B
+ * are fp32 or bf16 (a_dtype, b_dtype); C is fp32 (ldc >= N). beta == 0 does
+ * not read C. M, N, K >= 0 (an empty product only scales C). */
+opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
+                    float alpha, const void* A, int32_t a_dtype, int64_t lda,
+                    const void* B, int32_t b_dtype, int64_t ldb,
+                    float beta, float* C, int64_t ldc, void* stream);
+
+/* Q = the positive-diagonal-R orthonormal factor of the d x d fp32 matrix Z
+ * (row-major, stride d). Z is overwritten with the Householder factorisation
+ * (R on and above the diagonal, reflectors below). Q must not overlap Z.
+ * `workspace` is device memory of opt_orthonormalize_workspace_size(d) bytes. */
+opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes);
+opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
+                              uint64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MATOPT_H_ */

@@ -1,0 +1,820 @@
+// C ABI of the rotated-basis matrix-optimizer step: argument checks, the
+// micro-group planner, the workspace layout and the per-step launch schedule.
+//
+// Planner (Canzona page, section 3.2.2 micro-group scheduling; section 6.1
+// group size): matrices are ordered by cost m*n*(m+n) descending, ties by
+// input position (a stable longest-processing-time order), and packed next-fit
+// into micro-groups whose fp32 gradient payload sum(4 m n) stays within the
+// capacity; a new group opens when the next matrix does not fit. Inside one
+// group every phase is a single grouped launch whose problems are again in
+// LPT order (costliest k first), so the hardware dispatcher hands the long
+// tiles out first.
+//
+// Workspace: [device work lists of every group | scratch of one group]. The
+// scratch of a group is either its rotation buffers (U^T G, U^T M, G~, m~;
+// 4 m n floats per matrix, reused for U u and u) or its refresh buffers (Gram
+// products, the QR inputs Z and the QR scratch), never both at once, and the
+// groups run one after another on the stream, so one maximum-sized scratch
+// serves them all.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "matopt.h"
+#include "internal.h"
+
+using namespace matopt;
+
+namespace {
+
+thread_local std::string g_err;
+
+opt_status fail(opt_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+opt_status hip_fail(hipError_t e, const char* where) {
+    return fail(OPT_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Mat {
+    opt_matrix_desc d;
+    int idx;
+    double cost;
+    bool bf16;
+};
+
+// Byte offsets into the table image (host) / table region (device).
+struct GemmLaunch {
+    int variant = 0;
+    int nprob = 0;
+    int total_tiles = 0;
+    uint64_t probs = 0;
+    uint64_t tb = 0;
+};
+struct EwLaunch {
+    int nseg = 0;
+    int64_t chunks = 0;
+    uint64_t segs = 0;
+};
+struct QrBatch {
+    int njobs = 0;
+    uint64_t jobs = 0;
+    std::vector<int> np;   // panels per job, descending
+    int max_d = 0;
+};
+struct CopyLaunch {
+    int n = 0;
+    uint64_t jobs = 0;
+    int max_d = 0;
+};
+
+struct Group {
+    std::vector<int> mats;   // indices into opt_group_s::mats, LPT order
+    EwLaunch mom, adam;
+    std::vector<GemmLaunch> rot_left, rot_right, back_left, back_right;
+    std::vector<GemmLaunch> prod1, prod2;
+    CopyLaunch comp;
+    QrBatch qr;
+    uint64_t rot_bytes = 0, ref_bytes = 0;
+};
+
+// Append-only image of device tables with 256-byte aligned entries.
+struct Image {
+    std::vector<uint8_t> bytes;
+    template <class T>
+    uint64_t put(const std::vector<T>& v) {
+        const uint64_t off = align_up(bytes.size());
+        bytes.resize(off + sizeof(T) * v.size());
+        if (!v.empty()) memcpy(bytes.data() + off, v.data(), sizeof(T) * v.size());
+        return off;
+    }
+};
+
+}  // namespace
+
+struct opt_group_s {
+    std::vector<Mat> mats;
+    opt_hparams hp{};
+    int64_t t = 0;
+    std::vector<Group> groups;
+    char* ws = nullptr;
+    uint64_t ws_bytes = 0;
+    Image img;
+    uint64_t table_bytes = 0, scratch_bytes = 0;
+    int device = 0;
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> pool;
+    size_t pool_used = 0;
+    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> recs;
+};
+
+namespace {
+
+// ---------------------------------------------------------------- checks ----
+
+opt_status check_hparams(const opt_hparams* hp) {
+    if (!hp) return fail(OPT_EINVAL, "hparams is NULL");
+    if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f)) return fail(OPT_EINVAL, "beta1 must be in [0, 1)");
+    if (!(hp->beta2 >= 0.f && hp->beta2 < 1.f)) return fail(OPT_EINVAL, "beta2 must be in [0, 1)");
+    if (!(hp->eps > 0.f) || !std::isfinite(hp->eps)) return fail(OPT_EINVAL, "eps must be finite and > 0");
+    if (!std::isfinite(hp->lr)) return fail(OPT_EINVAL, "lr must be finite");
+    if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
+    if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
+    if (hp->flags != 0) return fail(OPT_EINVAL, "flags must be 0");
+    return OPT_OK;
+}
+
+uint64_t capacity_of(const opt_hparams* hp) {
+    return hp->capacity_bytes ? hp->capacity_bytes : (1ull << 29);
+}
+
+struct Span {
+    uintptr_t lo, hi;
+    int mat;
+    const char* what;
+};
+
+opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparams* hp,
+                       bool need_ptrs) {
+    if (!d) return fail(OPT_EINVAL, "descs is NULL");
+    if (count < 1 || count > OPT_MAX_MATRICES)
+        return fail(OPT_EINVAL, "count must be in [1, %d]", OPT_MAX_MATRICES);
+    opt_status st = check_hparams(hp);
+    if (st) return st;
+    const uint64_t cap = capacity_of(hp);
+    std::vector<Span> spans;
+    for (int i = 0; i < count; ++i) {
+        const opt_matrix_desc& x = d[i];
+        if (x.m < 1 || x.n < 1) return fail(OPT_EINVAL, "matrix %d: m and n must be >= 1", i);
+        if (x.m > OPT_MAX_DIM || x.n > OPT_MAX_DIM)
+            return fail(OPT_EUNSUPPORTED, "matrix %d: m and n must be <= %d", i, OPT_MAX_DIM);
+        if (x.M_dtype != OPT_F32 && x.M_dtype != OPT_BF16)
+            return fail(OPT_EUNSUPPORTED, "matrix %d: M_dtype must be OPT_F32 or OPT_BF16", i);
+        if ((uint64_t)4 * x.m * x.n > cap)
+            return fail(OPT_EINVAL,
+                        "matrix %d: its gradient payload 4*m*n = %llu exceeds the micro-group "
+                        "capacity %llu (a matrix is never split)",
+                        i, (unsigned long long)(4ull * x.m * x.n), (unsigned long long)cap);
+        if (!need_ptrs) continue;
+        if (!x.W || !x.G || !x.M || !x.v || !x.U || !x.V)
+            return fail(OPT_EINVAL, "matrix %d: a tensor pointer is NULL", i);
+        const uint64_t mn = (uint64_t)x.m * x.n;
+        const uint64_t esz = x.M_dtype == OPT_BF16 ? 2 : 4;
+        auto add = [&](const void* p, uint64_t bytes, const char* what) {
+            spans.push_back({(uintptr_t)p, (uintptr_t)p + bytes, i, what});
+        };
+        add(x.W, 4 * mn, "W");
+        add(x.G, 4 * mn, "G");
+        add(x.M, esz * mn, "M");
+        add(x.v, 4 * mn, "v");
+        add(x.U, 4ull * x.m * x.m, "U");
+        add(x.V, 4ull * x.n * x.n, "V");
+        if (!aligned(x.W, 4) || !aligned(x.G, 4) || !aligned(x.v, 4) || !aligned(x.U, 4) ||
+            !aligned(x.V, 4) || !aligned(x.M, esz))
+            return fail(OPT_EINVAL, "matrix %d: a tensor pointer is not aligned to its element", i);
+    }
+    if (need_ptrs) {
+        std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+        for (size_t k = 1; k < spans.size(); ++k)
+            if (spans[k].lo < spans[k - 1].hi)
+                return fail(OPT_EINVAL, "tensors overlap: %s of matrix %d and %s of matrix %d",
+                            spans[k - 1].what, spans[k - 1].mat, spans[k].what, spans[k].mat);
+    }
+    return OPT_OK;
+}
+
+// --------------------------------------------------------------- planning ----
+
+void plan_groups(const opt_matrix_desc* d, int32_t count, const opt_hparams* hp,
+                 std::vector<int>& order, std::vector<std::vector<int>>& groups) {
+    order.resize(count);
+    std::iota(order.begin(), order.end(), 0);
+    auto cost = [&](int i) { return (double)d[i].m * (double)d[i].n * (double)(d[i].m + d[i].n); };
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost(a) > cost(b); });
+    const uint64_t cap = capacity_of(hp);
+    groups.clear();
+    uint64_t used = 0;
+    for (int i : order) {
+        const uint64_t bytes = 4ull * d[i].m * d[i].n;
+        if (groups.empty() || used + bytes > cap) {
+            groups.emplace_back();
+            used = 0;
+        }
+        groups.back().push_back(i);
+        used += bytes;
+    }
+}
+
+// Vector loads need 4-element groups that never straddle the end of a row.
+uint32_t vec_flags(const void* A, int64_t lda, int64_t a_cols, bool a_bf16, const void* B, int64_t ldb,
+                   int64_t b_cols, bool b_bf16) {
+    uint32_t f = 0;
+    if (lda % 4 == 0 && a_cols % 4 == 0 && aligned(A, a_bf16 ? 8 : 16)) f |= GF_A_VEC;
+    if (ldb % 4 == 0 && b_cols % 4 == 0 && aligned(B, b_bf16 ? 8 : 16)) f |= GF_B_VEC;
+    return f;
+}
+
+struct PGemm {
+    GemmProb p;
+    int variant;
+};
+
+// op(A) is M x K: A stored M x K (at = false) or K x M (at = true); op(B) is
+// K x N: B stored K x N (bt = false) or N x K (bt = true).
+PGemm mk(bool at, bool bt, const void* A, bool a_bf16, int64_t lda, const void* B, bool b_bf16,
+         int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N, int64_t K, float alpha, float beta) {
+    PGemm g;
+    GemmProb& p = g.p;
+    p = GemmProb{};
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.flags = vec_flags(A, lda, at ? M : K, a_bf16, B, ldb, bt ? K : N, b_bf16);
+    p.alpha = alpha;
+    p.beta = beta;
+    p.tiles_m = (int32_t)((M + kGemmBM - 1) / kGemmBM);
+    p.tiles_n = (int32_t)((N + kGemmBN - 1) / kGemmBN);
+    g.variant = gemm_variant(at, bt, a_bf16, b_bf16);
+    return g;
+}
+
+// One grouped launch per operand variant present in the phase.
+std::vector<GemmLaunch> put_gemm(Image& img, const std::vector<PGemm>& all) {
+    std::vector<GemmLaunch> out;
+    for (int v = 0; v < 16; ++v) {
+        std::vector<GemmProb> probs;
+        for (const PGemm& x : all)
+            if (x.variant == v && x.p.tiles_m > 0 && x.p.tiles_n > 0) probs.push_back(x.p);
+        if (probs.empty()) continue;
+        // LPT over tiles: the cost of a tile grows with K.
+        std::stable_sort(probs.begin(), probs.end(),
+                         [](const GemmProb& a, const GemmProb& b) { return a.K > b.K; });
+        std::vector<int32_t> tb;
+        int total = 0;
+        for (const GemmProb& p : probs) {
+            tb.push_back(total);
+            total += p.tiles_m * p.tiles_n;
+        }
+        GemmLaunch L;
+        L.variant = v;
+        L.nprob = (int)probs.size();
+        L.total_tiles = total;
+        L.probs = img.put(probs);
+        L.tb = img.put(tb);
+        out.push_back(L);
+    }
+    return out;
+}
+
+EwLaunch put_ew(Image& img, std::vector<EwSeg> segs) {
+    int64_t chunks = 0;
+    for (EwSeg& s : segs) {
+        s.chunk_begin = chunks;
+        chunks += (s.n + kEwChunk - 1) / kEwChunk;
+    }
+    EwLaunch L;
+    L.nseg = (int)segs.size();
+    L.chunks = chunks;
+    L.segs = img.put(segs);
+    return L;
+}
+
+int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
+
+struct QrBytes {
+    uint64_t Z, T, part, W2;
+};
+QrBytes qr_job_bytes(int64_t d) {
+    QrBytes b;
+    b.Z = align_up(4ull * d * d);
+    b.T = align_up(4ull * panels((int)d) * kQrPB * kQrPB);
+    b.part = align_up(4ull * kQrMaxSplits * kQrPB * d);
+    b.W2 = align_up(4ull * kQrPB * d);
+    return b;
+}
+
+// Build every table of the group object. `scratch` is the device address of
+// the scratch region (any value when only sizes are wanted).
+void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scratch) {
+    g->groups.clear();
+    g->img.bytes.clear();
+    g->scratch_bytes = 0;
+    for (const std::vector<int>& members : plan) {
+        Group G;
+        G.mats = members;
+        // ---- rotation scratch
+        std::vector<PGemm> left, right, bl, br;
+        std::vector<EwSeg> mom, adam;
+        uint64_t off = 0;
+        for (int mi : members) {
+            const Mat& M = g->mats[mi];
+            const opt_matrix_desc& x = M.d;
+            const int64_t m = x.m, n = x.n, mn = m * n;
+            float* TG = (float*)(scratch + off); off += align_up(4ull * mn);
+            float* TM = (float*)(scratch + off); off += align_up(4ull * mn);
+            float* Gt = (float*)(scratch + off); off += align_up(4ull * mn);
+            float* mt = (float*)(scratch + off); off += align_up(4ull * mn);
+            // U^T G, U^T M (A = U stored m x m read transposed)
+            left.push_back(mk(true, false, x.U, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
+            left.push_back(mk(true, false, x.U, false, m, x.M, M.bf16, n, TM, n, m, n, m, 1.f, 0.f));
+            // (U^T G) V, (U^T M) V
+            right.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
+            right.push_back(mk(false, false, TM, false, n, x.V, false, n, mt, n, m, n, n, 1.f, 0.f));
+            // U u (u in the m~ slot) -> TG slot
+            bl.push_back(mk(false, false, x.U, false, m, mt, false, n, TG, n, m, n, m, 1.f, 0.f));
+            // W += (-1 * lr) (U u) V^T  (B = V stored n x n read transposed)
+            br.push_back(mk(false, true, TG, false, n, x.V, false, n, x.W, n, m, n, n, -1.f, 1.f));
+            EwSeg e{};
+            e.a = x.G;
+            e.b = x.M;
+            e.n = mn;
+            e.b_bf16 = M.bf16;
+            e.vec = aligned(x.G, 16) && aligned(x.M, M.bf16 ? 8 : 16);
+            mom.push_back(e);
+            EwSeg a{};
+            a.a = Gt;
+            a.b = mt;
+            a.c = x.v;
+            a.n = mn;
+            a.vec = aligned(Gt, 16) && aligned(mt, 16) && aligned(x.v, 16);
+            adam.push_back(a);
+        }
+        G.rot_bytes = off;
+        G.rot_left = put_gemm(g->img, left);
+        G.rot_right = put_gemm(g->img, right);
+        G.back_left = put_gemm(g->img, bl);
+        G.back_right = put_gemm(g->img, br);
+        G.mom = put_ew(g->img, mom);
+        G.adam = put_ew(g->img, adam);
+
+        // ---- refresh scratch
+        off = 0;
+        std::vector<PGemm> p1, p2;
+        std::vector<CopyJob> comp;
+        struct JobSrc { int64_t d; float* Z; float* X; };
+        std::vector<JobSrc> jsrc;
+        for (int mi : members) {
+            const Mat& M = g->mats[mi];
+            const opt_matrix_desc& x = M.d;
+            const int64_t m = x.m, n = x.n, r = std::min(m, n);
+            float* B1U = (float*)(scratch + off); off += align_up(4ull * n * r);
+            float* B1V = (float*)(scratch + off); off += align_up(4ull * m * r);
+            float* ZU = (float*)(scratch + off); off += align_up(4ull * m * m);
+            float* ZV = (float*)(scratch + off); off += align_up(4ull * n * n);
+            // B1U = M^T U[:, :r]   (n x r): A = M stored m x n read transposed
+            p1.push_back(mk(true, false, x.M, M.bf16, n, x.U, false, m, B1U, r, n, r, m, 1.f, 0.f));
+            // B1V = M V[:, :r]     (m x r)
+            p1.push_back(mk(false, false, x.M, M.bf16, n, x.V, false, n, B1V, r, m, r, n, 1.f, 0.f));
+            // ZU[:, :r] = M B1U     (m x r)
+            p2.push_back(mk(false, false, x.M, M.bf16, n, B1U, false, r, ZU, m, m, r, n, 1.f, 0.f));
+            // ZV[:, :r] = M^T B1V   (n x r)
+            p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
+            if (r < m) comp.push_back({x.U, ZU, (int32_t)m, (int32_t)r});
+            if (r < n) comp.push_back({x.V, ZV, (int32_t)n, (int32_t)r});
+            jsrc.push_back({m, ZU, x.U});
+            jsrc.push_back({n, ZV, x.V});
+        }
+        std::stable_sort(jsrc.begin(), jsrc.end(), [](const JobSrc& a, const JobSrc& b) { return a.d > b.d; });
+        std::vector<QrJob> jobs;
+        for (const JobSrc& s : jsrc) {
+            QrBytes b = qr_job_bytes(s.d);
+            QrJob j{};
+            j.Z = s.Z;
+            j.X = s.X;
+            j.d = (int32_t)s.d;
+            j.np = panels((int)s.d);
+            j.T = (float*)(scratch + off); off += b.T;
+            j.part = (float*)(scratch + off); off += b.part;
+            j.W2 = (float*)(scratch + off); off += b.W2;
+            jobs.push_back(j);
+            G.qr.np.push_back(j.np);
+        }
+        G.ref_bytes = off;
+        G.prod1 = put_gemm(g->img, p1);
+        G.prod2 = put_gemm(g->img, p2);
+        G.comp.n = (int)comp.size();
+        G.comp.max_d = 0;
+        for (const CopyJob& c : comp) G.comp.max_d = std::max(G.comp.max_d, (int)c.d);
+        G.comp.jobs = g->img.put(comp);
+        G.qr.njobs = (int)jobs.size();
+        G.qr.max_d = jobs.empty() ? 0 : jobs[0].d;
+        G.qr.jobs = g->img.put(jobs);
+        g->scratch_bytes = std::max(g->scratch_bytes, std::max(G.rot_bytes, G.ref_bytes));
+        g->groups.push_back(std::move(G));
+    }
+    g->table_bytes = align_up(g->img.bytes.size());
+}
+
+// ------------------------------------------------------------- execution ----
+
+template <class T>
+const T* dptr(const opt_group_s* g, uint64_t off) {
+    return (const T*)(g->ws + off);
+}
+
+hipEvent_t next_event(opt_group_s* g) {
+    if (g->pool_used == g->pool.size()) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        g->pool.push_back(e);
+    }
+    return g->pool[g->pool_used++];
+}
+
+struct PhaseScope {
+    opt_group_s* g;
+    int phase;
+    hipStream_t s;
+    hipEvent_t b = nullptr;
+    PhaseScope(opt_group_s* g_, int ph, hipStream_t s_) : g(g_), phase(ph), s(s_) {
+        if (g->timing) {
+            b = next_event(g);
+            if (b) (void)hipEventRecord(b, s);
+        }
+    }
+    ~PhaseScope() {
+        if (g->timing && b) {
+            hipEvent_t e = next_event(g);
+            if (e) {
+                (void)hipEventRecord(e, s);
+                g->recs.push_back({phase, {b, e}});
+            }
+        }
+    }
+};
+
+hipError_t run_gemm(const opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alpha_scale,
+                    hipStream_t s) {
+    for (const GemmLaunch& L : Ls) {
+        hipError_t e = launch_gemm_grouped(L.variant, dptr<GemmProb>(g, L.probs), dptr<int32_t>(g, L.tb),
+                                           L.nprob, L.total_tiles, alpha_scale, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, int max_d, hipStream_t s) {
+    const int njobs = (int)np.size();
+    if (njobs == 0) return hipSuccess;
+    const int maxp = np[0];
+    hipError_t e;
+    auto active = [&](int p) {
+        int a = 0;
+        while (a < njobs && np[a] > p) ++a;
+        return a;
+    };
+    for (int p = 0; p < maxp; ++p) {
+        const int na = active(p);
+        if ((e = launch_qr_panel(jobs, na, p, s))) return e;
+        if ((e = launch_qr_dots(jobs, na, p, max_d, 0, s))) return e;
+        if ((e = launch_qr_reduce(jobs, na, p, max_d, 0, s))) return e;
+        if ((e = launch_qr_update(jobs, na, p, max_d, 0, s))) return e;
+    }
+    if ((e = launch_qr_init_q(jobs, njobs, max_d, s))) return e;
+    for (int p = maxp - 1; p >= 0; --p) {
+        const int na = active(p);
+        if ((e = launch_qr_dots(jobs, na, p, max_d, 1, s))) return e;
+        if ((e = launch_qr_reduce(jobs, na, p, max_d, 1, s))) return e;
+        if ((e = launch_qr_update(jobs, na, p, max_d, 1, s))) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_refresh(opt_group_s* g, const Group& G, int power_iters, hipStream_t s) {
+    PhaseScope ps(g, OPT_PHASE_REFRESH, s);
+    hipError_t e;
+    for (int it = 0; it < power_iters; ++it) {
+        if ((e = run_gemm(g, G.prod1, 1.f, s))) return e;
+        if ((e = run_gemm(g, G.prod2, 1.f, s))) return e;
+        if ((e = launch_copy_cols(dptr<CopyJob>(g, G.comp.jobs), G.comp.n, G.comp.max_d, s))) return e;
+        if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.max_d, s))) return e;
+    }
+    return hipSuccess;
+}
+
+opt_status check_group(opt_group_t g) {
+    if (!g) return fail(OPT_EINVAL, "group is NULL");
+    return OPT_OK;
+}
+
+opt_status set_device(opt_group_t g) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != g->device) return fail(OPT_ESTATE, "group was created on device %d, current device is %d",
+                                      g->device, cur);
+    return OPT_OK;
+}
+
+}  // namespace
+
+// =================================================================== ABI ====
+
+extern "C" {
+
+const char* opt_last_error(void) { return g_err.c_str(); }
+
+opt_status opt_plan(const opt_matrix_desc* descs, int32_t count, const opt_hparams* hp,
+                    int32_t* order, int32_t* group_of, int32_t* num_groups) {
+    opt_status st = check_descs(descs, count, hp, false);
+    if (st) return st;
+    std::vector<int> ord;
+    std::vector<std::vector<int>> groups;
+    plan_groups(descs, count, hp, ord, groups);
+    if (order)
+        for (int k = 0; k < count; ++k) order[k] = ord[k];
+    if (group_of)
+        for (size_t gi = 0; gi < groups.size(); ++gi)
+            for (int i : groups[gi]) group_of[i] = (int32_t)gi;
+    if (num_groups) *num_groups = (int32_t)groups.size();
+    return OPT_OK;
+}
+
+opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
+                                    const opt_hparams* hp, uint64_t* bytes) {
+    if (!bytes) return fail(OPT_EINVAL, "bytes is NULL");
+    opt_status st = check_descs(descs, count, hp, false);
+    if (st) return st;
+    std::vector<int> ord;
+    std::vector<std::vector<int>> plan;
+    plan_groups(descs, count, hp, ord, plan);
+    opt_group_s tmp;
+    for (int i = 0; i < count; ++i) {
+        Mat M{descs[i], i, 0.0, descs[i].M_dtype == OPT_BF16};
+        tmp.mats.push_back(M);
+    }
+    build(&tmp, plan, (char*)(uintptr_t)kAlign);
+    *bytes = tmp.table_bytes + tmp.scratch_bytes;
+    return OPT_OK;
+}
+
+opt_status opt_group_create(const opt_matrix_desc* descs, int32_t count, const opt_hparams* hp,
+                            void* workspace, uint64_t workspace_bytes, void* stream,
+                            opt_group_t* out) {
+    if (!out) return fail(OPT_EINVAL, "out is NULL");
+    *out = nullptr;
+    opt_status st = check_descs(descs, count, hp, true);
+    if (st) return st;
+    if (!workspace) return fail(OPT_EINVAL, "workspace is NULL");
+    if (!aligned(workspace, kAlign)) return fail(OPT_EINVAL, "workspace must be 256-byte aligned");
+    uint64_t need = 0;
+    if ((st = opt_group_workspace_size(descs, count, hp, &need))) return st;
+    if (workspace_bytes < need)
+        return fail(OPT_ENOWS, "workspace has %llu bytes, %llu needed",
+                    (unsigned long long)workspace_bytes, (unsigned long long)need);
+    {
+        const uintptr_t lo = (uintptr_t)workspace, hi = lo + need;
+        for (int i = 0; i < count; ++i) {
+            const opt_matrix_desc& x = descs[i];
+            const void* ptrs[6] = {x.W, x.G, x.M, x.v, x.U, x.V};
+            for (const void* p : ptrs)
+                if ((uintptr_t)p >= lo && (uintptr_t)p < hi)
+                    return fail(OPT_EINVAL, "matrix %d: a tensor lies inside the workspace", i);
+        }
+    }
+    opt_group_s* g = new opt_group_s();
+    g->hp = *hp;
+    if (!g->hp.capacity_bytes) g->hp.capacity_bytes = 1ull << 29;
+    for (int i = 0; i < count; ++i) {
+        Mat M{descs[i], i, (double)descs[i].m * descs[i].n * (descs[i].m + descs[i].n),
+              descs[i].M_dtype == OPT_BF16};
+        g->mats.push_back(M);
+    }
+    std::vector<int> ord;
+    std::vector<std::vector<int>> plan;
+    plan_groups(descs, count, hp, ord, plan);
+    g->ws = (char*)workspace;
+    g->ws_bytes = workspace_bytes;
+    // Two passes: the table size does not depend on the scratch address.
+    build(g, plan, (char*)(uintptr_t)kAlign);
+    const uint64_t tbytes = g->table_bytes;
+    build(g, plan, g->ws + tbytes);
+    if (g->table_bytes != tbytes) {
+        delete g;
+        return fail(OPT_ESTATE, "internal: table layout changed between passes");
+    }
+    hipError_t e = hipGetDevice(&g->device);
+    if (e != hipSuccess) {
+        delete g;
+        return hip_fail(e, "hipGetDevice");
+    }
+    if (!g->img.bytes.empty()) {
+        e = hipMemcpyAsync(g->ws, g->img.bytes.data(), g->img.bytes.size(), hipMemcpyHostToDevice,
+                           (hipStream_t)stream);
+        if (e != hipSuccess) {
+            delete g;
+            return hip_fail(e, "hipMemcpyAsync(work lists)");
+        }
+    }
+    *out = g;
+    return OPT_OK;
+}
+
+opt_status opt_group_step(opt_group_t g, void* stream) {
+    opt_status st = check_group(g);
+    if (st || (st = set_device(g))) return st;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before step");
+    hipStream_t s = (hipStream_t)stream;
+    g->t += 1;
+    const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
+    for (const Group& G : g->groups) {
+        {
+            PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+            e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
+            if (e) return hip_fail(e, "momentum launch");
+        }
+        if (refresh && (e = run_refresh(g, G, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+        {
+            PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
+            if ((e = run_gemm(g, G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");
+        }
+        {
+            PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
+            if ((e = run_gemm(g, G.rot_right, 1.f, s))) return hip_fail(e, "rotation launch");
+        }
+        {
+            PhaseScope ps(g, OPT_PHASE_ADAM, s);
+            e = launch_rotated_adam(dptr<EwSeg>(g, G.adam.segs), G.adam.nseg, G.adam.chunks, g->hp.beta2,
+                                    g->hp.eps, s);
+            if (e) return hip_fail(e, "rotated Adam launch");
+        }
+        {
+            PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
+            if ((e = run_gemm(g, G.back_left, 1.f, s))) return hip_fail(e, "rotation launch");
+        }
+        {
+            PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s);
+            if ((e = run_gemm(g, G.back_right, g->hp.lr, s))) return hip_fail(e, "update launch");
+        }
+    }
+    return OPT_OK;
+}
+
+opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* stream) {
+    opt_status st = check_group(g);
+    if (st || (st = set_device(g))) return st;
+    if (power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
+    for (const Group& G : g->groups)
+        if ((e = run_refresh(g, G, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
+    return OPT_OK;
+}
+
+opt_status opt_group_get_step(opt_group_t g, int64_t* t) {
+    if (opt_status st = check_group(g)) return st;
+    if (!t) return fail(OPT_EINVAL, "t is NULL");
+    *t = g->t;
+    return OPT_OK;
+}
+
+opt_status opt_group_set_step(opt_group_t g, int64_t t) {
+    if (opt_status st = check_group(g)) return st;
+    if (t < 0) return fail(OPT_EINVAL, "t must be >= 0");
+    g->t = t;
+    return OPT_OK;
+}
+
+opt_status opt_group_set_lr(opt_group_t g, float lr) {
+    if (opt_status st = check_group(g)) return st;
+    if (!std::isfinite(lr)) return fail(OPT_EINVAL, "lr must be finite");
+    g->hp.lr = lr;
+    return OPT_OK;
+}
+
+opt_status opt_group_set_timing(opt_group_t g, int32_t enable) {
+    if (opt_status st = check_group(g)) return st;
+    g->timing = enable != 0;
+    g->recs.clear();
+    g->pool_used = 0;
+    return OPT_OK;
+}
+
+opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
+    if (opt_status st = check_group(g)) return st;
+    double acc[OPT_NUM_PHASES] = {0};
+    int64_t cnt[OPT_NUM_PHASES] = {0};
+    if (!g->recs.empty()) {
+        hipError_t e = hipEventSynchronize(g->recs.back().second.second);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+        for (auto& r : g->recs) {
+            float t = 0.f;
+            e = hipEventElapsedTime(&t, r.second.first, r.second.second);
+            if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+            acc[r.first] += t;
+            cnt[r.first] += 1;
+        }
+    }
+    for (int i = 0; i < OPT_NUM_PHASES; ++i) {
+        if (ms) ms[i] = acc[i];
+        if (launches) launches[i] = cnt[i];
+    }
+    return OPT_OK;
+}
+
+void opt_group_destroy(opt_group_t g) {
+    if (!g) return;
+    for (hipEvent_t e : g->pool) (void)hipEventDestroy(e);
+    delete g;
+}
+
+// ------------------------------------------------------- building blocks ----
+
+opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                    const void* A, int32_t a_dtype, int64_t lda, const void* B, int32_t b_dtype,
+                    int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(OPT_EINVAL, "negative dimension");
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2)
+        return fail(OPT_EUNSUPPORTED, "dimension too large");
+    if ((a_dtype != OPT_F32 && a_dtype != OPT_BF16) || (b_dtype != OPT_F32 && b_dtype != OPT_BF16))
+        return fail(OPT_EUNSUPPORTED, "operand dtype must be OPT_F32 or OPT_BF16");
+    if (M == 0 || N == 0) return OPT_OK;
+    if (!C) return fail(OPT_EINVAL, "C is NULL");
+    if (ldc < N) return fail(OPT_EINVAL, "ldc < N");
+    if (K > 0) {
+        if (!A || !B) return fail(OPT_EINVAL, "A or B is NULL");
+        if (trans_a ? lda < M : lda < K) return fail(OPT_EINVAL, "lda too small");
+        if (trans_b ? ldb < K : ldb < N) return fail(OPT_EINVAL, "ldb too small");
+    }
+    const PGemm pg = mk(trans_a != 0, trans_b != 0, A, a_dtype == OPT_BF16, lda, B, b_dtype == OPT_BF16, ldb,
+                        C, ldc, M, N, K, alpha, beta);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before gemm");
+    e = launch_gemm_single(pg.variant, pg.p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return OPT_OK;
+}
+
+opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes) {
+    if (!bytes) return fail(OPT_EINVAL, "bytes is NULL");
+    if (d < 1) return fail(OPT_EINVAL, "d must be >= 1");
+    if (d > OPT_MAX_DIM) return fail(OPT_EUNSUPPORTED, "d must be <= %d", OPT_MAX_DIM);
+    QrBytes b = qr_job_bytes(d);
+    *bytes = align_up(sizeof(QrJob)) + b.T + b.part + b.W2;
+    return OPT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+__global__ void put_job_kernel(QrJob* dst, QrJob val) { *dst = val; }
+}  // namespace
+
+extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
+                                         uint64_t workspace_bytes, void* stream) {
+    uint64_t need = 0;
+    if (opt_status st = opt_orthonormalize_workspace_size(d, &need)) return st;
+    if (!Z || !Q || !workspace) return fail(OPT_EINVAL, "a pointer is NULL");
+    if (!aligned(workspace, kAlign)) return fail(OPT_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(OPT_ENOWS, "workspace too small: %llu < %llu",
+                                            (unsigned long long)workspace_bytes, (unsigned long long)need);
+    const uintptr_t zl = (uintptr_t)Z, zh = zl + 4ull * d * d, ql = (uintptr_t)Q, qh = ql + 4ull * d * d;
+    if (zl < qh && ql < zh) return fail(OPT_EINVAL, "Z and Q overlap");
+    QrBytes b = qr_job_bytes(d);
+    char* w = (char*)workspace;
+    QrJob j{};
+    j.Z = Z;
+    j.X = Q;
+    j.d = (int32_t)d;
+    j.np = panels((int)d);
+    uint64_t off = align_up(sizeof(QrJob));
+    j.T = (float*)(w + off); off += b.T;
+    j.part = (float*)(w + off); off += b.part;
+    j.W2 = (float*)(w + off);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before orthonormalize");
+    hipLaunchKernelGGL(put_job_kernel, dim3(1), dim3(1), 0, s, (QrJob*)w, j);
+    if ((e = hipGetLastError())) return hip_fail(e, "job upload");
+    std::vector<int> np{j.np};
+    if ((e = run_qr((const QrJob*)w, np, (int)d, s))) return hip_fail(e, "QR launch");
+    return OPT_OK;
+}

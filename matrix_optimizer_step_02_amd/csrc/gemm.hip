@@ -1,0 +1,429 @@
+// Grouped fp32 MFMA GEMM for gfx950 (CDNA4).
+//
+// Serves the two-sided rotations U^T X V, the rotation back U u V^T (with the
+// weight update fused into the epilogue), the Gram products of the basis
+// refresh, and the compact-WY trailing updates of the blocked QR.
+//
+// gfx950 has no reduced-precision fp32 matrix path, so the contraction runs on
+// v_mfma_f32_32x32x2_f32 (32x32 outputs, 2-deep k, fp32 accumulate). A
+// workgroup of 4 wavefronts owns a 128x128 tile, each wavefront a 64x64
+// quarter held as 2x2 MFMA accumulators (64 AGPR-class registers). K advances
+// in slabs of 32 staged through LDS with two buffers, so one barrier per slab
+// separates the store of slab k+1 from the reads of slab k; the global loads
+// of slab k+1 are issued before the MFMAs of slab k.
+//
+// LDS layouts keep every MFMA operand read conflict-free:
+//  * an operand whose non-k index is contiguous in memory (A stored K x M,
+//    B stored K x N) is kept k-major, [32][128], read 4 bytes per lane with
+//    32 consecutive lanes on consecutive words;
+//  * an operand whose k index is contiguous (A stored M x K, B stored N x K)
+//    is kept [128][32 + 4], read 16 bytes per lane. Within a group of 8 k
+//    values, MFMA s (0..3) takes k = 8g + s from lanes 0..31 and
+//    k = 8g + 4 + s from lanes 32..63, so one 16-byte read feeds four MFMAs;
+//    the row pitch of 36 words puts 8 consecutive rows on 8 distinct 4-bank
+//    groups.
+// The same k assignment is used for both operands, so the sum is unchanged.
+//
+// Work distribution: one workgroup per output tile; problems of a grouped
+// launch are concatenated in tile space in longest-processing-time order
+// (costliest k first) by the host. Consecutive workgroup ids are spread by
+// the dispatcher over the 8 XCDs, so ids are remapped in windows of 8 x 16
+// tiles to give each XCD 16 neighbouring tiles (shared A rows / B columns in
+// its own L2) while keeping the LPT order at window granularity.
+#include "internal.h"
+
+namespace matopt {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace {
+
+constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
+constexpr int NT = 256;
+constexpr int KPAD = BK + 4;   // pitch of k-contiguous LDS rows
+constexpr int XCD = 8;
+constexpr int XCD_RUN = 16;
+constexpr int GROUP_M = 4;
+
+template <bool AT> struct ALayout {
+    static constexpr int size = AT ? BK * BM : BM * KPAD;
+};
+template <bool BT> struct BLayout {
+    static constexpr int size = BT ? BN * KPAD : BK * BN;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Four consecutive elements (row, col..col+3) of a row-major stored matrix
+// with `rows` x `cols` valid elements, zero outside. The address is clamped
+// into the valid region so that every lane issues a load (no divergent
+// branches); the mask then zeroes what lies outside. With VEC the load is one
+// 16-byte (fp32) or 8-byte (bf16) access, which needs ld % 4 == 0,
+// cols % 4 == 0 and an aligned base (so a clamped group never leaves the row).
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4(const void* base, int64_t ld, int row, int col, int rows,
+                                       int cols, bool vec) {
+    const int64_t rc = row < rows ? row : rows - 1;
+    f32x4 v;
+    if (vec) {
+        const int last = (cols - 1) & ~3;
+        const int64_t off = rc * ld + (col < last ? col : last);
+        if (BF16) {
+            const uint2 u = *(const uint2*)((const uint16_t*)base + off);
+            v[0] = __uint_as_float(u.x << 16);
+            v[1] = __uint_as_float(u.x & 0xffff0000u);
+            v[2] = __uint_as_float(u.y << 16);
+            v[3] = __uint_as_float(u.y & 0xffff0000u);
+        } else {
+            v = *(const f32x4*)((const float*)base + off);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int ce = col + e < cols ? col + e : cols - 1;
+            if (BF16) v[e] = bf16_to_f32(((const uint16_t*)base)[rc * ld + ce]);
+            else      v[e] = ((const float*)base)[rc * ld + ce];
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (!(row < rows && col + e < cols)) v[e] = 0.f;
+    return v;
+}
+
+template <bool AT, bool ABF, bool UL>
+__device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, f32x4 (&r)[4]) {
+    const bool vec = p.flags & GF_A_VEC;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = tid + NT * q;
+        if (AT) {  // stored K x M: slab rows are k, 32 float4 per row of 128
+            const int rr = f >> 5, c4 = f & 31;
+            r[q] = load4<ABF>(p.A, p.lda, k0 + rr, m0 + 4 * c4, p.K, p.M, vec);
+        } else {   // stored M x K: slab rows are m, 8 float4 per row of 32
+            const int rr = f >> 3, c4 = f & 7;
+            const int row = m0 + rr, col = k0 + 4 * c4;
+            r[q] = load4<ABF>(p.A, p.lda, row, col, p.M, p.K, vec);
+            if (UL) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (row < col + e) r[q][e] = 0.f;
+                    else if (row == col + e) r[q][e] = 1.f;
+                }
+            }
+        }
+    }
+}
+
+template <bool BT, bool BBF>
+__device__ __forceinline__ void load_b(const GemmProb& p, int n0, int k0, f32x4 (&r)[4]) {
+    const bool vec = p.flags & GF_B_VEC;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = tid + NT * q;
+        if (BT) {  // stored N x K
+            const int rr = f >> 3, c4 = f & 7;
+            r[q] = load4<BBF>(p.B, p.ldb, n0 + rr, k0 + 4 * c4, p.N, p.K, vec);
+        } else {   // stored K x N
+            const int rr = f >> 5, c4 = f & 31;
+            r[q] = load4<BBF>(p.B, p.ldb, k0 + rr, n0 + 4 * c4, p.K, p.N, vec);
+        }
+    }
+}
+
+template <bool AT>
+__device__ __forceinline__ void store_a(float* As, const f32x4 (&r)[4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = tid + NT * q;
+        if (AT) {
+            const int rr = f >> 5, c4 = f & 31;
+            *(f32x4*)&As[rr * BM + 4 * c4] = r[q];
+        } else {
+            const int rr = f >> 3, c4 = f & 7;
+            *(f32x4*)&As[rr * KPAD + 4 * c4] = r[q];
+        }
+    }
+}
+
+template <bool BT>
+__device__ __forceinline__ void store_b(float* Bs, const f32x4 (&r)[4]) {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int f = tid + NT * q;
+        if (BT) {
+            const int rr = f >> 3, c4 = f & 7;
+            *(f32x4*)&Bs[rr * KPAD + 4 * c4] = r[q];
+        } else {
+            const int rr = f >> 5, c4 = f & 31;
+            *(f32x4*)&Bs[rr * BN + 4 * c4] = r[q];
+        }
+    }
+}
+
+template <bool AT, bool BT>
+__device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int wm, int wn, int lane,
+                                         f32x16 (&acc)[2][2]) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int g = 0; g < BK / 8; ++g) {
+        f32x4 a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = wm * 64 + i * 32 + l32;
+            if (AT) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * BM + row];
+            } else {
+                a[i] = *(const f32x4*)&As[row * KPAD + 8 * g + 4 * h];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = wn * 64 + j * 32 + l32;
+            if (BT) {
+                b[j] = *(const f32x4*)&Bs[col * KPAD + 8 * g + 4 * h];
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * BN + col];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j],
+                                                                    0, 0, 0);
+    }
+}
+
+template <bool AT, bool BT, bool ABF, bool BBF, bool UL>
+__device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
+                                          float* smem) {
+    constexpr int AS = ALayout<AT>::size, BS = BLayout<BT>::size;
+    float* As0 = smem;
+    float* As1 = smem + AS;
+    float* Bs0 = smem + 2 * AS;
+    float* Bs1 = smem + 2 * AS + BS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    f32x4 ra[4], rb[4];
+    if (nk > 0) {
+        load_a<AT, ABF, UL>(p, m0, 0, ra);
+        load_b<BT, BBF>(p, n0, 0, rb);
+        store_a<AT>(As0, ra);
+        store_b<BT>(Bs0, rb);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            load_a<AT, ABF, UL>(p, m0, (kt + 1) * BK, ra);
+            load_b<BT, BBF>(p, n0, (kt + 1) * BK, rb);
+        }
+        if (kt & 1) mma_slab<AT, BT>(As1, Bs1, wm, wn, lane, acc);
+        else        mma_slab<AT, BT>(As0, Bs0, wm, wn, lane, acc);
+        if (more) {
+            if (kt & 1) { store_a<AT>(As0, ra); store_b<BT>(Bs0, rb); }
+            else        { store_a<AT>(As1, ra); store_b<BT>(Bs1, rb); }
+        }
+        __syncthreads();
+    }
+
+    // Epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
+    // column l%32 of its 32x32 block: 32 lanes store 128 contiguous bytes.
+    const float alpha = p.alpha * alpha_scale, beta = p.beta;
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + l32;
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < p.M) {
+                    float* c = p.C + (int64_t)row * p.ldc + col;
+                    float val = alpha * acc[i][j][r];
+                    if (beta != 0.f) val += beta * *c;
+                    *c = val;
+                }
+            }
+        }
+}
+
+// Tile -> (row, column) of tiles, grouped by GROUP_M tile rows for L2 reuse.
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int per_group = GROUP_M * tiles_n;
+    const int gidx = t / per_group;
+    const int first = gidx * GROUP_M;
+    const int gsz = min(tiles_m - first, GROUP_M);
+    const int r = t - gidx * per_group;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+// Workgroup id -> logical tile: within each full window of XCD*XCD_RUN ids,
+// the ids the dispatcher sends to one XCD get XCD_RUN consecutive tiles.
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int win = XCD * XCD_RUN;
+    const int w0 = (bid / win) * win;
+    if (w0 + win > total) return bid;
+    const int r = bid - w0;
+    return w0 + (r % XCD) * XCD_RUN + r / XCD;
+}
+
+template <bool AT, bool BT>
+constexpr int smem_floats() {
+    return 2 * (ALayout<AT>::size + BLayout<BT>::size);
+}
+
+template <bool AT, bool BT, bool ABF, bool BBF>
+__global__ __launch_bounds__(NT, 2) void gemm_grouped_kernel(const GemmProb* __restrict__ probs,
+                                                           const int32_t* __restrict__ tile_begin,
+                                                           int nprob, int total_tiles,
+                                                           float alpha_scale) {
+    __shared__ __attribute__((aligned(16))) float smem[smem_floats<AT, BT>()];
+    const int bid = xcd_remap(blockIdx.x, total_tiles);
+    int lo = 0, hi = nprob - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tile_begin[mid] <= bid) lo = mid; else hi = mid - 1;
+    }
+    const GemmProb p = probs[lo];
+    int tm, tn;
+    raster(bid - tile_begin[lo], p.tiles_m, p.tiles_n, tm, tn);
+    gemm_tile<AT, BT, ABF, BBF, false>(p, tm, tn, alpha_scale, smem);
+}
+
+template <bool AT, bool BT, bool ABF, bool BBF>
+__global__ __launch_bounds__(NT, 2) void gemm_single_kernel(GemmProb p) {
+    __shared__ __attribute__((aligned(16))) float smem[smem_floats<AT, BT>()];
+    const int total = p.tiles_m * p.tiles_n;
+    const int bid = xcd_remap(blockIdx.x, total);
+    int tm, tn;
+    raster(bid, p.tiles_m, p.tiles_n, tm, tn);
+    gemm_tile<AT, BT, ABF, BBF, false>(p, tm, tn, 1.f, smem);
+}
+
+template <bool AT, bool BT, bool ABF, bool BBF>
+hipError_t grouped(const GemmProb* probs, const int32_t* tile_begin, int nprob, int total,
+                   float alpha_scale, hipStream_t s) {
+    if (total <= 0 || nprob <= 0) return hipSuccess;
+    gemm_grouped_kernel<AT, BT, ABF, BBF><<<dim3(total), dim3(NT), 0, s>>>(probs, tile_begin, nprob,
+                                                                            total, alpha_scale);
+    return hipGetLastError();
+}
+
+template <bool AT, bool BT, bool ABF, bool BBF>
+hipError_t single(const GemmProb& p, hipStream_t s) {
+    const int total = p.tiles_m * p.tiles_n;
+    if (total <= 0) return hipSuccess;
+    gemm_single_kernel<AT, BT, ABF, BBF><<<dim3(total), dim3(NT), 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// ---- QR trailing update: C -= Y W2 with Y the unit-lower reflector block ----
+//
+// Factorisation (q_mode 0) at panel p: C = Z[k:, k+jb:], Y = Z[k:, k:k+jb].
+// Q formation (q_mode 1): C = X[k:, k:]. W2 (jb x N') comes from qr_reduce.
+__global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restrict__ jobs, int p,
+                                                        int q_mode) {
+    __shared__ __attribute__((aligned(16))) float smem[smem_floats<false, false>()];
+    const QrJob J = jobs[blockIdx.y];
+    const int k = p * kQrPB;
+    if (k >= J.d) return;
+    const int jb = min(kQrPB, J.d - k);
+    const int L = J.d - k;
+    const int ncols = q_mode ? L : L - jb;
+    if (ncols <= 0) return;
+    GemmProb g;
+    g.A = J.Z + (int64_t)k * J.d + k;
+    g.B = J.W2;
+    g.C = (q_mode ? J.X : J.Z) + (int64_t)k * J.d + k + (q_mode ? 0 : jb);
+    g.lda = J.d;
+    g.ldb = J.d;
+    g.ldc = J.d;
+    g.M = L;
+    g.N = ncols;
+    g.K = jb;
+    g.flags = (J.d % 4 == 0) ? (GF_A_VEC | GF_B_VEC) : 0u;
+    g.alpha = -1.f;
+    g.beta = 1.f;
+    g.tiles_m = (L + BM - 1) / BM;
+    g.tiles_n = (ncols + BN - 1) / BN;
+    const int total = g.tiles_m * g.tiles_n;
+    if ((int)blockIdx.x >= total) return;
+    int tm, tn;
+    raster(xcd_remap(blockIdx.x, total), g.tiles_m, g.tiles_n, tm, tn);
+    gemm_tile<false, false, false, false, true>(g, tm, tn, 1.f, smem);
+}
+
+hipError_t launch_qr_update(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
+                            hipStream_t s) {
+    if (njobs <= 0) return hipSuccess;
+    const int k = p * kQrPB;
+    const int L = max_d - k;
+    if (L <= 0) return hipSuccess;
+    const int tiles = ((L + BM - 1) / BM) * ((L + BN - 1) / BN);
+    qr_update_kernel<<<dim3(tiles, njobs), dim3(NT), 0, s>>>(jobs, p, q_mode);
+    return hipGetLastError();
+}
+
+int gemm_tiles(int64_t M, int64_t N) {
+    return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
+}
+
+#define MATOPT_VARIANTS(X)                                                                         \
+    X(0, false, false, false, false) X(1, true, false, false, false) X(2, false, true, false, false)   \
+    X(3, true, true, false, false) X(4, false, false, true, false) X(5, true, false, true, false)      \
+    X(6, false, true, true, false) X(7, true, true, true, false) X(8, false, false, false, true)       \
+    X(9, true, false, false, true) X(10, false, true, false, true) X(11, true, true, false, true)      \
+    X(12, false, false, true, true) X(13, true, false, true, true) X(14, false, true, true, true)      \
+    X(15, true, true, true, true)
+
+hipError_t launch_gemm_grouped(int variant, const GemmProb* probs, const int32_t* tile_begin,
+                               int nprob, int total_tiles, float alpha_scale, hipStream_t s) {
+    switch (variant) {
+#define X(v, at, bt, abf, bbf) \
+    case v: return grouped<at, bt, abf, bbf>(probs, tile_begin, nprob, total_tiles, alpha_scale, s);
+        MATOPT_VARIANTS(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gemm_single(int variant, const GemmProb& prob, hipStream_t s) {
+    switch (variant) {
+#define X(v, at, bt, abf, bbf) \
+    case v: return single<at, bt, abf, bbf>(prob, s);
+        MATOPT_VARIANTS(X)
+#undef X
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace matopt

@@ -1,0 +1,121 @@
+// Internal structures shared by the host scheduler (api.hip) and the kernels.
+// Everything here is device-visible plain data: the host builds arrays of
+// these once per group and uploads them into the caller's workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace matopt {
+
+// ---------------------------------------------------------------- GEMM ----
+
+enum : uint32_t {
+    GF_A_VEC = 1u << 0,   // A: ld % 4 == 0 and 16-byte (fp32) / 8-byte (bf16) aligned base
+    GF_B_VEC = 1u << 1,
+};
+
+// One product C = alpha * alpha_scale * op(A) op(B) + beta * C. The launch's
+// template fixes whether A is stored K x M (transposed) and B stored N x K.
+struct GemmProb {
+    const void* A;
+    const void* B;
+    float* C;
+    int64_t lda, ldb, ldc;
+    int32_t M, N, K;
+    uint32_t flags;
+    float alpha, beta;
+    int32_t tiles_m, tiles_n;
+};
+
+// Launch variant: bit 0 A stored K x M (transposed), bit 1 B stored N x K,
+// bit 2 A is bfloat16, bit 3 B is bfloat16. All problems of one grouped
+// launch share the variant.
+inline int gemm_variant(bool at, bool bt, bool a_bf16, bool b_bf16) {
+    return (at ? 1 : 0) | (bt ? 2 : 0) | (a_bf16 ? 4 : 0) | (b_bf16 ? 8 : 0);
+}
+
+constexpr int kGemmBM = 128;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 32;
+
+// Grouped launch over `nprob` problems laid out back to back in tile space;
+// tile_begin[p] is the first tile of problem p (ascending, tile_begin[0] = 0).
+hipError_t launch_gemm_grouped(int variant, const GemmProb* probs, const int32_t* tile_begin,
+                               int nprob, int total_tiles, float alpha_scale, hipStream_t s);
+hipError_t launch_gemm_single(int variant, const GemmProb& prob, hipStream_t s);
+int gemm_tiles(int64_t M, int64_t N);
+
+// --------------------------------------------------------- elementwise ----
+
+struct EwSeg {
+    const float* a;       // momentum: G      rotated Adam: G~
+    void* b;              // momentum: M      rotated Adam: m~ in, u out (same slot)
+    float* c;             // rotated Adam: v
+    int64_t n;            // elements
+    int64_t chunk_begin;  // first chunk of this segment in the launch
+    int32_t b_bf16;       // momentum stored as bfloat16
+    int32_t vec;          // all pointers 16-byte aligned (vector path)
+};
+
+constexpr int kEwThreads = 256;
+constexpr int kEwPerThread = 16;
+constexpr int kEwChunk = kEwThreads * kEwPerThread;
+
+hipError_t launch_momentum(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1,
+                           hipStream_t s);
+hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta2,
+                               float eps, hipStream_t s);
+
+// ------------------------------------------------------------------ QR ----
+
+constexpr int kQrPB = 32;          // panel width (reflectors per compact-WY block)
+constexpr int kQrMaxSplits = 16;   // row splits of the reflector-transpose products
+constexpr int kQrPanelThreads = 512;
+
+// One d x d orthonormalisation: Z (row stride d) is factorised in place, Q is
+// formed in X. Scratch: T (np * PB * PB), part (kQrMaxSplits * PB * d),
+// W2 (PB * d).
+struct QrJob {
+    float* Z;
+    float* X;
+    float* T;
+    float* part;
+    float* W2;
+    int32_t d;
+    int32_t np;   // panels: ceil(d / PB)
+};
+
+// Jobs are sorted by d descending, so the jobs still active at panel p are a
+// prefix of the array; `njobs` passed to each launch is that prefix length,
+// `max_d` the d of job 0.
+hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, hipStream_t s);
+hipError_t launch_qr_dots(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
+                          hipStream_t s);
+hipError_t launch_qr_reduce(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
+                            hipStream_t s);
+hipError_t launch_qr_update(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
+                            hipStream_t s);
+hipError_t launch_qr_init_q(const QrJob* jobs, int njobs, int max_d, hipStream_t s);
+
+// Strided copy of columns [c0, d) of X into Z (both d x d, row stride d):
+// the completion block of the refresh input.
+struct CopyJob {
+    const float* src;
+    float* dst;
+    int32_t d;
+    int32_t c0;
+};
+hipError_t launch_copy_cols(const CopyJob* jobs, int njobs, int max_d, hipStream_t s);
+
+// Splits used by the reflector-transpose product at panel p of a d x d QR.
+__host__ __device__ inline int qr_splits(int rows) {
+    int s = (rows + 255) / 256;
+    return s < kQrMaxSplits ? (s < 1 ? 1 : s) : kQrMaxSplits;
+}
+__host__ __device__ inline int qr_chunk(int rows, int splits) {
+    int c = (rows + splits - 1) / splits;
+    return (c + 1) & ~1;
+}
+
+}  // namespace matopt

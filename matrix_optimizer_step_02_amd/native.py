@@ -1,0 +1,186 @@
+"""ctypes binding of libmatopt.so (include/matopt.h), argument marshalling only.
+
+Every function here has the name of the C entry point it calls and forwards
+plain pointers and sizes; all computation runs in the HIP library. If the
+library is missing or fails to load, every call raises: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_lib", "libmatopt.so")
+
+OPT_OK, OPT_EINVAL, OPT_ENOWS, OPT_EHIP, OPT_EUNSUPPORTED, OPT_ESTATE = 0, -1, -2, -3, -4, -5
+OPT_F32, OPT_BF16 = 0, 1
+OPT_MAX_DIM = 16384
+PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right")
+OPT_NUM_PHASES = len(PHASES)
+
+EXPORTED = (
+    "opt_group_workspace_size", "opt_group_create", "opt_group_step", "opt_group_refresh_basis",
+    "opt_group_get_step", "opt_group_set_step", "opt_group_set_lr", "opt_plan",
+    "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
+    "opt_gemm", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
+)
+
+
+class MatoptError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"matopt status {status}: {msg}")
+        self.status = status
+
+
+class opt_matrix_desc(C.Structure):
+    _fields_ = [
+        ("m", C.c_int64), ("n", C.c_int64),
+        ("W", C.c_void_p), ("G", C.c_void_p), ("M", C.c_void_p), ("M_dtype", C.c_int32),
+        ("v", C.c_void_p), ("U", C.c_void_p), ("V", C.c_void_p),
+    ]
+
+
+class opt_hparams(C.Structure):
+    _fields_ = [
+        ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("lr", C.c_float),
+        ("K", C.c_int32), ("power_iters", C.c_int32),
+        ("capacity_bytes", C.c_uint64), ("flags", C.c_uint32),
+    ]
+
+
+_lib: Optional[C.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load the library once. torch is imported first so that the HIP runtime
+    it ships is the one the library binds to (same soname)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  (binds libamdhip64 before the library is loaded)
+    if not os.path.exists(path):
+        raise MatoptError(OPT_ESTATE, f"{path} is missing: run __graft_entry__.build() first")
+    lib = C.CDLL(path)
+    vp, i32, i64, u64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_uint64, C.c_float
+    D, H = C.POINTER(opt_matrix_desc), C.POINTER(opt_hparams)
+    sig = {
+        "opt_group_workspace_size": ([D, i32, H, C.POINTER(u64)], i32),
+        "opt_group_create": ([D, i32, H, vp, u64, vp, C.POINTER(vp)], i32),
+        "opt_group_step": ([vp, vp], i32),
+        "opt_group_refresh_basis": ([vp, i32, vp], i32),
+        "opt_group_get_step": ([vp, C.POINTER(i64)], i32),
+        "opt_group_set_step": ([vp, i64], i32),
+        "opt_group_set_lr": ([vp, f32], i32),
+        "opt_plan": ([D, i32, H, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)], i32),
+        "opt_group_set_timing": ([vp, i32], i32),
+        "opt_group_read_timing": ([vp, C.POINTER(C.c_double), C.POINTER(i64)], i32),
+        "opt_group_destroy": ([vp], None),
+        "opt_last_error": ([], C.c_char_p),
+        "opt_gemm": ([i32, i32, i64, i64, i64, f32, vp, i32, i64, vp, i32, i64, f32, vp, i64, vp], i32),
+        "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
+        "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(st: int):
+    if st != OPT_OK:
+        raise MatoptError(st, load().opt_last_error().decode(errors="replace"))
+
+
+def _descs(descs: Sequence[opt_matrix_desc]):
+    arr = (opt_matrix_desc * len(descs))(*descs)
+    return arr, len(descs)
+
+
+def opt_last_error() -> str:
+    return load().opt_last_error().decode(errors="replace")
+
+
+def opt_group_workspace_size(descs, hp: opt_hparams) -> int:
+    arr, n = _descs(descs)
+    out = C.c_uint64(0)
+    _check(load().opt_group_workspace_size(arr, n, C.byref(hp), C.byref(out)))
+    return out.value
+
+
+def opt_group_create(descs, hp: opt_hparams, workspace_ptr: int, workspace_bytes: int,
+                     stream_ptr: int) -> int:
+    arr, n = _descs(descs)
+    out = C.c_void_p(0)
+    _check(load().opt_group_create(arr, n, C.byref(hp), C.c_void_p(workspace_ptr), workspace_bytes,
+                                   C.c_void_p(stream_ptr), C.byref(out)))
+    return out.value
+
+
+def opt_group_step(g: int, stream_ptr: int):
+    _check(load().opt_group_step(C.c_void_p(g), C.c_void_p(stream_ptr)))
+
+
+def opt_group_refresh_basis(g: int, power_iters: int, stream_ptr: int):
+    _check(load().opt_group_refresh_basis(C.c_void_p(g), power_iters, C.c_void_p(stream_ptr)))
+
+
+def opt_group_get_step(g: int) -> int:
+    t = C.c_int64(0)
+    _check(load().opt_group_get_step(C.c_void_p(g), C.byref(t)))
+    return t.value
+
+
+def opt_group_set_step(g: int, t: int):
+    _check(load().opt_group_set_step(C.c_void_p(g), t))
+
+
+def opt_group_set_lr(g: int, lr: float):
+    _check(load().opt_group_set_lr(C.c_void_p(g), lr))
+
+
+def opt_plan(descs, hp: opt_hparams):
+    """Returns (order, group_of, num_groups) of the micro-group planner."""
+    arr, n = _descs(descs)
+    order = (C.c_int32 * n)()
+    group_of = (C.c_int32 * n)()
+    ng = C.c_int32(0)
+    _check(load().opt_plan(arr, n, C.byref(hp), order, group_of, C.byref(ng)))
+    return list(order), list(group_of), ng.value
+
+
+def opt_group_set_timing(g: int, enable: bool):
+    _check(load().opt_group_set_timing(C.c_void_p(g), 1 if enable else 0))
+
+
+def opt_group_read_timing(g: int):
+    ms = (C.c_double * OPT_NUM_PHASES)()
+    cnt = (C.c_int64 * OPT_NUM_PHASES)()
+    _check(load().opt_group_read_timing(C.c_void_p(g), ms, cnt))
+    return {PHASES[i]: (ms[i], cnt[i]) for i in range(OPT_NUM_PHASES)}
+
+
+def opt_group_destroy(g: int):
+    if g:
+        load().opt_group_destroy(C.c_void_p(g))
+
+
+def opt_gemm(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int, a_dtype: int,
+             lda: int, B: int, b_dtype: int, ldb: int, beta: float, Cp: int, ldc: int, stream_ptr: int):
+    _check(load().opt_gemm(trans_a, trans_b, M, N, K, alpha, C.c_void_p(A), a_dtype, lda,
+                           C.c_void_p(B), b_dtype, ldb, beta, C.c_void_p(Cp), ldc,
+                           C.c_void_p(stream_ptr)))
+
+
+def opt_orthonormalize_workspace_size(d: int) -> int:
+    out = C.c_uint64(0)
+    _check(load().opt_orthonormalize_workspace_size(d, C.byref(out)))
+    return out.value
+
+
+def opt_orthonormalize(Z: int, Q: int, d: int, workspace: int, workspace_bytes: int, stream_ptr: int):
+    _check(load().opt_orthonormalize(C.c_void_p(Z), C.c_void_p(Q), d, C.c_void_p(workspace),
+                                     workspace_bytes, C.c_void_p(stream_ptr)))

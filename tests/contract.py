@@ -1,0 +1,151 @@
+"""Teacher-forced parity gates between the device path and the fp64 oracle.
+
+A free-running fp32 trajectory cannot match an fp64 one element by element
+on this method, for two reasons intrinsic to it: u = m~ / (sqrt(v) + eps)
+turns round-off into O(1/eps) values wherever v is still ~0 (the first step,
+the null block after a refresh), and basis columns past the conditioning of
+the Gram matrix are determined only up to O(u kappa). So every phase of the
+oracle consumes the device's own persisted output of the previous phase and
+each gate bounds the error that phase can add:
+
+* Gate M (momentum): oracle EMA of the device's previous M and the same G.
+  fp32: max relative error <= 1e-6. bf16: >= 99.99 % bit-identical, and every
+  element within one bf16 ulp of the reference plus the fp32 rounding of the
+  EMA's two terms, 2 u32 (|b1 M| + |(1-b1) G|): the device forms the sum in
+  fp32 and rounds once to bf16, the oracle rounds the exact sum; where the
+  two terms nearly cancel, their fp32 rounding exceeds one bf16 ulp of the
+  small result.
+* Gate A (refresh): oracle orthogonal iteration from the device's M and
+  previous U, V. (1) orthonormality of the device bases <= 1e-5; (2) forward
+  error <= 1e-4 on the well-determined columns, those whose prefix
+  conditioning kappa_j = max_{i<=j} 1/|R_ii| of the column-normalised one-shot
+  input [(A^p X)[:, :r] | X[:, r:]] is <= 1e2; the other columns are
+  determined only to O(u kappa) and are not compared (several results are
+  correct there); (3) the device Q must triangularise that input: the
+  strictly lower part of Q^T Z_hat, column-normalised, <= 1e-3.
+* Gate B (rotate, moments, apply): oracle from the device's W_{t-1},
+  v_{t-1}, M_t, U_t, V_t and the same G. v: max relative error <= 1e-4.
+  W elementwise: |W - W_ref| <= tau max|W_ref| + 6 lr sqrt((U.U) E^2 (V.V)^T)
+  where E_ab = 4 u32 sqrt(m+n) (rms(m~) + |u_ab| sqrt(1-b2) rms(G~)) /
+  (sqrt(v_ab) + eps) is the first-order fp32 error of u propagated
+  root-sum-square at 6 sigma; tau = 1e-4 (fp32 momentum) or 2e-2 (bf16).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List
+
+import numpy as np
+
+import oracle
+
+U32 = 2.0 ** -24
+
+
+def maxrel(x, ref) -> float:
+    ref = np.asarray(ref, np.float64)
+    den = np.max(np.abs(ref))
+    if den == 0:
+        return float(np.max(np.abs(np.asarray(x, np.float64))))
+    return float(np.max(np.abs(np.asarray(x, np.float64) - ref)) / den)
+
+
+@dataclass
+class GateReport:
+    name: str
+    ok: bool
+    metrics: Dict[str, float] = field(default_factory=dict)
+
+    def __str__(self):
+        ms = ", ".join(f"{k}={v:.3g}" for k, v in self.metrics.items())
+        return f"{self.name}: {'ok' if self.ok else 'FAIL'} ({ms})"
+
+
+def gate_momentum(M_prev, G, M_dev, beta1, m_dtype) -> GateReport:
+    ref = oracle.momentum_update(M_prev, G, beta1, m_dtype)
+    M_dev = np.asarray(M_dev, np.float64)
+    if m_dtype == "f32":
+        r = maxrel(M_dev, ref)
+        return GateReport("M", r <= 1e-6, {"maxrel": r})
+    same = float(np.mean(M_dev == ref))
+    b1 = oracle.as_f32_scalar(beta1)
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-38))[1] - 8)
+    f32_terms = 2 * U32 * (np.abs(b1 * np.asarray(M_prev, np.float64)) + np.abs((1 - b1) * np.asarray(G, np.float64)))
+    within = bool(np.all(np.abs(M_dev - ref) <= ulp + f32_terms))
+    return GateReport("M", within and same >= 0.9999, {"identical": same, "within_bound": float(within)})
+
+
+def _prefix_kappa(Zhat):
+    """Per-column prefix conditioning of the column-normalised matrix."""
+    norms = np.linalg.norm(Zhat, axis=0)
+    norms[norms == 0] = 1.0
+    R = np.linalg.qr(Zhat / norms, mode="r")
+    inv = 1.0 / np.maximum(np.abs(np.diag(R)), 1e-300)
+    return np.maximum.accumulate(inv)
+
+
+def one_shot_input(A, X, rank, passes):
+    Y = X.copy()
+    for _ in range(passes):
+        Y = A @ Y
+    if rank < X.shape[0]:
+        return np.concatenate([Y[:, :rank], X[:, rank:]], axis=1)
+    return Y
+
+
+def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True) -> GateReport:
+    """forward=False drops the element-wise comparison with the oracle (for
+    orders where its unblocked QR takes minutes) and keeps the properties
+    that pin the result at any size: orthonormality and triangularisation of
+    the one-shot input."""
+    X_dev = np.asarray(X_dev, np.float64)
+    d = X_dev.shape[0]
+    orth = float(np.max(np.abs(X_dev.T @ X_dev - np.eye(d))))
+    Zhat = one_shot_input(A, np.asarray(X_prev, np.float64), rank, passes)
+    good = np.zeros(d, bool)
+    fwd = 0.0
+    if forward:
+        ref = oracle.subspace_iteration(A, X_prev, rank, passes)
+        kappa = _prefix_kappa(Zhat)
+        good = kappa <= 1e2
+        fwd = float(np.max(np.abs(X_dev[:, good] - ref[:, good]))) if good.any() else 0.0
+    norms = np.linalg.norm(Zhat, axis=0)
+    norms[norms == 0] = 1.0
+    Rd = X_dev.T @ (Zhat / norms)
+    back = float(np.linalg.norm(np.tril(Rd, -1)) / max(np.linalg.norm(Rd), 1e-300))
+    ok = orth <= 1e-5 and fwd <= 1e-4 and back <= 1e-3
+    return GateReport(name, ok, {"orth": orth, "fwd_good": fwd, "good_cols": float(good.mean()),
+                                 "backward": back})
+
+
+def gate_refresh(M_t, U_prev, V_prev, U_dev, V_dev, passes, forward_max_d=1100) -> List[GateReport]:
+    M_t = np.asarray(M_t, np.float64)
+    m, n = M_t.shape
+    r = min(m, n)
+    return [gate_basis(U_dev, M_t @ M_t.T, np.asarray(U_prev, np.float64), r, passes, "A.U",
+                       forward=m <= forward_max_d),
+            gate_basis(V_dev, M_t.T @ M_t, np.asarray(V_prev, np.float64), r, passes, "A.V",
+                       forward=n <= forward_max_d)]
+
+
+def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, m_dtype) -> List[GateReport]:
+    W_ref, v_ref, it = oracle.rotated_adam_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+    rv = maxrel(v_dev, v_ref)
+    m, n = np.shape(W_prev)
+    b2 = oracle.as_f32_scalar(hp.beta2)
+    eps = oracle.as_f32_scalar(hp.eps)
+    lr = oracle.as_f32_scalar(hp.lr)
+    rms = lambda x: float(np.sqrt(np.mean(np.square(x))))
+    E = 4 * U32 * np.sqrt(m + n) * (rms(it["mt"]) + np.abs(it["u"]) * np.sqrt(1 - b2) * rms(it["Gt"]))
+    E = E / (np.sqrt(v_ref) + eps)
+    U = np.asarray(U_t, np.float64)
+    V = np.asarray(V_t, np.float64)
+    widen = 6.0 * lr * np.sqrt((U * U) @ (E * E) @ (V * V).T)
+    tau = 1e-4 if m_dtype == "f32" else 2e-2
+    base = tau * np.max(np.abs(W_ref))
+    err = np.abs(np.asarray(W_dev, np.float64) - W_ref)
+    ok_w = bool(np.all(err <= base + widen))
+    return [GateReport("B.v", rv <= 1e-4, {"maxrel": rv}),
+            GateReport("B.W", ok_w, {"maxrel": maxrel(W_dev, W_ref), "worst_ratio":
+                                     float(np.max(err / (base + widen)))})]

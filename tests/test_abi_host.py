@@ -1,0 +1,170 @@
+"""Host-side tests of the C ABI: the library loads, exports every entry point
+include/matopt.h declares, plans micro-groups as specified, and rejects bad
+arguments before touching the device (no GPU needed)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def N():
+    from matrix_optimizer_step_02_amd import native
+    if not os.path.exists(native.LIB_PATH):
+        pytest.skip("libmatopt.so not built (run __graft_entry__.build())")
+    native.load()
+    return native
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "matopt.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(opt_[a-z_]+)\s*\(", txt)))
+
+
+def test_every_declared_symbol_is_exported(N):
+    names = header_functions()
+    assert len(names) >= 15
+    lib = N.load()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(N.EXPORTED)
+
+
+def hp(N, **kw):
+    base = dict(beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-3, K=10, power_iters=1, capacity_bytes=0, flags=0)
+    base.update(kw)
+    return N.opt_hparams(**base)
+
+
+def descs(N, shapes, dtype=0, ptrs=False):
+    out = []
+    base = 1 << 40
+    for i, (m, n) in enumerate(shapes):
+        if ptrs:
+            p = [base + (i * 6 + k) * (1 << 32) for k in range(6)]
+            out.append(N.opt_matrix_desc(m, n, p[0], p[1], p[2], dtype, p[3], p[4], p[5]))
+        else:
+            out.append(N.opt_matrix_desc(m, n, 0, 0, 0, dtype, 0, 0, 0))
+    return out
+
+
+def ref_plan(shapes, cap=1 << 29):
+    """Independent statement of the planner: stable LPT by m*n*(m+n), next-fit
+    groups of total 4*m*n within the cap."""
+    order = sorted(range(len(shapes)), key=lambda i: -shapes[i][0] * shapes[i][1] * (shapes[i][0] + shapes[i][1]))
+    groups, used = [], None
+    for i in order:
+        b = 4 * shapes[i][0] * shapes[i][1]
+        if used is None or used + b > cap:
+            groups.append([])
+            used = 0
+        groups[-1].append(i)
+        used += b
+    gof = [0] * len(shapes)
+    for g, mem in enumerate(groups):
+        for i in mem:
+            gof[i] = g
+    return order, gof, len(groups)
+
+
+@pytest.mark.parametrize("key", ["tiny", "layer", "qwen3_1p7b", "microgroup_512mib", "qwen3_8b_half"])
+def test_plan_matches_reference(N, key):
+    wl = workloads.get(key)
+    shapes = [(s.m, s.n) for s in wl.matrices]
+    got = N.opt_plan(descs(N, shapes), hp(N))
+    assert got == ref_plan(shapes)
+
+
+def test_plan_known_counts(N):
+    q = [(s.m, s.n) for s in workloads.get("qwen3_1p7b").matrices]
+    assert N.opt_plan(descs(N, q), hp(N))[2] == 11
+    mg = [(s.m, s.n) for s in workloads.get("microgroup_512mib").matrices]
+    assert sum(4 * m * n for m, n in mg) == 1 << 29        # the draw fills the cap exactly
+    assert N.opt_plan(descs(N, mg), hp(N))[2] == 1
+
+
+def test_plan_lpt_ties_keep_input_order(N):
+    shapes = [(8, 8), (16, 4), (4, 16), (8, 8), (32, 32)]
+    order, _, _ = N.opt_plan(descs(N, shapes), hp(N))
+    assert order == [4, 0, 3, 1, 2] or order == [4, 1, 2, 0, 3]
+    costs = [shapes[i][0] * shapes[i][1] * sum(shapes[i]) for i in order]
+    assert costs == sorted(costs, reverse=True)
+    assert order == ref_plan(shapes)[0]
+
+
+def test_plan_custom_capacity(N):
+    shapes = [(64, 64)] * 10
+    order, gof, ng = N.opt_plan(descs(N, shapes), hp(N, capacity_bytes=3 * 4 * 64 * 64))
+    assert ng == 4 and gof == [0, 0, 0, 1, 1, 1, 2, 2, 2, 3]
+
+
+def err(N, fn, *a):
+    with pytest.raises(N.MatoptError) as e:
+        fn(*a)
+    return e.value.status
+
+
+def test_rejects_bad_hyperparameters(N):
+    d = descs(N, [(8, 8)])
+    for kw in (dict(beta1=1.0), dict(beta1=-0.1), dict(beta2=1.0), dict(eps=0.0), dict(eps=float("inf")),
+               dict(lr=float("nan")), dict(K=-1), dict(power_iters=0), dict(flags=1)):
+        assert err(N, N.opt_group_workspace_size, d, hp(N, **kw)) == N.OPT_EINVAL, kw
+
+
+def test_rejects_bad_shapes_and_dtypes(N):
+    assert err(N, N.opt_group_workspace_size, descs(N, [(0, 4)]), hp(N)) == N.OPT_EINVAL
+    assert err(N, N.opt_group_workspace_size, descs(N, [(4, -1)]), hp(N)) == N.OPT_EINVAL
+    assert err(N, N.opt_group_workspace_size, descs(N, [(N.OPT_MAX_DIM + 1, 4)]), hp(N)) == N.OPT_EUNSUPPORTED
+    assert err(N, N.opt_group_workspace_size, descs(N, [(4, 4)], dtype=7), hp(N)) == N.OPT_EUNSUPPORTED
+    # a matrix bigger than the capacity cannot be split
+    assert err(N, N.opt_group_workspace_size, descs(N, [(4096, 4096)]), hp(N, capacity_bytes=1 << 20)) == N.OPT_EINVAL
+    assert err(N, N.opt_group_workspace_size, [], hp(N)) == N.OPT_EINVAL
+
+
+def test_create_rejects_before_any_device_call(N):
+    h = hp(N)
+    ws = 1 << 44
+    assert err(N, N.opt_group_create, descs(N, [(8, 8)]), h, ws, 1 << 30, 0) == N.OPT_EINVAL  # null tensors
+    d = descs(N, [(8, 8), (8, 8)], ptrs=True)
+    d[1].W = d[0].W + 16  # overlaps matrix 0's W
+    assert err(N, N.opt_group_create, d, h, ws, 1 << 30, 0) == N.OPT_EINVAL
+    d = descs(N, [(8, 8)], ptrs=True)
+    need = N.opt_group_workspace_size(d, h)
+    assert err(N, N.opt_group_create, d, h, ws, need - 1, 0) == N.OPT_ENOWS
+    assert err(N, N.opt_group_create, d, h, 0, need, 0) == N.OPT_EINVAL
+    assert err(N, N.opt_group_create, d, h, ws + 8, need, 0) == N.OPT_EINVAL      # not 256-aligned
+    d[0].W = ws + 256                                                            # tensor inside workspace
+    assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
+    d = descs(N, [(8, 8)], ptrs=True)
+    d[0].M = d[0].M + 1                                                          # misaligned
+    assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
+
+
+def test_null_group_and_bad_building_block_args(N):
+    assert err(N, N.opt_group_step, 0, 0) == N.OPT_EINVAL
+    assert err(N, N.opt_group_get_step, 0) == N.OPT_EINVAL
+    assert err(N, N.opt_group_set_step, 0, 3) == N.OPT_EINVAL
+    assert err(N, N.opt_group_refresh_basis, 0, 1, 0) == N.OPT_EINVAL
+    N.opt_group_destroy(0)
+    assert err(N, N.opt_gemm, 0, 0, -1, 4, 4, 1.0, 1, 0, 4, 1, 0, 4, 0.0, 1, 4, 0) == N.OPT_EINVAL
+    assert err(N, N.opt_gemm, 0, 0, 4, 4, 4, 1.0, 1, 3, 4, 1, 0, 4, 0.0, 1, 4, 0) == N.OPT_EUNSUPPORTED
+    assert err(N, N.opt_gemm, 0, 0, 4, 4, 8, 1.0, 1, 0, 4, 1, 0, 4, 0.0, 1, 4, 0) == N.OPT_EINVAL  # lda < K
+    N.opt_gemm(0, 0, 0, 4, 4, 1.0, 0, 0, 4, 0, 0, 4, 0.0, 0, 4, 0)              # empty: no-op
+    assert err(N, N.opt_orthonormalize_workspace_size, 0) == N.OPT_EINVAL
+    assert err(N, N.opt_orthonormalize_workspace_size, N.OPT_MAX_DIM + 1) == N.OPT_EUNSUPPORTED
+    assert N.opt_orthonormalize_workspace_size(100) > 0
+
+
+def test_workspace_is_max_over_groups(N):
+    """Scratch is sized for the largest micro-group, not the sum."""
+    one_group = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 128), hp(N))  # 128 x 4 MiB = cap
+    two_groups = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 200), hp(N))
+    assert N.opt_plan(descs(N, [(1024, 1024)] * 200), hp(N))[2] == 2
+    assert one_group <= two_groups < 1.05 * one_group

@@ -1,0 +1,84 @@
+"""CPU tests of the parity gates themselves: an honest float32 emulation of
+each phase passes, a planted error fails."""
+
+import numpy as np
+import torch
+
+import oracle
+from tests import contract
+
+
+def rng(s):
+    return np.random.default_rng(s)
+
+
+def _emulate_momentum_bf16(M, G, b1=0.9):
+    b1 = np.float32(b1)
+    omb = np.float32(1) - b1
+    m32 = (b1 * M.astype(np.float32) + omb * G.astype(np.float32)).astype(np.float32)
+    return torch.from_numpy(m32).to(torch.bfloat16).double().numpy()
+
+
+def test_momentum_gate_bf16_accepts_fp32_rounding_near_cancellation():
+    r = rng(0)
+    M = oracle.round_bf16(r.standard_normal((256, 256)) * 1e-3)
+    G = oracle.round_f32(r.standard_normal((256, 256)) * 1e-3)
+    idx = (r.integers(0, 256, 5), r.integers(0, 256, 5))
+    G[idx] = oracle.round_f32(-9.0 * M[idx] * (1 + 1e-6))      # b1 M + (1-b1) G ~ 0
+    dev = _emulate_momentum_bf16(M, G)
+    assert contract.gate_momentum(M, G, dev, 0.9, "bf16").ok
+    bad = dev.copy()
+    bad[10, 11] = oracle.round_bf16(bad[10, 11] * 1.03)
+    assert not contract.gate_momentum(M, G, bad, 0.9, "bf16").ok
+
+
+def test_momentum_gate_fp32():
+    r = rng(1)
+    M = oracle.round_f32(r.standard_normal((64, 64)))
+    G = oracle.round_f32(r.standard_normal((64, 64)))
+    dev = (np.float32(0.9) * M.astype(np.float32) + np.float32(0.1) * G.astype(np.float32)).astype(np.float64)
+    assert contract.gate_momentum(M, G, dev, 0.9, "f32").ok
+    dev[0, 0] += 1e-4
+    assert not contract.gate_momentum(M, G, dev, 0.9, "f32").ok
+
+
+def test_basis_gate_accepts_fp32_qr_and_rejects_permuted_columns():
+    r = rng(2)
+    M = r.standard_normal((40, 60)) * 1e-2
+    A = M.T @ M
+    X0 = np.eye(60)
+    Z = contract.one_shot_input(A, X0, 40, 1).astype(np.float32)
+    q, rr = np.linalg.qr(Z)                                      # float32 LAPACK
+    q = (q * np.where(np.diag(rr) < 0, -1, 1)).astype(np.float64)
+    assert contract.gate_basis(q, A, X0, 40, 1, "V").ok
+    bad = q.copy()
+    bad[:, [0, 1]] = bad[:, [1, 0]]
+    assert not contract.gate_basis(bad, A, X0, 40, 1, "V").ok
+    flipped = q.copy()
+    flipped[:, 2] *= -1                                          # wrong sign convention
+    assert not contract.gate_basis(flipped, A, X0, 40, 1, "V").ok
+
+
+def test_apply_gate_accepts_fp32_emulation_and_rejects_error():
+    r = rng(3)
+    m, n = 24, 40
+    hp = oracle.Hyper()
+    W = oracle.round_f32(r.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(r.random((m, n)) * 1e-6)
+    M = oracle.round_f32(r.standard_normal((m, n)) * 1e-3)
+    G = oracle.round_f32(r.standard_normal((m, n)) * 1e-3)
+    U = oracle.round_f32(np.linalg.qr(r.standard_normal((m, m)))[0])
+    V = oracle.round_f32(np.linalg.qr(r.standard_normal((n, n)))[0])
+    f = np.float32
+    U32, V32 = U.astype(f), V.astype(f)
+    Gt = U32.T @ G.astype(f) @ V32
+    mt = U32.T @ M.astype(f) @ V32
+    v32 = (f(0.999) * v.astype(f) + f(0.001) * Gt * Gt).astype(f)
+    u = mt / (np.sqrt(v32) + f(1e-8))
+    W32 = (W.astype(f) - f(1e-3) * (U32 @ u @ V32.T)).astype(np.float64)
+    reps = contract.gate_apply(W, v, M, G, U, V, W32, v32.astype(np.float64), hp, "f32")
+    assert all(x.ok for x in reps), [str(x) for x in reps]
+    bad = W32.copy()
+    bad[5, 6] += 3e-4 * np.max(np.abs(W))
+    reps = contract.gate_apply(W, v, M, G, U, V, bad, v32.astype(np.float64), hp, "f32")
+    assert not all(x.ok for x in reps)
