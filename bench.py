@@ -110,6 +110,9 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-s", type=float, default=30.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-phase HIP events")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this many MiB first (a dispatch of known size "
+                         "for scaling hardware byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -129,6 +132,16 @@ def main(argv=None):
     params = sum(m * n for m, n in shapes)
     print(f"[bench] workload {wl.key}: {len(shapes)} matrices, {params / 1e9:.3f} G params, "
           f"M {wl.m_dtype}, K={wl.K}, p={wl.power_iters}", flush=True)
+
+    if args.calibrate_copy_mib > 0:
+        nel = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.randn(nel, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done", flush=True)
+        del src, dst
 
     states = []
     for i, s in enumerate(wl.matrices):

@@ -144,8 +144,10 @@ enum {
 /* enable != 0 starts recording (and clears the totals); 0 stops. */
 opt_status opt_group_set_timing(opt_group_t g, int32_t enable);
 /* Synchronises with the last recorded event, then writes for each phase the
- * summed milliseconds and the number of launches recorded since timing was
- * enabled (arrays of OPT_NUM_PHASES entries; either may be NULL). */
+ * summed milliseconds and the number of kernels launched in the timed scopes
+ * since timing was enabled (arrays of OPT_NUM_PHASES entries; either may be
+ * NULL). Every scope counts its grouped GEMM and elementwise launches; the
+ * refresh scope counts only its Gram-product GEMMs, not its many QR kernels. */
 opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches);
 
 void opt_group_destroy(opt_group_t g);   /* NULL is ignored; does not synchronise */

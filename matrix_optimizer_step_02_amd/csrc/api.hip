@@ -126,7 +126,13 @@ struct opt_group_s {
     bool timing = false;
     std::vector<hipEvent_t> pool;
     size_t pool_used = 0;
-    std::vector<std::pair<int, std::pair<hipEvent_t, hipEvent_t>>> recs;
+    struct Rec {
+        int phase;
+        hipEvent_t b, e;
+        int kernels;
+    };
+    std::vector<Rec> recs;
+    int kernels_in_scope = 0;   // kernels launched since the current phase scope opened
 };
 
 namespace {
@@ -448,12 +454,16 @@ hipEvent_t next_event(opt_group_s* g) {
     return g->pool[g->pool_used++];
 }
 
+// Events recorded on the step's stream around every launch sequence of a
+// phase; `kernels` counts the kernels the scope launched (a phase may need
+// one launch per operand variant), so per-launch averages can be formed.
 struct PhaseScope {
     opt_group_s* g;
     int phase;
     hipStream_t s;
     hipEvent_t b = nullptr;
     PhaseScope(opt_group_s* g_, int ph, hipStream_t s_) : g(g_), phase(ph), s(s_) {
+        g->kernels_in_scope = 0;
         if (g->timing) {
             b = next_event(g);
             if (b) (void)hipEventRecord(b, s);
@@ -464,18 +474,19 @@ struct PhaseScope {
             hipEvent_t e = next_event(g);
             if (e) {
                 (void)hipEventRecord(e, s);
-                g->recs.push_back({phase, {b, e}});
+                g->recs.push_back({phase, b, e, g->kernels_in_scope});
             }
         }
     }
 };
 
-hipError_t run_gemm(const opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alpha_scale,
+hipError_t run_gemm(opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alpha_scale,
                     hipStream_t s) {
     for (const GemmLaunch& L : Ls) {
         hipError_t e = launch_gemm_grouped(L.variant, dptr<GemmProb>(g, L.probs), dptr<int32_t>(g, L.tb),
                                            L.nprob, L.total_tiles, alpha_scale, s);
         if (e != hipSuccess) return e;
+        g->kernels_in_scope += 1;
     }
     return hipSuccess;
 }
@@ -650,6 +661,7 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
             e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
             if (e) return hip_fail(e, "momentum launch");
+            g->kernels_in_scope += G.mom.nseg > 0;
         }
         if (refresh && (e = run_refresh(g, G, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
         {
@@ -665,6 +677,7 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             e = launch_rotated_adam(dptr<EwSeg>(g, G.adam.segs), G.adam.nseg, G.adam.chunks, g->hp.beta2,
                                     g->hp.eps, s);
             if (e) return hip_fail(e, "rotated Adam launch");
+            g->kernels_in_scope += G.adam.nseg > 0;
         }
         {
             PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
@@ -723,14 +736,14 @@ opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
     double acc[OPT_NUM_PHASES] = {0};
     int64_t cnt[OPT_NUM_PHASES] = {0};
     if (!g->recs.empty()) {
-        hipError_t e = hipEventSynchronize(g->recs.back().second.second);
+        hipError_t e = hipEventSynchronize(g->recs.back().e);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
         for (auto& r : g->recs) {
             float t = 0.f;
-            e = hipEventElapsedTime(&t, r.second.first, r.second.second);
+            e = hipEventElapsedTime(&t, r.b, r.e);
             if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-            acc[r.first] += t;
-            cnt[r.first] += 1;
+            acc[r.phase] += t;
+            cnt[r.phase] += r.kernels;
         }
     }
     for (int i = 0; i < OPT_NUM_PHASES; ++i) {
