@@ -28,7 +28,10 @@
  * the cost m*n*(m+n), each group's fp32 gradient payload sum(4 m n) capped by
  * capacity_bytes (Canzona page, section 3.2.2 micro-group scheduling, section
  * 6.1: 512 MB-class groups). One step runs the groups one after another on the
- * caller's stream, each phase of a group as one grouped launch.
+ * caller's stream, each phase of a group as one grouped launch. A refresh is
+ * batched separately, over as many matrices as refresh_capacity_bytes of QR
+ * scratch allows, since its latency-bound QR panels need many matrices in
+ * flight to fill the GPU.
  *
  * Conventions for every call:
  *  - All matrices are dense row-major with row stride equal to their column
@@ -89,6 +92,9 @@ typedef struct {
     int32_t K;                /* refresh period in steps; 0 = no automatic refresh */
     int32_t power_iters;      /* orthogonal-iteration passes per refresh, >= 1 */
     uint64_t capacity_bytes;  /* micro-group cap on sum(4 m n); 0 selects 1 << 29 (512 MiB) */
+    uint64_t refresh_capacity_bytes; /* cap on the refresh scratch of one refresh batch (the
+                                        d x d QR inputs and their scratch); 0 selects 16 GiB.
+                                        A matrix larger than the cap forms a batch alone. */
     uint32_t flags;           /* reserved, must be 0 */
 } opt_hparams;
 

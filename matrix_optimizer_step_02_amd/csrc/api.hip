@@ -80,6 +80,7 @@ struct QrBatch {
     int njobs = 0;
     uint64_t jobs = 0;
     std::vector<int> np;   // panels per job, descending
+    std::vector<int> d;    // order per job, descending
     int max_d = 0;
 };
 struct CopyLaunch {
@@ -92,10 +93,16 @@ struct Group {
     std::vector<int> mats;   // indices into opt_group_s::mats, LPT order
     EwLaunch mom, adam;
     std::vector<GemmLaunch> rot_left, rot_right, back_left, back_right;
+    uint64_t rot_bytes = 0;
+};
+
+// Matrices refreshed together: Gram products, completion copies, QR jobs.
+struct RefreshBatch {
+    std::vector<int> mats;
     std::vector<GemmLaunch> prod1, prod2;
     CopyLaunch comp;
     QrBatch qr;
-    uint64_t rot_bytes = 0, ref_bytes = 0;
+    uint64_t ref_bytes = 0;
 };
 
 // Append-only image of device tables with 256-byte aligned entries.
@@ -117,6 +124,7 @@ struct opt_group_s {
     opt_hparams hp{};
     int64_t t = 0;
     std::vector<Group> groups;
+    std::vector<RefreshBatch> rbatches;
     char* ws = nullptr;
     uint64_t ws_bytes = 0;
     Image img;
@@ -153,6 +161,10 @@ opt_status check_hparams(const opt_hparams* hp) {
 
 uint64_t capacity_of(const opt_hparams* hp) {
     return hp->capacity_bytes ? hp->capacity_bytes : (1ull << 29);
+}
+
+uint64_t refresh_capacity_of(const opt_hparams* hp) {
+    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : (16ull << 30);
 }
 
 struct Span {
@@ -326,10 +338,39 @@ QrBytes qr_job_bytes(int64_t d) {
     return b;
 }
 
+// Refresh scratch of one matrix: Gram products B1U (n x r), B1V (m x r), the
+// QR inputs ZU (m x m), ZV (n x n) and the QR scratch of both orders.
+uint64_t refresh_bytes(int64_t m, int64_t n) {
+    const int64_t r = std::min(m, n);
+    QrBytes bu = qr_job_bytes(m), bv = qr_job_bytes(n);
+    return align_up(4ull * n * r) + align_up(4ull * m * r) + bu.Z + bv.Z + bu.T + bu.part + bu.W2 + bv.T +
+           bv.part + bv.W2;
+}
+
+// Refresh batches: matrices in LPT order, next-fit under the refresh cap (a
+// matrix above the cap forms a batch of its own).
+std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vector<std::vector<int>>& plan) {
+    const uint64_t cap = refresh_capacity_of(&g->hp);
+    std::vector<std::vector<int>> out;
+    uint64_t used = 0;
+    for (const std::vector<int>& members : plan)
+        for (int mi : members) {
+            const uint64_t b = refresh_bytes(g->mats[mi].d.m, g->mats[mi].d.n);
+            if (out.empty() || (used + b > cap && !out.back().empty())) {
+                out.emplace_back();
+                used = 0;
+            }
+            out.back().push_back(mi);
+            used += b;
+        }
+    return out;
+}
+
 // Build every table of the group object. `scratch` is the device address of
 // the scratch region (any value when only sizes are wanted).
 void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scratch) {
     g->groups.clear();
+    g->rbatches.clear();
     g->img.bytes.clear();
     g->scratch_bytes = 0;
     for (const std::vector<int>& members : plan) {
@@ -379,9 +420,14 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         G.back_right = put_gemm(g->img, br);
         G.mom = put_ew(g->img, mom);
         G.adam = put_ew(g->img, adam);
+        g->scratch_bytes = std::max(g->scratch_bytes, G.rot_bytes);
+        g->groups.push_back(std::move(G));
+    }
 
-        // ---- refresh scratch
-        off = 0;
+    for (const std::vector<int>& members : plan_refresh(g, plan)) {
+        RefreshBatch R;
+        R.mats = members;
+        uint64_t off = 0;
         std::vector<PGemm> p1, p2;
         std::vector<CopyJob> comp;
         struct JobSrc { int64_t d; float* Z; float* X; };
@@ -409,31 +455,32 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         }
         std::stable_sort(jsrc.begin(), jsrc.end(), [](const JobSrc& a, const JobSrc& b) { return a.d > b.d; });
         std::vector<QrJob> jobs;
-        for (const JobSrc& s : jsrc) {
-            QrBytes b = qr_job_bytes(s.d);
+        for (const JobSrc& js : jsrc) {
+            QrBytes b = qr_job_bytes(js.d);
             QrJob j{};
-            j.Z = s.Z;
-            j.X = s.X;
-            j.d = (int32_t)s.d;
-            j.np = panels((int)s.d);
+            j.Z = js.Z;
+            j.X = js.X;
+            j.d = (int32_t)js.d;
+            j.np = panels((int)js.d);
             j.T = (float*)(scratch + off); off += b.T;
             j.part = (float*)(scratch + off); off += b.part;
             j.W2 = (float*)(scratch + off); off += b.W2;
             jobs.push_back(j);
-            G.qr.np.push_back(j.np);
+            R.qr.np.push_back(j.np);
+            R.qr.d.push_back(j.d);
         }
-        G.ref_bytes = off;
-        G.prod1 = put_gemm(g->img, p1);
-        G.prod2 = put_gemm(g->img, p2);
-        G.comp.n = (int)comp.size();
-        G.comp.max_d = 0;
-        for (const CopyJob& c : comp) G.comp.max_d = std::max(G.comp.max_d, (int)c.d);
-        G.comp.jobs = g->img.put(comp);
-        G.qr.njobs = (int)jobs.size();
-        G.qr.max_d = jobs.empty() ? 0 : jobs[0].d;
-        G.qr.jobs = g->img.put(jobs);
-        g->scratch_bytes = std::max(g->scratch_bytes, std::max(G.rot_bytes, G.ref_bytes));
-        g->groups.push_back(std::move(G));
+        R.ref_bytes = off;
+        R.prod1 = put_gemm(g->img, p1);
+        R.prod2 = put_gemm(g->img, p2);
+        R.comp.n = (int)comp.size();
+        R.comp.max_d = 0;
+        for (const CopyJob& c : comp) R.comp.max_d = std::max(R.comp.max_d, (int)c.d);
+        R.comp.jobs = g->img.put(comp);
+        R.qr.njobs = (int)jobs.size();
+        R.qr.max_d = jobs.empty() ? 0 : jobs[0].d;
+        R.qr.jobs = g->img.put(jobs);
+        g->scratch_bytes = std::max(g->scratch_bytes, R.ref_bytes);
+        g->rbatches.push_back(std::move(R));
     }
     g->table_bytes = align_up(g->img.bytes.size());
 }
@@ -491,10 +538,33 @@ hipError_t run_gemm(opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alp
     return hipSuccess;
 }
 
-hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, int max_d, hipStream_t s) {
+// Runs of equal order among the jobs still active at panel p, in chunks of
+// at most kQrMaxClasses (one launch per chunk).
+std::vector<QrClasses> active_classes(const std::vector<int>& d, int p) {
+    std::vector<QrClasses> out;
+    QrClasses cur{};
+    for (size_t i = 0; i < d.size();) {
+        if (d[i] <= p * kQrPB) break;
+        size_t j = i;
+        while (j < d.size() && d[j] == d[i]) ++j;
+        if (cur.n == kQrMaxClasses) {
+            out.push_back(cur);
+            cur = QrClasses{};
+        }
+        cur.d[cur.n] = d[i];
+        cur.first[cur.n] = (int32_t)i;
+        cur.count[cur.n] = (int32_t)(j - i);
+        cur.n += 1;
+        i = j;
+    }
+    if (cur.n) out.push_back(cur);
+    return out;
+}
+
+hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vector<int>& d, hipStream_t s) {
     const int njobs = (int)np.size();
     if (njobs == 0) return hipSuccess;
-    const int maxp = np[0];
+    const int maxp = np[0], max_d = d[0];
     hipError_t e;
     auto active = [&](int p) {
         int a = 0;
@@ -502,30 +572,32 @@ hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, int max_d, hipS
         return a;
     };
     for (int p = 0; p < maxp; ++p) {
-        const int na = active(p);
-        if ((e = launch_qr_panel(jobs, na, p, s))) return e;
-        if ((e = launch_qr_dots(jobs, na, p, max_d, 0, s))) return e;
-        if ((e = launch_qr_reduce(jobs, na, p, max_d, 0, s))) return e;
-        if ((e = launch_qr_update(jobs, na, p, max_d, 0, s))) return e;
+        if ((e = launch_qr_panel(jobs, active(p), p, max_d, s))) return e;
+        for (const QrClasses& C : active_classes(d, p)) {
+            if ((e = launch_qr_dots(jobs, C, p, 0, s))) return e;
+            if ((e = launch_qr_reduce(jobs, C, p, 0, s))) return e;
+            if ((e = launch_qr_update(jobs, C, p, 0, s))) return e;
+        }
     }
     if ((e = launch_qr_init_q(jobs, njobs, max_d, s))) return e;
     for (int p = maxp - 1; p >= 0; --p) {
-        const int na = active(p);
-        if ((e = launch_qr_dots(jobs, na, p, max_d, 1, s))) return e;
-        if ((e = launch_qr_reduce(jobs, na, p, max_d, 1, s))) return e;
-        if ((e = launch_qr_update(jobs, na, p, max_d, 1, s))) return e;
+        for (const QrClasses& C : active_classes(d, p)) {
+            if ((e = launch_qr_dots(jobs, C, p, 1, s))) return e;
+            if ((e = launch_qr_reduce(jobs, C, p, 1, s))) return e;
+            if ((e = launch_qr_update(jobs, C, p, 1, s))) return e;
+        }
     }
     return hipSuccess;
 }
 
-hipError_t run_refresh(opt_group_s* g, const Group& G, int power_iters, hipStream_t s) {
+hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, hipStream_t s) {
     PhaseScope ps(g, OPT_PHASE_REFRESH, s);
     hipError_t e;
     for (int it = 0; it < power_iters; ++it) {
         if ((e = run_gemm(g, G.prod1, 1.f, s))) return e;
         if ((e = run_gemm(g, G.prod2, 1.f, s))) return e;
         if ((e = launch_copy_cols(dptr<CopyJob>(g, G.comp.jobs), G.comp.n, G.comp.max_d, s))) return e;
-        if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.max_d, s))) return e;
+        if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.d, s))) return e;
     }
     return hipSuccess;
 }
@@ -577,6 +649,7 @@ opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
     std::vector<std::vector<int>> plan;
     plan_groups(descs, count, hp, ord, plan);
     opt_group_s tmp;
+    tmp.hp = *hp;
     for (int i = 0; i < count; ++i) {
         Mat M{descs[i], i, 0.0, descs[i].M_dtype == OPT_BF16};
         tmp.mats.push_back(M);
@@ -656,14 +729,17 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     g->t += 1;
     const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
+    // Momentum of every group first: a refresh must see the updated M.
     for (const Group& G : g->groups) {
-        {
-            PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
-            e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
-            if (e) return hip_fail(e, "momentum launch");
-            g->kernels_in_scope += G.mom.nseg > 0;
-        }
-        if (refresh && (e = run_refresh(g, G, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+        PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+        e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
+        if (e) return hip_fail(e, "momentum launch");
+        g->kernels_in_scope += G.mom.nseg > 0;
+    }
+    if (refresh)
+        for (const RefreshBatch& R : g->rbatches)
+            if ((e = run_refresh(g, R, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+    for (const Group& G : g->groups) {
         {
             PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
             if ((e = run_gemm(g, G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");
@@ -697,8 +773,8 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
     if (power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
-    for (const Group& G : g->groups)
-        if ((e = run_refresh(g, G, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
+    for (const RefreshBatch& R : g->rbatches)
+        if ((e = run_refresh(g, R, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
     return OPT_OK;
 }
 
@@ -827,7 +903,7 @@ extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* wo
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before orthonormalize");
     hipLaunchKernelGGL(put_job_kernel, dim3(1), dim3(1), 0, s, (QrJob*)w, j);
     if ((e = hipGetLastError())) return hip_fail(e, "job upload");
-    std::vector<int> np{j.np};
-    if ((e = run_qr((const QrJob*)w, np, (int)d, s))) return hip_fail(e, "QR launch");
+    std::vector<int> np{j.np}, dd{(int)d};
+    if ((e = run_qr((const QrJob*)w, np, dd, s))) return hip_fail(e, "QR launch");
     return OPT_OK;
 }

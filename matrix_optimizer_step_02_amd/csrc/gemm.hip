@@ -206,6 +206,24 @@ __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int w
     }
 }
 
+// Old values of the C fragment a lane updates (beta != 0), in accumulator
+// order. All loads are issued before any store to C.
+__device__ __forceinline__ void load_c_fragment(const GemmProb& p, int m0, int n0, int wm, int wn, int lane,
+                                                float (&cold)[2][2][16]) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                cold[i][j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+            }
+        }
+}
+
 template <bool AT, bool BT, bool ABF, bool BBF, bool UL>
 __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
                                           float* smem) {
@@ -225,6 +243,8 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    float cold[2][2][16];
 
     const int nk = (p.K + BK - 1) / BK;
     f32x4 ra[4], rb[4];
@@ -252,8 +272,12 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
 
     // Epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
     // column l%32 of its 32x32 block: 32 lanes store 128 contiguous bytes.
+    // With beta != 0 every old value of the fragment is loaded before the
+    // first store, so the loads overlap (a store to C could otherwise alias a
+    // later load as far as the compiler can tell, serialising them).
     const float alpha = p.alpha * alpha_scale, beta = p.beta;
     const int h = lane >> 5, l32 = lane & 31;
+    if (beta != 0.f) load_c_fragment(p, m0, n0, wm, wn, lane, cold);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -264,11 +288,68 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < p.M) {
-                    float* c = p.C + (int64_t)row * p.ldc + col;
                     float val = alpha * acc[i][j][r];
-                    if (beta != 0.f) val += beta * *c;
-                    *c = val;
+                    if (beta != 0.f) val += beta * cold[i][j][r];
+                    p.C[(int64_t)row * p.ldc + col] = val;
                 }
+            }
+        }
+}
+
+// C += alpha op(A) op(B) for K <= 2 BK (the QR trailing updates, K = the
+// panel width): both K slabs go to the two LDS buffers at once, then the old
+// C fragment is requested so that its latency overlaps the MFMAs; the
+// operand staging registers are dead by then. A is not transposed, B is
+// stored K x N, both fp32.
+static_assert(kQrPB <= 2 * kGemmBK, "the QR update tile holds the whole panel width in two LDS slabs");
+
+template <bool UL>
+__device__ __forceinline__ void gemm_tile_short_k(const GemmProb& p, int tm, int tn, float* smem) {
+    constexpr int AS = ALayout<false>::size, BS = BLayout<false>::size;
+    float* As0 = smem;
+    float* As1 = smem + AS;
+    float* Bs0 = smem + 2 * AS;
+    float* Bs1 = smem + 2 * AS + BS;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (p.K + BK - 1) / BK;
+    {
+        f32x4 ra[4], rb[4];
+        load_a<false, false, UL>(p, m0, 0, ra);
+        load_b<false, false>(p, n0, 0, rb);
+        store_a<false>(As0, ra);
+        store_b<false>(Bs0, rb);
+        if (nk > 1) {
+            load_a<false, false, UL>(p, m0, BK, ra);
+            load_b<false, false>(p, n0, BK, rb);
+            store_a<false>(As1, ra);
+            store_b<false>(Bs1, rb);
+        }
+    }
+    __syncthreads();
+    float cold[2][2][16];
+    load_c_fragment(p, m0, n0, wm, wn, lane, cold);
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    mma_slab<false, false>(As0, Bs0, wm, wn, lane, acc);
+    if (nk > 1) mma_slab<false, false>(As1, Bs1, wm, wn, lane, acc);
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + l32;
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < p.M) p.C[(int64_t)row * p.ldc + col] = p.alpha * acc[i][j][r] + p.beta * cold[i][j][r];
             }
         }
 }
@@ -350,16 +431,16 @@ hipError_t single(const GemmProb& p, hipStream_t s) {
 //
 // Factorisation (q_mode 0) at panel p: C = Z[k:, k+jb:], Y = Z[k:, k:k+jb].
 // Q formation (q_mode 1): C = X[k:, k:]. W2 (jb x N') comes from qr_reduce.
-__global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restrict__ jobs, int p,
-                                                        int q_mode) {
+__global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restrict__ jobs, QrClasses C,
+                                                        int p, int q_mode) {
     __shared__ __attribute__((aligned(16))) float smem[smem_floats<false, false>()];
-    const QrJob J = jobs[blockIdx.y];
+    int job, local;
+    if (!qr_locate(C, QG_UPDATE, p, q_mode, blockIdx.x, job, local)) return;
+    const QrJob J = jobs[job];
     const int k = p * kQrPB;
-    if (k >= J.d) return;
     const int jb = min(kQrPB, J.d - k);
     const int L = J.d - k;
     const int ncols = q_mode ? L : L - jb;
-    if (ncols <= 0) return;
     GemmProb g;
     g.A = J.Z + (int64_t)k * J.d + k;
     g.B = J.W2;
@@ -375,21 +456,15 @@ __global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restric
     g.beta = 1.f;
     g.tiles_m = (L + BM - 1) / BM;
     g.tiles_n = (ncols + BN - 1) / BN;
-    const int total = g.tiles_m * g.tiles_n;
-    if ((int)blockIdx.x >= total) return;
     int tm, tn;
-    raster(xcd_remap(blockIdx.x, total), g.tiles_m, g.tiles_n, tm, tn);
-    gemm_tile<false, false, false, false, true>(g, tm, tn, 1.f, smem);
+    raster(local, g.tiles_m, g.tiles_n, tm, tn);
+    gemm_tile_short_k<true>(g, tm, tn, smem);
 }
 
-hipError_t launch_qr_update(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                            hipStream_t s) {
-    if (njobs <= 0) return hipSuccess;
-    const int k = p * kQrPB;
-    const int L = max_d - k;
-    if (L <= 0) return hipSuccess;
-    const int tiles = ((L + BM - 1) / BM) * ((L + BN - 1) / BN);
-    qr_update_kernel<<<dim3(tiles, njobs), dim3(NT), 0, s>>>(jobs, p, q_mode);
+hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_UPDATE, p, q_mode);
+    if (blocks <= 0) return hipSuccess;
+    qr_update_kernel<<<dim3(blocks), dim3(NT), 0, s>>>(jobs, C, p, q_mode);
     return hipGetLastError();
 }
 

@@ -69,7 +69,7 @@ hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks
 
 // ------------------------------------------------------------------ QR ----
 
-constexpr int kQrPB = 32;          // panel width (reflectors per compact-WY block)
+constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY block)
 constexpr int kQrMaxSplits = 16;   // row splits of the reflector-transpose products
 constexpr int kQrPanelThreads = 512;
 
@@ -87,15 +87,27 @@ struct QrJob {
 };
 
 // Jobs are sorted by d descending, so the jobs still active at panel p are a
-// prefix of the array; `njobs` passed to each launch is that prefix length,
-// `max_d` the d of job 0.
-hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, hipStream_t s);
-hipError_t launch_qr_dots(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                          hipStream_t s);
-hipError_t launch_qr_reduce(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                            hipStream_t s);
-hipError_t launch_qr_update(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                            hipStream_t s);
+// prefix of the array; `njobs` passed to the panel launch is that prefix
+// length, `max_d` the d of job 0. The other per-panel launches take the runs
+// of equal d ("classes") by value, so that their grids cover exactly the
+// blocks that exist: a grid sized for the largest job times the job count
+// would dispatch mostly empty workgroups.
+constexpr int kQrMaxClasses = 16;
+struct QrClasses {
+    int32_t n;
+    int32_t d[kQrMaxClasses];
+    int32_t first[kQrMaxClasses];   // index of the class's first job
+    int32_t count[kQrMaxClasses];
+};
+enum QrGridKind { QG_DOTS = 0, QG_REDUCE = 1, QG_UPDATE = 2 };
+
+__host__ __device__ inline int qr_splits(int rows);
+__host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p, int q_mode);
+
+hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s);
+hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
+hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
+hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
 hipError_t launch_qr_init_q(const QrJob* jobs, int njobs, int max_d, hipStream_t s);
 
 // Strided copy of columns [c0, d) of X into Z (both d x d, row stride d):
@@ -116,6 +128,43 @@ __host__ __device__ inline int qr_splits(int rows) {
 __host__ __device__ inline int qr_chunk(int rows, int splits) {
     int c = (rows + splits - 1) / splits;
     return (c + 1) & ~1;
+}
+
+// Blocks one job contributes to a per-panel launch: reflector-transpose
+// products (512 columns x one row split per block), their reduction (256
+// columns per block) and the trailing update (128 x 128 tiles).
+__host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p, int q_mode) {
+    const int k = p * kQrPB;
+    if (k >= d) return 0;
+    const int L = d - k;
+    const int jb = L < kQrPB ? L : kQrPB;
+    const int ncols = q_mode ? L : L - jb;
+    if (ncols <= 0) return 0;
+    if (kind == QG_DOTS) return ((ncols + 511) / 512) * qr_splits(L);
+    if (kind == QG_REDUCE) return (ncols + 255) / 256;
+    return ((L + kGemmBM - 1) / kGemmBM) * ((ncols + kGemmBN - 1) / kGemmBN);
+}
+
+__host__ __device__ inline int qr_total_blocks(const QrClasses& C, int kind, int p, int q_mode) {
+    int t = 0;
+    for (int c = 0; c < C.n; ++c) t += qr_blocks_per_job(kind, C.d[c], p, q_mode) * C.count[c];
+    return t;
+}
+
+// Block id -> (job, block within the job); false for no such block.
+__host__ __device__ inline bool qr_locate(const QrClasses& C, int kind, int p, int q_mode, int bid,
+                                          int& job, int& local) {
+    for (int c = 0; c < C.n; ++c) {
+        const int per = qr_blocks_per_job(kind, C.d[c], p, q_mode);
+        const int tot = per * C.count[c];
+        if (bid < tot) {
+            job = C.first[c] + bid / per;
+            local = bid % per;
+            return true;
+        }
+        bid -= tot;
+    }
+    return false;
 }
 
 }  // namespace matopt

@@ -6,14 +6,12 @@
 // reflections keep Q orthonormal to working precision regardless of the
 // conditioning of Z, which Cholesky- or Gram-Schmidt-based schemes do not.
 //
-// Factorisation, panel by panel (width PB = 32), right-looking:
+// Factorisation, panel by panel (width PB = 64), right-looking:
 //   1. qr_panel   one 512-thread workgroup per matrix factorises the L x PB
-//                 panel column by column (two passes over the panel rows per
-//                 column, two block reductions), stores the reflectors below
-//                 the diagonal of Z, R on and above it, and builds the
-//                 upper-triangular T of the compact WY form
-//                 H_0 ... H_{jb-1} = I - Y T Y^T by the forward recurrence
-//                 T[:j, j] = -tau_j T[:j, :j] (Y[:, :j]^T v_j).
+//                 panel in register-resident sub-panels (see below), stores
+//                 the reflectors below the diagonal of Z, R on and above it,
+//                 and the upper-triangular T of the compact WY form
+//                 H_0 ... H_{jb-1} = I - Y T Y^T.
 //   2. qr_dots    W = Y^T C for the trailing block C, split over rows into
 //                 partial sums (fp32 MFMA 32x32x2 straight from global memory:
 //                 both operands are read along their contiguous dimension).
@@ -39,141 +37,116 @@ constexpr int PB = kQrPB;
 constexpr int PT = kQrPanelThreads;
 constexpr int NW = PT / 64;
 
+// ---- panel factorisation -------------------------------------------------
+//
+// One 512-thread workgroup factorises the L x jb panel (jb <= PB) of one
+// matrix. Thread t owns panel rows i = t + 512 r (r < R). The panel is
+// processed in sub-panels of SB columns held entirely in registers
+// (a[r][c]); a sub-panel is first brought up to date with the reflectors of
+// the earlier sub-panels of this panel (left-looking, one SB-wide compact-WY
+// block at a time: A -= Y_q (T_q^T (Y_q^T A)), Y_q streamed from memory),
+// then factorised column by column without touching memory: per column one
+// block reduction for the norm below the diagonal and one for the inner
+// products of the new reflector with the other columns of the sub-panel
+// (trailing columns: update weights; leading columns: entries of T_q).
+// Finally the panel's reflectors are read back once to form their Gram
+// matrix S = Y^T Y with fp32 MFMA, and T of the whole panel follows row by
+// row from T[c][j] = -tau_j sum_{c<=l<j} T[c][l] S[l][j] (each row depends
+// only on itself, so the PB rows need no synchronisation).
+
+constexpr int SLOT = 64;  // values per wavefront in a reduction slot
+
 struct PanelShared {
-    float red[NW][PB];
-    float w[PB];
-    float T[PB][PB + 1];
-    float rsig[NW];
+    float red[2][NW][SLOT];
+    float Tq[PB][PB + 1];    // sub-panel T blocks on the diagonal (panel-relative indices)
+    float P[SLOT];
+    float P2[SLOT];
+    float tau[PB];
     float alpha;
+    float S[PB][PB + 1];     // Gram matrix of the panel's reflectors
+    union {
+        float gram[NW][32][33];  // per-wavefront partial Gram blocks
+        float Tf[PB][PB + 1];    // T of the whole panel
+    };
 };
+
+// Reduce-scatter of N (power of two, <= 64) values over a wavefront: after
+// log2(N) halving exchanges and a butterfly over the remaining lane bits,
+// lane l holds the wave sum of value index l >> (6 - log2 N).
+template <int N>
+__device__ __forceinline__ float rs_reduce(float (&v)[N], int lane, int mask) {
+    if constexpr (N == 1) {
+        float x = v[0];
+        for (int m = mask; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+        return x;
+    } else {
+        float h[N / 2];
+        const bool hi = lane & mask;
+#pragma unroll
+        for (int c = 0; c < N / 2; ++c) {
+            const float keep = hi ? v[N / 2 + c] : v[c];
+            const float give = hi ? v[c] : v[N / 2 + c];
+            h[c] = keep + __shfl_xor(give, mask, 64);
+        }
+        return rs_reduce<N / 2>(h, lane, mask >> 1);
+    }
+}
+
+template <int N>
+constexpr int ilog2() {
+    return N <= 1 ? 0 : 1 + ilog2<N / 2>();
+}
+
+// Block sum of N values per thread into sh.red[slot][*][0..N): afterwards
+// value c of the block is sum_w sh.red[slot][w][c]. One barrier.
+template <int N>
+__device__ __forceinline__ void block_partial(float (&v)[N], PanelShared& sh, int slot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float x = rs_reduce<N>(v, lane, 32);
+    constexpr int shift = 6 - ilog2<N>();
+    if ((lane & ((1 << shift) - 1)) == 0) sh.red[slot][wave][lane >> shift] = x;
+    __syncthreads();
+}
+
+__device__ __forceinline__ float block_value(const PanelShared& sh, int slot, int c) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += sh.red[slot][w][c];
+    return s;
+}
 
 struct PanelCtx {
-    float* A;      // top-left of the panel (row k, column k of Z)
+    float* A;     // top-left of the panel (row k, column k of Z)
     int64_t ld;
-    int L;         // rows of the panel
-    int jb;        // columns of the panel
-    bool vec;      // full-width panel with 16-byte aligned rows
+    int L;        // rows of the panel
+    int jb;       // columns of the panel
 };
 
-__device__ __forceinline__ void load_row(const PanelCtx& c, int i, float (&a)[PB]) {
-    const float* p = c.A + (int64_t)i * c.ld;
-    if (c.vec) {
-#pragma unroll
-        for (int q = 0; q < PB / 4; ++q) {
-            const f32x4 t = *(const f32x4*)(p + 4 * q);
-            a[4 * q + 0] = t[0];
-            a[4 * q + 1] = t[1];
-            a[4 * q + 2] = t[2];
-            a[4 * q + 3] = t[3];
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < PB; ++q) a[q] = q < c.jb ? p[q] : 0.f;
-    }
+// Reflector entry Y[i][c] (panel-relative): 0 above the diagonal, 1 on it.
+__device__ __forceinline__ float yval(const PanelCtx& c, int i, int col) {
+    if (i < col) return 0.f;
+    if (i == col) return 1.f;
+    return c.A[(int64_t)i * c.ld + col];
 }
 
-__device__ __forceinline__ void store_row(const PanelCtx& c, int i, const float (&a)[PB]) {
-    float* p = c.A + (int64_t)i * c.ld;
-    if (c.vec) {
-#pragma unroll
-        for (int q = 0; q < PB / 4; ++q) {
-            f32x4 t;
-            t[0] = a[4 * q + 0];
-            t[1] = a[4 * q + 1];
-            t[2] = a[4 * q + 2];
-            t[3] = a[4 * q + 3];
-            *(f32x4*)(p + 4 * q) = t;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < PB; ++q)
-            if (q < c.jb) p[q] = a[q];
-    }
-}
+template <int R, int SB>
+struct SubPanel {
+    float a[R][SB];
+    int c0;    // first panel column of the sub-panel
+    int sbw;   // its width (< SB only in a ragged last panel)
+};
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
-
-// Sum 32 per-thread values over the workgroup into sh.w[0..31].
-// Within a wavefront this is a reduce-scatter: at each of five exchange steps
-// a lane keeps one half of its remaining values (the upper half when its
-// partner bit is set) and adds the partner's copy of that half, so after
-// 16+8+4+2+1 shuffles lane l holds the sum over its 32 partner lanes of
-// value (l >> 1) & 31; one more exchange with lane l^1 completes the sum.
-__device__ __forceinline__ void block_sum32(float (&v)[PB], PanelShared& sh) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float r16[16];
-    {
-        const bool hi = lane & 32;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            const float keep = hi ? v[16 + c] : v[c];
-            const float give = hi ? v[c] : v[16 + c];
-            r16[c] = keep + __shfl_xor(give, 32, 64);
-        }
-    }
-    float r8[8];
-    {
-        const bool hi = lane & 16;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const float keep = hi ? r16[8 + c] : r16[c];
-            const float give = hi ? r16[c] : r16[8 + c];
-            r8[c] = keep + __shfl_xor(give, 16, 64);
-        }
-    }
-    float r4[4];
-    {
-        const bool hi = lane & 8;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float keep = hi ? r8[4 + c] : r8[c];
-            const float give = hi ? r8[c] : r8[4 + c];
-            r4[c] = keep + __shfl_xor(give, 8, 64);
-        }
-    }
-    float r2[2];
-    {
-        const bool hi = lane & 4;
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const float keep = hi ? r4[2 + c] : r4[c];
-            const float give = hi ? r4[c] : r4[2 + c];
-            r2[c] = keep + __shfl_xor(give, 4, 64);
-        }
-    }
-    float r1;
-    {
-        const bool hi = lane & 2;
-        const float keep = hi ? r2[1] : r2[0];
-        const float give = hi ? r2[0] : r2[1];
-        r1 = keep + __shfl_xor(give, 2, 64);
-    }
-    r1 += __shfl_xor(r1, 1, 64);
-    if ((lane & 1) == 0) sh.red[wave][(lane >> 1) & 31] = r1;
-    __syncthreads();
-    if (threadIdx.x < PB) {
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) s += sh.red[w][threadIdx.x];
-        sh.w[threadIdx.x] = s;
-    }
-    __syncthreads();
-}
-
-// Column J of the panel (J is a compile-time constant so that every register
-// array index below is static).
-template <int J>
-__device__ __forceinline__ void column_step(const PanelCtx& c, PanelShared& sh) {
-    if (J >= c.jb) return;
+// Column J of the current sub-panel (compile-time, so that register indices
+// are static). On entry sh.alpha holds its diagonal entry and slot `slot`
+// the partial sums of its squared norm below the diagonal.
+template <int R, int SB, int J>
+__device__ __forceinline__ void column_step(const PanelCtx& c, SubPanel<R, SB>& sp, PanelShared& sh,
+                                            int& slot) {
+    if (J >= sp.sbw) return;
     const int tid = threadIdx.x;
+    const int cj = sp.c0 + J;   // panel row of this column's diagonal
 
-    float sig = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) sig += sh.rsig[w];
+    const float sig = block_value(sh, slot, 0);
     const float alpha = sh.alpha;
     float beta, tau, scale;
     if (sig == 0.f) {
@@ -187,69 +160,76 @@ __device__ __forceinline__ void column_step(const PanelCtx& c, PanelShared& sh) 
         scale = 1.f / (alpha - beta);
     }
 
-    // Pass 1: dots of v_J with every other panel column (trailing columns give
-    // the update weights, leading columns hold earlier reflectors and give the
-    // inner products needed for T).
-    float part[PB];
+    // inner products of v_J with the other sub-panel columns
+    float part[SB];
 #pragma unroll
-    for (int q = 0; q < PB; ++q) part[q] = 0.f;
-    for (int i = tid; i < c.L; i += PT) {
-        if (i < J) continue;
-        float a[PB];
-        load_row(c, i, a);
-        const float vi = (i == J) ? 1.f : a[J] * scale;
+    for (int q = 0; q < SB; ++q) part[q] = 0.f;
 #pragma unroll
-        for (int q = 0; q < PB; ++q)
-            if (q != J) part[q] += vi * a[q];
-    }
-    block_sum32(part, sh);
-
-    if (tid < J) {
-        float s = 0.f;
-        for (int l = tid; l < J; ++l) s += sh.T[tid][l] * sh.w[l];
-        sh.T[tid][J] = -tau * s;
-    } else if (tid == J) {
-        sh.T[J][J] = tau;
-    }
-
-    float tw[PB];
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + PT * r;
+        if (i < c.L && i >= cj) {
+            const float vi = (i == cj) ? 1.f : sp.a[r][J] * scale;
 #pragma unroll
-    for (int q = 0; q < PB; ++q) tw[q] = q > J ? tau * sh.w[q] : 0.f;
-
-    // Pass 2: apply H_J to the trailing columns, store v_J and beta, and
-    // accumulate the squared norm of the next column below its diagonal.
-    float sig_part = 0.f;
-    for (int i = tid; i < c.L; i += PT) {
-        if (i < J) continue;
-        float a[PB];
-        load_row(c, i, a);
-        const float vi = (i == J) ? 1.f : a[J] * scale;
-#pragma unroll
-        for (int q = J + 1; q < PB; ++q) a[q] -= vi * tw[q];
-        a[J] = (i == J) ? beta : vi;
-        store_row(c, i, a);
-        if (J + 1 < PB && J + 1 < c.jb) {
-            if (i > J + 1) sig_part += a[J + 1] * a[J + 1];
-            else if (i == J + 1) sh.alpha = a[J + 1];
+            for (int q = 0; q < SB; ++q)
+                if (q != J) part[q] += vi * sp.a[r][q];
         }
     }
-    const float ws = wave_sum(sig_part);
-    if ((tid & 63) == 0) sh.rsig[tid >> 6] = ws;
-    __syncthreads();
+    slot ^= 1;
+    block_partial<SB>(part, sh, slot);
+    float w[SB];
+#pragma unroll
+    for (int q = 0; q < SB; ++q) w[q] = (q > J) ? block_value(sh, slot, q) : 0.f;
+
+    // T of the sub-panel, column J (rows < J use the inner products of v_J
+    // with the sub-panel's earlier reflectors)
+    if (tid < J) {
+        float s = 0.f;
+        for (int l = tid; l < J; ++l) s += sh.Tq[sp.c0 + tid][sp.c0 + l] * block_value(sh, slot, l);
+        sh.Tq[sp.c0 + tid][cj] = -tau * s;
+    } else if (tid == J) {
+        sh.Tq[cj][cj] = tau;
+        sh.tau[cj] = tau;
+    }
+
+    // apply H_J, store v_J and beta, and start the next column's norm
+    float sig_part = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = tid + PT * r;
+        if (i < c.L && i >= cj) {
+            const float vi = (i == cj) ? 1.f : sp.a[r][J] * scale;
+#pragma unroll
+            for (int q = J + 1; q < SB; ++q) sp.a[r][q] -= tau * vi * w[q];
+            sp.a[r][J] = (i == cj) ? beta : vi;
+        }
+        if constexpr (J + 1 < SB) {
+            if (i < c.L) {
+                if (i > cj + 1) sig_part += sp.a[r][J + 1] * sp.a[r][J + 1];
+                else if (i == cj + 1) sh.alpha = sp.a[r][J + 1];
+            }
+        }
+    }
+    if constexpr (J + 1 < SB) {
+        float v1[1] = {sig_part};
+        slot ^= 1;
+        block_partial<1>(v1, sh, slot);
+    }
 }
 
-template <int J>
-struct Columns {
-    __device__ __forceinline__ static void run(const PanelCtx& c, PanelShared& sh) {
-        column_step<J>(c, sh);
-        Columns<J + 1>::run(c, sh);
+template <int R, int SB, int J>
+struct SubColumns {
+    __device__ __forceinline__ static void run(const PanelCtx& c, SubPanel<R, SB>& sp, PanelShared& sh,
+                                               int& slot) {
+        column_step<R, SB, J>(c, sp, sh, slot);
+        SubColumns<R, SB, J + 1>::run(c, sp, sh, slot);
     }
 };
-template <>
-struct Columns<PB> {
-    __device__ __forceinline__ static void run(const PanelCtx&, PanelShared&) {}
+template <int R, int SB>
+struct SubColumns<R, SB, SB> {
+    __device__ __forceinline__ static void run(const PanelCtx&, SubPanel<R, SB>&, PanelShared&, int&) {}
 };
 
+template <int R, int SB>
 __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ jobs, int p) {
     __shared__ PanelShared sh;
     const QrJob Jb = jobs[blockIdx.x];
@@ -260,70 +240,235 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
     c.A = Jb.Z + (int64_t)k * c.ld + k;
     c.L = Jb.d - k;
     c.jb = min(PB, Jb.d - k);
-    c.vec = (c.jb == PB) && (Jb.d % 4 == 0);
     const int tid = threadIdx.x;
+    for (int e = tid; e < PB * (PB + 1); e += PT) (&sh.Tq[0][0])[e] = 0.f;
+    int slot = 0;
 
-    for (int e = tid; e < PB * (PB + 1); e += PT) (&sh.T[0][0])[e] = 0.f;
-    float sig_part = 0.f;
-    for (int i = tid; i < c.L; i += PT) {
-        const float x = c.A[(int64_t)i * c.ld];
-        if (i > 0) sig_part += x * x;
-        else sh.alpha = x;
+    SubPanel<R, SB> sp;
+    for (int s = 0; s * SB < c.jb; ++s) {
+        sp.c0 = s * SB;
+        sp.sbw = min(SB, c.jb - sp.c0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + PT * r;
+#pragma unroll
+            for (int q = 0; q < SB; ++q)
+                sp.a[r][q] = (i < c.L && q < sp.sbw) ? c.A[(int64_t)i * c.ld + sp.c0 + q] : 0.f;
+        }
+        // left-looking: apply the earlier sub-panels' reflector blocks in order
+        for (int qb = 0; qb < s; ++qb) {
+            const int y0 = qb * SB;
+            float part[SB * SB];
+#pragma unroll
+            for (int e = 0; e < SB * SB; ++e) part[e] = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = tid + PT * r;
+                if (i < c.L && i >= y0) {
+                    float y[SB];
+#pragma unroll
+                    for (int l = 0; l < SB; ++l) y[l] = yval(c, i, y0 + l);
+#pragma unroll
+                    for (int l = 0; l < SB; ++l)
+#pragma unroll
+                        for (int q = 0; q < SB; ++q) part[l * SB + q] += y[l] * sp.a[r][q];
+                }
+            }
+            slot ^= 1;
+            block_partial<SB * SB>(part, sh, slot);
+            if (tid < SB * SB) sh.P[tid] = block_value(sh, slot, tid);
+            __syncthreads();
+            if (tid < SB * SB) {   // P2 = T_q^T P
+                const int l = tid / SB, q = tid % SB;
+                float acc = 0.f;
+                for (int m = 0; m <= l; ++m) acc += sh.Tq[y0 + m][y0 + l] * sh.P[m * SB + q];
+                sh.P2[tid] = acc;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = tid + PT * r;
+                if (i < c.L && i >= y0) {
+                    float y[SB];
+#pragma unroll
+                    for (int l = 0; l < SB; ++l) y[l] = yval(c, i, y0 + l);
+#pragma unroll
+                    for (int q = 0; q < SB; ++q) {
+                        float acc = 0.f;
+#pragma unroll
+                        for (int l = 0; l < SB; ++l) acc += y[l] * sh.P2[l * SB + q];
+                        sp.a[r][q] -= acc;
+                    }
+                }
+            }
+        }
+        // norm of the first column below its diagonal
+        {
+            float sig_part = 0.f;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int i = tid + PT * r;
+                if (i < c.L) {
+                    if (i > sp.c0) sig_part += sp.a[r][0] * sp.a[r][0];
+                    else if (i == sp.c0) sh.alpha = sp.a[r][0];
+                }
+            }
+            float v1[1] = {sig_part};
+            slot ^= 1;
+            block_partial<1>(v1, sh, slot);
+        }
+        SubColumns<R, SB, 0>::run(c, sp, sh, slot);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int i = tid + PT * r;
+            if (i < c.L) {
+#pragma unroll
+                for (int q = 0; q < SB; ++q)
+                    if (q < sp.sbw) c.A[(int64_t)i * c.ld + sp.c0 + q] = sp.a[r][q];
+            }
+        }
+        __syncthreads();   // stored reflectors visible to the next sub-panel's loads; T_q complete
     }
-    const float ws = wave_sum(sig_part);
-    if ((tid & 63) == 0) sh.rsig[tid >> 6] = ws;
+
+    // Gram S = Y^T Y of the panel's reflectors (PB x PB) as 32x32 fp32 MFMA
+    // blocks: lane l of wave w supplies Y[row + l/32][32 b + l%32] as the
+    // operand of column block b. Eight row pairs are loaded before their
+    // MFMAs are issued.
+    {
+        constexpr int NB = PB / 32;
+        constexpr int U = 8;
+        const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+        f32x16 acc[NB][NB];
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[bi][bj][e] = 0.f;
+        const int rows_per = ((c.L + NW - 1) / NW + 1) & ~1;
+        const int r0 = wave * rows_per, r1 = min(c.L, r0 + rows_per);
+        for (int i0 = r0; i0 < r1; i0 += 2 * U) {
+            float y[U][NB];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int row = i0 + 2 * u + h;
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int col = 32 * b + l32;
+                    y[u][b] = (row < r1 && col < c.jb) ? yval(c, row, col) : 0.f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+                    for (int bj = 0; bj < NB; ++bj)
+                        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u][bi], y[u][bj], acc[bi][bj], 0, 0, 0);
+        }
+#pragma unroll
+        for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+            for (int bj = 0; bj < NB; ++bj) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sh.gram[wave][8 * (e >> 2) + 4 * h + (e & 3)][l32] = acc[bi][bj][e];
+                __syncthreads();
+                for (int e = tid; e < 32 * 32; e += PT) {
+                    const int i = e / 32, j = e % 32;
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w = 0; w < NW; ++w) sum += sh.gram[w][i][j];
+                    sh.S[32 * bi + i][32 * bj + j] = sum;
+                }
+                __syncthreads();
+            }
+    }
+    if (tid < PB) {
+        const int r = tid;
+        for (int j = 0; j < PB; ++j) {
+            float v = 0.f;
+            if (r < c.jb && j < c.jb && j >= r) {
+                if (j == r) {
+                    v = sh.tau[r];
+                } else {
+                    float sum = 0.f;
+                    for (int l = r; l < j; ++l) sum += sh.Tf[r][l] * sh.S[l][j];
+                    v = -sh.tau[j] * sum;
+                }
+            }
+            sh.Tf[r][j] = v;
+        }
+    }
     __syncthreads();
-
-    Columns<0>::run(c, sh);
-
     float* Tout = Jb.T + (int64_t)p * PB * PB;
-    for (int e = tid; e < PB * PB; e += PT) Tout[e] = sh.T[e / PB][e % PB];
+    for (int e = tid; e < PB * PB; e += PT) Tout[e] = sh.Tf[e / PB][e % PB];
 }
 
 // Partial products W_s = Y[rows of split s]^T C[rows of split s].
-// A wavefront owns a 32 x 128 block of W (four 32x32 MFMA accumulators that
-// share the Y operand); lane l supplies Y[row + l/32][l%32] and
+// A wavefront owns a PB x 128 block of W (PB/32 x 4 MFMA accumulators that
+// share operands); lane l supplies Y[row + l/32][32 b + l%32] and
 // C[row + l/32][col + l%32], i.e. 128-byte row segments of both matrices.
-__global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ jobs, int p,
-                                                     int q_mode) {
-    const QrJob Jb = jobs[blockIdx.z];
+__global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ jobs, QrClasses cls,
+                                                     int p, int q_mode) {
+    constexpr int NB = PB / 32;
+    int job, local;
+    if (!qr_locate(cls, QG_DOTS, p, q_mode, blockIdx.x, job, local)) return;
+    const QrJob Jb = jobs[job];
     const int k = p * PB;
-    if (k >= Jb.d) return;
     const int d = Jb.d;
     const int jb = min(PB, d - k), L = d - k;
     const int ncols = q_mode ? L : L - jb;
-    if (ncols <= 0) return;
     const int splits = qr_splits(L), kc = qr_chunk(L, splits);
-    const int s = blockIdx.y;
-    if (s >= splits) return;
+    const int nxb = (ncols + 511) / 512;
+    const int s = local / nxb;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, l32 = lane & 31;
-    const int j0 = blockIdx.x * 512 + wave * 128;
+    const int j0 = (local % nxb) * 512 + wave * 128;
     if (j0 >= ncols) return;
     const int r0 = s * kc, r1 = min(L, r0 + kc);
     const float* Y = Jb.Z + (int64_t)k * d + k;
     const float* C = q_mode ? Jb.X + (int64_t)k * d + k : Jb.Z + (int64_t)k * d + k + jb;
 
-    f32x16 acc[4];
+    f32x16 acc[NB][4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int a = 0; a < NB; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] = 0.f;
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-#pragma unroll 4
-    for (int i = r0; i < r1; i += 2) {
-        const int row = i + h;
-        float y = 0.f;
-        float x[4] = {0.f, 0.f, 0.f, 0.f};
-        if (row < r1) {
-            if (l32 < jb) y = row < l32 ? 0.f : (row == l32 ? 1.f : Y[(int64_t)row * d + l32]);
+    // Four row pairs per iteration: all loads are issued before the MFMAs
+    // that consume them.
+    constexpr int U = 4;
+    for (int i0 = r0; i0 < r1; i0 += 2 * U) {
+        float y[U][NB];
+        float x[U][4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = j0 + 32 * b + l32;
-                if (col < ncols) x[b] = C[(int64_t)row * d + col];
+        for (int u = 0; u < U; ++u) {
+            const int row = i0 + 2 * u + h;
+#pragma unroll
+            for (int a = 0; a < NB; ++a) y[u][a] = 0.f;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) x[u][b] = 0.f;
+            if (row < r1) {
+#pragma unroll
+                for (int a = 0; a < NB; ++a) {
+                    const int yc = 32 * a + l32;
+                    if (yc < jb) y[u][a] = row < yc ? 0.f : (row == yc ? 1.f : Y[(int64_t)row * d + yc]);
+                }
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const int col = j0 + 32 * b + l32;
+                    if (col < ncols) x[u][b] = C[(int64_t)row * d + col];
+                }
             }
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(y, x[b], acc[b], 0, 0, 0);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int a = 0; a < NB; ++a)
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u][a], x[u][b], acc[a][b], 0, 0, 0);
     }
 
     float* part = Jb.part + (int64_t)s * PB * d;
@@ -332,28 +477,30 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
         const int j = j0 + 32 * b + l32;
         if (j >= ncols) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int cc = 8 * (r >> 2) + 4 * h + (r & 3);
-            part[(int64_t)cc * d + j] = acc[b][r];
-        }
+        for (int a = 0; a < NB; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int cc = 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
+                part[(int64_t)cc * d + j] = acc[a][b][r];
+            }
     }
 }
 
 // W2[:, j] = T^T (sum_s W_s[:, j])  (factorisation)   or   T (...)  (Q formation).
-__global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, int p,
-                                                       int q_mode) {
+__global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, QrClasses C,
+                                                       int p, int q_mode) {
     __shared__ float Ts[PB][PB + 1];
-    const QrJob Jb = jobs[blockIdx.y];
+    int job, local;
+    if (!qr_locate(C, QG_REDUCE, p, q_mode, blockIdx.x, job, local)) return;
+    const QrJob Jb = jobs[job];
     const int k = p * PB;
-    if (k >= Jb.d) return;
     const int d = Jb.d;
     const int jb = min(PB, d - k), L = d - k;
     const int ncols = q_mode ? L : L - jb;
-    if (ncols <= 0) return;
     const float* Tp = Jb.T + (int64_t)p * PB * PB;
     for (int e = threadIdx.x; e < PB * PB; e += 256) Ts[e / PB][e % PB] = Tp[e];
     __syncthreads();
-    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int j = local * 256 + threadIdx.x;
     if (j >= ncols) return;
     const int splits = qr_splits(L);
     float w[PB];
@@ -400,33 +547,34 @@ __global__ __launch_bounds__(256) void copy_cols_kernel(const CopyJob* __restric
 
 }  // namespace
 
-hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, hipStream_t s) {
-    if (njobs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_panel_kernel, dim3(njobs), dim3(PT), 0, s, jobs, p);
+hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s) {
+    const int L = max_d - p * PB;
+    if (njobs <= 0 || L <= 0) return hipSuccess;
+    const int rows = (L + PT - 1) / PT;
+    dim3 g(njobs), b(PT);
+    if (rows <= 1)       qr_panel_kernel<1, 8><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 2)  qr_panel_kernel<2, 8><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 4)  qr_panel_kernel<4, 8><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 8)  qr_panel_kernel<8, 8><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 12) qr_panel_kernel<12, 8><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 16) qr_panel_kernel<16, 4><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 24) qr_panel_kernel<24, 4><<<g, b, 0, s>>>(jobs, p);
+    else if (rows <= 32) qr_panel_kernel<32, 4><<<g, b, 0, s>>>(jobs, p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_qr_dots(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                          hipStream_t s) {
-    const int k = p * PB;
-    const int L = max_d - k;
-    if (njobs <= 0 || L <= 0) return hipSuccess;
-    const int ncols = q_mode ? L : L - (L < PB ? L : PB);
-    if (ncols <= 0) return hipSuccess;
-    dim3 grid((ncols + 511) / 512, qr_splits(L), njobs);
-    hipLaunchKernelGGL(qr_dots_kernel, grid, dim3(256), 0, s, jobs, p, q_mode);
+hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_DOTS, p, q_mode);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qr_dots_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p, q_mode);
     return hipGetLastError();
 }
 
-hipError_t launch_qr_reduce(const QrJob* jobs, int njobs, int p, int max_d, int q_mode,
-                            hipStream_t s) {
-    const int k = p * PB;
-    const int L = max_d - k;
-    if (njobs <= 0 || L <= 0) return hipSuccess;
-    const int ncols = q_mode ? L : L - (L < PB ? L : PB);
-    if (ncols <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_reduce_kernel, dim3((ncols + 255) / 256, njobs), dim3(256), 0, s, jobs, p,
-                       q_mode);
+hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_REDUCE, p, q_mode);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qr_reduce_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p, q_mode);
     return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ class opt_hparams(C.Structure):
     _fields_ = [
         ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("lr", C.c_float),
         ("K", C.c_int32), ("power_iters", C.c_int32),
-        ("capacity_bytes", C.c_uint64), ("flags", C.c_uint32),
+        ("capacity_bytes", C.c_uint64), ("refresh_capacity_bytes", C.c_uint64), ("flags", C.c_uint32),
     ]
 
 

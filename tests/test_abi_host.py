@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(N):
 
 
 def hp(N, **kw):
-    base = dict(beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-3, K=10, power_iters=1, capacity_bytes=0, flags=0)
+    base = dict(beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-3, K=10, power_iters=1, capacity_bytes=0, refresh_capacity_bytes=0, flags=0)
     base.update(kw)
     return N.opt_hparams(**base)
 
@@ -163,8 +163,18 @@ def test_null_group_and_bad_building_block_args(N):
 
 
 def test_workspace_is_max_over_groups(N):
-    """Scratch is sized for the largest micro-group, not the sum."""
-    one_group = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 128), hp(N))  # 128 x 4 MiB = cap
-    two_groups = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 200), hp(N))
-    assert N.opt_plan(descs(N, [(1024, 1024)] * 200), hp(N))[2] == 2
+    """Scratch is sized for the largest micro-group (or refresh batch), not the sum."""
+    h = hp(N, refresh_capacity_bytes=1 << 30)
+    one_group = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 128), h)  # 128 x 4 MiB = cap
+    two_groups = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 200), h)
+    assert N.opt_plan(descs(N, [(1024, 1024)] * 200), h)[2] == 2
     assert one_group <= two_groups < 1.05 * one_group
+    assert one_group >= 128 * 4 * 4 * 1024 * 1024          # four m x n rotation buffers per matrix
+
+
+def test_refresh_batches_follow_their_cap(N):
+    d = descs(N, [(2048, 2048)] * 64)
+    small = N.opt_group_workspace_size(d, hp(N, refresh_capacity_bytes=1 << 28))
+    large = N.opt_group_workspace_size(d, hp(N, refresh_capacity_bytes=1 << 36))
+    assert small < large
+    assert large >= 64 * 2 * 4 * 2048 * 2048               # every QR input of one batch
