@@ -33,6 +33,15 @@ if ROOT not in sys.path:
 
 MI355X_FP32_MFMA_TFLOPS = 157.3
 MI355X_HBM_GBPS = 8000.0
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
+GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/internal.h")
+# Instantiations of gemm_grouped_kernel used by the rotation phases when the
+# momentum is bf16 (the Gram products of the refresh read bf16 M as A, so
+# they are the bf16-A instantiations and stay out of this set).
+ROTATION_VARIANTS = ("gemm_grouped_kernel<true, false, false, false>",
+                     "gemm_grouped_kernel<true, false, false, true>",
+                     "gemm_grouped_kernel<false, false, false, false>",
+                     "gemm_grouped_kernel<false, true, false, false>")
 
 METRIC = "optimizer steps/s + params updated/s per micro-group; HBM GB/s & MFMA util"
 
@@ -55,6 +64,61 @@ def elementwise_bytes(shapes, m_dtype):
     mb = 2 if m_dtype == "bf16" else 4
     mn = sum(m * n for m, n in shapes)
     return {"momentum": mn * (4 + 2 * mb), "adam": mn * 20.0}
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int, out_path: str = TRAFFIC_JSON):
+    """HBM bytes per rotation-GEMM launch from two rocprofv3 --pmc runs.
+
+    Each counter is scaled by what it reads for the calibration copy (the
+    first __amd_rocclr_copyBuffer dispatch, `calib_mib` MiB read and written).
+    """
+    import csv
+    def rows(path, counter):
+        with open(path) as f:
+            return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+    F, W = rows(fetch_csv, "FETCH_SIZE"), rows(write_csv, "WRITE_SIZE")
+    calib = calib_mib * (1 << 20)
+    cf = float(next(r for r in F if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
+    cw = float(next(r for r in W if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
+    sf, sw = calib / cf, calib / cw
+    rot = lambda r: any(v in r["Kernel_Name"] for v in ROTATION_VARIANTS)
+    fr = [float(r["Counter_Value"]) * 1024 * sf for r in F if rot(r)]
+    wr = [float(r["Counter_Value"]) * 1024 * sw for r in W if rot(r)]
+    out = {
+        "kernel": "gemm_grouped_kernel, rotation-phase instantiations",
+        "gemm_source_sha256": gemm_source_hash(),
+        "launches": len(fr),
+        "fetch_bytes_per_launch": sum(fr) / len(fr),
+        "write_bytes_per_launch": sum(wr) / len(wr),
+        "fetch_scale": sf, "write_scale": sw,
+        "calibration": f"{calib_mib} MiB device copy (__amd_rocclr_copyBuffer): FETCH_SIZE x{sf:.4f}, "
+                       f"WRITE_SIZE x{sw:.4f}",
+    }
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def traffic_per_launch():
+    """Counter bytes per rotation-GEMM launch, or None if the GEMM source has
+    changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
 
 def cpu_baseline(wl, budget_s: float):
@@ -113,7 +177,13 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (a dispatch of known size "
                          "for scaling hardware byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the rotation-GEMM traffic summary from two rocprofv3 --pmc "
+                         "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(*args.summarize_pmc, calib_mib=args.calibrate_copy_mib or 1024)))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -190,7 +260,8 @@ def main(argv=None):
         achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else None
         roofline = {
             "bound": "mfma", "achieved": achieved, "peak": MI355X_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None, "traffic": None,
+            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None,
+            "traffic": traffic_per_launch(),
             "kernel": "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)",
             "launches": launches, "avg_launch_ms": ms / max(launches, 1),
             "flops_per_launch": flops / max(launches, 1),

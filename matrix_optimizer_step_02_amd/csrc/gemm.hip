@@ -42,9 +42,15 @@ namespace {
 constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
 constexpr int NT = 256;
 constexpr int KPAD = BK + 4;   // pitch of k-contiguous LDS rows
+#ifndef MATOPT_XCD_RUN
+#define MATOPT_XCD_RUN 16
+#endif
+#ifndef MATOPT_GROUP_M
+#define MATOPT_GROUP_M 4
+#endif
 constexpr int XCD = 8;
-constexpr int XCD_RUN = 16;
-constexpr int GROUP_M = 4;
+constexpr int XCD_RUN = MATOPT_XCD_RUN;
+constexpr int GROUP_M = MATOPT_GROUP_M;
 
 template <bool AT> struct ALayout {
     static constexpr int size = AT ? BK * BM : BM * KPAD;
