@@ -35,13 +35,19 @@ MI355X_FP32_MFMA_TFLOPS = 157.3
 MI355X_HBM_GBPS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/internal.h")
-# Instantiations of gemm_grouped_kernel used by the rotation phases when the
-# momentum is bf16 (the Gram products of the refresh read bf16 M as A, so
-# they are the bf16-A instantiations and stay out of this set).
-ROTATION_VARIANTS = ("gemm_grouped_kernel<true, false, false, false>",
-                     "gemm_grouped_kernel<true, false, false, true>",
-                     "gemm_grouped_kernel<false, false, false, false>",
-                     "gemm_grouped_kernel<false, true, false, false>")
+# Operand variants (A transposed, B transposed, A bf16, B bf16) of
+# gemm_grouped_kernel used by the rotation phases when the momentum is bf16
+# (the Gram products of the refresh read bf16 M as A, so they are the bf16-A
+# instantiations and stay out of this set).
+ROTATION_VARIANTS = {("true", "false", "false", "false"), ("true", "false", "false", "true"),
+                     ("false", "false", "false", "false"), ("false", "true", "false", "false")}
+
+
+def is_rotation_gemm(kernel_name: str) -> bool:
+    import re
+    m = re.search(r"gemm_grouped_kernel<.*?(true|false), (true|false), (true|false), (true|false)>",
+                  kernel_name)
+    return bool(m) and tuple(m.groups()) in ROTATION_VARIANTS
 
 METRIC = "optimizer steps/s + params updated/s per micro-group; HBM GB/s & MFMA util"
 
@@ -90,7 +96,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int, out_path: str 
     cf = float(next(r for r in F if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
     cw = float(next(r for r in W if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
     sf, sw = calib / cf, calib / cw
-    rot = lambda r: any(v in r["Kernel_Name"] for v in ROTATION_VARIANTS)
+    rot = lambda r: is_rotation_gemm(r["Kernel_Name"])
     fr = [float(r["Counter_Value"]) * 1024 * sf for r in F if rot(r)]
     wr = [float(r["Counter_Value"]) * 1024 * sw for r in W if rot(r)]
     out = {

@@ -28,27 +28,47 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def command(out: str = LIB):
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
-            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-            "-o", out] + sources()
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
+def compile_cmd(src: str, obj: str):
+    return [hipcc()] + FLAGS + ["-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
 
 
 def build(verbose: bool = False) -> str:
+    """Compile every source to an object in parallel, then link the library."""
     os.makedirs(OUT_DIR, exist_ok=True)
+    objs, procs = [], []
+    for src in sources():
+        obj = os.path.join(OUT_DIR, os.path.basename(src) + ".o")
+        cmd = compile_cmd(src, obj)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    failed = False
+    for src, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out + err)
+            failed = True
+        elif verbose and err.strip():
+            sys.stderr.write(err)
+    if failed:
+        raise RuntimeError("hipcc failed building libmatopt.so")
     tmp = LIB + ".tmp"
-    cmd = command(tmp)
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmatopt.so")
-    if verbose and r.stderr.strip():
-        sys.stderr.write(r.stderr)
+        raise RuntimeError("hipcc failed linking libmatopt.so")
     os.replace(tmp, LIB)
+    for o in objs:
+        os.remove(o)
     return LIB
 
 

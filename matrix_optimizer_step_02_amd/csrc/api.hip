@@ -66,6 +66,7 @@ struct Mat {
 // Byte offsets into the table image (host) / table region (device).
 struct GemmLaunch {
     int variant = 0;
+    int cfg = 0;     // index into kGemmCfgs
     int nprob = 0;
     int total_tiles = 0;
     uint64_t probs = 0;
@@ -258,6 +259,25 @@ struct PGemm {
     int variant;
 };
 
+void set_tiles(GemmProb& p, int cfg) {
+    p.tiles_m = (p.M + kGemmCfgs[cfg].bm - 1) / kGemmCfgs[cfg].bm;
+    p.tiles_n = (p.N + kGemmCfgs[cfg].bn - 1) / kGemmCfgs[cfg].bn;
+}
+
+int tiles_of(const std::vector<GemmProb>& probs, int cfg) {
+    int t = 0;
+    for (GemmProb q : probs) {
+        set_tiles(q, cfg);
+        t += q.tiles_m * q.tiles_n;
+    }
+    return t;
+}
+
+// Large tiles when the launch has enough of them to fill the GPU.
+int choose_cfg(const std::vector<GemmProb>& probs) {
+    return tiles_of(probs, 1) >= kGemmLargeMinTiles ? 1 : 0;
+}
+
 // op(A) is M x K: A stored M x K (at = false) or K x M (at = true); op(B) is
 // K x N: B stored K x N (bt = false) or N x K (bt = true).
 PGemm mk(bool at, bool bt, const void* A, bool a_bf16, int64_t lda, const void* B, bool b_bf16,
@@ -277,8 +297,7 @@ PGemm mk(bool at, bool bt, const void* A, bool a_bf16, int64_t lda, const void* 
     p.flags = vec_flags(A, lda, at ? M : K, a_bf16, B, ldb, bt ? K : N, b_bf16);
     p.alpha = alpha;
     p.beta = beta;
-    p.tiles_m = (int32_t)((M + kGemmBM - 1) / kGemmBM);
-    p.tiles_n = (int32_t)((N + kGemmBN - 1) / kGemmBN);
+    set_tiles(p, 0);
     g.variant = gemm_variant(at, bt, a_bf16, b_bf16);
     return g;
 }
@@ -294,14 +313,17 @@ std::vector<GemmLaunch> put_gemm(Image& img, const std::vector<PGemm>& all) {
         // LPT over tiles: the cost of a tile grows with K.
         std::stable_sort(probs.begin(), probs.end(),
                          [](const GemmProb& a, const GemmProb& b) { return a.K > b.K; });
+        const int cfg = choose_cfg(probs);
         std::vector<int32_t> tb;
         int total = 0;
-        for (const GemmProb& p : probs) {
+        for (GemmProb& p : probs) {
+            set_tiles(p, cfg);
             tb.push_back(total);
             total += p.tiles_m * p.tiles_n;
         }
         GemmLaunch L;
         L.variant = v;
+        L.cfg = cfg;
         L.nprob = (int)probs.size();
         L.total_tiles = total;
         L.probs = img.put(probs);
@@ -530,7 +552,7 @@ struct PhaseScope {
 hipError_t run_gemm(opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alpha_scale,
                     hipStream_t s) {
     for (const GemmLaunch& L : Ls) {
-        hipError_t e = launch_gemm_grouped(L.variant, dptr<GemmProb>(g, L.probs), dptr<int32_t>(g, L.tb),
+        hipError_t e = launch_gemm_grouped(L.variant, L.cfg, dptr<GemmProb>(g, L.probs), dptr<int32_t>(g, L.tb),
                                            L.nprob, L.total_tiles, alpha_scale, s);
         if (e != hipSuccess) return e;
         g->kernels_in_scope += 1;
@@ -857,7 +879,10 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
                         C, ldc, M, N, K, alpha, beta);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before gemm");
-    e = launch_gemm_single(pg.variant, pg.p, (hipStream_t)stream);
+    GemmProb single = pg.p;
+    const int cfg = choose_cfg({single});
+    set_tiles(single, cfg);
+    e = launch_gemm_single(pg.variant, cfg, single, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return OPT_OK;
 }

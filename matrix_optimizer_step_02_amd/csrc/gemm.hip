@@ -5,20 +5,21 @@
 // refresh, and the compact-WY trailing updates of the blocked QR.
 //
 // gfx950 has no reduced-precision fp32 matrix path, so the contraction runs on
-// v_mfma_f32_32x32x2_f32 (32x32 outputs, 2-deep k, fp32 accumulate). A
-// workgroup of 4 wavefronts owns a 128x128 tile, each wavefront a 64x64
-// quarter held as 2x2 MFMA accumulators (64 AGPR-class registers). K advances
-// in slabs of 32 staged through LDS with two buffers, so one barrier per slab
+// v_mfma_f32_32x32x2_f32 (32x32 outputs, 2-deep k, fp32 accumulate). A tile
+// configuration Cfg<WAVES_M, WAVES_N, BLK_M, BLK_N> gives each wavefront a
+// (32 BLK_M) x (32 BLK_N) block of the output held as BLK_M x BLK_N MFMA
+// accumulators, and the workgroup WAVES_M x WAVES_N wavefronts. K advances in
+// slabs of 32 staged through LDS with two buffers, so one barrier per slab
 // separates the store of slab k+1 from the reads of slab k; the global loads
 // of slab k+1 are issued before the MFMAs of slab k.
 //
 // LDS layouts keep every MFMA operand read conflict-free:
 //  * an operand whose non-k index is contiguous in memory (A stored K x M,
-//    B stored K x N) is kept k-major, [32][128], read 4 bytes per lane with
-//    32 consecutive lanes on consecutive words;
+//    B stored K x N) is kept k-major, [32][BM or BN], read 4 bytes per lane
+//    with 32 consecutive lanes on consecutive words;
 //  * an operand whose k index is contiguous (A stored M x K, B stored N x K)
-//    is kept [128][32 + 4], read 16 bytes per lane. Within a group of 8 k
-//    values, MFMA s (0..3) takes k = 8g + s from lanes 0..31 and
+//    is kept [BM or BN][32 + 4], read 16 bytes per lane. Within a group of 8
+//    k values, MFMA s (0..3) takes k = 8g + s from lanes 0..31 and
 //    k = 8g + 4 + s from lanes 32..63, so one 16-byte read feeds four MFMAs;
 //    the row pitch of 36 words puts 8 consecutive rows on 8 distinct 4-bank
 //    groups.
@@ -27,9 +28,10 @@
 // Work distribution: one workgroup per output tile; problems of a grouped
 // launch are concatenated in tile space in longest-processing-time order
 // (costliest k first) by the host. Consecutive workgroup ids are spread by
-// the dispatcher over the 8 XCDs, so ids are remapped in windows of 8 x 16
-// tiles to give each XCD 16 neighbouring tiles (shared A rows / B columns in
-// its own L2) while keeping the LPT order at window granularity.
+// the dispatcher over the 8 XCDs, so ids are remapped in windows of
+// 8 x XCD_RUN tiles to give each XCD XCD_RUN neighbouring tiles (shared A
+// rows / B columns in its own L2) while keeping the LPT order at window
+// granularity.
 #include "internal.h"
 
 namespace matopt {
@@ -39,8 +41,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int NT = 256;
+constexpr int BK = kGemmBK;
 constexpr int KPAD = BK + 4;   // pitch of k-contiguous LDS rows
 #ifndef MATOPT_XCD_RUN
 #define MATOPT_XCD_RUN 16
@@ -52,12 +53,30 @@ constexpr int XCD = 8;
 constexpr int XCD_RUN = MATOPT_XCD_RUN;
 constexpr int GROUP_M = MATOPT_GROUP_M;
 
-template <bool AT> struct ALayout {
-    static constexpr int size = AT ? BK * BM : BM * KPAD;
+template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N>
+struct Cfg {
+    static constexpr int WM = WAVES_M, WN = WAVES_N, TM = BLK_M, TN = BLK_N;
+    static constexpr int NT = 64 * WAVES_M * WAVES_N;
+    static constexpr int BM = 32 * BLK_M * WAVES_M;
+    static constexpr int BN = 32 * BLK_N * WAVES_N;
+    static constexpr int QA = BM * BK / 4 / NT;   // float4 loads of A per thread per slab
+    static constexpr int QB = BN * BK / 4 / NT;
+    template <bool AT> static constexpr int a_size() { return AT ? BK * BM : BM * KPAD; }
+    template <bool BT> static constexpr int b_size() { return BT ? BN * KPAD : BK * BN; }
+    template <bool AT, bool BT> static constexpr int smem_floats() {
+        return 2 * (a_size<AT>() + b_size<BT>());
+    }
+    static_assert(QA * 4 * NT == BM * BK && QB * 4 * NT == BN * BK, "tile not divisible by the loaders");
 };
-template <bool BT> struct BLayout {
-    static constexpr int size = BT ? BN * KPAD : BK * BN;
-};
+
+// Configurations of the grouped launches (rotations, Gram products, opt_gemm).
+using SmallCfg = Cfg<2, 2, 2, 2>;
+using LargeCfg = Cfg<2, 4, 4, 2>;
+static_assert(SmallCfg::BM == kGemmCfgs[0].bm && SmallCfg::BN == kGemmCfgs[0].bn, "tile size mismatch");
+static_assert(LargeCfg::BM == kGemmCfgs[1].bm && LargeCfg::BN == kGemmCfgs[1].bn, "tile size mismatch");
+// Configuration of the QR trailing updates (short K, memory-bound C).
+using QrCfg = Cfg<2, 2, 2, 2>;
+static_assert(QrCfg::BM == kQrTile && QrCfg::BN == kQrTile, "QR tile size mismatch");
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
@@ -100,15 +119,15 @@ __device__ __forceinline__ f32x4 load4(const void* base, int64_t ld, int row, in
     return v;
 }
 
-template <bool AT, bool ABF, bool UL>
-__device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, f32x4 (&r)[4]) {
+template <class C, bool AT, bool ABF, bool UL>
+__device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, f32x4 (&r)[C::QA]) {
     const bool vec = p.flags & GF_A_VEC;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int f = tid + NT * q;
-        if (AT) {  // stored K x M: slab rows are k, 32 float4 per row of 128
-            const int rr = f >> 5, c4 = f & 31;
+    for (int q = 0; q < C::QA; ++q) {
+        const int f = tid + C::NT * q;
+        if (AT) {  // stored K x M: slab rows are k, BM/4 float4 per row
+            const int rr = f / (C::BM / 4), c4 = f % (C::BM / 4);
             r[q] = load4<ABF>(p.A, p.lda, k0 + rr, m0 + 4 * c4, p.K, p.M, vec);
         } else {   // stored M x K: slab rows are m, 8 float4 per row of 32
             const int rr = f >> 3, c4 = f & 7;
@@ -125,32 +144,32 @@ __device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, f32x4 
     }
 }
 
-template <bool BT, bool BBF>
-__device__ __forceinline__ void load_b(const GemmProb& p, int n0, int k0, f32x4 (&r)[4]) {
+template <class C, bool BT, bool BBF>
+__device__ __forceinline__ void load_b(const GemmProb& p, int n0, int k0, f32x4 (&r)[C::QB]) {
     const bool vec = p.flags & GF_B_VEC;
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int f = tid + NT * q;
+    for (int q = 0; q < C::QB; ++q) {
+        const int f = tid + C::NT * q;
         if (BT) {  // stored N x K
             const int rr = f >> 3, c4 = f & 7;
             r[q] = load4<BBF>(p.B, p.ldb, n0 + rr, k0 + 4 * c4, p.N, p.K, vec);
         } else {   // stored K x N
-            const int rr = f >> 5, c4 = f & 31;
+            const int rr = f / (C::BN / 4), c4 = f % (C::BN / 4);
             r[q] = load4<BBF>(p.B, p.ldb, k0 + rr, n0 + 4 * c4, p.K, p.N, vec);
         }
     }
 }
 
-template <bool AT>
-__device__ __forceinline__ void store_a(float* As, const f32x4 (&r)[4]) {
+template <class C, bool AT>
+__device__ __forceinline__ void store_a(float* As, const f32x4 (&r)[C::QA]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int f = tid + NT * q;
+    for (int q = 0; q < C::QA; ++q) {
+        const int f = tid + C::NT * q;
         if (AT) {
-            const int rr = f >> 5, c4 = f & 31;
-            *(f32x4*)&As[rr * BM + 4 * c4] = r[q];
+            const int rr = f / (C::BM / 4), c4 = f % (C::BM / 4);
+            *(f32x4*)&As[rr * C::BM + 4 * c4] = r[q];
         } else {
             const int rr = f >> 3, c4 = f & 7;
             *(f32x4*)&As[rr * KPAD + 4 * c4] = r[q];
@@ -158,204 +177,211 @@ __device__ __forceinline__ void store_a(float* As, const f32x4 (&r)[4]) {
     }
 }
 
-template <bool BT>
-__device__ __forceinline__ void store_b(float* Bs, const f32x4 (&r)[4]) {
+template <class C, bool BT>
+__device__ __forceinline__ void store_b(float* Bs, const f32x4 (&r)[C::QB]) {
     const int tid = threadIdx.x;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int f = tid + NT * q;
+    for (int q = 0; q < C::QB; ++q) {
+        const int f = tid + C::NT * q;
         if (BT) {
             const int rr = f >> 3, c4 = f & 7;
             *(f32x4*)&Bs[rr * KPAD + 4 * c4] = r[q];
         } else {
-            const int rr = f >> 5, c4 = f & 31;
-            *(f32x4*)&Bs[rr * BN + 4 * c4] = r[q];
+            const int rr = f / (C::BN / 4), c4 = f % (C::BN / 4);
+            *(f32x4*)&Bs[rr * C::BN + 4 * c4] = r[q];
         }
     }
 }
 
-template <bool AT, bool BT>
+template <class C>
+struct Acc {
+    f32x16 v[C::TM][C::TN];
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
+    }
+};
+
+template <class C, bool AT, bool BT>
 __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int wm, int wn, int lane,
-                                         f32x16 (&acc)[2][2]) {
+                                         Acc<C>& acc) {
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
     for (int g = 0; g < BK / 8; ++g) {
-        f32x4 a[2], b[2];
+        f32x4 a[C::TM], b[C::TN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int row = wm * 64 + i * 32 + l32;
+        for (int i = 0; i < C::TM; ++i) {
+            const int row = wm * 32 * C::TM + i * 32 + l32;
             if (AT) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * BM + row];
+                for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * C::BM + row];
             } else {
                 a[i] = *(const f32x4*)&As[row * KPAD + 8 * g + 4 * h];
             }
         }
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = wn * 64 + j * 32 + l32;
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = wn * 32 * C::TN + j * 32 + l32;
             if (BT) {
                 b[j] = *(const f32x4*)&Bs[col * KPAD + 8 * g + 4 * h];
             } else {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * BN + col];
+                for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * C::BN + col];
             }
         }
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc[i][j],
-                                                                    0, 0, 0);
+                for (int j = 0; j < C::TN; ++j)
+                    acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc.v[i][j], 0, 0, 0);
     }
 }
 
-// Old values of the C fragment a lane updates (beta != 0), in accumulator
-// order. All loads are issued before any store to C.
-__device__ __forceinline__ void load_c_fragment(const GemmProb& p, int m0, int n0, int wm, int wn, int lane,
-                                                float (&cold)[2][2][16]) {
+// Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32 of its 32x32 block: 32 lanes store 128 contiguous bytes.
+// With beta != 0 the old values of one row of blocks are all loaded before
+// any of them is stored (a store to C could otherwise alias a later load as
+// far as the compiler can tell, serialising them).
+template <class C>
+__device__ __forceinline__ void epilogue(const GemmProb& p, int m0, int n0, int wm, int wn, int lane,
+                                         const Acc<C>& acc, float alpha, float beta) {
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i) {
+        float cold[C::TN][16];
+        if (beta != 0.f) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + l32;
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                cold[i][j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    cold[j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+                }
             }
         }
-}
-
-template <bool AT, bool BT, bool ABF, bool BBF, bool UL>
-__device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
-                                          float* smem) {
-    constexpr int AS = ALayout<AT>::size, BS = BLayout<BT>::size;
-    float* As0 = smem;
-    float* As1 = smem + AS;
-    float* Bs0 = smem + 2 * AS;
-    float* Bs1 = smem + 2 * AS + BS;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    f32x16 acc[2][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    float cold[2][2][16];
-
-    const int nk = (p.K + BK - 1) / BK;
-    f32x4 ra[4], rb[4];
-    if (nk > 0) {
-        load_a<AT, ABF, UL>(p, m0, 0, ra);
-        load_b<BT, BBF>(p, n0, 0, rb);
-        store_a<AT>(As0, ra);
-        store_b<BT>(Bs0, rb);
-    }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const bool more = kt + 1 < nk;
-        if (more) {
-            load_a<AT, ABF, UL>(p, m0, (kt + 1) * BK, ra);
-            load_b<BT, BBF>(p, n0, (kt + 1) * BK, rb);
-        }
-        if (kt & 1) mma_slab<AT, BT>(As1, Bs1, wm, wn, lane, acc);
-        else        mma_slab<AT, BT>(As0, Bs0, wm, wn, lane, acc);
-        if (more) {
-            if (kt & 1) { store_a<AT>(As0, ra); store_b<BT>(Bs0, rb); }
-            else        { store_a<AT>(As1, ra); store_b<BT>(Bs1, rb); }
-        }
-        __syncthreads();
-    }
-
-    // Epilogue. Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
-    // column l%32 of its 32x32 block: 32 lanes store 128 contiguous bytes.
-    // With beta != 0 every old value of the fragment is loaded before the
-    // first store, so the loads overlap (a store to C could otherwise alias a
-    // later load as far as the compiler can tell, serialising them).
-    const float alpha = p.alpha * alpha_scale, beta = p.beta;
-    const int h = lane >> 5, l32 = lane & 31;
-    if (beta != 0.f) load_c_fragment(p, m0, n0, wm, wn, lane, cold);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
             if (col >= p.N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (row < p.M) {
-                    float val = alpha * acc[i][j][r];
-                    if (beta != 0.f) val += beta * cold[i][j][r];
+                    float val = alpha * acc.v[i][j][r];
+                    if (beta != 0.f) val += beta * cold[j][r];
                     p.C[(int64_t)row * p.ldc + col] = val;
                 }
             }
         }
+    }
 }
 
-// C += alpha op(A) op(B) for K <= 2 BK (the QR trailing updates, K = the
-// panel width): both K slabs go to the two LDS buffers at once, then the old
-// C fragment is requested so that its latency overlaps the MFMAs; the
-// operand staging registers are dead by then. A is not transposed, B is
-// stored K x N, both fp32.
+template <class C, bool AT, bool BT, bool ABF, bool BBF>
+__device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
+                                          float* smem) {
+    constexpr int AS = C::template a_size<AT>(), BS = C::template b_size<BT>();
+    // buffer b of A at smem + b*AS, of B at smem + 2*AS + b*BS; selected
+    // arithmetically so that the slab body is one straight-line block (a
+    // branch between two copies makes the compiler move every accumulator
+    // between register files at the join)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+
+    Acc<C> acc;
+    acc.zero();
+    const int nk = (p.K + BK - 1) / BK;
+    f32x4 ra[C::QA], rb[C::QB];
+    if (nk > 0) {
+        load_a<C, AT, ABF, false>(p, m0, 0, ra);
+        load_b<C, BT, BBF>(p, n0, 0, rb);
+        store_a<C, AT>(smem, ra);
+        store_b<C, BT>(smem + 2 * AS, rb);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            load_a<C, AT, ABF, false>(p, m0, (kt + 1) * BK, ra);
+            load_b<C, BT, BBF>(p, n0, (kt + 1) * BK, rb);
+        }
+        mma_slab<C, AT, BT>(smem + cur * AS, smem + 2 * AS + cur * BS, wm, wn, lane, acc);
+        if (more) {
+            store_a<C, AT>(smem + (cur ^ 1) * AS, ra);
+            store_b<C, BT>(smem + 2 * AS + (cur ^ 1) * BS, rb);
+        }
+        __syncthreads();
+    }
+    epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
+}
+
+// C += alpha A B for K <= 2 BK (the QR trailing updates, K = the panel
+// width): both K slabs go to the two LDS buffers at once, then the old C
+// fragment is requested so that its latency overlaps the MFMAs; the operand
+// staging registers are dead by then. A is not transposed and read as unit
+// lower trapezoidal (the stored reflectors), B is stored K x N, both fp32.
 static_assert(kQrPB <= 2 * kGemmBK, "the QR update tile holds the whole panel width in two LDS slabs");
 
-template <bool UL>
-__device__ __forceinline__ void gemm_tile_short_k(const GemmProb& p, int tm, int tn, float* smem) {
-    constexpr int AS = ALayout<false>::size, BS = BLayout<false>::size;
+__device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn, float* smem) {
+    using C = QrCfg;
+    constexpr int AS = C::a_size<false>(), BS = C::b_size<false>();
     float* As0 = smem;
     float* As1 = smem + AS;
     float* Bs0 = smem + 2 * AS;
     float* Bs1 = smem + 2 * AS + BS;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
     const int nk = (p.K + BK - 1) / BK;
     {
-        f32x4 ra[4], rb[4];
-        load_a<false, false, UL>(p, m0, 0, ra);
-        load_b<false, false>(p, n0, 0, rb);
-        store_a<false>(As0, ra);
-        store_b<false>(Bs0, rb);
+        f32x4 ra[C::QA], rb[C::QB];
+        load_a<C, false, false, true>(p, m0, 0, ra);
+        load_b<C, false, false>(p, n0, 0, rb);
+        store_a<C, false>(As0, ra);
+        store_b<C, false>(Bs0, rb);
         if (nk > 1) {
-            load_a<false, false, UL>(p, m0, BK, ra);
-            load_b<false, false>(p, n0, BK, rb);
-            store_a<false>(As1, ra);
-            store_b<false>(Bs1, rb);
+            load_a<C, false, false, true>(p, m0, BK, ra);
+            load_b<C, false, false>(p, n0, BK, rb);
+            store_a<C, false>(As1, ra);
+            store_b<C, false>(Bs1, rb);
         }
     }
     __syncthreads();
-    float cold[2][2][16];
-    load_c_fragment(p, m0, n0, wm, wn, lane, cold);
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    mma_slab<false, false>(As0, Bs0, wm, wn, lane, acc);
-    if (nk > 1) mma_slab<false, false>(As1, Bs1, wm, wn, lane, acc);
     const int h = lane >> 5, l32 = lane & 31;
+    float cold[C::TM][C::TN][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + l32;
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                cold[i][j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+            }
+        }
+    Acc<C> acc;
+    acc.zero();
+    mma_slab<C, false, false>(As0, Bs0, wm, wn, lane, acc);
+    if (nk > 1) mma_slab<C, false, false>(As1, Bs1, wm, wn, lane, acc);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
             if (col >= p.N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < p.M) p.C[(int64_t)row * p.ldc + col] = p.alpha * acc[i][j][r] + p.beta * cold[i][j][r];
+                const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row < p.M) p.C[(int64_t)row * p.ldc + col] = p.alpha * acc.v[i][j][r] + p.beta * cold[i][j][r];
             }
         }
 }
@@ -381,53 +407,46 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return w0 + (r % XCD) * XCD_RUN + r / XCD;
 }
 
-template <bool AT, bool BT>
-constexpr int smem_floats() {
-    return 2 * (ALayout<AT>::size + BLayout<BT>::size);
-}
+// A launch's problems: a device table (nprob > 0) or one problem passed by
+// value (nprob == 0, used by opt_gemm).
+struct GemmArgs {
+    const GemmProb* probs;
+    const int32_t* tile_begin;
+    int nprob;
+    int total_tiles;
+    float alpha_scale;
+    GemmProb single;
+};
 
-template <bool AT, bool BT, bool ABF, bool BBF>
-__global__ __launch_bounds__(NT, 2) void gemm_grouped_kernel(const GemmProb* __restrict__ probs,
-                                                           const int32_t* __restrict__ tile_begin,
-                                                           int nprob, int total_tiles,
-                                                           float alpha_scale) {
-    __shared__ __attribute__((aligned(16))) float smem[smem_floats<AT, BT>()];
-    const int bid = xcd_remap(blockIdx.x, total_tiles);
-    int lo = 0, hi = nprob - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tile_begin[mid] <= bid) lo = mid; else hi = mid - 1;
+template <class C, bool AT, bool BT, bool ABF, bool BBF>
+__global__ __launch_bounds__(C::NT) void gemm_grouped_kernel(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) float smem[C::template smem_floats<AT, BT>()];
+    const int bid = xcd_remap(blockIdx.x, args.total_tiles);
+    GemmProb p;
+    int t = bid;
+    if (args.nprob > 0) {
+        int lo = 0, hi = args.nprob - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (args.tile_begin[mid] <= bid) lo = mid; else hi = mid - 1;
+        }
+        p = args.probs[lo];
+        t = bid - args.tile_begin[lo];
+    } else {
+        p = args.single;
     }
-    const GemmProb p = probs[lo];
     int tm, tn;
-    raster(bid - tile_begin[lo], p.tiles_m, p.tiles_n, tm, tn);
-    gemm_tile<AT, BT, ABF, BBF, false>(p, tm, tn, alpha_scale, smem);
+    raster(t, p.tiles_m, p.tiles_n, tm, tn);
+    gemm_tile<C, AT, BT, ABF, BBF>(p, tm, tn, args.alpha_scale, smem);
 }
 
 template <bool AT, bool BT, bool ABF, bool BBF>
-__global__ __launch_bounds__(NT, 2) void gemm_single_kernel(GemmProb p) {
-    __shared__ __attribute__((aligned(16))) float smem[smem_floats<AT, BT>()];
-    const int total = p.tiles_m * p.tiles_n;
-    const int bid = xcd_remap(blockIdx.x, total);
-    int tm, tn;
-    raster(bid, p.tiles_m, p.tiles_n, tm, tn);
-    gemm_tile<AT, BT, ABF, BBF, false>(p, tm, tn, 1.f, smem);
-}
-
-template <bool AT, bool BT, bool ABF, bool BBF>
-hipError_t grouped(const GemmProb* probs, const int32_t* tile_begin, int nprob, int total,
-                   float alpha_scale, hipStream_t s) {
-    if (total <= 0 || nprob <= 0) return hipSuccess;
-    gemm_grouped_kernel<AT, BT, ABF, BBF><<<dim3(total), dim3(NT), 0, s>>>(probs, tile_begin, nprob,
-                                                                            total, alpha_scale);
-    return hipGetLastError();
-}
-
-template <bool AT, bool BT, bool ABF, bool BBF>
-hipError_t single(const GemmProb& p, hipStream_t s) {
-    const int total = p.tiles_m * p.tiles_n;
-    if (total <= 0) return hipSuccess;
-    gemm_single_kernel<AT, BT, ABF, BBF><<<dim3(total), dim3(NT), 0, s>>>(p);
+hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    if (cfg == 1)
+        gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
+    else
+        gemm_grouped_kernel<SmallCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -437,9 +456,9 @@ hipError_t single(const GemmProb& p, hipStream_t s) {
 //
 // Factorisation (q_mode 0) at panel p: C = Z[k:, k+jb:], Y = Z[k:, k:k+jb].
 // Q formation (q_mode 1): C = X[k:, k:]. W2 (jb x N') comes from qr_reduce.
-__global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restrict__ jobs, QrClasses C,
-                                                        int p, int q_mode) {
-    __shared__ __attribute__((aligned(16))) float smem[smem_floats<false, false>()];
+__global__ __launch_bounds__(QrCfg::NT) void qr_update_kernel(const QrJob* __restrict__ jobs,
+                                                            QrClasses C, int p, int q_mode) {
+    __shared__ __attribute__((aligned(16))) float smem[QrCfg::smem_floats<false, false>()];
     int job, local;
     if (!qr_locate(C, QG_UPDATE, p, q_mode, blockIdx.x, job, local)) return;
     const QrJob J = jobs[job];
@@ -460,22 +479,18 @@ __global__ __launch_bounds__(NT, 2) void qr_update_kernel(const QrJob* __restric
     g.flags = (J.d % 4 == 0) ? (GF_A_VEC | GF_B_VEC) : 0u;
     g.alpha = -1.f;
     g.beta = 1.f;
-    g.tiles_m = (L + BM - 1) / BM;
-    g.tiles_n = (ncols + BN - 1) / BN;
+    g.tiles_m = (L + QrCfg::BM - 1) / QrCfg::BM;
+    g.tiles_n = (ncols + QrCfg::BN - 1) / QrCfg::BN;
     int tm, tn;
     raster(local, g.tiles_m, g.tiles_n, tm, tn);
-    gemm_tile_short_k<true>(g, tm, tn, smem);
+    qr_update_tile(g, tm, tn, smem);
 }
 
 hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
     const int blocks = qr_total_blocks(C, QG_UPDATE, p, q_mode);
     if (blocks <= 0) return hipSuccess;
-    qr_update_kernel<<<dim3(blocks), dim3(NT), 0, s>>>(jobs, C, p, q_mode);
+    qr_update_kernel<<<dim3(blocks), dim3(QrCfg::NT), 0, s>>>(jobs, C, p, q_mode);
     return hipGetLastError();
-}
-
-int gemm_tiles(int64_t M, int64_t N) {
-    return (int)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
 }
 
 #define MATOPT_VARIANTS(X)                                                                         \
@@ -486,25 +501,35 @@ int gemm_tiles(int64_t M, int64_t N) {
     X(12, false, false, true, true) X(13, true, false, true, true) X(14, false, true, true, true)      \
     X(15, true, true, true, true)
 
-hipError_t launch_gemm_grouped(int variant, const GemmProb* probs, const int32_t* tile_begin,
-                               int nprob, int total_tiles, float alpha_scale, hipStream_t s) {
+static hipError_t dispatch(int variant, int cfg, const GemmArgs& a, hipStream_t s) {
     switch (variant) {
 #define X(v, at, bt, abf, bbf) \
-    case v: return grouped<at, bt, abf, bbf>(probs, tile_begin, nprob, total_tiles, alpha_scale, s);
+    case v: return launch<at, bt, abf, bbf>(cfg, a, s);
         MATOPT_VARIANTS(X)
 #undef X
         default: return hipErrorInvalidValue;
     }
 }
 
-hipError_t launch_gemm_single(int variant, const GemmProb& prob, hipStream_t s) {
-    switch (variant) {
-#define X(v, at, bt, abf, bbf) \
-    case v: return single<at, bt, abf, bbf>(prob, s);
-        MATOPT_VARIANTS(X)
-#undef X
-        default: return hipErrorInvalidValue;
-    }
+hipError_t launch_gemm_grouped(int variant, int cfg, const GemmProb* probs, const int32_t* tile_begin,
+                               int nprob, int total_tiles, float alpha_scale, hipStream_t s) {
+    if (nprob <= 0) return hipSuccess;
+    GemmArgs a{};
+    a.probs = probs;
+    a.tile_begin = tile_begin;
+    a.nprob = nprob;
+    a.total_tiles = total_tiles;
+    a.alpha_scale = alpha_scale;
+    return dispatch(variant, cfg, a, s);
+}
+
+hipError_t launch_gemm_single(int variant, int cfg, const GemmProb& prob, hipStream_t s) {
+    GemmArgs a{};
+    a.nprob = 0;
+    a.total_tiles = prob.tiles_m * prob.tiles_n;
+    a.alpha_scale = 1.f;
+    a.single = prob;
+    return dispatch(variant, cfg, a, s);
 }
 
 }  // namespace matopt

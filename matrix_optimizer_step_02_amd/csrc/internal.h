@@ -35,16 +35,26 @@ inline int gemm_variant(bool at, bool bt, bool a_bf16, bool b_bf16) {
     return (at ? 1 : 0) | (bt ? 2 : 0) | (a_bf16 ? 4 : 0) | (b_bf16 ? 8 : 0);
 }
 
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
+// Two tile configurations of the grouped GEMM (rotations, Gram products,
+// opt_gemm): 128x128 outputs per workgroup of 2x2 wavefronts (64x64 each),
+// and 256x256 per workgroup of 2x4 wavefronts (128x64 each), which reuses
+// every staged operand twice as often but needs many tiles to fill the GPU
+// (one workgroup per CU). A launch takes the large tiles when it has at
+// least kGemmLargeMinTiles of them.
+struct GemmTileCfg {
+    int bm, bn;
+};
+constexpr GemmTileCfg kGemmCfgs[2] = {{128, 128}, {256, 256}};
+constexpr int kGemmLargeMinTiles = 512;
 constexpr int kGemmBK = 32;
+constexpr int kQrTile = 128;   // output tile of the QR trailing update
 
 // Grouped launch over `nprob` problems laid out back to back in tile space;
 // tile_begin[p] is the first tile of problem p (ascending, tile_begin[0] = 0).
-hipError_t launch_gemm_grouped(int variant, const GemmProb* probs, const int32_t* tile_begin,
+// `cfg` indexes kGemmCfgs; every problem's tiles_m/tiles_n must use it.
+hipError_t launch_gemm_grouped(int variant, int cfg, const GemmProb* probs, const int32_t* tile_begin,
                                int nprob, int total_tiles, float alpha_scale, hipStream_t s);
-hipError_t launch_gemm_single(int variant, const GemmProb& prob, hipStream_t s);
-int gemm_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_single(int variant, int cfg, const GemmProb& prob, hipStream_t s);
 
 // --------------------------------------------------------- elementwise ----
 
@@ -142,7 +152,7 @@ __host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p, int q_m
     if (ncols <= 0) return 0;
     if (kind == QG_DOTS) return ((ncols + 511) / 512) * qr_splits(L);
     if (kind == QG_REDUCE) return (ncols + 255) / 256;
-    return ((L + kGemmBM - 1) / kGemmBM) * ((ncols + kGemmBN - 1) / kGemmBN);
+    return ((L + kQrTile - 1) / kQrTile) * ((ncols + kQrTile - 1) / kQrTile);
 }
 
 __host__ __device__ inline int qr_total_blocks(const QrClasses& C, int kind, int p, int q_mode) {

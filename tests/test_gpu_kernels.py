@@ -124,3 +124,28 @@ def test_orthonormalize_zero_and_rank_deficient():
     assert np.max(np.abs(Q.T @ Q - np.eye(70))) < 1e-5
     R = Q.T @ Z
     assert np.linalg.norm(np.tril(R, -1)) <= 1e-5 * np.linalg.norm(Z)
+
+
+@pytest.mark.parametrize("ta,tb,b_bf16", [(0, 0, 0), (1, 0, 1), (0, 1, 0)])
+def test_gemm_large_tile_configuration(ta, tb, b_bf16):
+    """A product with >= 512 tiles of 256 x 256 runs on the large-tile kernels;
+    compared on a sample of rows against float64."""
+    torch = _torch()
+    mo = _mo()
+    M, N, K = 5890, 5900, 333
+    g = torch.Generator(device="cuda").manual_seed(11)
+    A = torch.randn(*((K, M) if ta else (M, K)), generator=g, device="cuda")
+    B = torch.randn(*((N, K) if tb else (K, N)), generator=g, device="cuda")
+    if b_bf16:
+        B = B.to(torch.bfloat16)
+    C = torch.randn(M, N, generator=g, device="cuda")
+    C0 = C.clone()
+    mo.native.opt_gemm(ta, tb, M, N, K, 1.5, A.data_ptr(), 0, A.shape[1], B.data_ptr(), b_bf16, B.shape[1],
+                       -0.5, C.data_ptr(), N, mo.stream_ptr())
+    torch.cuda.synchronize()
+    rows = torch.tensor(sorted(set([0, 1, 255, 256, 257, M - 1] + list(range(3, M, 97)))), device="cuda")
+    opA = (A.T if ta else A).double()[rows]
+    opB = (B.T if tb else B).double()
+    ref = 1.5 * (opA @ opB) - 0.5 * C0.double()[rows]
+    bound = 2 * K * 2.0 ** -23 * (1.5 * (opA.abs() @ opB.abs()) + 0.5 * C0.double()[rows].abs())
+    assert float(((C.double()[rows] - ref).abs() / bound).max()) <= 1.0

@@ -101,3 +101,14 @@ def test_identity_bases_is_coordinatewise_adam():
             assert contract.maxrel(b["v"], v[i]) <= 2 ** -22
             assert np.max(np.abs(b["W"] - w[i])) <= 8 * 2 ** -24 * (np.max(np.abs(w[i])) + 10 * wl.lr)
     grp.close()
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_1p7b_full_size_sampled():
+    """The whole Qwen3-1.7B-shaped set (196 matrices, 11 micro-groups, the
+    launch configuration the bench times); gates on the first and last layer's
+    matrices of every shape, at the refresh step t = 1 and the plain step t = 2.
+    Bases of order > 1100 are checked through size-independent properties."""
+    wl = workloads.get("qwen3_1p7b")
+    idx = [i for i, s in enumerate(wl.matrices) if s.layer in (0, 27) and s.name.split(".")[1] in ("q", "k", "up", "down")]
+    _run_gated(wl, 2, {1, 2}, idx)
