@@ -112,3 +112,26 @@ def test_qwen3_1p7b_full_size_sampled():
     wl = workloads.get("qwen3_1p7b")
     idx = [i for i, s in enumerate(wl.matrices) if s.layer in (0, 27) and s.name.split(".")[1] in ("q", "k", "up", "down")]
     _run_gated(wl, 2, {1, 2}, idx)
+
+
+@pytest.mark.timeout(900)
+def test_microgroup_512mib_full_size_sampled():
+    """One exactly-full 512 MiB micro-group of fp32 state with two power
+    iterations per refresh (K = 5): the refresh steps t = 1 and t = 6 and the
+    plain step t = 2, on the largest matrix of each orientation and one of
+    the small ones."""
+    wl = workloads.get("microgroup_512mib")
+    _run_gated(wl, 6, {1, 2, 6}, [0, 2, 6])
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_8b_half_full_size_sampled():
+    """Layers 0-17 of the Qwen3-8B shapes at real size (126 matrices, bf16
+    momentum, anisotropic gradients): gates at the refresh step t = 1 and the
+    plain step t = 2 on the first layer's q, k, down and the last layer's up."""
+    wl = workloads.get("qwen3_8b_half")
+    idx = [i for i, s in enumerate(wl.matrices)
+           if (s.layer == 0 and s.name.split(".")[1] in ("q", "k", "down"))
+           or (s.layer == 17 and s.name.split(".")[1] == "up")]
+    assert len(idx) == 4
+    _run_gated(wl, 2, {1, 2}, idx)
