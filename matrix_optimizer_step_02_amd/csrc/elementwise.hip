@@ -15,6 +15,7 @@
 namespace matopt {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -44,48 +45,73 @@ __device__ __forceinline__ float ema(float b, float x, float omb, float y) {
     return __builtin_fmaf(b, x, omb * y);
 }
 
+constexpr int NQ = kEwPerThread / 4;   // 16-byte groups per thread and tensor
+
+__device__ __forceinline__ f32x4 widen_bf16x4(u32x2 raw) {
+    f32x4 m;
+    m[0] = __uint_as_float(raw.x << 16);
+    m[1] = __uint_as_float(raw.x & 0xffff0000u);
+    m[2] = __uint_as_float(raw.y << 16);
+    m[3] = __uint_as_float(raw.y & 0xffff0000u);
+    return m;
+}
+
+// Full, aligned chunks take the vector path, which issues every load of the
+// thread before the first store (the compiler cannot reorder them itself, as
+// the tensors might alias); a ragged or unaligned chunk goes element by
+// element.
 __global__ __launch_bounds__(kEwThreads) void momentum_kernel(const EwSeg* __restrict__ segs,
                                                               int nseg, float beta1) {
     const int64_t chunk = blockIdx.x;
     const EwSeg S = segs[find_seg(segs, nseg, chunk)];
     const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
     const float omb = 1.f - beta1;
+    gmem<const float> G = gptr(S.a);
+    if (S.vec && base + kEwChunk <= S.n) {
+        f32x4 g[NQ];
 #pragma unroll
-    for (int q = 0; q < kEwPerThread / 4; ++q) {
-        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
-        if (i >= S.n) break;
-        if (S.vec && i + 3 < S.n) {
-            const f32x4 g = *(const f32x4*)(S.a + i);
-            if (S.b_bf16) {
-                uint2 raw = *(const uint2*)((const uint16_t*)S.b + i);
-                f32x4 m;
-                m[0] = __uint_as_float(raw.x << 16);
-                m[1] = __uint_as_float(raw.x & 0xffff0000u);
-                m[2] = __uint_as_float(raw.y << 16);
-                m[3] = __uint_as_float(raw.y & 0xffff0000u);
-                uint16_t o[4];
+        for (int q = 0; q < NQ; ++q)
+            g[q] = *gptr((const f32x4*)(S.a + base + 4 * (q * kEwThreads + threadIdx.x)));
+        if (S.b_bf16) {
+            uint16_t* M = (uint16_t*)S.b + base;
+            u32x2 raw[NQ];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(ema(beta1, m[e], omb, g[e]));
-                uint2 w;
-                w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
-                w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
-                *(uint2*)((uint16_t*)S.b + i) = w;
-            } else {
-                f32x4 m = *(const f32x4*)((const float*)S.b + i);
+            for (int q = 0; q < NQ; ++q) raw[q] = *gptr((const u32x2*)(M + 4 * (q * kEwThreads + threadIdx.x)));
 #pragma unroll
-                for (int e = 0; e < 4; ++e) m[e] = ema(beta1, m[e], omb, g[e]);
-                *(f32x4*)((float*)S.b + i) = m;
+            for (int q = 0; q < NQ; ++q) {
+                const f32x4 m = widen_bf16x4(raw[q]);
+                uint32_t o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = f32_to_bf16(ema(beta1, m[e], omb, g[q][e]));
+                u32x2 w;
+                w.x = o[0] | (o[1] << 16);
+                w.y = o[2] | (o[3] << 16);
+                *gptr((u32x2*)(M + 4 * (q * kEwThreads + threadIdx.x))) = w;
             }
         } else {
-            for (int e = 0; e < 4 && i + e < S.n; ++e) {
-                const float g = S.a[i + e];
-                if (S.b_bf16) {
-                    uint16_t* p = (uint16_t*)S.b + i + e;
-                    *p = f32_to_bf16(ema(beta1, bf16_to_f32(*p), omb, g));
-                } else {
-                    float* p = (float*)S.b + i + e;
-                    *p = ema(beta1, *p, omb, g);
-                }
+            float* M = (float*)S.b + base;
+            f32x4 m[NQ];
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) m[q] = *gptr((const f32x4*)(M + 4 * (q * kEwThreads + threadIdx.x)));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[q][e] = ema(beta1, m[q][e], omb, g[q][e]);
+                *gptr((f32x4*)(M + 4 * (q * kEwThreads + threadIdx.x))) = m[q];
+            }
+        }
+        return;
+    }
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
+        for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            const float g = G[i + e];
+            if (S.b_bf16) {
+                gmem<uint16_t> p = gptr((uint16_t*)S.b + i + e);
+                *p = f32_to_bf16(ema(beta1, bf16_to_f32(*p), omb, g));
+            } else {
+                gmem<float> p = gptr((float*)S.b + i + e);
+                *p = ema(beta1, *p, omb, g);
             }
         }
     }
@@ -104,32 +130,44 @@ __global__ __launch_bounds__(kEwThreads) void rotated_adam_kernel(const EwSeg* _
     const EwSeg S = segs[find_seg(segs, nseg, chunk)];
     const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
     const float omb2 = 1.f - beta2;
-    float* mu = (float*)S.b;
+    if (S.vec && base + kEwChunk <= S.n) {
+        const float* Gt = S.a + base;
+        float* mu = (float*)S.b + base;
+        float* V = S.c + base;
+        f32x4 g[NQ], m[NQ], v[NQ];
 #pragma unroll
-    for (int q = 0; q < kEwPerThread / 4; ++q) {
-        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
-        if (i >= S.n) break;
-        if (S.vec && i + 3 < S.n) {
-            const f32x4 g = *(const f32x4*)(S.a + i);
-            const f32x4 m = *(const f32x4*)(mu + i);
-            const f32x4 v0 = *(const f32x4*)(S.c + i);
-            f32x4 v, u;
+        for (int q = 0; q < NQ; ++q) {
+            const int o = 4 * (q * kEwThreads + threadIdx.x);
+            g[q] = *gptr((const f32x4*)(Gt + o));
+            m[q] = *gptr((const f32x4*)(mu + o));
+            v[q] = *gptr((const f32x4*)(V + o));
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int o = 4 * (q * kEwThreads + threadIdx.x);
+            f32x4 u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float ve = v0[e], ue;
-                adam1(g[e], m[e], ve, ue, beta2, omb2, eps);
-                v[e] = ve;
+                float ve = v[q][e], ue;
+                adam1(g[q][e], m[q][e], ve, ue, beta2, omb2, eps);
+                v[q][e] = ve;
                 u[e] = ue;
             }
-            *(f32x4*)(S.c + i) = v;
-            *(f32x4*)(mu + i) = u;
-        } else {
-            for (int e = 0; e < 4 && i + e < S.n; ++e) {
-                float v = S.c[i + e], u;
-                adam1(S.a[i + e], mu[i + e], v, u, beta2, omb2, eps);
-                S.c[i + e] = v;
-                mu[i + e] = u;
-            }
+            *gptr((f32x4*)(V + o)) = v[q];
+            *gptr((f32x4*)(mu + o)) = u;
+        }
+        return;
+    }
+    gmem<const float> Gt = gptr(S.a);
+    gmem<float> mu = gptr((float*)S.b);
+    gmem<float> V = gptr(S.c);
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
+        for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            float v = V[i + e], u;
+            adam1(Gt[i + e], mu[i + e], v, u, beta2, omb2, eps);
+            V[i + e] = v;
+            mu[i + e] = u;
         }
     }
 }

@@ -37,6 +37,7 @@
 namespace matopt {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
@@ -78,40 +79,60 @@ static_assert(LargeCfg::BM == kGemmCfgs[1].bm && LargeCfg::BN == kGemmCfgs[1].bn
 using QrCfg = Cfg<2, 2, 2, 2>;
 static_assert(QrCfg::BM == kQrTile && QrCfg::BN == kQrTile, "QR tile size mismatch");
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-    return __uint_as_float(((uint32_t)h) << 16);
-}
+// Four consecutive elements (row, col..col+3) of a row-major stored matrix,
+// as loaded: fp32 values, or the raw bits of bf16 values. They are widened and
+// masked only when stored to LDS, after the current slab's MFMAs, so that the
+// load latency of slab k+1 overlaps the MFMAs of slab k.
+template <bool BF16> struct Raw4 { f32x4 v; };
+template <> struct Raw4<true> { u32x2 v; };
 
-// Four consecutive elements (row, col..col+3) of a row-major stored matrix
-// with `rows` x `cols` valid elements, zero outside. The address is clamped
-// into the valid region so that every lane issues a load (no divergent
-// branches); the mask then zeroes what lies outside. With VEC the load is one
-// 16-byte (fp32) or 8-byte (bf16) access, which needs ld % 4 == 0,
-// cols % 4 == 0 and an aligned base (so a clamped group never leaves the row).
+// The address is clamped into the valid `rows` x `cols` region so that every
+// lane issues a load at a valid address (no divergent branches); the values
+// outside are zeroed at the store. With VEC the load is one 16-byte (fp32) or
+// 8-byte (bf16) access, which needs ld % 4 == 0, cols % 4 == 0 and an aligned
+// base (so a clamped group never leaves the row).
 template <bool BF16>
-__device__ __forceinline__ f32x4 load4(const void* base, int64_t ld, int row, int col, int rows,
-                                       int cols, bool vec) {
+__device__ __forceinline__ Raw4<BF16> load4(const void* base, int64_t ld, int row, int col, int rows,
+                                            int cols, bool vec) {
     const int64_t rc = row < rows ? row : rows - 1;
-    f32x4 v;
+    Raw4<BF16> r;
     if (vec) {
         const int last = (cols - 1) & ~3;
         const int64_t off = rc * ld + (col < last ? col : last);
-        if (BF16) {
-            const uint2 u = *(const uint2*)((const uint16_t*)base + off);
-            v[0] = __uint_as_float(u.x << 16);
-            v[1] = __uint_as_float(u.x & 0xffff0000u);
-            v[2] = __uint_as_float(u.y << 16);
-            v[3] = __uint_as_float(u.y & 0xffff0000u);
-        } else {
-            v = *(const f32x4*)((const float*)base + off);
-        }
+        if constexpr (BF16) r.v = *gptr((const u32x2*)((const uint16_t*)base + off));
+        else                r.v = *gptr((const f32x4*)((const float*)base + off));
     } else {
+        if constexpr (BF16) {
+            uint32_t h[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ce = col + e < cols ? col + e : cols - 1;
-            if (BF16) v[e] = bf16_to_f32(((const uint16_t*)base)[rc * ld + ce]);
-            else      v[e] = ((const float*)base)[rc * ld + ce];
+            for (int e = 0; e < 4; ++e) {
+                const int ce = col + e < cols ? col + e : cols - 1;
+                h[e] = gptr((const uint16_t*)base)[rc * ld + ce];
+            }
+            r.v.x = h[0] | (h[1] << 16);
+            r.v.y = h[2] | (h[3] << 16);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ce = col + e < cols ? col + e : cols - 1;
+                r.v[e] = gptr((const float*)base)[rc * ld + ce];
+            }
         }
+    }
+    return r;
+}
+
+// Widen to fp32 and zero the elements outside the valid region.
+template <bool BF16>
+__device__ __forceinline__ f32x4 finish4(const Raw4<BF16>& r, int row, int col, int rows, int cols) {
+    f32x4 v;
+    if constexpr (BF16) {
+        v[0] = __uint_as_float(r.v.x << 16);
+        v[1] = __uint_as_float(r.v.x & 0xffff0000u);
+        v[2] = __uint_as_float(r.v.y << 16);
+        v[3] = __uint_as_float(r.v.y & 0xffff0000u);
+    } else {
+        v = r.v;
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -119,77 +140,75 @@ __device__ __forceinline__ f32x4 load4(const void* base, int64_t ld, int row, in
     return v;
 }
 
-template <class C, bool AT, bool ABF, bool UL>
-__device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, f32x4 (&r)[C::QA]) {
+// Element coordinates of the q-th float4 a thread moves in a slab: for an
+// operand kept k-major (A stored K x M, B stored K x N) the slab rows are k
+// with W/4 float4 per row; otherwise the slab rows are m (or n) with 8 float4
+// per row of 32 k values.
+template <class C, bool KMAJOR, int W>
+__device__ __forceinline__ void slab_pos(int q, int& rr, int& c4) {
+    const int f = threadIdx.x + C::NT * q;
+    if (KMAJOR) { rr = f / (W / 4); c4 = f % (W / 4); }
+    else        { rr = f >> 3;      c4 = f & 7; }
+}
+
+template <class C, bool AT, bool ABF>
+__device__ __forceinline__ void load_a(const GemmProb& p, int m0, int k0, Raw4<ABF> (&r)[C::QA]) {
     const bool vec = p.flags & GF_A_VEC;
-    const int tid = threadIdx.x;
 #pragma unroll
     for (int q = 0; q < C::QA; ++q) {
-        const int f = tid + C::NT * q;
-        if (AT) {  // stored K x M: slab rows are k, BM/4 float4 per row
-            const int rr = f / (C::BM / 4), c4 = f % (C::BM / 4);
-            r[q] = load4<ABF>(p.A, p.lda, k0 + rr, m0 + 4 * c4, p.K, p.M, vec);
-        } else {   // stored M x K: slab rows are m, 8 float4 per row of 32
-            const int rr = f >> 3, c4 = f & 7;
+        int rr, c4;
+        slab_pos<C, AT, C::BM>(q, rr, c4);
+        if (AT) r[q] = load4<ABF>(p.A, p.lda, k0 + rr, m0 + 4 * c4, p.K, p.M, vec);
+        else    r[q] = load4<ABF>(p.A, p.lda, m0 + rr, k0 + 4 * c4, p.M, p.K, vec);
+    }
+}
+
+template <class C, bool BT, bool BBF>
+__device__ __forceinline__ void load_b(const GemmProb& p, int n0, int k0, Raw4<BBF> (&r)[C::QB]) {
+    const bool vec = p.flags & GF_B_VEC;
+#pragma unroll
+    for (int q = 0; q < C::QB; ++q) {
+        int rr, c4;
+        slab_pos<C, !BT, C::BN>(q, rr, c4);
+        if (BT) r[q] = load4<BBF>(p.B, p.ldb, n0 + rr, k0 + 4 * c4, p.N, p.K, vec);
+        else    r[q] = load4<BBF>(p.B, p.ldb, k0 + rr, n0 + 4 * c4, p.K, p.N, vec);
+    }
+}
+
+// UL: A is read as unit lower trapezoidal (ones on the diagonal, zeros above).
+template <class C, bool AT, bool ABF, bool UL>
+__device__ __forceinline__ void store_a(float* As, const Raw4<ABF> (&r)[C::QA], const GemmProb& p, int m0,
+                                        int k0) {
+#pragma unroll
+    for (int q = 0; q < C::QA; ++q) {
+        int rr, c4;
+        slab_pos<C, AT, C::BM>(q, rr, c4);
+        if (AT) {
+            *(f32x4*)&As[rr * C::BM + 4 * c4] = finish4<ABF>(r[q], k0 + rr, m0 + 4 * c4, p.K, p.M);
+        } else {
             const int row = m0 + rr, col = k0 + 4 * c4;
-            r[q] = load4<ABF>(p.A, p.lda, row, col, p.M, p.K, vec);
+            f32x4 v = finish4<ABF>(r[q], row, col, p.M, p.K);
             if (UL) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    if (row < col + e) r[q][e] = 0.f;
-                    else if (row == col + e) r[q][e] = 1.f;
+                    if (row < col + e) v[e] = 0.f;
+                    else if (row == col + e) v[e] = 1.f;
                 }
             }
+            *(f32x4*)&As[rr * KPAD + 4 * c4] = v;
         }
     }
 }
 
 template <class C, bool BT, bool BBF>
-__device__ __forceinline__ void load_b(const GemmProb& p, int n0, int k0, f32x4 (&r)[C::QB]) {
-    const bool vec = p.flags & GF_B_VEC;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void store_b(float* Bs, const Raw4<BBF> (&r)[C::QB], const GemmProb& p, int n0,
+                                        int k0) {
 #pragma unroll
     for (int q = 0; q < C::QB; ++q) {
-        const int f = tid + C::NT * q;
-        if (BT) {  // stored N x K
-            const int rr = f >> 3, c4 = f & 7;
-            r[q] = load4<BBF>(p.B, p.ldb, n0 + rr, k0 + 4 * c4, p.N, p.K, vec);
-        } else {   // stored K x N
-            const int rr = f / (C::BN / 4), c4 = f % (C::BN / 4);
-            r[q] = load4<BBF>(p.B, p.ldb, k0 + rr, n0 + 4 * c4, p.K, p.N, vec);
-        }
-    }
-}
-
-template <class C, bool AT>
-__device__ __forceinline__ void store_a(float* As, const f32x4 (&r)[C::QA]) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int q = 0; q < C::QA; ++q) {
-        const int f = tid + C::NT * q;
-        if (AT) {
-            const int rr = f / (C::BM / 4), c4 = f % (C::BM / 4);
-            *(f32x4*)&As[rr * C::BM + 4 * c4] = r[q];
-        } else {
-            const int rr = f >> 3, c4 = f & 7;
-            *(f32x4*)&As[rr * KPAD + 4 * c4] = r[q];
-        }
-    }
-}
-
-template <class C, bool BT>
-__device__ __forceinline__ void store_b(float* Bs, const f32x4 (&r)[C::QB]) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int q = 0; q < C::QB; ++q) {
-        const int f = tid + C::NT * q;
-        if (BT) {
-            const int rr = f >> 3, c4 = f & 7;
-            *(f32x4*)&Bs[rr * KPAD + 4 * c4] = r[q];
-        } else {
-            const int rr = f / (C::BN / 4), c4 = f % (C::BN / 4);
-            *(f32x4*)&Bs[rr * C::BN + 4 * c4] = r[q];
-        }
+        int rr, c4;
+        slab_pos<C, !BT, C::BN>(q, rr, c4);
+        if (BT) *(f32x4*)&Bs[rr * KPAD + 4 * c4] = finish4<BBF>(r[q], n0 + rr, k0 + 4 * c4, p.N, p.K);
+        else    *(f32x4*)&Bs[rr * C::BN + 4 * c4] = finish4<BBF>(r[q], k0 + rr, n0 + 4 * c4, p.K, p.N);
     }
 }
 
@@ -262,7 +281,7 @@ __device__ __forceinline__ void epilogue(const GemmProb& p, int m0, int n0, int 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    cold[j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+                    cold[j][r] = (row < p.M && col < p.N) ? gptr(p.C)[(int64_t)row * p.ldc + col] : 0.f;
                 }
             }
         }
@@ -276,7 +295,7 @@ __device__ __forceinline__ void epilogue(const GemmProb& p, int m0, int n0, int 
                 if (row < p.M) {
                     float val = alpha * acc.v[i][j][r];
                     if (beta != 0.f) val += beta * cold[j][r];
-                    p.C[(int64_t)row * p.ldc + col] = val;
+                    gptr(p.C)[(int64_t)row * p.ldc + col] = val;
                 }
             }
         }
@@ -298,26 +317,26 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     Acc<C> acc;
     acc.zero();
     const int nk = (p.K + BK - 1) / BK;
-    f32x4 ra[C::QA], rb[C::QB];
+    Raw4<ABF> ra[C::QA];
+    Raw4<BBF> rb[C::QB];
     if (nk > 0) {
-        load_a<C, AT, ABF, false>(p, m0, 0, ra);
+        load_a<C, AT, ABF>(p, m0, 0, ra);
         load_b<C, BT, BBF>(p, n0, 0, rb);
-        store_a<C, AT>(smem, ra);
-        store_b<C, BT>(smem + 2 * AS, rb);
+        store_a<C, AT, ABF, false>(smem, ra, p, m0, 0);
+        store_b<C, BT, BBF>(smem + 2 * AS, rb, p, n0, 0);
     }
     __syncthreads();
+    // The loads of slab kt+1 are issued unconditionally: past the last slab
+    // they read clamped, valid addresses and fill the idle buffer with zeros,
+    // which keeps the slab body one basic block.
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            load_a<C, AT, ABF, false>(p, m0, (kt + 1) * BK, ra);
-            load_b<C, BT, BBF>(p, n0, (kt + 1) * BK, rb);
-        }
+        const int k1 = (kt + 1) * BK;
+        load_a<C, AT, ABF>(p, m0, k1, ra);
+        load_b<C, BT, BBF>(p, n0, k1, rb);
         mma_slab<C, AT, BT>(smem + cur * AS, smem + 2 * AS + cur * BS, wm, wn, lane, acc);
-        if (more) {
-            store_a<C, AT>(smem + (cur ^ 1) * AS, ra);
-            store_b<C, BT>(smem + 2 * AS + (cur ^ 1) * BS, rb);
-        }
+        store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
+        store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
         __syncthreads();
     }
     epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
@@ -342,16 +361,16 @@ __device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn
     const int m0 = tm * C::BM, n0 = tn * C::BN;
     const int nk = (p.K + BK - 1) / BK;
     {
-        f32x4 ra[C::QA], rb[C::QB];
-        load_a<C, false, false, true>(p, m0, 0, ra);
+        Raw4<false> ra[C::QA], rb[C::QB];
+        load_a<C, false, false>(p, m0, 0, ra);
         load_b<C, false, false>(p, n0, 0, rb);
-        store_a<C, false>(As0, ra);
-        store_b<C, false>(Bs0, rb);
+        store_a<C, false, false, true>(As0, ra, p, m0, 0);
+        store_b<C, false, false>(Bs0, rb, p, n0, 0);
         if (nk > 1) {
-            load_a<C, false, false, true>(p, m0, BK, ra);
+            load_a<C, false, false>(p, m0, BK, ra);
             load_b<C, false, false>(p, n0, BK, rb);
-            store_a<C, false>(As1, ra);
-            store_b<C, false>(Bs1, rb);
+            store_a<C, false, false, true>(As1, ra, p, m0, BK);
+            store_b<C, false, false>(Bs1, rb, p, n0, BK);
         }
     }
     __syncthreads();
@@ -365,7 +384,7 @@ __device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                cold[i][j][r] = (row < p.M && col < p.N) ? p.C[(int64_t)row * p.ldc + col] : 0.f;
+                cold[i][j][r] = (row < p.M && col < p.N) ? gptr(p.C)[(int64_t)row * p.ldc + col] : 0.f;
             }
         }
     Acc<C> acc;
@@ -381,7 +400,7 @@ __device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row < p.M) p.C[(int64_t)row * p.ldc + col] = p.alpha * acc.v[i][j][r] + p.beta * cold[i][j][r];
+                if (row < p.M) gptr(p.C)[(int64_t)row * p.ldc + col] = p.alpha * acc.v[i][j][r] + p.beta * cold[i][j][r];
             }
         }
 }

@@ -6,7 +6,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "matopt.h"
+
 namespace matopt {
+
+// Records the error text returned by opt_last_error() and passes st through.
+opt_status fail(opt_status st, const char* fmt, ...);
+
+// Pointers into device memory, as the global address space. Accesses through
+// a generic pointer compile to flat instructions, which the hardware counts
+// against both the vector-memory and the LDS counters, so every wait for an
+// LDS read would also wait for the outstanding global loads; accesses
+// through these compile to global instructions, counted against vmcnt only.
+template <class T> using gmem = __attribute__((address_space(1))) T*;
+template <class T> __device__ __forceinline__ gmem<T> gptr(T* p) { return (gmem<T>)p; }
 
 // ---------------------------------------------------------------- GEMM ----
 

@@ -116,7 +116,7 @@ __device__ __forceinline__ float block_value(const PanelShared& sh, int slot, in
 }
 
 struct PanelCtx {
-    float* A;     // top-left of the panel (row k, column k of Z)
+    gmem<float> A;   // top-left of the panel (row k, column k of Z)
     int64_t ld;
     int L;        // rows of the panel
     int jb;       // columns of the panel
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
     if (k >= Jb.d) return;
     PanelCtx c;
     c.ld = Jb.d;
-    c.A = Jb.Z + (int64_t)k * c.ld + k;
+    c.A = gptr(Jb.Z + (int64_t)k * c.ld + k);
     c.L = Jb.d - k;
     c.jb = min(PB, Jb.d - k);
     const int tid = threadIdx.x;
@@ -400,7 +400,7 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
         }
     }
     __syncthreads();
-    float* Tout = Jb.T + (int64_t)p * PB * PB;
+    gmem<float> Tout = gptr(Jb.T + (int64_t)p * PB * PB);
     for (int e = tid; e < PB * PB; e += PT) Tout[e] = sh.Tf[e / PB][e % PB];
 }
 
@@ -425,8 +425,8 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
     const int j0 = (local % nxb) * 512 + wave * 128;
     if (j0 >= ncols) return;
     const int r0 = s * kc, r1 = min(L, r0 + kc);
-    const float* Y = Jb.Z + (int64_t)k * d + k;
-    const float* C = q_mode ? Jb.X + (int64_t)k * d + k : Jb.Z + (int64_t)k * d + k + jb;
+    gmem<const float> Y = gptr((const float*)Jb.Z + (int64_t)k * d + k);
+    gmem<const float> C = gptr((const float*)(q_mode ? Jb.X + (int64_t)k * d + k : Jb.Z + (int64_t)k * d + k + jb));
 
     f32x16 acc[NB][4];
 #pragma unroll
@@ -471,7 +471,7 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u][a], x[u][b], acc[a][b], 0, 0, 0);
     }
 
-    float* part = Jb.part + (int64_t)s * PB * d;
+    gmem<float> part = gptr(Jb.part + (int64_t)s * PB * d);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int j = j0 + 32 * b + l32;
@@ -497,7 +497,7 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
     const int d = Jb.d;
     const int jb = min(PB, d - k), L = d - k;
     const int ncols = q_mode ? L : L - jb;
-    const float* Tp = Jb.T + (int64_t)p * PB * PB;
+    gmem<const float> Tp = gptr((const float*)Jb.T + (int64_t)p * PB * PB);
     for (int e = threadIdx.x; e < PB * PB; e += 256) Ts[e / PB][e % PB] = Tp[e];
     __syncthreads();
     const int j = local * 256 + threadIdx.x;
@@ -507,16 +507,18 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
 #pragma unroll
     for (int c = 0; c < PB; ++c) w[c] = 0.f;
     for (int s = 0; s < splits; ++s) {
-        const float* part = Jb.part + (int64_t)s * PB * d + j;
+        gmem<const float> part = gptr((const float*)Jb.part + (int64_t)s * PB * d + j);
 #pragma unroll
         for (int c = 0; c < PB; ++c) w[c] += part[(int64_t)c * d];
     }
-#pragma unroll
+    // c stays a rolled loop: unrolled, the compiler hoists all PB*PB LDS reads
+    // of T ahead of the products and spills.
+#pragma unroll 1
     for (int c = 0; c < PB; ++c) {
         float acc = 0.f;
 #pragma unroll
         for (int l = 0; l < PB; ++l) acc += (q_mode ? Ts[c][l] : Ts[l][c]) * w[l];
-        Jb.W2[(int64_t)c * d + j] = acc;
+        gptr(Jb.W2)[(int64_t)c * d + j] = acc;
     }
 }
 
@@ -530,8 +532,8 @@ __global__ __launch_bounds__(256) void qr_init_q_kernel(const QrJob* __restrict_
         if (e >= d * d) break;
         const int64_t i = e / d, j = e - i * d;
         float val = 0.f;
-        if (i == j) val = Jb.Z[i * d + i] < 0.f ? -1.f : 1.f;
-        Jb.X[e] = val;
+        if (i == j) val = gptr(Jb.Z)[i * d + i] < 0.f ? -1.f : 1.f;
+        gptr(Jb.X)[e] = val;
     }
 }
 
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(256) void copy_cols_kernel(const CopyJob* __restric
     const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= d * w) return;
     const int64_t i = e / w, j = J.c0 + (e - i * w);
-    J.dst[i * d + j] = J.src[i * d + j];
+    gptr(J.dst)[i * d + j] = gptr(J.src)[i * d + j];
 }
 
 }  // namespace
