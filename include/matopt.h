@@ -181,6 +181,48 @@ opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes);
 opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
                               uint64_t workspace_bytes, void* stream);
 
+/* ---- cross-rank planners (host only; no device memory, no stream) -------
+ * A job that shards its matrices over several ranks plans once, on the host,
+ * which rank steps which whole matrix; each rank then runs a group over its
+ * share. Costs are the caller's (e.g. flops per step: 6 m n (m + n) for the
+ * rotations plus the amortised refresh). Every floating-point sum is taken
+ * left to right in the order described, so the integer results are
+ * reproducible across implementations. */
+
+/* Alpha-balanced greedy LPT partition of data-parallel buckets over `ranks`
+ * ranks (the Canzona page, section 3.2.1, with the geometric alignment of
+ * section 4.2). Parameter i has cost cost[i] >= 0 (finite); bucket b holds the
+ * consecutive parameters bucket_begin[b] .. bucket_begin[b+1]-1
+ * (bucket_begin has nbuckets + 1 non-decreasing entries, from 0 to nparams).
+ * Buckets are placed by decreasing total cost W_b (ties in input order). For
+ * each bucket, with L_r the rank loads so far and T = (sum_r L_r + W_b) /
+ * ranks the mean after it, the target share of rank r is
+ * (1 - alpha) / ranks + alpha * max(0, T - L_r) / sum_s max(0, T - L_s)
+ * (1 / ranks when that sum is 0). The bucket is cut into `ranks` consecutive
+ * ranges, rank 0 first, only at parameter boundaries: boundary r (1 <= r <
+ * ranks) is the prefix of the bucket whose cost is nearest to W_b times the
+ * summed shares of ranks < r, searched from the previous boundary on, ties to
+ * the shorter prefix. Ranges may be empty. Outputs: owner[i] (nparams
+ * entries) and, if not NULL, load[r] (ranks entries), the summed cost of
+ * each rank's parameters. 0 <= alpha <= 1; ranks >= 1. */
+opt_status opt_partition_dp(const double* cost, int64_t nparams, const int64_t* bucket_begin,
+                            int32_t nbuckets, int32_t ranks, double alpha, int32_t* owner,
+                            double* load);
+
+/* Micro-groups with host ranks for tensor-parallel matrices (the Canzona
+ * page, section 3.2.2): parameters sorted by decreasing cost (ties in input
+ * order) are added in turn to the current micro-group; when the group's
+ * summed bytes would exceed `capacity_bytes` (0 selects 512 MiB) a new group
+ * is opened first (a parameter larger than the capacity forms a group alone).
+ * Inside a group each parameter goes to the host rank with the least cost
+ * assigned in that group so far (a min-heap over the ranks; ties to the
+ * lowest rank). Outputs (n entries each, any may be NULL): order[k], the
+ * input index of the k-th parameter in that order; group_of[i]; host_of[i];
+ * *num_groups. ranks >= 1; cost[i] >= 0 finite. */
+opt_status opt_plan_host_ranks(const double* cost, const uint64_t* bytes, int64_t n, int32_t ranks,
+                               uint64_t capacity_bytes, int32_t* order, int32_t* group_of,
+                               int32_t* host_of, int32_t* num_groups);
+
 #ifdef __cplusplus
 }
 #endif

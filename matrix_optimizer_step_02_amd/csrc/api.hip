@@ -34,10 +34,10 @@
 using namespace matopt;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-opt_status fail(opt_status st, const char* fmt, ...) {
+opt_status matopt::fail(opt_status st, const char* fmt, ...) {
     char buf[512];
     va_list ap;
     va_start(ap, fmt);
@@ -46,6 +46,8 @@ opt_status fail(opt_status st, const char* fmt, ...) {
     g_err = buf;
     return st;
 }
+
+namespace {
 
 opt_status hip_fail(hipError_t e, const char* where) {
     return fail(OPT_EHIP, "%s: %s", where, hipGetErrorString(e));

@@ -25,6 +25,7 @@ EXPORTED = (
     "opt_group_get_step", "opt_group_set_step", "opt_group_set_lr", "opt_plan",
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
     "opt_gemm", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
+    "opt_partition_dp", "opt_plan_host_ranks",
 )
 
 
@@ -81,6 +82,10 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "opt_gemm": ([i32, i32, i64, i64, i64, f32, vp, i32, i64, vp, i32, i64, f32, vp, i64, vp], i32),
         "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
         "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
+        "opt_partition_dp": ([C.POINTER(C.c_double), i64, C.POINTER(i64), i32, i32, C.c_double,
+                              C.POINTER(i32), C.POINTER(C.c_double)], i32),
+        "opt_plan_host_ranks": ([C.POINTER(C.c_double), C.POINTER(u64), i64, i32, u64, C.POINTER(i32),
+                                 C.POINTER(i32), C.POINTER(i32), C.POINTER(i32)], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -184,3 +189,28 @@ def opt_orthonormalize_workspace_size(d: int) -> int:
 def opt_orthonormalize(Z: int, Q: int, d: int, workspace: int, workspace_bytes: int, stream_ptr: int):
     _check(load().opt_orthonormalize(C.c_void_p(Z), C.c_void_p(Q), d, C.c_void_p(workspace),
                                      workspace_bytes, C.c_void_p(stream_ptr)))
+
+
+def opt_partition_dp(cost: Sequence[float], bucket_begin: Sequence[int], ranks: int, alpha: float):
+    """Returns (owner per parameter, load per rank)."""
+    n, nb = len(cost), len(bucket_begin) - 1
+    c = (C.c_double * max(n, 1))(*cost)
+    bb = (C.c_int64 * len(bucket_begin))(*bucket_begin)
+    owner = (C.c_int32 * max(n, 1))()
+    loads = (C.c_double * ranks)()
+    _check(load().opt_partition_dp(c, n, bb, nb, ranks, alpha, owner, loads))
+    return list(owner)[:n], list(loads)
+
+
+def opt_plan_host_ranks(cost: Sequence[float], nbytes: Sequence[int], ranks: int, capacity_bytes: int):
+    """Returns (order, group_of, host_of, num_groups)."""
+    n = len(cost)
+    c = (C.c_double * max(n, 1))(*cost)
+    b = (C.c_uint64 * max(n, 1))(*nbytes)
+    order = (C.c_int32 * max(n, 1))()
+    group_of = (C.c_int32 * max(n, 1))()
+    host_of = (C.c_int32 * max(n, 1))()
+    ng = C.c_int32(0)
+    _check(load().opt_plan_host_ranks(c, b, n, ranks, capacity_bytes, order, group_of, host_of,
+                                          C.byref(ng)))
+    return list(order)[:n], list(group_of)[:n], list(host_of)[:n], ng.value

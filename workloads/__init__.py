@@ -162,6 +162,25 @@ def qwen3_8b_half() -> Workload:
                     grad_kind="row_col_scaled", grad_std=1e-3)
 
 
+# Whole-model matrix lists for the cross-rank planners: every matrix of every
+# layer, in model order, with one data-parallel bucket per layer (a layer of
+# these models holds 48 M (1.7B) or 193 M (8B) parameters, above a typical
+# 40 M-parameter gradient bucket, so a bucket never spans two layers).
+PLANNING_MODELS = {
+    "qwen3_1p7b": (2048, 1024, 6144, 28),
+    "qwen3_8b": (4096, 1024, 12288, 36),
+}
+
+
+def planning_set(model: str):
+    """(matrices, bucket_begin) of a whole model; bucket b holds matrices
+    bucket_begin[b] .. bucket_begin[b+1]-1."""
+    hidden, kv, ffn, layers = PLANNING_MODELS[model]
+    mats = _qwen_like(hidden, kv, ffn, layers)
+    per_layer = len(mats) // layers
+    return mats, [per_layer * l for l in range(layers + 1)]
+
+
 WORKLOADS = {
     "tiny": tiny,
     "layer": layer,
