@@ -10,19 +10,29 @@
 // (32 BLK_M) x (32 BLK_N) block of the output held as BLK_M x BLK_N MFMA
 // accumulators, and the workgroup WAVES_M x WAVES_N wavefronts. K advances in
 // slabs of 32 staged through LDS with two buffers, so one barrier per slab
-// separates the store of slab k+1 from the reads of slab k; the global loads
-// of slab k+1 are issued before the MFMAs of slab k.
+// separates the fill of slab k+1 from the reads of slab k.
 //
-// LDS layouts keep every MFMA operand read conflict-free:
+// Operand staging. An fp32 operand goes from global memory straight into LDS
+// (global_load_lds: each wavefront instruction writes 64 lanes x 16 bytes to
+// one contiguous kilobyte of LDS, in lane order), so it takes no registers and
+// no LDS store instructions; the fill of slab k+1 is issued before the MFMAs
+// of slab k. Addresses are clamped into the operand, so rows and columns past
+// the edge hold copies of valid data that only reach outputs that are never
+// stored; k values past K are zeroed in LDS afterwards (only a last, partial
+// slab has any). A bf16 operand is loaded into registers, widened and masked,
+// and stored to the same LDS layout after the MFMAs.
+//
+// LDS layouts, unpadded, with every MFMA operand read conflict-free:
 //  * an operand whose non-k index is contiguous in memory (A stored K x M,
 //    B stored K x N) is kept k-major, [32][BM or BN], read 4 bytes per lane
 //    with 32 consecutive lanes on consecutive words;
 //  * an operand whose k index is contiguous (A stored M x K, B stored N x K)
-//    is kept [BM or BN][32 + 4], read 16 bytes per lane. Within a group of 8
-//    k values, MFMA s (0..3) takes k = 8g + s from lanes 0..31 and
-//    k = 8g + 4 + s from lanes 32..63, so one 16-byte read feeds four MFMAs;
-//    the row pitch of 36 words puts 8 consecutive rows on 8 distinct 4-bank
-//    groups.
+//    is kept [BM or BN][32], read 16 bytes per lane. Within a group of 8 k
+//    values, MFMA s (0..3) takes k = 8g + s from lanes 0..31 and k = 8g + 4 + s
+//    from lanes 32..63, so one 16-byte read feeds four MFMAs. The 16-byte
+//    group q of row r is stored at slot q ^ swz(r), swz(r) = (r + r/8) mod 8,
+//    which puts any 8 aligned consecutive rows, and the rows of one parity
+//    among any 16 aligned consecutive rows, on distinct slots.
 // The same k assignment is used for both operands, so the sum is unchanged.
 //
 // Work distribution: one workgroup per output tile; problems of a grouped
@@ -43,7 +53,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 namespace {
 
 constexpr int BK = kGemmBK;
-constexpr int KPAD = BK + 4;   // pitch of k-contiguous LDS rows
+static_assert(BK == 32, "the LDS layouts assume 32-deep slabs (8 groups of 4 k values per row)");
 #ifndef MATOPT_XCD_RUN
 #define MATOPT_XCD_RUN 16
 #endif
@@ -62,12 +72,14 @@ struct Cfg {
     static constexpr int BN = 32 * BLK_N * WAVES_N;
     static constexpr int QA = BM * BK / 4 / NT;   // float4 loads of A per thread per slab
     static constexpr int QB = BN * BK / 4 / NT;
-    template <bool AT> static constexpr int a_size() { return AT ? BK * BM : BM * KPAD; }
-    template <bool BT> static constexpr int b_size() { return BT ? BN * KPAD : BK * BN; }
-    template <bool AT, bool BT> static constexpr int smem_floats() {
-        return 2 * (a_size<AT>() + b_size<BT>());
-    }
+    static constexpr int AS = BM * BK;   // floats of one A buffer (either layout)
+    static constexpr int BS = BN * BK;
+    static constexpr int SMEM = 2 * (AS + BS);
+    static constexpr int NW = NT / 64;
+    static constexpr int CA = AS / 256 / NW;   // kilobyte LDS chunks of A filled per wavefront per slab
+    static constexpr int CB = BS / 256 / NW;
     static_assert(QA * 4 * NT == BM * BK && QB * 4 * NT == BN * BK, "tile not divisible by the loaders");
+    static_assert(CA * 256 * NW == AS && CB * 256 * NW == BS, "tile not divisible into LDS chunks");
 };
 
 // Configurations of the grouped launches (rotations, Gram products, opt_gemm).
@@ -78,6 +90,83 @@ static_assert(LargeCfg::BM == kGemmCfgs[1].bm && LargeCfg::BN == kGemmCfgs[1].bn
 // Configuration of the QR trailing updates (short K, memory-bound C).
 using QrCfg = Cfg<2, 2, 2, 2>;
 static_assert(QrCfg::BM == kQrTile && QrCfg::BN == kQrTile, "QR tile size mismatch");
+
+// Slot of 16-byte group q in row r of a k-contiguous LDS operand.
+__device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* gsrc_ptr;
+
+// Fill one slab of an fp32 operand into LDS buffer `buf` with direct loads.
+// The operand is stored row-major with leading dimension ld and `rows` x
+// `cols` valid elements. KMAJOR: LDS [32][R] from stored rows k0.. (k) and
+// columns c0.. (the tile's m or n); otherwise LDS [R][32] swizzled, from
+// stored rows c0.. (m or n) and columns k0.. (k). VEC: 16-byte loads (ld,
+// cols and the base 4-aligned); otherwise four 4-byte loads per 16 bytes.
+template <class C, bool KMAJOR, int R>
+__device__ __forceinline__ void dma_slab(float* buf, const float* base, int64_t ld, int rows, int cols,
+                                         int c0, int k0, bool vec) {
+    constexpr int CPW = R * BK / 256 / C::NW;   // chunks per wavefront
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (vec) {
+        const int last = cols - 4;
+#pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+            const int c = wave * CPW + t;
+            int grow, gcol;
+            if (KMAJOR) {
+                const int flat = c * 256 + 4 * lane;
+                grow = k0 + flat / R;
+                gcol = c0 + flat % R;
+            } else {
+                const int r = 8 * c + (lane >> 3);
+                grow = c0 + r;
+                gcol = k0 + 4 * ((lane & 7) ^ swz(r));
+            }
+            grow = grow < rows ? grow : rows - 1;
+            gcol = gcol < last ? gcol : last;
+            __builtin_amdgcn_global_load_lds((gsrc_ptr)(base + (int64_t)grow * ld + gcol),
+                                             (lds_ptr)(buf + c * 256), 16, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+            const int c = wave * CPW + t;
+#pragma unroll
+            for (int e4 = 0; e4 < 4; ++e4) {
+                const int f = c * 256 + 64 * e4 + lane;   // LDS float this lane writes
+                int grow, gcol;
+                if (KMAJOR) {
+                    grow = k0 + f / R;
+                    gcol = c0 + f % R;
+                } else {
+                    const int r = f >> 5, p = f & 31;
+                    grow = c0 + r;
+                    gcol = k0 + 4 * ((p >> 2) ^ swz(r)) + (p & 3);
+                }
+                grow = grow < rows ? grow : rows - 1;
+                gcol = gcol < cols ? gcol : cols - 1;
+                __builtin_amdgcn_global_load_lds((gsrc_ptr)(base + (int64_t)grow * ld + gcol),
+                                                 (lds_ptr)(buf + c * 256 + 64 * e4), 4, 0, 0);
+            }
+        }
+    }
+}
+
+// Zero the k values >= K of a slab filled by dma_slab (a partial last slab).
+template <class C, bool KMAJOR, int R>
+__device__ __forceinline__ void zero_k_tail(float* buf, int k0, int K) {
+    const int kv = K - k0;   // valid k values in this slab, 0 < kv < 32
+    for (int e = threadIdx.x; e < R * BK; e += C::NT) {
+        if (KMAJOR) {
+            if (e / R >= kv) buf[e] = 0.f;
+        } else {
+            const int r = e >> 5, kk = e & 31;
+            if (kk >= kv) buf[r * BK + 4 * ((kk >> 2) ^ swz(r)) + (kk & 3)] = 0.f;
+        }
+    }
+}
 
 // Four consecutive elements (row, col..col+3) of a row-major stored matrix,
 // as loaded: fp32 values, or the raw bits of bf16 values. They are widened and
@@ -195,7 +284,7 @@ __device__ __forceinline__ void store_a(float* As, const Raw4<ABF> (&r)[C::QA], 
                     else if (row == col + e) v[e] = 1.f;
                 }
             }
-            *(f32x4*)&As[rr * KPAD + 4 * c4] = v;
+            *(f32x4*)&As[rr * BK + 4 * (c4 ^ swz(rr))] = v;
         }
     }
 }
@@ -207,7 +296,7 @@ __device__ __forceinline__ void store_b(float* Bs, const Raw4<BBF> (&r)[C::QB], 
     for (int q = 0; q < C::QB; ++q) {
         int rr, c4;
         slab_pos<C, !BT, C::BN>(q, rr, c4);
-        if (BT) *(f32x4*)&Bs[rr * KPAD + 4 * c4] = finish4<BBF>(r[q], n0 + rr, k0 + 4 * c4, p.N, p.K);
+        if (BT) *(f32x4*)&Bs[rr * BK + 4 * (c4 ^ swz(rr))] = finish4<BBF>(r[q], n0 + rr, k0 + 4 * c4, p.N, p.K);
         else    *(f32x4*)&Bs[rr * C::BN + 4 * c4] = finish4<BBF>(r[q], k0 + rr, n0 + 4 * c4, p.K, p.N);
     }
 }
@@ -239,14 +328,14 @@ __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int w
 #pragma unroll
                 for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * C::BM + row];
             } else {
-                a[i] = *(const f32x4*)&As[row * KPAD + 8 * g + 4 * h];
+                a[i] = *(const f32x4*)&As[row * BK + 4 * ((2 * g + h) ^ swz(row))];
             }
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const int col = wn * 32 * C::TN + j * 32 + l32;
             if (BT) {
-                b[j] = *(const f32x4*)&Bs[col * KPAD + 8 * g + 4 * h];
+                b[j] = *(const f32x4*)&Bs[col * BK + 4 * ((2 * g + h) ^ swz(col))];
             } else {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * C::BN + col];
@@ -305,7 +394,7 @@ __device__ __forceinline__ void epilogue(const GemmProb& p, int m0, int n0, int 
 template <class C, bool AT, bool BT, bool ABF, bool BBF>
 __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
                                           float* smem) {
-    constexpr int AS = C::template a_size<AT>(), BS = C::template b_size<BT>();
+    constexpr int AS = C::AS, BS = C::BS;
     // buffer b of A at smem + b*AS, of B at smem + 2*AS + b*BS; selected
     // arithmetically so that the slab body is one straight-line block (a
     // branch between two copies makes the compiler move every accumulator
@@ -313,31 +402,55 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % C::WM, wn = wave / C::WM;
     const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const bool avec = p.flags & GF_A_VEC, bvec = p.flags & GF_B_VEC;
+
+    // direct fills of the fp32 operands, and the zeroing of k >= K after a
+    // partial slab has landed
+    auto fill = [&](int b, int k0) {
+        if constexpr (!ABF)
+            dma_slab<C, AT, C::BM>(smem + b * AS, (const float*)p.A, p.lda, AT ? p.K : p.M, AT ? p.M : p.K,
+                                   m0, k0, avec);
+        if constexpr (!BBF)
+            dma_slab<C, !BT, C::BN>(smem + 2 * AS + b * BS, (const float*)p.B, p.ldb, BT ? p.N : p.K,
+                                    BT ? p.K : p.N, n0, k0, bvec);
+    };
+    auto tail = [&](int b, int k0) {
+        if constexpr (!ABF) zero_k_tail<C, AT, C::BM>(smem + b * AS, k0, p.K);
+        if constexpr (!BBF) zero_k_tail<C, !BT, C::BN>(smem + 2 * AS + b * BS, k0, p.K);
+    };
 
     Acc<C> acc;
     acc.zero();
     const int nk = (p.K + BK - 1) / BK;
-    Raw4<ABF> ra[C::QA];
-    Raw4<BBF> rb[C::QB];
+    Raw4<ABF> ra[ABF ? C::QA : 1];
+    Raw4<BBF> rb[BBF ? C::QB : 1];
     if (nk > 0) {
-        load_a<C, AT, ABF>(p, m0, 0, ra);
-        load_b<C, BT, BBF>(p, n0, 0, rb);
-        store_a<C, AT, ABF, false>(smem, ra, p, m0, 0);
-        store_b<C, BT, BBF>(smem + 2 * AS, rb, p, n0, 0);
+        fill(0, 0);
+        if constexpr (ABF) { load_a<C, AT, ABF>(p, m0, 0, ra); store_a<C, AT, ABF, false>(smem, ra, p, m0, 0); }
+        if constexpr (BBF) { load_b<C, BT, BBF>(p, n0, 0, rb); store_b<C, BT, BBF>(smem + 2 * AS, rb, p, n0, 0); }
+        __syncthreads();
+        if (p.K < BK) {
+            tail(0, 0);
+            __syncthreads();
+        }
     }
-    __syncthreads();
-    // The loads of slab kt+1 are issued unconditionally: past the last slab
-    // they read clamped, valid addresses and fill the idle buffer with zeros,
-    // which keeps the slab body one basic block.
+    // The fill of slab kt+1 is issued unconditionally: past the last slab it
+    // reads clamped, valid addresses into the idle buffer, which keeps the
+    // slab body one basic block.
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const int k1 = (kt + 1) * BK;
-        load_a<C, AT, ABF>(p, m0, k1, ra);
-        load_b<C, BT, BBF>(p, n0, k1, rb);
+        fill(cur ^ 1, k1);
+        if constexpr (ABF) load_a<C, AT, ABF>(p, m0, k1, ra);
+        if constexpr (BBF) load_b<C, BT, BBF>(p, n0, k1, rb);
         mma_slab<C, AT, BT>(smem + cur * AS, smem + 2 * AS + cur * BS, wm, wn, lane, acc);
-        store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
-        store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
+        if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
+        if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
         __syncthreads();
+        if (k1 < p.K && k1 + BK > p.K) {
+            tail(cur ^ 1, k1);
+            __syncthreads();
+        }
     }
     epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
 }
@@ -351,7 +464,7 @@ static_assert(kQrPB <= 2 * kGemmBK, "the QR update tile holds the whole panel wi
 
 __device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn, float* smem) {
     using C = QrCfg;
-    constexpr int AS = C::a_size<false>(), BS = C::b_size<false>();
+    constexpr int AS = C::AS, BS = C::BS;
     float* As0 = smem;
     float* As1 = smem + AS;
     float* Bs0 = smem + 2 * AS;
@@ -439,7 +552,7 @@ struct GemmArgs {
 
 template <class C, bool AT, bool BT, bool ABF, bool BBF>
 __global__ __launch_bounds__(C::NT) void gemm_grouped_kernel(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) float smem[C::template smem_floats<AT, BT>()];
+    __shared__ __attribute__((aligned(16))) float smem[C::SMEM];
     const int bid = xcd_remap(blockIdx.x, args.total_tiles);
     GemmProb p;
     int t = bid;
@@ -477,7 +590,7 @@ hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
 // Q formation (q_mode 1): C = X[k:, k:]. W2 (jb x N') comes from qr_reduce.
 __global__ __launch_bounds__(QrCfg::NT) void qr_update_kernel(const QrJob* __restrict__ jobs,
                                                             QrClasses C, int p, int q_mode) {
-    __shared__ __attribute__((aligned(16))) float smem[QrCfg::smem_floats<false, false>()];
+    __shared__ __attribute__((aligned(16))) float smem[QrCfg::SMEM];
     int job, local;
     if (!qr_locate(C, QG_UPDATE, p, q_mode, blockIdx.x, job, local)) return;
     const QrJob J = jobs[job];
