@@ -314,6 +314,46 @@ struct Acc {
     }
 };
 
+// Operand fragments of k group g (8 k values) of a slab: a[i] feeds the
+// MFMAs of row block i, b[j] those of column block j (element s: MFMA s).
+template <class C, bool AT, bool BT>
+__device__ __forceinline__ void read_frags(const float* As, const float* Bs, int g, int wm, int wn, int lane,
+                                           f32x4 (&a)[C::TM], f32x4 (&b)[C::TN]) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * 32 * C::TM + i * 32 + l32;
+        if (AT) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * C::BM + row];
+        } else {
+            a[i] = *(const f32x4*)&As[row * BK + 4 * ((2 * g + h) ^ swz(row))];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+        const int col = wn * 32 * C::TN + j * 32 + l32;
+        if (BT) {
+            b[j] = *(const f32x4*)&Bs[col * BK + 4 * ((2 * g + h) ^ swz(col))];
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * C::BN + col];
+        }
+    }
+}
+
+// MFMAs s = S0 .. S1-1 of one k group.
+template <class C, int S0 = 0, int S1 = 4>
+__device__ __forceinline__ void mma_group(const f32x4 (&a)[C::TM], const f32x4 (&b)[C::TN], Acc<C>& acc) {
+#pragma unroll
+    for (int s = S0; s < S1; ++s)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[j][s], acc.v[i][j], 0, 0, 0);
+}
+
 template <class C, bool AT, bool BT>
 __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int wm, int wn, int lane,
                                          Acc<C>& acc) {
@@ -422,28 +462,49 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     Acc<C> acc;
     acc.zero();
     const int nk = (p.K + BK - 1) / BK;
+    if (nk == 0) {
+        epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
+        return;
+    }
     Raw4<ABF> ra[ABF ? C::QA : 1];
     Raw4<BBF> rb[BBF ? C::QB : 1];
-    if (nk > 0) {
-        fill(0, 0);
-        if constexpr (ABF) { load_a<C, AT, ABF>(p, m0, 0, ra); store_a<C, AT, ABF, false>(smem, ra, p, m0, 0); }
-        if constexpr (BBF) { load_b<C, BT, BBF>(p, n0, 0, rb); store_b<C, BT, BBF>(smem + 2 * AS, rb, p, n0, 0); }
+    fill(0, 0);
+    if constexpr (ABF) { load_a<C, AT, ABF>(p, m0, 0, ra); store_a<C, AT, ABF, false>(smem, ra, p, m0, 0); }
+    if constexpr (BBF) { load_b<C, BT, BBF>(p, n0, 0, rb); store_b<C, BT, BBF>(smem + 2 * AS, rb, p, n0, 0); }
+    __syncthreads();
+    if (p.K < BK) {
+        tail(0, 0);
         __syncthreads();
-        if (p.K < BK) {
-            tail(0, 0);
-            __syncthreads();
-        }
     }
-    // The fill of slab kt+1 is issued unconditionally: past the last slab it
-    // reads clamped, valid addresses into the idle buffer, which keeps the
-    // slab body one basic block.
+
+    // Software pipeline over the four k groups of a slab: the fragments of
+    // group g+1 are read after the first MFMAs of group g have been issued,
+    // so every wait for a fragment finds it read a group earlier. The slab's
+    // closing barrier sits before the MFMAs of its last group, and the reads
+    // of the next slab's first group follow right after it. The fill of slab
+    // kt+1 is issued unconditionally: past the last slab it reads clamped,
+    // valid addresses into the idle buffer, which keeps the slab body one
+    // basic block.
+    f32x4 fa0[C::TM], fb0[C::TN], fa1[C::TM], fb1[C::TN];
+    read_frags<C, AT, BT>(smem, smem + 2 * AS, 0, wm, wn, lane, fa0, fb0);
+#define MATOPT_PHASE(FA, FB, NEXT)                              \
+    mma_group<C, 0, 1>(FA, FB, acc);                            \
+    __builtin_amdgcn_sched_barrier(0);                          \
+    NEXT;                                                       \
+    __builtin_amdgcn_sched_barrier(0);                          \
+    mma_group<C, 1, 4>(FA, FB, acc);                            \
+    __builtin_amdgcn_sched_barrier(0);
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const int k1 = (kt + 1) * BK;
+        const float* As = smem + cur * AS;
+        const float* Bs = smem + 2 * AS + cur * BS;
         fill(cur ^ 1, k1);
         if constexpr (ABF) load_a<C, AT, ABF>(p, m0, k1, ra);
         if constexpr (BBF) load_b<C, BT, BBF>(p, n0, k1, rb);
-        mma_slab<C, AT, BT>(smem + cur * AS, smem + 2 * AS + cur * BS, wm, wn, lane, acc);
+        MATOPT_PHASE(fa0, fb0, (read_frags<C, AT, BT>(As, Bs, 1, wm, wn, lane, fa1, fb1)))
+        MATOPT_PHASE(fa1, fb1, (read_frags<C, AT, BT>(As, Bs, 2, wm, wn, lane, fa0, fb0)))
+        MATOPT_PHASE(fa0, fb0, (read_frags<C, AT, BT>(As, Bs, 3, wm, wn, lane, fa1, fb1)))
         if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
         if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
         __syncthreads();
@@ -451,7 +512,11 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
             tail(cur ^ 1, k1);
             __syncthreads();
         }
+        // the next slab's first group (past the last slab: values unused)
+        MATOPT_PHASE(fa1, fb1, (read_frags<C, AT, BT>(smem + (cur ^ 1) * AS, smem + 2 * AS + (cur ^ 1) * BS, 0,
+                                                      wm, wn, lane, fa0, fb0)))
     }
+#undef MATOPT_PHASE
     epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
 }
 
