@@ -81,6 +81,30 @@ def gemm_source_hash() -> str:
     return h.hexdigest()
 
 
+def rotation_dispatches(rows):
+    """The rotation-GEMM dispatches among profiled kernels: a step starts with
+    its run of momentum kernels; the refresh's Gram products and QR block
+    updates use the same GEMM instantiations as the rotations, so only steps
+    without a refresh (no QR kernel) are taken, and there every grouped GEMM
+    is a rotation phase."""
+    rows = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    steps, cur = [], None
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "momentum_kernel" in name:
+            if cur is None or cur["other"]:
+                cur = {"rows": [], "refresh": False, "other": False}
+                steps.append(cur)
+        elif cur is not None:
+            cur["other"] = True
+        if cur is None:
+            continue
+        cur["rows"].append(r)
+        if "qr_" in name or "copy_cols" in name:
+            cur["refresh"] = True
+    return [r for st in steps if not st["refresh"] for r in st["rows"] if is_rotation_gemm(r["Kernel_Name"])]
+
+
 def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int, out_path: str = TRAFFIC_JSON):
     """HBM bytes per rotation-GEMM launch from two rocprofv3 --pmc runs.
 
@@ -96,9 +120,8 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int, out_path: str 
     cf = float(next(r for r in F if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
     cw = float(next(r for r in W if "copyBuffer" in r["Kernel_Name"])["Counter_Value"]) * 1024
     sf, sw = calib / cf, calib / cw
-    rot = lambda r: is_rotation_gemm(r["Kernel_Name"])
-    fr = [float(r["Counter_Value"]) * 1024 * sf for r in F if rot(r)]
-    wr = [float(r["Counter_Value"]) * 1024 * sw for r in W if rot(r)]
+    fr = [float(r["Counter_Value"]) * 1024 * sf for r in rotation_dispatches(F)]
+    wr = [float(r["Counter_Value"]) * 1024 * sw for r in rotation_dispatches(W)]
     out = {
         "kernel": "gemm_grouped_kernel, rotation-phase instantiations",
         "gemm_source_sha256": gemm_source_hash(),

@@ -153,7 +153,8 @@ opt_status opt_group_set_timing(opt_group_t g, int32_t enable);
  * summed milliseconds and the number of kernels launched in the timed scopes
  * since timing was enabled (arrays of OPT_NUM_PHASES entries; either may be
  * NULL). Every scope counts its grouped GEMM and elementwise launches; the
- * refresh scope counts only its Gram-product GEMMs, not its many QR kernels. */
+ * refresh scope counts its grouped GEMMs (Gram products and the QR's outer-
+ * block updates), not the QR's panel and in-block kernels. */
 opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches);
 
 void opt_group_destroy(opt_group_t g);   /* NULL is ignored; does not synchronise */

@@ -85,6 +85,8 @@ struct QrBatch {
     std::vector<int> np;   // panels per job, descending
     std::vector<int> d;    // order per job, descending
     int max_d = 0;
+    // grouped GEMM launches of the outer blocks: [block][step] -> launches
+    std::vector<std::vector<std::vector<GemmLaunch>>> fact, qform;
 };
 struct CopyLaunch {
     int n = 0;
@@ -102,7 +104,7 @@ struct Group {
 // Matrices refreshed together: Gram products, completion copies, QR jobs.
 struct RefreshBatch {
     std::vector<int> mats;
-    std::vector<GemmLaunch> prod1, prod2;
+    std::vector<std::vector<GemmLaunch>> prod1, prod2;   // K-chunk steps, run in order
     CopyLaunch comp;
     QrBatch qr;
     uint64_t ref_bytes = 0;
@@ -350,8 +352,39 @@ EwLaunch put_ew(Image& img, std::vector<EwSeg> segs) {
 
 int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
 
+// Long products are split along K into chunks run as successive launches
+// that accumulate into C (beta = 1 after the first chunk): each launch's fp32
+// accumulation chain is then at most kChunkK / 2 MFMAs long, which keeps the
+// rounding error of the refresh products and of the QR's long reductions
+// near that of a blocked CPU GEMM instead of growing with the full K.
+constexpr int64_t kChunkK = 1024;
+
+// The K range [k0, k0 + kc) of a product, as a product of its own.
+PGemm k_slice(const PGemm& g, int64_t k0, int64_t kc, float beta) {
+    const bool at = g.variant & 1, bt = g.variant & 2, abf = g.variant & 4, bbf = g.variant & 8;
+    const GemmProb& p = g.p;
+    const char* A = (const char*)p.A + (at ? k0 * p.lda : k0) * (abf ? 2 : 4);
+    const char* B = (const char*)p.B + (bt ? k0 : k0 * p.ldb) * (bbf ? 2 : 4);
+    return mk(at, bt, A, abf, p.lda, B, bbf, p.ldb, p.C, p.ldc, p.M, p.N, kc, p.alpha, beta);
+}
+
+// Appends chunk c of g to steps[c] for every chunk of its K range.
+void add_k_chunked(std::vector<std::vector<PGemm>>& steps, const PGemm& g) {
+    const int64_t K = g.p.K;
+    for (int64_t c = 0; c == 0 || c * kChunkK < K; ++c) {
+        if ((int64_t)steps.size() <= c) steps.resize(c + 1);
+        const int64_t k0 = c * kChunkK;
+        steps[c].push_back(k_slice(g, k0, std::min(kChunkK, K - k0), c ? 1.f : g.p.beta));
+    }
+}
+
+
+
+int qr_blocks(int d) { return (d + kQrNB - 1) / kQrNB; }
+
 struct QrBytes {
-    uint64_t Z, T, part, W2;
+    uint64_t Z, T, part, W2, Yb, Wb, W2b, Sb;
+    uint64_t scratch() const { return T + part + W2 + Yb + Wb + W2b + Sb; }   // all but Z
 };
 QrBytes qr_job_bytes(int64_t d) {
     QrBytes b;
@@ -359,7 +392,105 @@ QrBytes qr_job_bytes(int64_t d) {
     b.T = align_up(4ull * panels((int)d) * kQrPB * kQrPB);
     b.part = align_up(4ull * kQrMaxSplits * kQrPB * d);
     b.W2 = align_up(4ull * kQrPB * d);
+    b.Yb = align_up(4ull * d * kQrNB);
+    b.Wb = align_up(4ull * kQrNB * d);
+    b.W2b = align_up(4ull * kQrNB * d);
+    b.Sb = align_up(4ull * qr_blocks((int)d) * kQrNB * kQrNB);
     return b;
+}
+
+// Carve a job's scratch (everything but Z and X) from `base`; returns the
+// bytes used.
+uint64_t qr_assign_scratch(QrJob& j, char* base) {
+    const QrBytes b = qr_job_bytes(j.d);
+    uint64_t off = 0;
+    j.T = (float*)(base + off); off += b.T;
+    j.part = (float*)(base + off); off += b.part;
+    j.W2 = (float*)(base + off); off += b.W2;
+    j.Yb = (float*)(base + off); off += b.Yb;
+    j.Wb = (float*)(base + off); off += b.Wb;
+    j.W2b = (float*)(base + off); off += b.W2b;
+    j.Sb = (float*)(base + off); off += b.Sb;
+    return off;
+}
+
+// Grouped-GEMM steps of the outer QR blocks of a set of jobs. For block b
+// (columns kB = b NB .. kB + w), each inner vector is one launch's problems,
+// run in order:
+//  fact[b]   S_b = Yb^T Yb and W = Yb^T C (C = Z[kB:, kB+w:]); the forward
+//            substitution W2_q = T_q^T (W_q - S_b[q, :q] W2[:q]) panel by
+//            panel; C -= Yb W2.
+//  qform[b]  W = Yb^T X[kB:, kB:]; the backward substitution
+//            W2_q = T_q (W_q - S_b[q, q+1:] W2[q+1:]); X[kB:, kB:] -= Yb W2.
+// Yb is rebuilt from Z by qr_copy_block before each block's steps. The
+// products over the L rows (S, W) run in K chunks (add_k_chunked).
+
+struct QrSteps {
+    std::vector<std::vector<std::vector<PGemm>>> fact, qform;
+};
+
+QrSteps qr_block_steps(const std::vector<QrJob>& jobs) {
+    constexpr int P = kQrPanelsPerBlock;
+    QrSteps S;
+    int maxb = 0;
+    for (const QrJob& j : jobs) maxb = std::max(maxb, qr_blocks(j.d));
+    S.fact.resize(maxb);
+    S.qform.resize(maxb);
+    for (int b = 0; b < maxb; ++b) {
+        const int64_t kB = (int64_t)b * kQrNB;
+        std::vector<std::vector<PGemm>> ws, qw;
+        std::vector<PGemm> upd, qupd;
+        std::vector<PGemm> sub_s[P], sub_t[P], qsub_s[P], qsub_t[P];
+        for (const QrJob& J : jobs) {
+            const int64_t d = J.d;
+            if (d <= kB) continue;
+            const int64_t L = d - kB, w = std::min<int64_t>(kQrNB, L), nc = L - w;
+            const int npb = (int)((w + kQrPB - 1) / kQrPB);
+            float* Sb = J.Sb + b * (int64_t)kQrNB * kQrNB;
+            float* Ct = J.Z + kB * d + kB + w;
+            float* Cx = J.X + kB * d + kB;
+            // S = Yb^T Yb, W = Yb^T C (factorisation) and W = Yb^T X[kB:, kB:] (Q formation)
+            add_k_chunked(ws, mk(true, false, J.Yb, false, kQrNB, J.Yb, false, kQrNB, Sb, kQrNB, w, w, L, 1.f, 0.f));
+            if (nc > 0)
+                add_k_chunked(ws, mk(true, false, J.Yb, false, kQrNB, Ct, false, d, J.Wb, d, w, nc, L, 1.f, 0.f));
+            add_k_chunked(qw, mk(true, false, J.Yb, false, kQrNB, Cx, false, d, J.Wb, d, w, L, L, 1.f, 0.f));
+            for (int q = 0; q < npb; ++q) {
+                const int64_t r0 = (int64_t)q * kQrPB, jb = std::min<int64_t>(kQrPB, w - r0), r1 = r0 + jb;
+                const float* Tq = J.T + (int64_t)(b * P + q) * kQrPB * kQrPB;
+                if (nc > 0) {
+                    if (q > 0)
+                        sub_s[q].push_back(mk(false, false, Sb + r0 * kQrNB, false, kQrNB, J.W2b, false, d,
+                                              J.Wb + r0 * d, d, jb, nc, r0, -1.f, 1.f));
+                    sub_t[q].push_back(mk(true, false, Tq, false, kQrPB, J.Wb + r0 * d, false, d, J.W2b + r0 * d, d,
+                                          jb, nc, jb, 1.f, 0.f));
+                }
+                if (q < npb - 1)
+                    qsub_s[q].push_back(mk(false, false, Sb + r0 * kQrNB + r1, false, kQrNB, J.W2b + r1 * d, false, d,
+                                           J.Wb + r0 * d, d, jb, L, w - r1, -1.f, 1.f));
+                qsub_t[q].push_back(mk(false, false, Tq, false, kQrPB, J.Wb + r0 * d, false, d, J.W2b + r0 * d, d,
+                                       jb, L, jb, 1.f, 0.f));
+            }
+            if (nc > 0)
+                upd.push_back(mk(false, false, J.Yb, false, kQrNB, J.W2b, false, d, Ct, d, L, nc, w, -1.f, 1.f));
+            qupd.push_back(mk(false, false, J.Yb, false, kQrNB, J.W2b, false, d, Cx, d, L, L, w, -1.f, 1.f));
+        }
+        auto add = [](std::vector<std::vector<PGemm>>& out, std::vector<PGemm>& v) {
+            if (!v.empty()) out.push_back(std::move(v));
+        };
+        for (std::vector<PGemm>& v : ws) add(S.fact[b], v);
+        for (int q = 0; q < P; ++q) {
+            add(S.fact[b], sub_s[q]);
+            add(S.fact[b], sub_t[q]);
+        }
+        add(S.fact[b], upd);
+        for (std::vector<PGemm>& v : qw) add(S.qform[b], v);
+        for (int q = P - 1; q >= 0; --q) {
+            add(S.qform[b], qsub_s[q]);
+            add(S.qform[b], qsub_t[q]);
+        }
+        add(S.qform[b], qupd);
+    }
+    return S;
 }
 
 // Refresh scratch of one matrix: Gram products B1U (n x r), B1V (m x r), the
@@ -367,8 +498,7 @@ QrBytes qr_job_bytes(int64_t d) {
 uint64_t refresh_bytes(int64_t m, int64_t n) {
     const int64_t r = std::min(m, n);
     QrBytes bu = qr_job_bytes(m), bv = qr_job_bytes(n);
-    return align_up(4ull * n * r) + align_up(4ull * m * r) + bu.Z + bv.Z + bu.T + bu.part + bu.W2 + bv.T +
-           bv.part + bv.W2;
+    return align_up(4ull * n * r) + align_up(4ull * m * r) + bu.Z + bv.Z + bu.scratch() + bv.scratch();
 }
 
 // Refresh batches: matrices in LPT order, next-fit under the refresh cap (a
@@ -480,22 +610,24 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         std::stable_sort(jsrc.begin(), jsrc.end(), [](const JobSrc& a, const JobSrc& b) { return a.d > b.d; });
         std::vector<QrJob> jobs;
         for (const JobSrc& js : jsrc) {
-            QrBytes b = qr_job_bytes(js.d);
             QrJob j{};
             j.Z = js.Z;
             j.X = js.X;
             j.d = (int32_t)js.d;
             j.np = panels((int)js.d);
-            j.T = (float*)(scratch + off); off += b.T;
-            j.part = (float*)(scratch + off); off += b.part;
-            j.W2 = (float*)(scratch + off); off += b.W2;
+            off += qr_assign_scratch(j, scratch + off);
             jobs.push_back(j);
             R.qr.np.push_back(j.np);
             R.qr.d.push_back(j.d);
         }
         R.ref_bytes = off;
-        R.prod1 = put_gemm(g->img, p1);
-        R.prod2 = put_gemm(g->img, p2);
+        {
+            std::vector<std::vector<PGemm>> s1, s2;
+            for (const PGemm& x : p1) add_k_chunked(s1, x);
+            for (const PGemm& x : p2) add_k_chunked(s2, x);
+            for (const std::vector<PGemm>& st : s1) R.prod1.push_back(put_gemm(g->img, st));
+            for (const std::vector<PGemm>& st : s2) R.prod2.push_back(put_gemm(g->img, st));
+        }
         R.comp.n = (int)comp.size();
         R.comp.max_d = 0;
         for (const CopyJob& c : comp) R.comp.max_d = std::max(R.comp.max_d, (int)c.d);
@@ -503,6 +635,17 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         R.qr.njobs = (int)jobs.size();
         R.qr.max_d = jobs.empty() ? 0 : jobs[0].d;
         R.qr.jobs = g->img.put(jobs);
+        {
+            const QrSteps st = qr_block_steps(jobs);
+            auto put_steps = [&](const std::vector<std::vector<std::vector<PGemm>>>& in,
+                                 std::vector<std::vector<std::vector<GemmLaunch>>>& out) {
+                out.resize(in.size());
+                for (size_t b = 0; b < in.size(); ++b)
+                    for (const std::vector<PGemm>& step : in[b]) out[b].push_back(put_gemm(g->img, step));
+            };
+            put_steps(st.fact, R.qr.fact);
+            put_steps(st.qform, R.qr.qform);
+        }
         g->scratch_bytes = std::max(g->scratch_bytes, R.ref_bytes);
         g->rbatches.push_back(std::move(R));
     }
@@ -585,31 +728,43 @@ std::vector<QrClasses> active_classes(const std::vector<int>& d, int p) {
     return out;
 }
 
-hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vector<int>& d, hipStream_t s) {
+// `block_steps(b, qform)` runs the grouped-GEMM steps of outer block b.
+template <class BlockSteps>
+hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vector<int>& d, hipStream_t s,
+                  BlockSteps&& block_steps) {
     const int njobs = (int)np.size();
     if (njobs == 0) return hipSuccess;
     const int maxp = np[0], max_d = d[0];
+    const int maxb = (max_d + kQrNB - 1) / kQrNB;
     hipError_t e;
-    auto active = [&](int p) {
+    auto active_p = [&](int p) {
         int a = 0;
         while (a < njobs && np[a] > p) ++a;
         return a;
     };
-    for (int p = 0; p < maxp; ++p) {
-        if ((e = launch_qr_panel(jobs, active(p), p, max_d, s))) return e;
-        for (const QrClasses& C : active_classes(d, p)) {
-            if ((e = launch_qr_dots(jobs, C, p, 0, s))) return e;
-            if ((e = launch_qr_reduce(jobs, C, p, 0, s))) return e;
-            if ((e = launch_qr_update(jobs, C, p, 0, s))) return e;
+    auto active_b = [&](int b) {
+        int a = 0;
+        while (a < njobs && d[a] > b * kQrNB) ++a;
+        return a;
+    };
+    for (int b = 0; b < maxb; ++b) {
+        for (int q = 0; q < kQrPanelsPerBlock; ++q) {
+            const int p = b * kQrPanelsPerBlock + q;
+            if (p >= maxp) break;
+            if ((e = launch_qr_panel(jobs, active_p(p), p, max_d, s))) return e;
+            for (const QrClasses& C : active_classes(d, p)) {
+                if ((e = launch_qr_dots(jobs, C, p, s))) return e;
+                if ((e = launch_qr_reduce(jobs, C, p, s))) return e;
+                if ((e = launch_qr_update(jobs, C, p, s))) return e;
+            }
         }
+        if ((e = launch_qr_copy_block(jobs, active_b(b), b, max_d, s))) return e;
+        if ((e = block_steps(b, false))) return e;
     }
     if ((e = launch_qr_init_q(jobs, njobs, max_d, s))) return e;
-    for (int p = maxp - 1; p >= 0; --p) {
-        for (const QrClasses& C : active_classes(d, p)) {
-            if ((e = launch_qr_dots(jobs, C, p, 1, s))) return e;
-            if ((e = launch_qr_reduce(jobs, C, p, 1, s))) return e;
-            if ((e = launch_qr_update(jobs, C, p, 1, s))) return e;
-        }
+    for (int b = maxb - 1; b >= 0; --b) {
+        if ((e = launch_qr_copy_block(jobs, active_b(b), b, max_d, s))) return e;
+        if ((e = block_steps(b, true))) return e;
     }
     return hipSuccess;
 }
@@ -618,10 +773,17 @@ hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, h
     PhaseScope ps(g, OPT_PHASE_REFRESH, s);
     hipError_t e;
     for (int it = 0; it < power_iters; ++it) {
-        if ((e = run_gemm(g, G.prod1, 1.f, s))) return e;
-        if ((e = run_gemm(g, G.prod2, 1.f, s))) return e;
+        for (const std::vector<GemmLaunch>& st : G.prod1)
+            if ((e = run_gemm(g, st, 1.f, s))) return e;
+        for (const std::vector<GemmLaunch>& st : G.prod2)
+            if ((e = run_gemm(g, st, 1.f, s))) return e;
         if ((e = launch_copy_cols(dptr<CopyJob>(g, G.comp.jobs), G.comp.n, G.comp.max_d, s))) return e;
-        if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.d, s))) return e;
+        auto steps = [&](int b, bool qform) -> hipError_t {
+            for (const std::vector<GemmLaunch>& st : (qform ? G.qr.qform : G.qr.fact)[b])
+                if (hipError_t e2 = run_gemm(g, st, 1.f, s)) return e2;
+            return hipSuccess;
+        };
+        if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.d, s, steps))) return e;
     }
     return hipSuccess;
 }
@@ -894,7 +1056,7 @@ opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes) {
     if (d < 1) return fail(OPT_EINVAL, "d must be >= 1");
     if (d > OPT_MAX_DIM) return fail(OPT_EUNSUPPORTED, "d must be <= %d", OPT_MAX_DIM);
     QrBytes b = qr_job_bytes(d);
-    *bytes = align_up(sizeof(QrJob)) + b.T + b.part + b.W2;
+    *bytes = align_up(sizeof(QrJob)) + b.scratch();
     return OPT_OK;
 }
 
@@ -914,23 +1076,31 @@ extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* wo
                                             (unsigned long long)workspace_bytes, (unsigned long long)need);
     const uintptr_t zl = (uintptr_t)Z, zh = zl + 4ull * d * d, ql = (uintptr_t)Q, qh = ql + 4ull * d * d;
     if (zl < qh && ql < zh) return fail(OPT_EINVAL, "Z and Q overlap");
-    QrBytes b = qr_job_bytes(d);
     char* w = (char*)workspace;
     QrJob j{};
     j.Z = Z;
     j.X = Q;
     j.d = (int32_t)d;
     j.np = panels((int)d);
-    uint64_t off = align_up(sizeof(QrJob));
-    j.T = (float*)(w + off); off += b.T;
-    j.part = (float*)(w + off); off += b.part;
-    j.W2 = (float*)(w + off);
+    qr_assign_scratch(j, w + align_up(sizeof(QrJob)));
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before orthonormalize");
     hipLaunchKernelGGL(put_job_kernel, dim3(1), dim3(1), 0, s, (QrJob*)w, j);
     if ((e = hipGetLastError())) return hip_fail(e, "job upload");
     std::vector<int> np{j.np}, dd{(int)d};
-    if ((e = run_qr((const QrJob*)w, np, dd, s))) return hip_fail(e, "QR launch");
+    // one job: every block step has one problem, passed by value
+    const QrSteps st = qr_block_steps({j});
+    auto steps = [&](int b, bool qform) -> hipError_t {
+        for (const std::vector<PGemm>& step : (qform ? st.qform : st.fact)[b])
+            for (const PGemm& pg : step) {
+                GemmProb p1 = pg.p;
+                const int cfg = choose_cfg({p1});
+                set_tiles(p1, cfg);
+                if (hipError_t e2 = launch_gemm_single(pg.variant, cfg, p1, s)) return e2;
+            }
+        return hipSuccess;
+    };
+    if ((e = run_qr((const QrJob*)w, np, dd, s, steps))) return hip_fail(e, "QR launch");
     return OPT_OK;
 }

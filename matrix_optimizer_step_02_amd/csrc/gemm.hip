@@ -649,24 +649,24 @@ hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// ---- QR trailing update: C -= Y W2 with Y the unit-lower reflector block ----
+// ---- QR in-block update: C -= Y W2 with Y the unit-lower reflector block ----
 //
-// Factorisation (q_mode 0) at panel p: C = Z[k:, k+jb:], Y = Z[k:, k:k+jb].
-// Q formation (q_mode 1): C = X[k:, k:]. W2 (jb x N') comes from qr_reduce.
+// At panel p: C = the rest of the outer block, Z[k:, k+jb : block end],
+// Y = Z[k:, k:k+jb]; W2 (jb x ncols) comes from qr_reduce.
 __global__ __launch_bounds__(QrCfg::NT) void qr_update_kernel(const QrJob* __restrict__ jobs,
-                                                            QrClasses C, int p, int q_mode) {
+                                                            QrClasses C, int p) {
     __shared__ __attribute__((aligned(16))) float smem[QrCfg::SMEM];
     int job, local;
-    if (!qr_locate(C, QG_UPDATE, p, q_mode, blockIdx.x, job, local)) return;
+    if (!qr_locate(C, QG_UPDATE, p, blockIdx.x, job, local)) return;
     const QrJob J = jobs[job];
     const int k = p * kQrPB;
     const int jb = min(kQrPB, J.d - k);
     const int L = J.d - k;
-    const int ncols = q_mode ? L : L - jb;
+    const int ncols = qr_inblock_cols(J.d, p);
     GemmProb g;
     g.A = J.Z + (int64_t)k * J.d + k;
     g.B = J.W2;
-    g.C = (q_mode ? J.X : J.Z) + (int64_t)k * J.d + k + (q_mode ? 0 : jb);
+    g.C = J.Z + (int64_t)k * J.d + k + jb;
     g.lda = J.d;
     g.ldb = J.d;
     g.ldc = J.d;
@@ -683,10 +683,10 @@ __global__ __launch_bounds__(QrCfg::NT) void qr_update_kernel(const QrJob* __res
     qr_update_tile(g, tm, tn, smem);
 }
 
-hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
-    const int blocks = qr_total_blocks(C, QG_UPDATE, p, q_mode);
+hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_UPDATE, p);
     if (blocks <= 0) return hipSuccess;
-    qr_update_kernel<<<dim3(blocks), dim3(QrCfg::NT), 0, s>>>(jobs, C, p, q_mode);
+    qr_update_kernel<<<dim3(blocks), dim3(QrCfg::NT), 0, s>>>(jobs, C, p);
     return hipGetLastError();
 }
 

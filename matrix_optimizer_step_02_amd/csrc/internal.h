@@ -93,25 +93,34 @@ hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks
 // ------------------------------------------------------------------ QR ----
 
 constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY block)
-constexpr int kQrMaxSplits = 16;   // row splits of the reflector-transpose products
+constexpr int kQrPanelsPerBlock = 4;
+constexpr int kQrNB = kQrPB * kQrPanelsPerBlock;   // outer block width
+constexpr int kQrMaxSplits = 16;   // row splits of the in-block reflector-transpose products
 constexpr int kQrPanelThreads = 512;
 
 // One d x d orthonormalisation: Z (row stride d) is factorised in place, Q is
-// formed in X. Scratch: T (np * PB * PB), part (kQrMaxSplits * PB * d),
-// W2 (PB * d).
+// formed in X. Scratch: T (np * PB * PB: the panels' compact-WY factors),
+// part (kQrMaxSplits * PB * d) and W2 (PB * d) for the in-block updates, and
+// for the outer blocks Yb (d * NB: the block's reflectors as an explicit
+// unit-lower matrix, row stride NB), Wb and W2b (NB * d each, row stride d)
+// and Sb (nb * NB * NB: every block's reflector Gram matrix).
 struct QrJob {
     float* Z;
     float* X;
     float* T;
     float* part;
     float* W2;
+    float* Yb;
+    float* Wb;
+    float* W2b;
+    float* Sb;
     int32_t d;
     int32_t np;   // panels: ceil(d / PB)
 };
 
 // Jobs are sorted by d descending, so the jobs still active at panel p are a
 // prefix of the array; `njobs` passed to the panel launch is that prefix
-// length, `max_d` the d of job 0. The other per-panel launches take the runs
+// length, `max_d` the d of job 0. The in-block update launches take the runs
 // of equal d ("classes") by value, so that their grids cover exactly the
 // blocks that exist: a grid sized for the largest job times the job count
 // would dispatch mostly empty workgroups.
@@ -124,14 +133,13 @@ struct QrClasses {
 };
 enum QrGridKind { QG_DOTS = 0, QG_REDUCE = 1, QG_UPDATE = 2 };
 
-__host__ __device__ inline int qr_splits(int rows);
-__host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p, int q_mode);
-
 hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s);
-hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
-hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
-hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s);
+hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
+hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
+hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
 hipError_t launch_qr_init_q(const QrJob* jobs, int njobs, int max_d, hipStream_t s);
+// Yb of outer block b for the first njobs jobs (those with d > b NB).
+hipError_t launch_qr_copy_block(const QrJob* jobs, int njobs, int b, int max_d, hipStream_t s);
 
 // Strided copy of columns [c0, d) of X into Z (both d x d, row stride d):
 // the completion block of the refresh input.
@@ -143,7 +151,7 @@ struct CopyJob {
 };
 hipError_t launch_copy_cols(const CopyJob* jobs, int njobs, int max_d, hipStream_t s);
 
-// Splits used by the reflector-transpose product at panel p of a d x d QR.
+// Splits used by the in-block reflector-transpose product over `rows` rows.
 __host__ __device__ inline int qr_splits(int rows) {
     int s = (rows + 255) / 256;
     return s < kQrMaxSplits ? (s < 1 ? 1 : s) : kQrMaxSplits;
@@ -153,32 +161,40 @@ __host__ __device__ inline int qr_chunk(int rows, int splits) {
     return (c + 1) & ~1;
 }
 
-// Blocks one job contributes to a per-panel launch: reflector-transpose
-// products (512 columns x one row split per block), their reduction (256
-// columns per block) and the trailing update (128 x 128 tiles).
-__host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p, int q_mode) {
+// Columns of Z that panel p of a d x d factorisation updates directly: the
+// rest of its outer block (the columns past the block are updated once per
+// block).
+__host__ __device__ inline int qr_inblock_cols(int d, int p) {
     const int k = p * kQrPB;
     if (k >= d) return 0;
-    const int L = d - k;
-    const int jb = L < kQrPB ? L : kQrPB;
-    const int ncols = q_mode ? L : L - jb;
+    const int jb = d - k < kQrPB ? d - k : kQrPB;
+    const int end_blk = (p / kQrPanelsPerBlock + 1) * kQrNB;
+    const int end = end_blk < d ? end_blk : d;
+    return end - k - jb;
+}
+
+// Blocks one job contributes to a per-panel launch: reflector-transpose
+// products (512 columns x one row split per block), their reduction (256
+// columns per block) and the in-block update (128 x 128 tiles).
+__host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p) {
+    const int ncols = qr_inblock_cols(d, p);
     if (ncols <= 0) return 0;
+    const int L = d - p * kQrPB;
     if (kind == QG_DOTS) return ((ncols + 511) / 512) * qr_splits(L);
     if (kind == QG_REDUCE) return (ncols + 255) / 256;
     return ((L + kQrTile - 1) / kQrTile) * ((ncols + kQrTile - 1) / kQrTile);
 }
 
-__host__ __device__ inline int qr_total_blocks(const QrClasses& C, int kind, int p, int q_mode) {
+__host__ __device__ inline int qr_total_blocks(const QrClasses& C, int kind, int p) {
     int t = 0;
-    for (int c = 0; c < C.n; ++c) t += qr_blocks_per_job(kind, C.d[c], p, q_mode) * C.count[c];
+    for (int c = 0; c < C.n; ++c) t += qr_blocks_per_job(kind, C.d[c], p) * C.count[c];
     return t;
 }
 
 // Block id -> (job, block within the job); false for no such block.
-__host__ __device__ inline bool qr_locate(const QrClasses& C, int kind, int p, int q_mode, int bid,
-                                          int& job, int& local) {
+__host__ __device__ inline bool qr_locate(const QrClasses& C, int kind, int p, int bid, int& job, int& local) {
     for (int c = 0; c < C.n; ++c) {
-        const int per = qr_blocks_per_job(kind, C.d[c], p, q_mode);
+        const int per = qr_blocks_per_job(kind, C.d[c], p);
         const int tot = per * C.count[c];
         if (bid < tot) {
             job = C.first[c] + bid / per;

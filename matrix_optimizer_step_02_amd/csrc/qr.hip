@@ -6,24 +6,35 @@
 // reflections keep Q orthonormal to working precision regardless of the
 // conditioning of Z, which Cholesky- or Gram-Schmidt-based schemes do not.
 //
-// Factorisation, panel by panel (width PB = 64), right-looking:
+// Two levels of blocking. Panels of PB = 64 columns are factorised one at a
+// time; each updates only the rest of its outer block of NB = 256 columns:
 //   1. qr_panel   one 512-thread workgroup per matrix factorises the L x PB
 //                 panel in register-resident sub-panels (see below), stores
 //                 the reflectors below the diagonal of Z, R on and above it,
 //                 and the upper-triangular T of the compact WY form
 //                 H_0 ... H_{jb-1} = I - Y T Y^T.
-//   2. qr_dots    W = Y^T C for the trailing block C, split over rows into
-//                 partial sums (fp32 MFMA 32x32x2 straight from global memory:
-//                 both operands are read along their contiguous dimension).
+//   2. qr_dots    W = Y^T C for the block's remaining columns C, split over
+//                 rows into partial sums (fp32 MFMA 32x32x2 straight from
+//                 global memory: both operands read along their contiguous
+//                 dimension).
 //   3. qr_reduce  sums the partials and applies T^T: W2 = T^T W.
 //   4. qr_update  C -= Y W2 on the grouped GEMM tile (unit-lower A loader).
+// After the block's panels, the columns right of the block get the block's
+// four reflector blocks in one pass on the grouped GEMM (host-side plan):
+// Yb = the block's reflectors as an explicit unit-lower matrix
+// (qr_copy_block), W = Yb^T C and the Gram matrix S = Yb^T Yb, then W2 by
+// block forward substitution (w_q = T_q^T (W_q - sum_{i<q} S_qi w_i), the
+// panels' transposed factors applied in order), then C -= Yb W2. The trailing
+// matrix is thus read and written once per 256 columns instead of once per
+// 64, with K = 256 products.
 // Q formation (backward accumulation): X = diag(sign(R_ii)) (qr_init_q, so
-// the sign convention costs nothing), then for panels from last to first
-// X[k:, k:] -= Y T (Y^T X[k:, k:]) with the same three kernels (q_mode 1).
+// the sign convention costs nothing), then for blocks from last to first
+// X[k:, k:] -= Yb W2 with W = Yb^T X[k:, k:] and the backward substitution
+// w_q = T_q (W_q - sum_{i>q} S_qi w_i).
 //
 // Several matrices are factorised in lock step: every launch covers all
-// matrices that still have panel p, which are a prefix of the job array
-// sorted by d descending.
+// matrices that still have panel p (block b), which are a prefix of the job
+// array sorted by d descending.
 #include "internal.h"
 
 namespace matopt {
@@ -409,15 +420,15 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
 // share operands); lane l supplies Y[row + l/32][32 b + l%32] and
 // C[row + l/32][col + l%32], i.e. 128-byte row segments of both matrices.
 __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ jobs, QrClasses cls,
-                                                     int p, int q_mode) {
+                                                     int p) {
     constexpr int NB = PB / 32;
     int job, local;
-    if (!qr_locate(cls, QG_DOTS, p, q_mode, blockIdx.x, job, local)) return;
+    if (!qr_locate(cls, QG_DOTS, p, blockIdx.x, job, local)) return;
     const QrJob Jb = jobs[job];
     const int k = p * PB;
     const int d = Jb.d;
     const int jb = min(PB, d - k), L = d - k;
-    const int ncols = q_mode ? L : L - jb;
+    const int ncols = qr_inblock_cols(d, p);
     const int splits = qr_splits(L), kc = qr_chunk(L, splits);
     const int nxb = (ncols + 511) / 512;
     const int s = local / nxb;
@@ -426,7 +437,7 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
     if (j0 >= ncols) return;
     const int r0 = s * kc, r1 = min(L, r0 + kc);
     gmem<const float> Y = gptr((const float*)Jb.Z + (int64_t)k * d + k);
-    gmem<const float> C = gptr((const float*)(q_mode ? Jb.X + (int64_t)k * d + k : Jb.Z + (int64_t)k * d + k + jb));
+    gmem<const float> C = gptr((const float*)Jb.Z + (int64_t)k * d + k + jb);
 
     f32x16 acc[NB][4];
 #pragma unroll
@@ -486,17 +497,16 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
     }
 }
 
-// W2[:, j] = T^T (sum_s W_s[:, j])  (factorisation)   or   T (...)  (Q formation).
-__global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, QrClasses C,
-                                                       int p, int q_mode) {
+// W2[:, j] = T^T (sum_s W_s[:, j]).
+__global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, QrClasses C, int p) {
     __shared__ float Ts[PB][PB + 1];
     int job, local;
-    if (!qr_locate(C, QG_REDUCE, p, q_mode, blockIdx.x, job, local)) return;
+    if (!qr_locate(C, QG_REDUCE, p, blockIdx.x, job, local)) return;
     const QrJob Jb = jobs[job];
     const int k = p * PB;
     const int d = Jb.d;
-    const int jb = min(PB, d - k), L = d - k;
-    const int ncols = q_mode ? L : L - jb;
+    const int L = d - k;
+    const int ncols = qr_inblock_cols(d, p);
     gmem<const float> Tp = gptr((const float*)Jb.T + (int64_t)p * PB * PB);
     for (int e = threadIdx.x; e < PB * PB; e += 256) Ts[e / PB][e % PB] = Tp[e];
     __syncthreads();
@@ -517,7 +527,7 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
     for (int c = 0; c < PB; ++c) {
         float acc = 0.f;
 #pragma unroll
-        for (int l = 0; l < PB; ++l) acc += (q_mode ? Ts[c][l] : Ts[l][c]) * w[l];
+        for (int l = 0; l < PB; ++l) acc += Ts[l][c] * w[l];
         gptr(Jb.W2)[(int64_t)c * d + j] = acc;
     }
 }
@@ -547,7 +557,35 @@ __global__ __launch_bounds__(256) void copy_cols_kernel(const CopyJob* __restric
     gptr(J.dst)[i * d + j] = gptr(J.src)[i * d + j];
 }
 
+// Yb[i][c] = Y[kB + i][kB + c] of outer block b as a unit-lower matrix
+// (zeros above the diagonal, ones on it, the stored reflectors below), for
+// i < d - kB and c < NB; columns past the matrix are zero.
+__global__ __launch_bounds__(256) void qr_copy_block_kernel(const QrJob* __restrict__ jobs, int b) {
+    const QrJob J = jobs[blockIdx.y];
+    const int kB = b * kQrNB;
+    const int64_t d = J.d, L = d - kB;
+    if (L <= 0) return;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= L * kQrNB) return;
+    const int64_t i = e / kQrNB;
+    const int c = (int)(e - i * kQrNB);
+    float v = 0.f;
+    if (kB + c < d) {
+        if (i == c) v = 1.f;
+        else if (i > c) v = gptr(J.Z)[(kB + i) * d + kB + c];
+    }
+    gptr(J.Yb)[e] = v;
+}
+
 }  // namespace
+
+hipError_t launch_qr_copy_block(const QrJob* jobs, int njobs, int b, int max_d, hipStream_t s) {
+    const int64_t L = (int64_t)max_d - (int64_t)b * kQrNB;
+    if (njobs <= 0 || L <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qr_copy_block_kernel, dim3((unsigned)((L * kQrNB + 255) / 256), njobs), dim3(256), 0, s,
+                       jobs, b);
+    return hipGetLastError();
+}
 
 hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s) {
     const int L = max_d - p * PB;
@@ -566,17 +604,17 @@ hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipSt
     return hipGetLastError();
 }
 
-hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
-    const int blocks = qr_total_blocks(C, QG_DOTS, p, q_mode);
+hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_DOTS, p);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_dots_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p, q_mode);
+    hipLaunchKernelGGL(qr_dots_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p);
     return hipGetLastError();
 }
 
-hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, int q_mode, hipStream_t s) {
-    const int blocks = qr_total_blocks(C, QG_REDUCE, p, q_mode);
+hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s) {
+    const int blocks = qr_total_blocks(C, QG_REDUCE, p);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_reduce_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p, q_mode);
+    hipLaunchKernelGGL(qr_reduce_kernel, dim3(blocks), dim3(256), 0, s, jobs, C, p);
     return hipGetLastError();
 }
 

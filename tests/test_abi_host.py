@@ -178,3 +178,16 @@ def test_refresh_batches_follow_their_cap(N):
     large = N.opt_group_workspace_size(d, hp(N, refresh_capacity_bytes=1 << 36))
     assert small < large
     assert large >= 64 * 2 * 4 * 2048 * 2048               # every QR input of one batch
+
+
+def test_bench_selects_rotation_dispatches_from_non_refresh_steps():
+    """The counter summary takes only grouped GEMMs of steps without a QR
+    kernel: the refresh uses the same GEMM instantiations."""
+    import bench
+    gemm = "void matopt::(anonymous namespace)::gemm_grouped_kernel<matopt::(anonymous namespace)::Cfg<2, 4, 4, 2>, false, false, false, false>(matopt::(anonymous namespace)::GemmArgs)"
+    seq = ["copyBuffer", "momentum_kernel", "momentum_kernel", gemm, "qr_panel_kernel", gemm, gemm,
+           "rotated_adam_kernel", gemm, "momentum_kernel", "momentum_kernel", gemm, gemm,
+           "rotated_adam_kernel", gemm, gemm]
+    rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": k} for i, k in enumerate(seq)]
+    picked = bench.rotation_dispatches(list(reversed(rows)))
+    assert [int(r["Dispatch_Id"]) for r in picked] == [12, 13, 15, 16]
