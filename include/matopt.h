@@ -123,6 +123,36 @@ opt_status opt_group_step(opt_group_t g, void* stream);
  * passes (>= 1); W, M, v and t are untouched. Enqueues on `stream`. */
 opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* stream);
 
+/* ---- state checks and basis repair ---------------------------------------
+ * Both use the group's workspace like step and refresh: calls on one group
+ * must not overlap in time (use one stream, or synchronise between them). */
+
+/* Health of one matrix. The Pipeline-parallelism page (section 5.1) checks
+ * that the rotation matrices stay orthogonal; the three-layer decoupling page
+ * flags a contaminated second moment when std(v) / mean(|v|) exceeds 10
+ * (section 4.3) and watches min(v) (section 4.4). */
+typedef struct {
+    double orth_U;      /* max_ij |(U^T U - I)_ij|, from an fp32 Gram matrix (floor ~1e-6); inf if not finite */
+    double orth_V;      /* the same for V */
+    double v_mean_abs;  /* mean |v| */
+    double v_std;       /* population standard deviation of v */
+    double v_min;       /* minimum of v (NaN entries skipped; they are counted below) */
+    double v_max;
+    int64_t nonfinite;  /* NaN and +-Inf entries of W, M and v */
+} opt_health;
+
+/* Fills out[i] for every matrix i (input order, `count` entries as given at
+ * create). Enqueues on `stream`, then synchronises it. Sums are float64. */
+opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream);
+
+/* Restores the orthonormality of every U and V with `iters` (>= 0)
+ * Newton-Schulz steps X <- X (3 I - X^T X) / 2, which converge quadratically
+ * to the polar factor X (X^T X)^(-1/2) (the Pipeline-parallelism page,
+ * section 5.1) when ||X^T X - I||_2 < 1 (check with opt_group_health first:
+ * orth < 1 / (order) suffices); one step takes a drift e to about 1.5 e^2,
+ * down to the fp32 floor. Enqueues on `stream`. */
+opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream);
+
 /* Step counter, for checkpoint/resume (all other state is caller-owned). */
 opt_status opt_group_get_step(opt_group_t g, int64_t* t);
 opt_status opt_group_set_step(opt_group_t g, int64_t t);   /* t >= 0 */

@@ -119,6 +119,14 @@ class RotatedAdamGroup:
         native.opt_group_set_lr(self._g, lr)
         self.hp.lr = lr
 
+    def health(self, stream=None):
+        """Per-matrix state checks: orthogonality drift of U and V, statistics
+        of v, non-finite count of W, M, v (synchronises the stream)."""
+        return native.opt_group_health(self._g, len(self.descs), stream_ptr(stream))
+
+    def reorthonormalize(self, iters: int = 1, stream=None):
+        native.opt_group_reorthonormalize(self._g, iters, stream_ptr(stream))
+
     def set_timing(self, enable: bool):
         native.opt_group_set_timing(self._g, enable)
 

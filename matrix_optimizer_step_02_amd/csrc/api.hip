@@ -101,13 +101,29 @@ struct Group {
     uint64_t rot_bytes = 0;
 };
 
+// One Newton-Schulz row chunk of a refresh batch's bases: P = X[rows] G
+// (K-chunk steps), then X[rows] = 1.5 X[rows] - 0.5 P.
+struct NsChunk {
+    std::vector<std::vector<GemmLaunch>> prod;
+    uint64_t jobs = 0;
+    int njobs = 0;
+    int64_t max_n = 0;
+};
+
 // Matrices refreshed together: Gram products, completion copies, QR jobs.
+// The same batch (and scratch layout) serves the state checks and the
+// re-orthonormalisation: gram forms X^T X of every basis in its QR input
+// buffer Z.
 struct RefreshBatch {
     std::vector<int> mats;
     std::vector<std::vector<GemmLaunch>> prod1, prod2;   // K-chunk steps, run in order
     CopyLaunch comp;
     QrBatch qr;
     uint64_t ref_bytes = 0;
+    std::vector<std::vector<GemmLaunch>> gram;
+    uint64_t drift_jobs = 0;
+    int ndrift = 0, drift_max_d = 0;
+    std::vector<NsChunk> ns;
 };
 
 // Append-only image of device tables with 256-byte aligned entries.
@@ -134,6 +150,11 @@ struct opt_group_s {
     uint64_t ws_bytes = 0;
     Image img;
     uint64_t table_bytes = 0, scratch_bytes = 0;
+    // state checks: one scan over every matrix (partials at the start of the
+    // scratch), per-matrix records in the table region
+    uint64_t health_segs = 0, health_out = 0;
+    int health_nseg = 0;
+    int64_t health_chunks = 0;
     int device = 0;
     // timing
     bool timing = false;
@@ -358,6 +379,10 @@ int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
 // rounding error of the refresh products and of the QR's long reductions
 // near that of a blocked CPU GEMM instead of growing with the full K.
 constexpr int64_t kChunkK = 1024;
+
+// Rows of a basis per Newton-Schulz product launch: the product goes to the
+// QR job's `part` buffer, which holds kQrMaxSplits * kQrPB rows of d floats.
+constexpr int64_t kNsRows = (int64_t)kQrMaxSplits * kQrPB;
 
 // The K range [k0, k0 + kc) of a product, as a product of its own.
 PGemm k_slice(const PGemm& g, int64_t k0, int64_t kc, float beta) {
@@ -584,7 +609,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         uint64_t off = 0;
         std::vector<PGemm> p1, p2;
         std::vector<CopyJob> comp;
-        struct JobSrc { int64_t d; float* Z; float* X; };
+        struct JobSrc { int64_t d; float* Z; float* X; int mat; int side; };
         std::vector<JobSrc> jsrc;
         for (int mi : members) {
             const Mat& M = g->mats[mi];
@@ -604,11 +629,13 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
             p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
             if (r < m) comp.push_back({x.U, ZU, (int32_t)m, (int32_t)r});
             if (r < n) comp.push_back({x.V, ZV, (int32_t)n, (int32_t)r});
-            jsrc.push_back({m, ZU, x.U});
-            jsrc.push_back({n, ZV, x.V});
+            jsrc.push_back({m, ZU, x.U, M.idx, 0});
+            jsrc.push_back({n, ZV, x.V, M.idx, 1});
         }
         std::stable_sort(jsrc.begin(), jsrc.end(), [](const JobSrc& a, const JobSrc& b) { return a.d > b.d; });
         std::vector<QrJob> jobs;
+        std::vector<DriftJob> drift;
+        for (const JobSrc& js : jsrc) drift.push_back({js.Z, (int32_t)js.d, js.mat, js.side});
         for (const JobSrc& js : jsrc) {
             QrJob j{};
             j.Z = js.Z;
@@ -646,8 +673,63 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
             put_steps(st.fact, R.qr.fact);
             put_steps(st.qform, R.qr.qform);
         }
+        // state checks and Newton-Schulz steps on the same buffers: G = X^T X
+        // in Z, P = X[rows] G in the job's part buffer (kNsRows x d)
+        {
+            std::vector<std::vector<PGemm>> gram;
+            int64_t max_d = 0;
+            for (const QrJob& j : jobs) {
+                const int64_t d = j.d;
+                max_d = std::max(max_d, d);
+                add_k_chunked(gram, mk(true, false, j.X, false, d, j.X, false, d, j.Z, d, d, d, d, 1.f, 0.f));
+            }
+            for (const std::vector<PGemm>& st : gram) R.gram.push_back(put_gemm(g->img, st));
+            R.ndrift = (int)drift.size();
+            R.drift_max_d = (int)max_d;
+            R.drift_jobs = g->img.put(drift);
+            for (int64_t r0 = 0; r0 < max_d; r0 += kNsRows) {
+                std::vector<std::vector<PGemm>> prod;
+                std::vector<NsJob> nj;
+                NsChunk C;
+                for (const QrJob& j : jobs) {
+                    const int64_t d = j.d;
+                    if (d <= r0) continue;
+                    const int64_t rows = std::min<int64_t>(kNsRows, d - r0);
+                    add_k_chunked(prod, mk(false, false, j.X + r0 * d, false, d, j.Z, false, d, j.part, d, rows, d, d,
+                                           1.f, 0.f));
+                    nj.push_back({j.X + r0 * d, j.part, rows * d});
+                    C.max_n = std::max(C.max_n, rows * d);
+                }
+                for (const std::vector<PGemm>& st : prod) C.prod.push_back(put_gemm(g->img, st));
+                C.njobs = (int)nj.size();
+                C.jobs = g->img.put(nj);
+                R.ns.push_back(std::move(C));
+            }
+        }
         g->scratch_bytes = std::max(g->scratch_bytes, R.ref_bytes);
         g->rbatches.push_back(std::move(R));
+    }
+    // state checks: every matrix, input order
+    {
+        std::vector<HealthSeg> hs;
+        int64_t chunks = 0;
+        for (const Mat& M : g->mats) {
+            HealthSeg h{};
+            h.W = M.d.W;
+            h.M = M.d.M;
+            h.v = M.d.v;
+            h.n = M.d.m * M.d.n;
+            h.chunk_begin = chunks;
+            h.m_bf16 = M.bf16;
+            h.out = M.idx;
+            chunks += (h.n + kEwChunk - 1) / kEwChunk;
+            hs.push_back(h);
+        }
+        g->health_nseg = (int)hs.size();
+        g->health_chunks = chunks;
+        g->health_segs = g->img.put(hs);
+        g->health_out = g->img.put(std::vector<HealthOut>(g->mats.size()));
+        g->scratch_bytes = std::max(g->scratch_bytes, align_up(sizeof(HealthPartial) * (uint64_t)chunks));
     }
     g->table_bytes = align_up(g->img.bytes.size());
 }
@@ -961,6 +1043,65 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
     for (const RefreshBatch& R : g->rbatches)
         if ((e = run_refresh(g, R, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
+    return OPT_OK;
+}
+
+opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
+    opt_status st = check_group(g);
+    if (st || (st = set_device(g))) return st;
+    if (!out) return fail(OPT_EINVAL, "out is NULL");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before health");
+    hipStream_t s = (hipStream_t)stream;
+    HealthOut* dout = (HealthOut*)(g->ws + g->health_out);
+    HealthPartial* part = (HealthPartial*)(g->ws + g->table_bytes);
+    const HealthSeg* segs = dptr<HealthSeg>(g, g->health_segs);
+    if ((e = launch_health_clear(dout, (int)g->mats.size(), s))) return hip_fail(e, "health launch");
+    if ((e = launch_health_partials(segs, g->health_nseg, g->health_chunks, part, s))) return hip_fail(e, "health launch");
+    if ((e = launch_health_final(segs, g->health_nseg, part, dout, s))) return hip_fail(e, "health launch");
+    for (const RefreshBatch& R : g->rbatches) {
+        for (const std::vector<GemmLaunch>& stp : R.gram)
+            if ((e = run_gemm(g, stp, 1.f, s))) return hip_fail(e, "Gram launch");
+        if ((e = launch_drift(dptr<DriftJob>(g, R.drift_jobs), R.ndrift, R.drift_max_d, dout, s)))
+            return hip_fail(e, "drift launch");
+    }
+    std::vector<HealthOut> h(g->mats.size());
+    if ((e = hipMemcpyAsync(h.data(), dout, sizeof(HealthOut) * h.size(), hipMemcpyDeviceToHost, s)))
+        return hip_fail(e, "health copy");
+    if ((e = hipStreamSynchronize(s))) return hip_fail(e, "health synchronise");
+    for (size_t i = 0; i < h.size(); ++i) {
+        const HealthOut& r = h[i];
+        const double n = (double)r.n, mean = r.s / n;
+        opt_health& o = out[i];
+        o.orth_U = __builtin_bit_cast(float, r.drift_u);
+        o.orth_V = __builtin_bit_cast(float, r.drift_v);
+        o.v_mean_abs = r.sabs / n;
+        o.v_std = std::sqrt(std::max(0.0, r.s2 / n - mean * mean));
+        o.v_min = r.vmin;
+        o.v_max = r.vmax;
+        o.nonfinite = r.nonfinite;
+    }
+    return OPT_OK;
+}
+
+opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream) {
+    opt_status st = check_group(g);
+    if (st || (st = set_device(g))) return st;
+    if (iters < 0) return fail(OPT_EINVAL, "iters must be >= 0");
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");
+    hipStream_t s = (hipStream_t)stream;
+    for (int it = 0; it < iters; ++it)
+        for (const RefreshBatch& R : g->rbatches) {
+            for (const std::vector<GemmLaunch>& stp : R.gram)
+                if ((e = run_gemm(g, stp, 1.f, s))) return hip_fail(e, "Gram launch");
+            for (const NsChunk& C : R.ns) {
+                for (const std::vector<GemmLaunch>& stp : C.prod)
+                    if ((e = run_gemm(g, stp, 1.f, s))) return hip_fail(e, "Newton-Schulz product launch");
+                if ((e = launch_ns_combine(dptr<NsJob>(g, C.jobs), C.njobs, C.max_n, s)))
+                    return hip_fail(e, "Newton-Schulz combine launch");
+            }
+        }
     return OPT_OK;
 }
 

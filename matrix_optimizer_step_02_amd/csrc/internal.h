@@ -141,6 +141,57 @@ hipError_t launch_qr_init_q(const QrJob* jobs, int njobs, int max_d, hipStream_t
 // Yb of outer block b for the first njobs jobs (those with d > b NB).
 hipError_t launch_qr_copy_block(const QrJob* jobs, int njobs, int b, int max_d, hipStream_t s);
 
+// -------------------------------------------------------------- health ----
+
+// One matrix of the state checks: W, M and v scanned in chunks of kEwChunk.
+struct HealthSeg {
+    const float* W;
+    const void* M;
+    const float* v;
+    int64_t n;            // elements
+    int64_t chunk_begin;  // first chunk of this matrix in the launch
+    int32_t m_bf16;
+    int32_t out;          // index of the matrix's record (input order)
+};
+// Per-chunk partial statistics of v and non-finite count of W, M, v.
+struct HealthPartial {
+    double sabs, s, s2;
+    float vmin, vmax;
+    int64_t nonfinite;
+};
+// Per-matrix record: sums in float64, extremes, and the orthogonality drifts
+// of U and V as float bit patterns (non-negative, so integer order is float
+// order and the maximum can be taken with an integer atomic).
+struct HealthOut {
+    double sabs, s, s2;
+    float vmin, vmax;
+    uint32_t drift_u, drift_v;
+    int64_t nonfinite;
+    int64_t n;
+};
+// max |G - I| of one d x d Gram matrix G = X^T X into out[out].drift_u or _v.
+struct DriftJob {
+    const float* G;
+    int32_t d;
+    int32_t out;
+    int32_t which;   // 0: U, 1: V
+};
+// X <- 1.5 X - 0.5 P over n contiguous elements (a Newton-Schulz step on a
+// block of rows, P = X G for those rows).
+struct NsJob {
+    float* X;
+    const float* P;
+    int64_t n;
+};
+
+hipError_t launch_health_clear(HealthOut* out, int n, hipStream_t s);
+hipError_t launch_health_partials(const HealthSeg* segs, int nseg, int64_t chunks, HealthPartial* part,
+                                  hipStream_t s);
+hipError_t launch_health_final(const HealthSeg* segs, int nseg, const HealthPartial* part, HealthOut* out,
+                               hipStream_t s);
+hipError_t launch_drift(const DriftJob* jobs, int njobs, int max_d, HealthOut* out, hipStream_t s);
+hipError_t launch_ns_combine(const NsJob* jobs, int njobs, int64_t max_n, hipStream_t s);
+
 // Strided copy of columns [c0, d) of X into Z (both d x d, row stride d):
 // the completion block of the refresh input.
 struct CopyJob {

@@ -25,7 +25,7 @@ EXPORTED = (
     "opt_group_get_step", "opt_group_set_step", "opt_group_set_lr", "opt_plan",
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
     "opt_gemm", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
-    "opt_partition_dp", "opt_plan_host_ranks",
+    "opt_partition_dp", "opt_plan_host_ranks", "opt_group_health", "opt_group_reorthonormalize",
 )
 
 
@@ -48,6 +48,13 @@ class opt_hparams(C.Structure):
         ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("lr", C.c_float),
         ("K", C.c_int32), ("power_iters", C.c_int32),
         ("capacity_bytes", C.c_uint64), ("refresh_capacity_bytes", C.c_uint64), ("flags", C.c_uint32),
+    ]
+
+
+class opt_health(C.Structure):
+    _fields_ = [
+        ("orth_U", C.c_double), ("orth_V", C.c_double), ("v_mean_abs", C.c_double), ("v_std", C.c_double),
+        ("v_min", C.c_double), ("v_max", C.c_double), ("nonfinite", C.c_int64),
     ]
 
 
@@ -82,6 +89,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "opt_gemm": ([i32, i32, i64, i64, i64, f32, vp, i32, i64, vp, i32, i64, f32, vp, i64, vp], i32),
         "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
         "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
+        "opt_group_health": ([vp, C.POINTER(opt_health), vp], i32),
+        "opt_group_reorthonormalize": ([vp, i32, vp], i32),
         "opt_partition_dp": ([C.POINTER(C.c_double), i64, C.POINTER(i64), i32, i32, C.c_double,
                               C.POINTER(i32), C.POINTER(C.c_double)], i32),
         "opt_plan_host_ranks": ([C.POINTER(C.c_double), C.POINTER(u64), i64, i32, u64, C.POINTER(i32),
@@ -155,6 +164,17 @@ def opt_plan(descs, hp: opt_hparams):
     ng = C.c_int32(0)
     _check(load().opt_plan(arr, n, C.byref(hp), order, group_of, C.byref(ng)))
     return list(order), list(group_of), ng.value
+
+
+def opt_group_health(g: int, count: int, stream_ptr: int):
+    """Returns a list of dicts (one per matrix, input order)."""
+    out = (opt_health * count)()
+    _check(load().opt_group_health(C.c_void_p(g), out, C.c_void_p(stream_ptr)))
+    return [{f: getattr(h, f) for f, _ in opt_health._fields_} for h in out]
+
+
+def opt_group_reorthonormalize(g: int, iters: int, stream_ptr: int):
+    _check(load().opt_group_reorthonormalize(C.c_void_p(g), iters, C.c_void_p(stream_ptr)))
 
 
 def opt_group_set_timing(g: int, enable: bool):
