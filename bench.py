@@ -203,6 +203,8 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-s", type=float, default=30.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-phase HIP events")
+    ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
+                    help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run a plain device copy of this many MiB first (a dispatch of known size "
                          "for scaling hardware byte counters)")
@@ -248,7 +250,8 @@ def main(argv=None):
         st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0)
         st["G"].copy_(workloads.gradient(wl, i, 1, dev))
         states.append(st)
-    hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes)
+    hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
+                  int(args.refresh_cap_gib * (1 << 30)))
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()

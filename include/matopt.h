@@ -93,7 +93,7 @@ typedef struct {
     int32_t power_iters;      /* orthogonal-iteration passes per refresh, >= 1 */
     uint64_t capacity_bytes;  /* micro-group cap on sum(4 m n); 0 selects 1 << 29 (512 MiB) */
     uint64_t refresh_capacity_bytes; /* cap on the refresh scratch of one refresh batch (the
-                                        d x d QR inputs and their scratch); 0 selects 16 GiB.
+                                        d x d QR inputs and their scratch); 0 selects 48 GiB.
                                         A matrix larger than the cap forms a batch alone. */
     uint32_t flags;           /* reserved, must be 0 */
 } opt_hparams;

@@ -26,7 +26,7 @@ class Hyper:
     K: int = 10
     power_iters: int = 1
     capacity_bytes: int = 1 << 29
-    refresh_capacity_bytes: int = 0   # 0: library default (16 GiB)
+    refresh_capacity_bytes: int = 0   # 0: library default (48 GiB)
 
     def c(self) -> native.opt_hparams:
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,

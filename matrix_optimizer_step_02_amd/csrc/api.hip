@@ -190,7 +190,7 @@ uint64_t capacity_of(const opt_hparams* hp) {
 }
 
 uint64_t refresh_capacity_of(const opt_hparams* hp) {
-    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : (16ull << 30);
+    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : (48ull << 30);
 }
 
 struct Span {
