@@ -52,8 +52,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 namespace {
 
-constexpr int BK = kGemmBK;
-static_assert(BK == 32, "the LDS layouts assume 32-deep slabs (8 groups of 4 k values per row)");
 #ifndef MATOPT_XCD_RUN
 #define MATOPT_XCD_RUN 16
 #endif
@@ -64,9 +62,11 @@ constexpr int XCD = 8;
 constexpr int XCD_RUN = MATOPT_XCD_RUN;
 constexpr int GROUP_M = MATOPT_GROUP_M;
 
-template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N>
+template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N, int SLAB_K = 32>
 struct Cfg {
     static constexpr int WM = WAVES_M, WN = WAVES_N, TM = BLK_M, TN = BLK_N;
+    static constexpr int BK = SLAB_K;   // k values per LDS slab
+    static_assert(BK == 16 || BK == 32, "slabs of 16 or 32 k values (4 or 8 groups of 4 per row)");
     static constexpr int NT = 64 * WAVES_M * WAVES_N;
     static constexpr int BM = 32 * BLK_M * WAVES_M;
     static constexpr int BN = 32 * BLK_N * WAVES_N;
@@ -83,16 +83,32 @@ struct Cfg {
 };
 
 // Configurations of the grouped launches (rotations, Gram products, opt_gemm).
+// The large tile: 256 x 128 outputs per workgroup of 2 x 2 wavefronts (128 x
+// 64 each) with 16-deep slabs: 48 KiB of LDS and at most 256 registers per
+// lane, so two workgroups share a CU and one's barrier or fill wait is
+// covered by the other's MFMAs (measured 1 % faster on the rotation phases
+// than 256 x 256 tiles of 8 wavefronts with 32-deep slabs, one per CU).
+#ifndef MATOPT_LARGE_CFG
+#define MATOPT_LARGE_CFG 2, 2, 4, 2, 16
+#endif
 using SmallCfg = Cfg<2, 2, 2, 2>;
-using LargeCfg = Cfg<2, 4, 4, 2>;
+using LargeCfg = Cfg<MATOPT_LARGE_CFG>;
 static_assert(SmallCfg::BM == kGemmCfgs[0].bm && SmallCfg::BN == kGemmCfgs[0].bn, "tile size mismatch");
 static_assert(LargeCfg::BM == kGemmCfgs[1].bm && LargeCfg::BN == kGemmCfgs[1].bn, "tile size mismatch");
 // Configuration of the QR trailing updates (short K, memory-bound C).
 using QrCfg = Cfg<2, 2, 2, 2>;
 static_assert(QrCfg::BM == kQrTile && QrCfg::BN == kQrTile, "QR tile size mismatch");
 
-// Slot of 16-byte group q in row r of a k-contiguous LDS operand.
-__device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
+// Slot of 16-byte group q in row r of a k-contiguous LDS operand with BK/4
+// groups per row: slot q ^ swz(r). For 8 groups, (r + r/8) mod 8; for 4,
+// ((r/2) ^ (r/4)) mod 4. Either way any 8 aligned consecutive rows, and the
+// rows of one residue among any 16 aligned consecutive rows, fall on distinct
+// 4-bank groups for a 16-byte read.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (BK == 32) return (r + (r >> 3)) & 7;
+    else return ((r >> 1) ^ (r >> 2)) & 3;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) const void* gsrc_ptr;
@@ -106,6 +122,7 @@ typedef __attribute__((address_space(1))) const void* gsrc_ptr;
 template <class C, bool KMAJOR, int R>
 __device__ __forceinline__ void dma_slab(float* buf, const float* base, int64_t ld, int rows, int cols,
                                          int c0, int k0, bool vec) {
+    constexpr int BK = C::BK, G = BK / 4;       // groups of 4 k values per row
     constexpr int CPW = R * BK / 256 / C::NW;   // chunks per wavefront
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -120,9 +137,9 @@ __device__ __forceinline__ void dma_slab(float* buf, const float* base, int64_t 
                 grow = k0 + flat / R;
                 gcol = c0 + flat % R;
             } else {
-                const int r = 8 * c + (lane >> 3);
+                const int r = (256 / BK) * c + lane / G;
                 grow = c0 + r;
-                gcol = k0 + 4 * ((lane & 7) ^ swz(r));
+                gcol = k0 + 4 * ((lane % G) ^ swz<BK>(r));
             }
             grow = grow < rows ? grow : rows - 1;
             gcol = gcol < last ? gcol : last;
@@ -141,9 +158,9 @@ __device__ __forceinline__ void dma_slab(float* buf, const float* base, int64_t 
                     grow = k0 + f / R;
                     gcol = c0 + f % R;
                 } else {
-                    const int r = f >> 5, p = f & 31;
+                    const int r = f / BK, p = f % BK;
                     grow = c0 + r;
-                    gcol = k0 + 4 * ((p >> 2) ^ swz(r)) + (p & 3);
+                    gcol = k0 + 4 * ((p >> 2) ^ swz<BK>(r)) + (p & 3);
                 }
                 grow = grow < rows ? grow : rows - 1;
                 gcol = gcol < cols ? gcol : cols - 1;
@@ -157,13 +174,14 @@ __device__ __forceinline__ void dma_slab(float* buf, const float* base, int64_t 
 // Zero the k values >= K of a slab filled by dma_slab (a partial last slab).
 template <class C, bool KMAJOR, int R>
 __device__ __forceinline__ void zero_k_tail(float* buf, int k0, int K) {
-    const int kv = K - k0;   // valid k values in this slab, 0 < kv < 32
+    constexpr int BK = C::BK;
+    const int kv = K - k0;   // valid k values in this slab, 0 < kv < BK
     for (int e = threadIdx.x; e < R * BK; e += C::NT) {
         if (KMAJOR) {
             if (e / R >= kv) buf[e] = 0.f;
         } else {
-            const int r = e >> 5, kk = e & 31;
-            if (kk >= kv) buf[r * BK + 4 * ((kk >> 2) ^ swz(r)) + (kk & 3)] = 0.f;
+            const int r = e / BK, kk = e % BK;
+            if (kk >= kv) buf[r * BK + 4 * ((kk >> 2) ^ swz<BK>(r)) + (kk & 3)] = 0.f;
         }
     }
 }
@@ -237,7 +255,7 @@ template <class C, bool KMAJOR, int W>
 __device__ __forceinline__ void slab_pos(int q, int& rr, int& c4) {
     const int f = threadIdx.x + C::NT * q;
     if (KMAJOR) { rr = f / (W / 4); c4 = f % (W / 4); }
-    else        { rr = f >> 3;      c4 = f & 7; }
+    else        { rr = f / (C::BK / 4); c4 = f % (C::BK / 4); }
 }
 
 template <class C, bool AT, bool ABF>
@@ -284,7 +302,7 @@ __device__ __forceinline__ void store_a(float* As, const Raw4<ABF> (&r)[C::QA], 
                     else if (row == col + e) v[e] = 1.f;
                 }
             }
-            *(f32x4*)&As[rr * BK + 4 * (c4 ^ swz(rr))] = v;
+            *(f32x4*)&As[rr * C::BK + 4 * (c4 ^ swz<C::BK>(rr))] = v;
         }
     }
 }
@@ -296,7 +314,7 @@ __device__ __forceinline__ void store_b(float* Bs, const Raw4<BBF> (&r)[C::QB], 
     for (int q = 0; q < C::QB; ++q) {
         int rr, c4;
         slab_pos<C, !BT, C::BN>(q, rr, c4);
-        if (BT) *(f32x4*)&Bs[rr * BK + 4 * (c4 ^ swz(rr))] = finish4<BBF>(r[q], n0 + rr, k0 + 4 * c4, p.N, p.K);
+        if (BT) *(f32x4*)&Bs[rr * C::BK + 4 * (c4 ^ swz<C::BK>(rr))] = finish4<BBF>(r[q], n0 + rr, k0 + 4 * c4, p.N, p.K);
         else    *(f32x4*)&Bs[rr * C::BN + 4 * c4] = finish4<BBF>(r[q], k0 + rr, n0 + 4 * c4, p.K, p.N);
     }
 }
@@ -327,14 +345,14 @@ __device__ __forceinline__ void read_frags(const float* As, const float* Bs, int
 #pragma unroll
             for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * C::BM + row];
         } else {
-            a[i] = *(const f32x4*)&As[row * BK + 4 * ((2 * g + h) ^ swz(row))];
+            a[i] = *(const f32x4*)&As[row * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(row))];
         }
     }
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
         const int col = wn * 32 * C::TN + j * 32 + l32;
         if (BT) {
-            b[j] = *(const f32x4*)&Bs[col * BK + 4 * ((2 * g + h) ^ swz(col))];
+            b[j] = *(const f32x4*)&Bs[col * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(col))];
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * C::BN + col];
@@ -359,7 +377,7 @@ __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int w
                                          Acc<C>& acc) {
     const int h = lane >> 5, l32 = lane & 31;
 #pragma unroll
-    for (int g = 0; g < BK / 8; ++g) {
+    for (int g = 0; g < C::BK / 8; ++g) {
         f32x4 a[C::TM], b[C::TN];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
@@ -368,14 +386,14 @@ __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int w
 #pragma unroll
                 for (int s = 0; s < 4; ++s) a[i][s] = As[(8 * g + 4 * h + s) * C::BM + row];
             } else {
-                a[i] = *(const f32x4*)&As[row * BK + 4 * ((2 * g + h) ^ swz(row))];
+                a[i] = *(const f32x4*)&As[row * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(row))];
             }
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const int col = wn * 32 * C::TN + j * 32 + l32;
             if (BT) {
-                b[j] = *(const f32x4*)&Bs[col * BK + 4 * ((2 * g + h) ^ swz(col))];
+                b[j] = *(const f32x4*)&Bs[col * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(col))];
             } else {
 #pragma unroll
                 for (int s = 0; s < 4; ++s) b[j][s] = Bs[(8 * g + 4 * h + s) * C::BN + col];
@@ -461,6 +479,7 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
 
     Acc<C> acc;
     acc.zero();
+    constexpr int BK = C::BK, NG = BK / 8;   // k groups of 8 per slab
     const int nk = (p.K + BK - 1) / BK;
     if (nk == 0) {
         epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
@@ -485,15 +504,8 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     // kt+1 is issued unconditionally: past the last slab it reads clamped,
     // valid addresses into the idle buffer, which keeps the slab body one
     // basic block.
-    f32x4 fa0[C::TM], fb0[C::TN], fa1[C::TM], fb1[C::TN];
-    read_frags<C, AT, BT>(smem, smem + 2 * AS, 0, wm, wn, lane, fa0, fb0);
-#define MATOPT_PHASE(FA, FB, NEXT)                              \
-    mma_group<C, 0, 1>(FA, FB, acc);                            \
-    __builtin_amdgcn_sched_barrier(0);                          \
-    NEXT;                                                       \
-    __builtin_amdgcn_sched_barrier(0);                          \
-    mma_group<C, 1, 4>(FA, FB, acc);                            \
-    __builtin_amdgcn_sched_barrier(0);
+    f32x4 fa[2][C::TM], fb[2][C::TN];
+    read_frags<C, AT, BT>(smem, smem + 2 * AS, 0, wm, wn, lane, fa[0], fb[0]);
     for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
         const int k1 = (kt + 1) * BK;
@@ -502,9 +514,15 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
         fill(cur ^ 1, k1);
         if constexpr (ABF) load_a<C, AT, ABF>(p, m0, k1, ra);
         if constexpr (BBF) load_b<C, BT, BBF>(p, n0, k1, rb);
-        MATOPT_PHASE(fa0, fb0, (read_frags<C, AT, BT>(As, Bs, 1, wm, wn, lane, fa1, fb1)))
-        MATOPT_PHASE(fa1, fb1, (read_frags<C, AT, BT>(As, Bs, 2, wm, wn, lane, fa0, fb0)))
-        MATOPT_PHASE(fa0, fb0, (read_frags<C, AT, BT>(As, Bs, 3, wm, wn, lane, fa1, fb1)))
+#pragma unroll
+        for (int g = 0; g < NG - 1; ++g) {
+            mma_group<C, 0, 1>(fa[g & 1], fb[g & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags<C, AT, BT>(As, Bs, g + 1, wm, wn, lane, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma_group<C, 1, 4>(fa[g & 1], fb[g & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
         if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
         __syncthreads();
@@ -512,23 +530,29 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
             tail(cur ^ 1, k1);
             __syncthreads();
         }
-        // the next slab's first group (past the last slab: values unused)
-        MATOPT_PHASE(fa1, fb1, (read_frags<C, AT, BT>(smem + (cur ^ 1) * AS, smem + 2 * AS + (cur ^ 1) * BS, 0,
-                                                      wm, wn, lane, fa0, fb0)))
+        // the last group, with the next slab's first group read behind its
+        // first MFMAs (past the last slab: values unused)
+        static_assert(NG % 2 == 0, "the last group's fragments are in slot 1");
+        mma_group<C, 0, 1>(fa[1], fb[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags<C, AT, BT>(smem + (cur ^ 1) * AS, smem + 2 * AS + (cur ^ 1) * BS, 0, wm, wn, lane, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_group<C, 1, 4>(fa[1], fb[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
     }
-#undef MATOPT_PHASE
     epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
 }
 
-// C += alpha A B for K <= 2 BK (the QR trailing updates, K = the panel
+// C += alpha A B for K <= 2 slabs (the QR in-block updates, K = the panel
 // width): both K slabs go to the two LDS buffers at once, then the old C
 // fragment is requested so that its latency overlaps the MFMAs; the operand
 // staging registers are dead by then. A is not transposed and read as unit
 // lower trapezoidal (the stored reflectors), B is stored K x N, both fp32.
-static_assert(kQrPB <= 2 * kGemmBK, "the QR update tile holds the whole panel width in two LDS slabs");
+static_assert(kQrPB <= 2 * QrCfg::BK, "the QR update tile holds the whole panel width in two LDS slabs");
 
 __device__ __forceinline__ void qr_update_tile(const GemmProb& p, int tm, int tn, float* smem) {
     using C = QrCfg;
+    constexpr int BK = C::BK;
     constexpr int AS = C::AS, BS = C::BS;
     float* As0 = smem;
     float* As1 = smem + AS;
@@ -616,7 +640,7 @@ struct GemmArgs {
 };
 
 template <class C, bool AT, bool BT, bool ABF, bool BBF>
-__global__ __launch_bounds__(C::NT) void gemm_grouped_kernel(GemmArgs args) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_grouped_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) float smem[C::SMEM];
     const int bid = xcd_remap(blockIdx.x, args.total_tiles);
     GemmProb p;

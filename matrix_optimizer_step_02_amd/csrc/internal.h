@@ -50,16 +50,18 @@ inline int gemm_variant(bool at, bool bt, bool a_bf16, bool b_bf16) {
 
 // Two tile configurations of the grouped GEMM (rotations, Gram products,
 // opt_gemm): 128x128 outputs per workgroup of 2x2 wavefronts (64x64 each),
-// and 256x256 per workgroup of 2x4 wavefronts (128x64 each), which reuses
-// every staged operand twice as often but needs many tiles to fill the GPU
-// (one workgroup per CU). A launch takes the large tiles when it has at
-// least kGemmLargeMinTiles of them.
+// and 256x128 per workgroup of 2x2 wavefronts (128x64 each), which reuses
+// every staged operand more but needs many tiles to fill the GPU. A launch
+// takes the large tiles when it has at least kGemmLargeMinTiles of them.
 struct GemmTileCfg {
     int bm, bn;
 };
-constexpr GemmTileCfg kGemmCfgs[2] = {{128, 128}, {256, 256}};
+#ifndef MATOPT_LARGE_BM
+#define MATOPT_LARGE_BM 256
+#define MATOPT_LARGE_BN 128
+#endif
+constexpr GemmTileCfg kGemmCfgs[2] = {{128, 128}, {MATOPT_LARGE_BM, MATOPT_LARGE_BN}};
 constexpr int kGemmLargeMinTiles = 512;
-constexpr int kGemmBK = 32;
 constexpr int kQrTile = 128;   // output tile of the QR trailing update
 
 // Grouped launch over `nprob` problems laid out back to back in tile space;
