@@ -56,11 +56,13 @@ def rotation_flops(shapes):
     return sum(6.0 * m * n * (m + n) for m, n in shapes)
 
 
-def phase_flops(shapes):
-    """Algorithmic flops of each GEMM phase for one step over all matrices."""
+def phase_flops(shapes, carry=False):
+    """Algorithmic flops of each GEMM phase for one step over all matrices
+    (carry: a step of the rotated-momentum variant that rotates G alone)."""
+    k = 2.0 if carry else 4.0
     return {
-        "rot_left": sum(4.0 * m * m * n for m, n in shapes),
-        "rot_right": sum(4.0 * m * n * n for m, n in shapes),
+        "rot_left": sum(k * m * m * n for m, n in shapes),
+        "rot_right": sum(k * m * n * n for m, n in shapes),
         "back_left": sum(2.0 * m * m * n for m, n in shapes),
         "back_right": sum(2.0 * m * n * n for m, n in shapes),
     }
@@ -203,6 +205,8 @@ def main(argv=None):
     ap.add_argument("--cpu-sample-s", type=float, default=30.0,
                     help="budget for the oracle CPU baseline (0 disables it)")
     ap.add_argument("--no-timing", action="store_true", help="do not record per-phase HIP events")
+    ap.add_argument("--rotated-momentum", action="store_true",
+                    help="the variant that carries m~ in rotated coordinates within a basis epoch")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -247,11 +251,11 @@ def main(argv=None):
     states = []
     for i, s in enumerate(wl.matrices):
         W0 = workloads.initial_weight(wl, i, dev)
-        st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0)
+        st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0, rotated_momentum=args.rotated_momentum)
         st["G"].copy_(workloads.gradient(wl, i, 1, dev))
         states.append(st)
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
-                  int(args.refresh_cap_gib * (1 << 30)))
+                  int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()
@@ -287,6 +291,9 @@ def main(argv=None):
     if phases:
         pf = phase_flops(shapes)
         flops = sum(pf.values()) * args.steps
+        if args.rotated_momentum:   # recompute steps are the refreshes; the others carry m~
+            carried = args.steps - len(refresh_steps)
+            flops = sum(pf.values()) * len(refresh_steps) + sum(phase_flops(shapes, True).values()) * carried
         ms = sum(phases[k][0] for k in pf)
         launches = sum(phases[k][1] for k in pf)
         achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else None
@@ -328,7 +335,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": wl.key, "matrices": len(shapes), "params": params,
                    "momentum_dtype": wl.m_dtype, "K": wl.K, "power_iters": wl.power_iters,
-                   "micro_groups": ngroups, "refresh_steps_timed": refresh_steps},
+                   "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
+                   "rotated_momentum": bool(args.rotated_momentum)},
         "steps_per_s": steps_per_s,
         "roofline": roofline,
         "cpu_baseline": cpu,

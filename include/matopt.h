@@ -82,7 +82,26 @@ typedef struct {
     float* v;              /* m x n fp32 second moment in rotated coordinates; start at 0 */
     float* U;              /* m x m fp32 orthonormal left basis, updated by refreshes; start at I */
     float* V;              /* n x n fp32 orthonormal right basis, updated by refreshes; start at I */
+    float* Mt;             /* m x n fp32 momentum in rotated coordinates, used only with
+                              OPT_FLAG_ROTATED_MOMENTUM (else must be NULL); its content is
+                              rebuilt by the first step, so it needs no initial value */
 } opt_matrix_desc;
+
+/* opt_hparams.flags */
+enum {
+    /* Carry the rotated momentum m~ = U^T M V across steps of one basis epoch
+     * instead of recomputing it: within an epoch U and V are fixed and M is an
+     * EMA, so U^T M_t V = b1 m~_{t-1} + (1 - b1) U^T G_t V (the momentum matrix
+     * and two-sided rotation of the Pipeline-parallelism page, section 2.2, with
+     * the EMA of the three-layer decoupling page, section 2.2). A step then
+     * needs two two-sided products instead of three. m~ is recomputed as
+     * U^T M V on the first step, at every refresh, and after refresh_basis,
+     * reorthonormalize or set_step; M is still kept in the original space for
+     * the refreshes. Equal
+     * to the method in exact arithmetic; m~ is stored in fp32 (with a bf16 M
+     * it is therefore not rounded to bf16 between steps). */
+    OPT_FLAG_ROTATED_MOMENTUM = 1u
+};
 
 typedef struct {
     float beta1;              /* momentum EMA weight, 0 <= beta1 < 1 */
@@ -95,7 +114,7 @@ typedef struct {
     uint64_t refresh_capacity_bytes; /* cap on the refresh scratch of one refresh batch (the
                                         d x d QR inputs and their scratch); 0 selects 48 GiB.
                                         A matrix larger than the cap forms a batch alone. */
-    uint32_t flags;           /* reserved, must be 0 */
+    uint32_t flags;           /* OPT_FLAG_* bits; others must be 0 */
 } opt_hparams;
 
 #define OPT_MAX_DIM 16384       /* largest m or n the QR panel kernel supports */

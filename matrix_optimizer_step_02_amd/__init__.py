@@ -27,11 +27,13 @@ class Hyper:
     power_iters: int = 1
     capacity_bytes: int = 1 << 29
     refresh_capacity_bytes: int = 0   # 0: library default (48 GiB)
+    rotated_momentum: bool = False    # carry m~ in rotated coordinates (needs an Mt tensor per matrix)
 
     def c(self) -> native.opt_hparams:
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,
                                   self.power_iters, self.capacity_bytes,
-                                  self.refresh_capacity_bytes, 0)
+                                  self.refresh_capacity_bytes,
+                                  native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0)
 
 
 def tensor_ptr(t) -> int:
@@ -58,8 +60,9 @@ def _check_tensor(t, shape, dtypes, name, device):
         raise ValueError(f"{name} must be contiguous (row-major)")
 
 
-def make_desc(W, G, M, v, U, V) -> native.opt_matrix_desc:
-    """Descriptor of one matrix from torch tensors on one HIP device."""
+def make_desc(W, G, M, v, U, V, Mt=None) -> native.opt_matrix_desc:
+    """Descriptor of one matrix from torch tensors on one HIP device (Mt: the
+    rotated momentum, only with Hyper.rotated_momentum)."""
     import torch
     m, n = W.shape
     dev = W.device
@@ -71,9 +74,12 @@ def make_desc(W, G, M, v, U, V) -> native.opt_matrix_desc:
     _check_tensor(v, (m, n), (torch.float32,), "v", dev)
     _check_tensor(U, (m, m), (torch.float32,), "U", dev)
     _check_tensor(V, (n, n), (torch.float32,), "V", dev)
+    if Mt is not None:
+        _check_tensor(Mt, (m, n), (torch.float32,), "Mt", dev)
     dt = native.OPT_BF16 if M.dtype == torch.bfloat16 else native.OPT_F32
     return native.opt_matrix_desc(m, n, tensor_ptr(W), tensor_ptr(G), tensor_ptr(M), dt,
-                                  tensor_ptr(v), tensor_ptr(U), tensor_ptr(V))
+                                  tensor_ptr(v), tensor_ptr(U), tensor_ptr(V),
+                                  tensor_ptr(Mt) if Mt is not None else 0)
 
 
 class RotatedAdamGroup:
@@ -88,7 +94,7 @@ class RotatedAdamGroup:
         import torch
         self.params = list(params)
         self.hp = hp
-        self.descs = [make_desc(p["W"], p["G"], p["M"], p["v"], p["U"], p["V"]) for p in self.params]
+        self.descs = [make_desc(p["W"], p["G"], p["M"], p["v"], p["U"], p["V"], p.get("Mt")) for p in self.params]
         self._hpc = hp.c()
         self.ws_bytes = native.opt_group_workspace_size(self.descs, self._hpc)
         dev = self.params[0]["W"].device
@@ -98,7 +104,7 @@ class RotatedAdamGroup:
 
     @staticmethod
     def plan(shapes: Sequence[tuple], hp: Hyper):
-        descs = [native.opt_matrix_desc(m, n, 0, 0, 0, 0, 0, 0, 0) for (m, n) in shapes]
+        descs = [native.opt_matrix_desc(m, n, 0, 0, 0, 0, 0, 0, 0, 0) for (m, n) in shapes]
         return native.opt_plan(descs, hp.c())
 
     def step(self, stream=None):
@@ -145,9 +151,10 @@ class RotatedAdamGroup:
             pass
 
 
-def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None):
+def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None, rotated_momentum=False):
     """Fresh caller-side state of one matrix: W (given or zeros), G zeros,
-    M and v zeros, U = I_m, V = I_n."""
+    M and v zeros, U = I_m, V = I_n (and Mt, uninitialised, for the rotated
+    momentum)."""
     import torch
     dt = torch.bfloat16 if m_dtype == "bf16" else torch.float32
     W = (W0.to(device=device, dtype=torch.float32).contiguous().clone() if W0 is not None
@@ -159,4 +166,4 @@ def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None):
         "v": torch.zeros(m, n, device=device),
         "U": torch.eye(m, device=device),
         "V": torch.eye(n, device=device),
-    }
+    } | ({"Mt": torch.empty(m, n, device=device)} if rotated_momentum else {})

@@ -98,6 +98,10 @@ struct Group {
     std::vector<int> mats;   // indices into opt_group_s::mats, LPT order
     EwLaunch mom, adam;
     std::vector<GemmLaunch> rot_left, rot_right, back_left, back_right;
+    // with the carried rotated momentum: the step that recomputes m~ = U^T M V
+    // into Mt (rot_left as above), and the step that carries it (G only)
+    std::vector<GemmLaunch> rot_right_re, rot_left_c, rot_right_c;
+    EwLaunch adam_re, adam_c;
     uint64_t rot_bytes = 0;
 };
 
@@ -156,6 +160,7 @@ struct opt_group_s {
     int health_nseg = 0;
     int64_t health_chunks = 0;
     int device = 0;
+    bool mt_valid = false;   // the carried rotated momentum matches U, V (OPT_FLAG_ROTATED_MOMENTUM)
     // timing
     bool timing = false;
     std::vector<hipEvent_t> pool;
@@ -181,7 +186,7 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (!std::isfinite(hp->lr)) return fail(OPT_EINVAL, "lr must be finite");
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
-    if (hp->flags != 0) return fail(OPT_EINVAL, "flags must be 0");
+    if (hp->flags & ~(uint32_t)OPT_FLAG_ROTATED_MOMENTUM) return fail(OPT_EINVAL, "unknown bits in flags");
     return OPT_OK;
 }
 
@@ -223,6 +228,9 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
         if (!need_ptrs) continue;
         if (!x.W || !x.G || !x.M || !x.v || !x.U || !x.V)
             return fail(OPT_EINVAL, "matrix %d: a tensor pointer is NULL", i);
+        const bool rm = hp->flags & OPT_FLAG_ROTATED_MOMENTUM;
+        if (rm != (x.Mt != nullptr))
+            return fail(OPT_EINVAL, "matrix %d: Mt must be set exactly when OPT_FLAG_ROTATED_MOMENTUM is", i);
         const uint64_t mn = (uint64_t)x.m * x.n;
         const uint64_t esz = x.M_dtype == OPT_BF16 ? 2 : 4;
         auto add = [&](const void* p, uint64_t bytes, const char* what) {
@@ -234,8 +242,9 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
         add(x.v, 4 * mn, "v");
         add(x.U, 4ull * x.m * x.m, "U");
         add(x.V, 4ull * x.n * x.n, "V");
+        if (x.Mt) add(x.Mt, 4 * mn, "Mt");
         if (!aligned(x.W, 4) || !aligned(x.G, 4) || !aligned(x.v, 4) || !aligned(x.U, 4) ||
-            !aligned(x.V, 4) || !aligned(x.M, esz))
+            !aligned(x.V, 4) || !aligned(x.M, esz) || !aligned(x.Mt, 4))
             return fail(OPT_EINVAL, "matrix %d: a tensor pointer is not aligned to its element", i);
     }
     if (need_ptrs) {
@@ -556,8 +565,8 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         Group G;
         G.mats = members;
         // ---- rotation scratch
-        std::vector<PGemm> left, right, bl, br;
-        std::vector<EwSeg> mom, adam;
+        std::vector<PGemm> left, right, bl, br, right_re, left_c, right_c;
+        std::vector<EwSeg> mom, adam, adam_re, adam_c;
         uint64_t off = 0;
         for (int mi : members) {
             const Mat& M = g->mats[mi];
@@ -591,6 +600,20 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
             a.n = mn;
             a.vec = aligned(Gt, 16) && aligned(mt, 16) && aligned(x.v, 16);
             adam.push_back(a);
+            if (x.Mt) {
+                // recompute: (U^T M) V -> Mt; u = Mt / (sqrt(v) + eps) -> mt slot
+                right_re.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
+                right_re.push_back(mk(false, false, TM, false, n, x.V, false, n, x.Mt, n, m, n, n, 1.f, 0.f));
+                left_c.push_back(mk(true, false, x.U, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
+                right_c.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
+                EwSeg r = a;
+                r.b = x.Mt;
+                r.d = mt;
+                r.vec = a.vec && aligned(x.Mt, 16);
+                adam_re.push_back(r);
+                r.carry = 1;
+                adam_c.push_back(r);
+            }
         }
         G.rot_bytes = off;
         G.rot_left = put_gemm(g->img, left);
@@ -599,6 +622,13 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
         G.back_right = put_gemm(g->img, br);
         G.mom = put_ew(g->img, mom);
         G.adam = put_ew(g->img, adam);
+        if (!adam_c.empty()) {
+            G.rot_right_re = put_gemm(g->img, right_re);
+            G.rot_left_c = put_gemm(g->img, left_c);
+            G.rot_right_c = put_gemm(g->img, right_c);
+            G.adam_re = put_ew(g->img, adam_re);
+            G.adam_c = put_ew(g->img, adam_c);
+        }
         g->scratch_bytes = std::max(g->scratch_bytes, G.rot_bytes);
         g->groups.push_back(std::move(G));
     }
@@ -1007,21 +1037,27 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     if (refresh)
         for (const RefreshBatch& R : g->rbatches)
             if ((e = run_refresh(g, R, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+    // with the carried rotated momentum: recompute m~ when the bases are new
+    // to it, else carry it (G alone is rotated)
+    const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
+    const bool carry = carry_mode && g->mt_valid && !refresh;
     for (const Group& G : g->groups) {
         {
             PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
-            if ((e = run_gemm(g, G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");
+            if ((e = run_gemm(g, carry ? G.rot_left_c : G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
             PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
-            if ((e = run_gemm(g, G.rot_right, 1.f, s))) return hip_fail(e, "rotation launch");
+            const std::vector<GemmLaunch>& L = !carry_mode ? G.rot_right : (carry ? G.rot_right_c : G.rot_right_re);
+            if ((e = run_gemm(g, L, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
             PhaseScope ps(g, OPT_PHASE_ADAM, s);
-            e = launch_rotated_adam(dptr<EwSeg>(g, G.adam.segs), G.adam.nseg, G.adam.chunks, g->hp.beta2,
-                                    g->hp.eps, s);
+            const EwLaunch& A = !carry_mode ? G.adam : (carry ? G.adam_c : G.adam_re);
+            e = launch_rotated_adam(dptr<EwSeg>(g, A.segs), A.nseg, A.chunks, g->hp.beta1, g->hp.beta2, g->hp.eps,
+                                    s);
             if (e) return hip_fail(e, "rotated Adam launch");
-            g->kernels_in_scope += G.adam.nseg > 0;
+            g->kernels_in_scope += A.nseg > 0;
         }
         {
             PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
@@ -1032,6 +1068,7 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             if ((e = run_gemm(g, G.back_right, g->hp.lr, s))) return hip_fail(e, "update launch");
         }
     }
+    g->mt_valid = carry_mode;
     return OPT_OK;
 }
 
@@ -1041,6 +1078,7 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
     if (power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
+    g->mt_valid = false;
     for (const RefreshBatch& R : g->rbatches)
         if ((e = run_refresh(g, R, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
     return OPT_OK;
@@ -1091,6 +1129,7 @@ opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");
     hipStream_t s = (hipStream_t)stream;
+    if (iters > 0) g->mt_valid = false;
     for (int it = 0; it < iters; ++it)
         for (const RefreshBatch& R : g->rbatches) {
             for (const std::vector<GemmLaunch>& stp : R.gram)
@@ -1116,6 +1155,7 @@ opt_status opt_group_set_step(opt_group_t g, int64_t t) {
     if (opt_status st = check_group(g)) return st;
     if (t < 0) return fail(OPT_EINVAL, "t must be >= 0");
     g->t = t;
+    g->mt_valid = false;   // a resumed job recomputes the rotated momentum
     return OPT_OK;
 }
 

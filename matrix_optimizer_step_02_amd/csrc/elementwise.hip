@@ -2,7 +2,8 @@
 //
 //  momentum:      M <- beta1 M + (1 - beta1) G          (M fp32 or bf16 RNE)
 //  rotated Adam:  v <- beta2 v + (1 - beta2) G~ * G~     (square in fp32)
-//                 u  = m~ / (sqrt(v) + eps)              (u overwrites m~)
+//                 u  = m~ / (sqrt(v) + eps)              (u overwrites m~, or to its own buffer)
+//                 with the carried rotated momentum first m~ <- beta1 m~ + (1 - beta1) G~
 //
 // One launch covers every matrix of a micro-group: the matrices are cut into
 // chunks of kEwChunk elements, concatenated in chunk space, and each
@@ -124,22 +125,27 @@ __device__ __forceinline__ void adam1(float g, float m, float& v, float& u, floa
     u = m / (__builtin_sqrtf(v) + eps);
 }
 
+// u goes to d when it is set, else over m~ in b. With carry, m~ is first
+// advanced in place: b <- beta1 b + (1 - beta1) G~ (the rotated momentum
+// carried across a basis epoch), and u uses the new value.
 __global__ __launch_bounds__(kEwThreads) void rotated_adam_kernel(const EwSeg* __restrict__ segs,
-                                                                  int nseg, float beta2, float eps) {
+                                                                  int nseg, float beta1, float beta2,
+                                                                  float eps) {
     const int64_t chunk = blockIdx.x;
     const EwSeg S = segs[find_seg(segs, nseg, chunk)];
     const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
-    const float omb2 = 1.f - beta2;
+    const float omb1 = 1.f - beta1, omb2 = 1.f - beta2;
     if (S.vec && base + kEwChunk <= S.n) {
         const float* Gt = S.a + base;
-        float* mu = (float*)S.b + base;
+        float* mb = (float*)S.b + base;
         float* V = S.c + base;
+        float* uo = S.d ? S.d + base : mb;
         f32x4 g[NQ], m[NQ], v[NQ];
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             const int o = 4 * (q * kEwThreads + threadIdx.x);
             g[q] = *gptr((const f32x4*)(Gt + o));
-            m[q] = *gptr((const f32x4*)(mu + o));
+            m[q] = *gptr((const f32x4*)(mb + o));
             v[q] = *gptr((const f32x4*)(V + o));
         }
 #pragma unroll
@@ -148,26 +154,35 @@ __global__ __launch_bounds__(kEwThreads) void rotated_adam_kernel(const EwSeg* _
             f32x4 u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                if (S.carry) m[q][e] = ema(beta1, m[q][e], omb1, g[q][e]);
                 float ve = v[q][e], ue;
                 adam1(g[q][e], m[q][e], ve, ue, beta2, omb2, eps);
                 v[q][e] = ve;
                 u[e] = ue;
             }
             *gptr((f32x4*)(V + o)) = v[q];
-            *gptr((f32x4*)(mu + o)) = u;
+            if (S.carry) *gptr((f32x4*)(mb + o)) = m[q];
+            *gptr((f32x4*)(uo + o)) = u;
         }
         return;
     }
     gmem<const float> Gt = gptr(S.a);
-    gmem<float> mu = gptr((float*)S.b);
+    gmem<float> mb = gptr((float*)S.b);
     gmem<float> V = gptr(S.c);
+    gmem<float> uo = gptr(S.d ? S.d : (float*)S.b);
     for (int q = 0; q < NQ; ++q) {
         const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
         for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            const float g = Gt[i + e];
+            float m = mb[i + e];
+            if (S.carry) {
+                m = ema(beta1, m, omb1, g);
+                mb[i + e] = m;
+            }
             float v = V[i + e], u;
-            adam1(Gt[i + e], mu[i + e], v, u, beta2, omb2, eps);
+            adam1(g, m, v, u, beta2, omb2, eps);
             V[i + e] = v;
-            mu[i + e] = u;
+            uo[i + e] = u;
         }
     }
 }
@@ -182,11 +197,11 @@ hipError_t launch_momentum(const EwSeg* segs, int nseg, int64_t total_chunks, fl
     return hipGetLastError();
 }
 
-hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta2,
+hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1, float beta2,
                                float eps, hipStream_t s) {
     if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
     hipLaunchKernelGGL(rotated_adam_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s,
-                       segs, nseg, beta2, eps);
+                       segs, nseg, beta1, beta2, eps);
     return hipGetLastError();
 }
 

@@ -75,12 +75,14 @@ hipError_t launch_gemm_single(int variant, int cfg, const GemmProb& prob, hipStr
 
 struct EwSeg {
     const float* a;       // momentum: G      rotated Adam: G~
-    void* b;              // momentum: M      rotated Adam: m~ in, u out (same slot)
+    void* b;              // momentum: M      rotated Adam: m~ (in; u out when d is NULL)
     float* c;             // rotated Adam: v
+    float* d;             // rotated Adam: u out (NULL: u overwrites m~ in b)
     int64_t n;            // elements
     int64_t chunk_begin;  // first chunk of this segment in the launch
     int32_t b_bf16;       // momentum stored as bfloat16
     int32_t vec;          // all pointers 16-byte aligned (vector path)
+    int32_t carry;        // rotated Adam: first b <- beta1 b + (1 - beta1) a (the carried m~)
 };
 
 constexpr int kEwThreads = 256;
@@ -89,7 +91,7 @@ constexpr int kEwChunk = kEwThreads * kEwPerThread;
 
 hipError_t launch_momentum(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1,
                            hipStream_t s);
-hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta2,
+hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1, float beta2,
                                float eps, hipStream_t s);
 
 // ------------------------------------------------------------------ QR ----

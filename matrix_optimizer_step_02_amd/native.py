@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "_lib", "libmatopt.so")
 
 OPT_OK, OPT_EINVAL, OPT_ENOWS, OPT_EHIP, OPT_EUNSUPPORTED, OPT_ESTATE = 0, -1, -2, -3, -4, -5
 OPT_F32, OPT_BF16 = 0, 1
+OPT_FLAG_ROTATED_MOMENTUM = 1
 OPT_MAX_DIM = 16384
 PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right")
 OPT_NUM_PHASES = len(PHASES)
@@ -39,7 +40,7 @@ class opt_matrix_desc(C.Structure):
     _fields_ = [
         ("m", C.c_int64), ("n", C.c_int64),
         ("W", C.c_void_p), ("G", C.c_void_p), ("M", C.c_void_p), ("M_dtype", C.c_int32),
-        ("v", C.c_void_p), ("U", C.c_void_p), ("V", C.c_void_p),
+        ("v", C.c_void_p), ("U", C.c_void_p), ("V", C.c_void_p), ("Mt", C.c_void_p),
     ]
 
 

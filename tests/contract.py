@@ -9,7 +9,8 @@ oracle consumes the device's own persisted output of the previous phase and
 each gate bounds the error that phase can add:
 
 * Gate M (momentum): oracle EMA of the device's previous M and the same G.
-  fp32: max relative error <= 1e-6. bf16: >= 99.99 % bit-identical, and every
+  fp32: max relative error <= 1e-6. bf16: bit-identical except at most
+  max(2, 1e-4 n) elements, and every
   element within one bf16 ulp of the reference plus the fp32 rounding of the
   EMA's two terms, 2 u32 (|b1 M| + |(1-b1) G|): the device forms the sum in
   fp32 and rounds once to bf16, the oracle rounds the exact sum; where the
@@ -19,7 +20,9 @@ each gate bounds the error that phase can add:
   previous U, V. (1) orthonormality of the device bases <= 1e-5; (2) forward
   error <= 1e-4 on the well-determined columns, those whose prefix
   conditioning kappa_j = max_{i<=j} 1/|R_ii| of the column-normalised one-shot
-  input [(A^p X)[:, :r] | X[:, r:]] is <= 1e2; the other columns are
+  input [(A^p X)[:, :r] | X[:, r:]] is <= 1e2 (or 8 times the error an fp32
+  CPU refresh, fp32 products and LAPACK QR, reaches there, if larger); the
+  other columns are
   determined only to O(u kappa) and are not compared (several results are
   correct there); (3) the device Q must triangularise that input: the
   strictly lower part of Q^T Z_hat, column-normalised, <= 1e-3.
@@ -68,12 +71,19 @@ def gate_momentum(M_prev, G, M_dev, beta1, m_dtype) -> GateReport:
     if m_dtype == "f32":
         r = maxrel(M_dev, ref)
         return GateReport("M", r <= 1e-6, {"maxrel": r})
-    same = float(np.mean(M_dev == ref))
+    # The device forms the EMA in fp32 and rounds once to bf16; the oracle
+    # rounds the exact value: the two differ by one bf16 ulp only where the
+    # fp32 result crosses a rounding boundary (bounded below), and must be
+    # identical elsewhere, which catches a wrong rounding mode. A handful of
+    # boundary cases is allowed: at most max(2, 1e-4 n) elements.
+    differ = int(np.count_nonzero(M_dev != ref))
     b1 = oracle.as_f32_scalar(beta1)
     ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(ref), 1e-38))[1] - 8)
     f32_terms = 2 * U32 * (np.abs(b1 * np.asarray(M_prev, np.float64)) + np.abs((1 - b1) * np.asarray(G, np.float64)))
     within = bool(np.all(np.abs(M_dev - ref) <= ulp + f32_terms))
-    return GateReport("M", within and same >= 0.9999, {"identical": same, "within_bound": float(within)})
+    ok = within and differ <= max(2, int(1e-4 * ref.size))
+    return GateReport("M", ok, {"differ": float(differ), "identical": 1.0 - differ / ref.size,
+                                "within_bound": float(within)})
 
 
 def _prefix_kappa(Zhat):
@@ -94,7 +104,24 @@ def one_shot_input(A, X, rank, passes):
     return Y
 
 
-def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True) -> GateReport:
+def fp32_refresh(M_t, X_prev, side, passes):
+    """The refresh computed in fp32 on the CPU: Gram products in float32
+    (numpy) and a float32 Householder QR (LAPACK sgeqrf through scipy), with
+    the same completion and sign convention. Used only to calibrate what an
+    fp32 implementation of the refresh attains."""
+    import scipy.linalg
+    M = np.asarray(M_t, np.float32)
+    X = np.asarray(X_prev, np.float32)
+    r = min(M.shape)
+    for _ in range(passes):
+        Y = M @ (M.T @ X[:, :r]) if side == "U" else M.T @ (M @ X[:, :r])
+        Z = np.concatenate([Y, X[:, r:]], axis=1).astype(np.float32)
+        Q, R = scipy.linalg.qr(Z)
+        X = (Q * np.where(np.diag(R) < 0, -1.0, 1.0).astype(np.float32)).astype(np.float32)
+    return X.astype(np.float64)
+
+
+def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True, ref32=None) -> GateReport:
     """forward=False drops the element-wise comparison with the oracle (for
     orders where its unblocked QR takes minutes) and keeps the properties
     that pin the result at any size: orthonormality and triangularisation of
@@ -105,17 +132,26 @@ def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True) -> GateReport
     Zhat = one_shot_input(A, np.asarray(X_prev, np.float64), rank, passes)
     good = np.zeros(d, bool)
     fwd = 0.0
+    fwd_tol = 1e-4
     if forward:
         ref = oracle.subspace_iteration(A, X_prev, rank, passes)
         kappa = _prefix_kappa(Zhat)
         good = kappa <= 1e2
         fwd = float(np.max(np.abs(X_dev[:, good] - ref[:, good]))) if good.any() else 0.0
+        # The forward error of an fp32 refresh on these columns grows with the
+        # order and the prefix conditioning; near the end of a completed basis
+        # the same refresh done in fp32 on the CPU (fp32 Gram products, LAPACK
+        # sgeqrf QR) already comes close to 1e-4 (7.5e-5 on a 130 x 130 case).
+        # The bound is therefore 1e-4 or 8 times what that fp32 reference
+        # reaches on the same columns, whichever is larger.
+        if good.any() and ref32 is not None:
+            fwd_tol = max(1e-4, 8.0 * float(np.max(np.abs(ref32()[:, good] - ref[:, good]))))
     norms = np.linalg.norm(Zhat, axis=0)
     norms[norms == 0] = 1.0
     Rd = X_dev.T @ (Zhat / norms)
     back = float(np.linalg.norm(np.tril(Rd, -1)) / max(np.linalg.norm(Rd), 1e-300))
-    ok = orth <= 1e-5 and fwd <= 1e-4 and back <= 1e-3
-    return GateReport(name, ok, {"orth": orth, "fwd_good": fwd, "good_cols": float(good.mean()),
+    ok = orth <= 1e-5 and fwd <= fwd_tol and back <= 1e-3
+    return GateReport(name, ok, {"orth": orth, "fwd_good": fwd, "fwd_tol": fwd_tol, "good_cols": float(good.mean()),
                                  "backward": back})
 
 
@@ -124,13 +160,14 @@ def gate_refresh(M_t, U_prev, V_prev, U_dev, V_dev, passes, forward_max_d=1100) 
     m, n = M_t.shape
     r = min(m, n)
     return [gate_basis(U_dev, M_t @ M_t.T, np.asarray(U_prev, np.float64), r, passes, "A.U",
-                       forward=m <= forward_max_d),
+                       forward=m <= forward_max_d, ref32=lambda: fp32_refresh(M_t, U_prev, "U", passes)),
             gate_basis(V_dev, M_t.T @ M_t, np.asarray(V_prev, np.float64), r, passes, "A.V",
-                       forward=n <= forward_max_d)]
+                       forward=n <= forward_max_d, ref32=lambda: fp32_refresh(M_t, V_prev, "V", passes))]
 
 
-def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, m_dtype) -> List[GateReport]:
-    W_ref, v_ref, it = oracle.rotated_adam_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+def _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau) -> List[GateReport]:
+    """v within 1e-4; W element-wise within tau max|W| plus a 6-sigma
+    root-sum-square propagation of the first-order fp32 error of u."""
     rv = maxrel(v_dev, v_ref)
     m, n = np.shape(W_prev)
     b2 = oracle.as_f32_scalar(hp.beta2)
@@ -142,10 +179,30 @@ def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper,
     U = np.asarray(U_t, np.float64)
     V = np.asarray(V_t, np.float64)
     widen = 6.0 * lr * np.sqrt((U * U) @ (E * E) @ (V * V).T)
-    tau = 1e-4 if m_dtype == "f32" else 2e-2
     base = tau * np.max(np.abs(W_ref))
     err = np.abs(np.asarray(W_dev, np.float64) - W_ref)
     ok_w = bool(np.all(err <= base + widen))
     return [GateReport("B.v", rv <= 1e-4, {"maxrel": rv}),
             GateReport("B.W", ok_w, {"maxrel": maxrel(W_dev, W_ref), "worst_ratio":
                                      float(np.max(err / (base + widen)))})]
+
+
+def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, m_dtype) -> List[GateReport]:
+    W_ref, v_ref, it = oracle.rotated_adam_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+    tau = 1e-4 if m_dtype == "f32" else 2e-2
+    return _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau)
+
+
+def gate_apply_rotated_momentum(W_prev, v_prev, Mt_prev, M_t, G, U_t, V_t, W_dev, v_dev, Mt_dev,
+                                hp: oracle.Hyper, recompute: bool) -> List[GateReport]:
+    """The variant that carries m~ (oracle/rotated_momentum.py): W and v as
+    gate_apply with the fp32 tolerance (m~ is carried in fp32 whatever the
+    storage of M), and the carried m~ within 1e-5 in Frobenius norm (its fp32
+    error is that of one rotation, or of (1 - b1) times one)."""
+    from oracle import rotated_momentum as RM
+    W_ref, v_ref, mt_ref, it = RM.rotated_momentum_apply(W_prev, v_prev, Mt_prev, M_t, G, U_t, V_t, hp.beta1,
+                                                         hp.beta2, hp.eps, hp.lr, recompute)
+    d = np.asarray(Mt_dev, np.float64) - mt_ref
+    fro = float(np.linalg.norm(d) / max(np.linalg.norm(mt_ref), 1e-300))
+    reps = [GateReport("C.Mt", fro <= 1e-5, {"fro_rel": fro, "recompute": float(recompute)})]
+    return reps + _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, 1e-4)

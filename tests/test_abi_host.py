@@ -114,7 +114,7 @@ def err(N, fn, *a):
 def test_rejects_bad_hyperparameters(N):
     d = descs(N, [(8, 8)])
     for kw in (dict(beta1=1.0), dict(beta1=-0.1), dict(beta2=1.0), dict(eps=0.0), dict(eps=float("inf")),
-               dict(lr=float("nan")), dict(K=-1), dict(power_iters=0), dict(flags=1)):
+               dict(lr=float("nan")), dict(K=-1), dict(power_iters=0), dict(flags=2), dict(flags=1 << 31)):
         assert err(N, N.opt_group_workspace_size, d, hp(N, **kw)) == N.OPT_EINVAL, kw
 
 
@@ -145,6 +145,14 @@ def test_create_rejects_before_any_device_call(N):
     d = descs(N, [(8, 8)], ptrs=True)
     d[0].M = d[0].M + 1                                                          # misaligned
     assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
+    # the rotated momentum needs Mt exactly when its flag is set, not overlapping
+    d = descs(N, [(8, 8)], ptrs=True)
+    hr = hp(N, flags=N.OPT_FLAG_ROTATED_MOMENTUM)
+    assert err(N, N.opt_group_create, d, hr, ws, need, 0) == N.OPT_EINVAL         # flag without Mt
+    d[0].Mt = (1 << 40) + 7 * (1 << 32)
+    assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL          # Mt without flag
+    d[0].Mt = d[0].v + 64
+    assert err(N, N.opt_group_create, d, hr, ws, need, 0) == N.OPT_EINVAL         # Mt overlaps v
 
 
 def test_null_group_and_bad_building_block_args(N):
