@@ -1,0 +1,92 @@
+"""Plain fp64 CPU oracle of the bf16-rotation variant of the step.
+
+TEST INFRASTRUCTURE. Only ``tests/`` and ``__graft_entry__.smoke()`` may
+import or call this module; it shares no code with the HIP path.
+
+[P3] "Pipeline parallelism and gradient staleness optimisation in distributed
+training", section 3.1 (mixed-precision configuration), keeps the rotation
+matrices in a 16-bit float format, on the grounds that the rotation is
+insensitive to their rounding. This variant takes that further: the two-sided
+rotations themselves run on 16-bit operands with binary32 accumulation. The
+16-bit format is bfloat16 rather than the page's float16 (a reading): a matrix
+product needs both operands in one format, the momentum is already bfloat16
+([P2] "Large-model distributed optimisation: three-layer decoupling of
+communication, memory and compute", section 3.3), and bfloat16 keeps the
+binary32 exponent range, so gradients need no scaling. The binary32 bases U,
+V stay the master copies that the refresh starts from; the rotations use
+their bfloat16 roundings.
+
+The rounding points, in order (rb = round to bfloat16, ties to even):
+
+    Ub = rb(U), Vb = rb(V), Gb = rb(G), Mb = rb(M)
+    SG = rb(Gb Vb),  SM = rb(Mb Vb)              right rotation, stored bf16
+    G~ = Ub^T SG,    m~ = Ub^T SM                left rotation, binary32 out
+    v  <- rf(b2 v + (1 - b2) G~^2);  u = m~ / (sqrt(v) + eps)
+    P  = rb(rb(u) Vb^T)                           right rotation back, bf16
+    W  <- rf(W - lr Ub P)                         left rotation back + apply
+
+Products are exact (float64) on the rounded operands; the device accumulates
+them in binary32, which differs from exact far below one bfloat16 ulp.
+
+The first step (t = 1) runs the method's own binary32 rotations. There v is
+zero, so u = m~ / (sqrt(v) + eps) turns every entry of G~ that is zero in
+exact arithmetic (after the step-1 refresh from M = (1 - b1) G, all of G~ off
+its leading diagonal) into (1 - b1) / sqrt(1 - b2) times the sign of its
+rounding error whenever that error exceeds eps / sqrt(1 - b2); bfloat16
+rounding errors of the rotation do (2^-9 |G| against 3e-7 for the default
+eps), which would make the first update a full-size step in roundoff
+directions. From t = 2 on v holds the first step's squares and the rounding
+enters only at its own relative size.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .rotated_adam import (Hyper, OracleState, as_f32_scalar, momentum_update, refresh_bases,
+                           refresh_due, rotated_adam_apply, round_bf16, round_f32)
+
+__all__ = ["bf16_rotation_apply", "step_bf16_rotation"]
+
+
+def bf16_rotation_apply(W, v, M, G, U, V, beta2: float, eps: float, lr: float):
+    """Rotate, run the Adam moments and apply, with the rotations on bfloat16
+    operands at the rounding points listed in the module docstring.
+
+    Returns (W_new, v_new, intermediates) with the float64 values of Ub, Vb,
+    SG, SM, Gt, mt, u, ub, P and dW = Ub P."""
+    b2 = as_f32_scalar(beta2)
+    eps = as_f32_scalar(eps)
+    lr = as_f32_scalar(lr)
+    Ub = round_bf16(U)
+    Vb = round_bf16(V)
+    Gb = round_bf16(G)
+    Mb = round_bf16(M)
+    SG = round_bf16(Gb @ Vb)
+    SM = round_bf16(Mb @ Vb)
+    Gt = Ub.T @ SG
+    mt = Ub.T @ SM
+    v_new = round_f32(b2 * np.asarray(v, np.float64) + (1.0 - b2) * (Gt * Gt))
+    u = mt / (np.sqrt(v_new) + eps)
+    ub = round_bf16(u)
+    P = round_bf16(ub @ Vb.T)
+    dW = Ub @ P
+    W_new = round_f32(np.asarray(W, np.float64) - lr * dW)
+    return W_new, v_new, {"Ub": Ub, "Vb": Vb, "SG": SG, "SM": SM, "Gt": Gt, "mt": mt, "u": u,
+                          "ub": ub, "P": P, "dW": dW}
+
+
+def step_bf16_rotation(state: OracleState, G, hp: Hyper) -> OracleState:
+    """One step of the variant on one matrix: momentum and refresh as the
+    method (binary32 bases), then bf16_rotation_apply, except at t = 1, where
+    the method's rotated_adam_apply runs. Mutates and returns ``state``."""
+    G = round_f32(G)
+    state.t += 1
+    state.M = momentum_update(state.M, G, hp.beta1, state.m_dtype)
+    refreshed = refresh_due(state.t, hp.K)
+    if refreshed:
+        state.U, state.V = refresh_bases(state.M, state.U, state.V, hp.power_iters)
+    apply = rotated_adam_apply if state.t == 1 else bf16_rotation_apply
+    state.W, state.v, inter = apply(state.W, state.v, state.M, G, state.U, state.V, hp.beta2, hp.eps, hp.lr)
+    state.last = dict(inter, refreshed=refreshed, bf16=state.t != 1)
+    return state

@@ -1,0 +1,137 @@
+"""Pins of the bf16-rotation variant's oracle (CPU).
+
+The variant rounds its rotation operands and intermediates to bfloat16. Where
+every rounding is exact (bfloat16-representable inputs rotated by signed
+permutations) it must equal the method with only u rounded; with identity
+bases it must be coordinate-wise Adam with a rounded u; its first step is the
+method's; elsewhere it must stay within bfloat16 rounding of the method.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bf16_rotation as B
+from tests import textbook
+
+HP = oracle.Hyper(0.9, 0.999, 1e-8, 1e-3, 3, 1)
+
+
+def signed_permutation(d, rng):
+    P = np.zeros((d, d))
+    P[np.arange(d), rng.permutation(d)] = rng.choice([-1.0, 1.0], d)
+    return P
+
+
+@pytest.mark.parametrize("shape", [(6, 9), (9, 6), (8, 8)])
+def test_signed_permutation_bases_are_the_method_with_rounded_u(shape):
+    """Signed permutations are orthogonal and exact in bfloat16, and so are
+    the products of bfloat16 matrices with them: every rounding point except
+    u is exact, so v is bitwise the method's and W the method's update with
+    u rounded to bfloat16. The bases are not symmetric, so a transposed
+    basis anywhere in the variant changes the result."""
+    m, n = shape
+    rng = np.random.default_rng(3)
+    U = signed_permutation(m, rng)
+    V = signed_permutation(n, rng)
+    assert not np.array_equal(U, U.T) and not np.array_equal(V, V.T)
+    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(rng.random((m, n)) * 1e-5)
+    Wm, vm, im = oracle.rotated_adam_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    Wb, vb, ib = B.bf16_rotation_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    assert np.array_equal(vb, vm)
+    assert np.array_equal(ib["Gt"], im["Gt"]) and np.array_equal(ib["mt"], im["mt"])
+    lr = oracle.as_f32_scalar(HP.lr)
+    expect = oracle.round_f32(W - lr * (U @ oracle.round_bf16(im["u"]) @ V.T))
+    assert np.array_equal(Wb, expect)
+    assert not np.array_equal(oracle.round_bf16(im["u"]), im["u"])   # the rounding of u is exercised
+
+
+def test_identity_bases_are_coordinatewise_adam_with_rounded_u():
+    m, n = 5, 7
+    rng = np.random.default_rng(4)
+    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = textbook.f32(rng.standard_normal((m, n)) * 1e-2)
+    v = textbook.f32(rng.random((m, n)) * 1e-5)
+    Wb, vb, _ = B.bf16_rotation_apply(W, v, M, G, np.eye(m), np.eye(n), HP.beta2, HP.eps, HP.lr)
+    b2, e, a = (float(np.float32(x)) for x in (HP.beta2, HP.eps, HP.lr))
+    for i in range(m):
+        for j in range(n):
+            vij = textbook.f32(b2 * v[i, j] + (1.0 - b2) * G[i, j] * G[i, j])
+            uij = oracle.round_bf16(np.array([M[i, j] / (np.sqrt(vij) + e)]))[0]
+            assert vb[i, j] == vij
+            assert Wb[i, j] == textbook.f32(W[i, j] - a * uij)
+
+
+def _trajectories(m, n, steps, seed, m_dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    W0 = rng.standard_normal((m, n)) * 1e-2
+    a = oracle.OracleState.fresh(W0, m_dtype)
+    b = oracle.OracleState.fresh(W0, m_dtype)
+    out = []
+    for _ in range(steps):
+        G = rng.standard_normal((m, n)) * 1e-2
+        Wa, Wb = a.W.copy(), b.W.copy()
+        oracle.step(a, G, HP)
+        B.step_bf16_rotation(b, G, HP)
+        out.append(((Wa - a.W), (Wb - b.W), a.last["refreshed"], b.last["bf16"]))
+    return W0, a, b, out
+
+
+def test_first_step_is_the_method():
+    _, a, b, out = _trajectories(12, 20, 1, 5)
+    dA, dB, _, bf16 = out[0]
+    assert np.array_equal(dA, dB) and np.array_equal(a.v, b.v) and not bf16
+
+
+@pytest.mark.parametrize("shape", [(24, 40), (40, 24), (32, 32)])
+def test_apply_within_bf16_rounding_of_the_method(shape):
+    """From the same established state (v from three earlier steps), the
+    variant's update differs from the method's by the bfloat16 roundings of
+    its eight operands and intermediates, each at most 2^-9 relative: the
+    update within 8 * 2^-9 in Frobenius norm, v within 2^-6 of its maximum
+    (G~ enters squared)."""
+    m, n = shape
+    rng = np.random.default_rng(6)
+    st = oracle.OracleState.fresh(rng.standard_normal((m, n)) * 1e-2, "bf16")
+    for _ in range(3):
+        oracle.step(st, rng.standard_normal((m, n)) * 1e-2, HP)
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.momentum_update(st.M, G, HP.beta1, "bf16")
+    _, vm, im = oracle.rotated_adam_apply(st.W, st.v, M, G, st.U, st.V, HP.beta2, HP.eps, HP.lr)
+    _, vb, ib = B.bf16_rotation_apply(st.W, st.v, M, G, st.U, st.V, HP.beta2, HP.eps, HP.lr)
+    rel = np.linalg.norm(ib["dW"] - im["dW"]) / np.linalg.norm(im["dW"])
+    assert 1e-4 < rel <= 8 * 2.0 ** -9
+    assert np.max(np.abs(vb - vm)) <= 2.0 ** -6 * np.max(vm)
+
+
+def test_trajectory_stays_near_the_method_across_refreshes():
+    """Seven steps with a refresh every three: the accumulated change of W
+    stays within 10 % of the method's in Frobenius norm (the first bf16 step
+    after the first, where v still holds one step of squares, contributes the
+    most) and the gap shrinks as v accumulates."""
+    W0, a, b, out = _trajectories(24, 40, 7, 7)
+    cum = [np.linalg.norm(o[1] - o[0]) / np.linalg.norm(o[0]) for o in out]
+    total = np.linalg.norm((b.W - W0) - (a.W - W0)) / np.linalg.norm(a.W - W0)
+    assert total <= 0.1
+    assert cum[-1] < cum[1]
+    assert [o[2] for o in out] == [True, False, False, True, False, False, True]
+    assert [o[3] for o in out] == [False] + [True] * 6
+
+
+def test_first_step_in_bf16_would_be_dominated_by_roundoff():
+    """Why the first step runs in binary32: with v = 0 the bf16 rotation's
+    roundoff in directions where G~ is tiny is divided by eps-sized
+    denominators, and the update grows well beyond the method's."""
+    rng = np.random.default_rng(8)
+    m, n = 24, 40
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.momentum_update(np.zeros((m, n)), G, HP.beta1, "bf16")
+    U, V = oracle.refresh_bases(M, np.eye(m), np.eye(n), 1)
+    z = np.zeros((m, n))
+    _, _, im = oracle.rotated_adam_apply(z, z, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    _, _, ib = B.bf16_rotation_apply(z, z, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    assert np.linalg.norm(ib["dW"]) > 1.5 * np.linalg.norm(im["dW"])
