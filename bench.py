@@ -32,6 +32,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MI355X_FP32_MFMA_TFLOPS = 157.3
+MI355X_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 MFMA (no sparsity)
 MI355X_HBM_GBPS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/internal.h")
@@ -207,6 +208,8 @@ def main(argv=None):
     ap.add_argument("--no-timing", action="store_true", help="do not record per-phase HIP events")
     ap.add_argument("--rotated-momentum", action="store_true",
                     help="the variant that carries m~ in rotated coordinates within a basis epoch")
+    ap.add_argument("--bf16-rotation", action="store_true",
+                    help="the variant that runs the rotations on bf16 operands (fp32 accumulation)")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -255,7 +258,8 @@ def main(argv=None):
         st["G"].copy_(workloads.gradient(wl, i, 1, dev))
         states.append(st)
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
-                  int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum)
+                  int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum,
+                  bf16_rotation=args.bf16_rotation)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()
@@ -297,11 +301,15 @@ def main(argv=None):
         ms = sum(phases[k][0] for k in pf)
         launches = sum(phases[k][1] for k in pf)
         achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else None
+        peak = MI355X_BF16_MFMA_TFLOPS if args.bf16_rotation else MI355X_FP32_MFMA_TFLOPS
+        kernel = ("gemm16_kernel (bf16 rotation phases: (X V)^T, U^T S^T, (u V^T)^T, W -= lr U P^T)"
+                  if args.bf16_rotation else
+                  "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)")
         roofline = {
-            "bound": "mfma", "achieved": achieved, "peak": MI355X_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None,
-            "traffic": traffic_per_launch(),
-            "kernel": "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)",
+            "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak if achieved else None,
+            "traffic": None if args.bf16_rotation else traffic_per_launch(),
+            "kernel": kernel,
             "launches": launches, "avg_launch_ms": ms / max(launches, 1),
             "flops_per_launch": flops / max(launches, 1),
         }
@@ -331,12 +339,13 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if args.bf16_rotation else "f32",
         "data": "synthetic",
         "config": {"workload": wl.key, "matrices": len(shapes), "params": params,
                    "momentum_dtype": wl.m_dtype, "K": wl.K, "power_iters": wl.power_iters,
                    "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
-                   "rotated_momentum": bool(args.rotated_momentum)},
+                   "rotated_momentum": bool(args.rotated_momentum),
+                   "bf16_rotation": bool(args.bf16_rotation)},
         "steps_per_s": steps_per_s,
         "roofline": roofline,
         "cpu_baseline": cpu,

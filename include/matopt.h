@@ -100,7 +100,24 @@ enum {
      * the refreshes. Equal
      * to the method in exact arithmetic; m~ is stored in fp32 (with a bf16 M
      * it is therefore not rounded to bf16 between steps). */
-    OPT_FLAG_ROTATED_MOMENTUM = 1u
+    OPT_FLAG_ROTATED_MOMENTUM = 1u,
+    /* Run the rotations on bfloat16 operands with fp32 accumulation (the
+     * rotation matrices kept in 16-bit floats, as in the Pipeline-parallelism
+     * page, section 3.1; bfloat16 rather than float16 so that one operand
+     * format serves the bases, the bf16 momentum and the gradient). U, V stay
+     * fp32 and are what the refresh updates; bf16 copies of U, U^T, V, V^T
+     * live in the workspace and are rebuilt on the first step after a
+     * refresh, a create, refresh_basis, reorthonormalize or set_step (a caller
+     * that writes U or V itself must call opt_group_set_step afterwards). The
+     * bf16 roundings: G, M, the bases, the right rotations X V, u and the
+     * rotation back u V^T; G~, m~, v and W stay fp32. The first step of a
+     * group (t = 1, where v = 0) uses the fp32 rotations: there u divides by
+     * sqrt(v) + eps and bf16 roundoff in directions where G~ vanishes would
+     * become full-size entries of u. Cannot be combined with
+     * OPT_FLAG_ROTATED_MOMENTUM (OPT_EUNSUPPORTED). The workspace grows by the
+     * bf16 bases, 4 (m m8 + n n8) bytes per matrix (m8, n8: m, n rounded up
+     * to a multiple of 8). */
+    OPT_FLAG_BF16_ROTATION = 2u
 };
 
 typedef struct {
@@ -222,6 +239,19 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
                     float alpha, const void* A, int32_t a_dtype, int64_t lda,
                     const void* B, int32_t b_dtype, int64_t ldb,
                     float beta, float* C, int64_t ldc, void* stream);
+
+/* C = alpha * A B^T + beta * C with bfloat16 operands and fp32 accumulation
+ * (the product of the bf16-rotation variant, section 3.1 of the pipeline-
+ * parallelism page keeping the rotation matrices in 16-bit floats). A is M x K
+ * and B is N x K, both bf16, row-major with k contiguous (row strides lda,
+ * ldb >= K); K, lda and ldb must be multiples of 8 and A, B 16-byte aligned
+ * (OPT_EINVAL otherwise). C is M x N row-major (ldc >= N): fp32 when c_dtype
+ * is OPT_F32, or bf16 rounded to nearest even when c_dtype is OPT_BF16, which
+ * requires beta == 0. beta == 0 does not read C. M, N, K >= 0; an empty
+ * product only scales C. Enqueued on `stream`; no allocation. */
+opt_status opt_gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, float beta, void* C, int32_t c_dtype, int64_t ldc,
+                         void* stream);
 
 /* Q = the positive-diagonal-R orthonormal factor of the d x d fp32 matrix Z
  * (row-major, stride d). Z is overwritten with the Householder factorisation

@@ -28,12 +28,14 @@ class Hyper:
     capacity_bytes: int = 1 << 29
     refresh_capacity_bytes: int = 0   # 0: library default (48 GiB)
     rotated_momentum: bool = False    # carry m~ in rotated coordinates (needs an Mt tensor per matrix)
+    bf16_rotation: bool = False       # rotations on bf16 operands (fp32 accumulation) from the second step
 
     def c(self) -> native.opt_hparams:
+        flags = (native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0) | \
+                (native.OPT_FLAG_BF16_ROTATION if self.bf16_rotation else 0)
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,
                                   self.power_iters, self.capacity_bytes,
-                                  self.refresh_capacity_bytes,
-                                  native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0)
+                                  self.refresh_capacity_bytes, flags)
 
 
 def tensor_ptr(t) -> int:

@@ -29,7 +29,7 @@
 #include <vector>
 
 #include "matopt.h"
-#include "internal.h"
+#include "variant_bf16.h"
 
 using namespace matopt;
 
@@ -63,6 +63,8 @@ struct Mat {
     int idx;
     double cost;
     bool bf16;
+    // bf16-rotation variant: bf16 copies of U, U^T (m x m8) and V, V^T (n x n8)
+    uint16_t *Ub = nullptr, *Utb = nullptr, *Vb = nullptr, *Vtb = nullptr;
 };
 
 // Byte offsets into the table image (host) / table region (device).
@@ -78,6 +80,19 @@ struct EwLaunch {
     int nseg = 0;
     int64_t chunks = 0;
     uint64_t segs = 0;
+};
+struct Gemm16Launch {
+    bool out16 = false;
+    int cfg = 0;     // index into kGemm16Cfgs
+    int nprob = 0;
+    int total_tiles = 0;
+    uint64_t probs = 0;
+    uint64_t tb = 0;
+};
+struct PackLaunch {
+    int njobs = 0;
+    int64_t chunks = 0;
+    uint64_t jobs = 0;
 };
 struct QrBatch {
     int njobs = 0;
@@ -102,6 +117,14 @@ struct Group {
     // into Mt (rot_left as above), and the step that carries it (G only)
     std::vector<GemmLaunch> rot_right_re, rot_left_c, rot_right_c;
     EwLaunch adam_re, adam_c;
+    // bf16 rotations: S = (X V)^T for X in {G, M}, then U^T S^T into G~, m~;
+    // P = (u V^T)^T, then W -= lr U P^T. Matrices with n % 8 == 0 take the
+    // fused elementwise launches (bf16 side outputs), others the plain ones
+    // followed by packs to a padded row stride.
+    std::vector<Gemm16Launch> r16_right, r16_left, r16_back_right, r16_back_left;
+    EwLaunch mom16, adam16;
+    EwLaunch mom_r, adam_r;   // ragged matrices
+    PackLaunch pack_in, pack_u;
     uint64_t rot_bytes = 0;
 };
 
@@ -154,6 +177,12 @@ struct opt_group_s {
     uint64_t ws_bytes = 0;
     Image img;
     uint64_t table_bytes = 0, scratch_bytes = 0;
+    // bf16-rotation variant: the bases' bf16 copies (after the tables, before
+    // the scratch), their conversion launch, and whether they match U, V
+    uint64_t bases_bytes = 0;
+    uint64_t basis_jobs = 0;
+    int basis_njobs = 0, basis_tiles = 0;
+    bool bases16_valid = false;
     // state checks: one scan over every matrix (partials at the start of the
     // scratch), per-matrix records in the table region
     uint64_t health_segs = 0, health_out = 0;
@@ -186,7 +215,10 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (!std::isfinite(hp->lr)) return fail(OPT_EINVAL, "lr must be finite");
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
-    if (hp->flags & ~(uint32_t)OPT_FLAG_ROTATED_MOMENTUM) return fail(OPT_EINVAL, "unknown bits in flags");
+    if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION))
+        return fail(OPT_EINVAL, "unknown bits in flags");
+    if ((hp->flags & OPT_FLAG_ROTATED_MOMENTUM) && (hp->flags & OPT_FLAG_BF16_ROTATION))
+        return fail(OPT_EUNSUPPORTED, "OPT_FLAG_BF16_ROTATION cannot be combined with OPT_FLAG_ROTATED_MOMENTUM");
     return OPT_OK;
 }
 
@@ -312,6 +344,39 @@ int choose_cfg(const std::vector<GemmProb>& probs) {
     return tiles_of(probs, 1) >= kGemmLargeMinTiles ? 1 : 0;
 }
 
+// bf16 NT products (C = alpha A B^T + beta C, k contiguous in both operands).
+Gemm16Prob g16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
+               int64_t N, int64_t K, float alpha, float beta, int64_t pad_n) {
+    Gemm16Prob p{};
+    p.A = (const uint16_t*)A;
+    p.B = (const uint16_t*)B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int32_t)M;
+    p.N = (int32_t)N;
+    p.K = (int32_t)K;
+    p.pad_n = (int32_t)pad_n;
+    p.alpha = alpha;
+    p.beta = beta;
+    return p;
+}
+
+void set_tiles16(Gemm16Prob& p, int cfg) {
+    p.tiles_m = (p.M + kGemm16Cfgs[cfg].bm - 1) / kGemm16Cfgs[cfg].bm;
+    p.tiles_n = (std::max(p.N, p.pad_n) + kGemm16Cfgs[cfg].bn - 1) / kGemm16Cfgs[cfg].bn;
+}
+
+int choose_cfg16(const std::vector<Gemm16Prob>& probs) {
+    int64_t t = 0;
+    for (Gemm16Prob p : probs) {
+        set_tiles16(p, 1);
+        t += (int64_t)p.tiles_m * p.tiles_n;
+    }
+    return t >= kGemm16LargeMinTiles ? 1 : 0;
+}
+
 // op(A) is M x K: A stored M x K (at = false) or K x M (at = true); op(B) is
 // K x N: B stored K x N (bt = false) or N x K (bt = true).
 PGemm mk(bool at, bool bt, const void* A, bool a_bf16, int64_t lda, const void* B, bool b_bf16,
@@ -378,6 +443,64 @@ EwLaunch put_ew(Image& img, std::vector<EwSeg> segs) {
     L.chunks = chunks;
     L.segs = img.put(segs);
     return L;
+}
+
+// One launch of bf16 products with one output type, LPT over tiles (the cost
+// of a tile grows with K).
+Gemm16Launch put_gemm16(Image& img, std::vector<Gemm16Prob> probs, bool out16) {
+    Gemm16Launch L;
+    L.out16 = out16;
+    probs.erase(std::remove_if(probs.begin(), probs.end(),
+                               [](const Gemm16Prob& p) { return p.M <= 0 || std::max(p.N, p.pad_n) <= 0; }),
+                probs.end());
+    if (probs.empty()) return L;
+    std::stable_sort(probs.begin(), probs.end(), [](const Gemm16Prob& a, const Gemm16Prob& b) { return a.K > b.K; });
+    L.cfg = choose_cfg16(probs);
+    std::vector<int32_t> tb;
+    int total = 0;
+    for (Gemm16Prob& p : probs) {
+        set_tiles16(p, L.cfg);
+        tb.push_back(total);
+        total += p.tiles_m * p.tiles_n;
+    }
+    L.nprob = (int)probs.size();
+    L.total_tiles = total;
+    L.probs = img.put(probs);
+    L.tb = img.put(tb);
+    return L;
+}
+
+EwLaunch put_ew16(Image& img, std::vector<Ew16Seg> segs) {
+    int64_t chunks = 0;
+    for (Ew16Seg& s : segs) {
+        s.chunk_begin = chunks;
+        chunks += (s.n + kEwChunk - 1) / kEwChunk;
+    }
+    EwLaunch L;
+    L.nseg = (int)segs.size();
+    L.chunks = chunks;
+    L.segs = img.put(segs);
+    return L;
+}
+
+PackLaunch put_pack(Image& img, std::vector<PackJob> jobs) {
+    int64_t chunks = 0;
+    for (PackJob& j : jobs) {
+        j.chunk_begin = chunks;
+        chunks += (j.rows * j.ld_dst + kEwChunk - 1) / kEwChunk;
+    }
+    PackLaunch L;
+    L.njobs = (int)jobs.size();
+    L.chunks = chunks;
+    L.jobs = img.put(jobs);
+    return L;
+}
+
+int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
+
+// Bytes of the bf16 copies of one matrix's bases: U, U^T (m x m8), V, V^T (n x n8).
+uint64_t bases16_bytes(int64_t m, int64_t n) {
+    return 2 * align_up(2ull * m * round8(m)) + 2 * align_up(2ull * n * round8(n));
 }
 
 int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
@@ -554,13 +677,45 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
     return out;
 }
 
-// Build every table of the group object. `scratch` is the device address of
-// the scratch region (any value when only sizes are wanted).
-void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scratch) {
+// Build every table of the group object. `region` is the device address of
+// the workspace past the tables (any value when only sizes are wanted): the
+// bf16 bases (bf16-rotation variant only), then the scratch.
+void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* region) {
     g->groups.clear();
     g->rbatches.clear();
     g->img.bytes.clear();
     g->scratch_bytes = 0;
+    const bool r16 = g->hp.flags & OPT_FLAG_BF16_ROTATION;
+    g->bases_bytes = 0;
+    if (r16) {
+        std::vector<BasisJob> bj;
+        int tiles = 0;
+        for (Mat& M : g->mats) {
+            const int64_t m = M.d.m, n = M.d.n, m8 = round8(m), n8 = round8(n);
+            char* p = region + g->bases_bytes;
+            M.Ub = (uint16_t*)p; p += align_up(2ull * m * m8);
+            M.Utb = (uint16_t*)p; p += align_up(2ull * m * m8);
+            M.Vb = (uint16_t*)p; p += align_up(2ull * n * n8);
+            M.Vtb = (uint16_t*)p;
+            g->bases_bytes += bases16_bytes(m, n);
+            for (int side = 0; side < 2; ++side) {
+                BasisJob j{};
+                j.X = side ? M.d.V : M.d.U;
+                j.Xb = side ? M.Vb : M.Ub;
+                j.Xt = side ? M.Vtb : M.Utb;
+                j.d = (int32_t)(side ? n : m);
+                j.dp = (int32_t)round8(j.d);
+                j.tile_begin = tiles;
+                const int per = (j.dp + kBasisTile - 1) / kBasisTile;
+                tiles += per * per;
+                bj.push_back(j);
+            }
+        }
+        g->basis_njobs = (int)bj.size();
+        g->basis_tiles = tiles;
+        g->basis_jobs = g->img.put(bj);
+    }
+    char* scratch = region + g->bases_bytes;
     for (const std::vector<int>& members : plan) {
         Group G;
         G.mats = members;
@@ -616,6 +771,85 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* scra
             }
         }
         G.rot_bytes = off;
+        if (r16) {
+            std::vector<Gemm16Prob> s_right, s_left, s_bright, s_bleft;
+            std::vector<Ew16Seg> m16, a16;
+            std::vector<EwSeg> mr, ar;
+            std::vector<PackJob> pin, pu;
+            uint64_t o = 0;
+            for (int mi : members) {
+                const Mat& M = g->mats[mi];
+                const opt_matrix_desc& x = M.d;
+                const int64_t m = x.m, n = x.n, mn = m * n, m8 = round8(m), n8 = round8(n);
+                const bool flat = n % 8 == 0;
+                const bool m_direct = flat && M.bf16 && aligned(x.M, 16);
+                uint16_t* Gb = (uint16_t*)(scratch + o); o += align_up(2ull * m * n8);   // later u
+                uint16_t* Mb = m_direct ? (uint16_t*)x.M : (uint16_t*)(scratch + o);
+                if (!m_direct) o += align_up(2ull * m * n8);
+                uint16_t* SG = (uint16_t*)(scratch + o); o += align_up(2ull * n * m8);   // later P
+                uint16_t* SM = (uint16_t*)(scratch + o); o += align_up(2ull * n * m8);
+                float* Gt = (float*)(scratch + o); o += align_up(4ull * mn);
+                float* mt = (float*)(scratch + o); o += align_up(4ull * mn);
+                // S = (X V)^T: S[j][i] = sum_k V^T[j][k] X[i][k]   (n x m, row stride m8)
+                s_right.push_back(g16(M.Vtb, n8, Gb, n8, SG, m8, n, m, n8, 1.f, 0.f, m8));
+                s_right.push_back(g16(M.Vtb, n8, Mb, n8, SM, m8, n, m, n8, 1.f, 0.f, m8));
+                // G~ = U^T S^T: G~[i][j] = sum_k U^T[i][k] S[j][k]  (m x n fp32)
+                s_left.push_back(g16(M.Utb, m8, SG, m8, Gt, n, m, n, m8, 1.f, 0.f, n));
+                s_left.push_back(g16(M.Utb, m8, SM, m8, mt, n, m, n, m8, 1.f, 0.f, n));
+                // P = (u V^T)^T: P[j][k] = sum_l V[j][l] u[k][l]   (n x m, into SG)
+                s_bright.push_back(g16(M.Vb, n8, Gb, n8, SG, m8, n, m, n8, 1.f, 0.f, m8));
+                // W -= lr U P^T: sum_k U[i][k] P[j][k]
+                s_bleft.push_back(g16(M.Ub, m8, SG, m8, x.W, n, m, n, m8, -1.f, 1.f, n));
+                if (flat) {
+                    Ew16Seg e{};
+                    e.a = x.G;
+                    e.b = x.M;
+                    e.o1 = Gb;
+                    e.o2 = m_direct ? nullptr : Mb;
+                    e.n = mn;
+                    e.b_bf16 = M.bf16;
+                    e.vec = aligned(x.G, 16) && aligned(x.M, M.bf16 ? 8 : 16);
+                    m16.push_back(e);
+                    Ew16Seg a{};
+                    a.a = Gt;
+                    a.b = mt;
+                    a.c = x.v;
+                    a.o1 = Gb;
+                    a.n = mn;
+                    a.vec = aligned(x.v, 16);
+                    a16.push_back(a);
+                } else {
+                    EwSeg e{};
+                    e.a = x.G;
+                    e.b = x.M;
+                    e.n = mn;
+                    e.b_bf16 = M.bf16;
+                    e.vec = aligned(x.G, 16) && aligned(x.M, M.bf16 ? 8 : 16);
+                    mr.push_back(e);
+                    pin.push_back({x.G, Gb, m, n, n, n8, 0, 0});
+                    pin.push_back({x.M, Mb, m, n, n, n8, 0, (int32_t)M.bf16});
+                    EwSeg a{};
+                    a.a = Gt;
+                    a.b = mt;   // u over m~, then packed into Gb's buffer
+                    a.c = x.v;
+                    a.n = mn;
+                    a.vec = aligned(x.v, 16);
+                    ar.push_back(a);
+                    pu.push_back({mt, Gb, m, n, n, n8, 0, 0});
+                }
+            }
+            G.r16_right.push_back(put_gemm16(g->img, s_right, true));
+            G.r16_left.push_back(put_gemm16(g->img, s_left, false));
+            G.r16_back_right.push_back(put_gemm16(g->img, s_bright, true));
+            G.r16_back_left.push_back(put_gemm16(g->img, s_bleft, false));
+            G.mom16 = put_ew16(g->img, m16);
+            G.adam16 = put_ew16(g->img, a16);
+            G.mom_r = put_ew(g->img, mr);
+            G.adam_r = put_ew(g->img, ar);
+            G.pack_in = put_pack(g->img, pin);
+            G.pack_u = put_pack(g->img, pu);
+            G.rot_bytes = std::max(G.rot_bytes, o);
+        }
         G.rot_left = put_gemm(g->img, left);
         G.rot_right = put_gemm(g->img, right);
         G.back_left = put_gemm(g->img, bl);
@@ -817,6 +1051,23 @@ hipError_t run_gemm(opt_group_s* g, const std::vector<GemmLaunch>& Ls, float alp
     return hipSuccess;
 }
 
+hipError_t run_gemm16(opt_group_s* g, const std::vector<Gemm16Launch>& Ls, float alpha_scale, hipStream_t s) {
+    for (const Gemm16Launch& L : Ls) {
+        if (L.nprob == 0) continue;
+        hipError_t e = launch_gemm16_grouped(L.out16, L.cfg, dptr<Gemm16Prob>(g, L.probs), dptr<int32_t>(g, L.tb),
+                                             L.nprob, L.total_tiles, alpha_scale, s);
+        if (e != hipSuccess) return e;
+        g->kernels_in_scope += 1;
+    }
+    return hipSuccess;
+}
+
+hipError_t run_pack(opt_group_s* g, const PackLaunch& L, hipStream_t s) {
+    if (L.njobs == 0) return hipSuccess;
+    g->kernels_in_scope += 1;
+    return launch_pack16(dptr<PackJob>(g, L.jobs), L.njobs, L.chunks, s);
+}
+
 // Runs of equal order among the jobs still active at panel p, in chunks of
 // at most kQrMaxClasses (one launch per chunk).
 std::vector<QrClasses> active_classes(const std::vector<int>& d, int p) {
@@ -953,7 +1204,7 @@ opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
         tmp.mats.push_back(M);
     }
     build(&tmp, plan, (char*)(uintptr_t)kAlign);
-    *bytes = tmp.table_bytes + tmp.scratch_bytes;
+    *bytes = tmp.table_bytes + tmp.bases_bytes + tmp.scratch_bytes;
     return OPT_OK;
 }
 
@@ -1027,6 +1278,77 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     g->t += 1;
     const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
+    // bf16 rotations from the second step on (the first, with v = 0, in fp32)
+    if ((g->hp.flags & OPT_FLAG_BF16_ROTATION) && g->t > 1) {
+        // The bf16 copies of G and M live in the scratch that the refresh and
+        // every micro-group share, so each group makes its own right before
+        // its rotations: with the momentum update on steps without a refresh,
+        // after the refresh (which must see the updated M) otherwise.
+        if (refresh) {
+            for (const Group& G : g->groups) {
+                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+                e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
+                if (e) return hip_fail(e, "momentum launch");
+                g->kernels_in_scope += G.mom.nseg > 0;
+            }
+            for (const RefreshBatch& R : g->rbatches)
+                if ((e = run_refresh(g, R, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+            g->bases16_valid = false;
+        }
+        if (!g->bases16_valid) {
+            PhaseScope ps(g, OPT_PHASE_REFRESH, s);
+            if ((e = launch_basis16(dptr<BasisJob>(g, g->basis_jobs), g->basis_njobs, g->basis_tiles, s)))
+                return hip_fail(e, "basis conversion launch");
+            g->kernels_in_scope += 1;
+            g->bases16_valid = true;
+        }
+        for (const Group& G : g->groups) {
+            {
+                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+                if (refresh) {
+                    e = launch_convert16(dptr<Ew16Seg>(g, G.mom16.segs), G.mom16.nseg, G.mom16.chunks, s);
+                    g->kernels_in_scope += G.mom16.nseg > 0;
+                } else {
+                    e = launch_momentum16(dptr<Ew16Seg>(g, G.mom16.segs), G.mom16.nseg, G.mom16.chunks, g->hp.beta1,
+                                          s);
+                    if (!e)
+                        e = launch_momentum(dptr<EwSeg>(g, G.mom_r.segs), G.mom_r.nseg, G.mom_r.chunks, g->hp.beta1,
+                                            s);
+                    g->kernels_in_scope += (G.mom16.nseg > 0) + (G.mom_r.nseg > 0);
+                }
+                if (!e) e = run_pack(g, G.pack_in, s);
+                if (e) return hip_fail(e, "momentum launch");
+            }
+            {
+                PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
+                if ((e = run_gemm16(g, G.r16_right, 1.f, s))) return hip_fail(e, "rotation launch");
+            }
+            {
+                PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
+                if ((e = run_gemm16(g, G.r16_left, 1.f, s))) return hip_fail(e, "rotation launch");
+            }
+            {
+                PhaseScope ps(g, OPT_PHASE_ADAM, s);
+                e = launch_adam16(dptr<Ew16Seg>(g, G.adam16.segs), G.adam16.nseg, G.adam16.chunks, g->hp.beta2,
+                                  g->hp.eps, s);
+                if (!e)
+                    e = launch_rotated_adam(dptr<EwSeg>(g, G.adam_r.segs), G.adam_r.nseg, G.adam_r.chunks,
+                                            g->hp.beta1, g->hp.beta2, g->hp.eps, s);
+                if (!e) e = run_pack(g, G.pack_u, s);
+                if (e) return hip_fail(e, "rotated Adam launch");
+                g->kernels_in_scope += (G.adam16.nseg > 0) + (G.adam_r.nseg > 0);
+            }
+            {
+                PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s);
+                if ((e = run_gemm16(g, G.r16_back_right, 1.f, s))) return hip_fail(e, "rotation launch");
+            }
+            {
+                PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
+                if ((e = run_gemm16(g, G.r16_back_left, g->hp.lr, s))) return hip_fail(e, "update launch");
+            }
+        }
+        return OPT_OK;
+    }
     // Momentum of every group first: a refresh must see the updated M.
     for (const Group& G : g->groups) {
         PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
@@ -1079,6 +1401,7 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
     g->mt_valid = false;
+    g->bases16_valid = false;
     for (const RefreshBatch& R : g->rbatches)
         if ((e = run_refresh(g, R, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
     return OPT_OK;
@@ -1092,7 +1415,7 @@ opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before health");
     hipStream_t s = (hipStream_t)stream;
     HealthOut* dout = (HealthOut*)(g->ws + g->health_out);
-    HealthPartial* part = (HealthPartial*)(g->ws + g->table_bytes);
+    HealthPartial* part = (HealthPartial*)(g->ws + g->table_bytes + g->bases_bytes);
     const HealthSeg* segs = dptr<HealthSeg>(g, g->health_segs);
     if ((e = launch_health_clear(dout, (int)g->mats.size(), s))) return hip_fail(e, "health launch");
     if ((e = launch_health_partials(segs, g->health_nseg, g->health_chunks, part, s))) return hip_fail(e, "health launch");
@@ -1129,7 +1452,7 @@ opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");
     hipStream_t s = (hipStream_t)stream;
-    if (iters > 0) g->mt_valid = false;
+    if (iters > 0) g->mt_valid = g->bases16_valid = false;
     for (int it = 0; it < iters; ++it)
         for (const RefreshBatch& R : g->rbatches) {
             for (const std::vector<GemmLaunch>& stp : R.gram)
@@ -1156,6 +1479,7 @@ opt_status opt_group_set_step(opt_group_t g, int64_t t) {
     if (t < 0) return fail(OPT_EINVAL, "t must be >= 0");
     g->t = t;
     g->mt_valid = false;   // a resumed job recomputes the rotated momentum
+    g->bases16_valid = false;   // and the bf16 bases (the caller may have written U, V)
     return OPT_OK;
 }
 
@@ -1229,6 +1553,35 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
     set_tiles(single, cfg);
     e = launch_gemm_single(pg.variant, cfg, single, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
+    return OPT_OK;
+}
+
+opt_status opt_gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, float beta, void* C, int32_t c_dtype, int64_t ldc,
+                         void* stream) {
+    if (M < 0 || N < 0 || K < 0) return fail(OPT_EINVAL, "negative dimension");
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2)
+        return fail(OPT_EUNSUPPORTED, "dimension too large");
+    if (c_dtype != OPT_F32 && c_dtype != OPT_BF16) return fail(OPT_EUNSUPPORTED, "c_dtype must be OPT_F32 or OPT_BF16");
+    if (c_dtype == OPT_BF16 && beta != 0.f) return fail(OPT_EINVAL, "a bf16 C needs beta == 0");
+    if (M == 0 || N == 0) return OPT_OK;
+    if (!C) return fail(OPT_EINVAL, "C is NULL");
+    if (ldc < N) return fail(OPT_EINVAL, "ldc < N");
+    if (!aligned(C, c_dtype == OPT_F32 ? 4 : 2)) return fail(OPT_EINVAL, "C is not aligned to its element size");
+    if (K % 8) return fail(OPT_EINVAL, "K must be a multiple of 8");
+    if (K > 0) {
+        if (!A || !B) return fail(OPT_EINVAL, "A or B is NULL");
+        if (lda < K || ldb < K) return fail(OPT_EINVAL, "lda and ldb must be >= K");
+        if (lda % 8 || ldb % 8) return fail(OPT_EINVAL, "lda and ldb must be multiples of 8");
+        if (!aligned(A, 16) || !aligned(B, 16)) return fail(OPT_EINVAL, "A and B must be 16-byte aligned");
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pending HIP error before gemm");
+    Gemm16Prob p = g16(A, lda, B, ldb, C, ldc, M, N, K, alpha, beta, N);
+    const int cfg = choose_cfg16({p});
+    set_tiles16(p, cfg);
+    e = launch_gemm16_single(c_dtype == OPT_BF16, cfg, p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "bf16 gemm launch");
     return OPT_OK;
 }
 

@@ -5,13 +5,18 @@
 //                 u  = m~ / (sqrt(v) + eps)              (u overwrites m~, or to its own buffer)
 //                 with the carried rotated momentum first m~ <- beta1 m~ + (1 - beta1) G~
 //
+// and for the bf16-rotation variant the same two updates with bf16 side
+// outputs (G and M rounded for the rotations, u rounded), the conversion of
+// the bases to bf16 copies (row-major and transposed) and a pack of a
+// matrix to bf16 with a padded row stride.
+//
 // One launch covers every matrix of a micro-group: the matrices are cut into
 // chunks of kEwChunk elements, concatenated in chunk space, and each
 // workgroup finds its matrix by a binary search over the chunk offsets. A
 // thread moves four 16-byte groups (fp32) per tensor, and for each group the
 // 256 threads of the workgroup touch one contiguous 4 KiB span, so every
 // access is a full-line, coalesced one.
-#include "internal.h"
+#include "variant_bf16.h"
 
 namespace matopt {
 
@@ -187,7 +192,221 @@ __global__ __launch_bounds__(kEwThreads) void rotated_adam_kernel(const EwSeg* _
     }
 }
 
+// ------------------------------------------------ bf16-rotation variant ----
+
+__device__ __forceinline__ int find_seg16(const Ew16Seg* segs, int nseg, int64_t chunk) {
+    int lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (segs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__device__ __forceinline__ u32x2 pack_bf16x4(f32x4 x) {
+    u32x2 w;
+    w.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    w.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    return w;
+}
+
+// UPDATE: the momentum update of momentum_kernel, plus bf16 copies of G (o1)
+// and of the new M (o2, when set) for the rotations. Otherwise only the
+// copies, of G and of M as stored.
+template <bool UPDATE>
+__global__ __launch_bounds__(kEwThreads) void momentum16_kernel(const Ew16Seg* __restrict__ segs, int nseg,
+                                                                float beta1) {
+    const int64_t chunk = blockIdx.x;
+    const Ew16Seg S = segs[find_seg16(segs, nseg, chunk)];
+    const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
+    const float omb = 1.f - beta1;
+    if (S.vec && base + kEwChunk <= S.n) {
+        f32x4 g[NQ], m[NQ];
+        u32x2 raw[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t o = base + 4 * (q * kEwThreads + threadIdx.x);
+            g[q] = *gptr((const f32x4*)(S.a + o));
+            if (S.b_bf16) raw[q] = *gptr((const u32x2*)((const uint16_t*)S.b + o));
+            else          m[q] = *gptr((const f32x4*)((const float*)S.b + o));
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t o = base + 4 * (q * kEwThreads + threadIdx.x);
+            if (S.b_bf16) m[q] = widen_bf16x4(raw[q]);
+            *gptr((u32x2*)(S.o1 + o)) = pack_bf16x4(g[q]);
+            if (UPDATE) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) m[q][e] = ema(beta1, m[q][e], omb, g[q][e]);
+                if (S.b_bf16) *gptr((u32x2*)((uint16_t*)S.b + o)) = pack_bf16x4(m[q]);
+                else          *gptr((f32x4*)((float*)S.b + o)) = m[q];
+            }
+            if (S.o2) *gptr((u32x2*)(S.o2 + o)) = pack_bf16x4(m[q]);
+        }
+        return;
+    }
+    gmem<const float> G = gptr(S.a);
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
+        for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            const float g = G[i + e];
+            gptr(S.o1)[i + e] = f32_to_bf16(g);
+            float mn;
+            if (S.b_bf16) {
+                gmem<uint16_t> p = gptr((uint16_t*)S.b + i + e);
+                mn = bf16_to_f32(*p);
+                if (UPDATE) {
+                    mn = ema(beta1, mn, omb, g);
+                    *p = f32_to_bf16(mn);
+                }
+            } else {
+                gmem<float> p = gptr((float*)S.b + i + e);
+                mn = *p;
+                if (UPDATE) {
+                    mn = ema(beta1, mn, omb, g);
+                    *p = mn;
+                }
+            }
+            if (S.o2) gptr(S.o2)[i + e] = f32_to_bf16(mn);
+        }
+    }
+}
+
+// v <- beta2 v + (1 - beta2) G~^2; u = m~ / (sqrt(v) + eps) stored as bf16 in o1.
+__global__ __launch_bounds__(kEwThreads) void adam16_kernel(const Ew16Seg* __restrict__ segs, int nseg,
+                                                            float beta2, float eps) {
+    const int64_t chunk = blockIdx.x;
+    const Ew16Seg S = segs[find_seg16(segs, nseg, chunk)];
+    const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
+    const float omb2 = 1.f - beta2;
+    if (S.vec && base + kEwChunk <= S.n) {
+        f32x4 g[NQ], m[NQ], v[NQ];
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t o = base + 4 * (q * kEwThreads + threadIdx.x);
+            g[q] = *gptr((const f32x4*)(S.a + o));
+            m[q] = *gptr((const f32x4*)((const float*)S.b + o));
+            v[q] = *gptr((const f32x4*)(S.c + o));
+        }
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            const int64_t o = base + 4 * (q * kEwThreads + threadIdx.x);
+            f32x4 u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float ve = v[q][e], ue;
+                adam1(g[q][e], m[q][e], ve, ue, beta2, omb2, eps);
+                v[q][e] = ve;
+                u[e] = ue;
+            }
+            *gptr((f32x4*)(S.c + o)) = v[q];
+            *gptr((u32x2*)(S.o1 + o)) = pack_bf16x4(u);
+        }
+        return;
+    }
+    gmem<const float> Gt = gptr(S.a);
+    gmem<const float> mb = gptr((const float*)S.b);
+    gmem<float> V = gptr(S.c);
+    for (int q = 0; q < NQ; ++q) {
+        const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
+        for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            float v = V[i + e], u;
+            adam1(Gt[i + e], mb[i + e], v, u, beta2, omb2, eps);
+            V[i + e] = v;
+            gptr(S.o1)[i + e] = f32_to_bf16(u);
+        }
+    }
+}
+
+// Element e of a job's padded destination: row e / ld_dst, column e % ld_dst.
+__global__ __launch_bounds__(kEwThreads) void pack16_kernel(const PackJob* __restrict__ jobs, int njobs) {
+    const int64_t chunk = blockIdx.x;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+    }
+    const PackJob J = jobs[lo];
+    const int64_t total = J.rows * J.ld_dst;
+    const int64_t base = (chunk - J.chunk_begin) * kEwChunk;
+    for (int k = threadIdx.x; k < kEwChunk; k += kEwThreads) {
+        const int64_t e = base + k;
+        if (e >= total) break;
+        const int64_t r = e / J.ld_dst, c = e % J.ld_dst;
+        uint16_t h = 0;
+        if (c < J.cols) {
+            const int64_t si = r * J.ld_src + c;
+            h = J.src_bf16 ? gptr((const uint16_t*)J.src)[si] : f32_to_bf16(gptr((const float*)J.src)[si]);
+        }
+        gptr(J.dst)[e] = h;
+    }
+}
+
+// One 32 x 32 tile of a basis: Xb[r][c] = X[r][c] and Xt[c][r] = X[r][c] for
+// the tile's r, c < dp, with zeros where r or c >= d; rows of Xb and Xt past
+// d are not stored. The transposed tile goes through LDS so that both the
+// reads and the writes are along rows.
+__global__ __launch_bounds__(256) void basis16_kernel(const BasisJob* __restrict__ jobs, int njobs) {
+    __shared__ float tile[kBasisTile][kBasisTile + 1];
+    const int bid = blockIdx.x;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].tile_begin <= bid) lo = mid; else hi = mid - 1;
+    }
+    const BasisJob J = jobs[lo];
+    const int per_row = (J.dp + kBasisTile - 1) / kBasisTile;
+    const int t = bid - J.tile_begin;
+    const int R = (t / per_row) * kBasisTile, Cc = (t % per_row) * kBasisTile;
+    const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
+    for (int y = y0; y < kBasisTile; y += 8) {
+        const int r = R + y, c = Cc + x;
+        const float val = (r < J.d && c < J.d) ? gptr(J.X)[(int64_t)r * J.d + c] : 0.f;
+        tile[y][x] = val;
+        if (r < J.d && c < J.dp) gptr(J.Xb)[(int64_t)r * J.dp + c] = f32_to_bf16(val);
+    }
+    __syncthreads();
+    for (int y = y0; y < kBasisTile; y += 8) {
+        const int i = Cc + y, k = R + x;   // Xt[i][k] = X[k][i]
+        if (i < J.d && k < J.dp) gptr(J.Xt)[(int64_t)i * J.dp + k] = f32_to_bf16(tile[x][y]);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_momentum16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta1, hipStream_t s) {
+    if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(momentum16_kernel<true>, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, segs, nseg,
+                       beta1);
+    return hipGetLastError();
+}
+
+hipError_t launch_convert16(const Ew16Seg* segs, int nseg, int64_t total_chunks, hipStream_t s) {
+    if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(momentum16_kernel<false>, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, segs, nseg,
+                       0.f);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta2, float eps,
+                         hipStream_t s) {
+    if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(adam16_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, segs, nseg, beta2,
+                       eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack16(const PackJob* jobs, int njobs, int64_t total_chunks, hipStream_t s) {
+    if (njobs <= 0 || total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(pack16_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, jobs, njobs);
+    return hipGetLastError();
+}
+
+hipError_t launch_basis16(const BasisJob* jobs, int njobs, int total_tiles, hipStream_t s) {
+    if (njobs <= 0 || total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(basis16_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, jobs, njobs);
+    return hipGetLastError();
+}
 
 hipError_t launch_momentum(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1,
                            hipStream_t s) {

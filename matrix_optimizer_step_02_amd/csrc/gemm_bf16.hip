@@ -1,0 +1,301 @@
+// Grouped bf16 MFMA GEMM for gfx950 (CDNA4): C = alpha A B^T (+ beta C).
+//
+// Serves the four rotations of the bf16-rotation variant. Every product is
+// arranged so that both operands are stored with k contiguous (A is M x K,
+// B is N x K, both row-major): with a bf16 operand each lane of
+// v_mfma_f32_32x32x16_bf16 takes eight consecutive k values of one row, one
+// 16-byte LDS read, and an operand whose k index is strided would need a
+// transposing stage instead.
+//
+// Tiles. Cfg16<WAVES_M, WAVES_N, BLK_M, BLK_N>: each wavefront holds a
+// (32 BLK_M) x (32 BLK_N) block of the output as BLK_M x BLK_N accumulators
+// of 32 x 32; the large configuration gives each of 4 wavefronts 128 x 128,
+// so per 16-deep k step a wavefront reads 4 + 4 fragments (8 KiB of LDS) for
+// 16 MFMAs, half the LDS bandwidth the MFMAs could consume. K advances in
+// slabs of 64 (128 bytes per row) through two LDS buffers.
+//
+// Staging. Operands go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane: one wavefront instruction writes 8
+// rows of 128 bytes). The 16-byte group q of row r lands in slot
+// q ^ ((r ^ r/8) mod 8): the 16 lanes of one read phase (rows r..r+15, one
+// group) then hit distinct bank groups for both 32- and 64-bank LDS. Loads
+// outside the operand (rows past M or N, k past K) read a zero block instead,
+// so padded slots add nothing and no k tail needs clearing.
+//
+// Pipeline (as in the fp32 GEMM): the fill of slab k+1 is issued before the
+// MFMAs of slab k; the fragments of k step s+1 are read after the first row
+// of MFMAs of step s; the slab barrier sits before the last step's MFMAs.
+//
+// Work distribution: one workgroup per output tile, problems concatenated in
+// tile space in longest-processing-time order by the host, workgroup ids
+// remapped so that each XCD gets runs of neighbouring tiles.
+#include "variant_bf16.h"
+
+namespace matopt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Zero bytes read by every load that falls outside an operand.
+__device__ __attribute__((aligned(64))) uint32_t g_gemm16_zero[16];
+
+namespace {
+
+constexpr int XCD = 8;
+constexpr int XCD_RUN = 16;
+constexpr int GROUP_M = 4;
+
+template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N>
+struct Cfg16 {
+    static constexpr int WM = WAVES_M, WN = WAVES_N, TM = BLK_M, TN = BLK_N;
+    static constexpr int BK = 64;          // k values per LDS slab: rows of 128 bytes
+    static constexpr int NS = BK / 16;     // MFMA k steps per slab
+    static constexpr int NT = 64 * WM * WN, NW = NT / 64;
+    static constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
+    static constexpr int AB = BM * BK * 2, BB = BN * BK * 2;   // bytes of one A / B buffer
+    static constexpr int SMEM = 2 * (AB + BB);
+    static_assert((AB / 1024) % NW == 0 && (BB / 1024) % NW == 0, "tile not divisible into LDS chunks");
+    static_assert(NS % 2 == 0, "the last k step's fragments are in slot 1");
+};
+using Small16 = Cfg16<2, 2, 2, 2>;
+using Large16 = Cfg16<2, 2, 4, 4>;
+static_assert(Small16::BM == kGemm16Cfgs[0].bm && Small16::BN == kGemm16Cfgs[0].bn, "tile size mismatch");
+static_assert(Large16::BM == kGemm16Cfgs[1].bm && Large16::BN == kGemm16Cfgs[1].bn, "tile size mismatch");
+
+__device__ __forceinline__ int swz16(int r) { return (r ^ (r >> 3)) & 7; }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* gsrc_ptr;
+
+// One slab (R rows x 64 k) of an operand into LDS buffer `buf`: rows r0.. of
+// a row-major bf16 matrix with `rows` rows, k0.. of its K columns.
+template <class C, int R>
+__device__ __forceinline__ void dma16(char* buf, const uint16_t* base, int64_t ld, int rows, int K, int r0,
+                                      int k0) {
+    constexpr int CPW = R / 8 / C::NW;   // 1 KiB chunks (8 rows) per wavefront
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int t = 0; t < CPW; ++t) {
+        const int c = wave * CPW + t;
+        const int r = 8 * c + (lane >> 3);
+        const int k = k0 + 8 * ((lane & 7) ^ swz16(r));
+        const int grow = r0 + r;
+        const void* src = (grow < rows && k < K) ? (const void*)(base + (int64_t)grow * ld + k)
+                                                  : (const void*)g_gemm16_zero;
+        __builtin_amdgcn_global_load_lds((gsrc_ptr)src, (lds_ptr)(buf + c * 1024), 16, 0, 0);
+    }
+}
+
+// Fragments of k step s: lane l takes row (or column) l % 32 of each 32-block
+// and k values 16 s + 8 (l / 32) .. +7 of the slab.
+template <class C>
+__device__ __forceinline__ void frags16(const char* As, const char* Bs, int s, int wm, int wn, int lane,
+                                        bf16x8 (&a)[C::TM], bf16x8 (&b)[C::TN]) {
+    const int q = 2 * s + (lane >> 5), l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+        const int row = wm * 32 * C::TM + i * 32 + l32;
+        a[i] = *(const bf16x8*)(As + row * 128 + ((q ^ swz16(row)) << 4));
+    }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+        const int col = wn * 32 * C::TN + j * 32 + l32;
+        b[j] = *(const bf16x8*)(Bs + col * 128 + ((q ^ swz16(col)) << 4));
+    }
+}
+
+// MFMAs of accumulator rows I0 .. I1-1 for one k step.
+template <class C, int I0, int I1>
+__device__ __forceinline__ void mma16(const bf16x8 (&a)[C::TM], const bf16x8 (&b)[C::TN],
+                                      f32x16 (&acc)[C::TM][C::TN]) {
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4,
+// column l % 32 of its 32 x 32 block.
+template <class C, bool OUT16>
+__device__ __forceinline__ void epi16(const Gemm16Prob& p, int m0, int n0, int wm, int wn, int lane,
+                                      const f32x16 (&acc)[C::TM][C::TN], float alpha) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+        float cold[C::TN][16];
+        if (!OUT16 && p.beta != 0.f) {
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    cold[j][r] = (row < p.M && col < p.N) ? gptr((const float*)p.C)[(int64_t)row * p.ldc + col] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
+            if (OUT16 ? col >= p.pad_n : col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (row >= p.M) continue;
+                if (OUT16) {
+                    gptr((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = col < p.N ? to_bf16(alpha * acc[i][j][r]) : 0;
+                } else {
+                    float val = alpha * acc[i][j][r];
+                    if (p.beta != 0.f) val += p.beta * cold[j][r];
+                    gptr((float*)p.C)[(int64_t)row * p.ldc + col] = val;
+                }
+            }
+        }
+    }
+}
+
+template <class C, bool OUT16>
+__device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, float alpha_scale, char* smem) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    // buffer b of A at smem + b AB, of B at smem + 2 AB + b BB
+    auto fill = [&](int b, int k0) {
+        dma16<C, C::BM>(smem + b * C::AB, p.A, p.lda, p.M, p.K, m0, k0);
+        dma16<C, C::BN>(smem + 2 * C::AB + b * C::BB, p.B, p.ldb, p.N, p.K, n0, k0);
+    };
+    f32x16 acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int nk = (p.K + C::BK - 1) / C::BK;
+    const float alpha = p.alpha * alpha_scale;
+    if (nk == 0) {
+        epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha);
+        return;
+    }
+    fill(0, 0);
+    __syncthreads();
+    bf16x8 fa[2][C::TM], fb[2][C::TN];
+    frags16<C>(smem, smem + 2 * C::AB, 0, wm, wn, lane, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const char* As = smem + cur * C::AB;
+        const char* Bs = smem + 2 * C::AB + cur * C::BB;
+        // past the last slab the fill reads only the zero block into the idle buffer
+        fill(cur ^ 1, (kt + 1) * C::BK);
+#pragma unroll
+        for (int s = 0; s < C::NS - 1; ++s) {
+            mma16<C, 0, 1>(fa[s & 1], fb[s & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+            frags16<C>(As, Bs, s + 1, wm, wn, lane, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mma16<C, 1, C::TM>(fa[s & 1], fb[s & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        mma16<C, 0, 1>(fa[1], fb[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        frags16<C>(smem + (cur ^ 1) * C::AB, smem + 2 * C::AB + (cur ^ 1) * C::BB, 0, wm, wn, lane, fa[0], fb[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        mma16<C, 1, C::TM>(fa[1], fb[1], acc);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha);
+}
+
+// Tile -> (row, column) of tiles, grouped by GROUP_M tile rows for L2 reuse.
+__device__ __forceinline__ void raster16(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+    const int per_group = GROUP_M * tiles_n;
+    const int gidx = t / per_group;
+    const int first = gidx * GROUP_M;
+    const int gsz = min(tiles_m - first, GROUP_M);
+    const int r = t - gidx * per_group;
+    tm = first + r % gsz;
+    tn = r / gsz;
+}
+
+// Workgroup id -> logical tile: within each full window of XCD * XCD_RUN
+// ids, the ids the dispatcher sends to one XCD get XCD_RUN consecutive tiles.
+__device__ __forceinline__ int xcd_remap16(int bid, int total) {
+    const int win = XCD * XCD_RUN;
+    const int w0 = (bid / win) * win;
+    if (w0 + win > total) return bid;
+    const int r = bid - w0;
+    return w0 + (r % XCD) * XCD_RUN + r / XCD;
+}
+
+struct Gemm16Args {
+    const Gemm16Prob* probs;
+    const int32_t* tile_begin;
+    int nprob;
+    int total_tiles;
+    float alpha_scale;
+    Gemm16Prob single;
+};
+
+template <class C, bool OUT16>
+__global__ __launch_bounds__(C::NT) void gemm16_kernel(Gemm16Args args) {
+    __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+    const int bid = xcd_remap16(blockIdx.x, args.total_tiles);
+    Gemm16Prob p;
+    int t = bid;
+    if (args.nprob > 0) {
+        int lo = 0, hi = args.nprob - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (args.tile_begin[mid] <= bid) lo = mid; else hi = mid - 1;
+        }
+        p = args.probs[lo];
+        t = bid - args.tile_begin[lo];
+    } else {
+        p = args.single;
+    }
+    int tm, tn;
+    raster16(t, p.tiles_m, p.tiles_n, tm, tn);
+    tile16<C, OUT16>(p, tm, tn, args.alpha_scale, smem);
+}
+
+template <bool OUT16>
+hipError_t launch16(int cfg, const Gemm16Args& a, hipStream_t s) {
+    if (a.total_tiles <= 0) return hipSuccess;
+    if (cfg == 1)
+        gemm16_kernel<Large16, OUT16><<<dim3(a.total_tiles), dim3(Large16::NT), 0, s>>>(a);
+    else
+        gemm16_kernel<Small16, OUT16><<<dim3(a.total_tiles), dim3(Small16::NT), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm16_grouped(bool c_bf16, int cfg, const Gemm16Prob* probs, const int32_t* tile_begin,
+                                 int nprob, int total_tiles, float alpha_scale, hipStream_t s) {
+    if (nprob <= 0) return hipSuccess;
+    Gemm16Args a{};
+    a.probs = probs;
+    a.tile_begin = tile_begin;
+    a.nprob = nprob;
+    a.total_tiles = total_tiles;
+    a.alpha_scale = alpha_scale;
+    return c_bf16 ? launch16<true>(cfg, a, s) : launch16<false>(cfg, a, s);
+}
+
+hipError_t launch_gemm16_single(bool c_bf16, int cfg, const Gemm16Prob& prob, hipStream_t s) {
+    Gemm16Args a{};
+    a.nprob = 0;
+    a.total_tiles = prob.tiles_m * prob.tiles_n;
+    a.alpha_scale = 1.f;
+    a.single = prob;
+    return c_bf16 ? launch16<true>(cfg, a, s) : launch16<false>(cfg, a, s);
+}
+
+}  // namespace matopt

@@ -26,6 +26,9 @@ each gate bounds the error that phase can add:
   determined only to O(u kappa) and are not compared (several results are
   correct there); (3) the device Q must triangularise that input: the
   strictly lower part of Q^T Z_hat, column-normalised, <= 1e-3.
+* Gate B16 (the bf16-rotation variant, gate_apply_bf16): as gate B against
+  oracle/bf16_rotation.py, with each bf16 intermediate allowed one bf16 ulp
+  (a rounding flip) and the errors propagated root-sum-square at 6 sigma.
 * Gate B (rotate, moments, apply): oracle from the device's W_{t-1},
   v_{t-1}, M_t, U_t, V_t and the same G. v: max relative error <= 1e-4.
   W elementwise: |W - W_ref| <= tau max|W_ref| + 6 lr sqrt((U.U) E^2 (V.V)^T)
@@ -191,6 +194,54 @@ def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper,
     W_ref, v_ref, it = oracle.rotated_adam_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
     tau = 1e-4 if m_dtype == "f32" else 2e-2
     return _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau)
+
+
+def ulp_bf16(x):
+    """One bfloat16 ulp at |x|: 2^(e - 8) for |x| = f 2^e, 0.5 <= f < 1."""
+    x = np.abs(np.asarray(x, np.float64))
+    return np.ldexp(1.0, np.frexp(np.maximum(x, 2.0 ** -126))[1] - 8)
+
+
+def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, tau=1e-3) -> List[GateReport]:
+    """The bf16-rotation variant (oracle/bf16_rotation.py), teacher-forced
+    like gate_apply. The device rounds the same quantities to bf16 but from
+    binary32 accumulations, so each stored bf16 intermediate (S = rb(X Vb),
+    u, P = rb(ub Vb^T)) may sit one bf16 ulp from the oracle's where the
+    accumulation crosses a rounding boundary. The model gives every such
+    element its full ulp (an upper bound on a flip) plus the binary32
+    accumulation error 4 u32 sqrt(K) of each product, propagates them root-
+    sum-square through the products (G~ = Ub^T S, P, dW = Ub P) and through u
+    as in gate B, and bounds W element-wise by
+    lr (tau max|dW_ref| + 6 e_dW) + 2^-23 |W_ref| (one binary32 rounding of W)
+    and v by (1 - b2) 2 |G~| 6 e_G~ + 2^-23 |v_ref| + 1e-6 max|v_ref|."""
+    from oracle import bf16_rotation as B
+    W_ref, v_ref, it = B.bf16_rotation_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+    b2 = oracle.as_f32_scalar(hp.beta2)
+    eps = oracle.as_f32_scalar(hp.eps)
+    lr = oracle.as_f32_scalar(hp.lr)
+    Ub, Vb = it["Ub"], it["Vb"]
+    m, n = Ub.shape[0], Vb.shape[0]
+    U2, V2 = Ub * Ub, Vb * Vb
+    rss = lambda A2, B2: np.sqrt(A2 @ B2)
+    Gb = oracle.round_bf16(G)
+    Mb = oracle.round_bf16(M_t)
+    eSG = ulp_bf16(it["SG"]) + 4 * U32 * np.sqrt(n) * rss(Gb * Gb, V2)
+    eSM = ulp_bf16(it["SM"]) + 4 * U32 * np.sqrt(n) * rss(Mb * Mb, V2)
+    eGt = rss(U2.T, eSG ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SG"] ** 2)
+    emt = rss(U2.T, eSM ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SM"] ** 2)
+    u = it["u"]
+    Eu = ulp_bf16(u) + (emt + np.abs(u) * np.sqrt(1 - b2) * eGt) / (np.sqrt(v_ref) + eps)
+    eP = rss(Eu ** 2, V2.T) + ulp_bf16(it["P"]) + 4 * U32 * np.sqrt(n) * rss(it["ub"] ** 2, V2.T)
+    edW = rss(U2, eP ** 2) + 4 * U32 * np.sqrt(m) * rss(U2, it["P"] ** 2)
+    bound_w = lr * (tau * np.max(np.abs(it["dW"])) + 6 * edW) + 2.0 ** -23 * np.abs(W_ref)
+    err_w = np.abs(np.asarray(W_dev, np.float64) - W_ref)
+    bound_v = (1 - b2) * 2 * np.abs(it["Gt"]) * 6 * eGt + 2.0 ** -23 * np.abs(v_ref) + 1e-6 * np.max(v_ref)
+    err_v = np.abs(np.asarray(v_dev, np.float64) - v_ref)
+    return [GateReport("B16.v", bool(np.all(err_v <= bound_v)), {"maxrel": maxrel(v_dev, v_ref),
+                                                                 "worst_ratio": float(np.max(err_v / bound_v))}),
+            GateReport("B16.W", bool(np.all(err_w <= bound_w)),
+                       {"dW_maxrel": float(np.max(err_w) / lr / max(np.max(np.abs(it["dW"])), 1e-300)),
+                        "worst_ratio": float(np.max(err_w / bound_w))})]
 
 
 def gate_apply_rotated_momentum(W_prev, v_prev, Mt_prev, M_t, G, U_t, V_t, W_dev, v_dev, Mt_dev,

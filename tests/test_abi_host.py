@@ -25,7 +25,7 @@ def N():
 def header_functions():
     txt = open(os.path.join(ROOT, "include", "matopt.h")).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(opt_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(opt_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_every_declared_symbol_is_exported(N):
@@ -114,8 +114,28 @@ def err(N, fn, *a):
 def test_rejects_bad_hyperparameters(N):
     d = descs(N, [(8, 8)])
     for kw in (dict(beta1=1.0), dict(beta1=-0.1), dict(beta2=1.0), dict(eps=0.0), dict(eps=float("inf")),
-               dict(lr=float("nan")), dict(K=-1), dict(power_iters=0), dict(flags=2), dict(flags=1 << 31)):
+               dict(lr=float("nan")), dict(K=-1), dict(power_iters=0), dict(flags=4), dict(flags=1 << 31)):
         assert err(N, N.opt_group_workspace_size, d, hp(N, **kw)) == N.OPT_EINVAL, kw
+
+
+def test_flag_combinations(N):
+    d = descs(N, [(8, 8)])
+    N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
+    both = N.OPT_FLAG_BF16_ROTATION | N.OPT_FLAG_ROTATED_MOMENTUM
+    assert err(N, N.opt_group_workspace_size, d, hp(N, flags=both)) == N.OPT_EUNSUPPORTED
+
+
+def test_bf16_rotation_workspace_holds_the_bf16_bases(N):
+    """The variant adds bf16 copies of U, U^T, V, V^T for every matrix
+    (rows padded to multiples of 8 elements) to the shared scratch."""
+    shapes = [(130, 67), (64, 64), (24, 40)]
+    d = descs(N, shapes)
+    base = N.opt_group_workspace_size(d, hp(N))
+    var = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
+    r8 = lambda x: (x + 7) // 8 * 8
+    bases = sum(2 * 2 * m * r8(m) + 2 * 2 * n * r8(n) for m, n in shapes)
+    assert var >= base + bases
+    assert var < base + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
 
 
 def test_rejects_bad_shapes_and_dtypes(N):
@@ -165,6 +185,14 @@ def test_null_group_and_bad_building_block_args(N):
     assert err(N, N.opt_gemm, 0, 0, 4, 4, 4, 1.0, 1, 3, 4, 1, 0, 4, 0.0, 1, 4, 0) == N.OPT_EUNSUPPORTED
     assert err(N, N.opt_gemm, 0, 0, 4, 4, 8, 1.0, 1, 0, 4, 1, 0, 4, 0.0, 1, 4, 0) == N.OPT_EINVAL  # lda < K
     N.opt_gemm(0, 0, 0, 4, 4, 1.0, 0, 0, 4, 0, 0, 4, 0.0, 0, 4, 0)              # empty: no-op
+    # bf16 GEMM: K, lda, ldb multiples of 8, A and B 16-byte aligned, a bf16 C without beta
+    g16 = dict(M=4, N=4, K=8, alpha=1.0, A=1 << 40, lda=8, B=1 << 41, ldb=8, beta=0.0, Cp=1 << 42, c_dtype=0,
+               ldc=4, stream_ptr=0)
+    for kw, st in ((dict(K=7), N.OPT_EINVAL), (dict(lda=12), N.OPT_EINVAL), (dict(A=(1 << 40) + 8), N.OPT_EINVAL),
+                   (dict(c_dtype=1, beta=1.0), N.OPT_EINVAL), (dict(c_dtype=5), N.OPT_EUNSUPPORTED),
+                   (dict(ldc=3), N.OPT_EINVAL), (dict(M=-1), N.OPT_EINVAL), (dict(lda=4, K=8), N.OPT_EINVAL)):
+        assert err(N, lambda: N.opt_gemm_bf16(**dict(g16, **kw))) == st, kw
+    N.opt_gemm_bf16(**dict(g16, M=0))                                           # empty: no-op
     assert err(N, N.opt_orthonormalize_workspace_size, 0) == N.OPT_EINVAL
     assert err(N, N.opt_orthonormalize_workspace_size, N.OPT_MAX_DIM + 1) == N.OPT_EUNSUPPORTED
     assert N.opt_orthonormalize_workspace_size(100) > 0

@@ -82,3 +82,51 @@ def test_apply_gate_accepts_fp32_emulation_and_rejects_error():
     bad[5, 6] += 3e-4 * np.max(np.abs(W))
     reps = contract.gate_apply(W, v, M, G, U, V, bad, v32.astype(np.float64), hp, "f32")
     assert not all(x.ok for x in reps)
+
+
+def _emulate_bf16_rotation(W, v, M, G, U, V, hp, transposed_u=False):
+    """The bf16-rotation step with binary32 accumulation and the device's
+    rounding points, through torch on the CPU (bf16 casts round to nearest
+    even)."""
+    t = lambda x: torch.from_numpy(np.asarray(x, np.float64)).float()
+    bf = lambda x: x.to(torch.bfloat16).float()
+    Ub, Vb = bf(t(U)), bf(t(V))
+    if transposed_u:
+        Ub = Ub.T.contiguous()
+    SG = bf(bf(t(G)) @ Vb)
+    SM = bf(bf(t(M)) @ Vb)
+    Gt = Ub.T @ SG
+    mt = Ub.T @ SM
+    v32 = np.float32(hp.beta2) * t(v) + (1 - np.float32(hp.beta2)) * Gt * Gt
+    u = mt / (torch.sqrt(v32) + np.float32(hp.eps))
+    P = bf(bf(u) @ Vb.T)
+    W32 = t(W) - np.float32(hp.lr) * (Ub @ P)
+    return W32.double().numpy(), v32.double().numpy()
+
+
+def _bf16_case(seed, m, n):
+    r = rng(seed)
+    W = oracle.round_f32(r.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(r.random((m, n)) * 1e-5)
+    M = oracle.round_bf16(r.standard_normal((m, n)) * 1e-3)
+    G = oracle.round_f32(r.standard_normal((m, n)) * 1e-2)
+    U = oracle.round_f32(np.linalg.qr(r.standard_normal((m, m)))[0])
+    V = oracle.round_f32(np.linalg.qr(r.standard_normal((n, n)))[0])
+    return W, v, M, G, U, V
+
+
+def test_bf16_apply_gate_accepts_emulation_and_rejects_errors():
+    hp = oracle.Hyper()
+    for seed, (m, n) in enumerate([(24, 40), (64, 64), (96, 48)]):
+        W, v, M, G, U, V = _bf16_case(10 + seed, m, n)
+        Wd, vd = _emulate_bf16_rotation(W, v, M, G, U, V, hp)
+        reps = contract.gate_apply_bf16(W, v, M, G, U, V, Wd, vd, hp)
+        assert all(x.ok for x in reps), [str(x) for x in reps]
+        # a transposed left basis, a 10 % larger step, one corrupted element
+        Wt, vt = _emulate_bf16_rotation(W, v, M, G, U, V, hp, transposed_u=True)
+        assert not all(x.ok for x in contract.gate_apply_bf16(W, v, M, G, U, V, Wt, vt, hp))
+        Wl = oracle.round_f32(W + 1.1 * (Wd - W))
+        assert not contract.gate_apply_bf16(W, v, M, G, U, V, Wl, vd, hp)[1].ok
+        Wc = Wd.copy()
+        Wc[3, 5] -= 0.2 * np.float32(hp.lr) * np.max(np.abs(Wd - W)) / np.float32(hp.lr)
+        assert not contract.gate_apply_bf16(W, v, M, G, U, V, Wc, vd, hp)[1].ok

@@ -1,0 +1,95 @@
+"""GPU parity of the bf16-rotation variant (OPT_FLAG_BF16_ROTATION) against
+oracle/bf16_rotation.py, teacher-forced (tests/contract.py): each step the
+device's persisted state before the step feeds the oracle. The first step
+runs the fp32 rotations (gate B), later steps the bf16 ones (gate B16); the
+momentum and the refresh are the method's (gates M and A)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import contract, harness
+
+pytestmark = pytest.mark.gpu
+
+
+def _build(wl, capacity=None):
+    import matrix_optimizer_step_02_amd as mo
+    hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, capacity or wl.capacity_bytes,
+                  bf16_rotation=True)
+    return harness.build_group(wl, "cuda", hp)
+
+
+def _run(wl, steps, check_mats, events=None, capacity=None, min_groups=1):
+    import torch
+    grp, states = _build(wl, capacity)
+    assert grp.plan([(x.m, x.n) for x in wl.matrices], grp.hp)[2] >= min_groups
+    hp = harness.oracle_hyper(wl)
+    failures = []
+    for t in range(1, steps + 1):
+        if events and t in events:
+            events[t](grp)
+        harness.load_gradients(wl, states, t)
+        torch.cuda.synchronize()
+        before = {i: harness.snap(states[i]) for i in check_mats}
+        grp.step()
+        torch.cuda.synchronize()
+        refreshed = oracle.refresh_due(t, wl.K)
+        for i in check_mats:
+            a, b = before[i], harness.snap(states[i])
+            reps = [contract.gate_momentum(a["M"], a["G"], b["M"], wl.beta1, wl.m_dtype)]
+            if refreshed:
+                reps += contract.gate_refresh(b["M"], a["U"], a["V"], b["U"], b["V"], wl.power_iters)
+            elif not (events and t in events):
+                reps.append(contract.GateReport("A.unchanged", np.array_equal(a["U"], b["U"])
+                                                and np.array_equal(a["V"], b["V"])))
+            if t == 1:
+                reps += contract.gate_apply(a["W"], a["v"], b["M"], a["G"], b["U"], b["V"], b["W"], b["v"], hp,
+                                            wl.m_dtype)
+            else:
+                reps += contract.gate_apply_bf16(a["W"], a["v"], b["M"], a["G"], b["U"], b["V"], b["W"], b["v"], hp)
+            line = f"t={t} mat={i} {wl.matrices[i].m}x{wl.matrices[i].n}: " + "; ".join(map(str, reps))
+            print(line, flush=True)
+            failures += [line for r in reps if not r.ok]
+    grp.close()
+    assert not failures, "\n".join(failures)
+
+
+@pytest.mark.parametrize("m_dtype", ["f32", "bf16"])
+def test_bf16_rotation_ragged_shapes(m_dtype):
+    """Refresh every 3 steps over 7; shapes with n % 8 != 0 (the padded
+    path), n % 8 == 0 (fused side outputs), tiles with ragged edges."""
+    mats = (workloads.MatrixSpec("a", 37, 53), workloads.MatrixSpec("b", 130, 67),
+            workloads.MatrixSpec("c", 200, 200), workloads.MatrixSpec("d", 64, 96),
+            workloads.MatrixSpec("e", 24, 40))
+    wl = workloads.Workload("ragged_b16", 7, "ragged", mats, m_dtype, K=3, power_iters=1, steps=7,
+                            grad_kind="iid", grad_std=1e-2)
+    _run(wl, 7, range(len(mats)))
+
+
+def test_bf16_rotation_layer_shapes():
+    """The transformer-layer workload (1024 x 1024, 1024 x 3072, 3072 x 1024,
+    bf16 momentum, refresh every 10): 12 steps cover the refresh at t = 11."""
+    wl = workloads.get("layer")
+    _run(wl, 12, [1, 5, 6])
+
+
+def test_bf16_rotation_rebuilds_bases_after_external_changes():
+    """refresh_basis and set_step between steps change or may change U, V:
+    the next step must rotate with bf16 copies of the new bases."""
+    wl = workloads.get("layer")
+    wl = workloads.Workload(wl.key, wl.index, wl.title, wl.matrices, wl.m_dtype, K=0, power_iters=1, steps=6,
+                            grad_kind=wl.grad_kind, grad_std=wl.grad_std)
+    events = {3: lambda g: g.refresh_basis(1), 5: lambda g: setattr(g, "t", g.t)}
+    _run(wl, 6, [0, 4, 6], events)
+
+
+def test_bf16_rotation_several_micro_groups():
+    """A 16 MiB cap splits the layer workload into several micro-groups that
+    share one scratch: each group's bf16 copies of G and M must be made after
+    the previous group's rotations, and after the refresh (K = 3)."""
+    wl = workloads.get("layer")
+    wl = workloads.Workload(wl.key, wl.index, wl.title, wl.matrices, wl.m_dtype, K=3, power_iters=1, steps=5,
+                            grad_kind=wl.grad_kind, grad_std=wl.grad_std)
+    _run(wl, 5, [0, 3, 6], capacity=1 << 24, min_groups=3)
