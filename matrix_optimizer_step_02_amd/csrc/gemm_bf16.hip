@@ -35,6 +35,8 @@ namespace matopt {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Zero bytes read by every load that falls outside an operand.
 __device__ __attribute__((aligned(64))) uint32_t g_gemm16_zero[16];
@@ -120,43 +122,86 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Accumulator register r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4,
-// column l % 32 of its 32 x 32 block.
+// Epilogue through LDS. Accumulator register r of lane l holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of its 32 x 32 block, so a
+// direct store would write four rows per register group with 4-byte accesses.
+// Instead each wavefront copies one 32-row slice of its block (32 x 32 TN
+// values) into its own LDS region, row-major with a row stride of
+// 32 TN + 8 floats (the two half-waves, 4 rows apart, then fill all 64 banks),
+// reads it back as 16-byte row segments and writes those with 16-byte stores
+// (8-byte for bf16), reading old C the same way when beta != 0. The LDS
+// buffers are free once every wavefront has passed the barrier that follows
+// the main loop.
+template <class C>
+struct Epi16 {
+    static constexpr int W = 32 * C::TN;        // columns of a wavefront's block
+    static constexpr int LD = W + 8;            // LDS row stride (floats)
+    static constexpr int REGION = 32 * LD;      // floats per wavefront
+    static constexpr int LPR = W / 4;           // lanes per row (4 floats each)
+    static constexpr int RPI = 64 / LPR;        // rows per read instruction
+    static_assert(C::NW * REGION * 4 <= C::SMEM, "epilogue staging does not fit in LDS");
+    static_assert(64 % LPR == 0, "a row must split evenly over the lanes");
+};
+
 template <class C, bool OUT16>
 __device__ __forceinline__ void epi16(const Gemm16Prob& p, int m0, int n0, int wm, int wn, int lane,
-                                      const f32x16 (&acc)[C::TM][C::TN], float alpha) {
+                                      const f32x16 (&acc)[C::TM][C::TN], float alpha, char* smem) {
+    using E = Epi16<C>;
     const int h = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    float* reg = (float*)smem + wave * E::REGION;
+    const int col0 = n0 + wn * E::W;
+    // 16-byte (fp32) or 8-byte (bf16) groups of 4 columns need ldc % 4 == 0 and an aligned C
+    const bool vec = (p.ldc % 4 == 0) && (((uintptr_t)p.C) % (OUT16 ? 8 : 16) == 0);
+    const int lim = OUT16 ? p.pad_n : p.N;   // columns stored (bf16: zeros in [N, pad_n))
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
-        float cold[C::TN][16];
-        if (!OUT16 && p.beta != 0.f) {
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
+        for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    cold[j][r] = (row < p.M && col < p.N) ? gptr((const float*)p.C)[(int64_t)row * p.ldc + col] : 0.f;
-                }
-            }
-        }
+            for (int r = 0; r < 16; ++r)
+                reg[(8 * (r >> 2) + 4 * h + (r & 3)) * E::LD + j * 32 + l32] = alpha * acc[i][j][r];
+        __syncthreads();
+        const int row0 = m0 + wm * 32 * C::TM + i * 32;
 #pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
-            if (OUT16 ? col >= p.pad_n : col >= p.N) continue;
+        for (int it = 0; it < 32 / E::RPI; ++it) {
+            const int rl = it * E::RPI + lane / E::LPR, c4 = 4 * (lane % E::LPR);
+            const int row = row0 + rl, col = col0 + c4;
+            const f32x4 v = *(const f32x4*)&reg[rl * E::LD + c4];
+            if (row >= p.M || col >= lim) continue;
+            const int64_t off = (int64_t)row * p.ldc + col;
+            if (OUT16) {
+                uint16_t o[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 32 * C::TM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (row >= p.M) continue;
-                if (OUT16) {
-                    gptr((uint16_t*)p.C)[(int64_t)row * p.ldc + col] = col < p.N ? to_bf16(alpha * acc[i][j][r]) : 0;
+                for (int e = 0; e < 4; ++e) o[e] = col + e < p.N ? to_bf16(v[e]) : 0;
+                if (vec && col + 3 < lim) {
+                    u32x2 w;
+                    w.x = (uint32_t)o[0] | ((uint32_t)o[1] << 16);
+                    w.y = (uint32_t)o[2] | ((uint32_t)o[3] << 16);
+                    *gptr((u32x2*)((uint16_t*)p.C + off)) = w;
                 } else {
-                    float val = alpha * acc[i][j][r];
-                    if (p.beta != 0.f) val += p.beta * cold[j][r];
-                    gptr((float*)p.C)[(int64_t)row * p.ldc + col] = val;
+                    for (int e = 0; e < 4 && col + e < lim; ++e) gptr((uint16_t*)p.C)[off + e] = o[e];
+                }
+            } else {
+                f32x4 out = v;
+                if (vec && col + 3 < lim) {
+                    if (p.beta != 0.f) {
+                        const f32x4 old = *gptr((const f32x4*)((const float*)p.C + off));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) out[e] += p.beta * old[e];
+                    }
+                    *gptr((f32x4*)((float*)p.C + off)) = out;
+                } else {
+                    for (int e = 0; e < 4 && col + e < lim; ++e) {
+                        float x = out[e];
+                        if (p.beta != 0.f) x += p.beta * gptr((const float*)p.C)[off + e];
+                        gptr((float*)p.C)[off + e] = x;
+                    }
                 }
             }
         }
+        __syncthreads();
     }
 }
 
@@ -180,7 +225,7 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     const int nk = (p.K + C::BK - 1) / C::BK;
     const float alpha = p.alpha * alpha_scale;
     if (nk == 0) {
-        epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha);
+        epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);
         return;
     }
     fill(0, 0);
@@ -210,7 +255,7 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         mma16<C, 1, C::TM>(fa[1], fb[1], acc);
         __builtin_amdgcn_sched_barrier(0);
     }
-    epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha);
+    epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);
 }
 
 // Tile -> (row, column) of tiles, grouped by GROUP_M tile rows for L2 reuse.
