@@ -153,9 +153,10 @@ def traffic_per_launch():
     return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
 
-def cpu_baseline(wl, budget_s: float):
+def cpu_baseline(wl, budget_s: float, muon_iters: int = 0):
     """The oracle as it stands, one non-refresh step on one matrix of each
-    distinct shape, weighted by shape counts, scaled to parameters/s."""
+    distinct shape, weighted by shape counts, scaled to parameters/s
+    (muon_iters > 0: the orthogonalised-momentum oracle instead)."""
     import numpy as np
     import oracle
     import workloads
@@ -174,7 +175,11 @@ def cpu_baseline(wl, budget_s: float):
         G = workloads.gradient(wl, i, 1).double().numpy()
         # basis from an earlier refresh: the identity is as costly for the oracle as any other
         t0 = time.time()
-        oracle.step(st, G, hp)
+        if muon_iters:
+            from oracle import muon
+            muon.muon_apply(st.W, st.M, G, wl.beta1, wl.lr, muon_iters, wl.m_dtype)
+        else:
+            oracle.step(st, G, hp)
         dt = time.time() - t0
         total_s += dt * c
         done.append((m, n, c, dt))
@@ -190,9 +195,11 @@ def cpu_baseline(wl, budget_s: float):
         "unit": "params/s",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
-        "sample": ("one non-refresh fp64 oracle step on one matrix of each distinct shape "
+        "sample": ((f"one fp64 orthogonalised-momentum oracle step ({muon_iters} Newton-Schulz iterations)"
+                    if muon_iters else "one non-refresh fp64 oracle step")
+                   + " on one matrix of each distinct shape "
                    + ", ".join(f"{m}x{n} ({dt:.2f} s, x{c})" for m, n, c, dt in done)
-                   + "; refresh steps excluded, so this over-states the oracle's rate"),
+                   + ("" if muon_iters else "; refresh steps excluded, so this over-states the oracle's rate")),
         "host_cpus": os.cpu_count(),
     }
 
@@ -210,6 +217,9 @@ def main(argv=None):
                     help="the variant that carries m~ in rotated coordinates within a basis epoch")
     ap.add_argument("--bf16-rotation", action="store_true",
                     help="the variant that runs the rotations on bf16 operands (fp32 accumulation)")
+    ap.add_argument("--muon", action="store_true",
+                    help="the orthogonalised-momentum step (Newton-Schulz polar factor of M) instead")
+    ap.add_argument("--ns-iters", type=int, default=5, help="Newton-Schulz iterations of --muon")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -254,12 +264,13 @@ def main(argv=None):
     states = []
     for i, s in enumerate(wl.matrices):
         W0 = workloads.initial_weight(wl, i, dev)
-        st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0, rotated_momentum=args.rotated_momentum)
+        st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0, rotated_momentum=args.rotated_momentum,
+                          bases=not args.muon)
         st["G"].copy_(workloads.gradient(wl, i, 1, dev))
         states.append(st)
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
                   int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum,
-                  bf16_rotation=args.bf16_rotation)
+                  bf16_rotation=args.bf16_rotation, muon=args.muon, ns_iters=args.ns_iters if args.muon else 0)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()
@@ -292,7 +303,21 @@ def main(argv=None):
 
     roofline = None
     extra = {}
-    if phases:
+    if phases and args.muon:
+        ns_flops = sum(4.0 * min(m, n) ** 2 * max(m, n) for m, n in shapes) * args.ns_iters
+        ms = phases["ortho"][0]
+        achieved = ns_flops * args.steps / (ms * 1e-3) / 1e12 if ms > 0 else None
+        roofline = {
+            "bound": "mfma", "achieved": achieved, "peak": MI355X_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None, "traffic": None,
+            "kernel": "gemm_grouped_kernel (Newton-Schulz X^T X and X (X^T X); the phase time includes the "
+                      "norm, scaling and combine kernels)",
+            "launches": phases["ortho"][1], "avg_launch_ms": ms / max(phases["ortho"][1], 1),
+            "flops_per_step": ns_flops,
+        }
+        extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
+        extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
+    elif phases:
         pf = phase_flops(shapes)
         flops = sum(pf.values()) * args.steps
         if args.rotated_momentum:   # recompute steps are the refreshes; the others carry m~
@@ -326,7 +351,7 @@ def main(argv=None):
     cpu = None
     if args.cpu_sample_s > 0:
         print("[bench] timing the oracle on the host (cpu_baseline)", flush=True)
-        cpu = cpu_baseline(wl, args.cpu_sample_s)
+        cpu = cpu_baseline(wl, args.cpu_sample_s, args.ns_iters if args.muon else 0)
 
     out = {
         "metric": METRIC,
@@ -345,7 +370,8 @@ def main(argv=None):
                    "momentum_dtype": wl.m_dtype, "K": wl.K, "power_iters": wl.power_iters,
                    "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
                    "rotated_momentum": bool(args.rotated_momentum),
-                   "bf16_rotation": bool(args.bf16_rotation)},
+                   "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
+                   **({"ns_iters": args.ns_iters} if args.muon else {})},
         "steps_per_s": steps_per_s,
         "roofline": roofline,
         "cpu_baseline": cpu,

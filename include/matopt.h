@@ -79,7 +79,8 @@ typedef struct {
     const float* G;        /* m x n fp32 gradient, read by every step (caller refills it) */
     void* M;               /* m x n momentum, fp32 or bf16 (M_dtype), updated in place; start at 0 */
     int32_t M_dtype;       /* opt_dtype */
-    float* v;              /* m x n fp32 second moment in rotated coordinates; start at 0 */
+    float* v;              /* m x n fp32 second moment in rotated coordinates; start at 0
+                              (NULL allowed with OPT_FLAG_MUON, as for U and V) */
     float* U;              /* m x m fp32 orthonormal left basis, updated by refreshes; start at I */
     float* V;              /* n x n fp32 orthonormal right basis, updated by refreshes; start at I */
     float* Mt;             /* m x n fp32 momentum in rotated coordinates, used only with
@@ -117,7 +118,17 @@ enum {
      * OPT_FLAG_ROTATED_MOMENTUM (OPT_EUNSUPPORTED). The workspace grows by the
      * bf16 bases, 4 (m m8 + n n8) bytes per matrix (m8, n8: m, n rounded up
      * to a multiple of 8). */
-    OPT_FLAG_BF16_ROTATION = 2u
+    OPT_FLAG_BF16_ROTATION = 2u,
+    /* A second matrix optimizer on the same groups: the orthogonalised
+     * momentum step (Muon-style; the Canzona page, sections 1 and 7, names
+     * Muon and its orthogonalisation without a formula). M is the same EMA,
+     * then O = the orthogonal polar factor of M approximated by ns_iters
+     * steps of the cubic Newton-Schulz iteration X <- 1.5 X - 0.5 X X^T X
+     * from X = M / ||M||_F (on the side with the smaller Gram matrix), and
+     * W <- W - lr O. v, U, V are unused (may be NULL), as are beta2, eps, K
+     * and power_iters; refresh_basis, health and reorthonormalize return
+     * OPT_EUNSUPPORTED. Cannot be combined with the other flags. */
+    OPT_FLAG_MUON = 4u
 };
 
 typedef struct {
@@ -132,6 +143,7 @@ typedef struct {
                                         d x d QR inputs and their scratch); 0 selects 48 GiB.
                                         A matrix larger than the cap forms a batch alone. */
     uint32_t flags;           /* OPT_FLAG_* bits; others must be 0 */
+    int32_t ns_iters;         /* Newton-Schulz iterations of OPT_FLAG_MUON, >= 1 there; else ignored */
 } opt_hparams;
 
 #define OPT_MAX_DIM 16384       /* largest m or n the QR panel kernel supports */
@@ -211,7 +223,8 @@ enum {
     OPT_PHASE_ADAM = 4,       /* v and u in the rotated basis (elementwise) */
     OPT_PHASE_BACK_LEFT = 5,  /* U u                          (grouped GEMM) */
     OPT_PHASE_BACK_RIGHT = 6, /* W -= lr (U u) V^T            (grouped GEMM + apply) */
-    OPT_NUM_PHASES = 7
+    OPT_PHASE_ORTHO = 7,      /* OPT_FLAG_MUON: norm, Newton-Schulz products and combines, apply */
+    OPT_NUM_PHASES = 8
 };
 /* enable != 0 starts recording (and clears the totals); 0 stops. */
 opt_status opt_group_set_timing(opt_group_t g, int32_t enable);

@@ -29,13 +29,16 @@ class Hyper:
     refresh_capacity_bytes: int = 0   # 0: library default (48 GiB)
     rotated_momentum: bool = False    # carry m~ in rotated coordinates (needs an Mt tensor per matrix)
     bf16_rotation: bool = False       # rotations on bf16 operands (fp32 accumulation) from the second step
+    muon: bool = False                # orthogonalised-momentum step instead (no v, U, V)
+    ns_iters: int = 0                 # Newton-Schulz iterations of the muon step (>= 1 there)
 
     def c(self) -> native.opt_hparams:
         flags = (native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0) | \
-                (native.OPT_FLAG_BF16_ROTATION if self.bf16_rotation else 0)
+                (native.OPT_FLAG_BF16_ROTATION if self.bf16_rotation else 0) | \
+                (native.OPT_FLAG_MUON if self.muon else 0)
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,
                                   self.power_iters, self.capacity_bytes,
-                                  self.refresh_capacity_bytes, flags)
+                                  self.refresh_capacity_bytes, flags, self.ns_iters)
 
 
 def tensor_ptr(t) -> int:
@@ -73,14 +76,14 @@ def make_desc(W, G, M, v, U, V, Mt=None) -> native.opt_matrix_desc:
     _check_tensor(W, (m, n), (torch.float32,), "W", dev)
     _check_tensor(G, (m, n), (torch.float32,), "G", dev)
     _check_tensor(M, (m, n), (torch.float32, torch.bfloat16), "M", dev)
-    _check_tensor(v, (m, n), (torch.float32,), "v", dev)
-    _check_tensor(U, (m, m), (torch.float32,), "U", dev)
-    _check_tensor(V, (n, n), (torch.float32,), "V", dev)
+    for t, shape, name in ((v, (m, n), "v"), (U, (m, m), "U"), (V, (n, n), "V")):
+        if t is not None:   # absent only for the muon step
+            _check_tensor(t, shape, (torch.float32,), name, dev)
     if Mt is not None:
         _check_tensor(Mt, (m, n), (torch.float32,), "Mt", dev)
     dt = native.OPT_BF16 if M.dtype == torch.bfloat16 else native.OPT_F32
     return native.opt_matrix_desc(m, n, tensor_ptr(W), tensor_ptr(G), tensor_ptr(M), dt,
-                                  tensor_ptr(v), tensor_ptr(U), tensor_ptr(V),
+                                  *(tensor_ptr(t) if t is not None else 0 for t in (v, U, V)),
                                   tensor_ptr(Mt) if Mt is not None else 0)
 
 
@@ -96,7 +99,8 @@ class RotatedAdamGroup:
         import torch
         self.params = list(params)
         self.hp = hp
-        self.descs = [make_desc(p["W"], p["G"], p["M"], p["v"], p["U"], p["V"], p.get("Mt")) for p in self.params]
+        self.descs = [make_desc(p["W"], p["G"], p["M"], p.get("v"), p.get("U"), p.get("V"), p.get("Mt"))
+                      for p in self.params]
         self._hpc = hp.c()
         self.ws_bytes = native.opt_group_workspace_size(self.descs, self._hpc)
         dev = self.params[0]["W"].device
@@ -153,19 +157,21 @@ class RotatedAdamGroup:
             pass
 
 
-def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None, rotated_momentum=False):
+def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None, rotated_momentum=False,
+              bases=True):
     """Fresh caller-side state of one matrix: W (given or zeros), G zeros,
     M and v zeros, U = I_m, V = I_n (and Mt, uninitialised, for the rotated
-    momentum)."""
+    momentum). bases=False leaves out v, U and V (the muon step)."""
     import torch
     dt = torch.bfloat16 if m_dtype == "bf16" else torch.float32
     W = (W0.to(device=device, dtype=torch.float32).contiguous().clone() if W0 is not None
          else torch.zeros(m, n, device=device))
-    return {
+    st = {
         "W": W,
         "G": torch.zeros(m, n, device=device),
         "M": torch.zeros(m, n, device=device, dtype=dt),
-        "v": torch.zeros(m, n, device=device),
-        "U": torch.eye(m, device=device),
-        "V": torch.eye(n, device=device),
-    } | ({"Mt": torch.empty(m, n, device=device)} if rotated_momentum else {})
+    }
+    if bases:
+        st |= {"v": torch.zeros(m, n, device=device), "U": torch.eye(m, device=device),
+               "V": torch.eye(n, device=device)}
+    return st | ({"Mt": torch.empty(m, n, device=device)} if rotated_momentum else {})

@@ -30,6 +30,7 @@
 
 #include "matopt.h"
 #include "variant_bf16.h"
+#include "variant_muon.h"
 
 using namespace matopt;
 
@@ -125,6 +126,13 @@ struct Group {
     EwLaunch mom16, adam16;
     EwLaunch mom_r, adam_r;   // ragged matrices
     PackLaunch pack_in, pack_u;
+    // orthogonalised momentum (OPT_FLAG_MUON): MuonSeg list (EwLaunch of
+    // MuonSeg), the Gram and product launches of one Newton-Schulz step, and
+    // the norm partials and inverse norms in the scratch
+    EwLaunch mu;
+    std::vector<GemmLaunch> mu_gram, mu_prod;
+    double* mu_part = nullptr;
+    float* mu_inv = nullptr;
     uint64_t rot_bytes = 0;
 };
 
@@ -215,8 +223,12 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (!std::isfinite(hp->lr)) return fail(OPT_EINVAL, "lr must be finite");
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
-    if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION))
+    if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON))
         return fail(OPT_EINVAL, "unknown bits in flags");
+    if ((hp->flags & OPT_FLAG_MUON) && hp->flags != OPT_FLAG_MUON)
+        return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON cannot be combined with other flags");
+    if ((hp->flags & OPT_FLAG_MUON) && hp->ns_iters < 1)
+        return fail(OPT_EINVAL, "ns_iters must be >= 1 with OPT_FLAG_MUON");
     if ((hp->flags & OPT_FLAG_ROTATED_MOMENTUM) && (hp->flags & OPT_FLAG_BF16_ROTATION))
         return fail(OPT_EUNSUPPORTED, "OPT_FLAG_BF16_ROTATION cannot be combined with OPT_FLAG_ROTATED_MOMENTUM");
     return OPT_OK;
@@ -258,7 +270,8 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
                         "capacity %llu (a matrix is never split)",
                         i, (unsigned long long)(4ull * x.m * x.n), (unsigned long long)cap);
         if (!need_ptrs) continue;
-        if (!x.W || !x.G || !x.M || !x.v || !x.U || !x.V)
+        const bool muon = hp->flags & OPT_FLAG_MUON;
+        if (!x.W || !x.G || !x.M || (!muon && (!x.v || !x.U || !x.V)))
             return fail(OPT_EINVAL, "matrix %d: a tensor pointer is NULL", i);
         const bool rm = hp->flags & OPT_FLAG_ROTATED_MOMENTUM;
         if (rm != (x.Mt != nullptr))
@@ -271,9 +284,9 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
         add(x.W, 4 * mn, "W");
         add(x.G, 4 * mn, "G");
         add(x.M, esz * mn, "M");
-        add(x.v, 4 * mn, "v");
-        add(x.U, 4ull * x.m * x.m, "U");
-        add(x.V, 4ull * x.n * x.n, "V");
+        if (x.v) add(x.v, 4 * mn, "v");
+        if (x.U) add(x.U, 4ull * x.m * x.m, "U");
+        if (x.V) add(x.V, 4ull * x.n * x.n, "V");
         if (x.Mt) add(x.Mt, 4 * mn, "Mt");
         if (!aligned(x.W, 4) || !aligned(x.G, 4) || !aligned(x.v, 4) || !aligned(x.U, 4) ||
             !aligned(x.V, 4) || !aligned(x.M, esz) || !aligned(x.Mt, 4))
@@ -716,9 +729,67 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->basis_jobs = g->img.put(bj);
     }
     char* scratch = region + g->bases_bytes;
+    const bool muon = g->hp.flags & OPT_FLAG_MUON;
     for (const std::vector<int>& members : plan) {
         Group G;
         G.mats = members;
+        if (muon) {
+            // X, P (m x n) and the Gram matrix A (p x p, p = min(m, n)) per
+            // matrix, then the norm partials and the inverse norms
+            std::vector<MuonSeg> segs;
+            std::vector<PGemm> gram, prod;
+            uint64_t off = 0;
+            int64_t chunks = 0;
+            for (int mi : members) {
+                const Mat& M = g->mats[mi];
+                const opt_matrix_desc& x = M.d;
+                const int64_t m = x.m, n = x.n, p = std::min(m, n), mn = m * n;
+                float* X = (float*)(scratch + off); off += align_up(4ull * mn);
+                float* P = (float*)(scratch + off); off += align_up(4ull * mn);
+                float* A = (float*)(scratch + off); off += align_up(4ull * p * p);
+                if (m >= n) {
+                    gram.push_back(mk(true, false, X, false, n, X, false, n, A, n, n, n, m, 1.f, 0.f));   // X^T X
+                    prod.push_back(mk(false, false, X, false, n, A, false, n, P, n, m, n, n, 1.f, 0.f));  // X A
+                } else {
+                    gram.push_back(mk(false, true, X, false, n, X, false, n, A, m, m, m, n, 1.f, 0.f));   // X X^T
+                    prod.push_back(mk(false, false, A, false, m, X, false, n, P, n, m, n, m, 1.f, 0.f));  // A X
+                }
+                MuonSeg sg{};
+                sg.M = x.M;
+                sg.X = X;
+                sg.P = P;
+                sg.W = x.W;
+                sg.n = mn;
+                sg.chunk_begin = chunks;
+                sg.m_bf16 = M.bf16;
+                sg.slot = (int32_t)segs.size();
+                chunks += (mn + kEwChunk - 1) / kEwChunk;
+                segs.push_back(sg);
+            }
+            G.mu_part = (double*)(scratch + off); off += align_up(8ull * chunks);
+            G.mu_inv = (float*)(scratch + off); off += align_up(4ull * segs.size());
+            G.mu.nseg = (int)segs.size();
+            G.mu.chunks = chunks;
+            G.mu.segs = g->img.put(segs);
+            G.mu_gram = put_gemm(g->img, gram);
+            G.mu_prod = put_gemm(g->img, prod);
+            std::vector<EwSeg> mom;
+            for (int mi : members) {
+                const Mat& M = g->mats[mi];
+                EwSeg e{};
+                e.a = M.d.G;
+                e.b = M.d.M;
+                e.n = M.d.m * M.d.n;
+                e.b_bf16 = M.bf16;
+                e.vec = aligned(M.d.G, 16) && aligned(M.d.M, M.bf16 ? 8 : 16);
+                mom.push_back(e);
+            }
+            G.mom = put_ew(g->img, mom);
+            G.rot_bytes = off;
+            g->scratch_bytes = std::max(g->scratch_bytes, G.rot_bytes);
+            g->groups.push_back(std::move(G));
+            continue;
+        }
         // ---- rotation scratch
         std::vector<PGemm> left, right, bl, br, right_re, left_c, right_c;
         std::vector<EwSeg> mom, adam, adam_re, adam_c;
@@ -867,7 +938,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->groups.push_back(std::move(G));
     }
 
-    for (const std::vector<int>& members : plan_refresh(g, plan)) {
+    for (const std::vector<int>& members : muon ? std::vector<std::vector<int>>{} : plan_refresh(g, plan)) {
         RefreshBatch R;
         R.mats = members;
         uint64_t off = 0;
@@ -974,7 +1045,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->rbatches.push_back(std::move(R));
     }
     // state checks: every matrix, input order
-    {
+    if (!muon) {
         std::vector<HealthSeg> hs;
         int64_t chunks = 0;
         for (const Mat& M : g->mats) {
@@ -1277,6 +1348,33 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before step");
     hipStream_t s = (hipStream_t)stream;
     g->t += 1;
+    if (g->hp.flags & OPT_FLAG_MUON) {
+        // orthogonalised momentum: M, then per group X_0 = M / ||M||_F and
+        // ns_iters Newton-Schulz steps, the last one fused with the update
+        for (const Group& G : g->groups) {
+            PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+            e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
+            if (e) return hip_fail(e, "momentum launch");
+            g->kernels_in_scope += G.mom.nseg > 0;
+        }
+        for (const Group& G : g->groups) {
+            PhaseScope ps(g, OPT_PHASE_ORTHO, s);
+            const MuonSeg* segs = dptr<MuonSeg>(g, G.mu.segs);
+            e = launch_muon_norm(segs, G.mu.nseg, G.mu.chunks, G.mu_part, G.mu_inv, s);
+            if (!e) e = launch_muon_scale(segs, G.mu.nseg, G.mu.chunks, G.mu_inv, s);
+            if (e) return hip_fail(e, "orthogonalisation launch");
+            g->kernels_in_scope += 3;
+            for (int it = 0; it < g->hp.ns_iters; ++it) {
+                if ((e = run_gemm(g, G.mu_gram, 1.f, s))) return hip_fail(e, "Newton-Schulz Gram launch");
+                if ((e = run_gemm(g, G.mu_prod, 1.f, s))) return hip_fail(e, "Newton-Schulz product launch");
+                const bool last = it + 1 == g->hp.ns_iters;
+                if ((e = launch_muon_combine(segs, G.mu.nseg, G.mu.chunks, last, g->hp.lr, s)))
+                    return hip_fail(e, "Newton-Schulz combine launch");
+                g->kernels_in_scope += 1;
+            }
+        }
+        return OPT_OK;
+    }
     const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
     // bf16 rotations from the second step on (the first, with v = 0, in fp32)
     if ((g->hp.flags & OPT_FLAG_BF16_ROTATION) && g->t > 1) {
@@ -1397,6 +1495,7 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
 opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* stream) {
     opt_status st = check_group(g);
     if (st || (st = set_device(g))) return st;
+    if (g->hp.flags & OPT_FLAG_MUON) return fail(OPT_EUNSUPPORTED, "no bases with OPT_FLAG_MUON");
     if (power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
@@ -1410,6 +1509,7 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
 opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
     opt_status st = check_group(g);
     if (st || (st = set_device(g))) return st;
+    if (g->hp.flags & OPT_FLAG_MUON) return fail(OPT_EUNSUPPORTED, "no bases with OPT_FLAG_MUON");
     if (!out) return fail(OPT_EINVAL, "out is NULL");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before health");
@@ -1448,6 +1548,7 @@ opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
 opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream) {
     opt_status st = check_group(g);
     if (st || (st = set_device(g))) return st;
+    if (g->hp.flags & OPT_FLAG_MUON) return fail(OPT_EUNSUPPORTED, "no bases with OPT_FLAG_MUON");
     if (iters < 0) return fail(OPT_EINVAL, "iters must be >= 0");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");

@@ -47,41 +47,60 @@ constexpr int XCD = 8;
 constexpr int XCD_RUN = 16;
 constexpr int GROUP_M = 4;
 
-template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N>
+// SLAB_K: k values per LDS slab (rows of 2 SLAB_K bytes); STAGES: LDS
+// buffers in the fill ring (2: fill slab k+1 during slab k; 4: slab k+3).
+template <int WAVES_M, int WAVES_N, int BLK_M, int BLK_N, int SLAB_K = 64, int STAGES = 2>
 struct Cfg16 {
     static constexpr int WM = WAVES_M, WN = WAVES_N, TM = BLK_M, TN = BLK_N;
-    static constexpr int BK = 64;          // k values per LDS slab: rows of 128 bytes
+    static constexpr int BK = SLAB_K, ST = STAGES;
+    static constexpr int RB = 2 * BK;      // bytes per LDS row
+    static constexpr int CH = BK / 8;      // 16-byte groups per row
     static constexpr int NS = BK / 16;     // MFMA k steps per slab
     static constexpr int NT = 64 * WM * WN, NW = NT / 64;
     static constexpr int BM = 32 * TM * WM, BN = 32 * TN * WN;
-    static constexpr int AB = BM * BK * 2, BB = BN * BK * 2;   // bytes of one A / B buffer
-    static constexpr int SMEM = 2 * (AB + BB);
+    static constexpr int AB = BM * RB, BB = BN * RB;   // bytes of one A / B buffer
+    static constexpr int SMEM = ST * (AB + BB);
+    static constexpr int DMA_PER_SLAB = (AB + BB) / 1024 / NW;   // fill instructions per wavefront
+    static_assert(BK == 32 || BK == 64, "slabs of 32 or 64 k values");
+    static_assert(ST == 2 || ST == 4, "two or four LDS stages");
     static_assert((AB / 1024) % NW == 0 && (BB / 1024) % NW == 0, "tile not divisible into LDS chunks");
-    static_assert(NS % 2 == 0, "the last k step's fragments are in slot 1");
+    static_assert(ST == 4 || NS % 2 == 0, "the last k step's fragments are in slot 1");
 };
+#ifndef MATOPT_GEMM16_LARGE
+#define MATOPT_GEMM16_LARGE 2, 2, 4, 4, 32, 4
+#endif
 using Small16 = Cfg16<2, 2, 2, 2>;
-using Large16 = Cfg16<2, 2, 4, 4>;
+using Large16 = Cfg16<MATOPT_GEMM16_LARGE>;
 static_assert(Small16::BM == kGemm16Cfgs[0].bm && Small16::BN == kGemm16Cfgs[0].bn, "tile size mismatch");
 static_assert(Large16::BM == kGemm16Cfgs[1].bm && Large16::BN == kGemm16Cfgs[1].bn, "tile size mismatch");
 
-__device__ __forceinline__ int swz16(int r) { return (r ^ (r >> 3)) & 7; }
+// Slot of 16-byte group q of LDS row r: q ^ swz16<BK>(r). With 8 groups per
+// row (r ^ r/8) mod 8, with 4 groups ((r/2) ^ (r/4)) mod 4: the 16 lanes of a
+// read phase (rows r..r+15 of one group) hit distinct bank groups for both
+// 32- and 64-bank LDS.
+template <int BK>
+__device__ __forceinline__ int swz16(int r) {
+    if constexpr (BK == 64) return (r ^ (r >> 3)) & 7;
+    else return ((r >> 1) ^ (r >> 2)) & 3;
+}
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(1))) const void* gsrc_ptr;
 
-// One slab (R rows x 64 k) of an operand into LDS buffer `buf`: rows r0.. of
+// One slab (R rows x BK k) of an operand into LDS buffer `buf`: rows r0.. of
 // a row-major bf16 matrix with `rows` rows, k0.. of its K columns.
 template <class C, int R>
 __device__ __forceinline__ void dma16(char* buf, const uint16_t* base, int64_t ld, int rows, int K, int r0,
                                       int k0) {
-    constexpr int CPW = R / 8 / C::NW;   // 1 KiB chunks (8 rows) per wavefront
+    constexpr int RPC = 1024 / C::RB;    // rows per 1 KiB chunk
+    constexpr int CPW = R / RPC / C::NW; // chunks per wavefront
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
     for (int t = 0; t < CPW; ++t) {
         const int c = wave * CPW + t;
-        const int r = 8 * c + (lane >> 3);
-        const int k = k0 + 8 * ((lane & 7) ^ swz16(r));
+        const int r = RPC * c + lane / C::CH;
+        const int k = k0 + 8 * ((lane % C::CH) ^ swz16<C::BK>(r));
         const int grow = r0 + r;
         const void* src = (grow < rows && k < K) ? (const void*)(base + (int64_t)grow * ld + k)
                                                   : (const void*)g_gemm16_zero;
@@ -98,12 +117,12 @@ __device__ __forceinline__ void frags16(const char* As, const char* Bs, int s, i
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
         const int row = wm * 32 * C::TM + i * 32 + l32;
-        a[i] = *(const bf16x8*)(As + row * 128 + ((q ^ swz16(row)) << 4));
+        a[i] = *(const bf16x8*)(As + row * C::RB + ((q ^ swz16<C::BK>(row)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) {
         const int col = wn * 32 * C::TN + j * 32 + l32;
-        b[j] = *(const bf16x8*)(Bs + col * 128 + ((q ^ swz16(col)) << 4));
+        b[j] = *(const bf16x8*)(Bs + col * C::RB + ((q ^ swz16<C::BK>(col)) << 4));
     }
 }
 
@@ -205,15 +224,43 @@ __device__ __forceinline__ void epi16(const Gemm16Prob& p, int m0, int n0, int w
     }
 }
 
+// s_waitcnt immediate (gfx9 layout) that waits until at most `vm` vector
+// memory operations of this wavefront are outstanding (and, with lgkm0, all
+// LDS reads have returned); the other counters are left alone.
+constexpr int waitcnt_imm(int vm, bool lgkm0) {
+    return (vm & 15) | (7 << 4) | ((lgkm0 ? 0 : 15) << 8) | ((vm >> 4) << 14);
+}
+
+// Slab barrier. With two stages the next slab's fill is the only one in
+// flight and __syncthreads (which drains every counter) is exact. With a
+// ring of ST stages each wavefront waits only until the fill of the next
+// slab has landed, leaving the ST - 2 newer fills in flight (fills complete
+// in issue order), and until its own LDS reads of the slab being released
+// have returned; the barrier then makes every wavefront's part visible. The
+// empty asm statements keep the compiler from moving memory accesses across.
+template <class C>
+__device__ __forceinline__ void slab_barrier() {
+    if constexpr (C::ST == 2) {
+        __syncthreads();
+    } else {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm((C::ST - 2) * C::DMA_PER_SLAB, true));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    }
+}
+
 template <class C, bool OUT16>
 __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, float alpha_scale, char* smem) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % C::WM, wn = wave / C::WM;
     const int m0 = tm * C::BM, n0 = tn * C::BN;
-    // buffer b of A at smem + b AB, of B at smem + 2 AB + b BB
+    // ring buffer b of A at smem + b AB, of B at smem + ST AB + b BB
+    auto abuf = [&](int b) { return smem + b * C::AB; };
+    auto bbuf = [&](int b) { return smem + C::ST * C::AB + b * C::BB; };
     auto fill = [&](int b, int k0) {
-        dma16<C, C::BM>(smem + b * C::AB, p.A, p.lda, p.M, p.K, m0, k0);
-        dma16<C, C::BN>(smem + 2 * C::AB + b * C::BB, p.B, p.ldb, p.N, p.K, n0, k0);
+        dma16<C, C::BM>(abuf(b), p.A, p.lda, p.M, p.K, m0, k0);
+        dma16<C, C::BN>(bbuf(b), p.B, p.ldb, p.N, p.K, n0, k0);
     };
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -228,16 +275,20 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);
         return;
     }
-    fill(0, 0);
-    __syncthreads();
+    // slabs 0 .. ST-2 in flight; slab 0 landed before the first reads
+#pragma unroll
+    for (int st = 0; st < C::ST - 1; ++st) fill(st, st * C::BK);
+    slab_barrier<C>();
     bf16x8 fa[2][C::TM], fb[2][C::TN];
-    frags16<C>(smem, smem + 2 * C::AB, 0, wm, wn, lane, fa[0], fb[0]);
+    frags16<C>(abuf(0), bbuf(0), 0, wm, wn, lane, fa[0], fb[0]);
+    int cur = 0;
     for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const char* As = smem + cur * C::AB;
-        const char* Bs = smem + 2 * C::AB + cur * C::BB;
-        // past the last slab the fill reads only the zero block into the idle buffer
-        fill(cur ^ 1, (kt + 1) * C::BK);
+        const int nxt = cur + 1 == C::ST ? 0 : cur + 1;
+        const int fb_ = cur == 0 ? C::ST - 1 : cur - 1;   // buffer of slab kt + ST - 1
+        const char* As = abuf(cur);
+        const char* Bs = bbuf(cur);
+        // past the last slab the fill reads only the zero block into an idle buffer
+        fill(fb_, (kt + C::ST - 1) * C::BK);
 #pragma unroll
         for (int s = 0; s < C::NS - 1; ++s) {
             mma16<C, 0, 1>(fa[s & 1], fb[s & 1], acc);
@@ -247,13 +298,14 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
             mma16<C, 1, C::TM>(fa[s & 1], fb[s & 1], acc);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
+        slab_barrier<C>();
         mma16<C, 0, 1>(fa[1], fb[1], acc);
         __builtin_amdgcn_sched_barrier(0);
-        frags16<C>(smem + (cur ^ 1) * C::AB, smem + 2 * C::AB + (cur ^ 1) * C::BB, 0, wm, wn, lane, fa[0], fb[0]);
+        frags16<C>(abuf(nxt), bbuf(nxt), 0, wm, wn, lane, fa[0], fb[0]);
         __builtin_amdgcn_sched_barrier(0);
         mma16<C, 1, C::TM>(fa[1], fb[1], acc);
         __builtin_amdgcn_sched_barrier(0);
+        cur = nxt;
     }
     epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);
 }

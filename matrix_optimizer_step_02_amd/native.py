@@ -18,8 +18,9 @@ OPT_OK, OPT_EINVAL, OPT_ENOWS, OPT_EHIP, OPT_EUNSUPPORTED, OPT_ESTATE = 0, -1, -
 OPT_F32, OPT_BF16 = 0, 1
 OPT_FLAG_ROTATED_MOMENTUM = 1
 OPT_FLAG_BF16_ROTATION = 2
+OPT_FLAG_MUON = 4
 OPT_MAX_DIM = 16384
-PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right")
+PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho")
 OPT_NUM_PHASES = len(PHASES)
 
 EXPORTED = (
@@ -50,6 +51,7 @@ class opt_hparams(C.Structure):
         ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float), ("lr", C.c_float),
         ("K", C.c_int32), ("power_iters", C.c_int32),
         ("capacity_bytes", C.c_uint64), ("refresh_capacity_bytes", C.c_uint64), ("flags", C.c_uint32),
+        ("ns_iters", C.c_int32),
     ]
 
 

@@ -29,6 +29,9 @@ each gate bounds the error that phase can add:
 * Gate B16 (the bf16-rotation variant, gate_apply_bf16): as gate B against
   oracle/bf16_rotation.py, with each bf16 intermediate allowed one bf16 ulp
   (a rounding flip) and the errors propagated root-sum-square at 6 sigma.
+* Gate MU (the orthogonalised-momentum step, gate_muon): W within
+  lr 1e-4 max|O| plus one binary32 rounding of the oracle's Newton-Schulz
+  result from the device's M_t.
 * Gate B (rotate, moments, apply): oracle from the device's W_{t-1},
   v_{t-1}, M_t, U_t, V_t and the same G. v: max relative error <= 1e-4.
   W elementwise: |W - W_ref| <= tau max|W_ref| + 6 lr sqrt((U.U) E^2 (V.V)^T)
@@ -242,6 +245,23 @@ def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.H
             GateReport("B16.W", bool(np.all(err_w <= bound_w)),
                        {"dW_maxrel": float(np.max(err_w) / lr / max(np.max(np.abs(it["dW"])), 1e-300)),
                         "worst_ratio": float(np.max(err_w / bound_w))})]
+
+
+def gate_muon(W_prev, M_t, W_dev, hp: oracle.Hyper, iters: int, tau=1e-4) -> GateReport:
+    """The orthogonalised-momentum step (oracle/muon.py), teacher-forced from
+    the device's M_t and W_{t-1}: |W - W_ref| <= lr tau max|O_ref| +
+    2^-23 |W_ref| (tau: the fp32 tolerance, applied to the update itself; one
+    binary32 rounding of W). An fp32 emulation of the iteration stays within
+    7e-7 of max|O| after 10 iterations."""
+    from oracle import muon
+    O = muon.newton_schulz_polar(M_t, iters)
+    lr = oracle.as_f32_scalar(hp.lr)
+    W_ref = oracle.round_f32(np.asarray(W_prev, np.float64) - lr * O)
+    err = np.abs(np.asarray(W_dev, np.float64) - W_ref)
+    bound = lr * tau * np.max(np.abs(O)) + 2.0 ** -23 * np.abs(W_ref)
+    O_dev = (np.asarray(W_prev, np.float64) - np.asarray(W_dev, np.float64)) / lr
+    return GateReport("MU.W", bool(np.all(err <= bound)),
+                      {"O_maxrel": maxrel(O_dev, O), "worst_ratio": float(np.max(err / bound))})
 
 
 def gate_apply_rotated_momentum(W_prev, v_prev, Mt_prev, M_t, G, U_t, V_t, W_dev, v_dev, Mt_dev,

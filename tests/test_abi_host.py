@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(N):
 
 
 def hp(N, **kw):
-    base = dict(beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-3, K=10, power_iters=1, capacity_bytes=0, refresh_capacity_bytes=0, flags=0)
+    base = dict(beta1=0.9, beta2=0.999, eps=1e-8, lr=1e-3, K=10, power_iters=1, capacity_bytes=0, refresh_capacity_bytes=0, flags=0,
+                ns_iters=0)
     base.update(kw)
     return N.opt_hparams(**base)
 
@@ -123,6 +124,21 @@ def test_flag_combinations(N):
     N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
     both = N.OPT_FLAG_BF16_ROTATION | N.OPT_FLAG_ROTATED_MOMENTUM
     assert err(N, N.opt_group_workspace_size, d, hp(N, flags=both)) == N.OPT_EUNSUPPORTED
+
+
+def test_muon_flag_checks(N):
+    d = descs(N, [(8, 8)])
+    N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_MUON, ns_iters=2))
+    assert err(N, N.opt_group_workspace_size, d, hp(N, flags=N.OPT_FLAG_MUON)) == N.OPT_EINVAL    # ns_iters 0
+    for other in (N.OPT_FLAG_BF16_ROTATION, N.OPT_FLAG_ROTATED_MOMENTUM):
+        assert err(N, N.opt_group_workspace_size, d, hp(N, flags=N.OPT_FLAG_MUON | other, ns_iters=2)) == \
+            N.OPT_EUNSUPPORTED
+    # v, U, V may be NULL with the flag, not without it
+    d = descs(N, [(8, 8)], ptrs=True)
+    d[0].v = d[0].U = d[0].V = 0
+    need = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_MUON, ns_iters=2))
+    assert err(N, N.opt_group_create, d, hp(N), 1 << 44, 1 << 30, 0) == N.OPT_EINVAL
+    assert need < 1 << 20
 
 
 def test_bf16_rotation_workspace_holds_the_bf16_bases(N):

@@ -130,3 +130,27 @@ def test_bf16_apply_gate_accepts_emulation_and_rejects_errors():
         Wc = Wd.copy()
         Wc[3, 5] -= 0.2 * np.float32(hp.lr) * np.max(np.abs(Wd - W)) / np.float32(hp.lr)
         assert not contract.gate_apply_bf16(W, v, M, G, U, V, Wc, vd, hp)[1].ok
+
+
+def _emulate_muon(W, M, k, lr, transpose_gram=False):
+    X = torch.from_numpy(np.asarray(M, np.float64)).float()
+    X = X * (1.0 / torch.sqrt((X.double() ** 2).sum())).float()
+    m, n = X.shape
+    for _ in range(k):
+        wide = (m < n) != transpose_gram
+        P = (X @ X.T) @ X if wide else X @ (X.T @ X)
+        X = 1.5 * X - 0.5 * P
+    return (torch.from_numpy(np.asarray(W, np.float64)).float() - np.float32(lr) * X).double().numpy()
+
+
+def test_muon_gate_accepts_emulation_and_rejects_errors():
+    hp = oracle.Hyper()
+    r = rng(20)
+    for (m, n) in [(48, 80), (80, 48)]:
+        W = oracle.round_f32(r.standard_normal((m, n)) * 1e-2)
+        M = oracle.round_bf16(r.standard_normal((m, n)) * 1e-3)
+        assert contract.gate_muon(W, M, _emulate_muon(W, M, 5, hp.lr), hp, 5).ok
+        assert not contract.gate_muon(W, M, _emulate_muon(W, M, 4, hp.lr), hp, 5).ok          # one step short
+        assert not contract.gate_muon(W, M, _emulate_muon(W, M, 5, 1.01 * hp.lr), hp, 5).ok   # lr off by 1 %
+        # the Gram matrix of the wrong side is the same iteration: must pass too
+        assert contract.gate_muon(W, M, _emulate_muon(W, M, 5, hp.lr, transpose_gram=True), hp, 5).ok
