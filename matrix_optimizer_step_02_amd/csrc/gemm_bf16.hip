@@ -67,7 +67,7 @@ struct Cfg16 {
     static_assert(ST == 4 || NS % 2 == 0, "the last k step's fragments are in slot 1");
 };
 #ifndef MATOPT_GEMM16_LARGE
-#define MATOPT_GEMM16_LARGE 2, 2, 4, 4, 32, 4
+#define MATOPT_GEMM16_LARGE 2, 2, 4, 4, 64, 2
 #endif
 using Small16 = Cfg16<2, 2, 2, 2>;
 using Large16 = Cfg16<MATOPT_GEMM16_LARGE>;
