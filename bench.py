@@ -339,8 +339,8 @@ def main(argv=None):
             "flops_per_launch": flops / max(launches, 1),
         }
         eb = elementwise_bytes(shapes, wl.m_dtype)
-        extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items()}
-        extra["phase_launches"] = {k: v[1] for k, v in phases.items()}
+        extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
+        extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
         extra["phase_tflops"] = {k: (pf[k] * args.steps / (phases[k][0] * 1e-3) / 1e12 if phases[k][0] else None)
                                  for k in pf}
         extra["elementwise_gbps"] = {k: (eb[k] * args.steps / (phases[k][0] * 1e-3) / 1e9 if phases[k][0] else None)

@@ -43,9 +43,15 @@ __device__ __attribute__((aligned(64))) uint32_t g_gemm16_zero[16];
 
 namespace {
 
+#ifndef MATOPT_GEMM16_XCD_RUN
+#define MATOPT_GEMM16_XCD_RUN 16
+#endif
+#ifndef MATOPT_GEMM16_GROUP_M
+#define MATOPT_GEMM16_GROUP_M 4
+#endif
 constexpr int XCD = 8;
-constexpr int XCD_RUN = 16;
-constexpr int GROUP_M = 4;
+constexpr int XCD_RUN = MATOPT_GEMM16_XCD_RUN;
+constexpr int GROUP_M = MATOPT_GEMM16_GROUP_M;
 
 // SLAB_K: k values per LDS slab (rows of 2 SLAB_K bytes); STAGES: LDS
 // buffers in the fill ring (2: fill slab k+1 during slab k; 4: slab k+3).

@@ -161,6 +161,37 @@ def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True, ref32=None) -
                                  "backward": back})
 
 
+def gate_basis_sampled(X_dev, M_t, X_prev, side, passes, name, nsample=256, seed=0) -> GateReport:
+    """gate_basis without the forward comparison, on sampled rows and columns,
+    for orders where the full d^3 products take minutes on the host: rows S of
+    X^T X - I within 1e-5 of zero, and below the diagonal in columns C of
+    X^T Z_hat (column-normalised) within 1e-3 of their norm. C holds the
+    leading r + 8 columns (where the one-shot input is not the previous basis)
+    and a random sample. The one-shot input is formed from M without building
+    the d x d Gram matrix."""
+    X_dev = np.asarray(X_dev, np.float64)
+    X_prev = np.asarray(X_prev, np.float64)
+    M_t = np.asarray(M_t, np.float64)
+    d = X_dev.shape[0]
+    r = min(M_t.shape)
+    rng = np.random.default_rng(seed)
+    pick = lambda extra: np.unique(np.concatenate([extra, rng.choice(d, min(nsample, d), replace=False)]))
+    S = pick(np.concatenate([np.arange(min(8, d)), np.arange(max(d - 8, 0), d)]))
+    orth = float(np.max(np.abs(X_dev[:, S].T @ X_dev - np.eye(d)[S])))
+    Cols = pick(np.arange(min(r + 8, d)))
+    Y = X_prev[:, :r]
+    for _ in range(passes):
+        Y = M_t @ (M_t.T @ Y) if side == "U" else M_t.T @ (M_t @ Y)
+    Zc = np.where(Cols[None, :] < r, Y[:, np.minimum(Cols, r - 1)], X_prev[:, Cols])
+    norms = np.linalg.norm(Zc, axis=0)
+    norms[norms == 0] = 1.0
+    Cd = X_dev.T @ (Zc / norms)
+    low = np.arange(d)[:, None] > Cols[None, :]
+    back = float(np.linalg.norm(Cd[low]) / max(np.linalg.norm(Cd), 1e-300))
+    return GateReport(name, orth <= 1e-5 and back <= 1e-3, {"orth_sampled": orth, "backward_sampled": back,
+                                                           "rows": float(len(S)), "cols": float(len(Cols))})
+
+
 def gate_refresh(M_t, U_prev, V_prev, U_dev, V_dev, passes, forward_max_d=1100) -> List[GateReport]:
     M_t = np.asarray(M_t, np.float64)
     m, n = M_t.shape

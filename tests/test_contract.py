@@ -154,3 +154,19 @@ def test_muon_gate_accepts_emulation_and_rejects_errors():
         assert not contract.gate_muon(W, M, _emulate_muon(W, M, 5, 1.01 * hp.lr), hp, 5).ok   # lr off by 1 %
         # the Gram matrix of the wrong side is the same iteration: must pass too
         assert contract.gate_muon(W, M, _emulate_muon(W, M, 5, hp.lr, transpose_gram=True), hp, 5).ok
+
+
+def test_sampled_basis_gate_accepts_lapack_and_rejects_swaps():
+    r = rng(30)
+    M = r.standard_normal((200, 12)) * 1e-2
+    X0 = np.eye(200)
+    Z = contract.one_shot_input(M @ M.T, X0, 12, 1)
+    q, rr = np.linalg.qr(Z.astype(np.float32))
+    q = (q * np.where(np.diag(rr) < 0, -1, 1)).astype(np.float64)
+    assert contract.gate_basis_sampled(q, M, X0, "U", 1, "U", nsample=64).ok
+    bad = q.copy()
+    bad[:, [3, 150]] = bad[:, [150, 3]]                       # a completion column moved into the leading block
+    assert not contract.gate_basis_sampled(bad, M, X0, "U", 1, "U", nsample=64).ok
+    skew = q.copy()
+    skew[:, 5] += 1e-3 * skew[:, 6]                           # not orthonormal
+    assert not contract.gate_basis_sampled(skew, M, X0, "U", 1, "U", nsample=64).ok
