@@ -46,7 +46,8 @@ import numpy as np
 from .rotated_adam import (Hyper, OracleState, as_f32_scalar, momentum_update, refresh_bases,
                            refresh_due, rotated_adam_apply, round_bf16, round_f32)
 
-__all__ = ["bf16_rotation_apply", "step_bf16_rotation"]
+__all__ = ["bf16_rotation_apply", "step_bf16_rotation", "bf16_rotated_momentum_apply",
+           "step_bf16_rotated_momentum"]
 
 
 def bf16_rotation_apply(W, v, M, G, U, V, beta2: float, eps: float, lr: float):
@@ -90,3 +91,59 @@ def step_bf16_rotation(state: OracleState, G, hp: Hyper) -> OracleState:
     state.W, state.v, inter = apply(state.W, state.v, state.M, G, state.U, state.V, hp.beta2, hp.eps, hp.lr)
     state.last = dict(inter, refreshed=refreshed, bf16=state.t != 1)
     return state
+
+
+def bf16_rotated_momentum_apply(W, v, mt_prev, M, G, U, V, beta1: float, beta2: float, eps: float, lr: float,
+                                recompute: bool):
+    """Both variants together: the rotations on bf16 operands as in
+    bf16_rotation_apply, and m~ carried in binary32 within a basis epoch as
+    in oracle/rotated_momentum.py. recompute: m~ = rf(Ub^T rb(rb(M) Vb));
+    otherwise m~ = rf(b1 m~_prev + (1 - b1) G~), with G~ = Ub^T rb(rb(G) Vb).
+    Returns (W_new, v_new, mt_new, intermediates)."""
+    b1 = as_f32_scalar(beta1)
+    b2 = as_f32_scalar(beta2)
+    eps = as_f32_scalar(eps)
+    lr = as_f32_scalar(lr)
+    Ub = round_bf16(U)
+    Vb = round_bf16(V)
+    SG = round_bf16(round_bf16(G) @ Vb)
+    Gt = Ub.T @ SG
+    if recompute:
+        SM = round_bf16(round_bf16(M) @ Vb)
+        mt = round_f32(Ub.T @ SM)
+    else:
+        SM = None
+        mt = round_f32(b1 * np.asarray(mt_prev, np.float64) + (1.0 - b1) * Gt)
+    v_new = round_f32(b2 * np.asarray(v, np.float64) + (1.0 - b2) * (Gt * Gt))
+    u = mt / (np.sqrt(v_new) + eps)
+    ub = round_bf16(u)
+    P = round_bf16(ub @ Vb.T)
+    dW = Ub @ P
+    W_new = round_f32(np.asarray(W, np.float64) - lr * dW)
+    return W_new, v_new, mt, {"Ub": Ub, "Vb": Vb, "SG": SG, "SM": SM, "Gt": Gt, "mt": mt, "u": u, "ub": ub,
+                              "P": P, "dW": dW}
+
+
+def step_bf16_rotated_momentum(state: OracleState, mt, G, hp: Hyper, mt_valid: bool):
+    """One step of the two variants together on one matrix. The first step
+    (t = 1) is the fp32 rotated-momentum step (recomputing m~); later steps
+    use bf16_rotated_momentum_apply, recomputing m~ at refreshes and whenever
+    it is not valid. Returns the new m~; ``state`` is updated in place."""
+    from .rotated_momentum import rotated_momentum_apply
+    G = round_f32(G)
+    state.t += 1
+    state.M = momentum_update(state.M, G, hp.beta1, state.m_dtype)
+    refreshed = refresh_due(state.t, hp.K)
+    if refreshed:
+        state.U, state.V = refresh_bases(state.M, state.U, state.V, hp.power_iters)
+    recompute = refreshed or not mt_valid
+    if state.t == 1:
+        state.W, state.v, mt_new, inter = rotated_momentum_apply(state.W, state.v, mt, state.M, G, state.U,
+                                                                 state.V, hp.beta1, hp.beta2, hp.eps, hp.lr,
+                                                                 recompute=True)
+    else:
+        state.W, state.v, mt_new, inter = bf16_rotated_momentum_apply(state.W, state.v, mt, state.M, G, state.U,
+                                                                      state.V, hp.beta1, hp.beta2, hp.eps, hp.lr,
+                                                                      recompute)
+    state.last = dict(inter, refreshed=refreshed, bf16=state.t != 1, recompute=recompute)
+    return mt_new

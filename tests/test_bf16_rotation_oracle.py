@@ -135,3 +135,73 @@ def test_first_step_in_bf16_would_be_dominated_by_roundoff():
     _, _, im = oracle.rotated_adam_apply(z, z, M, G, U, V, HP.beta2, HP.eps, HP.lr)
     _, _, ib = B.bf16_rotation_apply(z, z, M, G, U, V, HP.beta2, HP.eps, HP.lr)
     assert np.linalg.norm(ib["dW"]) > 1.5 * np.linalg.norm(im["dW"])
+
+
+# ---- both variants together: bf16 rotations and the carried m~ -------------
+
+@pytest.mark.parametrize("recompute", [True, False])
+def test_combined_signed_permutation_bases_are_the_carried_method_with_rounded_u(recompute):
+    """With signed-permutation bases and bf16-exact G and M every rounding
+    except u's is exact, so the combination equals the fp32 carried-momentum
+    oracle with u rounded: m~ and v bitwise, W with rb(u)."""
+    from oracle import rotated_momentum as RM
+    m, n = 7, 10
+    rng = np.random.default_rng(11)
+    U, V = signed_permutation(m, rng), signed_permutation(n, rng)
+    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(rng.random((m, n)) * 1e-5)
+    mt0 = oracle.round_f32(rng.standard_normal((m, n)) * 1e-3)
+    Wr, vr, mtr, ir = RM.rotated_momentum_apply(W, v, mt0, M, G, U, V, HP.beta1, HP.beta2, HP.eps, HP.lr, recompute)
+    Wb, vb, mtb, ib = B.bf16_rotated_momentum_apply(W, v, mt0, M, G, U, V, HP.beta1, HP.beta2, HP.eps, HP.lr,
+                                                    recompute)
+    assert np.array_equal(mtb, mtr) and np.array_equal(vb, vr)
+    lr = oracle.as_f32_scalar(HP.lr)
+    assert np.array_equal(Wb, oracle.round_f32(W - lr * (U @ oracle.round_bf16(ir["u"]) @ V.T)))
+
+
+def test_combined_recompute_is_the_bf16_variant():
+    """A recomputing step of the combination is the bf16 variant's step with
+    m~ rounded to binary32 (where the device stores it)."""
+    m, n = 12, 20
+    rng = np.random.default_rng(12)
+    U = rand_q(m, rng)
+    V = rand_q(n, rng)
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(rng.random((m, n)) * 1e-5)
+    _, vb, ib = B.bf16_rotation_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    _, vc, mtc, ic = B.bf16_rotated_momentum_apply(W, v, None, M, G, U, V, HP.beta1, HP.beta2, HP.eps, HP.lr, True)
+    assert np.array_equal(vb, vc) and np.array_equal(mtc, oracle.round_f32(ib["mt"]))
+
+
+def test_combined_trajectory_stays_near_the_method():
+    """Seven steps, refresh every three: within 10 % of the method's
+    accumulated update; the first step is bitwise the fp32 carried-momentum
+    step, then bf16 steps carry m~ between refreshes."""
+    from oracle import rotated_momentum as RM
+    rng = np.random.default_rng(13)
+    m, n = 24, 40
+    W0 = rng.standard_normal((m, n)) * 1e-2
+    a = oracle.OracleState.fresh(W0, "bf16")
+    b = oracle.OracleState.fresh(W0, "bf16")
+    c = oracle.OracleState.fresh(W0, "bf16")
+    mt, valid, recs = None, False, []
+    for t in range(1, 8):
+        G = rng.standard_normal((m, n)) * 1e-2
+        oracle.step(a, G, HP)
+        mt = B.step_bf16_rotated_momentum(b, mt, G, HP, valid)
+        valid = True
+        recs.append(b.last["recompute"])
+        if t == 1:
+            RM.step_rotated_momentum(c, None, G, HP, False)
+            assert np.array_equal(c.W, b.W) and np.array_equal(c.v, b.v)
+    assert recs == [True, False, False, True, False, False, True]
+    assert np.linalg.norm((b.W - W0) - (a.W - W0)) / np.linalg.norm(a.W - W0) <= 0.1
+
+
+def rand_q(d, rng):
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))
