@@ -347,6 +347,9 @@ def main(argv=None):
                                      for k in eb}
         if refresh_steps:
             extra["refresh_ms_each"] = phases["refresh"][0] / len(refresh_steps)
+            # algorithmic flops of one refresh: p (8 m n r + (8/3)(m^3 + n^3)) per matrix
+            rf = sum(wl.power_iters * (8.0 * m * n * min(m, n) + (8.0 / 3.0) * (m ** 3 + n ** 3)) for m, n in shapes)
+            extra["refresh_tflops"] = rf / (extra["refresh_ms_each"] * 1e-3) / 1e12
 
     cpu = None
     if args.cpu_sample_s > 0:

@@ -114,8 +114,9 @@ enum {
      * rotation back u V^T; G~, m~, v and W stay fp32. The first step of a
      * group (t = 1, where v = 0) uses the fp32 rotations: there u divides by
      * sqrt(v) + eps and bf16 roundoff in directions where G~ vanishes would
-     * become full-size entries of u. Cannot be combined with
-     * OPT_FLAG_ROTATED_MOMENTUM (OPT_EUNSUPPORTED). The workspace grows by the
+     * become full-size entries of u. With OPT_FLAG_ROTATED_MOMENTUM as well,
+     * m~ is carried in Mt (fp32) as that flag describes and only G is rotated
+     * on the steps that carry it. The workspace grows by the
      * bf16 bases, 4 (m m8 + n n8) bytes per matrix (m8, n8: m, n rounded up
      * to a multiple of 8). */
     OPT_FLAG_BF16_ROTATION = 2u,

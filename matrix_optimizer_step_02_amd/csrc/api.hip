@@ -125,6 +125,11 @@ struct Group {
     std::vector<Gemm16Launch> r16_right, r16_left, r16_back_right, r16_back_left;
     EwLaunch mom16, adam16;
     EwLaunch mom_r, adam_r;   // ragged matrices
+    // with the carried rotated momentum as well: the step that carries m~
+    // (G alone rotated, m~ advanced in the Adam kernel) and the step that
+    // recomputes it into Mt
+    std::vector<Gemm16Launch> r16_right_c, r16_left_c, r16_left_re;
+    EwLaunch adam16_c, adam16_re, adam_r_c, adam_r_re;
     PackLaunch pack_in, pack_u;
     // orthogonalised momentum (OPT_FLAG_MUON): MuonSeg list (EwLaunch of
     // MuonSeg), the Gram and product launches of one Newton-Schulz step, and
@@ -229,8 +234,6 @@ opt_status check_hparams(const opt_hparams* hp) {
         return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON cannot be combined with other flags");
     if ((hp->flags & OPT_FLAG_MUON) && hp->ns_iters < 1)
         return fail(OPT_EINVAL, "ns_iters must be >= 1 with OPT_FLAG_MUON");
-    if ((hp->flags & OPT_FLAG_ROTATED_MOMENTUM) && (hp->flags & OPT_FLAG_BF16_ROTATION))
-        return fail(OPT_EUNSUPPORTED, "OPT_FLAG_BF16_ROTATION cannot be combined with OPT_FLAG_ROTATED_MOMENTUM");
     return OPT_OK;
 }
 
@@ -843,9 +846,9 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         }
         G.rot_bytes = off;
         if (r16) {
-            std::vector<Gemm16Prob> s_right, s_left, s_bright, s_bleft;
-            std::vector<Ew16Seg> m16, a16;
-            std::vector<EwSeg> mr, ar;
+            std::vector<Gemm16Prob> s_right, s_left, s_bright, s_bleft, s_right_c, s_left_c, s_left_re;
+            std::vector<Ew16Seg> m16, a16, a16_c, a16_re;
+            std::vector<EwSeg> mr, ar, ar_c, ar_re;
             std::vector<PackJob> pin, pu;
             uint64_t o = 0;
             for (int mi : members) {
@@ -867,6 +870,13 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 // G~ = U^T S^T: G~[i][j] = sum_k U^T[i][k] S[j][k]  (m x n fp32)
                 s_left.push_back(g16(M.Utb, m8, SG, m8, Gt, n, m, n, m8, 1.f, 0.f, n));
                 s_left.push_back(g16(M.Utb, m8, SM, m8, mt, n, m, n, m8, 1.f, 0.f, n));
+                if (x.Mt) {
+                    // carried m~: G alone on carrying steps; m~ into Mt on recomputing ones
+                    s_right_c.push_back(s_right[s_right.size() - 2]);
+                    s_left_c.push_back(s_left[s_left.size() - 2]);
+                    s_left_re.push_back(s_left[s_left.size() - 2]);
+                    s_left_re.push_back(g16(M.Utb, m8, SM, m8, x.Mt, n, m, n, m8, 1.f, 0.f, n));
+                }
                 // P = (u V^T)^T: P[j][k] = sum_l V[j][l] u[k][l]   (n x m, into SG)
                 s_bright.push_back(g16(M.Vb, n8, Gb, n8, SG, m8, n, m, n8, 1.f, 0.f, m8));
                 // W -= lr U P^T: sum_k U[i][k] P[j][k]
@@ -889,6 +899,13 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                     a.n = mn;
                     a.vec = aligned(x.v, 16);
                     a16.push_back(a);
+                    if (x.Mt) {
+                        a.b = x.Mt;
+                        a.vec = aligned(x.v, 16) && aligned(x.Mt, 16);
+                        a16_re.push_back(a);
+                        a.carry = 1;
+                        a16_c.push_back(a);
+                    }
                 } else {
                     EwSeg e{};
                     e.a = x.G;
@@ -907,6 +924,14 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                     a.vec = aligned(x.v, 16);
                     ar.push_back(a);
                     pu.push_back({mt, Gb, m, n, n, n8, 0, 0});
+                    if (x.Mt) {
+                        a.b = x.Mt;   // u to the m~ scratch (packed from there), m~ kept in Mt
+                        a.d = mt;
+                        a.vec = aligned(x.v, 16) && aligned(x.Mt, 16);
+                        ar_re.push_back(a);
+                        a.carry = 1;
+                        ar_c.push_back(a);
+                    }
                 }
             }
             G.r16_right.push_back(put_gemm16(g->img, s_right, true));
@@ -919,6 +944,15 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             G.adam_r = put_ew(g->img, ar);
             G.pack_in = put_pack(g->img, pin);
             G.pack_u = put_pack(g->img, pu);
+            if (!s_right_c.empty()) {
+                G.r16_right_c.push_back(put_gemm16(g->img, s_right_c, true));
+                G.r16_left_c.push_back(put_gemm16(g->img, s_left_c, false));
+                G.r16_left_re.push_back(put_gemm16(g->img, s_left_re, false));
+                G.adam16_c = put_ew16(g->img, a16_c);
+                G.adam16_re = put_ew16(g->img, a16_re);
+                G.adam_r_c = put_ew(g->img, ar_c);
+                G.adam_r_re = put_ew(g->img, ar_re);
+            }
             G.rot_bytes = std::max(G.rot_bytes, o);
         }
         G.rot_left = put_gemm(g->img, left);
@@ -1378,6 +1412,8 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
     // bf16 rotations from the second step on (the first, with v = 0, in fp32)
     if ((g->hp.flags & OPT_FLAG_BF16_ROTATION) && g->t > 1) {
+        const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
+        const bool carry = carry_mode && g->mt_valid && !refresh;
         // The bf16 copies of G and M live in the scratch that the refresh and
         // every micro-group share, so each group makes its own right before
         // its rotations: with the momentum update on steps without a refresh,
@@ -1419,22 +1455,26 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             }
             {
                 PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
-                if ((e = run_gemm16(g, G.r16_right, 1.f, s))) return hip_fail(e, "rotation launch");
+                if ((e = run_gemm16(g, carry ? G.r16_right_c : G.r16_right, 1.f, s)))
+                    return hip_fail(e, "rotation launch");
             }
             {
                 PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
-                if ((e = run_gemm16(g, G.r16_left, 1.f, s))) return hip_fail(e, "rotation launch");
+                const std::vector<Gemm16Launch>& L = !carry_mode ? G.r16_left : (carry ? G.r16_left_c : G.r16_left_re);
+                if ((e = run_gemm16(g, L, 1.f, s))) return hip_fail(e, "rotation launch");
             }
             {
                 PhaseScope ps(g, OPT_PHASE_ADAM, s);
-                e = launch_adam16(dptr<Ew16Seg>(g, G.adam16.segs), G.adam16.nseg, G.adam16.chunks, g->hp.beta2,
+                const EwLaunch& A16 = !carry_mode ? G.adam16 : (carry ? G.adam16_c : G.adam16_re);
+                const EwLaunch& AR = !carry_mode ? G.adam_r : (carry ? G.adam_r_c : G.adam_r_re);
+                e = launch_adam16(dptr<Ew16Seg>(g, A16.segs), A16.nseg, A16.chunks, g->hp.beta1, g->hp.beta2,
                                   g->hp.eps, s);
                 if (!e)
-                    e = launch_rotated_adam(dptr<EwSeg>(g, G.adam_r.segs), G.adam_r.nseg, G.adam_r.chunks,
-                                            g->hp.beta1, g->hp.beta2, g->hp.eps, s);
+                    e = launch_rotated_adam(dptr<EwSeg>(g, AR.segs), AR.nseg, AR.chunks, g->hp.beta1, g->hp.beta2,
+                                            g->hp.eps, s);
                 if (!e) e = run_pack(g, G.pack_u, s);
                 if (e) return hip_fail(e, "rotated Adam launch");
-                g->kernels_in_scope += (G.adam16.nseg > 0) + (G.adam_r.nseg > 0);
+                g->kernels_in_scope += (A16.nseg > 0) + (AR.nseg > 0);
             }
             {
                 PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s);
@@ -1445,6 +1485,7 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
                 if ((e = run_gemm16(g, G.r16_back_left, g->hp.lr, s))) return hip_fail(e, "update launch");
             }
         }
+        g->mt_valid = carry_mode;
         return OPT_OK;
     }
     // Momentum of every group first: a refresh must see the updated M.

@@ -272,13 +272,14 @@ __global__ __launch_bounds__(kEwThreads) void momentum16_kernel(const Ew16Seg* _
     }
 }
 
-// v <- beta2 v + (1 - beta2) G~^2; u = m~ / (sqrt(v) + eps) stored as bf16 in o1.
+// v <- beta2 v + (1 - beta2) G~^2; u = m~ / (sqrt(v) + eps) stored as bf16 in
+// o1. With carry, m~ (fp32, in b) is first advanced: b <- beta1 b + (1 - beta1) G~.
 __global__ __launch_bounds__(kEwThreads) void adam16_kernel(const Ew16Seg* __restrict__ segs, int nseg,
-                                                            float beta2, float eps) {
+                                                            float beta1, float beta2, float eps) {
     const int64_t chunk = blockIdx.x;
     const Ew16Seg S = segs[find_seg16(segs, nseg, chunk)];
     const int64_t base = (chunk - S.chunk_begin) * kEwChunk;
-    const float omb2 = 1.f - beta2;
+    const float omb1 = 1.f - beta1, omb2 = 1.f - beta2;
     if (S.vec && base + kEwChunk <= S.n) {
         f32x4 g[NQ], m[NQ], v[NQ];
 #pragma unroll
@@ -294,24 +295,31 @@ __global__ __launch_bounds__(kEwThreads) void adam16_kernel(const Ew16Seg* __res
             f32x4 u;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                if (S.carry) m[q][e] = ema(beta1, m[q][e], omb1, g[q][e]);
                 float ve = v[q][e], ue;
                 adam1(g[q][e], m[q][e], ve, ue, beta2, omb2, eps);
                 v[q][e] = ve;
                 u[e] = ue;
             }
             *gptr((f32x4*)(S.c + o)) = v[q];
+            if (S.carry) *gptr((f32x4*)((float*)S.b + o)) = m[q];
             *gptr((u32x2*)(S.o1 + o)) = pack_bf16x4(u);
         }
         return;
     }
     gmem<const float> Gt = gptr(S.a);
-    gmem<const float> mb = gptr((const float*)S.b);
+    gmem<float> mb = gptr((float*)S.b);
     gmem<float> V = gptr(S.c);
     for (int q = 0; q < NQ; ++q) {
         const int64_t i = base + 4 * ((int64_t)q * kEwThreads + threadIdx.x);
         for (int e = 0; e < 4 && i + e < S.n; ++e) {
+            float m = mb[i + e];
+            if (S.carry) {
+                m = ema(beta1, m, omb1, Gt[i + e]);
+                mb[i + e] = m;
+            }
             float v = V[i + e], u;
-            adam1(Gt[i + e], mb[i + e], v, u, beta2, omb2, eps);
+            adam1(Gt[i + e], m, v, u, beta2, omb2, eps);
             V[i + e] = v;
             gptr(S.o1)[i + e] = f32_to_bf16(u);
         }
@@ -388,11 +396,11 @@ hipError_t launch_convert16(const Ew16Seg* segs, int nseg, int64_t total_chunks,
     return hipGetLastError();
 }
 
-hipError_t launch_adam16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta2, float eps,
+hipError_t launch_adam16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta1, float beta2, float eps,
                          hipStream_t s) {
     if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
-    hipLaunchKernelGGL(adam16_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, segs, nseg, beta2,
-                       eps);
+    hipLaunchKernelGGL(adam16_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, segs, nseg, beta1,
+                       beta2, eps);
     return hipGetLastError();
 }
 

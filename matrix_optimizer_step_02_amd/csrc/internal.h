@@ -97,7 +97,10 @@ hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks
 // ------------------------------------------------------------------ QR ----
 
 constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY block)
-constexpr int kQrPanelsPerBlock = 4;
+#ifndef MATOPT_QR_PANELS_PER_BLOCK
+#define MATOPT_QR_PANELS_PER_BLOCK 4
+#endif
+constexpr int kQrPanelsPerBlock = MATOPT_QR_PANELS_PER_BLOCK;
 constexpr int kQrNB = kQrPB * kQrPanelsPerBlock;   // outer block width
 constexpr int kQrMaxSplits = 16;   // row splits of the in-block reflector-transpose products
 constexpr int kQrPanelThreads = 512;

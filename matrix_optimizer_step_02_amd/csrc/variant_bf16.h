@@ -42,7 +42,8 @@ hipError_t launch_gemm16_single(bool c_bf16, int cfg, const Gemm16Prob& prob, hi
 //  momentum: a = G, b = M (fp32 or bf16, updated); o1 = bf16 copy of G,
 //            o2 = bf16 copy of the new M (NULL when M is bf16 and the
 //            rotation reads it directly).
-//  Adam:     a = G~, b = m~, c = v (updated); o1 = u rounded to bf16.
+//  Adam:     a = G~, b = m~, c = v (updated); o1 = u rounded to bf16; with
+//            carry, first b <- beta1 b + (1 - beta1) a (the carried m~, fp32).
 // The bf16 outputs are row-major with the row stride equal to the number of
 // columns, so the vector path needs n % 8 == 0; other shapes take EwSeg
 // launches and a pack to a padded layout.
@@ -56,13 +57,14 @@ struct Ew16Seg {
     int64_t chunk_begin;
     int32_t b_bf16;
     int32_t vec;
+    int32_t carry;
 };
 
 hipError_t launch_momentum16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta1, hipStream_t s);
 // The bf16 copies of G and M (as stored) alone, for a step whose refresh ran
 // between the momentum update and the rotations.
 hipError_t launch_convert16(const Ew16Seg* segs, int nseg, int64_t total_chunks, hipStream_t s);
-hipError_t launch_adam16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta2, float eps,
+hipError_t launch_adam16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta1, float beta2, float eps,
                          hipStream_t s);
 
 // Rows x cols of an fp32 or bf16 matrix (row stride ld_src) to bf16 with row

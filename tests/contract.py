@@ -236,7 +236,8 @@ def ulp_bf16(x):
     return np.ldexp(1.0, np.frexp(np.maximum(x, 2.0 ** -126))[1] - 8)
 
 
-def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, tau=1e-3) -> List[GateReport]:
+def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, tau=1e-3,
+                    Mt_prev=None, Mt_dev=None, recompute=True) -> List[GateReport]:
     """The bf16-rotation variant (oracle/bf16_rotation.py), teacher-forced
     like gate_apply. The device rounds the same quantities to bf16 but from
     binary32 accumulations, so each stored bf16 intermediate (S = rb(X Vb),
@@ -247,9 +248,21 @@ def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.H
     sum-square through the products (G~ = Ub^T S, P, dW = Ub P) and through u
     as in gate B, and bounds W element-wise by
     lr (tau max|dW_ref| + 6 e_dW) + 2^-23 |W_ref| (one binary32 rounding of W)
-    and v by (1 - b2) 2 |G~| 6 e_G~ + 2^-23 |v_ref| + 1e-6 max|v_ref|."""
+    and v by (1 - b2) 2 |G~| 6 e_G~ + 2^-23 |v_ref| + 1e-6 max|v_ref|.
+
+    With Mt_dev (the carried rotated momentum as well): the oracle is
+    bf16_rotated_momentum_apply from the device's Mt_prev; a carried m~ has
+    the error (1 - b1) e_G~ of its new term, a recomputed one that of
+    Ub^T rb(rb(M) Vb); Mt is bounded by 6 times that plus two binary32
+    roundings."""
     from oracle import bf16_rotation as B
-    W_ref, v_ref, it = B.bf16_rotation_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+    carried = Mt_dev is not None
+    if carried:
+        W_ref, v_ref, mt_ref, it = B.bf16_rotated_momentum_apply(W_prev, v_prev, Mt_prev, M_t, G, U_t, V_t,
+                                                                 hp.beta1, hp.beta2, hp.eps, hp.lr, recompute)
+    else:
+        W_ref, v_ref, it = B.bf16_rotation_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
+    b1 = oracle.as_f32_scalar(hp.beta1)
     b2 = oracle.as_f32_scalar(hp.beta2)
     eps = oracle.as_f32_scalar(hp.eps)
     lr = oracle.as_f32_scalar(hp.lr)
@@ -258,11 +271,14 @@ def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.H
     U2, V2 = Ub * Ub, Vb * Vb
     rss = lambda A2, B2: np.sqrt(A2 @ B2)
     Gb = oracle.round_bf16(G)
-    Mb = oracle.round_bf16(M_t)
     eSG = ulp_bf16(it["SG"]) + 4 * U32 * np.sqrt(n) * rss(Gb * Gb, V2)
-    eSM = ulp_bf16(it["SM"]) + 4 * U32 * np.sqrt(n) * rss(Mb * Mb, V2)
     eGt = rss(U2.T, eSG ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SG"] ** 2)
-    emt = rss(U2.T, eSM ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SM"] ** 2)
+    if carried and not recompute:
+        emt = (1 - b1) * eGt
+    else:
+        Mb = oracle.round_bf16(M_t)
+        eSM = ulp_bf16(it["SM"]) + 4 * U32 * np.sqrt(n) * rss(Mb * Mb, V2)
+        emt = rss(U2.T, eSM ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SM"] ** 2)
     u = it["u"]
     Eu = ulp_bf16(u) + (emt + np.abs(u) * np.sqrt(1 - b2) * eGt) / (np.sqrt(v_ref) + eps)
     eP = rss(Eu ** 2, V2.T) + ulp_bf16(it["P"]) + 4 * U32 * np.sqrt(n) * rss(it["ub"] ** 2, V2.T)
@@ -271,11 +287,18 @@ def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.H
     err_w = np.abs(np.asarray(W_dev, np.float64) - W_ref)
     bound_v = (1 - b2) * 2 * np.abs(it["Gt"]) * 6 * eGt + 2.0 ** -23 * np.abs(v_ref) + 1e-6 * np.max(v_ref)
     err_v = np.abs(np.asarray(v_dev, np.float64) - v_ref)
-    return [GateReport("B16.v", bool(np.all(err_v <= bound_v)), {"maxrel": maxrel(v_dev, v_ref),
+    reps = [GateReport("B16.v", bool(np.all(err_v <= bound_v)), {"maxrel": maxrel(v_dev, v_ref),
                                                                  "worst_ratio": float(np.max(err_v / bound_v))}),
             GateReport("B16.W", bool(np.all(err_w <= bound_w)),
                        {"dW_maxrel": float(np.max(err_w) / lr / max(np.max(np.abs(it["dW"])), 1e-300)),
                         "worst_ratio": float(np.max(err_w / bound_w))})]
+    if carried:
+        bound_m = 6 * emt + 2.0 ** -22 * np.abs(mt_ref) + 1e-30
+        err_m = np.abs(np.asarray(Mt_dev, np.float64) - mt_ref)
+        reps.insert(0, GateReport("C16.Mt", bool(np.all(err_m <= bound_m)),
+                                  {"maxrel": maxrel(Mt_dev, mt_ref), "worst_ratio": float(np.max(err_m / bound_m)),
+                                   "recompute": float(recompute)}))
+    return reps
 
 
 def gate_muon(W_prev, M_t, W_dev, hp: oracle.Hyper, iters: int, tau=1e-4) -> GateReport:

@@ -122,8 +122,7 @@ def test_rejects_bad_hyperparameters(N):
 def test_flag_combinations(N):
     d = descs(N, [(8, 8)])
     N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
-    both = N.OPT_FLAG_BF16_ROTATION | N.OPT_FLAG_ROTATED_MOMENTUM
-    assert err(N, N.opt_group_workspace_size, d, hp(N, flags=both)) == N.OPT_EUNSUPPORTED
+    N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION | N.OPT_FLAG_ROTATED_MOMENTUM))
 
 
 def test_muon_flag_checks(N):

@@ -93,3 +93,80 @@ def test_bf16_rotation_several_micro_groups():
     wl = workloads.Workload(wl.key, wl.index, wl.title, wl.matrices, wl.m_dtype, K=3, power_iters=1, steps=5,
                             grad_kind=wl.grad_kind, grad_std=wl.grad_std)
     _run(wl, 5, [0, 3, 6], capacity=1 << 24, min_groups=3)
+
+
+@pytest.mark.timeout(900)
+def test_bf16_rotation_qwen3_1p7b_full_size_sampled():
+    """The whole Qwen3-1.7B-shaped set in the launch configuration the bench
+    times (196 matrices, 11 micro-groups): the fp32 first step with its
+    refresh and the first bf16 step, gated on the first and last layer's q,
+    k, up and down."""
+    wl = workloads.get("qwen3_1p7b")
+    idx = [i for i, s in enumerate(wl.matrices)
+           if s.layer in (0, 27) and s.name.split(".")[1] in ("q", "k", "up", "down")]
+    _run(wl, 2, idx)
+
+
+# ---- with the carried rotated momentum as well ------------------------------
+
+def _run_combined(wl, steps, check_mats, events=None):
+    import torch
+    import matrix_optimizer_step_02_amd as mo
+    hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes, bf16_rotation=True,
+                  rotated_momentum=True)
+    states = [mo.new_state(s.m, s.n, wl.m_dtype, "cuda", W0=workloads.initial_weight(wl, i, "cuda"),
+                           rotated_momentum=True) for i, s in enumerate(wl.matrices)]
+    grp = mo.RotatedAdamGroup(states, hp)
+    ohp = harness.oracle_hyper(wl)
+    keys = ("W", "G", "M", "v", "U", "V", "Mt")
+    failures = []
+    valid = False
+    for t in range(1, steps + 1):
+        if events and t in events:
+            events[t](grp)
+            valid = False
+        harness.load_gradients(wl, states, t)
+        torch.cuda.synchronize()
+        before = {i: harness.snap(states[i], keys) for i in check_mats}
+        grp.step()
+        torch.cuda.synchronize()
+        refreshed = oracle.refresh_due(t, wl.K)
+        recompute = refreshed or not valid
+        for i in check_mats:
+            a, b = before[i], harness.snap(states[i], keys)
+            reps = [contract.gate_momentum(a["M"], a["G"], b["M"], wl.beta1, wl.m_dtype)]
+            if refreshed:
+                reps += contract.gate_refresh(b["M"], a["U"], a["V"], b["U"], b["V"], wl.power_iters)
+            if t == 1:
+                reps += contract.gate_apply_rotated_momentum(a["W"], a["v"], a["Mt"], b["M"], a["G"], b["U"], b["V"],
+                                                             b["W"], b["v"], b["Mt"], ohp, True)
+            else:
+                reps += contract.gate_apply_bf16(a["W"], a["v"], b["M"], a["G"], b["U"], b["V"], b["W"], b["v"], ohp,
+                                                 Mt_prev=a["Mt"], Mt_dev=b["Mt"], recompute=recompute)
+            line = f"t={t} mat={i} {wl.matrices[i].m}x{wl.matrices[i].n}: " + "; ".join(map(str, reps))
+            print(line, flush=True)
+            failures += [line for r in reps if not r.ok]
+        valid = True
+    grp.close()
+    assert not failures, "\n".join(failures)
+
+
+@pytest.mark.parametrize("m_dtype", ["f32", "bf16"])
+def test_bf16_rotation_with_carried_momentum_ragged(m_dtype):
+    """Refresh every 3 steps over 7 (recomputing m~ at t = 1, 4, 7, carrying
+    it otherwise), padded and unpadded shapes."""
+    mats = (workloads.MatrixSpec("a", 37, 53), workloads.MatrixSpec("b", 130, 67),
+            workloads.MatrixSpec("c", 200, 200), workloads.MatrixSpec("d", 64, 96))
+    wl = workloads.Workload("ragged_b16rm", 7, "ragged", mats, m_dtype, K=3, power_iters=1, steps=7,
+                            grad_kind="iid", grad_std=1e-2)
+    _run_combined(wl, 7, range(len(mats)))
+
+
+def test_bf16_rotation_with_carried_momentum_layer_and_events():
+    """Layer shapes with K = 0; refresh_basis before t = 3 and set_step
+    before t = 5 invalidate m~ (recomputed on those steps)."""
+    wl = workloads.get("layer")
+    wl = workloads.Workload(wl.key, wl.index, wl.title, wl.matrices, wl.m_dtype, K=0, power_iters=1, steps=6,
+                            grad_kind=wl.grad_kind, grad_std=wl.grad_std)
+    events = {3: lambda g: g.refresh_basis(1), 5: lambda g: setattr(g, "t", g.t)}
+    _run_combined(wl, 6, [0, 4, 6], events)

@@ -65,3 +65,13 @@ def test_muon_rejects_the_basis_entry_points():
             fn()
         assert e.value.status == mo.native.OPT_EUNSUPPORTED
     grp.close()
+
+
+@pytest.mark.timeout(900)
+def test_muon_qwen3_1p7b_full_size_sampled():
+    """The Qwen3-1.7B-shaped set in the bench's configuration (5 iterations),
+    gated on the first and last layer's q, k, up and down."""
+    wl = workloads.get("qwen3_1p7b")
+    idx = [i for i, s in enumerate(wl.matrices)
+           if s.layer in (0, 27) and s.name.split(".")[1] in ("q", "k", "up", "down")]
+    _run(wl, 2, 5, idx)
