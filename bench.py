@@ -341,8 +341,12 @@ def main(argv=None):
         eb = elementwise_bytes(shapes, wl.m_dtype)
         extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
         extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
-        extra["phase_tflops"] = {k: (pf[k] * args.steps / (phases[k][0] * 1e-3) / 1e12 if phases[k][0] else None)
-                                 for k in pf}
+        # per phase: the flops of the timed steps (carrying steps of the
+        # rotated-momentum variant rotate G alone)
+        pf_c = phase_flops(shapes, True)
+        n_full = len(refresh_steps) if args.rotated_momentum else args.steps
+        extra["phase_tflops"] = {k: ((pf[k] * n_full + pf_c[k] * (args.steps - n_full)) / (phases[k][0] * 1e-3) / 1e12
+                                     if phases[k][0] else None) for k in pf}
         extra["elementwise_gbps"] = {k: (eb[k] * args.steps / (phases[k][0] * 1e-3) / 1e9 if phases[k][0] else None)
                                      for k in eb}
         if refresh_steps:
