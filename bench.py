@@ -35,7 +35,8 @@ MI355X_FP32_MFMA_TFLOPS = 157.3
 MI355X_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 MFMA (no sparsity)
 MI355X_HBM_GBPS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
-GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/internal.h")
+GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/gemm.h",
+                "matrix_optimizer_step_02_amd/csrc/gmem.h")
 # Operand variants (A transposed, B transposed, A bf16, B bf16) of
 # gemm_grouped_kernel used by the rotation phases when the momentum is bf16
 # (the Gram products of the refresh read bf16 M as A, so they are the bf16-A

@@ -6,70 +6,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm.h"   // the grouped GEMM (rotations, Gram products, QR block updates)
+#include "gmem.h"
 #include "matopt.h"
 
 namespace matopt {
 
 // Records the error text returned by opt_last_error() and passes st through.
 opt_status fail(opt_status st, const char* fmt, ...);
-
-// Pointers into device memory, as the global address space. Accesses through
-// a generic pointer compile to flat instructions, which the hardware counts
-// against both the vector-memory and the LDS counters, so every wait for an
-// LDS read would also wait for the outstanding global loads; accesses
-// through these compile to global instructions, counted against vmcnt only.
-template <class T> using gmem = __attribute__((address_space(1))) T*;
-template <class T> __device__ __forceinline__ gmem<T> gptr(T* p) { return (gmem<T>)p; }
-
-// ---------------------------------------------------------------- GEMM ----
-
-enum : uint32_t {
-    GF_A_VEC = 1u << 0,   // A: ld % 4 == 0 and 16-byte (fp32) / 8-byte (bf16) aligned base
-    GF_B_VEC = 1u << 1,
-};
-
-// One product C = alpha * alpha_scale * op(A) op(B) + beta * C. The launch's
-// template fixes whether A is stored K x M (transposed) and B stored N x K.
-struct GemmProb {
-    const void* A;
-    const void* B;
-    float* C;
-    int64_t lda, ldb, ldc;
-    int32_t M, N, K;
-    uint32_t flags;
-    float alpha, beta;
-    int32_t tiles_m, tiles_n;
-};
-
-// Launch variant: bit 0 A stored K x M (transposed), bit 1 B stored N x K,
-// bit 2 A is bfloat16, bit 3 B is bfloat16. All problems of one grouped
-// launch share the variant.
-inline int gemm_variant(bool at, bool bt, bool a_bf16, bool b_bf16) {
-    return (at ? 1 : 0) | (bt ? 2 : 0) | (a_bf16 ? 4 : 0) | (b_bf16 ? 8 : 0);
-}
-
-// Two tile configurations of the grouped GEMM (rotations, Gram products,
-// opt_gemm): 128x128 outputs per workgroup of 2x2 wavefronts (64x64 each),
-// and 256x128 per workgroup of 2x2 wavefronts (128x64 each), which reuses
-// every staged operand more but needs many tiles to fill the GPU. A launch
-// takes the large tiles when it has at least kGemmLargeMinTiles of them.
-struct GemmTileCfg {
-    int bm, bn;
-};
-#ifndef MATOPT_LARGE_BM
-#define MATOPT_LARGE_BM 256
-#define MATOPT_LARGE_BN 128
-#endif
-constexpr GemmTileCfg kGemmCfgs[2] = {{128, 128}, {MATOPT_LARGE_BM, MATOPT_LARGE_BN}};
-constexpr int kGemmLargeMinTiles = 512;
-constexpr int kQrTile = 128;   // output tile of the QR trailing update
-
-// Grouped launch over `nprob` problems laid out back to back in tile space;
-// tile_begin[p] is the first tile of problem p (ascending, tile_begin[0] = 0).
-// `cfg` indexes kGemmCfgs; every problem's tiles_m/tiles_n must use it.
-hipError_t launch_gemm_grouped(int variant, int cfg, const GemmProb* probs, const int32_t* tile_begin,
-                               int nprob, int total_tiles, float alpha_scale, hipStream_t s);
-hipError_t launch_gemm_single(int variant, int cfg, const GemmProb& prob, hipStream_t s);
 
 // --------------------------------------------------------- elementwise ----
 
