@@ -151,8 +151,14 @@ typedef struct {
 #define OPT_MAX_MATRICES 65536
 
 /* Bytes of device workspace a group over these matrices needs (host only).
- * The workspace holds the device-side work lists and the scratch of one
- * micro-group (reused by every group in turn). */
+ * The workspace holds the device-side work lists, copies of the bases and the
+ * scratch of one micro-group (reused by every group in turn). The copies:
+ * with fp32 rotations (no flag, or OPT_FLAG_ROTATED_MOMENTUM alone) U^T in
+ * fp32, 4 m^2 bytes per matrix, so that U^T G and U^T M read rows of U^T;
+ * with OPT_FLAG_BF16_ROTATION the bf16 bases described there. They are
+ * rebuilt on the first step after a create, a refresh, refresh_basis,
+ * reorthonormalize or set_step: a caller that writes U or V itself must call
+ * opt_group_set_step afterwards. */
 opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
                                     const opt_hparams* hp, uint64_t* bytes);
 
@@ -202,7 +208,8 @@ opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream);
  * down to the fp32 floor. Enqueues on `stream`. */
 opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream);
 
-/* Step counter, for checkpoint/resume (all other state is caller-owned). */
+/* Step counter, for checkpoint/resume (all other state is caller-owned;
+ * set_step also marks the workspace copies of U and V for a rebuild). */
 opt_status opt_group_get_step(opt_group_t g, int64_t* t);
 opt_status opt_group_set_step(opt_group_t g, int64_t t);   /* t >= 0 */
 opt_status opt_group_set_lr(opt_group_t g, float lr);      /* finite */

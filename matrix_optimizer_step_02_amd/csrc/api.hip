@@ -66,6 +66,8 @@ struct Mat {
     bool bf16;
     // bf16-rotation variant: bf16 copies of U, U^T (m x m8) and V, V^T (n x n8)
     uint16_t *Ub = nullptr, *Utb = nullptr, *Vb = nullptr, *Vtb = nullptr;
+    // fp32 rotations: U^T (m x m), so that U^T [G | M] reads k-contiguous rows
+    float* Ut = nullptr;
 };
 
 // Byte offsets into the table image (host) / table region (device).
@@ -157,6 +159,12 @@ struct NsChunk {
 struct RefreshBatch {
     std::vector<int> mats;
     std::vector<std::vector<GemmLaunch>> prod1, prod2;   // K-chunk steps, run in order
+    // Gram products of the matrices with bf16 M on bf16 MFMA: split jobs
+    // (M^T, and the three bf16 pieces of the fp32 operand, transposed), then
+    // one launch per piece accumulating into the fp32 product
+    uint64_t split1 = 0, split2 = 0;
+    int nsplit1 = 0, nsplit2 = 0, tiles1 = 0, tiles2 = 0;
+    std::vector<Gemm16Launch> p1_16, p2_16;
     CopyLaunch comp;
     QrBatch qr;
     uint64_t ref_bytes = 0;
@@ -190,12 +198,15 @@ struct opt_group_s {
     uint64_t ws_bytes = 0;
     Image img;
     uint64_t table_bytes = 0, scratch_bytes = 0;
-    // bf16-rotation variant: the bases' bf16 copies (after the tables, before
-    // the scratch), their conversion launch, and whether they match U, V
+    // copies of the bases after the tables, before the scratch: bf16 U, U^T,
+    // V, V^T (bf16-rotation variant) or fp32 U^T (fp32 rotations), their
+    // conversion launch, and whether they match U, V
     uint64_t bases_bytes = 0;
     uint64_t basis_jobs = 0;
     int basis_njobs = 0, basis_tiles = 0;
-    bool bases16_valid = false;
+    uint64_t transpose_jobs = 0;
+    int transpose_njobs = 0, transpose_tiles = 0;
+    bool copies_valid = false;
     // state checks: one scan over every matrix (partials at the start of the
     // scratch), per-matrix records in the table region
     uint64_t health_segs = 0, health_out = 0;
@@ -528,6 +539,25 @@ int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
 // near that of a blocked CPU GEMM instead of growing with the full K.
 constexpr int64_t kChunkK = 1024;
 
+// The bf16 products take up to kChunkK16 of K per launch: 16 k per MFMA, so
+// the same 512-MFMA bound on an fp32 accumulation chain.
+constexpr int64_t kChunkK16 = 8192;
+
+// Appends the K chunks of a bf16 NT product (k contiguous in A and B) to
+// steps[next], steps[next + 1], ...; returns the index after the last.
+size_t add_k_chunked16(std::vector<std::vector<Gemm16Prob>>& steps, size_t next, const Gemm16Prob& g) {
+    for (int64_t k0 = 0; k0 == 0 || k0 < g.K; k0 += kChunkK16, ++next) {
+        if (steps.size() <= next) steps.resize(next + 1);
+        Gemm16Prob c = g;
+        c.A = g.A + k0;
+        c.B = g.B + k0;
+        c.K = (int32_t)std::min<int64_t>(kChunkK16, g.K - k0);
+        if (k0) c.beta = 1.f;
+        steps[next].push_back(c);
+    }
+    return next;
+}
+
 // Rows of a basis per Newton-Schulz product launch: the product goes to the
 // QR job's `part` buffer, which holds kQrMaxSplits * kQrPB rows of d floats.
 constexpr int64_t kNsRows = (int64_t)kQrMaxSplits * kQrPB;
@@ -668,6 +698,20 @@ QrSteps qr_block_steps(const std::vector<QrJob>& jobs) {
 
 // Refresh scratch of one matrix: Gram products B1U (n x r), B1V (m x r), the
 // QR inputs ZU (m x m), ZV (n x n) and the QR scratch of both orders.
+// Matrices whose Gram products run on bf16 MFMA: bf16 M that the bf16 GEMM
+// can read directly (rows of a multiple of 8 elements, 16-byte aligned).
+bool gram16_eligible(const Mat& M) {
+    return M.bf16 && M.d.m % 8 == 0 && M.d.n % 8 == 0 && aligned(M.d.M, 16);
+}
+
+// Extra refresh scratch of an eligible matrix: M^T (bf16, n x m) and the
+// three bf16 pieces of U_r^T (r x m) and of V_r^T (r x n), whose space the
+// pieces of B1V^T and B1U^T reuse.
+uint64_t gram16_bytes(int64_t m, int64_t n) {
+    const int64_t r = std::min(m, n);
+    return align_up(2ull * n * m) + align_up(6ull * r * m) + align_up(6ull * r * n);
+}
+
 uint64_t refresh_bytes(int64_t m, int64_t n) {
     const int64_t r = std::min(m, n);
     QrBytes bu = qr_job_bytes(m), bv = qr_job_bytes(n);
@@ -682,7 +726,8 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
     uint64_t used = 0;
     for (const std::vector<int>& members : plan)
         for (int mi : members) {
-            const uint64_t b = refresh_bytes(g->mats[mi].d.m, g->mats[mi].d.n);
+            const uint64_t b = refresh_bytes(g->mats[mi].d.m, g->mats[mi].d.n) +
+                               (gram16_eligible(g->mats[mi]) ? gram16_bytes(g->mats[mi].d.m, g->mats[mi].d.n) : 0);
             if (out.empty() || (used + b > cap && !out.back().empty())) {
                 out.emplace_back();
                 used = 0;
@@ -731,8 +776,29 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->basis_tiles = tiles;
         g->basis_jobs = g->img.put(bj);
     }
-    char* scratch = region + g->bases_bytes;
     const bool muon = g->hp.flags & OPT_FLAG_MUON;
+    g->transpose_njobs = g->transpose_tiles = 0;
+    if (!r16 && !muon) {
+        std::vector<TransposeJob> tj;
+        int tiles = 0;
+        for (Mat& M : g->mats) {
+            const int64_t m = M.d.m;
+            M.Ut = (float*)(region + g->bases_bytes);
+            g->bases_bytes += align_up(4ull * m * m);
+            TransposeJob j{};
+            j.X = M.d.U;
+            j.Xt = M.Ut;
+            j.d = (int32_t)m;
+            j.tile_begin = tiles;
+            const int per = (int)((m + kTransposeTile - 1) / kTransposeTile);
+            tiles += per * per;
+            tj.push_back(j);
+        }
+        g->transpose_njobs = (int)tj.size();
+        g->transpose_tiles = tiles;
+        g->transpose_jobs = g->img.put(tj);
+    }
+    char* scratch = region + g->bases_bytes;
     for (const std::vector<int>& members : plan) {
         Group G;
         G.mats = members;
@@ -805,9 +871,11 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             float* TM = (float*)(scratch + off); off += align_up(4ull * mn);
             float* Gt = (float*)(scratch + off); off += align_up(4ull * mn);
             float* mt = (float*)(scratch + off); off += align_up(4ull * mn);
-            // U^T G, U^T M (A = U stored m x m read transposed)
-            left.push_back(mk(true, false, x.U, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
-            left.push_back(mk(true, false, x.U, false, m, x.M, M.bf16, n, TM, n, m, n, m, 1.f, 0.f));
+            // U^T G, U^T M (A = the U^T copy, or U stored m x m read transposed)
+            const bool at = !M.Ut;
+            const float* UA = M.Ut ? M.Ut : x.U;
+            left.push_back(mk(at, false, UA, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
+            left.push_back(mk(at, false, UA, false, m, x.M, M.bf16, n, TM, n, m, n, m, 1.f, 0.f));
             // (U^T G) V, (U^T M) V
             right.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
             right.push_back(mk(false, false, TM, false, n, x.V, false, n, mt, n, m, n, n, 1.f, 0.f));
@@ -833,7 +901,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 // recompute: (U^T M) V -> Mt; u = Mt / (sqrt(v) + eps) -> mt slot
                 right_re.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
                 right_re.push_back(mk(false, false, TM, false, n, x.V, false, n, x.Mt, n, m, n, n, 1.f, 0.f));
-                left_c.push_back(mk(true, false, x.U, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
+                left_c.push_back(mk(at, false, UA, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
                 right_c.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
                 EwSeg r = a;
                 r.b = x.Mt;
@@ -977,6 +1045,25 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         R.mats = members;
         uint64_t off = 0;
         std::vector<PGemm> p1, p2;
+        std::vector<std::vector<Gemm16Prob>> q1, q2;
+        std::vector<SplitJob> sj1, sj2;
+        int t1 = 0, t2 = 0;
+        auto split = [](std::vector<SplitJob>& v, int& tiles, const void* src, bool src_bf16, int64_t ld_src,
+                        int64_t rows, int64_t cols, uint16_t* dst, int npieces) {
+            SplitJob j{};
+            j.src = src;
+            j.dst = dst;
+            j.ld_src = ld_src;
+            j.ld_dst = rows;
+            j.piece_stride = rows * cols;
+            j.rows = (int32_t)rows;
+            j.cols = (int32_t)cols;
+            j.npieces = npieces;
+            j.src_bf16 = src_bf16;
+            j.tile_begin = tiles;
+            tiles += (int)(((rows + 31) / 32) * ((cols + 31) / 32));
+            v.push_back(j);
+        };
         std::vector<CopyJob> comp;
         struct JobSrc { int64_t d; float* Z; float* X; int mat; int side; };
         std::vector<JobSrc> jsrc;
@@ -988,14 +1075,37 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             float* B1V = (float*)(scratch + off); off += align_up(4ull * m * r);
             float* ZU = (float*)(scratch + off); off += align_up(4ull * m * m);
             float* ZV = (float*)(scratch + off); off += align_up(4ull * n * n);
-            // B1U = M^T U[:, :r]   (n x r): A = M stored m x n read transposed
-            p1.push_back(mk(true, false, x.M, M.bf16, n, x.U, false, m, B1U, r, n, r, m, 1.f, 0.f));
-            // B1V = M V[:, :r]     (m x r)
-            p1.push_back(mk(false, false, x.M, M.bf16, n, x.V, false, n, B1V, r, m, r, n, 1.f, 0.f));
-            // ZU[:, :r] = M B1U     (m x r)
-            p2.push_back(mk(false, false, x.M, M.bf16, n, B1U, false, r, ZU, m, m, r, n, 1.f, 0.f));
-            // ZV[:, :r] = M^T B1V   (n x r)
-            p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
+            if (gram16_eligible(M)) {
+                // bf16 M exactly, the fp32 operand as three exact bf16 pieces:
+                // every Gram product is three bf16 NT products accumulating in fp32
+                uint16_t* Mt = (uint16_t*)(scratch + off); off += align_up(2ull * n * m);
+                uint16_t* Up = (uint16_t*)(scratch + off); off += align_up(6ull * r * m);   // later B1V^T pieces
+                uint16_t* Vp = (uint16_t*)(scratch + off); off += align_up(6ull * r * n);   // later B1U^T pieces
+                const uint16_t* Mb = (const uint16_t*)x.M;
+                split(sj1, t1, x.M, true, n, m, n, Mt, 1);          // M^T (n x m)
+                split(sj1, t1, x.U, false, m, m, r, Up, 3);         // U[:, :r]^T pieces (r x m)
+                split(sj1, t1, x.V, false, n, n, r, Vp, 3);         // V[:, :r]^T pieces (r x n)
+                split(sj2, t2, B1U, false, r, n, r, Vp, 3);         // B1U^T pieces (r x n)
+                split(sj2, t2, B1V, false, r, m, r, Up, 3);         // B1V^T pieces (r x m)
+                // pieces in order hi, mid, lo, each in K chunks, accumulating
+                size_t a = 0, b = 0, c = 0, d = 0;
+                for (int pc = 0; pc < 3; ++pc) {
+                    const float beta = pc ? 1.f : 0.f;
+                    a = add_k_chunked16(q1, a, g16(Mt, m, Up + pc * r * m, m, B1U, r, n, r, m, 1.f, beta, r));  // M^T U_r
+                    b = add_k_chunked16(q1, b, g16(Mb, n, Vp + pc * r * n, n, B1V, r, m, r, n, 1.f, beta, r));  // M V_r
+                    c = add_k_chunked16(q2, c, g16(Mb, n, Vp + pc * r * n, n, ZU, m, m, r, n, 1.f, beta, r));   // M B1U
+                    d = add_k_chunked16(q2, d, g16(Mt, m, Up + pc * r * m, m, ZV, n, n, r, m, 1.f, beta, r));   // M^T B1V
+                }
+            } else {
+                // B1U = M^T U[:, :r]   (n x r): A = M stored m x n read transposed
+                p1.push_back(mk(true, false, x.M, M.bf16, n, x.U, false, m, B1U, r, n, r, m, 1.f, 0.f));
+                // B1V = M V[:, :r]     (m x r)
+                p1.push_back(mk(false, false, x.M, M.bf16, n, x.V, false, n, B1V, r, m, r, n, 1.f, 0.f));
+                // ZU[:, :r] = M B1U     (m x r)
+                p2.push_back(mk(false, false, x.M, M.bf16, n, B1U, false, r, ZU, m, m, r, n, 1.f, 0.f));
+                // ZV[:, :r] = M^T B1V   (n x r)
+                p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
+            }
             if (r < m) comp.push_back({x.U, ZU, (int32_t)m, (int32_t)r});
             if (r < n) comp.push_back({x.V, ZV, (int32_t)n, (int32_t)r});
             jsrc.push_back({m, ZU, x.U, M.idx, 0});
@@ -1023,6 +1133,16 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             for (const PGemm& x : p2) add_k_chunked(s2, x);
             for (const std::vector<PGemm>& st : s1) R.prod1.push_back(put_gemm(g->img, st));
             for (const std::vector<PGemm>& st : s2) R.prod2.push_back(put_gemm(g->img, st));
+            if (!sj1.empty()) {
+                R.nsplit1 = (int)sj1.size();
+                R.nsplit2 = (int)sj2.size();
+                R.tiles1 = t1;
+                R.tiles2 = t2;
+                R.split1 = g->img.put(sj1);
+                R.split2 = g->img.put(sj2);
+                for (const std::vector<Gemm16Prob>& st : q1) R.p1_16.push_back(put_gemm16(g->img, st, false));
+                for (const std::vector<Gemm16Prob>& st : q2) R.p2_16.push_back(put_gemm16(g->img, st, false));
+            }
         }
         R.comp.n = (int)comp.size();
         R.comp.max_d = 0;
@@ -1241,8 +1361,16 @@ hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, h
     PhaseScope ps(g, OPT_PHASE_REFRESH, s);
     hipError_t e;
     for (int it = 0; it < power_iters; ++it) {
+        if (G.nsplit1) {
+            if ((e = launch_split16(dptr<SplitJob>(g, G.split1), G.nsplit1, G.tiles1, s))) return e;
+            if ((e = run_gemm16(g, G.p1_16, 1.f, s))) return e;
+        }
         for (const std::vector<GemmLaunch>& st : G.prod1)
             if ((e = run_gemm(g, st, 1.f, s))) return e;
+        if (G.nsplit2) {
+            if ((e = launch_split16(dptr<SplitJob>(g, G.split2), G.nsplit2, G.tiles2, s))) return e;
+            if ((e = run_gemm16(g, G.p2_16, 1.f, s))) return e;
+        }
         for (const std::vector<GemmLaunch>& st : G.prod2)
             if ((e = run_gemm(g, st, 1.f, s))) return e;
         if ((e = launch_copy_cols(dptr<CopyJob>(g, G.comp.jobs), G.comp.n, G.comp.max_d, s))) return e;
@@ -1427,14 +1555,14 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             }
             for (const RefreshBatch& R : g->rbatches)
                 if ((e = run_refresh(g, R, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
-            g->bases16_valid = false;
+            g->copies_valid = false;
         }
-        if (!g->bases16_valid) {
+        if (!g->copies_valid) {
             PhaseScope ps(g, OPT_PHASE_REFRESH, s);
             if ((e = launch_basis16(dptr<BasisJob>(g, g->basis_jobs), g->basis_njobs, g->basis_tiles, s)))
                 return hip_fail(e, "basis conversion launch");
             g->kernels_in_scope += 1;
-            g->bases16_valid = true;
+            g->copies_valid = true;
         }
         for (const Group& G : g->groups) {
             {
@@ -1495,9 +1623,19 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
         if (e) return hip_fail(e, "momentum launch");
         g->kernels_in_scope += G.mom.nseg > 0;
     }
-    if (refresh)
+    if (refresh) {
         for (const RefreshBatch& R : g->rbatches)
             if ((e = run_refresh(g, R, g->hp.power_iters, s))) return hip_fail(e, "refresh launch");
+        g->copies_valid = false;
+    }
+    if (g->transpose_njobs && !g->copies_valid) {
+        PhaseScope ps(g, OPT_PHASE_REFRESH, s);
+        if ((e = launch_transpose32(dptr<TransposeJob>(g, g->transpose_jobs), g->transpose_njobs,
+                                    g->transpose_tiles, s)))
+            return hip_fail(e, "basis transpose launch");
+        g->kernels_in_scope += 1;
+        g->copies_valid = true;
+    }
     // with the carried rotated momentum: recompute m~ when the bases are new
     // to it, else carry it (G alone is rotated)
     const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
@@ -1541,7 +1679,7 @@ opt_status opt_group_refresh_basis(opt_group_t g, int32_t power_iters, void* str
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before refresh");
     g->mt_valid = false;
-    g->bases16_valid = false;
+    g->copies_valid = false;
     for (const RefreshBatch& R : g->rbatches)
         if ((e = run_refresh(g, R, power_iters, (hipStream_t)stream))) return hip_fail(e, "refresh launch");
     return OPT_OK;
@@ -1594,7 +1732,7 @@ opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");
     hipStream_t s = (hipStream_t)stream;
-    if (iters > 0) g->mt_valid = g->bases16_valid = false;
+    if (iters > 0) g->mt_valid = g->copies_valid = false;
     for (int it = 0; it < iters; ++it)
         for (const RefreshBatch& R : g->rbatches) {
             for (const std::vector<GemmLaunch>& stp : R.gram)
@@ -1621,7 +1759,7 @@ opt_status opt_group_set_step(opt_group_t g, int64_t t) {
     if (t < 0) return fail(OPT_EINVAL, "t must be >= 0");
     g->t = t;
     g->mt_valid = false;   // a resumed job recomputes the rotated momentum
-    g->bases16_valid = false;   // and the bf16 bases (the caller may have written U, V)
+    g->copies_valid = false;   // and the copies of the bases (the caller may have written U, V)
     return OPT_OK;
 }
 

@@ -380,7 +380,80 @@ __global__ __launch_bounds__(256) void basis16_kernel(const BasisJob* __restrict
     }
 }
 
+__global__ __launch_bounds__(256) void transpose32_kernel(const TransposeJob* __restrict__ jobs, int njobs) {
+    __shared__ float tile[kTransposeTile][kTransposeTile + 1];
+    const int bid = blockIdx.x;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].tile_begin <= bid) lo = mid; else hi = mid - 1;
+    }
+    const TransposeJob J = jobs[lo];
+    const int per_row = (J.d + kTransposeTile - 1) / kTransposeTile;
+    const int t = bid - J.tile_begin;
+    const int R = (t / per_row) * kTransposeTile, Cc = (t % per_row) * kTransposeTile;
+    const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
+    for (int y = y0; y < kTransposeTile; y += 8) {
+        const int r = R + y, c = Cc + x;
+        if (r < J.d && c < J.d) tile[y][x] = gptr(J.X)[(int64_t)r * J.d + c];
+    }
+    __syncthreads();
+    for (int y = y0; y < kTransposeTile; y += 8) {
+        const int i = Cc + y, k = R + x;   // Xt[i][k] = X[k][i]
+        if (i < J.d && k < J.d) gptr(J.Xt)[(int64_t)i * J.d + k] = tile[x][y];
+    }
+}
+
+// Tiles of a split job: tile t covers k in [32 (t / CT), +32), c in
+// [32 (t % CT), +32) with CT = ceil(cols / 32) column tiles; the LDS tile is
+// read along c and written along k.
+__global__ __launch_bounds__(256) void split16_kernel(const SplitJob* __restrict__ jobs, int njobs) {
+    __shared__ float tile[32][33];
+    const int bid = blockIdx.x;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].tile_begin <= bid) lo = mid; else hi = mid - 1;
+    }
+    const SplitJob J = jobs[lo];
+    const int ct = (J.cols + 31) / 32;
+    const int t = bid - J.tile_begin;
+    const int k0 = (t / ct) * 32, c0 = (t % ct) * 32;
+    const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
+    for (int y = y0; y < 32; y += 8) {
+        const int k = k0 + y, c = c0 + x;
+        float v = 0.f;
+        if (k < J.rows && c < J.cols) {
+            const int64_t si = (int64_t)k * J.ld_src + c;
+            v = J.src_bf16 ? bf16_to_f32(gptr((const uint16_t*)J.src)[si]) : gptr((const float*)J.src)[si];
+        }
+        tile[y][x] = v;
+    }
+    __syncthreads();
+    for (int y = y0; y < 32; y += 8) {
+        const int c = c0 + y, k = k0 + x;
+        if (c >= J.cols || k >= J.ld_dst) continue;
+        const float v = tile[x][y];
+        const int64_t di = (int64_t)c * J.ld_dst + k;
+        const uint16_t h = f32_to_bf16(v);
+        gptr(J.dst)[di] = h;
+        if (J.npieces == 3) {
+            const float r1 = v - bf16_to_f32(h);
+            const uint16_t m = f32_to_bf16(r1);
+            const float r2 = r1 - bf16_to_f32(m);
+            gptr(J.dst)[J.piece_stride + di] = m;
+            gptr(J.dst)[2 * J.piece_stride + di] = f32_to_bf16(r2);
+        }
+    }
+}
+
 }  // namespace
+
+hipError_t launch_split16(const SplitJob* jobs, int njobs, int total_tiles, hipStream_t s) {
+    if (njobs <= 0 || total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(split16_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, jobs, njobs);
+    return hipGetLastError();
+}
 
 hipError_t launch_momentum16(const Ew16Seg* segs, int nseg, int64_t total_chunks, float beta1, hipStream_t s) {
     if (nseg <= 0 || total_chunks <= 0) return hipSuccess;
@@ -413,6 +486,12 @@ hipError_t launch_pack16(const PackJob* jobs, int njobs, int64_t total_chunks, h
 hipError_t launch_basis16(const BasisJob* jobs, int njobs, int total_tiles, hipStream_t s) {
     if (njobs <= 0 || total_tiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(basis16_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, jobs, njobs);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose32(const TransposeJob* jobs, int njobs, int total_tiles, hipStream_t s) {
+    if (njobs <= 0 || total_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose32_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, jobs, njobs);
     return hipGetLastError();
 }
 

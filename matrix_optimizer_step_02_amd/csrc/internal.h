@@ -38,6 +38,18 @@ hipError_t launch_momentum(const EwSeg* segs, int nseg, int64_t total_chunks, fl
 hipError_t launch_rotated_adam(const EwSeg* segs, int nseg, int64_t total_chunks, float beta1, float beta2,
                                float eps, hipStream_t s);
 
+// A d x d fp32 matrix X to its transpose Xt (both row-major, row stride d):
+// 32 x 32 tiles through LDS, reads and writes along rows; tile_begin is the
+// job's first tile of ceil(d / 32)^2.
+struct TransposeJob {
+    const float* X;
+    float* Xt;
+    int32_t d;
+    int32_t tile_begin;
+};
+constexpr int kTransposeTile = 32;
+hipError_t launch_transpose32(const TransposeJob* jobs, int njobs, int total_tiles, hipStream_t s);
+
 // ------------------------------------------------------------------ QR ----
 
 constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY block)

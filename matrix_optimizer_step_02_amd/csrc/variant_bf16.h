@@ -91,4 +91,23 @@ struct BasisJob {
 constexpr int kBasisTile = 32;
 hipError_t launch_basis16(const BasisJob* jobs, int njobs, int total_tiles, hipStream_t s);
 
+// Transposed bf16 pieces of a rows x cols block X (fp32 or bf16, row stride
+// ld_src): dst + p * piece_stride holds piece p as a cols x ld_dst row-major
+// matrix, dst_p[c][k] = piece_p(X[k][c]) for k < rows, zeros for rows <= k <
+// ld_dst. With npieces == 3 (fp32 X) the pieces are hi = rb(x),
+// mid = rb(x - hi), lo = x - hi - mid, which sum to x exactly (each residual
+// is exact in fp32 and lo fits in bf16), so a product with X equals the sum of
+// three bf16 products up to fp32 accumulation; with npieces == 1 the single
+// piece is rb(x) (an exact transpose for bf16 X). 32 x 32 tiles over
+// ld_dst x cols; tile_begin is the job's first tile.
+struct SplitJob {
+    const void* src;
+    uint16_t* dst;
+    int64_t ld_src, ld_dst, piece_stride;
+    int32_t rows, cols;
+    int32_t npieces, src_bf16;
+    int32_t tile_begin;
+};
+hipError_t launch_split16(const SplitJob* jobs, int njobs, int total_tiles, hipStream_t s);
+
 }  // namespace matopt

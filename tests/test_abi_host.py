@@ -140,17 +140,23 @@ def test_muon_flag_checks(N):
     assert need < 1 << 20
 
 
-def test_bf16_rotation_workspace_holds_the_bf16_bases(N):
-    """The variant adds bf16 copies of U, U^T, V, V^T for every matrix
-    (rows padded to multiples of 8 elements) to the shared scratch."""
+def test_workspace_holds_the_copies_of_the_bases(N):
+    """The fp32 rotations keep an fp32 U^T (4 m^2 bytes, 256-byte aligned)
+    per matrix; the bf16 variant instead keeps bf16 U, U^T, V, V^T (rows
+    padded to multiples of 8 elements) and a larger scratch; Muon keeps
+    neither."""
     shapes = [(130, 67), (64, 64), (24, 40)]
     d = descs(N, shapes)
     base = N.opt_group_workspace_size(d, hp(N))
     var = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
+    rm = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_ROTATED_MOMENTUM))
     r8 = lambda x: (x + 7) // 8 * 8
+    a256 = lambda x: (x + 255) // 256 * 256
+    ut = sum(a256(4 * m * m) for m, _ in shapes)
     bases = sum(2 * 2 * m * r8(m) + 2 * 2 * n * r8(n) for m, n in shapes)
-    assert var >= base + bases
-    assert var < base + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
+    assert base > ut and rm == base
+    assert var >= base - ut + bases
+    assert var < base - ut + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
 
 
 def test_rejects_bad_shapes_and_dtypes(N):
@@ -214,10 +220,12 @@ def test_null_group_and_bad_building_block_args(N):
 
 
 def test_workspace_is_max_over_groups(N):
-    """Scratch is sized for the largest micro-group (or refresh batch), not the sum."""
+    """Scratch is sized for the largest micro-group (or refresh batch), not
+    the sum; the fp32 U^T copies (4 MiB per matrix here) are per matrix."""
     h = hp(N, refresh_capacity_bytes=1 << 30)
-    one_group = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 128), h)  # 128 x 4 MiB = cap
-    two_groups = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 200), h)
+    ut = 4 * 1024 * 1024
+    one_group = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 128), h) - 128 * ut  # 128 x 4 MiB = cap
+    two_groups = N.opt_group_workspace_size(descs(N, [(1024, 1024)] * 200), h) - 200 * ut
     assert N.opt_plan(descs(N, [(1024, 1024)] * 200), h)[2] == 2
     assert one_group <= two_groups < 1.05 * one_group
     assert one_group >= 128 * 4 * 4 * 1024 * 1024          # four m x n rotation buffers per matrix

@@ -135,3 +135,45 @@ def test_qwen3_8b_half_full_size_sampled():
            or (s.layer == 17 and s.name.split(".")[1] == "up")]
     assert len(idx) == 4
     _run_gated(wl, 2, {1, 2}, idx)
+
+
+def test_rotations_follow_bases_changed_between_steps():
+    """The fp32 rotations read U^T from a workspace copy of U: after
+    refresh_basis, and after the caller writes new orthogonal U, V and calls
+    set_step, the next step must rotate with the new bases (gate B against
+    the bases as they are before that step)."""
+    import torch
+    mats = (workloads.MatrixSpec("a", 37, 53), workloads.MatrixSpec("b", 130, 67),
+            workloads.MatrixSpec("c", 96, 96))
+    wl = workloads.Workload("bases_changed", 11, "bases changed", mats, "bf16", K=0, power_iters=1, steps=5,
+                            grad_kind="iid", grad_std=1e-2)
+    grp, states = harness.build_group(wl)
+    hp = harness.oracle_hyper(wl)
+    rng = np.random.default_rng(23)
+    failures = []
+    for t in range(1, 6):
+        if t == 3:
+            grp.refresh_basis(1)
+        if t == 4:
+            for st in states:
+                for key in ("U", "V"):
+                    d = st[key].shape[0]
+                    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+                    st[key].copy_(torch.tensor(q * np.sign(np.diag(r)), dtype=torch.float32))
+            grp.t = grp.t
+        harness.load_gradients(wl, states, t)
+        torch.cuda.synchronize()
+        before = [harness.snap(s) for s in states]
+        grp.step()
+        torch.cuda.synchronize()
+        for i, st in enumerate(states):
+            a, b = before[i], harness.snap(st)
+            assert np.array_equal(a["U"], b["U"]) and np.array_equal(a["V"], b["V"])
+            reps = [contract.gate_momentum(a["M"], a["G"], b["M"], wl.beta1, wl.m_dtype)]
+            reps += contract.gate_apply(a["W"], a["v"], b["M"], a["G"], b["U"], b["V"], b["W"], b["v"], hp,
+                                        wl.m_dtype)
+            line = f"t={t} mat={i}: " + "; ".join(map(str, reps))
+            print(line, flush=True)
+            failures += [line for r in reps if not r.ok]
+    grp.close()
+    assert not failures, "\n".join(failures)
