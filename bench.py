@@ -38,11 +38,13 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/gemm.h",
                 "matrix_optimizer_step_02_amd/csrc/gmem.h")
 # Operand variants (A transposed, B transposed, A bf16, B bf16) of
-# gemm_grouped_kernel used by the rotation phases when the momentum is bf16
-# (the Gram products of the refresh read bf16 M as A, so they are the bf16-A
-# instantiations and stay out of this set).
-ROTATION_VARIANTS = {("true", "false", "false", "false"), ("true", "false", "false", "true"),
-                     ("false", "false", "false", "false"), ("false", "true", "false", "false")}
+# gemm_grouped_kernel used by the rotation phases when the momentum is bf16:
+# U^T G and U^T M read the fp32 U^T copy (B fp32, then bf16), (.)V and U u are
+# plain, (.)V^T reads V transposed. The refresh's Gram products of a bf16 M
+# run on the bf16 GEMM; its QR launches share instantiations with these, so
+# the counters take steps without a refresh.
+ROTATION_VARIANTS = {("false", "false", "false", "false"), ("false", "false", "false", "true"),
+                     ("false", "true", "false", "false")}
 
 
 def is_rotation_gemm(kernel_name: str) -> bool:
