@@ -243,10 +243,12 @@ def test_bench_selects_rotation_dispatches_from_non_refresh_steps():
     """The counter summary takes only grouped GEMMs of steps without a QR
     kernel: the refresh uses the same GEMM instantiations."""
     import bench
-    gemm = "void matopt::(anonymous namespace)::gemm_grouped_kernel<matopt::(anonymous namespace)::Cfg<2, 4, 4, 2>, false, false, false, false>(matopt::(anonymous namespace)::GemmArgs)"
+    name = ("void matopt::(anonymous namespace)::gemm_grouped_kernel<matopt::(anonymous namespace)::"
+            "Cfg<2, 2, 4, 2, 16>, false, {}, false, {}>(matopt::(anonymous namespace)::GemmArgs)")
+    gemm, bf16_b, bt = name.format("false", "false"), name.format("false", "true"), name.format("true", "false")
     seq = ["copyBuffer", "momentum_kernel", "momentum_kernel", gemm, "qr_panel_kernel", gemm, gemm,
-           "rotated_adam_kernel", gemm, "momentum_kernel", "momentum_kernel", gemm, gemm,
-           "rotated_adam_kernel", gemm, gemm]
+           "rotated_adam_kernel", gemm, "momentum_kernel", "momentum_kernel", gemm, bf16_b, gemm,
+           "rotated_adam_kernel", gemm, bt, "gemm16_kernel<Cfg16<2, 2, 4, 4, 64, 2>, false>(Gemm16Args)"]
     rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": k} for i, k in enumerate(seq)]
     picked = bench.rotation_dispatches(list(reversed(rows)))
-    assert [int(r["Dispatch_Id"]) for r in picked] == [12, 13, 15, 16]
+    assert [int(r["Dispatch_Id"]) for r in picked] == [12, 13, 14, 16, 17]
