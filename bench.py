@@ -35,8 +35,9 @@ MI355X_FP32_MFMA_TFLOPS = 157.3
 MI355X_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 MFMA (no sparsity)
 MI355X_HBM_GBPS = 8000.0
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
+# the kernel's sources and the schedule that decides what each launch holds
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/gemm.h",
-                "matrix_optimizer_step_02_amd/csrc/gmem.h")
+                "matrix_optimizer_step_02_amd/csrc/gmem.h", "matrix_optimizer_step_02_amd/csrc/api.hip")
 def is_rotation_gemm(kernel_name: str) -> bool:
     """Any instantiation of the fp32 grouped GEMM: in a step without a
     refresh every one of its launches is a rotation phase."""
@@ -49,16 +50,34 @@ def rotation_flops(shapes):
     return sum(6.0 * m * n * (m + n) for m, n in shapes)
 
 
-def phase_flops(shapes, carry=False):
+def pieced(m, n, m_dtype, plain_fp32):
+    """Whether the library runs this matrix's momentum product U^T M (m > n)
+    or M V (else) as three bf16 products against exact pieces of the basis:
+    fp32 rotations of a bf16 M with m, n multiples of 8."""
+    return plain_fp32 and m_dtype == "bf16" and m % 8 == 0 and n % 8 == 0
+
+
+def phase_flops(shapes, carry=False, m_dtype="f32", plain_fp32=False):
     """Algorithmic flops of each GEMM phase for one step over all matrices
-    (carry: a step of the rotated-momentum variant that rotates G alone)."""
-    k = 2.0 if carry else 4.0
-    return {
-        "rot_left": sum(k * m * m * n for m, n in shapes),
-        "rot_right": sum(k * m * n * n for m, n in shapes),
-        "back_left": sum(2.0 * m * m * n for m, n in shapes),
-        "back_right": sum(2.0 * m * n * n for m, n in shapes),
-    }
+    (carry: a step of the rotated-momentum variant that rotates G alone;
+    plain_fp32: the method's fp32 rotations with no flag, where a bf16 M's
+    larger product moves to the pieced phase)."""
+    out = {"rot_left": 0.0, "rot_right": 0.0, "back_left": 0.0, "back_right": 0.0}
+    for m, n in shapes:
+        out["rot_left"] += 2.0 * m * m * n
+        out["rot_right"] += 2.0 * m * n * n
+        out["back_left"] += 2.0 * m * m * n
+        out["back_right"] += 2.0 * m * n * n
+        if carry:
+            continue
+        if pieced(m, n, m_dtype, plain_fp32):
+            # U^T M (tall) or M V (wide/square) pieced, the other product fp32
+            out["rot_pieced"] = out.get("rot_pieced", 0.0) + 2.0 * m * n * max(m, n)
+            out["rot_right" if m > n else "rot_left"] += 2.0 * m * n * min(m, n)
+        else:
+            out["rot_left"] += 2.0 * m * m * n
+            out["rot_right"] += 2.0 * m * n * n
+    return out
 
 
 def elementwise_bytes(shapes, m_dtype):
@@ -212,6 +231,8 @@ def main(argv=None):
     ap.add_argument("--muon", action="store_true",
                     help="the orthogonalised-momentum step (Newton-Schulz polar factor of M) instead")
     ap.add_argument("--ns-iters", type=int, default=5, help="Newton-Schulz iterations of --muon")
+    ap.add_argument("--fp32-momentum-rotation", action="store_true",
+                    help="keep a bf16 momentum's rotation on fp32 MFMAs (no pieced bf16 products)")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -262,7 +283,8 @@ def main(argv=None):
         states.append(st)
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
                   int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum,
-                  bf16_rotation=args.bf16_rotation, muon=args.muon, ns_iters=args.ns_iters if args.muon else 0)
+                  bf16_rotation=args.bf16_rotation, muon=args.muon, ns_iters=args.ns_iters if args.muon else 0,
+                  fp32_momentum_rotation=args.fp32_momentum_rotation)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()
@@ -310,7 +332,10 @@ def main(argv=None):
         extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
         extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
     elif phases:
-        pf = phase_flops(shapes)
+        plain = not (args.rotated_momentum or args.bf16_rotation or args.fp32_momentum_rotation)
+        pf_all = phase_flops(shapes, m_dtype=wl.m_dtype, plain_fp32=plain)
+        # the roofline is the dominant kernel's: the pieced bf16 products are reported beside it
+        pf = {k: v for k, v in pf_all.items() if k != "rot_pieced"}
         flops = sum(pf.values()) * args.steps
         if args.rotated_momentum:   # recompute steps are the refreshes; the others carry m~
             carried = args.steps - len(refresh_steps)
@@ -321,6 +346,8 @@ def main(argv=None):
         peak = MI355X_BF16_MFMA_TFLOPS if args.bf16_rotation else MI355X_FP32_MFMA_TFLOPS
         kernel = ("gemm16_kernel (bf16 rotation phases: (X V)^T, U^T S^T, (u V^T)^T, W -= lr U P^T)"
                   if args.bf16_rotation else
+                  "gemm_grouped_kernel (fp32 rotation phases: U^T G, (U^T G) V, the fp32 product of M's "
+                  "chain, U u, W -= lr (.)V^T)" if "rot_pieced" in pf_all else
                   "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)")
         roofline = {
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
@@ -341,6 +368,20 @@ def main(argv=None):
                                      if phases[k][0] else None) for k in pf}
         extra["elementwise_gbps"] = {k: (eb[k] * args.steps / (phases[k][0] * 1e-3) / 1e9 if phases[k][0] else None)
                                      for k in eb}
+        if "rot_pieced" in pf_all and phases["rot_pieced"][0]:
+            # fp32-equivalent algorithmic flops (2 m n max(m, n) per pieced matrix);
+            # the bf16 MFMAs do three times as many
+            ms_p = phases["rot_pieced"][0]
+            eq = pf_all["rot_pieced"] * args.steps / (ms_p * 1e-3) / 1e12
+            extra["pieced"] = {
+                "kernel": "gemm16_kernel (U^T M or M V of a bf16 M, three exact bf16 pieces of the basis) "
+                          "and the M^T copies it reads",
+                "flops_per_step": pf_all["rot_pieced"], "ms_per_step": ms_p / args.steps,
+                "fp32_equiv_tflops": eq, "bf16_mfma_tflops": 3 * eq,
+                "bf16_frac": 3 * eq / MI355X_BF16_MFMA_TFLOPS,
+                "rotations_tflops": (sum(pf_all.values()) * args.steps
+                                     / ((ms + ms_p) * 1e-3) / 1e12),
+            }
         if refresh_steps:
             extra["refresh_ms_each"] = phases["refresh"][0] / len(refresh_steps)
             # algorithmic flops of one refresh: p (8 m n r + (8/3)(m^3 + n^3)) per matrix
@@ -370,6 +411,7 @@ def main(argv=None):
                    "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
                    "rotated_momentum": bool(args.rotated_momentum),
                    "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
+                   "fp32_momentum_rotation": bool(args.fp32_momentum_rotation),
                    **({"ns_iters": args.ns_iters} if args.muon else {})},
         "steps_per_s": steps_per_s,
         "roofline": roofline,

@@ -129,7 +129,17 @@ enum {
      * W <- W - lr O. v, U, V are unused (may be NULL), as are beta2, eps, K
      * and power_iters; refresh_basis, health and reorthonormalize return
      * OPT_EUNSUPPORTED. Cannot be combined with the other flags. */
-    OPT_FLAG_MUON = 4u
+    OPT_FLAG_MUON = 4u,
+    /* By default the fp32 rotations of a bf16 momentum (m and n multiples of
+     * 8, M 16-byte aligned, no other flag) run the product of M's chain with
+     * the larger flop count, U^T M when m > n and M V otherwise, on bf16
+     * MFMAs: the fp32 basis is split into three bf16 pieces hi = rb(x),
+     * mid = rb(x - hi), lo = x - hi - mid that sum to it exactly, and the
+     * three products with the (exactly bf16) M accumulate in one fp32 chain,
+     * so the result differs from an fp32 product by accumulation order only.
+     * The pieces of U^T or V^T (6 d^2 bytes per matrix, d = m or n) are made
+     * with the U^T copy. This flag keeps every rotation on fp32 MFMAs. */
+    OPT_FLAG_FP32_MOMENTUM_ROTATION = 8u
 };
 
 typedef struct {
@@ -232,7 +242,8 @@ enum {
     OPT_PHASE_BACK_LEFT = 5,  /* U u                          (grouped GEMM) */
     OPT_PHASE_BACK_RIGHT = 6, /* W -= lr (U u) V^T            (grouped GEMM + apply) */
     OPT_PHASE_ORTHO = 7,      /* OPT_FLAG_MUON: norm, Newton-Schulz products and combines, apply */
-    OPT_NUM_PHASES = 8
+    OPT_PHASE_ROT_PIECED = 8, /* bf16 M's pieced product (U^T M or M V) and the M^T it reads */
+    OPT_NUM_PHASES = 9
 };
 /* enable != 0 starts recording (and clears the totals); 0 stops. */
 opt_status opt_group_set_timing(opt_group_t g, int32_t enable);

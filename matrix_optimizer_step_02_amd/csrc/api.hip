@@ -68,6 +68,13 @@ struct Mat {
     uint16_t *Ub = nullptr, *Utb = nullptr, *Vb = nullptr, *Vtb = nullptr;
     // fp32 rotations: U^T (m x m), so that U^T [G | M] reads k-contiguous rows
     float* Ut = nullptr;
+    // fp32 rotations of a bf16 M (m, n multiples of 8): the product of M's
+    // rotation chain with the larger flop count runs as three bf16 products
+    // against exact bf16 pieces of the basis. Tall (m > n): U^T M with the
+    // pieces of U^T; otherwise M V with the pieces of V^T. Bp holds the three
+    // pieces of that transposed basis (d x d each, d = m or n).
+    uint16_t* Bp = nullptr;
+    bool tall = false;
 };
 
 // Byte offsets into the table image (host) / table region (device).
@@ -116,6 +123,11 @@ struct Group {
     std::vector<int> mats;   // indices into opt_group_s::mats, LPT order
     EwLaunch mom, adam;
     std::vector<GemmLaunch> rot_left, rot_right, back_left, back_right;
+    // M's pieced bf16 products (matrices with Bp), and the M^T copies that
+    // the tall ones read
+    std::vector<Gemm16Launch> rot_m16;
+    uint64_t mt_split = 0;
+    int mt_nsplit = 0, mt_tiles = 0;
     // with the carried rotated momentum: the step that recomputes m~ = U^T M V
     // into Mt (rot_left as above), and the step that carries it (G only)
     std::vector<GemmLaunch> rot_right_re, rot_left_c, rot_right_c;
@@ -206,6 +218,8 @@ struct opt_group_s {
     int basis_njobs = 0, basis_tiles = 0;
     uint64_t transpose_jobs = 0;
     int transpose_njobs = 0, transpose_tiles = 0;
+    uint64_t pieces_jobs = 0;   // bf16 pieces of U^T or V^T (Mat::Bp)
+    int pieces_njobs = 0, pieces_tiles = 0;
     bool copies_valid = false;
     // state checks: one scan over every matrix (partials at the start of the
     // scratch), per-matrix records in the table region
@@ -239,7 +253,8 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (!std::isfinite(hp->lr)) return fail(OPT_EINVAL, "lr must be finite");
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
-    if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON))
+    if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
+                                OPT_FLAG_FP32_MOMENTUM_ROTATION))
         return fail(OPT_EINVAL, "unknown bits in flags");
     if ((hp->flags & OPT_FLAG_MUON) && hp->flags != OPT_FLAG_MUON)
         return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON cannot be combined with other flags");
@@ -371,6 +386,9 @@ int choose_cfg(const std::vector<GemmProb>& probs) {
     return tiles_of(probs, 1) >= kGemmLargeMinTiles ? 1 : 0;
 }
 
+// Period of a pieced product's k range: K rounded up to whole 64-deep slabs.
+int32_t kper16(int64_t K) { return (int32_t)std::max<int64_t>(64, (K + 63) / 64 * 64); }
+
 // bf16 NT products (C = alpha A B^T + beta C, k contiguous in both operands).
 Gemm16Prob g16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
                int64_t N, int64_t K, float alpha, float beta, int64_t pad_n) {
@@ -384,9 +402,22 @@ Gemm16Prob g16(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, 
     p.M = (int32_t)M;
     p.N = (int32_t)N;
     p.K = (int32_t)K;
+    p.np = 1;
+    p.kper = kper16(K);
     p.pad_n = (int32_t)pad_n;
     p.alpha = alpha;
     p.beta = beta;
+    return p;
+}
+
+// The sum over three pieces of one operand (hi, mid, lo of an fp32 matrix,
+// `ps` elements apart) against the same other operand, in one accumulation
+// chain: A = pieces (a_pieces) or B = pieces.
+Gemm16Prob g16_pieced(const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc, int64_t M,
+                      int64_t N, int64_t K, bool a_pieces, int64_t ps) {
+    Gemm16Prob p = g16(A, lda, B, ldb, C, ldc, M, N, K, 1.f, 0.f, N);
+    p.np = 3;
+    (a_pieces ? p.a_ps : p.b_ps) = ps;
     return p;
 }
 
@@ -481,7 +512,8 @@ Gemm16Launch put_gemm16(Image& img, std::vector<Gemm16Prob> probs, bool out16) {
                                [](const Gemm16Prob& p) { return p.M <= 0 || std::max(p.N, p.pad_n) <= 0; }),
                 probs.end());
     if (probs.empty()) return L;
-    std::stable_sort(probs.begin(), probs.end(), [](const Gemm16Prob& a, const Gemm16Prob& b) { return a.K > b.K; });
+    std::stable_sort(probs.begin(), probs.end(),
+                     [](const Gemm16Prob& a, const Gemm16Prob& b) { return a.np * a.K > b.np * b.K; });
     L.cfg = choose_cfg16(probs);
     std::vector<int32_t> tb;
     int total = 0;
@@ -552,6 +584,7 @@ size_t add_k_chunked16(std::vector<std::vector<Gemm16Prob>>& steps, size_t next,
         c.A = g.A + k0;
         c.B = g.B + k0;
         c.K = (int32_t)std::min<int64_t>(kChunkK16, g.K - k0);
+        c.kper = kper16(c.K);
         if (k0) c.beta = 1.f;
         steps[next].push_back(c);
     }
@@ -738,6 +771,16 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
     return out;
 }
 
+// Matrices whose momentum rotation takes the pieced bf16 product: fp32
+// rotations without the carried rotated momentum, a bf16 M that the bf16
+// GEMM reads directly (16-byte aligned), and m, n multiples of 8 (rows of M,
+// M^T and the pieces are whole 16-byte groups).
+bool pieced_eligible(const opt_group_s* g, const Mat& M) {
+    const uint32_t off = OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
+                         OPT_FLAG_FP32_MOMENTUM_ROTATION;
+    return !(g->hp.flags & off) && M.bf16 && M.d.m % 8 == 0 && M.d.n % 8 == 0 && aligned(M.d.M, 16);
+}
+
 // Build every table of the group object. `region` is the device address of
 // the workspace past the tables (any value when only sizes are wanted): the
 // bf16 bases (bf16-rotation variant only), then the scratch.
@@ -797,6 +840,33 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->transpose_njobs = (int)tj.size();
         g->transpose_tiles = tiles;
         g->transpose_jobs = g->img.put(tj);
+        std::vector<SplitJob> pj;
+        int ptiles = 0;
+        for (Mat& M : g->mats) {
+            M.Bp = nullptr;
+            if (!pieced_eligible(g, M)) continue;
+            const int64_t m = M.d.m, n = M.d.n;
+            M.tall = m > n;
+            const int64_t d = M.tall ? m : n;
+            M.Bp = (uint16_t*)(region + g->bases_bytes);
+            g->bases_bytes += align_up(6ull * d * d);
+            // piece p of X^T: Bp[p d^2 + c d + k] = piece_p(X[k][c])
+            SplitJob j{};
+            j.src = M.tall ? M.d.U : M.d.V;
+            j.dst = M.Bp;
+            j.ld_src = d;
+            j.ld_dst = d;
+            j.piece_stride = d * d;
+            j.rows = j.cols = (int32_t)d;
+            j.npieces = 3;
+            j.src_bf16 = 0;
+            j.tile_begin = ptiles;
+            ptiles += (int)(((d + 31) / 32) * ((d + 31) / 32));
+            pj.push_back(j);
+        }
+        g->pieces_njobs = (int)pj.size();
+        g->pieces_tiles = ptiles;
+        g->pieces_jobs = g->img.put(pj);
     }
     char* scratch = region + g->bases_bytes;
     for (const std::vector<int>& members : plan) {
@@ -862,6 +932,9 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         // ---- rotation scratch
         std::vector<PGemm> left, right, bl, br, right_re, left_c, right_c;
         std::vector<EwSeg> mom, adam, adam_re, adam_c;
+        std::vector<Gemm16Prob> m16;
+        std::vector<SplitJob> mts;
+        int mt_tiles = 0;
         uint64_t off = 0;
         for (int mi : members) {
             const Mat& M = g->mats[mi];
@@ -875,10 +948,33 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             const bool at = !M.Ut;
             const float* UA = M.Ut ? M.Ut : x.U;
             left.push_back(mk(at, false, UA, false, m, x.G, false, n, TG, n, m, n, m, 1.f, 0.f));
-            left.push_back(mk(at, false, UA, false, m, x.M, M.bf16, n, TM, n, m, n, m, 1.f, 0.f));
-            // (U^T G) V, (U^T M) V
             right.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
-            right.push_back(mk(false, false, TM, false, n, x.V, false, n, mt, n, m, n, n, 1.f, 0.f));
+            if (M.Bp && M.tall) {
+                // U^T M = sum_p piece_p(U^T) M: B = M^T (bf16, n x m) in the G~ slot,
+                // consumed before (U^T G) V overwrites it; then (U^T M) V
+                SplitJob j{};
+                j.src = x.M;
+                j.dst = (uint16_t*)Gt;
+                j.ld_src = n;
+                j.ld_dst = m;
+                j.rows = (int32_t)m;
+                j.cols = (int32_t)n;
+                j.npieces = 1;
+                j.src_bf16 = 1;
+                j.tile_begin = mt_tiles;
+                mt_tiles += (int)(((m + 31) / 32) * ((n + 31) / 32));
+                mts.push_back(j);
+                m16.push_back(g16_pieced(M.Bp, m, Gt, m, TM, n, m, n, m, true, m * m));
+                right.push_back(mk(false, false, TM, false, n, x.V, false, n, mt, n, m, n, n, 1.f, 0.f));
+            } else if (M.Bp) {
+                // M V = sum_p M piece_p(V^T)^T into the U^T M slot, then U^T (M V)
+                m16.push_back(g16_pieced(x.M, n, M.Bp, n, TM, n, m, n, n, false, n * n));
+                left.push_back(mk(at, false, UA, false, m, TM, false, n, mt, n, m, n, m, 1.f, 0.f));
+            } else {
+                // U^T M, then (U^T M) V
+                left.push_back(mk(at, false, UA, false, m, x.M, M.bf16, n, TM, n, m, n, m, 1.f, 0.f));
+                right.push_back(mk(false, false, TM, false, n, x.V, false, n, mt, n, m, n, n, 1.f, 0.f));
+            }
             // U u (u in the m~ slot) -> TG slot
             bl.push_back(mk(false, false, x.U, false, m, mt, false, n, TG, n, m, n, m, 1.f, 0.f));
             // W += (-1 * lr) (U u) V^T  (B = V stored n x n read transposed)
@@ -1025,6 +1121,12 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         }
         G.rot_left = put_gemm(g->img, left);
         G.rot_right = put_gemm(g->img, right);
+        if (!m16.empty()) {
+            G.rot_m16.push_back(put_gemm16(g->img, m16, false));
+            G.mt_nsplit = (int)mts.size();
+            G.mt_tiles = mt_tiles;
+            G.mt_split = g->img.put(mts);
+        }
         G.back_left = put_gemm(g->img, bl);
         G.back_right = put_gemm(g->img, br);
         G.mom = put_ew(g->img, mom);
@@ -1633,7 +1735,10 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
         if ((e = launch_transpose32(dptr<TransposeJob>(g, g->transpose_jobs), g->transpose_njobs,
                                     g->transpose_tiles, s)))
             return hip_fail(e, "basis transpose launch");
-        g->kernels_in_scope += 1;
+        if (g->pieces_njobs &&
+            (e = launch_split16(dptr<SplitJob>(g, g->pieces_jobs), g->pieces_njobs, g->pieces_tiles, s)))
+            return hip_fail(e, "basis pieces launch");
+        g->kernels_in_scope += 1 + (g->pieces_njobs > 0);
         g->copies_valid = true;
     }
     // with the carried rotated momentum: recompute m~ when the bases are new
@@ -1641,6 +1746,15 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
     const bool carry = carry_mode && g->mt_valid && !refresh;
     for (const Group& G : g->groups) {
+        if (!G.rot_m16.empty()) {
+            PhaseScope ps(g, OPT_PHASE_ROT_PIECED, s);
+            if (G.mt_nsplit) {
+                if ((e = launch_split16(dptr<SplitJob>(g, G.mt_split), G.mt_nsplit, G.mt_tiles, s)))
+                    return hip_fail(e, "momentum transpose launch");
+                g->kernels_in_scope += 1;
+            }
+            if ((e = run_gemm16(g, G.rot_m16, 1.f, s))) return hip_fail(e, "rotation launch");
+        }
         {
             PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
             if ((e = run_gemm(g, carry ? G.rot_left_c : G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");

@@ -264,9 +264,16 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     // ring buffer b of A at smem + b AB, of B at smem + ST AB + b BB
     auto abuf = [&](int b) { return smem + b * C::AB; };
     auto bbuf = [&](int b) { return smem + C::ST * C::AB + b * C::BB; };
+    // slab k0 of the concatenated range lies in period q at kk = k0 - q kper
+    // (kper is a multiple of the slab depth); past the last period every
+    // load reads the zero block
     auto fill = [&](int b, int k0) {
-        dma16<C, C::BM>(abuf(b), p.A, p.lda, p.M, p.K, m0, k0);
-        dma16<C, C::BN>(bbuf(b), p.B, p.ldb, p.N, p.K, n0, k0);
+        int q = k0 / p.kper;
+        const int kk = k0 - q * p.kper;
+        const int kv = q < p.np ? p.K : 0;
+        q = min(q, p.np - 1);
+        dma16<C, C::BM>(abuf(b), p.A + q * p.a_ps, p.lda, p.M, kv, m0, kk);
+        dma16<C, C::BN>(bbuf(b), p.B + q * p.b_ps, p.ldb, p.N, kv, n0, kk);
     };
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
@@ -275,7 +282,7 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int nk = (p.K + C::BK - 1) / C::BK;
+    const int nk = p.np == 1 ? (p.K + C::BK - 1) / C::BK : p.np * (p.kper / C::BK);
     const float alpha = p.alpha * alpha_scale;
     if (nk == 0) {
         epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);

@@ -15,12 +15,22 @@ namespace matopt {
 // k is one 16-byte load). C is fp32 (ldc) or, for c_bf16 launches, bf16
 // rounded to nearest even with beta = 0; a bf16 C also gets zeros in columns
 // [N, pad_n) of each row (the zero k padding of a later product's operand).
+//
+// Pieced products. The k range can be a sum of `np` periods: the product is
+// sum_{q < np} A_q B_q^T with A_q = A + q a_ps and B_q = B + q b_ps (element
+// offsets), each over the same K. An operand with a piece stride of 0 is
+// read again in every period. This is how an fp32 operand split into three
+// exact bf16 pieces (hi, mid, lo) meets a bf16 operand in one accumulation
+// chain. Each period starts on a 64-aligned slab (kper = K rounded up to 64);
+// np = 1 with zero piece strides is the plain product.
 struct Gemm16Prob {
     const uint16_t* A;
     const uint16_t* B;
     void* C;
     int64_t lda, ldb, ldc;
+    int64_t a_ps, b_ps;
     int32_t M, N, K;
+    int32_t np, kper;
     int32_t pad_n;
     float alpha, beta;
     int32_t tiles_m, tiles_n;

@@ -19,8 +19,9 @@ OPT_F32, OPT_BF16 = 0, 1
 OPT_FLAG_ROTATED_MOMENTUM = 1
 OPT_FLAG_BF16_ROTATION = 2
 OPT_FLAG_MUON = 4
+OPT_FLAG_FP32_MOMENTUM_ROTATION = 8
 OPT_MAX_DIM = 16384
-PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho")
+PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho", "rot_pieced")
 OPT_NUM_PHASES = len(PHASES)
 
 EXPORTED = (

@@ -159,6 +159,26 @@ def test_workspace_holds_the_copies_of_the_bases(N):
     assert var < base - ut + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
 
 
+def test_workspace_holds_the_pieces_of_the_momentum_bases(N):
+    """A bf16 M with both sides multiples of 8 gets the three bf16 pieces of
+    U^T (m > n) or V^T (m <= n), 6 d^2 bytes (256-byte aligned), beside the
+    fp32 U^T copy (and a few work-list entries); fp32 M, ragged sides, and
+    the flag that keeps the rotations on fp32 MFMAs add nothing."""
+    shapes = [(200, 72), (72, 264), (136, 136), (130, 67), (8, 8)]
+    a256 = lambda x: (x + 255) // 256 * 256
+    bf = descs(N, shapes, dtype=N.OPT_BF16)
+    pieced = N.opt_group_workspace_size(bf, hp(N))
+    plain = N.opt_group_workspace_size(bf, hp(N, flags=N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+    f32 = descs(N, shapes)
+    pieces = sum(a256(6 * max(m, n) ** 2) for m, n in shapes if m % 8 == 0 and n % 8 == 0)
+    assert 0 <= pieced - plain - pieces < 16 * 1024    # plus the work lists of the new launches
+    assert N.opt_group_workspace_size(f32, hp(N)) == \
+        N.opt_group_workspace_size(f32, hp(N, flags=N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+    for other in (N.OPT_FLAG_ROTATED_MOMENTUM, N.OPT_FLAG_BF16_ROTATION):
+        assert N.opt_group_workspace_size(bf, hp(N, flags=other)) == \
+            N.opt_group_workspace_size(bf, hp(N, flags=other | N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+
+
 def test_rejects_bad_shapes_and_dtypes(N):
     assert err(N, N.opt_group_workspace_size, descs(N, [(0, 4)]), hp(N)) == N.OPT_EINVAL
     assert err(N, N.opt_group_workspace_size, descs(N, [(4, -1)]), hp(N)) == N.OPT_EINVAL
