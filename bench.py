@@ -34,6 +34,8 @@ if ROOT not in sys.path:
 MI355X_FP32_MFMA_TFLOPS = 157.3
 MI355X_BF16_MFMA_TFLOPS = 2500.0   # dense bf16 MFMA (no sparsity)
 MI355X_HBM_GBPS = 8000.0
+# ceiling of an fp32 product done as six bf16 MFMA products (three-piece split)
+X6_FP32_EQUIV_TFLOPS = MI355X_BF16_MFMA_TFLOPS / 6
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
 # the kernel's sources and the schedule that decides what each launch holds
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/gemm.h",
@@ -231,8 +233,8 @@ def main(argv=None):
     ap.add_argument("--muon", action="store_true",
                     help="the orthogonalised-momentum step (Newton-Schulz polar factor of M) instead")
     ap.add_argument("--ns-iters", type=int, default=5, help="Newton-Schulz iterations of --muon")
-    ap.add_argument("--fp32-momentum-rotation", action="store_true",
-                    help="keep a bf16 momentum's rotation on fp32 MFMAs (no pieced bf16 products)")
+    ap.add_argument("--fp32-mfma", action="store_true",
+                    help="keep the fp32 products on fp32 MFMAs (no bf16-piece products)")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -284,7 +286,7 @@ def main(argv=None):
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
                   int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum,
                   bf16_rotation=args.bf16_rotation, muon=args.muon, ns_iters=args.ns_iters if args.muon else 0,
-                  fp32_momentum_rotation=args.fp32_momentum_rotation)
+                  fp32_mfma=args.fp32_mfma)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     torch.cuda.synchronize()
@@ -332,7 +334,7 @@ def main(argv=None):
         extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
         extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
     elif phases:
-        plain = not (args.rotated_momentum or args.bf16_rotation or args.fp32_momentum_rotation)
+        plain = not (args.rotated_momentum or args.bf16_rotation or args.fp32_mfma)
         pf_all = phase_flops(shapes, m_dtype=wl.m_dtype, plain_fp32=plain)
         # the roofline is the dominant kernel's: the pieced bf16 products are reported beside it
         pf = {k: v for k, v in pf_all.items() if k != "rot_pieced"}
@@ -343,12 +345,16 @@ def main(argv=None):
         ms = sum(phases[k][0] for k in pf)
         launches = sum(phases[k][1] for k in pf)
         achieved = flops / (ms * 1e-3) / 1e12 if ms > 0 else None
-        peak = MI355X_BF16_MFMA_TFLOPS if args.bf16_rotation else MI355X_FP32_MFMA_TFLOPS
+        x6 = not (args.bf16_rotation or args.fp32_mfma)
+        peak = (MI355X_BF16_MFMA_TFLOPS if args.bf16_rotation else
+                X6_FP32_EQUIV_TFLOPS if x6 else MI355X_FP32_MFMA_TFLOPS)
         kernel = ("gemm16_kernel (bf16 rotation phases: (X V)^T, U^T S^T, (u V^T)^T, W -= lr U P^T)"
                   if args.bf16_rotation else
-                  "gemm_grouped_kernel (fp32 rotation phases: U^T G, (U^T G) V, the fp32 product of M's "
-                  "chain, U u, W -= lr (.)V^T)" if "rot_pieced" in pf_all else
-                  "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)")
+                  "gemm_grouped_kernel (fp32 rotation phases on bf16 MFMAs, six piece products: U^T G, "
+                  "(U^T G) V, the other product of M's chain, U u, W -= lr (.)V^T)" if "rot_pieced" in pf_all else
+                  ("gemm_grouped_kernel (rotation phases on bf16 MFMAs, six piece products: U^T[G|M], (.)V, "
+                   "U u, W -= lr (.)V^T)" if x6 else
+                   "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)"))
         roofline = {
             "bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
             "frac": achieved / peak if achieved else None,
@@ -356,6 +362,9 @@ def main(argv=None):
             "kernel": kernel,
             "launches": launches, "avg_launch_ms": ms / max(launches, 1),
             "flops_per_launch": flops / max(launches, 1),
+            **({"peak_basis": "fp32-equivalent ceiling of six bf16 MFMA products per fp32 product "
+                              "(2.5 PFLOP/s dense bf16 / 6)",
+                "frac_of_fp32_mfma_peak": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None} if x6 else {}),
         }
         eb = elementwise_bytes(shapes, wl.m_dtype)
         extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
@@ -411,7 +420,7 @@ def main(argv=None):
                    "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
                    "rotated_momentum": bool(args.rotated_momentum),
                    "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
-                   "fp32_momentum_rotation": bool(args.fp32_momentum_rotation),
+                   "fp32_mfma": bool(args.fp32_mfma),
                    **({"ns_iters": args.ns_iters} if args.muon else {})},
         "steps_per_s": steps_per_s,
         "roofline": roofline,

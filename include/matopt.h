@@ -130,16 +130,22 @@ enum {
      * and power_iters; refresh_basis, health and reorthonormalize return
      * OPT_EUNSUPPORTED. Cannot be combined with the other flags. */
     OPT_FLAG_MUON = 4u,
-    /* By default the fp32 rotations of a bf16 momentum (m and n multiples of
-     * 8, M 16-byte aligned, no other flag) run the product of M's chain with
-     * the larger flop count, U^T M when m > n and M V otherwise, on bf16
-     * MFMAs: the fp32 basis is split into three bf16 pieces hi = rb(x),
-     * mid = rb(x - hi), lo = x - hi - mid that sum to it exactly, and the
-     * three products with the (exactly bf16) M accumulate in one fp32 chain,
-     * so the result differs from an fp32 product by accumulation order only.
-     * The pieces of U^T or V^T (6 d^2 bytes per matrix, d = m or n) are made
-     * with the U^T copy. This flag keeps every rotation on fp32 MFMAs. */
-    OPT_FLAG_FP32_MOMENTUM_ROTATION = 8u
+    /* By default the fp32 products of the rotations and of the refresh run on
+     * bf16 MFMAs (2.5 PFLOP/s dense against 157 TFLOP/s for fp32), at fp32
+     * accuracy:
+     *  - every fp32 operand value splits exactly into three bf16 pieces
+     *    hi = rb(x), mid = rb(x - hi), lo = x - hi - mid in registers, and the
+     *    six piece products that matter (hi hi, hi mid, mid hi, hi lo, mid mid,
+     *    lo hi) accumulate in fp32; the three left out are below 2^-23 of the
+     *    product, about one fp32 rounding (the bf16x6 scheme of Henry, Tang
+     *    and Heinecke, ARITH 2019);
+     *  - a bf16 momentum (m and n multiples of 8, M 16-byte aligned, no
+     *    other flag) is exactly bf16, so the product of M's chain with the
+     *    larger flop count (U^T M when m > n, M V otherwise) needs only three
+     *    products, against stored pieces of U^T or V^T (6 d^2 bytes per
+     *    matrix, d = m or n, made with the U^T copy), in one fp32 chain.
+     * This flag keeps every one of these products on fp32 MFMAs. */
+    OPT_FLAG_FP32_MFMA = 8u
 };
 
 typedef struct {
@@ -271,6 +277,18 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
                     float alpha, const void* A, int32_t a_dtype, int64_t lda,
                     const void* B, int32_t b_dtype, int64_t ldb,
                     float beta, float* C, int64_t ldc, void* stream);
+
+/* opt_gemm on bf16 MFMAs at fp32 accuracy (the bf16x6 scheme of Henry, Tang
+ * and Heinecke, ARITH 2019, as the step uses it by default): each fp32
+ * operand value splits exactly into three bf16 pieces, the six piece products
+ * that matter accumulate in fp32, and the ones left out are below 2^-23 of
+ * each product. Same arguments as opt_gemm; the supported layouts are
+ * (trans_a, trans_b, a_dtype, b_dtype) = (0, 0, F32, F32), (1, 0, F32, F32),
+ * (0, 1, F32, F32) and (0, 0, F32, BF16); others return OPT_EUNSUPPORTED. */
+opt_status opt_gemm_x6(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void* A, int32_t a_dtype, int64_t lda,
+                       const void* B, int32_t b_dtype, int64_t ldb,
+                       float beta, float* C, int64_t ldc, void* stream);
 
 /* C = alpha * A B^T + beta * C with bfloat16 operands and fp32 accumulation
  * (the product of the bf16-rotation variant, section 3.1 of the pipeline-

@@ -31,13 +31,13 @@ class Hyper:
     bf16_rotation: bool = False       # rotations on bf16 operands (fp32 accumulation) from the second step
     muon: bool = False                # orthogonalised-momentum step instead (no v, U, V)
     ns_iters: int = 0                 # Newton-Schulz iterations of the muon step (>= 1 there)
-    fp32_momentum_rotation: bool = False  # no pieced bf16 products for a bf16 M's rotation
+    fp32_mfma: bool = False           # keep the fp32 products on fp32 MFMAs (no bf16-piece products)
 
     def c(self) -> native.opt_hparams:
         flags = (native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0) | \
                 (native.OPT_FLAG_BF16_ROTATION if self.bf16_rotation else 0) | \
                 (native.OPT_FLAG_MUON if self.muon else 0) | \
-                (native.OPT_FLAG_FP32_MOMENTUM_ROTATION if self.fp32_momentum_rotation else 0)
+                (native.OPT_FLAG_FP32_MFMA if self.fp32_mfma else 0)
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,
                                   self.power_iters, self.capacity_bytes,
                                   self.refresh_capacity_bytes, flags, self.ns_iters)

@@ -254,7 +254,7 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
     if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
-                                OPT_FLAG_FP32_MOMENTUM_ROTATION))
+                                OPT_FLAG_FP32_MFMA))
         return fail(OPT_EINVAL, "unknown bits in flags");
     if ((hp->flags & OPT_FLAG_MUON) && hp->flags != OPT_FLAG_MUON)
         return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON cannot be combined with other flags");
@@ -460,7 +460,8 @@ PGemm mk(bool at, bool bt, const void* A, bool a_bf16, int64_t lda, const void* 
 }
 
 // One grouped launch per operand variant present in the phase.
-std::vector<GemmLaunch> put_gemm(Image& img, const std::vector<PGemm>& all) {
+// x6: launches of a variant that has the bf16-piece mode run in it.
+std::vector<GemmLaunch> put_gemm(Image& img, const std::vector<PGemm>& all, bool x6 = false) {
     std::vector<GemmLaunch> out;
     for (int v = 0; v < 16; ++v) {
         std::vector<GemmProb> probs;
@@ -479,7 +480,7 @@ std::vector<GemmLaunch> put_gemm(Image& img, const std::vector<PGemm>& all) {
             total += p.tiles_m * p.tiles_n;
         }
         GemmLaunch L;
-        L.variant = v;
+        L.variant = v | (x6 && gemm_x6_available(v) ? GV_X6 : 0);
         L.cfg = cfg;
         L.nprob = (int)probs.size();
         L.total_tiles = total;
@@ -777,7 +778,7 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
 // M^T and the pieces are whole 16-byte groups).
 bool pieced_eligible(const opt_group_s* g, const Mat& M) {
     const uint32_t off = OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
-                         OPT_FLAG_FP32_MOMENTUM_ROTATION;
+                         OPT_FLAG_FP32_MFMA;
     return !(g->hp.flags & off) && M.bf16 && M.d.m % 8 == 0 && M.d.n % 8 == 0 && aligned(M.d.M, 16);
 }
 
@@ -1119,22 +1120,23 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             }
             G.rot_bytes = std::max(G.rot_bytes, o);
         }
-        G.rot_left = put_gemm(g->img, left);
-        G.rot_right = put_gemm(g->img, right);
+        const bool x6 = !(g->hp.flags & OPT_FLAG_FP32_MFMA);
+        G.rot_left = put_gemm(g->img, left, x6);
+        G.rot_right = put_gemm(g->img, right, x6);
         if (!m16.empty()) {
             G.rot_m16.push_back(put_gemm16(g->img, m16, false));
             G.mt_nsplit = (int)mts.size();
             G.mt_tiles = mt_tiles;
             G.mt_split = g->img.put(mts);
         }
-        G.back_left = put_gemm(g->img, bl);
-        G.back_right = put_gemm(g->img, br);
+        G.back_left = put_gemm(g->img, bl, x6);
+        G.back_right = put_gemm(g->img, br, x6);
         G.mom = put_ew(g->img, mom);
         G.adam = put_ew(g->img, adam);
         if (!adam_c.empty()) {
-            G.rot_right_re = put_gemm(g->img, right_re);
-            G.rot_left_c = put_gemm(g->img, left_c);
-            G.rot_right_c = put_gemm(g->img, right_c);
+            G.rot_right_re = put_gemm(g->img, right_re, x6);
+            G.rot_left_c = put_gemm(g->img, left_c, x6);
+            G.rot_right_c = put_gemm(g->img, right_c, x6);
             G.adam_re = put_ew(g->img, adam_re);
             G.adam_c = put_ew(g->img, adam_c);
         }
@@ -1142,6 +1144,8 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         g->groups.push_back(std::move(G));
     }
 
+    // the refresh's Gram products and QR block updates on bf16 MFMAs too
+    const bool rx6 = !(g->hp.flags & OPT_FLAG_FP32_MFMA);
     for (const std::vector<int>& members : muon ? std::vector<std::vector<int>>{} : plan_refresh(g, plan)) {
         RefreshBatch R;
         R.mats = members;
@@ -1233,8 +1237,8 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             std::vector<std::vector<PGemm>> s1, s2;
             for (const PGemm& x : p1) add_k_chunked(s1, x);
             for (const PGemm& x : p2) add_k_chunked(s2, x);
-            for (const std::vector<PGemm>& st : s1) R.prod1.push_back(put_gemm(g->img, st));
-            for (const std::vector<PGemm>& st : s2) R.prod2.push_back(put_gemm(g->img, st));
+            for (const std::vector<PGemm>& st : s1) R.prod1.push_back(put_gemm(g->img, st, rx6));
+            for (const std::vector<PGemm>& st : s2) R.prod2.push_back(put_gemm(g->img, st, rx6));
             if (!sj1.empty()) {
                 R.nsplit1 = (int)sj1.size();
                 R.nsplit2 = (int)sj2.size();
@@ -1259,7 +1263,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                                  std::vector<std::vector<std::vector<GemmLaunch>>>& out) {
                 out.resize(in.size());
                 for (size_t b = 0; b < in.size(); ++b)
-                    for (const std::vector<PGemm>& step : in[b]) out[b].push_back(put_gemm(g->img, step));
+                    for (const std::vector<PGemm>& step : in[b]) out[b].push_back(put_gemm(g->img, step, rx6));
             };
             put_steps(st.fact, R.qr.fact);
             put_steps(st.qform, R.qr.qform);
@@ -1922,9 +1926,10 @@ void opt_group_destroy(opt_group_t g) {
 
 // ------------------------------------------------------- building blocks ----
 
-opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, float alpha,
-                    const void* A, int32_t a_dtype, int64_t lda, const void* B, int32_t b_dtype,
-                    int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+namespace {
+opt_status gemm_entry(bool x6, int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                      const void* A, int32_t a_dtype, int64_t lda, const void* B, int32_t b_dtype, int64_t ldb,
+                      float beta, float* C, int64_t ldc, void* stream) {
     if (M < 0 || N < 0 || K < 0) return fail(OPT_EINVAL, "negative dimension");
     if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2)
         return fail(OPT_EUNSUPPORTED, "dimension too large");
@@ -1940,14 +1945,31 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
     }
     const PGemm pg = mk(trans_a != 0, trans_b != 0, A, a_dtype == OPT_BF16, lda, B, b_dtype == OPT_BF16, ldb,
                         C, ldc, M, N, K, alpha, beta);
+    if (x6 && !gemm_x6_available(pg.variant))
+        return fail(OPT_EUNSUPPORTED, "no bf16-piece product for this operand layout and dtype combination");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before gemm");
     GemmProb single = pg.p;
     const int cfg = choose_cfg({single});
     set_tiles(single, cfg);
-    e = launch_gemm_single(pg.variant, cfg, single, (hipStream_t)stream);
+    e = launch_gemm_single(pg.variant | (x6 ? GV_X6 : 0), cfg, single, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "gemm launch");
     return OPT_OK;
+}
+}  // namespace
+
+opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                    const void* A, int32_t a_dtype, int64_t lda, const void* B, int32_t b_dtype,
+                    int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    return gemm_entry(false, trans_a, trans_b, M, N, K, alpha, A, a_dtype, lda, B, b_dtype, ldb, beta, C, ldc,
+                      stream);
+}
+
+opt_status opt_gemm_x6(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int32_t a_dtype, int64_t lda, const void* B, int32_t b_dtype,
+                       int64_t ldb, float beta, float* C, int64_t ldc, void* stream) {
+    return gemm_entry(true, trans_a, trans_b, M, N, K, alpha, A, a_dtype, lda, B, b_dtype, ldb, beta, C, ldc,
+                      stream);
 }
 
 opt_status opt_gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,

@@ -49,6 +49,7 @@ namespace matopt {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 namespace {
 
@@ -409,6 +410,62 @@ __device__ __forceinline__ void mma_slab(const float* As, const float* Bs, int w
     }
 }
 
+// ---- fp32 products on bf16 MFMAs (X6 mode) ----
+//
+// An fp32 value x splits into three bf16 values hi = rb(x), mid = rb(x - hi),
+// lo = rb(x - hi - mid) (rb: round to nearest even). Both residuals are exact
+// in fp32, and the last has at most 8 significant bits, so hi + mid + lo = x
+// exactly for finite x. A product a b is then the sum of the nine piece
+// products; the six kept here (hi hi, hi mid, mid hi, hi lo, mid mid, lo hi)
+// leave out terms below 2^-23 |a b| in all, about one fp32 rounding of the
+// product, and every piece product is exact in the fp32 accumulator. So one
+// k step of 16 on v_mfma_f32_32x32x16_bf16 (six MFMAs per 32 x 32 block) does
+// the work of eight v_mfma_f32_32x32x2_f32 at fp32 accuracy; the matrix
+// cores' bf16 rate being 16 times the fp32 one, it takes 6/16 of the time at
+// peak.
+//
+// The operands stay fp32 in LDS (the same layouts and fills as the fp32
+// path); a k step takes the fragments of two consecutive groups of 8 k
+// values, and lane l's element e (0..7) of a bf16 fragment is the value of k
+// 8 (g + e/4) + 4 (l/32) + e%4: the same assignment for both operands, so the
+// sum over the step's 16 k values is unchanged.
+struct Pieces {
+    bf16x8 hi, mid, lo;
+};
+
+__device__ __forceinline__ Pieces split8(const f32x4& x0, const f32x4& x1) {
+    Pieces p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const __bf16 h = (__bf16)x;
+        const float r1 = x - (float)h;
+        const __bf16 m = (__bf16)r1;
+        const float r2 = r1 - (float)m;
+        p.hi[e] = h;
+        p.mid[e] = m;
+        p.lo[e] = (__bf16)r2;
+    }
+    return p;
+}
+
+// One k step of 16 for the blocks of A row block i: the six piece products,
+// smallest first.
+template <class C>
+__device__ __forceinline__ void mma6_row(const Pieces& a, const Pieces (&b)[C::TN], f32x16 (&acc)[C::TN]) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+        f32x16 c = acc[j];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.lo, b[j].hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].mid, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].lo, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].hi, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].mid, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].hi, c, 0, 0, 0);
+        acc[j] = c;
+    }
+}
+
 // Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32 of its 32x32 block: 32 lanes store 128 contiguous bytes.
 // With beta != 0 the old values of one row of blocks are all loaded before
@@ -449,7 +506,41 @@ __device__ __forceinline__ void epilogue(const GemmProb& p, int m0, int n0, int 
     }
 }
 
-template <class C, bool AT, bool BT, bool ABF, bool BBF>
+// The same stores one 32 x 32 block at a time (old values of the block
+// loaded first), for tiles whose main loop leaves fewer registers free.
+template <class C>
+__device__ __forceinline__ void epilogue_blocks(const GemmProb& p, int m0, int n0, int wm, int wn, int lane,
+                                                const Acc<C>& acc, float alpha, float beta) {
+    const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn * 32 * C::TN + j * 32 + l32;
+            const int row0 = m0 + wm * 32 * C::TM + i * 32 + 4 * h;
+            float cold[16];
+            if (beta != 0.f) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = row0 + 8 * (r >> 2) + (r & 3);
+                    cold[r] = (row < p.M && col < p.N) ? gptr(p.C)[(int64_t)row * p.ldc + col] : 0.f;
+                }
+            }
+            if (col >= p.N) continue;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = row0 + 8 * (r >> 2) + (r & 3);
+                if (row < p.M) {
+                    float val = alpha * acc.v[i][j][r];
+                    if (beta != 0.f) val += beta * cold[r];
+                    gptr(p.C)[(int64_t)row * p.ldc + col] = val;
+                }
+            }
+        }
+    }
+}
+
+template <class C, bool AT, bool BT, bool ABF, bool BBF, bool X6>
 __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, float alpha_scale,
                                           float* smem) {
     constexpr int AS = C::AS, BS = C::BS;
@@ -494,6 +585,75 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     if (p.K < BK) {
         tail(0, 0);
         __syncthreads();
+    }
+
+    if constexpr (X6) {
+        // fp32 products on bf16 MFMAs, one k step of 16 (two groups of 8) at
+        // a time. B's fragments of the step are read and split first; then
+        // row block by row block, A's fragments of block i + 1 are read while
+        // block i is split and its MFMAs issue, so only one block of A is
+        // live. The reads at the top of a slab follow its barrier (the other
+        // workgroup on the CU covers that wait).
+        static_assert(NG % 2 == 0, "k steps of two groups");
+        const int h = lane >> 5, l32 = lane & 31;
+        auto frag_a = [&](const float* As, int g, int i) {
+            const int row = wm * 32 * C::TM + i * 32 + l32;
+            f32x4 a;
+            if (AT) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] = As[(8 * g + 4 * h + e) * C::BM + row];
+            } else {
+                a = *(const f32x4*)&As[row * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(row))];
+            }
+            return a;
+        };
+        auto frag_b = [&](const float* Bs, int g, int j) {
+            const int col = wn * 32 * C::TN + j * 32 + l32;
+            f32x4 b;
+            if (BT) {
+                b = *(const f32x4*)&Bs[col * C::BK + 4 * ((2 * g + h) ^ swz<C::BK>(col))];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) b[e] = Bs[(8 * g + 4 * h + e) * C::BN + col];
+            }
+            return b;
+        };
+        for (int kt = 0; kt < nk; ++kt) {
+            const int cur = kt & 1;
+            const int k1 = (kt + 1) * BK;
+            const float* As = smem + cur * AS;
+            const float* Bs = smem + 2 * AS + cur * BS;
+            fill(cur ^ 1, k1);
+            if constexpr (ABF) load_a<C, AT, ABF>(p, m0, k1, ra);
+            if constexpr (BBF) load_b<C, BT, BBF>(p, n0, k1, rb);
+#pragma unroll
+            for (int st = 0; st < NG / 2; ++st) {
+                Pieces pb[C::TN];
+#pragma unroll
+                for (int j = 0; j < C::TN; ++j) pb[j] = split8(frag_b(Bs, 2 * st, j), frag_b(Bs, 2 * st + 1, j));
+                f32x4 a0 = frag_a(As, 2 * st, 0), a1 = frag_a(As, 2 * st + 1, 0);
+#pragma unroll
+                for (int i = 0; i < C::TM; ++i) {
+                    const Pieces pa = split8(a0, a1);
+                    if (i + 1 < C::TM) {
+                        a0 = frag_a(As, 2 * st, i + 1);
+                        a1 = frag_a(As, 2 * st + 1, i + 1);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    mma6_row<C>(pa, pb, acc.v[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
+            if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
+            __syncthreads();
+            if (k1 < p.K && k1 + BK > p.K) {
+                tail(cur ^ 1, k1);
+                __syncthreads();
+            }
+        }
+        epilogue_blocks<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
+        return;
     }
 
     // Software pipeline over the four k groups of a slab: the fragments of
@@ -639,7 +799,7 @@ struct GemmArgs {
     GemmProb single;
 };
 
-template <class C, bool AT, bool BT, bool ABF, bool BBF>
+template <class C, bool AT, bool BT, bool ABF, bool BBF, bool X6>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_grouped_kernel(GemmArgs args) {
     __shared__ __attribute__((aligned(16))) float smem[C::SMEM];
     const int bid = xcd_remap(blockIdx.x, args.total_tiles);
@@ -658,16 +818,16 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     int tm, tn;
     raster(t, p.tiles_m, p.tiles_n, tm, tn);
-    gemm_tile<C, AT, BT, ABF, BBF>(p, tm, tn, args.alpha_scale, smem);
+    gemm_tile<C, AT, BT, ABF, BBF, X6>(p, tm, tn, args.alpha_scale, smem);
 }
 
-template <bool AT, bool BT, bool ABF, bool BBF>
+template <bool AT, bool BT, bool ABF, bool BBF, bool X6 = false>
 hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
     if (cfg == 1)
-        gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
+        gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
     else
-        gemm_grouped_kernel<SmallCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+        gemm_grouped_kernel<SmallCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -728,6 +888,12 @@ static hipError_t dispatch(int variant, int cfg, const GemmArgs& a, hipStream_t 
     case v: return launch<at, bt, abf, bbf>(cfg, a, s);
         MATOPT_VARIANTS(X)
 #undef X
+        // fp32 products on bf16 MFMAs: the operand variants of the rotations
+        // and of the refresh's products
+        case GV_X6 | 0: return launch<false, false, false, false, true>(cfg, a, s);
+        case GV_X6 | 1: return launch<true, false, false, false, true>(cfg, a, s);
+        case GV_X6 | 2: return launch<false, true, false, false, true>(cfg, a, s);
+        case GV_X6 | 8: return launch<false, false, false, true, true>(cfg, a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -19,7 +19,7 @@ OPT_F32, OPT_BF16 = 0, 1
 OPT_FLAG_ROTATED_MOMENTUM = 1
 OPT_FLAG_BF16_ROTATION = 2
 OPT_FLAG_MUON = 4
-OPT_FLAG_FP32_MOMENTUM_ROTATION = 8
+OPT_FLAG_FP32_MFMA = 8
 OPT_MAX_DIM = 16384
 PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho", "rot_pieced")
 OPT_NUM_PHASES = len(PHASES)
@@ -28,7 +28,7 @@ EXPORTED = (
     "opt_group_workspace_size", "opt_group_create", "opt_group_step", "opt_group_refresh_basis",
     "opt_group_get_step", "opt_group_set_step", "opt_group_set_lr", "opt_plan",
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
-    "opt_gemm", "opt_gemm_bf16", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
+    "opt_gemm", "opt_gemm_x6", "opt_gemm_bf16", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
     "opt_partition_dp", "opt_plan_host_ranks", "opt_group_health", "opt_group_reorthonormalize",
 )
 
@@ -92,6 +92,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "opt_group_destroy": ([vp], None),
         "opt_last_error": ([], C.c_char_p),
         "opt_gemm": ([i32, i32, i64, i64, i64, f32, vp, i32, i64, vp, i32, i64, f32, vp, i64, vp], i32),
+        "opt_gemm_x6": ([i32, i32, i64, i64, i64, f32, vp, i32, i64, vp, i32, i64, f32, vp, i64, vp], i32),
         "opt_gemm_bf16": ([i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i32, i64, vp], i32),
         "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
         "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
@@ -204,6 +205,13 @@ def opt_gemm(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A
     _check(load().opt_gemm(trans_a, trans_b, M, N, K, alpha, C.c_void_p(A), a_dtype, lda,
                            C.c_void_p(B), b_dtype, ldb, beta, C.c_void_p(Cp), ldc,
                            C.c_void_p(stream_ptr)))
+
+
+def opt_gemm_x6(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int, a_dtype: int,
+                lda: int, B: int, b_dtype: int, ldb: int, beta: float, Cp: int, ldc: int, stream_ptr: int):
+    _check(load().opt_gemm_x6(trans_a, trans_b, M, N, K, alpha, C.c_void_p(A), a_dtype, lda,
+                              C.c_void_p(B), b_dtype, ldb, beta, C.c_void_p(Cp), ldc,
+                              C.c_void_p(stream_ptr)))
 
 
 def opt_gemm_bf16(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, beta: float,

@@ -168,15 +168,15 @@ def test_workspace_holds_the_pieces_of_the_momentum_bases(N):
     a256 = lambda x: (x + 255) // 256 * 256
     bf = descs(N, shapes, dtype=N.OPT_BF16)
     pieced = N.opt_group_workspace_size(bf, hp(N))
-    plain = N.opt_group_workspace_size(bf, hp(N, flags=N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+    plain = N.opt_group_workspace_size(bf, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
     f32 = descs(N, shapes)
     pieces = sum(a256(6 * max(m, n) ** 2) for m, n in shapes if m % 8 == 0 and n % 8 == 0)
     assert 0 <= pieced - plain - pieces < 16 * 1024    # plus the work lists of the new launches
     assert N.opt_group_workspace_size(f32, hp(N)) == \
-        N.opt_group_workspace_size(f32, hp(N, flags=N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+        N.opt_group_workspace_size(f32, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
     for other in (N.OPT_FLAG_ROTATED_MOMENTUM, N.OPT_FLAG_BF16_ROTATION):
         assert N.opt_group_workspace_size(bf, hp(N, flags=other)) == \
-            N.opt_group_workspace_size(bf, hp(N, flags=other | N.OPT_FLAG_FP32_MOMENTUM_ROTATION))
+            N.opt_group_workspace_size(bf, hp(N, flags=other | N.OPT_FLAG_FP32_MFMA))
 
 
 def test_rejects_bad_shapes_and_dtypes(N):

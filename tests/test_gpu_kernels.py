@@ -23,7 +23,7 @@ def _mo():
     return mo
 
 
-def _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=1.0, beta=0.0, seed=0):
+def _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=1.0, beta=0.0, seed=0, x6=False):
     torch = _torch()
     mo = _mo()
     N_ = mo.native
@@ -40,8 +40,8 @@ def _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=1.0, beta=0.0, seed=0):
     C0 = C.double().cpu().numpy()
     lda = ashape[1]
     ldb = bshape[1]
-    N_.opt_gemm(ta, tb, M, N, K, alpha, A.data_ptr(), int(a_bf16), lda, B.data_ptr(), int(b_bf16), ldb,
-                beta, C.data_ptr(), N, mo.stream_ptr())
+    (N_.opt_gemm_x6 if x6 else N_.opt_gemm)(ta, tb, M, N, K, alpha, A.data_ptr(), int(a_bf16), lda, B.data_ptr(),
+                                             int(b_bf16), ldb, beta, C.data_ptr(), N, mo.stream_ptr())
     torch.cuda.synchronize()
     An = A.double().cpu().numpy()
     Bn = B.double().cpu().numpy()
@@ -51,6 +51,30 @@ def _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=1.0, beta=0.0, seed=0):
     bound = 2 * max(K, 1) * 2.0 ** -23 * (np.abs(alpha) * (np.abs(opA) @ np.abs(opB)) + np.abs(beta * C0)) + 1e-30
     err = np.abs(C.double().cpu().numpy() - ref)
     return float(np.max(err / bound))
+
+
+@pytest.mark.parametrize("ta,tb,a_bf16,b_bf16", [(0, 0, 0, 0), (1, 0, 0, 0), (0, 1, 0, 0), (0, 0, 0, 1)])
+def test_gemm_x6_variants(ta, tb, a_bf16, b_bf16):
+    """fp32 products on bf16 MFMAs (three-piece split, six piece products):
+    the fp32 dot-product bound holds element by element (the terms left out
+    add at most 2^-23 (|A| |B|)_ij), on ragged shapes, k tails shorter than
+    a 16-deep MFMA step, both tile configurations and beta != 0."""
+    print(f"gemm_x6 ta={ta} tb={tb} abf={a_bf16} bbf={b_bf16}", flush=True)
+    for (M, N, K) in [(130, 67, 45), (256, 384, 512), (1, 1, 1), (33, 129, 3), (200, 300, 1000),
+                      (4096, 2048, 200)]:
+        r = _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=-0.75, beta=0.5, x6=True)
+        print(f"  {M}x{N}x{K}: worst err/bound {r:.3f}", flush=True)
+        assert r <= 1.0, (M, N, K, r)
+
+
+def test_gemm_x6_rejects_other_layouts():
+    import matrix_optimizer_step_02_amd as mo
+    torch = _torch()
+    A = torch.zeros(8, 8, device="cuda")
+    C = torch.zeros(8, 8, device="cuda")
+    with pytest.raises(mo.MatoptError):
+        mo.native.opt_gemm_x6(1, 1, 8, 8, 8, 1.0, A.data_ptr(), 0, 8, A.data_ptr(), 0, 8, 0.0, C.data_ptr(), 8,
+                              mo.stream_ptr())
 
 
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
