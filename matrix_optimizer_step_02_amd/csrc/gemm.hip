@@ -50,6 +50,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -433,19 +436,31 @@ struct Pieces {
     bf16x8 hi, mid, lo;
 };
 
+// Pairs of values: one v_cvt_pk_bf16_f32 per piece and pair, the widening
+// back to fp32 a shift or a mask, the residuals plain fp32 subtractions.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const f32x2 x = {x0, x1};
+    const bf16x2 h = __builtin_convertvector(x, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    const f32x2 r1 = {x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u)};
+    const bf16x2 m = __builtin_convertvector(r1, bf16x2);
+    const uint32_t mb = __builtin_bit_cast(uint32_t, m);
+    const f32x2 r2 = {r1[0] - __uint_as_float(mb << 16), r1[1] - __uint_as_float(mb & 0xffff0000u)};
+    hi = hb;
+    mid = mb;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, bf16x2));
+}
+
 __device__ __forceinline__ Pieces split8(const f32x4& x0, const f32x4& x1) {
+    uint32_t h[4], m[4], l[4];
+    split2(x0[0], x0[1], h[0], m[0], l[0]);
+    split2(x0[2], x0[3], h[1], m[1], l[1]);
+    split2(x1[0], x1[1], h[2], m[2], l[2]);
+    split2(x1[2], x1[3], h[3], m[3], l[3]);
     Pieces p;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = e < 4 ? x0[e] : x1[e - 4];
-        const __bf16 h = (__bf16)x;
-        const float r1 = x - (float)h;
-        const __bf16 m = (__bf16)r1;
-        const float r2 = r1 - (float)m;
-        p.hi[e] = h;
-        p.mid[e] = m;
-        p.lo[e] = (__bf16)r2;
-    }
+    p.hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+    p.mid = __builtin_bit_cast(bf16x8, (u32x4){m[0], m[1], m[2], m[3]});
+    p.lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
     return p;
 }
 
@@ -589,11 +604,12 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
 
     if constexpr (X6) {
         // fp32 products on bf16 MFMAs, one k step of 16 (two groups of 8) at
-        // a time. B's fragments of the step are read and split first; then
-        // row block by row block, A's fragments of block i + 1 are read while
-        // block i is split and its MFMAs issue, so only one block of A is
-        // live. The reads at the top of a slab follow its barrier (the other
-        // workgroup on the CU covers that wait).
+        // a time. B's fragments of the step are split first; then row block
+        // by row block, A's fragments of block i + 1 are read while block i
+        // is split and its MFMAs issue, so only one block of A is live. The
+        // slab barrier sits before the last row block's MFMAs, and the next
+        // slab's B and first A fragments are read behind it, so their latency
+        // overlaps those MFMAs.
         static_assert(NG % 2 == 0, "k steps of two groups");
         const int h = lane >> 5, l32 = lane & 31;
         auto frag_a = [&](const float* As, int g, int i) {
@@ -618,11 +634,22 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
             }
             return b;
         };
+        // fragments of the current k step: B (both groups) and A's row block 0
+        f32x4 b0[C::TN], b1[C::TN], a0, a1;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            b0[j] = frag_b(smem + 2 * AS, 0, j);
+            b1[j] = frag_b(smem + 2 * AS, 1, j);
+        }
+        a0 = frag_a(smem, 0, 0);
+        a1 = frag_a(smem, 1, 0);
         for (int kt = 0; kt < nk; ++kt) {
             const int cur = kt & 1;
             const int k1 = (kt + 1) * BK;
             const float* As = smem + cur * AS;
             const float* Bs = smem + 2 * AS + cur * BS;
+            const float* An = smem + (cur ^ 1) * AS;
+            const float* Bn = smem + 2 * AS + (cur ^ 1) * BS;
             fill(cur ^ 1, k1);
             if constexpr (ABF) load_a<C, AT, ABF>(p, m0, k1, ra);
             if constexpr (BBF) load_b<C, BT, BBF>(p, n0, k1, rb);
@@ -630,26 +657,46 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
             for (int st = 0; st < NG / 2; ++st) {
                 Pieces pb[C::TN];
 #pragma unroll
-                for (int j = 0; j < C::TN; ++j) pb[j] = split8(frag_b(Bs, 2 * st, j), frag_b(Bs, 2 * st + 1, j));
-                f32x4 a0 = frag_a(As, 2 * st, 0), a1 = frag_a(As, 2 * st + 1, 0);
+                for (int j = 0; j < C::TN; ++j) pb[j] = split8(b0[j], b1[j]);
 #pragma unroll
                 for (int i = 0; i < C::TM; ++i) {
                     const Pieces pa = split8(a0, a1);
                     if (i + 1 < C::TM) {
                         a0 = frag_a(As, 2 * st, i + 1);
                         a1 = frag_a(As, 2 * st + 1, i + 1);
+                    } else if (st + 1 < NG / 2) {
+                        // the next k step of the same slab
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) {
+                            b0[j] = frag_b(Bs, 2 * st + 2, j);
+                            b1[j] = frag_b(Bs, 2 * st + 3, j);
+                        }
+                        a0 = frag_a(As, 2 * st + 2, 0);
+                        a1 = frag_a(As, 2 * st + 3, 0);
+                    } else {
+                        // every fragment of this slab is in registers: the slab
+                        // barrier goes before the last row block's MFMAs, and
+                        // the next slab's first fragments are read behind it
+                        // (past the last slab: values unused)
+                        if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
+                        if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
+                        __syncthreads();
+                        if (k1 < p.K && k1 + BK > p.K) {
+                            tail(cur ^ 1, k1);
+                            __syncthreads();
+                        }
+#pragma unroll
+                        for (int j = 0; j < C::TN; ++j) {
+                            b0[j] = frag_b(Bn, 0, j);
+                            b1[j] = frag_b(Bn, 1, j);
+                        }
+                        a0 = frag_a(An, 0, 0);
+                        a1 = frag_a(An, 1, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     mma6_row<C>(pa, pb, acc.v[i]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-            if constexpr (ABF) store_a<C, AT, ABF, false>(smem + (cur ^ 1) * AS, ra, p, m0, k1);
-            if constexpr (BBF) store_b<C, BT, BBF>(smem + 2 * AS + (cur ^ 1) * BS, rb, p, n0, k1);
-            __syncthreads();
-            if (k1 < p.K && k1 + BK > p.K) {
-                tail(cur ^ 1, k1);
-                __syncthreads();
             }
         }
         epilogue_blocks<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
