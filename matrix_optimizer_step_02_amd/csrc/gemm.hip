@@ -468,17 +468,20 @@ __device__ __forceinline__ Pieces split8(const f32x4& x0, const f32x4& x1) {
 // smallest first.
 template <class C>
 __device__ __forceinline__ void mma6_row(const Pieces& a, const Pieces (&b)[C::TN], f32x16 (&acc)[C::TN]) {
+    // piece product by piece product across the row's column blocks, so that
+    // consecutive MFMAs go to different accumulators
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-        f32x16 c = acc[j];
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.lo, b[j].hi, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].mid, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].lo, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].hi, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].mid, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].hi, c, 0, 0, 0);
-        acc[j] = c;
-    }
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.lo, b[j].hi, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].mid, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].lo, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b[j].hi, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].mid, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b[j].hi, acc[j], 0, 0, 0);
 }
 
 // Accumulator register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
