@@ -323,11 +323,13 @@ def main(argv=None):
         ns_flops = sum(4.0 * min(m, n) ** 2 * max(m, n) for m, n in shapes) * args.ns_iters
         ms = phases["ortho"][0]
         achieved = ns_flops * args.steps / (ms * 1e-3) / 1e12 if ms > 0 else None
+        mpeak = MI355X_FP32_MFMA_TFLOPS if args.fp32_mfma else X6_FP32_EQUIV_TFLOPS
         roofline = {
-            "bound": "mfma", "achieved": achieved, "peak": MI355X_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / MI355X_FP32_MFMA_TFLOPS if achieved else None, "traffic": None,
-            "kernel": "gemm_grouped_kernel (Newton-Schulz X^T X and X (X^T X); the phase time includes the "
-                      "norm, scaling and combine kernels)",
+            "bound": "mfma", "achieved": achieved, "peak": mpeak, "unit": "TFLOP/s",
+            "frac": achieved / mpeak if achieved else None, "traffic": None,
+            "kernel": "gemm_grouped_kernel (Newton-Schulz X^T X and X (X^T X)"
+                      + ("" if args.fp32_mfma else " on bf16 MFMAs, six piece products")
+                      + "; the phase time includes the norm, scaling and combine kernels)",
             "launches": phases["ortho"][1], "avg_launch_ms": ms / max(phases["ortho"][1], 1),
             "flops_per_step": ns_flops,
         }

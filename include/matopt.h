@@ -128,7 +128,7 @@ enum {
      * from X = M / ||M||_F (on the side with the smaller Gram matrix), and
      * W <- W - lr O. v, U, V are unused (may be NULL), as are beta2, eps, K
      * and power_iters; refresh_basis, health and reorthonormalize return
-     * OPT_EUNSUPPORTED. Cannot be combined with the other flags. */
+     * OPT_EUNSUPPORTED. Combines with OPT_FLAG_FP32_MFMA only. */
     OPT_FLAG_MUON = 4u,
     /* By default the fp32 products of the rotations and of the refresh run on
      * bf16 MFMAs (2.5 PFLOP/s dense against 157 TFLOP/s for fp32), at fp32
@@ -144,7 +144,8 @@ enum {
      *    larger flop count (U^T M when m > n, M V otherwise) needs only three
      *    products, against stored pieces of U^T or V^T (6 d^2 bytes per
      *    matrix, d = m or n, made with the U^T copy), in one fp32 chain.
-     * This flag keeps every one of these products on fp32 MFMAs. */
+     * The Newton-Schulz products of OPT_FLAG_MUON run the same way. This flag
+     * keeps every one of these products on fp32 MFMAs. */
     OPT_FLAG_FP32_MFMA = 8u
 };
 

@@ -256,8 +256,8 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
                                 OPT_FLAG_FP32_MFMA))
         return fail(OPT_EINVAL, "unknown bits in flags");
-    if ((hp->flags & OPT_FLAG_MUON) && hp->flags != OPT_FLAG_MUON)
-        return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON cannot be combined with other flags");
+    if ((hp->flags & OPT_FLAG_MUON) && (hp->flags & ~(uint32_t)OPT_FLAG_FP32_MFMA) != OPT_FLAG_MUON)
+        return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON combines with OPT_FLAG_FP32_MFMA only");
     if ((hp->flags & OPT_FLAG_MUON) && hp->ns_iters < 1)
         return fail(OPT_EINVAL, "ns_iters must be >= 1 with OPT_FLAG_MUON");
     return OPT_OK;
@@ -911,8 +911,10 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             G.mu.nseg = (int)segs.size();
             G.mu.chunks = chunks;
             G.mu.segs = g->img.put(segs);
-            G.mu_gram = put_gemm(g->img, gram);
-            G.mu_prod = put_gemm(g->img, prod);
+            // the Newton-Schulz products on bf16 MFMAs too, unless told otherwise
+            const bool mx6 = !(g->hp.flags & OPT_FLAG_FP32_MFMA);
+            G.mu_gram = put_gemm(g->img, gram, mx6);
+            G.mu_prod = put_gemm(g->img, prod, mx6);
             std::vector<EwSeg> mom;
             for (int mi : members) {
                 const Mat& M = g->mats[mi];

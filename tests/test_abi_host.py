@@ -128,6 +128,7 @@ def test_flag_combinations(N):
 def test_muon_flag_checks(N):
     d = descs(N, [(8, 8)])
     N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_MUON, ns_iters=2))
+    N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_MUON | N.OPT_FLAG_FP32_MFMA, ns_iters=2))
     assert err(N, N.opt_group_workspace_size, d, hp(N, flags=N.OPT_FLAG_MUON)) == N.OPT_EINVAL    # ns_iters 0
     for other in (N.OPT_FLAG_BF16_ROTATION, N.OPT_FLAG_ROTATED_MOMENTUM):
         assert err(N, N.opt_group_workspace_size, d, hp(N, flags=N.OPT_FLAG_MUON | other, ns_iters=2)) == \

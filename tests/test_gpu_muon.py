@@ -12,11 +12,11 @@ from tests import contract, harness
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, steps, iters, check_mats, capacity=None):
+def _run(wl, steps, iters, check_mats, capacity=None, fp32_mfma=False):
     import torch
     import matrix_optimizer_step_02_amd as mo
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, capacity or wl.capacity_bytes,
-                  muon=True, ns_iters=iters)
+                  muon=True, ns_iters=iters, fp32_mfma=fp32_mfma)
     states = [mo.new_state(s.m, s.n, wl.m_dtype, "cuda", W0=workloads.initial_weight(wl, i, "cuda"), bases=False)
               for i, s in enumerate(wl.matrices)]
     grp = mo.RotatedAdamGroup(states, hp)
@@ -40,13 +40,16 @@ def _run(wl, steps, iters, check_mats, capacity=None):
     assert not failures, "\n".join(failures)
 
 
-@pytest.mark.parametrize("m_dtype,iters", [("f32", 1), ("bf16", 5), ("f32", 10)])
-def test_muon_ragged_shapes(m_dtype, iters):
+@pytest.mark.parametrize("m_dtype,iters,fp32_mfma", [("f32", 1, False), ("bf16", 5, False), ("f32", 10, False),
+                                                     ("bf16", 5, True)])
+def test_muon_ragged_shapes(m_dtype, iters, fp32_mfma):
+    """Ragged shapes; the Newton-Schulz products on bf16 MFMAs (the default)
+    and on fp32 MFMAs."""
     mats = (workloads.MatrixSpec("a", 37, 53), workloads.MatrixSpec("b", 130, 67),
             workloads.MatrixSpec("c", 200, 200), workloads.MatrixSpec("d", 64, 96))
     wl = workloads.Workload("ragged_mu", 7, "ragged", mats, m_dtype, K=0, power_iters=1, steps=3,
                             grad_kind="iid", grad_std=1e-2)
-    _run(wl, 3, iters, range(len(mats)))
+    _run(wl, 3, iters, range(len(mats)), fp32_mfma=fp32_mfma)
 
 
 def test_muon_layer_shapes_several_micro_groups():
