@@ -264,10 +264,30 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     // ring buffer b of A at smem + b AB, of B at smem + ST AB + b BB
     auto abuf = [&](int b) { return smem + b * C::AB; };
     auto bbuf = [&](int b) { return smem + C::ST * C::AB + b * C::BB; };
-    // slab k0 of the concatenated range lies in period q at kk = k0 - q kper
-    // (kper is a multiple of the slab depth); past the last period every
-    // load reads the zero block
-    auto fill = [&](int b, int k0) {
+    // Pieced products with two stages run their slabs k-slab by k-slab, the
+    // periods of one k-slab back to back: slab t is k-slab t / np of period
+    // t % np. An operand read again in every period (piece stride 0) is then
+    // filled once per k-slab and stays in its buffer (k-slab parity) while
+    // the other operand's pieces stream through theirs (slab parity), so
+    // the fills move (np + 1) instead of 2 np operand slabs per k-slab.
+    const bool inter = C::ST == 2 && p.np > 1;
+    auto buf_a = [&](int t) { return inter && p.a_ps == 0 ? (t / p.np) & 1 : t & 1; };
+    auto buf_b = [&](int t) { return inter && p.b_ps == 0 ? (t / p.np) & 1 : t & 1; };
+    // Otherwise slab t covers k0 = t BK of the concatenated range: period q
+    // at kk = k0 - q kper (kper is a multiple of the slab depth). Past the
+    // last slab every load reads the zero block.
+    auto fill = [&](int b, int t) {
+        if (inter) {
+            const int ks = t / p.np, q = t - ks * p.np;
+            const int k0 = ks * C::BK;
+            const int kv = k0 < p.K ? p.K : 0;
+            if (p.a_ps != 0 || q == 0)
+                dma16<C, C::BM>(abuf(buf_a(t)), p.A + q * p.a_ps, p.lda, p.M, kv, m0, k0);
+            if (p.b_ps != 0 || q == 0)
+                dma16<C, C::BN>(bbuf(buf_b(t)), p.B + q * p.b_ps, p.ldb, p.N, kv, n0, k0);
+            return;
+        }
+        const int k0 = t * C::BK;
         int q = k0 / p.kper;
         const int kk = k0 - q * p.kper;
         const int kv = q < p.np ? p.K : 0;
@@ -282,7 +302,9 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int nk = p.np == 1 ? (p.K + C::BK - 1) / C::BK : p.np * (p.kper / C::BK);
+    const int nk = p.np == 1 ? (p.K + C::BK - 1) / C::BK
+                 : inter    ? p.np * ((p.K + C::BK - 1) / C::BK)
+                            : p.np * (p.kper / C::BK);
     const float alpha = p.alpha * alpha_scale;
     if (nk == 0) {
         epi16<C, OUT16>(p, m0, n0, wm, wn, lane, acc, alpha, smem);
@@ -290,7 +312,7 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     }
     // slabs 0 .. ST-2 in flight; slab 0 landed before the first reads
 #pragma unroll
-    for (int st = 0; st < C::ST - 1; ++st) fill(st, st * C::BK);
+    for (int st = 0; st < C::ST - 1; ++st) fill(st, st);
     slab_barrier<C>();
     bf16x8 fa[2][C::TM], fb[2][C::TN];
     frags16<C>(abuf(0), bbuf(0), 0, wm, wn, lane, fa[0], fb[0]);
@@ -298,10 +320,10 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     for (int kt = 0; kt < nk; ++kt) {
         const int nxt = cur + 1 == C::ST ? 0 : cur + 1;
         const int fb_ = cur == 0 ? C::ST - 1 : cur - 1;   // buffer of slab kt + ST - 1
-        const char* As = abuf(cur);
-        const char* Bs = bbuf(cur);
+        const char* As = abuf(inter ? buf_a(kt) : cur);
+        const char* Bs = bbuf(inter ? buf_b(kt) : cur);
         // past the last slab the fill reads only the zero block into an idle buffer
-        fill(fb_, (kt + C::ST - 1) * C::BK);
+        fill(fb_, kt + C::ST - 1);
 #pragma unroll
         for (int s = 0; s < C::NS - 1; ++s) {
             mma16<C, 0, 1>(fa[s & 1], fb[s & 1], acc);
@@ -314,7 +336,8 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         slab_barrier<C>();
         mma16<C, 0, 1>(fa[1], fb[1], acc);
         __builtin_amdgcn_sched_barrier(0);
-        frags16<C>(abuf(nxt), bbuf(nxt), 0, wm, wn, lane, fa[0], fb[0]);
+        frags16<C>(abuf(inter ? buf_a(kt + 1) : nxt), bbuf(inter ? buf_b(kt + 1) : nxt), 0, wm, wn, lane, fa[0],
+                   fb[0]);
         __builtin_amdgcn_sched_barrier(0);
         mma16<C, 1, C::TM>(fa[1], fb[1], acc);
         __builtin_amdgcn_sched_barrier(0);
