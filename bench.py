@@ -423,6 +423,10 @@ def main(argv=None):
                    "rotated_momentum": bool(args.rotated_momentum),
                    "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
                    "fp32_mfma": bool(args.fp32_mfma),
+                   # how the fp32 products execute: six bf16 MFMA piece products each (fp32 accuracy),
+                   # or fp32 MFMAs
+                   "fp32_products": ("fp32 MFMA" if args.fp32_mfma
+                                     else "bf16 MFMA, three-piece split, six piece products"),
                    **({"ns_iters": args.ns_iters} if args.muon else {})},
         "steps_per_s": steps_per_s,
         "roofline": roofline,
