@@ -173,7 +173,8 @@ typedef struct {
  * with fp32 rotations (no flag, or OPT_FLAG_ROTATED_MOMENTUM alone) U^T in
  * fp32, 4 m^2 bytes per matrix, so that U^T G and U^T M read rows of U^T,
  * and without flags, for a bf16 M with both sides multiples of 8, the three
- * bf16 pieces of U^T (m > n) or V^T (else), 6 d^2 bytes (OPT_FLAG_FP32_MFMA);
+ * bf16 pieces of U^T (m > n) or V^T (else), 6 d^2 bytes (none with
+ * OPT_FLAG_FP32_MFMA);
  * with OPT_FLAG_BF16_ROTATION the bf16 bases described there. They are
  * rebuilt on the first step after a create, a refresh, refresh_basis,
  * reorthonormalize or set_step: a caller that writes U or V itself must call
