@@ -52,17 +52,17 @@ def rotation_flops(shapes):
     return sum(6.0 * m * n * (m + n) for m, n in shapes)
 
 
-def pieced(m, n, m_dtype, plain_fp32):
+def pieced(m, n, m_dtype, no_flags):
     """Whether the library runs this matrix's momentum product U^T M (m > n)
     or M V (else) as three bf16 products against exact pieces of the basis:
     fp32 rotations of a bf16 M with m, n multiples of 8."""
-    return plain_fp32 and m_dtype == "bf16" and m % 8 == 0 and n % 8 == 0
+    return no_flags and m_dtype == "bf16" and m % 8 == 0 and n % 8 == 0
 
 
-def phase_flops(shapes, carry=False, m_dtype="f32", plain_fp32=False):
+def phase_flops(shapes, carry=False, m_dtype="f32", no_flags=False):
     """Algorithmic flops of each GEMM phase for one step over all matrices
     (carry: a step of the rotated-momentum variant that rotates G alone;
-    plain_fp32: the method's fp32 rotations with no flag, where a bf16 M's
+    no_flags: the method's fp32 rotations with no flag, where a bf16 M's
     larger product moves to the pieced phase)."""
     out = {"rot_left": 0.0, "rot_right": 0.0, "back_left": 0.0, "back_right": 0.0}
     for m, n in shapes:
@@ -72,7 +72,7 @@ def phase_flops(shapes, carry=False, m_dtype="f32", plain_fp32=False):
         out["back_right"] += 2.0 * m * n * n
         if carry:
             continue
-        if pieced(m, n, m_dtype, plain_fp32):
+        if pieced(m, n, m_dtype, no_flags):
             # U^T M (tall) or M V (wide/square) pieced, the other product fp32
             out["rot_pieced"] = out.get("rot_pieced", 0.0) + 2.0 * m * n * max(m, n)
             out["rot_right" if m > n else "rot_left"] += 2.0 * m * n * min(m, n)
@@ -336,8 +336,8 @@ def main(argv=None):
         extra["phase_ms_per_step"] = {k: v[0] / args.steps for k, v in phases.items() if v[1]}
         extra["phase_launches"] = {k: v[1] for k, v in phases.items() if v[1]}
     elif phases:
-        plain = not (args.rotated_momentum or args.bf16_rotation or args.fp32_mfma)
-        pf_all = phase_flops(shapes, m_dtype=wl.m_dtype, plain_fp32=plain)
+        no_flags = not (args.rotated_momentum or args.bf16_rotation or args.fp32_mfma)
+        pf_all = phase_flops(shapes, m_dtype=wl.m_dtype, no_flags=no_flags)
         # the roofline is the dominant kernel's: the pieced bf16 products are reported beside it
         pf = {k: v for k, v in pf_all.items() if k != "rot_pieced"}
         flops = sum(pf.values()) * args.steps
