@@ -273,3 +273,23 @@ def test_bench_selects_rotation_dispatches_from_non_refresh_steps():
     rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": k} for i, k in enumerate(seq)]
     picked = bench.rotation_dispatches(list(reversed(rows)))
     assert [int(r["Dispatch_Id"]) for r in picked] == [12, 13, 14, 16, 17]
+
+
+def test_bench_flop_accounting_covers_the_rotations_once():
+    """Whatever the path, the per-phase flops of a full step add up to the
+    rotations' 6 m n (m + n); without flags a bf16 M with sides multiples of
+    8 moves 2 m n max(m, n) to the pieced phase (U^T M when m > n, M V
+    otherwise), and the carrying step of the rotated momentum rotates G
+    alone (4 m n (m + n))."""
+    import bench
+    shapes = [(2048, 2048), (2048, 1024), (2048, 6144), (6144, 2048), (130, 67), (8, 16)]
+    total = bench.rotation_flops(shapes)
+    for m_dtype in ("f32", "bf16"):
+        for no_flags in (False, True):
+            pf = bench.phase_flops(shapes, m_dtype=m_dtype, no_flags=no_flags)
+            assert abs(sum(pf.values()) - total) <= 1e-9 * total
+            pieced = sum(2.0 * m * n * max(m, n) for m, n in shapes
+                         if no_flags and m_dtype == "bf16" and m % 8 == 0 and n % 8 == 0)
+            assert pf.get("rot_pieced", 0.0) == pieced
+    carry = bench.phase_flops(shapes, carry=True)
+    assert abs(sum(carry.values()) - sum(4.0 * m * n * (m + n) for m, n in shapes)) <= 1e-9 * total
