@@ -25,11 +25,14 @@ Source: the Canzona page (aitangshan.cn), cited by section:
 
 Readings where the section is silent or garbled (each listed in the design doc):
 
-* the "ideal mean" of a bucket's step is the mean load after the bucket is
-  placed, (sum(L) + W_b) / R: with alpha = 1 the bucket then brings every
-  rank below that mean up to it exactly (before the cuts are discretised);
-  the mean before placement would hand a whole bucket to the few ranks that
-  trail, the opposite of what alpha = 1 being best implies;
+* the "ideal mean" against which a rank's deficit is measured is the mean
+  of the loads before the bucket, sum(L) / R, as the section's listing
+  computes it (the comparison in the listing's test of the deficit sum is
+  lost in the extraction; "greater than zero" is the only reading that
+  avoids a division by zero);
+  with alpha = 1 a bucket therefore goes to the ranks below that mean in
+  proportion to their deficits, and to every rank evenly when none trails
+  (the first bucket, or equal loads);
 * a bucket's parameters keep their physical order and rank r receives one
   consecutive range, ranks in increasing order (ZeRO-1 geometry); the cut
   for boundary r is the parameter boundary whose prefix cost is nearest to
@@ -66,13 +69,16 @@ def matrix_step_cost(m: int, n: int, K: int, power_iters: int) -> float:
 
 
 def bucket_shares(loads: Sequence[float], W: float, alpha: float) -> List[float]:
-    """Target share of each rank for a bucket of cost W (section 3.2.1)."""
+    """Target share of each rank for a bucket of cost W (section 3.2.1):
+    deficits against the mean of the current loads, sum(L) / R, normalised
+    to fill shares; mixed with the even split by alpha. W does not enter the
+    shares (it scales the cut targets in atomic_cuts)."""
     R = len(loads)
     total = 0.0
     for x in loads:
         total += x
-    mean_after = (total + W) / R
-    deficits = [max(0.0, mean_after - x) for x in loads]
+    mean = total / R
+    deficits = [max(0.0, mean - x) for x in loads]
     dsum = 0.0
     for d in deficits:
         dsum += d

@@ -53,51 +53,68 @@ def test_alpha_zero_ignores_earlier_loads():
     assert P.bucket_shares([7.0, 0.0, 3.0], 4.0, 0.0) == [1 / 3] * 3
 
 
-def _water_filling_holds():
-    """alpha = 1 with every rank at or below the mean after the bucket: each
-    rank's share is its gap to that mean, and a bucket of fine parameters
-    whose cut targets fall on boundaries levels all ranks at that mean."""
+def _printed_shares_hold():
+    """The Canzona page, section 3.2.1: a rank's deficit is its gap below the
+    mean of the current loads, sum(L) / R; at alpha = 1 the shares are the
+    deficits normalised. Loads [4, 2, 0, 3] have mean 9/4, deficits
+    [0, 1/4, 9/4, 0] (sum 5/2), so a bucket of 11 is shared [0, 0.1, 0.9, 0]
+    whatever its cost; at alpha = 1/2 the even split enters half-way:
+    [1/8, 7/40, 23/40, 1/8]. Cut into 44 parameters of 1/4, the targets
+    0, 1.1, 11 snap to boundaries 0, 4, 44."""
     loads = [4.0, 2.0, 0.0, 3.0]
-    W = 11.0                                  # mean after = 20 / 4 = 5
-    shares = P.bucket_shares(loads, W, 1.0)
-    if shares != pytest.approx([1 / 11, 3 / 11, 5 / 11, 2 / 11], rel=1e-15):
+    if P.bucket_shares(loads, 11.0, 1.0) != pytest.approx([0.0, 0.1, 0.9, 0.0], rel=1e-15, abs=1e-300):
         return False
-    cuts = P.atomic_cuts([0.25] * 44, shares)
-    added = [0.25 * (cuts[r + 1] - cuts[r]) for r in range(4)]
-    return cuts == [0, 4, 16, 36, 44] and [x + y for x, y in zip(loads, added)] == [5.0] * 4
+    if P.bucket_shares(loads, 11.0, 0.5) != pytest.approx([1 / 8, 7 / 40, 23 / 40, 1 / 8], rel=1e-15):
+        return False
+    cuts = P.atomic_cuts([0.25] * 44, P.bucket_shares(loads, 11.0, 1.0))
+    return cuts == [0, 0, 4, 44, 44]
 
 
-def test_alpha_one_fills_the_gaps_to_the_new_mean():
-    assert _water_filling_holds()
+def test_alpha_one_shares_follow_the_printed_deficits():
+    assert _printed_shares_hold()
 
 
-def test_alpha_one_balances_fine_grained_buckets_within_one_parameter():
-    """Many buckets of many small parameters: alpha = 1 ends within one
-    parameter's cost of perfect balance."""
+def test_shares_closed_forms():
+    """No rank below the mean (the first bucket, equal loads): the even split
+    for every alpha. Two ranks with loads a > b: at alpha the trailing rank
+    gets (1 - alpha)/2 + alpha, the leading one (1 - alpha)/2."""
+    for alpha in (0.0, 0.3, 1.0):
+        assert P.bucket_shares([0.0] * 5, 7.0, alpha) == pytest.approx([0.2] * 5, rel=1e-15)
+        assert P.bucket_shares([3.0] * 4, 1.0, alpha) == pytest.approx([0.25] * 4, rel=1e-15)
+        assert P.bucket_shares([5.0, 2.0], 9.0, alpha) == pytest.approx(
+            [(1 - alpha) / 2, (1 - alpha) / 2 + alpha], rel=1e-15, abs=1e-300)
+
+
+def test_alpha_one_gives_nothing_to_ranks_at_or_above_the_mean():
+    """At alpha = 1 a bucket is placed only on ranks whose load was below the
+    mean of the loads before it (unless no rank trailed); over random cases."""
     rng = random.Random(3)
-    costs, bb = [], [0]
-    for b in range(12):
-        k = rng.randint(20, 40)
-        costs += [rng.uniform(0.5, 1.0) for _ in range(k)]
-        bb.append(len(costs))
-    for R in (3, 5, 8):
-        _, loads = P.alpha_balanced_partition(costs, bb, R, 1.0)
-        assert max(loads) - sum(loads) / R <= max(costs)
-
-
-def test_planted_mean_before_placement_is_caught(monkeypatch):
-    """Deficits against the mean before the bucket (the other reading) give
-    different shares whenever a rank lies between the two means: the
-    water-filling pin fails."""
-    def shares_before(loads, W, alpha):
-        R = len(loads)
+    for case in range(200):
+        R = rng.randint(2, 9)
+        loads = [rng.choice([0.0, 1.0, 2.0, rng.uniform(0, 5)]) for _ in range(R)]
+        costs = [rng.uniform(0.1, 1.0) for _ in range(rng.randint(1, 30))]
+        shares = P.bucket_shares(loads, sum(costs), 1.0)
+        cuts = P.atomic_cuts(costs, shares)
         mean = sum(loads) / R
+        if any(x < mean for x in loads):
+            for r in range(R):
+                if loads[r] >= mean:
+                    assert shares[r] == 0.0 and cuts[r + 1] == cuts[r]
+
+
+def test_planted_mean_after_placement_is_caught(monkeypatch):
+    """Deficits against the mean after the bucket, (sum(L) + W) / R (a reading
+    that water-fills every trailing rank), give [1/11, 3/11, 5/11, 2/11] on
+    the printed case: the pin fails."""
+    def shares_after(loads, W, alpha):
+        R = len(loads)
+        mean = (sum(loads) + W) / R
         d = [max(0.0, mean - x) for x in loads]
         s = sum(d)
         fill = [x / s for x in d] if s > 0 else [1.0 / R] * R
         return [(1 - alpha) / R + alpha * f for f in fill]
-    monkeypatch.setattr(P, "bucket_shares", shares_before)
-    assert not _water_filling_holds()
+    monkeypatch.setattr(P, "bucket_shares", shares_after)
+    assert not _printed_shares_hold()
 
 
 def test_planted_unsorted_buckets_are_caught(monkeypatch):
