@@ -329,10 +329,11 @@ opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
  * consecutive parameters bucket_begin[b] .. bucket_begin[b+1]-1
  * (bucket_begin has nbuckets + 1 non-decreasing entries, from 0 to nparams).
  * Buckets are placed by decreasing total cost W_b (ties in input order). For
- * each bucket, with L_r the rank loads so far and T = (sum_r L_r + W_b) /
- * ranks the mean after it, the target share of rank r is
+ * each bucket, with L_r the rank loads so far and T = sum_r L_r / ranks the
+ * mean of those loads (the section's deficit against the ideal mean), the
+ * target share of rank r is
  * (1 - alpha) / ranks + alpha * max(0, T - L_r) / sum_s max(0, T - L_s)
- * (1 / ranks when that sum is 0). The bucket is cut into `ranks` consecutive
+ * (1 / ranks when that sum is 0, e.g. for the first bucket). The bucket is cut into `ranks` consecutive
  * ranges, rank 0 first, only at parameter boundaries: boundary r (1 <= r <
  * ranks) is the prefix of the bucket whose cost is nearest to W_b times the
  * summed shares of ranks < r, searched from the previous boundary on, ties to

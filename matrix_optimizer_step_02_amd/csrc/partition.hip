@@ -20,16 +20,17 @@ using namespace matopt;
 
 namespace {
 
-// Rank targets of one bucket of cost W given the loads so far.
-void bucket_shares(const std::vector<double>& load, double W, double alpha, std::vector<double>& share) {
+// Rank targets of one bucket given the loads so far: each rank's deficit
+// below the mean of the current loads, normalised, mixed with the even split.
+void bucket_shares(const std::vector<double>& load, double alpha, std::vector<double>& share) {
     const int R = (int)load.size();
     double total = 0.0;
     for (double x : load) total += x;
-    const double mean_after = (total + W) / R;
+    const double mean = total / R;
     std::vector<double> deficit(R);
     double dsum = 0.0;
     for (int r = 0; r < R; ++r) {
-        deficit[r] = std::max(0.0, mean_after - load[r]);
+        deficit[r] = std::max(0.0, mean - load[r]);
         dsum += deficit[r];
     }
     const double even = 1.0 / R;
@@ -94,7 +95,7 @@ extern "C" opt_status opt_partition_dp(const double* cost, int64_t nparams, cons
     std::vector<int64_t> cut;
     for (int32_t b : order) {
         const int64_t lo = bucket_begin[b], k = bucket_begin[b + 1] - lo;
-        bucket_shares(L, W[b], alpha, share);
+        bucket_shares(L, alpha, share);
         atomic_cuts(cost + lo, k, share, cut);
         for (int r = 0; r < ranks; ++r)
             for (int64_t j = cut[r]; j < cut[r + 1]; ++j) {
