@@ -255,12 +255,17 @@ enum {
     OPT_PHASE_ROT_PIECED = 8, /* bf16 M's pieced product (U^T M or M V) and the M^T it reads */
     OPT_NUM_PHASES = 9
 };
-/* enable != 0 starts recording (and clears the totals); 0 stops. */
+/* enable != 0 starts recording and clears the totals; 0 stops. Enabling
+ * creates the HIP events for 64 steps' worth of phase scopes up front (so a
+ * step never creates one); a call on the group's device. */
 opt_status opt_group_set_timing(opt_group_t g, int32_t enable);
-/* Synchronises with the last recorded event, then writes for each phase the
- * summed milliseconds and the number of kernels launched in the timed scopes
- * since timing was enabled (arrays of OPT_NUM_PHASES entries; either may be
- * NULL). Every scope counts its grouped GEMM and elementwise launches; the
+/* Synchronises with the last recorded event, folds the records into the
+ * totals and frees the event pool for the next 64 steps, then writes for
+ * each phase the summed milliseconds and the number of kernels launched in
+ * the timed scopes since timing was enabled (arrays of OPT_NUM_PHASES
+ * entries; either may be NULL). Returns OPT_ESTATE (after writing the totals)
+ * if more scopes were entered between two reads than the pool holds: the
+ * totals then miss the scopes that found no event. Every scope counts its grouped GEMM and elementwise launches; the
  * refresh scope counts its grouped GEMMs (Gram products and the QR's outer-
  * block updates), not the QR's panel and in-block kernels. */
 opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches);

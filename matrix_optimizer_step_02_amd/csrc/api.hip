@@ -228,10 +228,16 @@ struct opt_group_s {
     int64_t health_chunks = 0;
     int device = 0;
     bool mt_valid = false;   // the carried rotated momentum matches U, V (OPT_FLAG_ROTATED_MOMENTUM)
-    // timing
+    // timing: events are created when timing is enabled (never inside a
+    // step); a scope that finds the pool used up is not recorded and is
+    // reported by read_timing, which folds the records into the totals and
+    // frees the pool again
     bool timing = false;
+    bool timing_overflow = false;
     std::vector<hipEvent_t> pool;
     size_t pool_used = 0;
+    double acc_ms[OPT_NUM_PHASES] = {};
+    int64_t acc_kernels[OPT_NUM_PHASES] = {};
     struct Rec {
         int phase;
         hipEvent_t b, e;
@@ -277,8 +283,10 @@ struct Span {
     const char* what;
 };
 
+// `spans_out`, when given, receives the byte range of every tensor (with
+// need_ptrs), sorted by start address.
 opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparams* hp,
-                       bool need_ptrs) {
+                       bool need_ptrs, std::vector<Span>* spans_out = nullptr) {
     if (!d) return fail(OPT_EINVAL, "descs is NULL");
     if (count < 1 || count > OPT_MAX_MATRICES)
         return fail(OPT_EINVAL, "count must be in [1, %d]", OPT_MAX_MATRICES);
@@ -328,6 +336,7 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
                 return fail(OPT_EINVAL, "tensors overlap: %s of matrix %d and %s of matrix %d",
                             spans[k - 1].what, spans[k - 1].mat, spans[k].what, spans[k].mat);
     }
+    if (spans_out) *spans_out = std::move(spans);
     return OPT_OK;
 }
 
@@ -791,6 +800,9 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
     g->img.bytes.clear();
     g->scratch_bytes = 0;
     const bool r16 = g->hp.flags & OPT_FLAG_BF16_ROTATION;
+    // the tables depend on the flags, never on whether a pointer is set, so
+    // that the size query (which reads no pointer) matches create
+    const bool rmf = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
     g->bases_bytes = 0;
     if (r16) {
         std::vector<BasisJob> bj;
@@ -996,7 +1008,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             a.n = mn;
             a.vec = aligned(Gt, 16) && aligned(mt, 16) && aligned(x.v, 16);
             adam.push_back(a);
-            if (x.Mt) {
+            if (rmf) {
                 // recompute: (U^T M) V -> Mt; u = Mt / (sqrt(v) + eps) -> mt slot
                 right_re.push_back(mk(false, false, TG, false, n, x.V, false, n, Gt, n, m, n, n, 1.f, 0.f));
                 right_re.push_back(mk(false, false, TM, false, n, x.V, false, n, x.Mt, n, m, n, n, 1.f, 0.f));
@@ -1037,7 +1049,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 // G~ = U^T S^T: G~[i][j] = sum_k U^T[i][k] S[j][k]  (m x n fp32)
                 s_left.push_back(g16(M.Utb, m8, SG, m8, Gt, n, m, n, m8, 1.f, 0.f, n));
                 s_left.push_back(g16(M.Utb, m8, SM, m8, mt, n, m, n, m8, 1.f, 0.f, n));
-                if (x.Mt) {
+                if (rmf) {
                     // carried m~: G alone on carrying steps; m~ into Mt on recomputing ones
                     s_right_c.push_back(s_right[s_right.size() - 2]);
                     s_left_c.push_back(s_left[s_left.size() - 2]);
@@ -1066,7 +1078,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                     a.n = mn;
                     a.vec = aligned(x.v, 16);
                     a16.push_back(a);
-                    if (x.Mt) {
+                    if (rmf) {
                         a.b = x.Mt;
                         a.vec = aligned(x.v, 16) && aligned(x.Mt, 16);
                         a16_re.push_back(a);
@@ -1091,7 +1103,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                     a.vec = aligned(x.v, 16);
                     ar.push_back(a);
                     pu.push_back({mt, Gb, m, n, n, n8, 0, 0});
-                    if (x.Mt) {
+                    if (rmf) {
                         a.b = x.Mt;   // u to the m~ scratch (packed from there), m~ kept in Mt
                         a.d = mt;
                         a.vec = aligned(x.v, 16) && aligned(x.Mt, 16);
@@ -1340,11 +1352,21 @@ const T* dptr(const opt_group_s* g, uint64_t off) {
 
 hipEvent_t next_event(opt_group_s* g) {
     if (g->pool_used == g->pool.size()) {
-        hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return nullptr;
-        g->pool.push_back(e);
+        g->timing_overflow = true;
+        return nullptr;
     }
     return g->pool[g->pool_used++];
+}
+
+// Steps whose scopes the event pool holds between two reads of the timing.
+constexpr int kTimingSteps = 64;
+
+// Upper bound on the phase scopes of one step (or one refresh_basis): the
+// momentum, the four rotation phases, the Adam phase and the pieced product
+// of every micro-group, one refresh scope per refresh batch, the copies of
+// the bases, plus a margin.
+size_t scopes_per_step(const opt_group_s* g) {
+    return 8 * g->groups.size() + 2 * g->rbatches.size() + 4;
 }
 
 // Events recorded on the step's stream around every launch sequence of a
@@ -1367,7 +1389,8 @@ struct PhaseScope {
             hipEvent_t e = next_event(g);
             if (e) {
                 (void)hipEventRecord(e, s);
-                g->recs.push_back({phase, b, e, g->kernels_in_scope});
+                if (g->recs.size() < g->recs.capacity()) g->recs.push_back({phase, b, e, g->kernels_in_scope});
+                else g->timing_overflow = true;
             }
         }
     }
@@ -1554,7 +1577,8 @@ opt_status opt_group_create(const opt_matrix_desc* descs, int32_t count, const o
                             opt_group_t* out) {
     if (!out) return fail(OPT_EINVAL, "out is NULL");
     *out = nullptr;
-    opt_status st = check_descs(descs, count, hp, true);
+    std::vector<Span> spans;
+    opt_status st = check_descs(descs, count, hp, true, &spans);
     if (st) return st;
     if (!workspace) return fail(OPT_EINVAL, "workspace is NULL");
     if (!aligned(workspace, kAlign)) return fail(OPT_EINVAL, "workspace must be 256-byte aligned");
@@ -1564,14 +1588,12 @@ opt_status opt_group_create(const opt_matrix_desc* descs, int32_t count, const o
         return fail(OPT_ENOWS, "workspace has %llu bytes, %llu needed",
                     (unsigned long long)workspace_bytes, (unsigned long long)need);
     {
+        // every tensor's whole byte range against the part of the workspace
+        // the group uses
         const uintptr_t lo = (uintptr_t)workspace, hi = lo + need;
-        for (int i = 0; i < count; ++i) {
-            const opt_matrix_desc& x = descs[i];
-            const void* ptrs[6] = {x.W, x.G, x.M, x.v, x.U, x.V};
-            for (const void* p : ptrs)
-                if ((uintptr_t)p >= lo && (uintptr_t)p < hi)
-                    return fail(OPT_EINVAL, "matrix %d: a tensor lies inside the workspace", i);
-        }
+        for (const Span& sp : spans)
+            if (sp.lo < hi && lo < sp.hi)
+                return fail(OPT_EINVAL, "matrix %d: %s overlaps the workspace", sp.mat, sp.what);
     }
     opt_group_s* g = new opt_group_s();
     g->hp = *hp;
@@ -1892,16 +1914,31 @@ opt_status opt_group_set_lr(opt_group_t g, float lr) {
 
 opt_status opt_group_set_timing(opt_group_t g, int32_t enable) {
     if (opt_status st = check_group(g)) return st;
-    g->timing = enable != 0;
     g->recs.clear();
     g->pool_used = 0;
+    g->timing_overflow = false;
+    for (int i = 0; i < OPT_NUM_PHASES; ++i) {
+        g->acc_ms[i] = 0.0;
+        g->acc_kernels[i] = 0;
+    }
+    g->timing = false;
+    if (enable) {
+        const size_t events = 2 * scopes_per_step(g) * kTimingSteps;
+        if (opt_status st = set_device(g)) return st;
+        while (g->pool.size() < events) {
+            hipEvent_t e;
+            hipError_t he = hipEventCreate(&e);
+            if (he != hipSuccess) return hip_fail(he, "hipEventCreate");
+            g->pool.push_back(e);
+        }
+        g->recs.reserve(events / 2);
+        g->timing = true;
+    }
     return OPT_OK;
 }
 
 opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
     if (opt_status st = check_group(g)) return st;
-    double acc[OPT_NUM_PHASES] = {0};
-    int64_t cnt[OPT_NUM_PHASES] = {0};
     if (!g->recs.empty()) {
         hipError_t e = hipEventSynchronize(g->recs.back().e);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
@@ -1909,14 +1946,20 @@ opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
             float t = 0.f;
             e = hipEventElapsedTime(&t, r.b, r.e);
             if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
-            acc[r.phase] += t;
-            cnt[r.phase] += r.kernels;
+            g->acc_ms[r.phase] += t;
+            g->acc_kernels[r.phase] += r.kernels;
         }
+        g->recs.clear();
     }
+    g->pool_used = 0;
     for (int i = 0; i < OPT_NUM_PHASES; ++i) {
-        if (ms) ms[i] = acc[i];
-        if (launches) launches[i] = cnt[i];
+        if (ms) ms[i] = g->acc_ms[i];
+        if (launches) launches[i] = g->acc_kernels[i];
     }
+    if (g->timing_overflow)
+        return fail(OPT_ESTATE, "timing: more phase scopes than the %d steps the event pool holds were "
+                                "recorded between two reads; the totals miss some",
+                    kTimingSteps);
     return OPT_OK;
 }
 

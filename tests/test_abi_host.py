@@ -145,7 +145,8 @@ def test_workspace_holds_the_copies_of_the_bases(N):
     """The fp32 rotations keep an fp32 U^T (4 m^2 bytes, 256-byte aligned)
     per matrix; the bf16 variant instead keeps bf16 U, U^T, V, V^T (rows
     padded to multiples of 8 elements) and a larger scratch; Muon keeps
-    neither."""
+    neither. The carried rotated momentum adds the work lists of its two
+    kinds of step (its m~ is caller-owned)."""
     shapes = [(130, 67), (64, 64), (24, 40)]
     d = descs(N, shapes)
     base = N.opt_group_workspace_size(d, hp(N))
@@ -155,7 +156,7 @@ def test_workspace_holds_the_copies_of_the_bases(N):
     a256 = lambda x: (x + 255) // 256 * 256
     ut = sum(a256(4 * m * m) for m, _ in shapes)
     bases = sum(2 * 2 * m * r8(m) + 2 * 2 * n * r8(n) for m, n in shapes)
-    assert base > ut and rm == base
+    assert base > ut and base < rm < base + 64 * 1024     # the carried momentum adds only work lists
     assert var >= base - ut + bases
     assert var < base - ut + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
 
@@ -204,6 +205,18 @@ def test_create_rejects_before_any_device_call(N):
     assert err(N, N.opt_group_create, d, h, ws + 8, need, 0) == N.OPT_EINVAL      # not 256-aligned
     d[0].W = ws + 256                                                            # tensor inside workspace
     assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
+    d = descs(N, [(8, 8)], ptrs=True)
+    d[0].W = ws - 64                                  # starts below the workspace, its tail runs into it
+    assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
+    assert "overlaps the workspace" in N.opt_last_error()
+    d = descs(N, [(8, 8)], ptrs=True)
+    hr = hp(N, flags=N.OPT_FLAG_ROTATED_MOMENTUM)
+    need_r = N.opt_group_workspace_size(d, hr)       # no pointer is read: Mt may be unset here
+    d[0].Mt = (1 << 40) + 7 * (1 << 32)
+    assert N.opt_group_workspace_size(d, hr) == need_r
+    d[0].Mt = ws + need_r - 4                         # the carried momentum starts in the last word
+    assert err(N, N.opt_group_create, d, hr, ws, need_r, 0) == N.OPT_EINVAL
+    assert "Mt overlaps the workspace" in N.opt_last_error()
     d = descs(N, [(8, 8)], ptrs=True)
     d[0].M = d[0].M + 1                                                          # misaligned
     assert err(N, N.opt_group_create, d, h, ws, need, 0) == N.OPT_EINVAL
