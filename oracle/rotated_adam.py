@@ -63,6 +63,7 @@ __all__ = [
     "householder_qr",
     "orthonormal_factor",
     "subspace_iteration",
+    "leading_subspace_iteration",
     "refresh_bases",
     "rotated_adam_apply",
     "refresh_due",
@@ -161,7 +162,7 @@ def momentum_update(M, G, beta1: float, m_dtype: str):
                  m_dtype)
 
 
-def householder_qr(Z):
+def householder_qr(Z, q_cols=None):
     """Unblocked Householder QR of a square or tall matrix: Z = Q R.
 
     Column j is reduced by the reflector H_j = I - tau_j v_j v_j^T with
@@ -172,6 +173,11 @@ def householder_qr(Z):
     the reflectors to the identity in reverse order.
 
     Returns (Q, R) with Q of shape (rows, rows) and R of shape (rows, cols).
+    With q_cols = k (at most cols) only the leading k columns of Q are
+    formed, the reflectors applied to the first k columns of the identity:
+    Q is then rows x k. Q[:, j] = H_0 ... H_j e_j depends only on the
+    reflectors of columns 0..j, so these are the leading columns of the
+    full Q.
     """
     A = np.array(Z, dtype=np.float64, copy=True)
     rows, cols = A.shape
@@ -195,8 +201,11 @@ def householder_qr(Z):
         A[j + 1:, j] = 0.0
         A[j, j] = beta
         reflectors.append((v, tau))
-    Q = np.eye(rows)
-    for j in range(cols - 1, -1, -1):
+    k = rows if q_cols is None else q_cols
+    if k > rows or (q_cols is not None and k > cols):
+        raise ValueError("q_cols must not exceed the column count")
+    Q = np.eye(rows, k)
+    for j in range(min(cols, k) - 1, -1, -1):
         v, tau = reflectors[j]
         if v is None:
             continue
@@ -205,15 +214,35 @@ def householder_qr(Z):
     return Q, np.triu(A)
 
 
-def orthonormal_factor(Z):
+def orthonormal_factor(Z, q_cols=None):
     """The Q factor of Z = QR normalised so that diag(R) > 0.
 
     A zero diagonal entry of R counts as positive. For a full-rank square Z
-    this Q is unique, whatever reflector convention produced it.
+    this Q is unique, whatever reflector convention produced it. With
+    q_cols = k only its leading k columns are formed (householder_qr).
     """
-    Q, R = householder_qr(Z)
-    signs = np.where(np.diag(R) < 0.0, -1.0, 1.0)
+    Q, R = householder_qr(Z, q_cols)
+    signs = np.where(np.diag(R)[:Q.shape[1]] < 0.0, -1.0, 1.0)
     return Q * signs[np.newaxis, :]
+
+
+def leading_subspace_iteration(M, X_lead, side: str, passes: int):
+    """The leading k columns of subspace_iteration for the left (side 'U',
+    A = M M^T) or right ('V', A = M^T M) basis of M, for k <= r = min(m, n):
+    the first k columns of a QR factor depend only on the first k columns of
+    its input, and those of A X depend only on those of X, so each pass is
+    Y = A X_lead (formed as M (M^T X_lead) or M^T (M X_lead)) followed by the
+    leading k columns of the positive-diagonal QR of Y. Exactly the
+    iteration's arithmetic restricted to those columns (no completion is
+    needed below the rank)."""
+    M = np.asarray(M, np.float64)
+    X = np.asarray(X_lead, np.float64)
+    if X.shape[1] > min(M.shape):
+        raise ValueError("leading_subspace_iteration needs k <= min(m, n)")
+    for _ in range(passes):
+        Y = M @ (M.T @ X) if side == "U" else M.T @ (M @ X)
+        X = orthonormal_factor(Y, q_cols=Y.shape[1])
+    return X
 
 
 def subspace_iteration(A, X, rank: int, passes: int):

@@ -92,6 +92,48 @@ def test_orthonormal_factor_diagonal_signs():
     assert np.allclose(Q, np.diag([1.0, -1.0, 1.0, -1.0]), atol=0)
 
 
+@pytest.mark.parametrize("rows,cols,k", [(40, 40, 7), (300, 64, 64), (300, 64, 1), (128, 96, 50)])
+def test_thin_orthonormal_factor_matches_lapack_reduced_qr(rows, cols, k):
+    """The leading k columns of the positive-diagonal Q, formed without the
+    rest, against LAPACK's reduced QR (dgeqrf + dorgqr) with the same signs,
+    and against the leading columns of the full factor."""
+    Z = rng(rows + k).standard_normal((rows, cols)) * np.logspace(0, -3, cols)[None, :]
+    Qk = ra.orthonormal_factor(Z, q_cols=k)
+    assert Qk.shape == (rows, k)
+    q, r = np.linalg.qr(Z[:, :k], mode="reduced")
+    q = q * np.where(np.diag(r) < 0, -1.0, 1.0)
+    assert np.max(np.abs(Qk - q)) < 1e-11
+    if rows == cols:
+        assert np.max(np.abs(Qk - ra.orthonormal_factor(Z)[:, :k])) < 1e-13
+
+
+@pytest.mark.parametrize("shape,p,side", [((60, 24), 1, "U"), ((60, 24), 2, "V"), ((24, 60), 3, "U"),
+                                          ((33, 33), 2, "V")])
+def test_leading_subspace_iteration_equals_the_full_iteration(shape, p, side):
+    """The leading k <= r columns of the refresh, iterated on their own,
+    equal those of the full orthogonal iteration with completion, from a
+    random orthogonal start."""
+    m, n = shape
+    M = rng(m * n + p).standard_normal(shape) * np.logspace(0, -1, n)[None, :]
+    d = m if side == "U" else n
+    X0 = rand_orth(d, 3 + p)
+    A = M @ M.T if side == "U" else M.T @ M
+    full = ra.subspace_iteration(A, X0, min(m, n), p)
+    k = min(m, n) - 3
+    lead = ra.leading_subspace_iteration(M, X0[:, :k], side, p)
+    assert np.max(np.abs(lead - full[:, :k])) < 1e-11
+
+
+def test_planted_transposed_gram_in_the_leading_iteration_is_caught(monkeypatch):
+    """The leading-column iteration on the wrong Gram matrix (V's operator
+    for U) fails the comparison with the full iteration."""
+    M = rng(9).standard_normal((30, 30)) * np.logspace(0, -1, 30)[None, :]
+    X0 = rand_orth(30, 4)
+    full = ra.subspace_iteration(M @ M.T, X0, 30, 1)
+    wrong = ra.leading_subspace_iteration(M, X0[:, :10], "V", 1)
+    assert np.max(np.abs(wrong - full[:, :10])) > 1e-3
+
+
 # --------------------------------------------------------------------------
 # Refresh: orthogonal iteration
 # --------------------------------------------------------------------------
