@@ -20,12 +20,18 @@ each gate bounds the error that phase can add:
   previous U, V. (1) orthonormality of the device bases <= 1e-5; (2) forward
   error <= 1e-4 on the well-determined columns, those whose prefix
   conditioning kappa_j = max_{i<=j} 1/|R_ii| of the column-normalised one-shot
-  input [(A^p X)[:, :r] | X[:, r:]] is <= 1e2 (or 8 times the error an fp32
-  CPU refresh, fp32 products and LAPACK QR, reaches there, if larger); the
-  other columns are
-  determined only to O(u kappa) and are not compared (several results are
-  correct there); (3) the device Q must triangularise that input: the
-  strictly lower part of Q^T Z_hat, column-normalised, <= 1e-3.
+  input [(A^p X)[:, :r] | X[:, r:]] is <= 1e2 (or 4 times the error an fp32
+  CPU refresh, fp32 products and LAPACK QR, reaches there, if larger: the
+  device has measured at up to 2.2 times that reference); the other columns
+  are determined only to O(u kappa) and are not compared (several results
+  are correct there). Above order 1100, where the oracle's full unblocked QR
+  takes minutes, the comparison runs on the leading k = min(r, 256) columns,
+  which the oracle forms on their own (the first columns of a QR factor
+  depend only on the first columns of its input); (3) the device Q must
+  triangularise that input: the strictly lower part of Q^T Z_hat,
+  column-normalised, <= 1e-3; (4) the sign convention diag R > 0: every
+  diagonal entry of Q^T Z_hat (column-normalised) larger than 1e-2 in
+  magnitude is positive (smaller ones are sign-ambiguous at fp32 round-off).
 * Gate B16 (the bf16-rotation variant, gate_apply_bf16): as gate B against
   oracle/bf16_rotation.py, with each bf16 intermediate allowed one bf16 ulp
   (a rounding flip) and the errors propagated root-sum-square at 6 sigma.
@@ -37,7 +43,10 @@ each gate bounds the error that phase can add:
   W elementwise: |W - W_ref| <= tau max|W_ref| + 6 lr sqrt((U.U) E^2 (V.V)^T)
   where E_ab = 4 u32 sqrt(m+n) (rms(m~) + |u_ab| sqrt(1-b2) rms(G~)) /
   (sqrt(v_ab) + eps) is the first-order fp32 error of u propagated
-  root-sum-square at 6 sigma; tau = 1e-4 (fp32 momentum) or 2e-2 (bf16).
+  root-sum-square at 6 sigma; tau = 1e-4 for either storage of M. The
+  2e-2 allowed for a bf16 momentum covers its storage rounding, which gate M
+  checks; here the oracle reads the device's own stored M, so the rounding
+  adds nothing and the fp32 tolerance applies.
 """
 
 from __future__ import annotations
@@ -127,48 +136,96 @@ def fp32_refresh(M_t, X_prev, side, passes):
     return X.astype(np.float64)
 
 
-def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True, ref32=None) -> GateReport:
-    """forward=False drops the element-wise comparison with the oracle (for
-    orders where its unblocked QR takes minutes) and keeps the properties
-    that pin the result at any size: orthonormality and triangularisation of
-    the one-shot input."""
+def fp32_refresh_leading(M_t, X_lead, side, passes):
+    """fp32_refresh on the leading k <= r columns alone (fp32 Gram products,
+    LAPACK sgeqrf on the d x k block), as the oracle's leading-column
+    iteration: the fp32 reference of the thin comparison."""
+    import scipy.linalg
+    M = np.asarray(M_t, np.float32)
+    X = np.asarray(X_lead, np.float32)
+    for _ in range(passes):
+        Y = (M @ (M.T @ X) if side == "U" else M.T @ (M @ X)).astype(np.float32)
+        Q, R = scipy.linalg.qr(Y, mode="economic")
+        X = (Q * np.where(np.diag(R) < 0, -1.0, 1.0).astype(np.float32)).astype(np.float32)
+    return X.astype(np.float64)
+
+
+# Factor on what an fp32 CPU refresh reaches, for the forward bound: the
+# device's forward error on the well-determined columns has measured at
+# 0.9-2.2 times that reference's (25 gated bases of orders 67-3072); twice
+# the largest ratio seen.
+FWD_FACTOR = 4.0
+
+# Leading columns compared element by element above the order where the
+# oracle's full QR takes minutes.
+LEAD_COLS = 256
+
+
+def _sign_check(Rd_diag):
+    """diag R > 0: diagonal entries of Q^T Z_hat (column-normalised) above
+    1e-2 in magnitude must be positive; returns (ok, count checked, min)."""
+    big = np.abs(Rd_diag) > 1e-2
+    return bool(np.all(Rd_diag[big] > 0)), int(big.sum()), float(np.min(Rd_diag[big])) if big.any() else 0.0
+
+
+def _forward(X_dev_cols, ref, Zhat_cols, ref32):
+    """Forward error on the well-determined columns among those given and its
+    bound (1e-4, or FWD_FACTOR times what an fp32 reference reaches)."""
+    kappa = _prefix_kappa(Zhat_cols)
+    good = kappa <= 1e2
+    fwd = float(np.max(np.abs(X_dev_cols[:, good] - ref[:, good]))) if good.any() else 0.0
+    fwd_tol = 1e-4
+    if good.any() and ref32 is not None:
+        fwd_tol = max(1e-4, FWD_FACTOR * float(np.max(np.abs(ref32()[:, good] - ref[:, good]))))
+    return fwd, fwd_tol, good
+
+
+def gate_basis(X_dev, A, X_prev, rank, passes, name, forward=True, ref32=None, M_t=None, side=None,
+               ref32_lead=None) -> GateReport:
+    """forward=False compares only the leading k = min(rank, LEAD_COLS)
+    columns with the oracle (for orders where its full unblocked QR takes
+    minutes; needs M_t and side), which the oracle forms on their own.
+    Orthonormality, triangularisation of the one-shot input and the sign
+    convention are checked on the whole basis either way."""
     X_dev = np.asarray(X_dev, np.float64)
+    X_prev = np.asarray(X_prev, np.float64)
     d = X_dev.shape[0]
     orth = float(np.max(np.abs(X_dev.T @ X_dev - np.eye(d))))
-    Zhat = one_shot_input(A, np.asarray(X_prev, np.float64), rank, passes)
-    good = np.zeros(d, bool)
-    fwd = 0.0
-    fwd_tol = 1e-4
+    Zhat = one_shot_input(A, X_prev, rank, passes)
     if forward:
         ref = oracle.subspace_iteration(A, X_prev, rank, passes)
-        kappa = _prefix_kappa(Zhat)
-        good = kappa <= 1e2
-        fwd = float(np.max(np.abs(X_dev[:, good] - ref[:, good]))) if good.any() else 0.0
         # The forward error of an fp32 refresh on these columns grows with the
         # order and the prefix conditioning; near the end of a completed basis
         # the same refresh done in fp32 on the CPU (fp32 Gram products, LAPACK
         # sgeqrf QR) already comes close to 1e-4 (7.5e-5 on a 130 x 130 case).
-        # The bound is therefore 1e-4 or 8 times what that fp32 reference
-        # reaches on the same columns, whichever is larger.
-        if good.any() and ref32 is not None:
-            fwd_tol = max(1e-4, 8.0 * float(np.max(np.abs(ref32()[:, good] - ref[:, good]))))
+        fwd, fwd_tol, good = _forward(X_dev, ref, Zhat, ref32)
+        ncols = d
+    else:
+        k = min(rank, LEAD_COLS)
+        ref = oracle.leading_subspace_iteration(M_t, X_prev[:, :k], side, passes)
+        fwd, fwd_tol, good = _forward(X_dev[:, :k], ref, Zhat[:, :k], ref32_lead)
+        ncols = k
     norms = np.linalg.norm(Zhat, axis=0)
     norms[norms == 0] = 1.0
     Rd = X_dev.T @ (Zhat / norms)
     back = float(np.linalg.norm(np.tril(Rd, -1)) / max(np.linalg.norm(Rd), 1e-300))
-    ok = orth <= 1e-5 and fwd <= fwd_tol and back <= 1e-3
-    return GateReport(name, ok, {"orth": orth, "fwd_good": fwd, "fwd_tol": fwd_tol, "good_cols": float(good.mean()),
-                                 "backward": back})
+    sign_ok, nsign, dmin = _sign_check(np.diag(Rd))
+    ok = orth <= 1e-5 and fwd <= fwd_tol and back <= 1e-3 and sign_ok
+    return GateReport(name, ok, {"orth": orth, "fwd_good": fwd, "fwd_tol": fwd_tol, "fwd_cols": float(ncols),
+                                 "good_cols": float(good.sum()), "backward": back, "diag_min": dmin,
+                                 "sign_cols": float(nsign)})
 
 
 def gate_basis_sampled(X_dev, M_t, X_prev, side, passes, name, nsample=256, seed=0) -> GateReport:
-    """gate_basis without the forward comparison, on sampled rows and columns,
-    for orders where the full d^3 products take minutes on the host: rows S of
-    X^T X - I within 1e-5 of zero, and below the diagonal in columns C of
-    X^T Z_hat (column-normalised) within 1e-3 of their norm. C holds the
-    leading r + 8 columns (where the one-shot input is not the previous basis)
-    and a random sample. The one-shot input is formed from M without building
-    the d x d Gram matrix."""
+    """gate_basis on sampled rows and columns, for orders where the full d^3
+    products take minutes on the host: rows S of X^T X - I within 1e-5 of
+    zero; below the diagonal in columns C of X^T Z_hat (column-normalised)
+    within 1e-3 of their norm, and the diagonal entries of those columns
+    positive where they exceed 1e-2; the leading min(r, 256) columns against
+    the oracle's leading-column iteration (forward bound as gate_basis). C
+    holds the leading r + 8 columns (where the one-shot input is not the
+    previous basis) and a random sample. The one-shot input is formed from M
+    without building the d x d Gram matrix."""
     X_dev = np.asarray(X_dev, np.float64)
     X_prev = np.asarray(X_prev, np.float64)
     M_t = np.asarray(M_t, np.float64)
@@ -188,18 +245,32 @@ def gate_basis_sampled(X_dev, M_t, X_prev, side, passes, name, nsample=256, seed
     Cd = X_dev.T @ (Zc / norms)
     low = np.arange(d)[:, None] > Cols[None, :]
     back = float(np.linalg.norm(Cd[low]) / max(np.linalg.norm(Cd), 1e-300))
-    return GateReport(name, orth <= 1e-5 and back <= 1e-3, {"orth_sampled": orth, "backward_sampled": back,
-                                                           "rows": float(len(S)), "cols": float(len(Cols))})
+    sign_ok, nsign, dmin = _sign_check(Cd[Cols, np.arange(len(Cols))])
+    k = min(r, LEAD_COLS)
+    ref = oracle.leading_subspace_iteration(M_t, X_prev[:, :k], side, passes)
+    fwd, fwd_tol, good = _forward(X_dev[:, :k], ref, Y[:, :k],
+                                  lambda: fp32_refresh_leading(M_t, X_prev[:, :k], side, passes))
+    ok = orth <= 1e-5 and back <= 1e-3 and sign_ok and fwd <= fwd_tol
+    return GateReport(name, ok, {"orth_sampled": orth, "backward_sampled": back, "rows": float(len(S)),
+                                 "cols": float(len(Cols)), "diag_min": dmin, "sign_cols": float(nsign),
+                                 "fwd_good": fwd, "fwd_tol": fwd_tol, "good_cols": float(good.sum())})
 
 
 def gate_refresh(M_t, U_prev, V_prev, U_dev, V_dev, passes, forward_max_d=1100) -> List[GateReport]:
     M_t = np.asarray(M_t, np.float64)
     m, n = M_t.shape
     r = min(m, n)
-    return [gate_basis(U_dev, M_t @ M_t.T, np.asarray(U_prev, np.float64), r, passes, "A.U",
-                       forward=m <= forward_max_d, ref32=lambda: fp32_refresh(M_t, U_prev, "U", passes)),
-            gate_basis(V_dev, M_t.T @ M_t, np.asarray(V_prev, np.float64), r, passes, "A.V",
-                       forward=n <= forward_max_d, ref32=lambda: fp32_refresh(M_t, V_prev, "V", passes))]
+    k = min(r, LEAD_COLS)
+    U_prev = np.asarray(U_prev, np.float64)
+    V_prev = np.asarray(V_prev, np.float64)
+    return [gate_basis(U_dev, M_t @ M_t.T, U_prev, r, passes, "A.U",
+                       forward=m <= forward_max_d, ref32=lambda: fp32_refresh(M_t, U_prev, "U", passes),
+                       M_t=M_t, side="U",
+                       ref32_lead=lambda: fp32_refresh_leading(M_t, U_prev[:, :k], "U", passes)),
+            gate_basis(V_dev, M_t.T @ M_t, V_prev, r, passes, "A.V",
+                       forward=n <= forward_max_d, ref32=lambda: fp32_refresh(M_t, V_prev, "V", passes),
+                       M_t=M_t, side="V",
+                       ref32_lead=lambda: fp32_refresh_leading(M_t, V_prev[:, :k], "V", passes))]
 
 
 def _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau) -> List[GateReport]:
@@ -226,8 +297,7 @@ def _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau) -> List
 
 def gate_apply(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, m_dtype) -> List[GateReport]:
     W_ref, v_ref, it = oracle.rotated_adam_apply(W_prev, v_prev, M_t, G, U_t, V_t, hp.beta2, hp.eps, hp.lr)
-    tau = 1e-4 if m_dtype == "f32" else 2e-2
-    return _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, tau)
+    return _gate_w_v(W_prev, W_ref, v_ref, it, U_t, V_t, W_dev, v_dev, hp, 1e-4)
 
 
 def ulp_bf16(x):

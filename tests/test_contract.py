@@ -170,3 +170,71 @@ def test_sampled_basis_gate_accepts_lapack_and_rejects_swaps():
     skew = q.copy()
     skew[:, 5] += 1e-3 * skew[:, 6]                           # not orthonormal
     assert not contract.gate_basis_sampled(skew, M, X0, "U", 1, "U", nsample=64).ok
+
+
+def test_basis_gate_at_large_orders_compares_leading_columns_and_signs(monkeypatch):
+    """forward=False (orders where the oracle's full QR takes minutes): the
+    leading columns are compared with the oracle's leading-column iteration,
+    and the sign convention is checked on the whole basis. A fp32 LAPACK
+    refresh passes; a perturbed leading column and a flipped completion
+    column fail."""
+    monkeypatch.setattr(contract, "LEAD_COLS", 32)
+    r = rng(40)
+    M = r.standard_normal((300, 120)) * 1e-2
+    X0 = contract.fp32_refresh(M, np.eye(300), "U", 1)         # a warm, non-identity start
+    q = contract.fp32_refresh(M, X0, "U", 2)
+    gate = lambda X: contract.gate_refresh(M, X0, np.eye(120), X, contract.fp32_refresh(M, np.eye(120), "V", 2),
+                                           2, forward_max_d=100)
+    reps = gate(q)
+    assert all(x.ok for x in reps), [str(x) for x in reps]
+    assert reps[0].metrics["fwd_cols"] == 32 and reps[0].metrics["good_cols"] > 0
+    bad = q.copy()
+    bad[:, 3] += 1e-3 * bad[:, 4]
+    assert not gate(bad)[0].ok
+    flipped = q.copy()
+    flipped[:, 250] *= -1                                          # a completion column with the wrong sign
+    rep = gate(flipped)[0]
+    assert not rep.ok and rep.metrics["orth"] <= 1e-5 and rep.metrics["fwd_good"] <= rep.metrics["fwd_tol"]
+
+
+def test_sampled_basis_gate_rejects_a_flipped_sign():
+    r = rng(31)
+    M = r.standard_normal((200, 12)) * 1e-2
+    X0 = np.eye(200)
+    Z = contract.one_shot_input(M @ M.T, X0, 12, 1)
+    q, rr = np.linalg.qr(Z.astype(np.float32))
+    q = (q * np.where(np.diag(rr) < 0, -1, 1)).astype(np.float64)
+    flipped = q.copy()
+    flipped[:, 5] *= -1                                            # leading block: also the forward check
+    assert not contract.gate_basis_sampled(flipped, M, X0, "U", 1, "U", nsample=64).ok
+    flipped = q.copy()
+    flipped[:, 13] *= -1                                           # first completion column (always sampled)
+    rep = contract.gate_basis_sampled(flipped, M, X0, "U", 1, "U", nsample=64)
+    assert not rep.ok and rep.metrics["diag_min"] < 0
+
+
+def test_apply_gate_holds_a_bf16_momentum_to_the_fp32_tolerance():
+    """The oracle reads the device's stored bf16 M, so the rotations see the
+    same values and the fp32 tolerance applies: an fp32 emulation passes and
+    a 1e-3 relative error of the update (inside the old 2e-2 allowance)
+    fails."""
+    r = rng(33)
+    m, n = 24, 40
+    hp = oracle.Hyper()
+    W = oracle.round_f32(r.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(r.random((m, n)) * 1e-6)
+    M = oracle.round_bf16(r.standard_normal((m, n)) * 1e-3)
+    G = oracle.round_f32(r.standard_normal((m, n)) * 1e-3)
+    U = oracle.round_f32(np.linalg.qr(r.standard_normal((m, m)))[0])
+    V = oracle.round_f32(np.linalg.qr(r.standard_normal((n, n)))[0])
+    f = np.float32
+    U32, V32 = U.astype(f), V.astype(f)
+    Gt = U32.T @ G.astype(f) @ V32
+    mt = U32.T @ M.astype(f) @ V32
+    v32 = (f(0.999) * v.astype(f) + f(0.001) * Gt * Gt).astype(f)
+    u = mt / (np.sqrt(v32) + f(1e-8))
+    dW = (U32 @ u @ V32.T).astype(np.float64)
+    W32 = oracle.round_f32(W - f(1e-3) * dW)
+    assert all(x.ok for x in contract.gate_apply(W, v, M, G, U, V, W32, v32.astype(np.float64), hp, "bf16"))
+    off = oracle.round_f32(W - f(1e-3) * dW * (1 + 1e-3))
+    assert not all(x.ok for x in contract.gate_apply(W, v, M, G, U, V, off, v32.astype(np.float64), hp, "bf16"))
