@@ -1563,8 +1563,24 @@ opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
     plan_groups(descs, count, hp, ord, plan);
     opt_group_s tmp;
     tmp.hp = *hp;
+    // The tables are built and thrown away: tensor pointers the caller has
+    // not set yet get a stand-in address (256-byte aligned, like a real
+    // allocation, and never dereferenced) so that no address arithmetic
+    // starts from a null pointer.
+    const uintptr_t stand_in = kAlign << 4;
+    auto or_stand_in = [&](auto* p) { return p ? p : (decltype(p))stand_in; };
     for (int i = 0; i < count; ++i) {
-        Mat M{descs[i], i, 0.0, descs[i].M_dtype == OPT_BF16};
+        opt_matrix_desc x = descs[i];
+        x.W = or_stand_in(x.W);
+        x.G = or_stand_in(x.G);
+        x.M = or_stand_in(x.M);
+        if (!(hp->flags & OPT_FLAG_MUON)) {
+            x.v = or_stand_in(x.v);
+            x.U = or_stand_in(x.U);
+            x.V = or_stand_in(x.V);
+        }
+        if (hp->flags & OPT_FLAG_ROTATED_MOMENTUM) x.Mt = or_stand_in(x.Mt);
+        Mat M{x, i, 0.0, x.M_dtype == OPT_BF16};
         tmp.mats.push_back(M);
     }
     build(&tmp, plan, (char*)(uintptr_t)kAlign);
