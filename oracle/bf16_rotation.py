@@ -6,37 +6,33 @@ import or call this module; it shares no code with the HIP path.
 [P3] "Pipeline parallelism and gradient staleness optimisation in distributed
 training", section 3.1 (mixed-precision configuration), keeps the rotation
 matrices in a 16-bit float format, on the grounds that the rotation is
-insensitive to their rounding. This variant takes that further: the two-sided
-rotations themselves run on 16-bit operands with binary32 accumulation. The
-16-bit format is bfloat16 rather than the page's float16 (a reading): a matrix
-product needs both operands in one format, the momentum is already bfloat16
-([P2] "Large-model distributed optimisation: three-layer decoupling of
-communication, memory and compute", section 3.3), and bfloat16 keeps the
-binary32 exponent range, so gradients need no scaling. The binary32 bases U,
-V stay the master copies that the refresh starts from; the rotations use
-their bfloat16 roundings.
+insensitive to their rounding. That is all this oracle rounds beyond the
+method: the step rotates with the 16-bit bases Ub = rb(U), Vb = rb(V) (rb =
+round to bfloat16, ties to even; bfloat16 rather than the page's float16 is a
+reading: it keeps the binary32 exponent range and is the momentum's format in
+[P2] "Large-model distributed optimisation: three-layer decoupling of
+communication, memory and compute", section 3.3), and every product is exact:
 
-The rounding points, in order (rb = round to bfloat16, ties to even):
-
-    Ub = rb(U), Vb = rb(V), Gb = rb(G), Mb = rb(M)
-    SG = rb(Gb Vb),  SM = rb(Mb Vb)              right rotation, stored bf16
-    G~ = Ub^T SG,    m~ = Ub^T SM                left rotation, binary32 out
+    Ub = rb(U), Vb = rb(V)
+    G~ = Ub^T G Vb,  m~ = Ub^T M Vb              (M as stored: bf16 or binary32)
     v  <- rf(b2 v + (1 - b2) G~^2);  u = m~ / (sqrt(v) + eps)
-    P  = rb(rb(u) Vb^T)                           right rotation back, bf16
-    W  <- rf(W - lr Ub P)                         left rotation back + apply
+    W  <- rf(W - lr Ub u Vb^T)
 
-Products are exact (float64) on the rounded operands; the device accumulates
-them in binary32, which differs from exact far below one bfloat16 ulp.
+The device computes these products on bf16 operands with binary32
+accumulation, so it also rounds G (and an fp32 M), the right rotations G Vb
+and M Vb, u and u Vb^T to bfloat16. Those roundings are an implementation's,
+not the method's: the parity gate bounds them as errors (tests/contract.py,
+gate_apply_bf16) instead of this oracle reproducing them.
 
 The first step (t = 1) runs the method's own binary32 rotations. There v is
 zero, so u = m~ / (sqrt(v) + eps) turns every entry of G~ that is zero in
 exact arithmetic (after the step-1 refresh from M = (1 - b1) G, all of G~ off
 its leading diagonal) into (1 - b1) / sqrt(1 - b2) times the sign of its
-rounding error whenever that error exceeds eps / sqrt(1 - b2); bfloat16
-rounding errors of the rotation do (2^-9 |G| against 3e-7 for the default
-eps), which would make the first update a full-size step in roundoff
-directions. From t = 2 on v holds the first step's squares and the rounding
-enters only at its own relative size.
+rounding error whenever that error exceeds eps / sqrt(1 - b2); a rotation
+with 16-bit bases has errors of that size (2^-9 relative against 3e-7 for the
+default eps), which would make the first update a full-size step in
+roundoff directions. From t = 2 on v holds the first step's squares and the
+rounding enters only at its own relative size.
 """
 
 from __future__ import annotations
@@ -51,30 +47,27 @@ __all__ = ["bf16_rotation_apply", "step_bf16_rotation", "bf16_rotated_momentum_a
 
 
 def bf16_rotation_apply(W, v, M, G, U, V, beta2: float, eps: float, lr: float):
-    """Rotate, run the Adam moments and apply, with the rotations on bfloat16
-    operands at the rounding points listed in the module docstring.
+    """Rotate, run the Adam moments and apply with the bases rounded to
+    bfloat16, every product exact (the module docstring's formulas).
 
     Returns (W_new, v_new, intermediates) with the float64 values of Ub, Vb,
-    SG, SM, Gt, mt, u, ub, P and dW = Ub P."""
+    SG = G Vb, SM = M Vb, Gt, mt, u, P = u Vb^T and dW = Ub P."""
     b2 = as_f32_scalar(beta2)
     eps = as_f32_scalar(eps)
     lr = as_f32_scalar(lr)
     Ub = round_bf16(U)
     Vb = round_bf16(V)
-    Gb = round_bf16(G)
-    Mb = round_bf16(M)
-    SG = round_bf16(Gb @ Vb)
-    SM = round_bf16(Mb @ Vb)
+    SG = np.asarray(G, np.float64) @ Vb
+    SM = np.asarray(M, np.float64) @ Vb
     Gt = Ub.T @ SG
     mt = Ub.T @ SM
     v_new = round_f32(b2 * np.asarray(v, np.float64) + (1.0 - b2) * (Gt * Gt))
     u = mt / (np.sqrt(v_new) + eps)
-    ub = round_bf16(u)
-    P = round_bf16(ub @ Vb.T)
+    P = u @ Vb.T
     dW = Ub @ P
     W_new = round_f32(np.asarray(W, np.float64) - lr * dW)
     return W_new, v_new, {"Ub": Ub, "Vb": Vb, "SG": SG, "SM": SM, "Gt": Gt, "mt": mt, "u": u,
-                          "ub": ub, "P": P, "dW": dW}
+                          "P": P, "dW": dW}
 
 
 def step_bf16_rotation(state: OracleState, G, hp: Hyper) -> OracleState:
@@ -95,32 +88,31 @@ def step_bf16_rotation(state: OracleState, G, hp: Hyper) -> OracleState:
 
 def bf16_rotated_momentum_apply(W, v, mt_prev, M, G, U, V, beta1: float, beta2: float, eps: float, lr: float,
                                 recompute: bool):
-    """Both variants together: the rotations on bf16 operands as in
+    """Both variants together: the bases rounded to bfloat16 as in
     bf16_rotation_apply, and m~ carried in binary32 within a basis epoch as
-    in oracle/rotated_momentum.py. recompute: m~ = rf(Ub^T rb(rb(M) Vb));
-    otherwise m~ = rf(b1 m~_prev + (1 - b1) G~), with G~ = Ub^T rb(rb(G) Vb).
-    Returns (W_new, v_new, mt_new, intermediates)."""
+    in oracle/rotated_momentum.py. recompute: m~ = rf(Ub^T M Vb); otherwise
+    m~ = rf(b1 m~_prev + (1 - b1) G~), with G~ = Ub^T G Vb. Every product
+    exact. Returns (W_new, v_new, mt_new, intermediates)."""
     b1 = as_f32_scalar(beta1)
     b2 = as_f32_scalar(beta2)
     eps = as_f32_scalar(eps)
     lr = as_f32_scalar(lr)
     Ub = round_bf16(U)
     Vb = round_bf16(V)
-    SG = round_bf16(round_bf16(G) @ Vb)
+    SG = np.asarray(G, np.float64) @ Vb
     Gt = Ub.T @ SG
     if recompute:
-        SM = round_bf16(round_bf16(M) @ Vb)
+        SM = np.asarray(M, np.float64) @ Vb
         mt = round_f32(Ub.T @ SM)
     else:
         SM = None
         mt = round_f32(b1 * np.asarray(mt_prev, np.float64) + (1.0 - b1) * Gt)
     v_new = round_f32(b2 * np.asarray(v, np.float64) + (1.0 - b2) * (Gt * Gt))
     u = mt / (np.sqrt(v_new) + eps)
-    ub = round_bf16(u)
-    P = round_bf16(ub @ Vb.T)
+    P = u @ Vb.T
     dW = Ub @ P
     W_new = round_f32(np.asarray(W, np.float64) - lr * dW)
-    return W_new, v_new, mt, {"Ub": Ub, "Vb": Vb, "SG": SG, "SM": SM, "Gt": Gt, "mt": mt, "u": u, "ub": ub,
+    return W_new, v_new, mt, {"Ub": Ub, "Vb": Vb, "SG": SG, "SM": SM, "Gt": Gt, "mt": mt, "u": u,
                               "P": P, "dW": dW}
 
 

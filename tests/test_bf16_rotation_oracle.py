@@ -1,10 +1,12 @@
 """Pins of the bf16-rotation variant's oracle (CPU).
 
-The variant rounds its rotation operands and intermediates to bfloat16. Where
-every rounding is exact (bfloat16-representable inputs rotated by signed
-permutations) it must equal the method with only u rounded; with identity
-bases it must be coordinate-wise Adam with a rounded u; its first step is the
-method's; elsewhere it must stay within bfloat16 rounding of the method.
+The variant is the method with its rotation matrices stored in 16-bit floats
+(the pipeline-staleness page, section 3.1): U and V are rounded to bfloat16
+and nothing else. Where that rounding is exact (signed-permutation or
+identity bases) it must be bitwise the method; its result must depend on U,
+V only through their roundings; a brute-force Kronecker evaluation of the
+two-sided rotation must agree on tiny inputs; its first step is the method's;
+elsewhere it must stay within the bases' rounding of the method.
 """
 
 import numpy as np
@@ -24,35 +26,33 @@ def signed_permutation(d, rng):
 
 
 @pytest.mark.parametrize("shape", [(6, 9), (9, 6), (8, 8)])
-def test_signed_permutation_bases_are_the_method_with_rounded_u(shape):
-    """Signed permutations are orthogonal and exact in bfloat16, and so are
-    the products of bfloat16 matrices with them: every rounding point except
-    u is exact, so v is bitwise the method's and W the method's update with
-    u rounded to bfloat16. The bases are not symmetric, so a transposed
-    basis anywhere in the variant changes the result."""
+def test_signed_permutation_bases_are_the_method(shape):
+    """Signed permutations are orthogonal and exact in bfloat16, so rounding
+    the bases changes nothing: W, v and every intermediate are bitwise the
+    method's. The bases are not symmetric, so a transposed basis anywhere in
+    the variant changes the result; u is not bfloat16-representable, so a
+    rounding of u (not part of the method) would show."""
     m, n = shape
     rng = np.random.default_rng(3)
     U = signed_permutation(m, rng)
     V = signed_permutation(n, rng)
     assert not np.array_equal(U, U.T) and not np.array_equal(V, V.T)
-    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
     M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
     W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
     v = oracle.round_f32(rng.random((m, n)) * 1e-5)
     Wm, vm, im = oracle.rotated_adam_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
     Wb, vb, ib = B.bf16_rotation_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
-    assert np.array_equal(vb, vm)
-    assert np.array_equal(ib["Gt"], im["Gt"]) and np.array_equal(ib["mt"], im["mt"])
-    lr = oracle.as_f32_scalar(HP.lr)
-    expect = oracle.round_f32(W - lr * (U @ oracle.round_bf16(im["u"]) @ V.T))
-    assert np.array_equal(Wb, expect)
-    assert not np.array_equal(oracle.round_bf16(im["u"]), im["u"])   # the rounding of u is exercised
+    assert np.array_equal(vb, vm) and np.array_equal(Wb, Wm)
+    for k in ("Gt", "mt", "u", "dW"):
+        assert np.array_equal(ib[k], im[k]), k
+    assert not np.array_equal(oracle.round_bf16(im["u"]), im["u"])
 
 
-def test_identity_bases_are_coordinatewise_adam_with_rounded_u():
+def test_identity_bases_are_coordinatewise_adam():
     m, n = 5, 7
     rng = np.random.default_rng(4)
-    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    G = textbook.f32(rng.standard_normal((m, n)) * 1e-2)
     M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
     W = textbook.f32(rng.standard_normal((m, n)) * 1e-2)
     v = textbook.f32(rng.random((m, n)) * 1e-5)
@@ -61,9 +61,78 @@ def test_identity_bases_are_coordinatewise_adam_with_rounded_u():
     for i in range(m):
         for j in range(n):
             vij = textbook.f32(b2 * v[i, j] + (1.0 - b2) * G[i, j] * G[i, j])
-            uij = oracle.round_bf16(np.array([M[i, j] / (np.sqrt(vij) + e)]))[0]
+            uij = M[i, j] / (np.sqrt(vij) + e)
             assert vb[i, j] == vij
             assert Wb[i, j] == textbook.f32(W[i, j] - a * uij)
+
+
+def test_result_depends_on_the_bases_only_through_their_roundings():
+    """The 16-bit storage of the bases is the only rounding the variant adds:
+    passing rb(U), rb(V) instead of U, V gives bitwise the same step, and
+    random orthogonal bases are not bfloat16-exact, so the step differs from
+    the method's."""
+    m, n = 12, 20
+    rng = np.random.default_rng(14)
+    U, V = rand_q(m, rng), rand_q(n, rng)
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(rng.random((m, n)) * 1e-5)
+    a = B.bf16_rotation_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    b = B.bf16_rotation_apply(W, v, M, G, oracle.round_bf16(U), oracle.round_bf16(V), HP.beta2, HP.eps, HP.lr)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    Wm, _, _ = oracle.rotated_adam_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    assert not np.array_equal(a[0], Wm)
+
+
+def test_two_sided_rotation_by_kronecker_brute_force():
+    """vec(Ub^T X Vb) = (Vb kron Ub)^T vec(X) and vec(Ub u Vb^T) = (Vb kron
+    Ub) vec(u) (column-major vec): the rotations evaluated as one Kronecker
+    matrix-vector product per operand, on tiny random orthogonal bases,
+    against the oracle's two-sided products."""
+    m, n = 3, 5
+    rng = np.random.default_rng(15)
+    U, V = rand_q(m, rng), rand_q(n, rng)
+    Ub, Vb = oracle.round_bf16(U), oracle.round_bf16(V)
+    K = np.kron(Vb, Ub)
+    vec = lambda X: X.reshape(-1, order="F")
+    unvec = lambda x: x.reshape((m, n), order="F")
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
+    v = oracle.round_f32(rng.random((m, n)) * 1e-5)
+    _, _, it = B.bf16_rotation_apply(W, v, M, G, U, V, HP.beta2, HP.eps, HP.lr)
+    assert np.max(np.abs(unvec(K.T @ vec(G)) - it["Gt"])) <= 1e-16
+    assert np.max(np.abs(unvec(K.T @ vec(M)) - it["mt"])) <= 1e-16
+    assert np.max(np.abs(unvec(K @ vec(it["u"])) - it["dW"])) <= 1e-12 * np.max(np.abs(it["dW"]))
+
+
+def test_planted_rounding_of_u_is_caught(monkeypatch):
+    """The old reading rounded u (and the right rotations) to bfloat16 as the
+    device stores them: the signed-permutation pin rejects it."""
+    real = B.bf16_rotation_apply
+
+    def rounding_u(W, v, M, G, U, V, beta2, eps, lr):
+        W1, v1, it = real(W, v, M, G, U, V, beta2, eps, lr)
+        ub = oracle.round_bf16(it["u"])
+        dW = it["Ub"] @ ub @ it["Vb"].T
+        return oracle.round_f32(W - oracle.as_f32_scalar(lr) * dW), v1, dict(it, u=ub, dW=dW)
+    monkeypatch.setattr(B, "bf16_rotation_apply", rounding_u)
+    with pytest.raises(AssertionError):
+        test_signed_permutation_bases_are_the_method((6, 9))
+
+
+def test_planted_unrounded_left_basis_is_caught(monkeypatch):
+    """A variant that forgets to round U fails the roundings-only pin."""
+    real_round = oracle.round_bf16
+    calls = {"n": 0}
+
+    def skip_first(x):
+        calls["n"] += 1
+        return np.asarray(x, np.float64) if calls["n"] % 2 == 1 else real_round(x)   # Ub unrounded
+    monkeypatch.setattr(B, "round_bf16", skip_first)
+    with pytest.raises(AssertionError):
+        test_result_depends_on_the_bases_only_through_their_roundings()
 
 
 def _trajectories(m, n, steps, seed, m_dtype="bf16"):
@@ -91,9 +160,10 @@ def test_first_step_is_the_method():
 def test_apply_within_bf16_rounding_of_the_method(shape):
     """From the same established state (v from three earlier steps), the
     variant's update differs from the method's by the bfloat16 roundings of
-    its eight operands and intermediates, each at most 2^-9 relative: the
-    update within 8 * 2^-9 in Frobenius norm, v within 2^-6 of its maximum
-    (G~ enters squared)."""
+    the bases, each entry at most 2^-9 relative, which enter the update four
+    times (two in G~ through u's denominator, two in m~ and the rotation
+    back): the update within 8 * 2^-9 in Frobenius norm, v within 2^-6 of its
+    maximum (G~ enters squared)."""
     m, n = shape
     rng = np.random.default_rng(6)
     st = oracle.OracleState.fresh(rng.standard_normal((m, n)) * 1e-2, "bf16")
@@ -140,15 +210,14 @@ def test_first_step_in_bf16_would_be_dominated_by_roundoff():
 # ---- both variants together: bf16 rotations and the carried m~ -------------
 
 @pytest.mark.parametrize("recompute", [True, False])
-def test_combined_signed_permutation_bases_are_the_carried_method_with_rounded_u(recompute):
-    """With signed-permutation bases and bf16-exact G and M every rounding
-    except u's is exact, so the combination equals the fp32 carried-momentum
-    oracle with u rounded: m~ and v bitwise, W with rb(u)."""
+def test_combined_signed_permutation_bases_are_the_carried_method(recompute):
+    """With signed-permutation bases the combination equals the fp32
+    carried-momentum oracle bitwise: m~, v and W."""
     from oracle import rotated_momentum as RM
     m, n = 7, 10
     rng = np.random.default_rng(11)
     U, V = signed_permutation(m, rng), signed_permutation(n, rng)
-    G = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    G = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
     M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
     W = oracle.round_f32(rng.standard_normal((m, n)) * 1e-2)
     v = oracle.round_f32(rng.random((m, n)) * 1e-5)
@@ -156,9 +225,7 @@ def test_combined_signed_permutation_bases_are_the_carried_method_with_rounded_u
     Wr, vr, mtr, ir = RM.rotated_momentum_apply(W, v, mt0, M, G, U, V, HP.beta1, HP.beta2, HP.eps, HP.lr, recompute)
     Wb, vb, mtb, ib = B.bf16_rotated_momentum_apply(W, v, mt0, M, G, U, V, HP.beta1, HP.beta2, HP.eps, HP.lr,
                                                     recompute)
-    assert np.array_equal(mtb, mtr) and np.array_equal(vb, vr)
-    lr = oracle.as_f32_scalar(HP.lr)
-    assert np.array_equal(Wb, oracle.round_f32(W - lr * (U @ oracle.round_bf16(ir["u"]) @ V.T)))
+    assert np.array_equal(mtb, mtr) and np.array_equal(vb, vr) and np.array_equal(Wb, Wr)
 
 
 def test_combined_recompute_is_the_bf16_variant():
