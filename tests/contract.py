@@ -33,8 +33,10 @@ each gate bounds the error that phase can add:
   diagonal entry of Q^T Z_hat (column-normalised) larger than 1e-2 in
   magnitude is positive (smaller ones are sign-ambiguous at fp32 round-off).
 * Gate B16 (the bf16-rotation variant, gate_apply_bf16): as gate B against
-  oracle/bf16_rotation.py, with each bf16 intermediate allowed one bf16 ulp
-  (a rounding flip) and the errors propagated root-sum-square at 6 sigma.
+  oracle/bf16_rotation.py (the method with U, V rounded to bfloat16, products
+  exact); the device's own bf16 roundings of G, M and the intermediates are
+  bounded as errors (half an ulp each, the input roundings carried exactly)
+  and propagated root-sum-square at 6 sigma.
 * Gate MU (the orthogonalised-momentum step, gate_muon): W within
   lr 1e-4 max|O| plus one binary32 rounding of the oracle's Newton-Schulz
   result from the device's M_t.
@@ -312,17 +314,19 @@ def ulp_bf16(x):
 
 def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.Hyper, tau=1e-3,
                     Mt_prev=None, Mt_dev=None, recompute=True) -> List[GateReport]:
-    """The bf16-rotation variant (oracle/bf16_rotation.py), teacher-forced
-    like gate_apply. The device rounds the same quantities to bf16 but from
-    binary32 accumulations, so each stored bf16 intermediate (S = rb(X Vb),
-    u, P = rb(ub Vb^T)) may sit one bf16 ulp from the oracle's where the
-    accumulation crosses a rounding boundary. The model gives every such
-    element its full ulp (an upper bound on a flip) plus the binary32
-    accumulation error 4 u32 sqrt(K) of each product, propagates them root-
-    sum-square through the products (G~ = Ub^T S, P, dW = Ub P) and through u
-    as in gate B, and bounds W element-wise by
-    lr (tau max|dW_ref| + 6 e_dW) + 2^-23 |W_ref| (one binary32 rounding of W)
-    and v by (1 - b2) 2 |G~| 6 e_G~ + 2^-23 |v_ref| + 1e-6 max|v_ref|.
+    """The bf16-rotation variant (oracle/bf16_rotation.py: the method with U
+    and V rounded to bfloat16, every product exact), teacher-forced like
+    gate_apply. The device runs the products on bfloat16 operands with
+    binary32 accumulation, so it also rounds G (and an fp32 M) and the
+    intermediates S = X Vb (X in {G, M}), u and P = u Vb^T to bfloat16; the
+    oracle does not. The gate bounds that: each device rounding is at most
+    half a bf16 ulp of its value, the known rounding errors of G and M are
+    carried through the right rotation exactly (|(rb(X) - X) Vb|), and each
+    product adds its binary32 accumulation error 4 u32 sqrt(K); errors are
+    propagated root-sum-square through the products (G~ = Ub^T S, P, dW =
+    Ub P) and through u as in gate B, and W is bounded element-wise by
+    lr (tau max|dW_ref| + 6 e_dW) + 2^-23 |W_ref| (one binary32 rounding of
+    W), v by (1 - b2) 2 |G~| 6 e_G~ + 2^-23 |v_ref| + 1e-6 max|v_ref|.
 
     With Mt_dev (the carried rotated momentum as well): the oracle is
     bf16_rotated_momentum_apply from the device's Mt_prev; a carried m~ has
@@ -344,18 +348,24 @@ def gate_apply_bf16(W_prev, v_prev, M_t, G, U_t, V_t, W_dev, v_dev, hp: oracle.H
     m, n = Ub.shape[0], Vb.shape[0]
     U2, V2 = Ub * Ub, Vb * Vb
     rss = lambda A2, B2: np.sqrt(A2 @ B2)
-    Gb = oracle.round_bf16(G)
-    eSG = ulp_bf16(it["SG"]) + 4 * U32 * np.sqrt(n) * rss(Gb * Gb, V2)
+    half = lambda x: 0.5 * ulp_bf16(x)
+
+    def right_rotation_error(X, S):
+        """Device rb(rb(X) Vb) against the exact X Vb."""
+        X = np.asarray(X, np.float64)
+        D = oracle.round_bf16(X) - X
+        return np.abs(D @ Vb) + half(S) + 4 * U32 * np.sqrt(n) * rss(X * X, V2)
+
+    eSG = right_rotation_error(G, it["SG"])
     eGt = rss(U2.T, eSG ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SG"] ** 2)
     if carried and not recompute:
         emt = (1 - b1) * eGt
     else:
-        Mb = oracle.round_bf16(M_t)
-        eSM = ulp_bf16(it["SM"]) + 4 * U32 * np.sqrt(n) * rss(Mb * Mb, V2)
+        eSM = right_rotation_error(M_t, it["SM"])
         emt = rss(U2.T, eSM ** 2) + 4 * U32 * np.sqrt(m) * rss(U2.T, it["SM"] ** 2)
     u = it["u"]
-    Eu = ulp_bf16(u) + (emt + np.abs(u) * np.sqrt(1 - b2) * eGt) / (np.sqrt(v_ref) + eps)
-    eP = rss(Eu ** 2, V2.T) + ulp_bf16(it["P"]) + 4 * U32 * np.sqrt(n) * rss(it["ub"] ** 2, V2.T)
+    Eu = half(u) + (emt + np.abs(u) * np.sqrt(1 - b2) * eGt) / (np.sqrt(v_ref) + eps)
+    eP = rss(Eu ** 2, V2.T) + half(it["P"]) + 4 * U32 * np.sqrt(n) * rss(u ** 2, V2.T)
     edW = rss(U2, eP ** 2) + 4 * U32 * np.sqrt(m) * rss(U2, it["P"] ** 2)
     bound_w = lr * (tau * np.max(np.abs(it["dW"])) + 6 * edW) + 2.0 ** -23 * np.abs(W_ref)
     err_w = np.abs(np.asarray(W_dev, np.float64) - W_ref)
