@@ -320,6 +320,21 @@ opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes);
 opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
                               uint64_t workspace_bytes, void* stream);
 
+/* opt_orthonormalize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The QR job record and scratch live in a
+ * fixed device array inside the library, sized for one matrix of order
+ * OPT_STATIC_MAX_DIM (about 34 MiB); every GPU the library runs on holds its
+ * own copy until the process ends. Same kernels and results as
+ * opt_orthonormalize. d > OPT_STATIC_MAX_DIM returns OPT_EUNSUPPORTED; no
+ * device memory is allocated or freed. The array keeps whatever the last call
+ * left in it (no kernel relies on its contents at entry), and all calls on one
+ * GPU share it: calls that overlap in time on one GPU (different streams or
+ * host threads without synchronisation between them) race and must not be
+ * made. Enqueues on `stream`. */
+#define OPT_STATIC_MAX_DIM 4096
+opt_status opt_orthonormalize_static(float* Z, float* Q, int64_t d, void* stream);
+
 /* ---- cross-rank planners (host only; no device memory, no stream) -------
  * A job that shards its matrices over several ranks plans once, on the host,
  * which rank steps which whole matrix; each rank then runs a group over its

@@ -23,6 +23,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <utility>
@@ -55,7 +56,7 @@ opt_status hip_fail(hipError_t e, const char* where) {
 }
 
 constexpr uint64_t kAlign = 256;
-uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+constexpr uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -572,7 +573,7 @@ uint64_t bases16_bytes(int64_t m, int64_t n) {
     return 2 * align_up(2ull * m * round8(m)) + 2 * align_up(2ull * n * round8(n));
 }
 
-int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
+constexpr int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
 
 // Long products are split along K into chunks run as successive launches
 // that accumulate into C (beta = 1 after the first chunk): each launch's fp32
@@ -626,14 +627,14 @@ void add_k_chunked(std::vector<std::vector<PGemm>>& steps, const PGemm& g) {
 
 
 
-int qr_blocks(int d) { return (d + kQrNB - 1) / kQrNB; }
+constexpr int qr_blocks(int d) { return (d + kQrNB - 1) / kQrNB; }
 
 struct QrBytes {
     uint64_t Z, T, part, W2, Yb, Wb, W2b, Sb;
-    uint64_t scratch() const { return T + part + W2 + Yb + Wb + W2b + Sb; }   // all but Z
+    constexpr uint64_t scratch() const { return T + part + W2 + Yb + Wb + W2b + Sb; }   // all but Z
 };
-QrBytes qr_job_bytes(int64_t d) {
-    QrBytes b;
+constexpr QrBytes qr_job_bytes(int64_t d) {
+    QrBytes b{};
     b.Z = align_up(4ull * d * d);
     b.T = align_up(4ull * panels((int)d) * kQrPB * kQrPB);
     b.part = align_up(4ull * kQrMaxSplits * kQrPB * d);
@@ -2077,24 +2078,18 @@ namespace {
 __global__ void put_job_kernel(QrJob* dst, QrJob val) { *dst = val; }
 }  // namespace
 
-extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
-                                         uint64_t workspace_bytes, void* stream) {
-    uint64_t need = 0;
-    if (opt_status st = opt_orthonormalize_workspace_size(d, &need)) return st;
-    if (!Z || !Q || !workspace) return fail(OPT_EINVAL, "a pointer is NULL");
-    if (!aligned(workspace, kAlign)) return fail(OPT_EINVAL, "workspace must be 256-byte aligned");
-    if (workspace_bytes < need) return fail(OPT_ENOWS, "workspace too small: %llu < %llu",
-                                            (unsigned long long)workspace_bytes, (unsigned long long)need);
+namespace {
+// The QR of one d x d matrix with its job record and scratch at `workspace`
+// (at least opt_orthonormalize_workspace_size(d) bytes, 256-byte aligned).
+opt_status orthonormalize_in(float* Z, float* Q, int64_t d, char* w, hipStream_t s) {
     const uintptr_t zl = (uintptr_t)Z, zh = zl + 4ull * d * d, ql = (uintptr_t)Q, qh = ql + 4ull * d * d;
     if (zl < qh && ql < zh) return fail(OPT_EINVAL, "Z and Q overlap");
-    char* w = (char*)workspace;
     QrJob j{};
     j.Z = Z;
     j.X = Q;
     j.d = (int32_t)d;
     j.np = panels((int)d);
     qr_assign_scratch(j, w + align_up(sizeof(QrJob)));
-    hipStream_t s = (hipStream_t)stream;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before orthonormalize");
     hipLaunchKernelGGL(put_job_kernel, dim3(1), dim3(1), 0, s, (QrJob*)w, j);
@@ -2114,4 +2109,70 @@ extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* wo
     };
     if ((e = run_qr((const QrJob*)w, np, dd, s, steps))) return hip_fail(e, "QR launch");
     return OPT_OK;
+}
+}  // namespace
+
+extern "C" opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
+                                         uint64_t workspace_bytes, void* stream) {
+    uint64_t need = 0;
+    if (opt_status st = opt_orthonormalize_workspace_size(d, &need)) return st;
+    if (!Z || !Q || !workspace) return fail(OPT_EINVAL, "a pointer is NULL");
+    if (!aligned(workspace, kAlign)) return fail(OPT_EINVAL, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need) return fail(OPT_ENOWS, "workspace too small: %llu < %llu",
+                                            (unsigned long long)workspace_bytes, (unsigned long long)need);
+    return orthonormalize_in(Z, Q, d, (char*)workspace, (hipStream_t)stream);
+}
+
+// ------------------------------------------ the entry point that allocates nothing ----
+//
+// opt_orthonormalize_static keeps its QR job record and scratch in `scratch`,
+// a file-scope device array sized for one job of order OPT_STATIC_MAX_DIM.
+// Each GPU the library runs on holds its own copy until the process ends. In
+// host code the array's name is only a host-side stand-in, so its device
+// address on each device is taken once with hipGetSymbolAddress (with that
+// device current) and only that address is passed to kernels.
+
+namespace {
+constexpr uint64_t kStaticScratchBytes = align_up(sizeof(QrJob)) + qr_job_bytes(OPT_STATIC_MAX_DIM).scratch();
+static_assert(kStaticScratchBytes <= (40ull << 20), "the fixed scratch is meant to stay modest");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+// The current device's address of `scratch`, looked up on its first use there.
+opt_status static_scratch(char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(OPT_EUNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || !aligned(p, kAlign)) return fail(OPT_EHIP, "scratch has no aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = (char*)g_scratch_ptr[dev];
+    return OPT_OK;
+}
+}  // namespace
+
+extern "C" opt_status opt_orthonormalize_static(float* Z, float* Q, int64_t d, void* stream) {
+    if (d < 1) return fail(OPT_EINVAL, "d must be >= 1");
+    if (d > OPT_STATIC_MAX_DIM)
+        return fail(OPT_EUNSUPPORTED,
+                    "d = %lld exceeds %d, the largest order the fixed scratch of opt_orthonormalize_static "
+                    "holds (use opt_orthonormalize with a workspace)",
+                    (long long)d, OPT_STATIC_MAX_DIM);
+    if (!Z || !Q) return fail(OPT_EINVAL, "a pointer is NULL");
+    static_assert(align_up(sizeof(QrJob)) + qr_job_bytes(1).scratch() <= kStaticScratchBytes, "");
+    char* w = nullptr;
+    if (opt_status st = static_scratch(&w)) return st;
+    return orthonormalize_in(Z, Q, d, w, (hipStream_t)stream);
 }

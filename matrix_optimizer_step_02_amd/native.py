@@ -21,6 +21,7 @@ OPT_FLAG_BF16_ROTATION = 2
 OPT_FLAG_MUON = 4
 OPT_FLAG_FP32_MFMA = 8
 OPT_MAX_DIM = 16384
+OPT_STATIC_MAX_DIM = 4096
 PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho", "rot_pieced")
 OPT_NUM_PHASES = len(PHASES)
 
@@ -30,6 +31,7 @@ EXPORTED = (
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
     "opt_gemm", "opt_gemm_x6", "opt_gemm_bf16", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
     "opt_partition_dp", "opt_plan_host_ranks", "opt_group_health", "opt_group_reorthonormalize",
+    "opt_orthonormalize_static",
 )
 
 
@@ -96,6 +98,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "opt_gemm_bf16": ([i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i32, i64, vp], i32),
         "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
         "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
+        "opt_orthonormalize_static": ([vp, vp, i64, vp], i32),
         "opt_group_health": ([vp, C.POINTER(opt_health), vp], i32),
         "opt_group_reorthonormalize": ([vp, i32, vp], i32),
         "opt_partition_dp": ([C.POINTER(C.c_double), i64, C.POINTER(i64), i32, i32, C.c_double,
@@ -229,6 +232,10 @@ def opt_orthonormalize_workspace_size(d: int) -> int:
 def opt_orthonormalize(Z: int, Q: int, d: int, workspace: int, workspace_bytes: int, stream_ptr: int):
     _check(load().opt_orthonormalize(C.c_void_p(Z), C.c_void_p(Q), d, C.c_void_p(workspace),
                                      workspace_bytes, C.c_void_p(stream_ptr)))
+
+
+def opt_orthonormalize_static(Z: int, Q: int, d: int, stream_ptr: int):
+    _check(load().opt_orthonormalize_static(C.c_void_p(Z), C.c_void_p(Q), d, C.c_void_p(stream_ptr)))
 
 
 def opt_partition_dp(cost: Sequence[float], bucket_begin: Sequence[int], ranks: int, alpha: float):

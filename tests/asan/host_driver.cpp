@@ -165,6 +165,8 @@ void argument_errors() {
                OPT_EINVAL, "gemm negative");
     expect(opt_gemm_bf16(4, 4, 7, 1.f, (void*)base, 8, (void*)base, 8, 0.f, (void*)base, 0, 4, nullptr) == OPT_EINVAL,
            "gemm16 K");
+    expect(opt_orthonormalize_static(nullptr, nullptr, OPT_STATIC_MAX_DIM + 1, nullptr) == OPT_EUNSUPPORTED,
+           "static qr: order");
     expect(std::strlen(opt_last_error()) > 0, "error text");
 }
 
