@@ -40,10 +40,10 @@ from __future__ import annotations
 import numpy as np
 
 from .rotated_adam import (Hyper, OracleState, as_f32_scalar, momentum_update, refresh_bases,
-                           refresh_due, rotated_adam_apply, round_bf16, round_f32)
+                           refresh_due, rotated_adam_apply, round_bf16, round_f32, subspace_iteration)
 
 __all__ = ["bf16_rotation_apply", "step_bf16_rotation", "bf16_rotated_momentum_apply",
-           "step_bf16_rotated_momentum"]
+           "step_bf16_rotated_momentum", "refresh_bases_bf16", "step_bf16_storage"]
 
 
 def bf16_rotation_apply(W, v, M, G, U, V, beta2: float, eps: float, lr: float):
@@ -139,3 +139,39 @@ def step_bf16_rotated_momentum(state: OracleState, mt, G, hp: Hyper, mt_valid: b
                                                                       recompute)
     state.last = dict(inter, refreshed=refreshed, bf16=state.t != 1, recompute=recompute)
     return mt_new
+
+
+# ---- 16-bit storage of the bases --------------------------------------------
+#
+# [P3] section 3.1 stores the rotation matrices in 16 bits (about 15 % of the
+# memory saved). With the bases kept only in bfloat16 the refresh starts from
+# the stored values and its result is stored rounded; every step rotates with
+# the stored bases, the first one included (there is no binary32 copy to take
+# instead).
+
+
+def refresh_bases_bf16(M, U16, V16, power_iters: int):
+    """The refresh of rotated_adam.refresh_bases warm-started from the stored
+    16-bit bases (their exact values), the result rounded once to bfloat16."""
+    M = np.asarray(M, np.float64)
+    m, n = M.shape
+    r = min(m, n)
+    U = subspace_iteration(M @ M.T, np.asarray(U16, np.float64), r, power_iters)
+    V = subspace_iteration(M.T @ M, np.asarray(V16, np.float64), r, power_iters)
+    return round_bf16(U), round_bf16(V)
+
+
+def step_bf16_storage(state: OracleState, G, hp: Hyper) -> OracleState:
+    """One step with the bases stored in bfloat16 (state.U, state.V hold
+    bfloat16 values): momentum, the refresh from the stored bases when due,
+    then bf16_rotation_apply at every step. Mutates and returns ``state``."""
+    G = round_f32(G)
+    state.t += 1
+    state.M = momentum_update(state.M, G, hp.beta1, state.m_dtype)
+    refreshed = refresh_due(state.t, hp.K)
+    if refreshed:
+        state.U, state.V = refresh_bases_bf16(state.M, state.U, state.V, hp.power_iters)
+    state.W, state.v, inter = bf16_rotation_apply(state.W, state.v, state.M, G, state.U, state.V, hp.beta2,
+                                                  hp.eps, hp.lr)
+    state.last = dict(inter, refreshed=refreshed, bf16=True)
+    return state

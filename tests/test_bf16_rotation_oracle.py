@@ -272,3 +272,52 @@ def test_combined_trajectory_stays_near_the_method():
 def rand_q(d, rng):
     q, r = np.linalg.qr(rng.standard_normal((d, d)))
     return q * np.sign(np.diag(r))
+
+
+# ---- bases stored in 16 bits -------------------------------------------------
+
+def test_stored_bases_are_bfloat16_and_within_half_an_ulp_of_lapack():
+    """After a refresh the stored bases are bfloat16 values, each within half
+    a bfloat16 ulp (plus fp64 round-off) of the positive-diagonal LAPACK QR of
+    the Gram matrix applied to the stored start, on the well-determined
+    columns (a single pass from the identity: U = qr(M M^T))."""
+    m, n = 24, 40
+    rng = np.random.default_rng(21)
+    M = oracle.round_bf16(rng.standard_normal((m, n)) * 1e-2)
+    U16, V16 = B.refresh_bases_bf16(M, np.eye(m), np.eye(n), 1)
+    assert np.array_equal(U16, oracle.round_bf16(U16)) and np.array_equal(V16, oracle.round_bf16(V16))
+    q, r = np.linalg.qr(M @ M.T)
+    q = q * np.where(np.diag(r) < 0, -1.0, 1.0)
+    from tests.contract import ulp_bf16
+    assert np.all(np.abs(U16 - q) <= 0.5 * ulp_bf16(q) + 1e-12)
+
+
+def test_storage_trajectory_keeps_bases_in_16_bits_and_stays_near_the_method():
+    """Seven steps with a refresh every three from 16-bit bases: the stored
+    bases stay bfloat16 throughout, the refresh starts from them, and the
+    accumulated update stays within 10 % of the method's after the first
+    step (which, with 16-bit bases and v = 0, is large: see the module)."""
+    rng = np.random.default_rng(23)
+    m, n = 24, 40
+    W0 = rng.standard_normal((m, n)) * 1e-2
+    a = oracle.OracleState.fresh(W0, "bf16")
+    b = oracle.OracleState.fresh(W0, "bf16")
+    for t in range(1, 8):
+        G = rng.standard_normal((m, n)) * 1e-2
+        Wa, Wb = a.W.copy(), b.W.copy()
+        oracle.step(a, G, HP)
+        B.step_bf16_storage(b, G, HP)
+        assert np.array_equal(b.U, oracle.round_bf16(b.U)) and np.array_equal(b.V, oracle.round_bf16(b.V))
+        if t == 1:
+            first = (np.linalg.norm(b.W - Wb), np.linalg.norm(a.W - Wa))
+            W1a, W1b = a.W.copy(), b.W.copy()
+    later = np.linalg.norm((b.W - W1b) - (a.W - W1a)) / np.linalg.norm(a.W - W1a)
+    assert later <= 0.1
+    assert first[0] > first[1]
+
+
+def test_planted_binary32_storage_is_caught(monkeypatch):
+    """Bases stored in binary32 instead of 16 bits fail the storage pin."""
+    monkeypatch.setattr(B, "round_bf16", oracle.round_f32)
+    with pytest.raises(AssertionError):
+        test_stored_bases_are_bfloat16_and_within_half_an_ulp_of_lapack()
