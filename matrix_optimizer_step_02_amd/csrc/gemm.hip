@@ -753,6 +753,233 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
     epilogue<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
 }
 
+// ---- fp32 products on bf16 MFMAs, each operand value split once ----
+//
+// The X6 products of the grouped launches. Each workgroup loads a 16-deep k
+// slab of both operands from global memory into registers, splits every
+// value once into its three bf16 pieces (split2 above) and writes the pieces
+// to LDS as three planes; the wavefronts then read ready bf16 fragments, so
+// no value is split twice (a wavefront that split its own fragments would
+// split each A and B value once per wavefront that reads it: twice in a
+// 2 x 2 arrangement). LDS holds two slabs; the pieces of slab k + 1 are
+// written while slab k's MFMAs run, and slab k + 2 is loaded into registers
+// behind them: one barrier per slab.
+//
+// LDS layout: per operand and piece a plane of R rows (the tile's m or n)
+// by 16 k values in bf16, 32 bytes per row. MFMA lane l takes 8 bf16 of
+// row l % 32 at k = 8 (l / 32) .. +7 (one ds_read_b128, the same k order for
+// A and B); half h of row r sits at byte 32 r + 16 (h ^ ((r / 8) % 2)), which
+// puts the sixteen rows that one phase of a read touches on distinct 16-byte
+// bank groups.
+//
+// Fills: an operand whose k index is contiguous in memory is loaded 16 bytes
+// (four k values) per lane, four lanes per row; one whose k index is the
+// memory row (k-major) is loaded four k rows at a time, one element per lane,
+// the lanes along the contiguous index. Rows past the operand, and k past K,
+// are loaded from clamped addresses and zeroed before the split. A bf16
+// operand (B only) is exact in its high piece: its plane is the loaded
+// value, and the three products with its zero pieces are skipped.
+
+// The X6 products split each value once, at the fill (gemm_x6_kernel);
+// MATOPT_X6_REGISTER_SPLIT selects the in-register split of
+// gemm_grouped_kernel's X6 path instead.
+#ifdef MATOPT_X6_REGISTER_SPLIT
+constexpr bool kX6SplitAtFill = false;
+#else
+constexpr bool kX6SplitAtFill = true;
+#endif
+
+template <class C, bool BBF>
+struct X6Lds {
+    static constexpr int PA = C::BM * 32;   // bytes of one A piece plane
+    static constexpr int PB = C::BN * 32;
+    static constexpr int NPB = BBF ? 1 : 3;
+    static constexpr int BUF = 3 * PA + NPB * PB;
+    static constexpr int BYTES = 2 * BUF;
+};
+
+__device__ __forceinline__ int x6_off(int r, int half) { return r * 32 + 16 * (half ^ ((r >> 3) & 1)); }
+
+// One operand's slab in registers: R rows of 16 k values as quads of four k
+// values, Q quads per thread.
+template <int R, bool KMAJ, bool BF, int NT>
+struct X6Fill {
+    static constexpr int Q = R * 4 / NT;
+    static_assert(Q * NT == R * 4, "tile rows not divisible among the threads");
+    float v[Q][4];
+
+    // quad i of this thread: row r (0..R-1) of the tile, quad q (0..3) of the slab
+    __device__ __forceinline__ static void pos(int i, int& r, int& q) {
+        const int f = (int)threadIdx.x + NT * i;
+        if (KMAJ) { r = f % R; q = f / R; }
+        else      { r = f >> 2; q = f & 3; }
+    }
+
+    // base: the operand; rows_v: valid rows (m or n), K; ld: leading dimension
+    __device__ __forceinline__ void load(const void* base, int64_t ld, int r0, int rows_v, int k0, int K, bool vec) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            int r, q;
+            pos(i, r, q);
+            const int row = r0 + r, kq = k0 + 4 * q;
+            const int rc = row < rows_v ? row : rows_v - 1;
+            if (KMAJ) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int ke = kq + e < K ? kq + e : K - 1;
+                    if constexpr (BF)
+                        v[i][e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)ke * ld + rc] << 16);
+                    else
+                        v[i][e] = gptr((const float*)base)[(int64_t)ke * ld + rc];
+                }
+            } else {
+                static_assert(!BF || KMAJ, "a bf16 operand is read k-major");
+                if (vec) {
+                    const int last = (K - 1) & ~3;
+                    const f32x4 x = *gptr((const f32x4*)((const float*)base + (int64_t)rc * ld + (kq < last ? kq : last)));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[i][e] = x[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ke = kq + e < K ? kq + e : K - 1;
+                        v[i][e] = gptr((const float*)base)[(int64_t)rc * ld + ke];
+                    }
+                }
+            }
+        }
+    }
+
+    // Zero what lies outside the operand, split, and write the planes
+    // (planes p at `lds` + p * plane_bytes).
+    __device__ __forceinline__ void put(char* lds, int plane_bytes, int r0, int rows_v, int k0, int K) const {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            int r, q;
+            pos(i, r, q);
+            const bool row_ok = r0 + r < rows_v;
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = (row_ok && k0 + 4 * q + e < K) ? v[i][e] : 0.f;
+            const int off = x6_off(r, q >> 1) + 8 * (q & 1);
+            if constexpr (BF) {
+                // exact bf16 values: the high halves of the widened words
+                const uint32_t w0 = (__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xffff0000u);
+                const uint32_t w1 = (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xffff0000u);
+                *(u32x2*)(lds + off) = (u32x2){w0, w1};
+            } else {
+                uint32_t h0, m0, l0, h1, m1, l1;
+                split2(x[0], x[1], h0, m0, l0);
+                split2(x[2], x[3], h1, m1, l1);
+                *(u32x2*)(lds + off) = (u32x2){h0, h1};
+                *(u32x2*)(lds + plane_bytes + off) = (u32x2){m0, m1};
+                *(u32x2*)(lds + 2 * plane_bytes + off) = (u32x2){l0, l1};
+            }
+        }
+    }
+};
+
+template <class C, bool AT, bool BT, bool BBF>
+__device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, float alpha_scale, char* smem) {
+    using L = X6Lds<C, BBF>;
+    constexpr int TM = C::TM, TN = C::TN, NPB = L::NPB;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave % C::WM, wn = wave / C::WM;
+    const int m0 = tm * C::BM, n0 = tn * C::BN;
+    const int h = lane >> 5, l32 = lane & 31;
+    const bool avec = p.flags & GF_A_VEC, bvec = p.flags & GF_B_VEC;
+
+    Acc<C> acc;
+    acc.zero();
+    const int nk = (p.K + 15) / 16;
+    if (nk == 0) {
+        epilogue_blocks<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
+        return;
+    }
+    // A: M x K (k contiguous) or stored K x M (k-major); B: stored K x N
+    // (k-major) or N x K (k contiguous)
+    X6Fill<C::BM, AT, false, C::NT> fa;
+    X6Fill<C::BN, !BT, BBF, C::NT> fb;
+    auto load = [&](int k0) {
+        fa.load(p.A, p.lda, m0, p.M, k0, p.K, avec);
+        fb.load(p.B, p.ldb, n0, p.N, k0, p.K, bvec);
+    };
+    auto put = [&](char* buf, int k0) {
+        fa.put(buf, L::PA, m0, p.M, k0, p.K);
+        fb.put(buf + 3 * L::PA, L::PB, n0, p.N, k0, p.K);
+    };
+    load(0);
+    put(smem, 0);
+    load(16);   // past K: clamped addresses, zeroed at the put
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const char* cur = smem + (kt & 1) * L::BUF;
+        char* nxt = smem + ((kt + 1) & 1) * L::BUF;
+        const char* Bp = cur + 3 * L::PA;
+        bf16x8 b[TN][NPB];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int off = x6_off(wn * 32 * TN + j * 32 + l32, h);
+#pragma unroll
+            for (int q = 0; q < NPB; ++q) b[j][q] = *(const bf16x8*)(Bp + q * L::PB + off);
+        }
+        bf16x8 a[3];
+        {
+            const int off = x6_off(wm * 32 * TM + l32, h);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) a[q] = *(const bf16x8*)(cur + q * L::PA + off);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            bf16x8 an[3];
+            if (i + 1 < TM) {
+                const int off = x6_off(wm * 32 * TM + (i + 1) * 32 + l32, h);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) an[q] = *(const bf16x8*)(cur + q * L::PA + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            // smallest piece products first; consecutive MFMAs go to
+            // different accumulators
+            if constexpr (BBF) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[j][0], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[j][0], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][0], acc.v[i][j], 0, 0, 0);
+            } else {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[j][0], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[j][1], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][2], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[j][0], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][1], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][0], acc.v[i][j], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (i == 0) {
+                // the next slab's pieces into the other buffer (read by every
+                // wavefront before the previous barrier), then the loads of the
+                // slab after it (past K: clamped, zeroed at their put)
+                put(nxt, (kt + 1) * 16);
+                load((kt + 2) * 16);
+            }
+            if (i + 1 < TM) {
+#pragma unroll
+                for (int q = 0; q < 3; ++q) a[q] = an[q];
+            }
+        }
+        __syncthreads();
+    }
+    epilogue_blocks<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
+}
+
 // C += alpha A B for K <= 2 slabs (the QR in-block updates, K = the panel
 // width): both K slabs go to the two LDS buffers at once, then the old C
 // fragment is requested so that its latency overlaps the MFMAs; the operand
@@ -871,13 +1098,44 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     gemm_tile<C, AT, BT, ABF, BBF, X6>(p, tm, tn, args.alpha_scale, smem);
 }
 
+// The X6 products: same problem tables and tiles as gemm_grouped_kernel.
+template <class C, bool AT, bool BT, bool BBF>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_x6_kernel(GemmArgs args) {
+    __shared__ __attribute__((aligned(16))) char smem[X6Lds<C, BBF>::BYTES];
+    const int bid = xcd_remap(blockIdx.x, args.total_tiles);
+    GemmProb p;
+    int t = bid;
+    if (args.nprob > 0) {
+        int lo = 0, hi = args.nprob - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (args.tile_begin[mid] <= bid) lo = mid; else hi = mid - 1;
+        }
+        p = args.probs[lo];
+        t = bid - args.tile_begin[lo];
+    } else {
+        p = args.single;
+    }
+    int tm, tn;
+    raster(t, p.tiles_m, p.tiles_n, tm, tn);
+    gemm_tile_x6<C, AT, BT, BBF>(p, tm, tn, args.alpha_scale, smem);
+}
+
 template <bool AT, bool BT, bool ABF, bool BBF, bool X6 = false>
 hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
-    if (cfg == 1)
-        gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
-    else
-        gemm_grouped_kernel<SmallCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+    if constexpr (X6 && kX6SplitAtFill) {
+        static_assert(!ABF, "the X6 products take an fp32 A");
+        if (cfg == 1)
+            gemm_x6_kernel<LargeCfg, AT, BT, BBF><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
+        else
+            gemm_x6_kernel<SmallCfg, AT, BT, BBF><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+    } else {
+        if (cfg == 1)
+            gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
+        else
+            gemm_grouped_kernel<SmallCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
