@@ -166,10 +166,30 @@ def traffic_per_launch():
     return t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def refresh_flops(m: int, n: int, p: int) -> float:
+    """Algorithmic flops of one refresh of an m x n matrix with p passes."""
+    return p * (8.0 * m * n * min(m, n) + (8.0 / 3.0) * (float(m) ** 3 + float(n) ** 3))
+
+
 def cpu_baseline(wl, budget_s: float, muon_iters: int = 0):
-    """The oracle as it stands, one non-refresh step on one matrix of each
-    distinct shape, weighted by shape counts, scaled to parameters/s
-    (muon_iters > 0: the orthogonalised-momentum oracle instead)."""
+    """The oracle as it stands, timed on the host: one non-refresh step on
+    one matrix of each distinct shape, and (for the method) one refresh step
+    on the shapes whose refresh fits the remaining budget, the others
+    estimated from the measured refresh rate (flops/s of the oracle's
+    refresh on the largest shape timed); combined at the workload's cadence
+    of one refresh per K steps, weighted by shape counts, scaled to
+    parameters/s (muon_iters > 0: the orthogonalised-momentum oracle)."""
     import numpy as np
     import oracle
     import workloads
@@ -203,18 +223,62 @@ def cpu_baseline(wl, budget_s: float, muon_iters: int = 0):
         threads = max((x.get("num_threads") or 0) for x in threadpool_info()) or None
     except Exception:
         pass
-    return {
-        "value": covered / total_s if total_s > 0 else None,
+    plain_value = covered / total_s if total_s > 0 else None
+    out = {
+        "value": plain_value,
         "unit": "params/s",
         "cores": threads or os.cpu_count(),
         "kind": "oracle",
-        "sample": ((f"one fp64 orthogonalised-momentum oracle step ({muon_iters} Newton-Schulz iterations)"
-                    if muon_iters else "one non-refresh fp64 oracle step")
-                   + " on one matrix of each distinct shape "
-                   + ", ".join(f"{m}x{n} ({dt:.2f} s, x{c})" for m, n, c, dt in done)
-                   + ("" if muon_iters else "; refresh steps excluded, so this over-states the oracle's rate")),
+        "cpu_model": cpu_model(),
         "host_cpus": os.cpu_count(),
     }
+    if muon_iters or wl.K <= 0:
+        out["sample"] = ((f"one fp64 orthogonalised-momentum oracle step ({muon_iters} Newton-Schulz iterations)"
+                          if muon_iters else "one fp64 oracle step")
+                         + " on one matrix of each distinct shape "
+                         + ", ".join(f"{m}x{n} ({dt:.2f} s, x{c})" for m, n, c, dt in done))
+        return out
+    # refresh steps: time one on the smaller shapes while the budget lasts
+    hp_r = oracle.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, 1, wl.power_iters)
+    refresh_s = {}
+    for (m, n), c in sorted(counts.items(), key=lambda kv: refresh_flops(*kv[0], wl.power_iters)):
+        est = None
+        if refresh_s:
+            (m0, n0), t0r = max(refresh_s.items(), key=lambda kv: refresh_flops(*kv[0], wl.power_iters))
+            est = t0r * refresh_flops(m, n, wl.power_iters) / refresh_flops(m0, n0, wl.power_iters)
+        if time.time() - t_start + (est or 0.0) > 3 * budget_s:
+            break
+        i = next(k for k, s in enumerate(wl.matrices) if (s.m, s.n) == (m, n))
+        st = oracle.OracleState.fresh(workloads.initial_weight(wl, i).double().numpy(), wl.m_dtype)
+        G = workloads.gradient(wl, i, 1).double().numpy()
+        t0 = time.time()
+        oracle.step(st, G, hp_r)          # t = 1: refresh, then the rotations
+        refresh_s[(m, n)] = time.time() - t0
+    if not refresh_s or len(done) < len(counts):
+        out["sample"] = "incomplete: the budget ran out before every shape was timed"
+        return out
+    (mr, nr), tr = max(refresh_s.items(), key=lambda kv: refresh_flops(*kv[0], wl.power_iters))
+    rate = refresh_flops(mr, nr, wl.power_iters) / tr      # oracle refresh flops/s on the largest timed shape
+    plain = {(m, n): dt for m, n, c, dt in done}
+    total = 0.0
+    parts = []
+    for (m, n), c in counts.items():
+        t_ref = refresh_s.get((m, n))
+        measured = t_ref is not None
+        if not measured:
+            t_ref = plain[(m, n)] + refresh_flops(m, n, wl.power_iters) / rate
+        total += c * ((wl.K - 1) * plain[(m, n)] + t_ref) / wl.K
+        parts.append(f"{m}x{n} x{c}: plain {plain[(m, n)]:.2f} s, refresh step {t_ref:.2f} s"
+                     + ("" if measured else " (estimated)"))
+    out["value"] = covered / total
+    out["plain_steps_value"] = plain_value
+    out["refresh_step_s"] = {f"{m}x{n}": t for (m, n), t in refresh_s.items()}
+    out["sample"] = ("fp64 oracle steps on one matrix of each distinct shape, combined at one refresh step per "
+                     f"K = {wl.K} steps: " + "; ".join(parts)
+                     + f". Refresh steps not timed are estimated from the oracle's refresh rate on {mr}x{nr} "
+                       f"({rate / 1e9:.1f} GFLOP/s); its unblocked QR runs slower at larger orders, so the "
+                       "estimate over-states the oracle's rate")
+    return out
 
 
 def main(argv=None):
@@ -289,6 +353,8 @@ def main(argv=None):
                   fp32_mfma=args.fp32_mfma)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
+    # caller-owned state: W, G, M, v, U, V (and Mt)
+    state_bytes = sum(t.numel() * t.element_size() for st in states for t in st.values())
     torch.cuda.synchronize()
     print(f"[bench] state ready, {ngroups} micro-groups, workspace {grp.ws_bytes / 1e9:.2f} GB", flush=True)
 
@@ -311,6 +377,7 @@ def main(argv=None):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     phases = grp.read_timing() if not args.no_timing else {}
+    group_ms = grp.read_group_timing() if not args.no_timing else []
     grp.set_timing(False)
 
     ms_per_step = 1e3 * elapsed / args.steps
@@ -399,6 +466,23 @@ def main(argv=None):
             rf = sum(wl.power_iters * (8.0 * m * n * min(m, n) + (8.0 / 3.0) * (m ** 3 + n ** 3)) for m, n in shapes)
             extra["refresh_tflops"] = rf / (extra["refresh_ms_each"] * 1e-3) / 1e12
 
+    if group_ms:
+        # per micro-group: its own launches (momentum, rotations, Adam, update,
+        # pieced product) per step; the refresh runs over refresh batches and is
+        # reported beside them
+        _, group_of, _ = mo.RotatedAdamGroup.plan(shapes, hp)
+        rows = []
+        for k, ms_k in enumerate(group_ms):
+            members = [i for i, gk in enumerate(group_of) if gk == k]
+            p_k = sum(shapes[i][0] * shapes[i][1] for i in members)
+            per_step = ms_k / args.steps
+            rows.append({"group": k, "matrices": len(members), "params": p_k, "ms_per_step": per_step,
+                         "steps_per_s": 1e3 / per_step if per_step > 0 else None,
+                         "params_per_s": p_k * 1e3 / per_step if per_step > 0 else None})
+        extra["micro_groups"] = rows
+        if phases and phases.get("refresh", (0, 0))[0]:
+            extra["refresh_ms_per_step"] = phases["refresh"][0] / args.steps
+
     cpu = None
     if args.cpu_sample_s > 0:
         print("[bench] timing the oracle on the host (cpu_baseline)", flush=True)
@@ -420,6 +504,8 @@ def main(argv=None):
         "config": {"workload": wl.key, "matrices": len(shapes), "params": params,
                    "momentum_dtype": wl.m_dtype, "K": wl.K, "power_iters": wl.power_iters,
                    "micro_groups": ngroups, "refresh_steps_timed": refresh_steps,
+                   "workspace_bytes": grp.ws_bytes,
+                   "state_bytes": state_bytes,
                    "rotated_momentum": bool(args.rotated_momentum),
                    "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
                    "fp32_mfma": bool(args.fp32_mfma),

@@ -269,6 +269,16 @@ opt_status opt_group_set_timing(opt_group_t g, int32_t enable);
  * refresh scope counts its grouped GEMMs (Gram products and the QR's outer-
  * block updates), not the QR's panel and in-block kernels. */
 opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches);
+/* The same totals per micro-group: ms[k] is the summed milliseconds of every
+ * timed scope of micro-group k (its momentum, rotation, Adam and update
+ * phases, and its pieced product), in the plan's group order (opt_plan's
+ * group_of); count must equal the number of micro-groups. The refresh and
+ * the copies of the bases run over refresh batches, not micro-groups, and
+ * are not included. Folds the records like opt_group_read_timing (either
+ * call reads what the other has not), with the same overflow report. The
+ * Canzona page (section 6.1) sizes micro-groups for throughput, which this
+ * reads off per group. */
+opt_status opt_group_read_group_timing(opt_group_t g, double* ms, int32_t count);
 
 void opt_group_destroy(opt_group_t g);   /* NULL is ignored; does not synchronise */
 

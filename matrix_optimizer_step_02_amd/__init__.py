@@ -147,6 +147,11 @@ class RotatedAdamGroup:
     def read_timing(self):
         return native.opt_group_read_timing(self._g)
 
+    def read_group_timing(self):
+        """Summed milliseconds of each micro-group's timed scopes (plan order)."""
+        _, _, ngroups = RotatedAdamGroup.plan([(int(d.m), int(d.n)) for d in self.descs], self.hp)
+        return native.opt_group_read_group_timing(self._g, ngroups)
+
     def close(self):
         if getattr(self, "_g", None):
             native.opt_group_destroy(self._g)

@@ -239,8 +239,10 @@ struct opt_group_s {
     size_t pool_used = 0;
     double acc_ms[OPT_NUM_PHASES] = {};
     int64_t acc_kernels[OPT_NUM_PHASES] = {};
+    std::vector<double> acc_group_ms;   // per micro-group, every phase of its scopes
     struct Rec {
         int phase;
+        int group;   // micro-group of the scope, -1 for the refresh batches and the basis copies
         hipEvent_t b, e;
         int kernels;
     };
@@ -1377,8 +1379,9 @@ struct PhaseScope {
     opt_group_s* g;
     int phase;
     hipStream_t s;
+    int group;
     hipEvent_t b = nullptr;
-    PhaseScope(opt_group_s* g_, int ph, hipStream_t s_) : g(g_), phase(ph), s(s_) {
+    PhaseScope(opt_group_s* g_, int ph, hipStream_t s_, int group_ = -1) : g(g_), phase(ph), s(s_), group(group_) {
         g->kernels_in_scope = 0;
         if (g->timing) {
             b = next_event(g);
@@ -1390,7 +1393,7 @@ struct PhaseScope {
             hipEvent_t e = next_event(g);
             if (e) {
                 (void)hipEventRecord(e, s);
-                if (g->recs.size() < g->recs.capacity()) g->recs.push_back({phase, b, e, g->kernels_in_scope});
+                if (g->recs.size() < g->recs.capacity()) g->recs.push_back({phase, group, b, e, g->kernels_in_scope});
                 else g->timing_overflow = true;
             }
         }
@@ -1448,6 +1451,26 @@ std::vector<QrClasses> active_classes(const std::vector<int>& d, int p) {
     return out;
 }
 
+// Panel p on the tall path (rows spread over workgroups, a launch per
+// column) when its tallest panel has more than kTallMinRows rows and all its
+// panels together at most kTallMaxRows: a few tall panels, which one
+// workgroup each would factorise with most of the GPU idle. With many
+// panels in flight the one-workgroup kernel already fills the GPU and reads
+// each panel once instead of once per column.
+constexpr int kTallMinRows = 4096;
+constexpr int64_t kTallMaxRows = 96 * 1024;
+bool use_tall_panels(const std::vector<int>& d, int p) {
+    int64_t rows = 0;
+    int tallest = 0;
+    for (int x : d) {
+        const int L = x - p * kQrPB;
+        if (L <= 0) break;
+        rows += L;
+        tallest = std::max(tallest, L);
+    }
+    return tallest > kTallMinRows && rows <= kTallMaxRows;
+}
+
 // `block_steps(b, qform)` runs the grouped-GEMM steps of outer block b.
 template <class BlockSteps>
 hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vector<int>& d, hipStream_t s,
@@ -1471,7 +1494,11 @@ hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vect
         for (int q = 0; q < kQrPanelsPerBlock; ++q) {
             const int p = b * kQrPanelsPerBlock + q;
             if (p >= maxp) break;
-            if ((e = launch_qr_panel(jobs, active_p(p), p, max_d, s))) return e;
+            if (use_tall_panels(d, p)) {
+                if ((e = launch_qr_panel_tall(jobs, active_p(p), active_classes(d, p), p, max_d, s))) return e;
+            } else if ((e = launch_qr_panel(jobs, active_p(p), p, max_d, s))) {
+                return e;
+            }
             for (const QrClasses& C : active_classes(d, p)) {
                 if ((e = launch_qr_dots(jobs, C, p, s))) return e;
                 if ((e = launch_qr_reduce(jobs, C, p, s))) return e;
@@ -1661,13 +1688,15 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
         // orthogonalised momentum: M, then per group X_0 = M / ||M||_F and
         // ns_iters Newton-Schulz steps, the last one fused with the update
         for (const Group& G : g->groups) {
-            PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+        const int gi = (int)(&G - g->groups.data());
+            PhaseScope ps(g, OPT_PHASE_MOMENTUM, s, gi);
             e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
             if (e) return hip_fail(e, "momentum launch");
             g->kernels_in_scope += G.mom.nseg > 0;
         }
         for (const Group& G : g->groups) {
-            PhaseScope ps(g, OPT_PHASE_ORTHO, s);
+        const int gi = (int)(&G - g->groups.data());
+            PhaseScope ps(g, OPT_PHASE_ORTHO, s, gi);
             const MuonSeg* segs = dptr<MuonSeg>(g, G.mu.segs);
             e = launch_muon_norm(segs, G.mu.nseg, G.mu.chunks, G.mu_part, G.mu_inv, s);
             if (!e) e = launch_muon_scale(segs, G.mu.nseg, G.mu.chunks, G.mu_inv, s);
@@ -1695,7 +1724,8 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
         // after the refresh (which must see the updated M) otherwise.
         if (refresh) {
             for (const Group& G : g->groups) {
-                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+        const int gi = (int)(&G - g->groups.data());
+                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s, gi);
                 e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
                 if (e) return hip_fail(e, "momentum launch");
                 g->kernels_in_scope += G.mom.nseg > 0;
@@ -1712,8 +1742,9 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             g->copies_valid = true;
         }
         for (const Group& G : g->groups) {
+        const int gi = (int)(&G - g->groups.data());
             {
-                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+                PhaseScope ps(g, OPT_PHASE_MOMENTUM, s, gi);
                 if (refresh) {
                     e = launch_convert16(dptr<Ew16Seg>(g, G.mom16.segs), G.mom16.nseg, G.mom16.chunks, s);
                     g->kernels_in_scope += G.mom16.nseg > 0;
@@ -1729,17 +1760,17 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
                 if (e) return hip_fail(e, "momentum launch");
             }
             {
-                PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
+                PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s, gi);
                 if ((e = run_gemm16(g, carry ? G.r16_right_c : G.r16_right, 1.f, s)))
                     return hip_fail(e, "rotation launch");
             }
             {
-                PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
+                PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s, gi);
                 const std::vector<Gemm16Launch>& L = !carry_mode ? G.r16_left : (carry ? G.r16_left_c : G.r16_left_re);
                 if ((e = run_gemm16(g, L, 1.f, s))) return hip_fail(e, "rotation launch");
             }
             {
-                PhaseScope ps(g, OPT_PHASE_ADAM, s);
+                PhaseScope ps(g, OPT_PHASE_ADAM, s, gi);
                 const EwLaunch& A16 = !carry_mode ? G.adam16 : (carry ? G.adam16_c : G.adam16_re);
                 const EwLaunch& AR = !carry_mode ? G.adam_r : (carry ? G.adam_r_c : G.adam_r_re);
                 e = launch_adam16(dptr<Ew16Seg>(g, A16.segs), A16.nseg, A16.chunks, g->hp.beta1, g->hp.beta2,
@@ -1752,11 +1783,11 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
                 g->kernels_in_scope += (A16.nseg > 0) + (AR.nseg > 0);
             }
             {
-                PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s);
+                PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s, gi);
                 if ((e = run_gemm16(g, G.r16_back_right, 1.f, s))) return hip_fail(e, "rotation launch");
             }
             {
-                PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
+                PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s, gi);
                 if ((e = run_gemm16(g, G.r16_back_left, g->hp.lr, s))) return hip_fail(e, "update launch");
             }
         }
@@ -1765,7 +1796,8 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     }
     // Momentum of every group first: a refresh must see the updated M.
     for (const Group& G : g->groups) {
-        PhaseScope ps(g, OPT_PHASE_MOMENTUM, s);
+        const int gi = (int)(&G - g->groups.data());
+        PhaseScope ps(g, OPT_PHASE_MOMENTUM, s, gi);
         e = launch_momentum(dptr<EwSeg>(g, G.mom.segs), G.mom.nseg, G.mom.chunks, g->hp.beta1, s);
         if (e) return hip_fail(e, "momentum launch");
         g->kernels_in_scope += G.mom.nseg > 0;
@@ -1791,8 +1823,9 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
     const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
     const bool carry = carry_mode && g->mt_valid && !refresh;
     for (const Group& G : g->groups) {
+        const int gi = (int)(&G - g->groups.data());
         if (!G.rot_m16.empty()) {
-            PhaseScope ps(g, OPT_PHASE_ROT_PIECED, s);
+            PhaseScope ps(g, OPT_PHASE_ROT_PIECED, s, gi);
             if (G.mt_nsplit) {
                 if ((e = launch_split16(dptr<SplitJob>(g, G.mt_split), G.mt_nsplit, G.mt_tiles, s)))
                     return hip_fail(e, "momentum transpose launch");
@@ -1801,16 +1834,16 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             if ((e = run_gemm16(g, G.rot_m16, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
-            PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s);
+            PhaseScope ps(g, OPT_PHASE_ROT_LEFT, s, gi);
             if ((e = run_gemm(g, carry ? G.rot_left_c : G.rot_left, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
-            PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s);
+            PhaseScope ps(g, OPT_PHASE_ROT_RIGHT, s, gi);
             const std::vector<GemmLaunch>& L = !carry_mode ? G.rot_right : (carry ? G.rot_right_c : G.rot_right_re);
             if ((e = run_gemm(g, L, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
-            PhaseScope ps(g, OPT_PHASE_ADAM, s);
+            PhaseScope ps(g, OPT_PHASE_ADAM, s, gi);
             const EwLaunch& A = !carry_mode ? G.adam : (carry ? G.adam_c : G.adam_re);
             e = launch_rotated_adam(dptr<EwSeg>(g, A.segs), A.nseg, A.chunks, g->hp.beta1, g->hp.beta2, g->hp.eps,
                                     s);
@@ -1818,11 +1851,11 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
             g->kernels_in_scope += A.nseg > 0;
         }
         {
-            PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s);
+            PhaseScope ps(g, OPT_PHASE_BACK_LEFT, s, gi);
             if ((e = run_gemm(g, G.back_left, 1.f, s))) return hip_fail(e, "rotation launch");
         }
         {
-            PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s);
+            PhaseScope ps(g, OPT_PHASE_BACK_RIGHT, s, gi);
             if ((e = run_gemm(g, G.back_right, g->hp.lr, s))) return hip_fail(e, "update launch");
         }
     }
@@ -1938,6 +1971,7 @@ opt_status opt_group_set_timing(opt_group_t g, int32_t enable) {
         g->acc_ms[i] = 0.0;
         g->acc_kernels[i] = 0;
     }
+    g->acc_group_ms.assign(g->groups.size(), 0.0);
     g->timing = false;
     if (enable) {
         const size_t events = 2 * scopes_per_step(g) * kTimingSteps;
@@ -1954,8 +1988,11 @@ opt_status opt_group_set_timing(opt_group_t g, int32_t enable) {
     return OPT_OK;
 }
 
-opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
-    if (opt_status st = check_group(g)) return st;
+namespace {
+// Synchronises with the last recorded event and folds the records into the
+// totals, freeing the event pool.
+opt_status fold_timing(opt_group_t g) {
+    g->acc_group_ms.resize(g->groups.size(), 0.0);
     if (!g->recs.empty()) {
         hipError_t e = hipEventSynchronize(g->recs.back().e);
         if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
@@ -1965,19 +2002,39 @@ opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
             if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
             g->acc_ms[r.phase] += t;
             g->acc_kernels[r.phase] += r.kernels;
+            if (r.group >= 0) g->acc_group_ms[r.group] += t;
         }
         g->recs.clear();
     }
     g->pool_used = 0;
-    for (int i = 0; i < OPT_NUM_PHASES; ++i) {
-        if (ms) ms[i] = g->acc_ms[i];
-        if (launches) launches[i] = g->acc_kernels[i];
-    }
     if (g->timing_overflow)
         return fail(OPT_ESTATE, "timing: more phase scopes than the %d steps the event pool holds were "
                                 "recorded between two reads; the totals miss some",
                     kTimingSteps);
     return OPT_OK;
+}
+}  // namespace
+
+opt_status opt_group_read_timing(opt_group_t g, double* ms, int64_t* launches) {
+    if (opt_status st = check_group(g)) return st;
+    const opt_status st = fold_timing(g);
+    if (st == OPT_EHIP) return st;
+    for (int i = 0; i < OPT_NUM_PHASES; ++i) {
+        if (ms) ms[i] = g->acc_ms[i];
+        if (launches) launches[i] = g->acc_kernels[i];
+    }
+    return st;
+}
+
+opt_status opt_group_read_group_timing(opt_group_t g, double* ms, int32_t count) {
+    if (opt_status st = check_group(g)) return st;
+    if (!ms) return fail(OPT_EINVAL, "ms is NULL");
+    if (count != (int32_t)g->groups.size())
+        return fail(OPT_EINVAL, "count is %d, the group has %d micro-groups", count, (int)g->groups.size());
+    const opt_status st = fold_timing(g);
+    if (st == OPT_EHIP) return st;
+    for (int32_t k = 0; k < count; ++k) ms[k] = g->acc_group_ms[k];
+    return st;
 }
 
 void opt_group_destroy(opt_group_t g) {

@@ -369,14 +369,32 @@ __global__ __launch_bounds__(256) void basis16_kernel(const BasisJob* __restrict
     const int x = threadIdx.x & 31, y0 = threadIdx.x >> 5;
     for (int y = y0; y < kBasisTile; y += 8) {
         const int r = R + y, c = Cc + x;
-        const float val = (r < J.d && c < J.d) ? gptr(J.X)[(int64_t)r * J.d + c] : 0.f;
+        float val = 0.f;
+        if (r < J.d && c < J.d)
+            val = J.x_bf16 ? __uint_as_float((uint32_t)gptr((const uint16_t*)J.X)[(int64_t)r * J.d + c] << 16)
+                           : gptr((const float*)J.X)[(int64_t)r * J.d + c];
         tile[y][x] = val;
-        if (r < J.d && c < J.dp) gptr(J.Xb)[(int64_t)r * J.dp + c] = f32_to_bf16(val);
+        if (J.Xb && r < J.d && c < J.dp) gptr(J.Xb)[(int64_t)r * J.dp + c] = f32_to_bf16(val);
     }
     __syncthreads();
     for (int y = y0; y < kBasisTile; y += 8) {
         const int i = Cc + y, k = R + x;   // Xt[i][k] = X[k][i]
         if (i < J.d && k < J.dp) gptr(J.Xt)[(int64_t)i * J.dp + k] = f32_to_bf16(tile[x][y]);
+    }
+}
+
+__global__ __launch_bounds__(kEwThreads) void cvt16_kernel(const CvtJob* __restrict__ jobs, int njobs) {
+    const int64_t chunk = blockIdx.x;
+    int lo = 0, hi = njobs - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].chunk_begin <= chunk) lo = mid; else hi = mid - 1;
+    }
+    const CvtJob J = jobs[lo];
+    const int64_t e0 = (chunk - J.chunk_begin) * kEwChunk;
+    for (int64_t e = e0 + threadIdx.x; e < J.n && e < e0 + kEwChunk; e += kEwThreads) {
+        if (J.to16) gptr((uint16_t*)J.dst)[e] = f32_to_bf16(gptr((const float*)J.src)[e]);
+        else gptr((float*)J.dst)[e] = __uint_as_float((uint32_t)gptr((const uint16_t*)J.src)[e] << 16);
     }
 }
 
@@ -486,6 +504,12 @@ hipError_t launch_pack16(const PackJob* jobs, int njobs, int64_t total_chunks, h
 hipError_t launch_basis16(const BasisJob* jobs, int njobs, int total_tiles, hipStream_t s) {
     if (njobs <= 0 || total_tiles <= 0) return hipSuccess;
     hipLaunchKernelGGL(basis16_kernel, dim3((unsigned)total_tiles), dim3(256), 0, s, jobs, njobs);
+    return hipGetLastError();
+}
+
+hipError_t launch_cvt16(const CvtJob* jobs, int njobs, int64_t total_chunks, hipStream_t s) {
+    if (njobs <= 0 || total_chunks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(cvt16_kernel, dim3((unsigned)total_chunks), dim3(kEwThreads), 0, s, jobs, njobs);
     return hipGetLastError();
 }
 

@@ -3,6 +3,8 @@
 // these once per group and uploads them into the caller's workspace.
 #pragma once
 
+#include <vector>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,9 +96,18 @@ struct QrClasses {
     int32_t first[kQrMaxClasses];   // index of the class's first job
     int32_t count[kQrMaxClasses];
 };
-enum QrGridKind { QG_DOTS = 0, QG_REDUCE = 1, QG_UPDATE = 2 };
+enum QrGridKind { QG_DOTS = 0, QG_REDUCE = 1, QG_UPDATE = 2, QG_TALL = 3 };
+
+// Rows per workgroup of the tall-panel path (qr_tall_*): a panel's rows are
+// split over ceil(L / kQrTallRows) workgroups.
+constexpr int kQrTallRows = 256;
 
 hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s);
+// The same panel factorisation with the rows of each panel spread over
+// workgroups and one launch per column (for few, tall panels); C holds the
+// runs of equal order of the first njobs jobs.
+hipError_t launch_qr_panel_tall(const QrJob* jobs, int njobs, const std::vector<QrClasses>& C, int p, int max_d,
+                                hipStream_t s);
 hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
 hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
 hipError_t launch_qr_update(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);
@@ -191,6 +202,10 @@ __host__ __device__ inline int qr_inblock_cols(int d, int p) {
 // products (512 columns x one row split per block), their reduction (256
 // columns per block) and the in-block update (128 x 128 tiles).
 __host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p) {
+    if (kind == QG_TALL) {
+        const int L = d - p * kQrPB;
+        return L > 0 ? (L + kQrTallRows - 1) / kQrTallRows : 0;
+    }
     const int ncols = qr_inblock_cols(d, p);
     if (ncols <= 0) return 0;
     const int L = d - p * kQrPB;

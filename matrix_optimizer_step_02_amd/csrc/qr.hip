@@ -577,6 +577,218 @@ __global__ __launch_bounds__(256) void qr_copy_block_kernel(const QrJob* __restr
     gptr(J.Yb)[e] = v;
 }
 
+// ---- tall panels: rows spread over many workgroups ---------------------
+//
+// A panel of L rows factorised by one workgroup streams its column block
+// through that one CU once per column (plus the left-looking passes), so a
+// tall panel of a few large matrices leaves most of the GPU idle. Here the
+// panel's rows are split into slices of kQrTallRows, one workgroup each,
+// over all active matrices at once, and every column of the panel is one
+// launch: launches j = -1 .. jb - 1, then the reflectors' Gram matrix and T.
+//
+// Launch j (column j of the panel, j >= 0): every workgroup sums the
+// partial column sums the previous launch left (in a fixed slice order, so
+// the result is the same in every workgroup and run), forms the reflector of
+// column j from alpha = A[j][j] and sigma = sum_{i > j} A[i][j]^2 exactly as
+// qr_panel_kernel does, and the update weights w_q = v_j^T A[:, q] =
+// A[j][q] + scale sum_{i > j} A[i][j] A[i][q]; it applies H_j to its rows
+// (A[i][q] -= tau v_i w_q, q > j), stores v below the diagonal and beta on
+// it, and leaves the partial sums of column j + 1 over its rows below j + 1
+// (A[i][j+1] A[i][q] for q >= j + 1, from the updated values) and, in the
+// workgroup holding row j + 1, that row. Launch -1 only leaves column 0's
+// sums. Thread t handles column q = t mod 64 of the rows rg + 4 r of its
+// slice (rg = t / 64, one wavefront each): the wavefront's 64 lanes read a
+// row's 64 entries at once, and the row's column-j and column-(j+1) entries,
+// which its own lanes j and j+1 rewrite, are read by the same instruction
+// before any lane stores.
+//
+// Scratch in the job's `part` buffer (floats; Gs = slices of the whole
+// order d): the partial sums [2][Gs][64] (ping-pong by column parity), the
+// diagonal row [2][64], tau [64], and the per-slice Gram blocks [Gs][64][64].
+
+__host__ __device__ inline int qr_tall_gmax(int d) { return (d + kQrTallRows - 1) / kQrTallRows; }
+
+struct TallScratch {
+    float* sums;   // [2][gmax][64]
+    float* row;    // [2][64]
+    float* tau;    // [64]
+    float* gram;   // [gmax][64][64]
+    __device__ TallScratch(const QrJob& J) {
+        const int gmax = qr_tall_gmax(J.d);
+        sums = J.part;
+        row = sums + 2 * gmax * 64;
+        tau = row + 128;
+        gram = tau + 64;
+    }
+};
+
+__global__ __launch_bounds__(256) void qr_tall_col_kernel(const QrJob* __restrict__ jobs, QrClasses cls, int p,
+                                                          int j) {
+    __shared__ float sD[64], sRow[64], red[4][64];
+    int job, slice;
+    if (!qr_locate(cls, QG_TALL, p, blockIdx.x, job, slice)) return;
+    const QrJob Jb = jobs[job];
+    const int d = Jb.d, k = p * PB, L = d - k, jb = min(PB, L);
+    if (j >= jb) return;
+    const int G = (L + kQrTallRows - 1) / kQrTallRows;
+    const TallScratch sc(Jb);
+    const int gmax = qr_tall_gmax(d);
+    const int tid = threadIdx.x, q = tid & 63, rg = tid >> 6;
+    gmem<float> A = gptr(Jb.Z + (int64_t)k * d + k);
+
+    // the reflector of column j
+    float beta = 0.f, tau = 0.f, scale = 0.f, w = 0.f, w1 = 0.f;
+    if (j >= 0) {
+        if (tid < 64) {
+            gmem<const float> in = gptr((const float*)sc.sums + (j & 1) * gmax * 64 + tid);
+            float sum = 0.f;
+            for (int g = 0; g < G; ++g) sum += in[g * 64];
+            sD[tid] = sum;
+            sRow[tid] = gptr(sc.row)[(j & 1) * 64 + tid];
+        }
+        __syncthreads();
+        const float alpha = sRow[j], sig = sD[j];
+        if (sig == 0.f) {
+            beta = alpha;
+        } else {
+            const float nrm = __builtin_sqrtf(alpha * alpha + sig);
+            beta = -__builtin_copysignf(nrm, alpha);
+            tau = (beta - alpha) / beta;
+            scale = 1.f / (alpha - beta);
+        }
+        if (q > j && q < jb) w = sRow[q] + scale * sD[q];
+        if (j + 1 < jb) w1 = sRow[j + 1] + scale * sD[j + 1];
+        if (slice == 0 && tid == 0) gptr(sc.tau)[j] = tau;
+    }
+    const int jn = j + 1;   // the column whose sums this launch leaves
+    const bool next = jn < jb;
+    const bool qn = next && q >= jn && q < jb;
+    float acc = 0.f;
+    const int r0 = slice * kQrTallRows;
+    const int r1 = min(L, r0 + kQrTallRows);
+    gmem<float> rowout = gptr(sc.row + (jn & 1) * 64);
+    constexpr int U = 4;   // rows in flight per wavefront
+    for (int i0 = r0 + rg; i0 < r1; i0 += 4 * U) {
+        float aj[U], aj1[U], aq[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + 4 * u;
+            const bool ok = i < r1 && i >= (j < 0 ? 0 : j);
+            const int ic = ok ? i : r0;
+            aj[u] = (j >= 0) ? A[(int64_t)ic * d + j] : 0.f;
+            aj1[u] = next ? A[(int64_t)ic * d + jn] : 0.f;
+            aq[u] = q < jb ? A[(int64_t)ic * d + q] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + 4 * u;
+            if (i >= r1 || i < (j < 0 ? 0 : j)) continue;
+            float anew = aq[u], a1 = aj1[u];
+            if (j >= 0) {
+                const float vi = (i == j) ? 1.f : scale * aj[u];
+                if (q > j && q < jb) {
+                    anew = aq[u] - tau * vi * w;
+                    A[(int64_t)i * d + q] = anew;
+                } else if (q == j) {
+                    A[(int64_t)i * d + j] = (i == j) ? beta : vi;
+                }
+                a1 = aj1[u] - tau * vi * w1;
+            }
+            if (qn) {
+                if (i > jn) acc += a1 * anew;
+                else if (i == jn) rowout[q] = anew;
+            }
+        }
+    }
+    if (!next) return;
+    red[rg][q] = acc;
+    __syncthreads();
+    if (tid < 64) {
+        const float sum = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+        gptr(sc.sums)[(jn & 1) * gmax * 64 + slice * 64 + tid] = sum;
+    }
+}
+
+// Per-slice Gram blocks of the panel's reflectors Y (unit lower: ones on the
+// diagonal, zeros above, the stored v below): thread (bl, bm) forms the 4 x 4
+// block S[4 bl .. +3][4 bm .. +3] over the slice's rows, staged through LDS.
+__global__ __launch_bounds__(256) void qr_tall_gram_kernel(const QrJob* __restrict__ jobs, QrClasses cls, int p) {
+    __shared__ float Ys[kQrTallRows][PB + 1];
+    int job, slice;
+    if (!qr_locate(cls, QG_TALL, p, blockIdx.x, job, slice)) return;
+    const QrJob Jb = jobs[job];
+    const int d = Jb.d, k = p * PB, L = d - k, jb = min(PB, L);
+    const TallScratch sc(Jb);
+    gmem<const float> A = gptr((const float*)Jb.Z + (int64_t)k * d + k);
+    const int r0 = slice * kQrTallRows, rows = min(L - r0, kQrTallRows);
+    for (int e = threadIdx.x; e < kQrTallRows * PB; e += 256) {
+        const int r = e / PB, c = e % PB, i = r0 + r;
+        float y = 0.f;
+        if (r < rows && c < jb) y = (i < c) ? 0.f : (i == c ? 1.f : A[(int64_t)i * d + c]);
+        Ys[r][c] = y;
+    }
+    __syncthreads();
+    const int bl = threadIdx.x / 16, bm = threadIdx.x % 16;
+    float acc[4][4] = {};
+    for (int r = 0; r < rows; ++r) {
+        float yl[4], ym[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            yl[e] = Ys[r][4 * bl + e];
+            ym[e] = Ys[r][4 * bm + e];
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] += yl[a] * ym[b];
+    }
+    gmem<float> out = gptr(sc.gram + (int64_t)slice * PB * PB);
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) out[(4 * bl + a) * PB + 4 * bm + b] = acc[a][b];
+}
+
+// T of the panel from the summed Gram blocks and tau, one workgroup per job,
+// by the recurrence of qr_panel_kernel: T[c][j] = -tau_j sum_{c<=l<j} T[c][l]
+// S[l][j], tau on the diagonal.
+__global__ __launch_bounds__(256) void qr_tall_t_kernel(const QrJob* __restrict__ jobs, int p) {
+    __shared__ float S[PB][PB + 1], Tf[PB][PB + 1], tau[PB];
+    const QrJob Jb = jobs[blockIdx.x];
+    const int d = Jb.d, k = p * PB;
+    if (k >= d) return;
+    const int L = d - k, jb = min(PB, L);
+    const int G = (L + kQrTallRows - 1) / kQrTallRows;
+    const TallScratch sc(Jb);
+    for (int e = threadIdx.x; e < PB * PB; e += 256) {
+        gmem<const float> g = gptr((const float*)sc.gram + e);
+        float sum = 0.f;
+        for (int s = 0; s < G; ++s) sum += g[(int64_t)s * PB * PB];
+        S[e / PB][e % PB] = sum;
+    }
+    if (threadIdx.x < PB) tau[threadIdx.x] = threadIdx.x < jb ? gptr((const float*)sc.tau)[threadIdx.x] : 0.f;
+    __syncthreads();
+    if (threadIdx.x < PB) {
+        const int r = threadIdx.x;
+        for (int j = 0; j < PB; ++j) {
+            float v = 0.f;
+            if (r < jb && j < jb && j >= r) {
+                if (j == r) {
+                    v = tau[r];
+                } else {
+                    float sum = 0.f;
+                    for (int l = r; l < j; ++l) sum += Tf[r][l] * S[l][j];
+                    v = -tau[j] * sum;
+                }
+            }
+            Tf[r][j] = v;
+        }
+    }
+    __syncthreads();
+    gmem<float> Tout = gptr(Jb.T + (int64_t)p * PB * PB);
+    for (int e = threadIdx.x; e < PB * PB; e += 256) Tout[e] = Tf[e / PB][e % PB];
+}
+
 }  // namespace
 
 hipError_t launch_qr_copy_block(const QrJob* jobs, int njobs, int b, int max_d, hipStream_t s) {
@@ -601,6 +813,26 @@ hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipSt
     else if (rows <= 24) qr_panel_kernel<24, 4><<<g, b, 0, s>>>(jobs, p);
     else if (rows <= 32) qr_panel_kernel<32, 4><<<g, b, 0, s>>>(jobs, p);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+// Panel p of the first njobs jobs on the tall path; C: their runs of equal
+// order (QG_TALL blocks per job = the slices of the panel).
+hipError_t launch_qr_panel_tall(const QrJob* jobs, int njobs, const std::vector<QrClasses>& C, int p, int max_d,
+                                hipStream_t s) {
+    const int L = max_d - p * PB;
+    if (njobs <= 0 || L <= 0) return hipSuccess;
+    const int jb = min(PB, L);
+    for (int j = -1; j < jb; ++j)
+        for (const QrClasses& c : C) {
+            const int blocks = qr_total_blocks(c, QG_TALL, p);
+            if (blocks > 0) hipLaunchKernelGGL(qr_tall_col_kernel, dim3(blocks), dim3(256), 0, s, jobs, c, p, j);
+        }
+    for (const QrClasses& c : C) {
+        const int blocks = qr_total_blocks(c, QG_TALL, p);
+        if (blocks > 0) hipLaunchKernelGGL(qr_tall_gram_kernel, dim3(blocks), dim3(256), 0, s, jobs, c, p);
+    }
+    hipLaunchKernelGGL(qr_tall_t_kernel, dim3(njobs), dim3(256), 0, s, jobs, p);
     return hipGetLastError();
 }
 

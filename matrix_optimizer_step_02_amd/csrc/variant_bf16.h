@@ -92,14 +92,27 @@ hipError_t launch_pack16(const PackJob* jobs, int njobs, int64_t total_chunks, h
 // (dp = d rounded up to 8) with zero columns [d, dp). 32 x 32 tiles over
 // dp x dp; tile_begin is the job's first tile.
 struct BasisJob {
-    const float* X;
-    uint16_t* Xb;
+    const void* X;      // fp32, or bf16 with x_bf16 (bases stored in 16 bits)
+    uint16_t* Xb;       // NULL: no row-padded copy (X itself serves, bf16 with d == dp)
     uint16_t* Xt;
     int32_t d, dp;
     int32_t tile_begin;
+    int32_t x_bf16;
 };
 constexpr int kBasisTile = 32;
 hipError_t launch_basis16(const BasisJob* jobs, int njobs, int total_tiles, hipStream_t s);
+
+// Bases stored in 16 bits: n elements between a bf16 basis and its fp32
+// working copy in the refresh scratch. to16 = 0 widens (exact), 1 rounds to
+// nearest even. Jobs are laid out back to back in chunks of kEwChunk.
+struct CvtJob {
+    const void* src;
+    void* dst;
+    int64_t n;
+    int64_t chunk_begin;
+    int32_t to16;
+};
+hipError_t launch_cvt16(const CvtJob* jobs, int njobs, int64_t total_chunks, hipStream_t s);
 
 // Transposed bf16 pieces of a rows x cols block X (fp32 or bf16, row stride
 // ld_src): dst + p * piece_stride holds piece p as a cols x ld_dst row-major

@@ -31,7 +31,7 @@ EXPORTED = (
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
     "opt_gemm", "opt_gemm_x6", "opt_gemm_bf16", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
     "opt_partition_dp", "opt_plan_host_ranks", "opt_group_health", "opt_group_reorthonormalize",
-    "opt_orthonormalize_static",
+    "opt_orthonormalize_static", "opt_group_read_group_timing",
 )
 
 
@@ -99,6 +99,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         "opt_orthonormalize_workspace_size": ([i64, C.POINTER(u64)], i32),
         "opt_orthonormalize": ([vp, vp, i64, vp, u64, vp], i32),
         "opt_orthonormalize_static": ([vp, vp, i64, vp], i32),
+        "opt_group_read_group_timing": ([vp, C.POINTER(C.c_double), i32], i32),
         "opt_group_health": ([vp, C.POINTER(opt_health), vp], i32),
         "opt_group_reorthonormalize": ([vp, i32, vp], i32),
         "opt_partition_dp": ([C.POINTER(C.c_double), i64, C.POINTER(i64), i32, i32, C.c_double,
@@ -189,6 +190,13 @@ def opt_group_reorthonormalize(g: int, iters: int, stream_ptr: int):
 
 def opt_group_set_timing(g: int, enable: bool):
     _check(load().opt_group_set_timing(C.c_void_p(g), 1 if enable else 0))
+
+
+def opt_group_read_group_timing(g: int, ngroups: int):
+    """Summed milliseconds of each micro-group's timed scopes."""
+    ms = (C.c_double * max(ngroups, 1))()
+    _check(load().opt_group_read_group_timing(C.c_void_p(g), ms, ngroups))
+    return list(ms)[:ngroups]
 
 
 def opt_group_read_timing(g: int):
