@@ -294,6 +294,8 @@ def main(argv=None):
                     help="the variant that carries m~ in rotated coordinates within a basis epoch")
     ap.add_argument("--bf16-rotation", action="store_true",
                     help="the variant that runs the rotations on bf16 operands (fp32 accumulation)")
+    ap.add_argument("--bf16-bases", action="store_true",
+                    help="with --bf16-rotation: U and V stored in bf16 only (the refresh widens and rounds them)")
     ap.add_argument("--muon", action="store_true",
                     help="the orthogonalised-momentum step (Newton-Schulz polar factor of M) instead")
     ap.add_argument("--ns-iters", type=int, default=5, help="Newton-Schulz iterations of --muon")
@@ -344,13 +346,13 @@ def main(argv=None):
     for i, s in enumerate(wl.matrices):
         W0 = workloads.initial_weight(wl, i, dev)
         st = mo.new_state(s.m, s.n, wl.m_dtype, dev, W0=W0, rotated_momentum=args.rotated_momentum,
-                          bases=not args.muon)
+                          bases=not args.muon, bases16=args.bf16_bases)
         st["G"].copy_(workloads.gradient(wl, i, 1, dev))
         states.append(st)
     hp = mo.Hyper(wl.beta1, wl.beta2, wl.eps, wl.lr, wl.K, wl.power_iters, wl.capacity_bytes,
                   int(args.refresh_cap_gib * (1 << 30)), rotated_momentum=args.rotated_momentum,
                   bf16_rotation=args.bf16_rotation, muon=args.muon, ns_iters=args.ns_iters if args.muon else 0,
-                  fp32_mfma=args.fp32_mfma)
+                  fp32_mfma=args.fp32_mfma, bf16_bases=args.bf16_bases)
     grp = mo.RotatedAdamGroup(states, hp)
     _, _, ngroups = mo.RotatedAdamGroup.plan(shapes, hp)
     # caller-owned state: W, G, M, v, U, V (and Mt)
@@ -507,7 +509,8 @@ def main(argv=None):
                    "workspace_bytes": grp.ws_bytes,
                    "state_bytes": state_bytes,
                    "rotated_momentum": bool(args.rotated_momentum),
-                   "bf16_rotation": bool(args.bf16_rotation), "muon": bool(args.muon),
+                   "bf16_rotation": bool(args.bf16_rotation), "bf16_bases": bool(args.bf16_bases),
+                   "muon": bool(args.muon),
                    "fp32_mfma": bool(args.fp32_mfma),
                    # how the fp32 products execute: six bf16 MFMA piece products each (fp32 accuracy),
                    # or fp32 MFMAs

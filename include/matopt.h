@@ -81,8 +81,9 @@ typedef struct {
     int32_t M_dtype;       /* opt_dtype */
     float* v;              /* m x n fp32 second moment in rotated coordinates; start at 0
                               (NULL allowed with OPT_FLAG_MUON, as for U and V) */
-    float* U;              /* m x m fp32 orthonormal left basis, updated by refreshes; start at I */
-    float* V;              /* n x n fp32 orthonormal right basis, updated by refreshes; start at I */
+    float* U;              /* m x m fp32 orthonormal left basis, updated by refreshes; start at I
+                              (bf16, 16-byte aligned, with OPT_FLAG_BF16_BASES: cast the pointer) */
+    float* V;              /* n x n fp32 orthonormal right basis, likewise */
     float* Mt;             /* m x n fp32 momentum in rotated coordinates, used only with
                               OPT_FLAG_ROTATED_MOMENTUM (else must be NULL); its content is
                               rebuilt by the first step, so it needs no initial value */
@@ -146,7 +147,19 @@ enum {
      *    matrix, d = m or n, made with the U^T copy), in one fp32 chain.
      * The Newton-Schulz products of OPT_FLAG_MUON run the same way. This flag
      * keeps every one of these products on fp32 MFMAs. */
-    OPT_FLAG_FP32_MFMA = 8u
+    OPT_FLAG_FP32_MFMA = 8u,
+    /* With OPT_FLAG_BF16_ROTATION: U and V are stored in bfloat16 and are the
+     * only copies of the bases (the Pipeline-parallelism page, section 3.1,
+     * keeps the rotation matrices in 16 bits, about 15 % of the memory). The
+     * descriptor's U and V point to bf16 m x m and n x n matrices, 16-byte
+     * aligned, initialised to I. A refresh widens them into fp32 copies in
+     * its scratch, runs the orthogonal iteration there and stores the result
+     * rounded to nearest even. Every step rotates with the stored bases,
+     * the first one included (there is no fp32 copy for it). Where m (n) is a
+     * multiple of 8 the caller's U (V) also serves as the rotations' bf16
+     * copy, so the workspace holds only U^T and V^T in bf16. Health checks
+     * and re-orthonormalisation return OPT_EUNSUPPORTED. */
+    OPT_FLAG_BF16_BASES = 16u
 };
 
 typedef struct {

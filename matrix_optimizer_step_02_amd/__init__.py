@@ -32,12 +32,14 @@ class Hyper:
     muon: bool = False                # orthogonalised-momentum step instead (no v, U, V)
     ns_iters: int = 0                 # Newton-Schulz iterations of the muon step (>= 1 there)
     fp32_mfma: bool = False           # keep the fp32 products on fp32 MFMAs (no bf16-piece products)
+    bf16_bases: bool = False          # U, V stored in bf16 only (with bf16_rotation)
 
     def c(self) -> native.opt_hparams:
         flags = (native.OPT_FLAG_ROTATED_MOMENTUM if self.rotated_momentum else 0) | \
                 (native.OPT_FLAG_BF16_ROTATION if self.bf16_rotation else 0) | \
                 (native.OPT_FLAG_MUON if self.muon else 0) | \
-                (native.OPT_FLAG_FP32_MFMA if self.fp32_mfma else 0)
+                (native.OPT_FLAG_FP32_MFMA if self.fp32_mfma else 0) | \
+                (native.OPT_FLAG_BF16_BASES if self.bf16_bases else 0)
         return native.opt_hparams(self.beta1, self.beta2, self.eps, self.lr, self.K,
                                   self.power_iters, self.capacity_bytes,
                                   self.refresh_capacity_bytes, flags, self.ns_iters)
@@ -78,9 +80,11 @@ def make_desc(W, G, M, v, U, V, Mt=None) -> native.opt_matrix_desc:
     _check_tensor(W, (m, n), (torch.float32,), "W", dev)
     _check_tensor(G, (m, n), (torch.float32,), "G", dev)
     _check_tensor(M, (m, n), (torch.float32, torch.bfloat16), "M", dev)
-    for t, shape, name in ((v, (m, n), "v"), (U, (m, m), "U"), (V, (n, n), "V")):
-        if t is not None:   # absent only for the muon step
-            _check_tensor(t, shape, (torch.float32,), name, dev)
+    if v is not None:
+        _check_tensor(v, (m, n), (torch.float32,), "v", dev)
+    for t, shape, name in ((U, (m, m), "U"), (V, (n, n), "V")):
+        if t is not None:   # absent only for the muon step; bf16 for bases stored in 16 bits
+            _check_tensor(t, shape, (torch.float32, torch.bfloat16), name, dev)
     if Mt is not None:
         _check_tensor(Mt, (m, n), (torch.float32,), "Mt", dev)
     dt = native.OPT_BF16 if M.dtype == torch.bfloat16 else native.OPT_F32
@@ -101,6 +105,11 @@ class RotatedAdamGroup:
         import torch
         self.params = list(params)
         self.hp = hp
+        want = torch.bfloat16 if hp.bf16_bases else torch.float32
+        for p in self.params:
+            for key in ("U", "V"):
+                if p.get(key) is not None and p[key].dtype != want:
+                    raise ValueError(f"{key} must be {want} (bf16_bases={hp.bf16_bases})")
         self.descs = [make_desc(p["W"], p["G"], p["M"], p.get("v"), p.get("U"), p.get("V"), p.get("Mt"))
                       for p in self.params]
         self._hpc = hp.c()
@@ -165,10 +174,11 @@ class RotatedAdamGroup:
 
 
 def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None, rotated_momentum=False,
-              bases=True):
+              bases=True, bases16=False):
     """Fresh caller-side state of one matrix: W (given or zeros), G zeros,
-    M and v zeros, U = I_m, V = I_n (and Mt, uninitialised, for the rotated
-    momentum). bases=False leaves out v, U and V (the muon step)."""
+    M and v zeros, U = I_m, V = I_n (bf16 with bases16) (and Mt,
+    uninitialised, for the rotated momentum). bases=False leaves out v, U
+    and V (the muon step)."""
     import torch
     dt = torch.bfloat16 if m_dtype == "bf16" else torch.float32
     W = (W0.to(device=device, dtype=torch.float32).contiguous().clone() if W0 is not None
@@ -179,6 +189,7 @@ def new_state(m: int, n: int, m_dtype: str = "f32", device="cuda", W0=None, rota
         "M": torch.zeros(m, n, device=device, dtype=dt),
     }
     if bases:
-        st |= {"v": torch.zeros(m, n, device=device), "U": torch.eye(m, device=device),
-               "V": torch.eye(n, device=device)}
+        bdt = torch.bfloat16 if bases16 else torch.float32
+        st |= {"v": torch.zeros(m, n, device=device), "U": torch.eye(m, device=device, dtype=bdt),
+               "V": torch.eye(n, device=device, dtype=bdt)}
     return st | ({"Mt": torch.empty(m, n, device=device)} if rotated_momentum else {})

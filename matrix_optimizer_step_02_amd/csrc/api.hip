@@ -185,6 +185,11 @@ struct RefreshBatch {
     uint64_t drift_jobs = 0;
     int ndrift = 0, drift_max_d = 0;
     std::vector<NsChunk> ns;
+    // bases stored in 16 bits: widen U, V into the refresh's fp32 copies
+    // before the first pass, round them back after the last
+    int nwiden = 0;
+    int64_t widen_chunks = 0, round_chunks = 0;
+    uint64_t widen = 0, round16 = 0;
 };
 
 // Append-only image of device tables with 256-byte aligned entries.
@@ -263,8 +268,10 @@ opt_status check_hparams(const opt_hparams* hp) {
     if (hp->K < 0) return fail(OPT_EINVAL, "K must be >= 0");
     if (hp->power_iters < 1) return fail(OPT_EINVAL, "power_iters must be >= 1");
     if (hp->flags & ~(uint32_t)(OPT_FLAG_ROTATED_MOMENTUM | OPT_FLAG_BF16_ROTATION | OPT_FLAG_MUON |
-                                OPT_FLAG_FP32_MFMA))
+                                OPT_FLAG_FP32_MFMA | OPT_FLAG_BF16_BASES))
         return fail(OPT_EINVAL, "unknown bits in flags");
+    if ((hp->flags & OPT_FLAG_BF16_BASES) && !(hp->flags & OPT_FLAG_BF16_ROTATION))
+        return fail(OPT_EINVAL, "OPT_FLAG_BF16_BASES needs OPT_FLAG_BF16_ROTATION");
     if ((hp->flags & OPT_FLAG_MUON) && (hp->flags & ~(uint32_t)OPT_FLAG_FP32_MFMA) != OPT_FLAG_MUON)
         return fail(OPT_EUNSUPPORTED, "OPT_FLAG_MUON combines with OPT_FLAG_FP32_MFMA only");
     if ((hp->flags & OPT_FLAG_MUON) && hp->ns_iters < 1)
@@ -318,6 +325,7 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
             return fail(OPT_EINVAL, "matrix %d: Mt must be set exactly when OPT_FLAG_ROTATED_MOMENTUM is", i);
         const uint64_t mn = (uint64_t)x.m * x.n;
         const uint64_t esz = x.M_dtype == OPT_BF16 ? 2 : 4;
+        const uint64_t bsz = (hp->flags & OPT_FLAG_BF16_BASES) ? 2 : 4;   // U, V
         auto add = [&](const void* p, uint64_t bytes, const char* what) {
             spans.push_back({(uintptr_t)p, (uintptr_t)p + bytes, i, what});
         };
@@ -325,12 +333,14 @@ opt_status check_descs(const opt_matrix_desc* d, int32_t count, const opt_hparam
         add(x.G, 4 * mn, "G");
         add(x.M, esz * mn, "M");
         if (x.v) add(x.v, 4 * mn, "v");
-        if (x.U) add(x.U, 4ull * x.m * x.m, "U");
-        if (x.V) add(x.V, 4ull * x.n * x.n, "V");
+        if (x.U) add(x.U, bsz * x.m * x.m, "U");
+        if (x.V) add(x.V, bsz * x.n * x.n, "V");
         if (x.Mt) add(x.Mt, 4 * mn, "Mt");
-        if (!aligned(x.W, 4) || !aligned(x.G, 4) || !aligned(x.v, 4) || !aligned(x.U, 4) ||
-            !aligned(x.V, 4) || !aligned(x.M, esz) || !aligned(x.Mt, 4))
+        if (!aligned(x.W, 4) || !aligned(x.G, 4) || !aligned(x.v, 4) || !aligned(x.U, bsz) ||
+            !aligned(x.V, bsz) || !aligned(x.M, esz) || !aligned(x.Mt, 4))
             return fail(OPT_EINVAL, "matrix %d: a tensor pointer is not aligned to its element", i);
+        if ((hp->flags & OPT_FLAG_BF16_BASES) && (!aligned(x.U, 16) || !aligned(x.V, 16)))
+            return fail(OPT_EINVAL, "matrix %d: with OPT_FLAG_BF16_BASES, U and V must be 16-byte aligned", i);
     }
     if (need_ptrs) {
         std::sort(spans.begin(), spans.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
@@ -570,11 +580,6 @@ PackLaunch put_pack(Image& img, std::vector<PackJob> jobs) {
 
 int64_t round8(int64_t x) { return (x + 7) / 8 * 8; }
 
-// Bytes of the bf16 copies of one matrix's bases: U, U^T (m x m8), V, V^T (n x n8).
-uint64_t bases16_bytes(int64_t m, int64_t n) {
-    return 2 * align_up(2ull * m * round8(m)) + 2 * align_up(2ull * n * round8(n));
-}
-
 constexpr int panels(int d) { return (d + kQrPB - 1) / kQrPB; }
 
 // Long products are split along K into chunks run as successive launches
@@ -639,7 +644,11 @@ constexpr QrBytes qr_job_bytes(int64_t d) {
     QrBytes b{};
     b.Z = align_up(4ull * d * d);
     b.T = align_up(4ull * panels((int)d) * kQrPB * kQrPB);
-    b.part = align_up(4ull * kQrMaxSplits * kQrPB * d);
+    // the in-block products' row splits, or the tall-panel path's sums, Gram
+    // blocks and barrier words (qr.hip), whichever is larger
+    const uint64_t gmax = (uint64_t)(d + kQrTallRows - 1) / kQrTallRows;
+    const uint64_t tall = gmax * (2 * kQrPB + kQrPB * kQrPB) + 256;
+    b.part = align_up(4ull * std::max<uint64_t>((uint64_t)kQrMaxSplits * kQrPB * d, tall));
     b.W2 = align_up(4ull * kQrPB * d);
     b.Yb = align_up(4ull * d * kQrNB);
     b.Wb = align_up(4ull * kQrNB * d);
@@ -772,8 +781,9 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
     uint64_t used = 0;
     for (const std::vector<int>& members : plan)
         for (int mi : members) {
-            const uint64_t b = refresh_bytes(g->mats[mi].d.m, g->mats[mi].d.n) +
-                               (gram16_eligible(g->mats[mi]) ? gram16_bytes(g->mats[mi].d.m, g->mats[mi].d.n) : 0);
+            const int64_t m = g->mats[mi].d.m, n = g->mats[mi].d.n;
+            const uint64_t b = refresh_bytes(m, n) + (gram16_eligible(g->mats[mi]) ? gram16_bytes(m, n) : 0) +
+                               ((g->hp.flags & OPT_FLAG_BF16_BASES) ? align_up(4ull * m * m) + align_up(4ull * n * n) : 0);
             if (out.empty() || (used + b > cap && !out.back().empty())) {
                 out.emplace_back();
                 used = 0;
@@ -806,22 +816,30 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
     // the tables depend on the flags, never on whether a pointer is set, so
     // that the size query (which reads no pointer) matches create
     const bool rmf = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
+    // bases stored in 16 bits: the caller's U (V) serves as the row-padded
+    // bf16 copy itself when its order is a multiple of 8
+    const bool b16 = g->hp.flags & OPT_FLAG_BF16_BASES;
     g->bases_bytes = 0;
     if (r16) {
         std::vector<BasisJob> bj;
         int tiles = 0;
         for (Mat& M : g->mats) {
             const int64_t m = M.d.m, n = M.d.n, m8 = round8(m), n8 = round8(n);
+            const bool own_u = b16 && m == m8, own_v = b16 && n == n8;
             char* p = region + g->bases_bytes;
-            M.Ub = (uint16_t*)p; p += align_up(2ull * m * m8);
+            const char* p0 = p;
+            if (own_u) M.Ub = (uint16_t*)M.d.U;
+            else { M.Ub = (uint16_t*)p; p += align_up(2ull * m * m8); }
             M.Utb = (uint16_t*)p; p += align_up(2ull * m * m8);
-            M.Vb = (uint16_t*)p; p += align_up(2ull * n * n8);
-            M.Vtb = (uint16_t*)p;
-            g->bases_bytes += bases16_bytes(m, n);
+            if (own_v) M.Vb = (uint16_t*)M.d.V;
+            else { M.Vb = (uint16_t*)p; p += align_up(2ull * n * n8); }
+            M.Vtb = (uint16_t*)p; p += align_up(2ull * n * n8);
+            g->bases_bytes += (uint64_t)(p - p0);
             for (int side = 0; side < 2; ++side) {
                 BasisJob j{};
-                j.X = side ? M.d.V : M.d.U;
-                j.Xb = side ? M.Vb : M.Ub;
+                j.X = side ? (const void*)M.d.V : (const void*)M.d.U;
+                j.x_bf16 = b16;
+                j.Xb = (side ? own_v : own_u) ? nullptr : (side ? M.Vb : M.Ub);
                 j.Xt = side ? M.Vtb : M.Utb;
                 j.d = (int32_t)(side ? n : m);
                 j.dp = (int32_t)round8(j.d);
@@ -1188,16 +1206,36 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             v.push_back(j);
         };
         std::vector<CopyJob> comp;
+        std::vector<CvtJob> widen, round16;
+        int64_t widen_chunks = 0, round_chunks = 0;
         struct JobSrc { int64_t d; float* Z; float* X; int mat; int side; };
         std::vector<JobSrc> jsrc;
         for (int mi : members) {
             const Mat& M = g->mats[mi];
-            const opt_matrix_desc& x = M.d;
+            opt_matrix_desc x = M.d;
             const int64_t m = x.m, n = x.n, r = std::min(m, n);
             float* B1U = (float*)(scratch + off); off += align_up(4ull * n * r);
             float* B1V = (float*)(scratch + off); off += align_up(4ull * m * r);
             float* ZU = (float*)(scratch + off); off += align_up(4ull * m * m);
             float* ZV = (float*)(scratch + off); off += align_up(4ull * n * n);
+            if (b16) {
+                // bases stored in 16 bits: the refresh works on fp32 copies in
+                // its scratch, widened from U, V before the first pass and
+                // rounded back into them after the last
+                float* XU = (float*)(scratch + off); off += align_up(4ull * m * m);
+                float* XV = (float*)(scratch + off); off += align_up(4ull * n * n);
+                for (int side = 0; side < 2; ++side) {
+                    const int64_t nel = side ? n * n : m * m;
+                    void* b = side ? (void*)x.V : (void*)x.U;
+                    float* f = side ? XV : XU;
+                    widen.push_back({b, f, nel, widen_chunks, 0});
+                    widen_chunks += (nel + kEwChunk - 1) / kEwChunk;
+                    round16.push_back({f, b, nel, round_chunks, 1});
+                    round_chunks += (nel + kEwChunk - 1) / kEwChunk;
+                }
+                x.U = XU;
+                x.V = XV;
+            }
             if (gram16_eligible(M)) {
                 // bf16 M exactly, the fp32 operand as three exact bf16 pieces:
                 // every Gram product is three bf16 NT products accumulating in fp32
@@ -1267,6 +1305,11 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 for (const std::vector<Gemm16Prob>& st : q2) R.p2_16.push_back(put_gemm16(g->img, st, false));
             }
         }
+        R.nwiden = (int)widen.size();
+        R.widen_chunks = widen_chunks;
+        R.widen = g->img.put(widen);
+        R.round_chunks = round_chunks;
+        R.round16 = g->img.put(round16);
         R.comp.n = (int)comp.size();
         R.comp.max_d = 0;
         for (const CopyJob& c : comp) R.comp.max_d = std::max(R.comp.max_d, (int)c.d);
@@ -1451,13 +1494,18 @@ std::vector<QrClasses> active_classes(const std::vector<int>& d, int p) {
     return out;
 }
 
-// Panel p on the tall path (rows spread over workgroups, a launch per
-// column) when its tallest panel has more than kTallMinRows rows and all its
-// panels together at most kTallMaxRows: a few tall panels, which one
-// workgroup each would factorise with most of the GPU idle. With many
-// panels in flight the one-workgroup kernel already fills the GPU and reads
-// each panel once instead of once per column.
-constexpr int kTallMinRows = 4096;
+// Panel p on the tall path (rows spread over resident workgroups, one
+// cooperative launch) when its tallest panel has more than kTallMinRows rows
+// and all its panels together at most kTallMaxRows (and the workgroups fit
+// on the device): a few tall panels, which one workgroup each would
+// factorise with most of the GPU idle. With many panels in flight the
+// one-workgroup kernel already fills the GPU. Measured on one matrix, the
+// tall path takes 0.58x the time at order 12288, 1.05x at 6144 and 1.3x at
+// 3072, hence the threshold.
+#ifndef MATOPT_TALL_MIN_ROWS
+#define MATOPT_TALL_MIN_ROWS 6144
+#endif
+constexpr int kTallMinRows = MATOPT_TALL_MIN_ROWS;
 constexpr int64_t kTallMaxRows = 96 * 1024;
 bool use_tall_panels(const std::vector<int>& d, int p) {
     int64_t rows = 0;
@@ -1494,8 +1542,9 @@ hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vect
         for (int q = 0; q < kQrPanelsPerBlock; ++q) {
             const int p = b * kQrPanelsPerBlock + q;
             if (p >= maxp) break;
-            if (use_tall_panels(d, p)) {
-                if ((e = launch_qr_panel_tall(jobs, active_p(p), active_classes(d, p), p, max_d, s))) return e;
+            const std::vector<QrClasses> cls = active_classes(d, p);
+            if (use_tall_panels(d, p) && qr_tall_blocks(cls, p) > 0 && qr_tall_blocks(cls, p) <= qr_coop_capacity()) {
+                if ((e = launch_qr_panel_tall(jobs, active_p(p), cls, p, max_d, s))) return e;
             } else if ((e = launch_qr_panel(jobs, active_p(p), p, max_d, s))) {
                 return e;
             }
@@ -1519,6 +1568,7 @@ hipError_t run_qr(const QrJob* jobs, const std::vector<int>& np, const std::vect
 hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, hipStream_t s) {
     PhaseScope ps(g, OPT_PHASE_REFRESH, s);
     hipError_t e;
+    if (G.nwiden && (e = launch_cvt16(dptr<CvtJob>(g, G.widen), G.nwiden, G.widen_chunks, s))) return e;
     for (int it = 0; it < power_iters; ++it) {
         if (G.nsplit1) {
             if ((e = launch_split16(dptr<SplitJob>(g, G.split1), G.nsplit1, G.tiles1, s))) return e;
@@ -1540,6 +1590,7 @@ hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, h
         };
         if ((e = run_qr(dptr<QrJob>(g, G.qr.jobs), G.qr.np, G.qr.d, s, steps))) return e;
     }
+    if (G.nwiden && (e = launch_cvt16(dptr<CvtJob>(g, G.round16), G.nwiden, G.round_chunks, s))) return e;
     return hipSuccess;
 }
 
@@ -1714,8 +1765,9 @@ opt_status opt_group_step(opt_group_t g, void* stream) {
         return OPT_OK;
     }
     const bool refresh = g->hp.K > 0 && (g->t - 1) % g->hp.K == 0;
-    // bf16 rotations from the second step on (the first, with v = 0, in fp32)
-    if ((g->hp.flags & OPT_FLAG_BF16_ROTATION) && g->t > 1) {
+    // bf16 rotations from the second step on (the first, with v = 0, in
+    // fp32), or from the first with bases stored in 16 bits (no fp32 copy)
+    if ((g->hp.flags & OPT_FLAG_BF16_ROTATION) && (g->t > 1 || (g->hp.flags & OPT_FLAG_BF16_BASES))) {
         const bool carry_mode = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
         const bool carry = carry_mode && g->mt_valid && !refresh;
         // The bf16 copies of G and M live in the scratch that the refresh and
@@ -1881,6 +1933,8 @@ opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
     opt_status st = check_group(g);
     if (st || (st = set_device(g))) return st;
     if (g->hp.flags & OPT_FLAG_MUON) return fail(OPT_EUNSUPPORTED, "no bases with OPT_FLAG_MUON");
+    if (g->hp.flags & OPT_FLAG_BF16_BASES)
+        return fail(OPT_EUNSUPPORTED, "state checks read fp32 bases; not with OPT_FLAG_BF16_BASES");
     if (!out) return fail(OPT_EINVAL, "out is NULL");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before health");
@@ -1920,6 +1974,8 @@ opt_status opt_group_reorthonormalize(opt_group_t g, int32_t iters, void* stream
     opt_status st = check_group(g);
     if (st || (st = set_device(g))) return st;
     if (g->hp.flags & OPT_FLAG_MUON) return fail(OPT_EUNSUPPORTED, "no bases with OPT_FLAG_MUON");
+    if (g->hp.flags & OPT_FLAG_BF16_BASES)
+        return fail(OPT_EUNSUPPORTED, "re-orthonormalisation works on fp32 bases; not with OPT_FLAG_BF16_BASES");
     if (iters < 0) return fail(OPT_EINVAL, "iters must be >= 0");
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "pending HIP error before re-orthonormalisation");

@@ -104,8 +104,14 @@ constexpr int kQrTallRows = 256;
 
 hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipStream_t s);
 // The same panel factorisation with the rows of each panel spread over
-// workgroups and one launch per column (for few, tall panels); C holds the
-// runs of equal order of the first njobs jobs.
+// workgroups of kQrTallRows rows, all resident at once (one cooperative
+// launch, a grid-wide barrier per column): for few, tall panels. C holds the
+// runs of equal order of the first njobs jobs. qr_tall_blocks gives the
+// workgroups it needs (-1 if C needs more than one launch) and
+// qr_coop_capacity how many the device holds; launch_qr_panel_tall returns
+// hipErrorInvalidValue without launching anything when they do not fit.
+int qr_tall_blocks(const std::vector<QrClasses>& C, int p);
+int qr_coop_capacity();
 hipError_t launch_qr_panel_tall(const QrJob* jobs, int njobs, const std::vector<QrClasses>& C, int p, int max_d,
                                 hipStream_t s);
 hipError_t launch_qr_dots(const QrJob* jobs, const QrClasses& C, int p, hipStream_t s);

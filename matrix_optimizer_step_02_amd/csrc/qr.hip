@@ -579,32 +579,43 @@ __global__ __launch_bounds__(256) void qr_copy_block_kernel(const QrJob* __restr
 
 // ---- tall panels: rows spread over many workgroups ---------------------
 //
-// A panel of L rows factorised by one workgroup streams its column block
-// through that one CU once per column (plus the left-looking passes), so a
-// tall panel of a few large matrices leaves most of the GPU idle. Here the
-// panel's rows are split into slices of kQrTallRows, one workgroup each,
-// over all active matrices at once, and every column of the panel is one
-// launch: launches j = -1 .. jb - 1, then the reflectors' Gram matrix and T.
+// One workgroup factorises a panel of L rows by streaming its column block
+// through one CU once per column (plus the left-looking passes), so a few
+// tall panels leave most of the GPU idle. Here a panel's rows are split into
+// slices of kQrTallRows, one workgroup each, over all active matrices at
+// once, in one cooperative launch (every workgroup resident, which the
+// runtime checks): each workgroup keeps its slice in LDS for the whole panel,
+// and the columns advance in lock step with one grid-wide barrier per
+// column.
 //
-// Launch j (column j of the panel, j >= 0): every workgroup sums the
-// partial column sums the previous launch left (in a fixed slice order, so
-// the result is the same in every workgroup and run), forms the reflector of
-// column j from alpha = A[j][j] and sigma = sum_{i > j} A[i][j]^2 exactly as
-// qr_panel_kernel does, and the update weights w_q = v_j^T A[:, q] =
-// A[j][q] + scale sum_{i > j} A[i][j] A[i][q]; it applies H_j to its rows
-// (A[i][q] -= tau v_i w_q, q > j), stores v below the diagonal and beta on
-// it, and leaves the partial sums of column j + 1 over its rows below j + 1
-// (A[i][j+1] A[i][q] for q >= j + 1, from the updated values) and, in the
-// workgroup holding row j + 1, that row. Launch -1 only leaves column 0's
-// sums. Thread t handles column q = t mod 64 of the rows rg + 4 r of its
-// slice (rg = t / 64, one wavefront each): the wavefront's 64 lanes read a
-// row's 64 entries at once, and the row's column-j and column-(j+1) entries,
-// which its own lanes j and j+1 rewrite, are read by the same instruction
-// before any lane stores.
+// Column j: every workgroup of a matrix sums the partial column sums its
+// slices left (in a fixed slice order, so all of them, in every run, get the
+// same values), forms the reflector of column j from alpha = A[j][j] and
+// sigma = sum_{i > j} A[i][j]^2 exactly as qr_panel_kernel does, and the
+// update weights w_q = v_j^T A[:, q] = A[j][q] + scale sum_{i > j} A[i][j]
+// A[i][q]; it applies H_j to its rows (A[i][q] -= tau v_i w_q, q > j),
+// stores v below the diagonal and beta on it, and leaves the partial sums of
+// column j + 1 over its rows below j + 1 (A[i][j+1] A[i][q], q >= j + 1, from
+// the updated values) and, in the workgroup holding row j + 1, that row. The
+// pass before column 0 only leaves column 0's sums. Thread t handles column
+// q = t mod 64 of the slice rows rg + 4 r (rg = t / 64, one wavefront each);
+// a wavefront reads a row's column-j and column-(j+1) entries, which its own
+// lanes j and j+1 rewrite, with the same instructions before any lane stores.
+// At the end each workgroup writes its rows back and the Gram block of its
+// slice of the reflectors; qr_tall_t_kernel forms T.
 //
-// Scratch in the job's `part` buffer (floats; Gs = slices of the whole
-// order d): the partial sums [2][Gs][64] (ping-pong by column parity), the
-// diagonal row [2][64], tau [64], and the per-slice Gram blocks [Gs][64][64].
+// The barrier: thread 0 of each workgroup adds one to a counter with release
+// semantics and waits, with acquire semantics, for the count of all
+// workgroups; the sums cross workgroups (and XCDs) through agent-scope atomic
+// stores and loads. Every wait is bounded: past about a quarter second the
+// workgroup raises the error flag, stops waiting (so the grid always drains)
+// and qr_tall_t_kernel turns that panel's T into NaN, so a failure shows in
+// the results instead of hanging the device.
+//
+// Scratch in the job's `part` buffer (floats; gmax = slices of the whole
+// order d): the partial sums [2][gmax][64] (ping-pong by column parity), the
+// diagonal row [2][64], tau [64], the per-slice Gram blocks [gmax][64][64],
+// then the barrier counter and error flag (the first job's are used).
 
 __host__ __device__ inline int qr_tall_gmax(int d) { return (d + kQrTallRows - 1) / kQrTallRows; }
 
@@ -613,140 +624,179 @@ struct TallScratch {
     float* row;    // [2][64]
     float* tau;    // [64]
     float* gram;   // [gmax][64][64]
+    unsigned* bar; // [0] counter, [1] error flag
     __device__ TallScratch(const QrJob& J) {
         const int gmax = qr_tall_gmax(J.d);
         sums = J.part;
         row = sums + 2 * gmax * 64;
         tau = row + 128;
         gram = tau + 64;
+        bar = (unsigned*)(gram + (int64_t)gmax * PB * PB);
     }
 };
 
-__global__ __launch_bounds__(256) void qr_tall_col_kernel(const QrJob* __restrict__ jobs, QrClasses cls, int p,
-                                                          int j) {
+__device__ __forceinline__ void coop_barrier(unsigned* bar, unsigned target) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(bar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned spins = 0;
+        while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target &&
+               __hip_atomic_load(bar + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++spins == (1u << 22)) {
+                __hip_atomic_store(bar + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(256) void qr_coop_panel_kernel(const QrJob* __restrict__ jobs, QrClasses cls, int p,
+                                                            int nblocks) {
+    __shared__ float As[kQrTallRows][PB];
     __shared__ float sD[64], sRow[64], red[4][64];
-    int job, slice;
-    if (!qr_locate(cls, QG_TALL, p, blockIdx.x, job, slice)) return;
+    int job = 0, slice = 0;
+    const bool have = qr_locate(cls, QG_TALL, p, blockIdx.x, job, slice);
     const QrJob Jb = jobs[job];
-    const int d = Jb.d, k = p * PB, L = d - k, jb = min(PB, L);
-    if (j >= jb) return;
+    const int d = Jb.d, k = p * PB, L = d - k, jb = have ? min(PB, L) : 0;
     const int G = (L + kQrTallRows - 1) / kQrTallRows;
     const TallScratch sc(Jb);
+    unsigned* bar = TallScratch(jobs[0]).bar;
     const int gmax = qr_tall_gmax(d);
     const int tid = threadIdx.x, q = tid & 63, rg = tid >> 6;
     gmem<float> A = gptr(Jb.Z + (int64_t)k * d + k);
-
-    // the reflector of column j
-    float beta = 0.f, tau = 0.f, scale = 0.f, w = 0.f, w1 = 0.f;
-    if (j >= 0) {
-        if (tid < 64) {
-            gmem<const float> in = gptr((const float*)sc.sums + (j & 1) * gmax * 64 + tid);
-            float sum = 0.f;
-            for (int g = 0; g < G; ++g) sum += in[g * 64];
-            sD[tid] = sum;
-            sRow[tid] = gptr(sc.row)[(j & 1) * 64 + tid];
-        }
-        __syncthreads();
-        const float alpha = sRow[j], sig = sD[j];
-        if (sig == 0.f) {
-            beta = alpha;
-        } else {
-            const float nrm = __builtin_sqrtf(alpha * alpha + sig);
-            beta = -__builtin_copysignf(nrm, alpha);
-            tau = (beta - alpha) / beta;
-            scale = 1.f / (alpha - beta);
-        }
-        if (q > j && q < jb) w = sRow[q] + scale * sD[q];
-        if (j + 1 < jb) w1 = sRow[j + 1] + scale * sD[j + 1];
-        if (slice == 0 && tid == 0) gptr(sc.tau)[j] = tau;
-    }
-    const int jn = j + 1;   // the column whose sums this launch leaves
-    const bool next = jn < jb;
-    const bool qn = next && q >= jn && q < jb;
-    float acc = 0.f;
     const int r0 = slice * kQrTallRows;
-    const int r1 = min(L, r0 + kQrTallRows);
-    gmem<float> rowout = gptr(sc.row + (jn & 1) * 64);
-    constexpr int U = 4;   // rows in flight per wavefront
-    for (int i0 = r0 + rg; i0 < r1; i0 += 4 * U) {
-        float aj[U], aj1[U], aq[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + 4 * u;
-            const bool ok = i < r1 && i >= (j < 0 ? 0 : j);
-            const int ic = ok ? i : r0;
-            aj[u] = (j >= 0) ? A[(int64_t)ic * d + j] : 0.f;
-            aj1[u] = next ? A[(int64_t)ic * d + jn] : 0.f;
-            aq[u] = q < jb ? A[(int64_t)ic * d + q] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + 4 * u;
-            if (i >= r1 || i < (j < 0 ? 0 : j)) continue;
-            float anew = aq[u], a1 = aj1[u];
-            if (j >= 0) {
-                const float vi = (i == j) ? 1.f : scale * aj[u];
-                if (q > j && q < jb) {
-                    anew = aq[u] - tau * vi * w;
-                    A[(int64_t)i * d + q] = anew;
-                } else if (q == j) {
-                    A[(int64_t)i * d + j] = (i == j) ? beta : vi;
-                }
-                a1 = aj1[u] - tau * vi * w1;
-            }
-            if (qn) {
-                if (i > jn) acc += a1 * anew;
-                else if (i == jn) rowout[q] = anew;
-            }
-        }
-    }
-    if (!next) return;
-    red[rg][q] = acc;
-    __syncthreads();
-    if (tid < 64) {
-        const float sum = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-        gptr(sc.sums)[(jn & 1) * gmax * 64 + slice * 64 + tid] = sum;
-    }
-}
+    const int rows = have ? min(L - r0, kQrTallRows) : 0;
 
-// Per-slice Gram blocks of the panel's reflectors Y (unit lower: ones on the
-// diagonal, zeros above, the stored v below): thread (bl, bm) forms the 4 x 4
-// block S[4 bl .. +3][4 bm .. +3] over the slice's rows, staged through LDS.
-__global__ __launch_bounds__(256) void qr_tall_gram_kernel(const QrJob* __restrict__ jobs, QrClasses cls, int p) {
-    __shared__ float Ys[kQrTallRows][PB + 1];
-    int job, slice;
-    if (!qr_locate(cls, QG_TALL, p, blockIdx.x, job, slice)) return;
-    const QrJob Jb = jobs[job];
-    const int d = Jb.d, k = p * PB, L = d - k, jb = min(PB, L);
-    const TallScratch sc(Jb);
-    gmem<const float> A = gptr((const float*)Jb.Z + (int64_t)k * d + k);
-    const int r0 = slice * kQrTallRows, rows = min(L - r0, kQrTallRows);
-    for (int e = threadIdx.x; e < kQrTallRows * PB; e += 256) {
-        const int r = e / PB, c = e % PB, i = r0 + r;
-        float y = 0.f;
-        if (r < rows && c < jb) y = (i < c) ? 0.f : (i == c ? 1.f : A[(int64_t)i * d + c]);
-        Ys[r][c] = y;
+    for (int e = tid; e < kQrTallRows * PB; e += 256) {
+        const int r = e / PB, c = e % PB;
+        As[r][c] = (r < rows && c < jb) ? A[(int64_t)(r0 + r) * d + c] : 0.f;
     }
     __syncthreads();
-    const int bl = threadIdx.x / 16, bm = threadIdx.x % 16;
-    float acc[4][4] = {};
+
+    unsigned nb = 0;
+    for (int j = -1; j < PB; ++j) {
+        if (j >= 0) coop_barrier(bar, (unsigned)nblocks * ++nb);
+        if (j >= jb) continue;   // this matrix's last panel is narrower: idle, but in every barrier
+        float beta = 0.f, tau = 0.f, scale = 0.f, w = 0.f, w1 = 0.f;
+        if (j >= 0) {
+            // the slices' partial sums of column j: the four wavefronts load
+            // every fourth slice at once (all loads in flight together), then
+            // the four sums are added in a fixed order
+            {
+                const float* in = sc.sums + (j & 1) * gmax * 64 + q;
+                float part[12];
+#pragma unroll
+                for (int u = 0; u < 12; ++u) {
+                    const int g = rg + 4 * u;
+                    part[u] = g < G ? ld_agent(in + g * 64) : 0.f;
+                }
+                float sum = 0.f;
+#pragma unroll
+                for (int u = 0; u < 12; ++u) sum += part[u];
+                for (int g = rg + 48; g < G; g += 4) sum += ld_agent(in + g * 64);   // orders past 12288
+                red[rg][q] = sum;
+                if (rg == 0) sRow[q] = ld_agent(sc.row + (j & 1) * 64 + q);
+            }
+            __syncthreads();
+            if (tid < 64) sD[tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+            __syncthreads();
+            const float alpha = sRow[j], sig = sD[j];
+            if (sig == 0.f) {
+                beta = alpha;
+            } else {
+                const float nrm = __builtin_sqrtf(alpha * alpha + sig);
+                beta = -__builtin_copysignf(nrm, alpha);
+                tau = (beta - alpha) / beta;
+                scale = 1.f / (alpha - beta);
+            }
+            if (q > j && q < jb) w = sRow[q] + scale * sD[q];
+            if (j + 1 < jb) w1 = sRow[j + 1] + scale * sD[j + 1];
+            if (slice == 0 && tid == 0) gptr(sc.tau)[j] = tau;
+        }
+        const int jn = j + 1;   // the column whose sums this pass leaves
+        const bool next = jn < jb;
+        const bool qn = next && q >= jn && q < jb;
+        const int lo = j < 0 ? 0 : j;   // rows above column j's diagonal are not touched
+        float acc = 0.f;
+        constexpr int U = 8;   // rows of a wavefront in flight
+        for (int rb = rg; rb < rows; rb += 4 * U) {
+            float aj[U], a1o[U], aq[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = min(rb + 4 * u, kQrTallRows - 1);
+                aj[u] = j >= 0 ? As[r][j] : 0.f;
+                a1o[u] = next ? As[r][jn] : 0.f;
+                aq[u] = As[r][q];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int r = rb + 4 * u, i = r0 + r;
+                if (r >= rows || i < lo) continue;
+                float anew = aq[u], a1 = a1o[u];
+                if (j >= 0) {
+                    const float vi = (i == j) ? 1.f : scale * aj[u];
+                    a1 = a1o[u] - tau * vi * w1;
+                    if (q > j && q < jb) anew = aq[u] - tau * vi * w;
+                    if (q > j) As[r][q] = anew;
+                    else if (q == j) As[r][j] = (i == j) ? beta : vi;
+                }
+                if (qn) {
+                    if (i > jn) acc += a1 * anew;
+                    else if (i == jn) st_agent(sc.row + (jn & 1) * 64 + q, anew);
+                }
+            }
+        }
+        if (!next) continue;
+        __syncthreads();   // red[] was read for this column's sums above
+        red[rg][q] = acc;
+        __syncthreads();
+        if (tid < 64) {
+            const float sum = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+            st_agent(sc.sums + (jn & 1) * gmax * 64 + slice * 64 + tid, sum);
+        }
+    }
+    __syncthreads();
+    // the factorised slice back to Z, and the slice's Gram block of Y
+    for (int e = tid; e < rows * PB; e += 256) {
+        const int r = e / PB, c = e % PB;
+        if (c < jb) A[(int64_t)(r0 + r) * d + c] = As[r][c];
+    }
+    if (!have) return;
+    const int bl = tid / 16, bm = tid % 16;
+    float g[4][4] = {};
     for (int r = 0; r < rows; ++r) {
+        const int i = r0 + r;
         float yl[4], ym[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            yl[e] = Ys[r][4 * bl + e];
-            ym[e] = Ys[r][4 * bm + e];
+            const int cl = 4 * bl + e, cm = 4 * bm + e;
+            yl[e] = (cl >= jb || i < cl) ? 0.f : (i == cl ? 1.f : As[r][cl]);
+            ym[e] = (cm >= jb || i < cm) ? 0.f : (i == cm ? 1.f : As[r][cm]);
         }
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] += yl[a] * ym[b];
+            for (int b = 0; b < 4; ++b) g[a][b] += yl[a] * ym[b];
     }
     gmem<float> out = gptr(sc.gram + (int64_t)slice * PB * PB);
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) out[(4 * bl + a) * PB + 4 * bm + b] = acc[a][b];
+        for (int b = 0; b < 4; ++b) out[(4 * bl + a) * PB + 4 * bm + b] = g[a][b];
+}
+
+__global__ void qr_coop_reset_kernel(const QrJob* __restrict__ jobs) {
+    unsigned* bar = TallScratch(jobs[0]).bar;
+    if (threadIdx.x < 2) bar[threadIdx.x] = 0u;
 }
 
 // T of the panel from the summed Gram blocks and tau, one workgroup per job,
@@ -767,6 +817,8 @@ __global__ __launch_bounds__(256) void qr_tall_t_kernel(const QrJob* __restrict_
         S[e / PB][e % PB] = sum;
     }
     if (threadIdx.x < PB) tau[threadIdx.x] = threadIdx.x < jb ? gptr((const float*)sc.tau)[threadIdx.x] : 0.f;
+    // a barrier that gave up (the error flag): make the failure visible
+    const bool failed = gptr((const unsigned*)TallScratch(jobs[0]).bar)[1] != 0u;
     __syncthreads();
     if (threadIdx.x < PB) {
         const int r = threadIdx.x;
@@ -786,7 +838,7 @@ __global__ __launch_bounds__(256) void qr_tall_t_kernel(const QrJob* __restrict_
     }
     __syncthreads();
     gmem<float> Tout = gptr(Jb.T + (int64_t)p * PB * PB);
-    for (int e = threadIdx.x; e < PB * PB; e += 256) Tout[e] = Tf[e / PB][e % PB];
+    for (int e = threadIdx.x; e < PB * PB; e += 256) Tout[e] = failed ? __builtin_nanf("") : Tf[e / PB][e % PB];
 }
 
 }  // namespace
@@ -816,22 +868,40 @@ hipError_t launch_qr_panel(const QrJob* jobs, int njobs, int p, int max_d, hipSt
     return hipGetLastError();
 }
 
-// Panel p of the first njobs jobs on the tall path; C: their runs of equal
-// order (QG_TALL blocks per job = the slices of the panel).
+// Workgroups of the cooperative panel kernel that can be resident at once
+// on the current device (0 if the runtime cannot launch it cooperatively).
+int qr_coop_capacity() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev]) return cached[dev] > 0 ? cached[dev] : 0;
+    int coop = 0, cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, qr_coop_panel_kernel, 256, 0) != hipSuccess) {
+        cached[dev] = -1;
+        return 0;
+    }
+    cached[dev] = cus * per > 0 ? cus * per : -1;
+    return cached[dev] > 0 ? cached[dev] : 0;
+}
+
+int qr_tall_blocks(const std::vector<QrClasses>& C, int p) {
+    if (C.size() != 1) return -1;   // one launch covers one set of classes
+    return qr_total_blocks(C[0], QG_TALL, p);
+}
+
 hipError_t launch_qr_panel_tall(const QrJob* jobs, int njobs, const std::vector<QrClasses>& C, int p, int max_d,
                                 hipStream_t s) {
     const int L = max_d - p * PB;
     if (njobs <= 0 || L <= 0) return hipSuccess;
-    const int jb = min(PB, L);
-    for (int j = -1; j < jb; ++j)
-        for (const QrClasses& c : C) {
-            const int blocks = qr_total_blocks(c, QG_TALL, p);
-            if (blocks > 0) hipLaunchKernelGGL(qr_tall_col_kernel, dim3(blocks), dim3(256), 0, s, jobs, c, p, j);
-        }
-    for (const QrClasses& c : C) {
-        const int blocks = qr_total_blocks(c, QG_TALL, p);
-        if (blocks > 0) hipLaunchKernelGGL(qr_tall_gram_kernel, dim3(blocks), dim3(256), 0, s, jobs, c, p);
-    }
+    int blocks = qr_tall_blocks(C, p);
+    if (blocks <= 0 || blocks > qr_coop_capacity()) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(qr_coop_reset_kernel, dim3(1), dim3(64), 0, s, jobs);
+    QrClasses c = C[0];
+    void* args[] = {(void*)&jobs, (void*)&c, (void*)&p, (void*)&blocks};
+    hipError_t e = hipLaunchCooperativeKernel((const void*)qr_coop_panel_kernel, dim3(blocks), dim3(256), args, 0, s);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(qr_tall_t_kernel, dim3(njobs), dim3(256), 0, s, jobs, p);
     return hipGetLastError();
 }

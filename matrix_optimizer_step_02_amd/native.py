@@ -20,6 +20,7 @@ OPT_FLAG_ROTATED_MOMENTUM = 1
 OPT_FLAG_BF16_ROTATION = 2
 OPT_FLAG_MUON = 4
 OPT_FLAG_FP32_MFMA = 8
+OPT_FLAG_BF16_BASES = 16
 OPT_MAX_DIM = 16384
 OPT_STATIC_MAX_DIM = 4096
 PHASES = ("momentum", "refresh", "rot_left", "rot_right", "adam", "back_left", "back_right", "ortho", "rot_pieced")

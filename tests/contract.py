@@ -262,6 +262,47 @@ def gate_basis_sampled(X_dev, M_t, X_prev, side, passes, name, nsample=256, seed
                                  "fwd_good": fwd, "fwd_tol": fwd_tol, "good_cols": float(good.sum())})
 
 
+def gate_basis16(X16_dev, M_t, X16_prev, side, passes, name) -> GateReport:
+    """A refresh whose result is stored in bfloat16 (bases stored in 16 bits;
+    oracle.bf16_rotation.refresh_bases_bf16), teacher-forced from the
+    device's previous stored basis. The device rounds its fp32 result, the
+    oracle the exact one: on the well-determined columns (prefix conditioning
+    <= 1e2, as gate A) each entry within one bf16 ulp of the exact basis plus
+    the fp32 forward bound of gate A; orthonormality within 2^-7 (rounding
+    each entry by at most 2^-9 relative moves X^T X - I by at most 2^-8);
+    the triangularisation of the one-shot input within 1e-2; the sign
+    convention as gate A."""
+    X = np.asarray(X16_dev, np.float64)
+    X0 = np.asarray(X16_prev, np.float64)
+    M_t = np.asarray(M_t, np.float64)
+    d = X.shape[0]
+    r = min(M_t.shape)
+    A = M_t @ M_t.T if side == "U" else M_t.T @ M_t
+    Zhat = one_shot_input(A, X0, r, passes)
+    if d <= 1100:
+        ref = oracle.subspace_iteration(A, X0, r, passes)
+        ref32 = fp32_refresh(M_t, X0, side, passes)
+        kappa = _prefix_kappa(Zhat)
+    else:   # the leading columns alone, as gate_basis does at large orders
+        k = min(r, LEAD_COLS)
+        ref = oracle.leading_subspace_iteration(M_t, X0[:, :k], side, passes)
+        ref32 = fp32_refresh_leading(M_t, X0[:, :k], side, passes)
+        kappa = _prefix_kappa(Zhat[:, :k])
+    good = kappa <= 1e2
+    fwd_tol = max(1e-4, FWD_FACTOR * float(np.max(np.abs(ref32[:, good] - ref[:, good])))) if good.any() else 1e-4
+    err = np.abs(X[:, :ref.shape[1]][:, good] - ref[:, good])
+    ratio = float(np.max(err / (ulp_bf16(ref[:, good]) + fwd_tol))) if good.any() else 0.0   # noqa: E501
+    orth = float(np.max(np.abs(X.T @ X - np.eye(d))))
+    norms = np.linalg.norm(Zhat, axis=0)
+    norms[norms == 0] = 1.0
+    Rd = X.T @ (Zhat / norms)
+    back = float(np.linalg.norm(np.tril(Rd, -1)) / max(np.linalg.norm(Rd), 1e-300))
+    sign_ok, nsign, dmin = _sign_check(np.diag(Rd))
+    ok = ratio <= 1.0 and orth <= 2.0 ** -7 and back <= 1e-2 and sign_ok
+    return GateReport(name, ok, {"fwd_ratio": ratio, "good_cols": float(good.sum()), "orth": orth,
+                                 "backward": back, "diag_min": dmin})
+
+
 def gate_refresh(M_t, U_prev, V_prev, U_dev, V_dev, passes, forward_max_d=1100) -> List[GateReport]:
     M_t = np.asarray(M_t, np.float64)
     m, n = M_t.shape

@@ -20,11 +20,12 @@ def oracle_hyper(wl):
 
 def build_group(wl, device="cuda", hp=None):
     import matrix_optimizer_step_02_amd as mo
+    hp = hp or hyper_of(wl)
     states = []
     for i, s in enumerate(wl.matrices):
         W0 = workloads.initial_weight(wl, i, device)
-        states.append(mo.new_state(s.m, s.n, wl.m_dtype, device, W0=W0))
-    grp = mo.RotatedAdamGroup(states, hp or hyper_of(wl))
+        states.append(mo.new_state(s.m, s.n, wl.m_dtype, device, W0=W0, bases16=hp.bf16_bases))
+    grp = mo.RotatedAdamGroup(states, hp)
     return grp, states
 
 

@@ -124,7 +124,26 @@ def test_orthonormalize_well_conditioned_matches_oracle(d):
     assert np.max(np.abs(Q.T @ Q - np.eye(d))) < 1e-5
 
 
-@pytest.mark.parametrize("d", [64, 300, 1024])
+@pytest.mark.parametrize("d", [6400, 8200])
+def test_orthonormalize_tall_panels_match_oracle(d):
+    """Panels of more than 6144 rows are factorised on the tall path (the
+    panel's rows spread over resident workgroups, one cooperative launch, a
+    grid-wide barrier per column). Well-conditioned input; the leading 320
+    columns of Q (which depend only on the leading columns of Z) against the
+    oracle's positive-diagonal factor of those columns, and the whole Q's
+    orthonormality."""
+    import oracle
+    print(f"qr tall d={d}", flush=True)
+    rng = np.random.default_rng(d)
+    Z = oracle.round_f32(np.eye(d) + 0.3 * rng.standard_normal((d, d)) / np.sqrt(d))
+    Q = _orthonormalize(Z)
+    k = 320
+    ref = oracle.orthonormal_factor(Z[:, :k], q_cols=k)
+    assert np.max(np.abs(Q[:, :k] - ref)) < 2e-5
+    assert np.max(np.abs(Q.T @ Q - np.eye(d))) < 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 300, 1024, 2500])
 def test_orthonormalize_gaussian_properties(d):
     print(f"qr gauss d={d}", flush=True)
     rng = np.random.default_rng(100 + d)
