@@ -41,9 +41,10 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "rotation_gemm_traffic.json")
 GEMM_SOURCES = ("matrix_optimizer_step_02_amd/csrc/gemm.hip", "matrix_optimizer_step_02_amd/csrc/gemm.h",
                 "matrix_optimizer_step_02_amd/csrc/gmem.h", "matrix_optimizer_step_02_amd/csrc/api.hip")
 def is_rotation_gemm(kernel_name: str) -> bool:
-    """Any instantiation of the fp32 grouped GEMM: in a step without a
-    refresh every one of its launches is a rotation phase."""
-    return "gemm_grouped_kernel<" in kernel_name
+    """Any instantiation of the grouped GEMM (fp32 MFMAs, or the fp32
+    products on bf16 MFMAs): in a step without a refresh every one of its
+    launches is a rotation phase."""
+    return "gemm_grouped_kernel<" in kernel_name or "gemm_x6_kernel<" in kernel_name
 
 METRIC = "optimizer steps/s + params updated/s per micro-group; HBM GB/s & MFMA util"
 

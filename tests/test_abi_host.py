@@ -280,9 +280,11 @@ def test_bench_selects_rotation_dispatches_from_non_refresh_steps():
     name = ("void matopt::(anonymous namespace)::gemm_grouped_kernel<matopt::(anonymous namespace)::"
             "Cfg<2, 2, 4, 2, 16>, false, {}, false, {}>(matopt::(anonymous namespace)::GemmArgs)")
     gemm, bf16_b, bt = name.format("false", "false"), name.format("false", "true"), name.format("true", "false")
+    x6 = ("void matopt::(anonymous namespace)::gemm_x6_kernel<matopt::(anonymous namespace)::Cfg<2, 2, 4, 2, 16>, "
+          "false, false, false>(matopt::(anonymous namespace)::GemmArgs)")
     seq = ["copyBuffer", "momentum_kernel", "momentum_kernel", gemm, "qr_panel_kernel", gemm, gemm,
            "rotated_adam_kernel", gemm, "momentum_kernel", "momentum_kernel", gemm, bf16_b, gemm,
-           "rotated_adam_kernel", gemm, bt, "gemm16_kernel<Cfg16<2, 2, 4, 4, 64, 2>, false>(Gemm16Args)"]
+           "rotated_adam_kernel", x6, bt, "gemm16_kernel<Cfg16<2, 2, 4, 4, 64, 2>, false>(Gemm16Args)"]
     rows = [{"Dispatch_Id": str(i + 1), "Kernel_Name": k} for i, k in enumerate(seq)]
     picked = bench.rotation_dispatches(list(reversed(rows)))
     assert [int(r["Dispatch_Id"]) for r in picked] == [12, 13, 14, 16, 17]
