@@ -140,7 +140,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str, calib_mib: int, out_path: str 
     fr = [float(r["Counter_Value"]) * 1024 * sf for r in rotation_dispatches(F)]
     wr = [float(r["Counter_Value"]) * 1024 * sw for r in rotation_dispatches(W)]
     out = {
-        "kernel": "gemm_grouped_kernel, rotation-phase instantiations",
+        "kernel": "gemm_x6_kernel (and gemm_grouped_kernel), rotation-phase instantiations",
         "gemm_source_sha256": gemm_source_hash(),
         "launches": len(fr),
         "fetch_bytes_per_launch": sum(fr) / len(fr),
@@ -302,6 +302,9 @@ def main(argv=None):
     ap.add_argument("--ns-iters", type=int, default=5, help="Newton-Schulz iterations of --muon")
     ap.add_argument("--fp32-mfma", action="store_true",
                     help="keep the fp32 products on fp32 MFMAs (no bf16-piece products)")
+    ap.add_argument("--compare-single", action="store_true",
+                    help="also time one plain product of the same flop count as an average rotation launch "
+                         "(opt_gemm_x6, square, fp32 operands) to compare the grouped launches' rate with")
     ap.add_argument("--refresh-cap-gib", type=float, default=0.0,
                     help="scratch cap of one refresh batch in GiB (0: the library default)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -485,6 +488,47 @@ def main(argv=None):
         extra["micro_groups"] = rows
         if phases and phases.get("refresh", (0, 0))[0]:
             extra["refresh_ms_per_step"] = phases["refresh"][0] / args.steps
+
+    if args.compare_single and roofline and roofline.get("flops_per_launch") and not (args.bf16_rotation or args.muon
+                                                                                      or args.fp32_mfma):
+        # one square fp32 product with the flops of an average rotation launch
+        f = roofline["flops_per_launch"]
+        side = max(256, int(round((f / 2.0) ** (1.0 / 3.0) / 256.0)) * 256)
+        A = torch.randn(side, side, device=dev)
+        B = torch.randn(side, side, device=dev)
+        Cm = torch.empty(side, side, device=dev)
+        s0 = mo.stream_ptr()
+        mo.native.opt_gemm_x6(0, 0, side, side, side, 1.0, A.data_ptr(), 0, side, B.data_ptr(), 0, side, 0.0,
+                              Cm.data_ptr(), side, s0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            mo.native.opt_gemm_x6(0, 0, side, side, side, 1.0, A.data_ptr(), 0, side, B.data_ptr(), 0, side, 0.0,
+                                  Cm.data_ptr(), side, s0)
+        e1.record()
+        torch.cuda.synchronize()
+        ms1 = e0.elapsed_time(e1) / 5
+        single = 2.0 * side ** 3 / (ms1 * 1e-3) / 1e12
+        # a practical ceiling for comparison only (not part of the product):
+        # torch's bf16 matmul (hipBLASLt) on the same shape, whose rate / 6 is
+        # what six bf16 piece products per fp32 product could reach at that
+        # library's efficiency
+        Ab, Bb = A.to(torch.bfloat16), B.to(torch.bfloat16)
+        torch.matmul(Ab, Bb)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            torch.matmul(Ab, Bb)
+        e1.record()
+        torch.cuda.synchronize()
+        bf16_lib = 2.0 * side ** 3 / (e0.elapsed_time(e1) / 5 * 1e-3) / 1e12
+        extra["single_product"] = {"shape": [side, side, side], "ms": ms1, "tflops": single,
+                                   "grouped_tflops": roofline["achieved"],
+                                   "grouped_over_single": roofline["achieved"] / single,
+                                   "hipblaslt_bf16_tflops": bf16_lib,
+                                   "grouped_over_hipblaslt_bf16_div6": roofline["achieved"] / (bf16_lib / 6)}
+        del A, B, Cm, Ab, Bb
 
     cpu = None
     if args.cpu_sample_s > 0:

@@ -171,8 +171,11 @@ typedef struct {
     int32_t power_iters;      /* orthogonal-iteration passes per refresh, >= 1 */
     uint64_t capacity_bytes;  /* micro-group cap on sum(4 m n); 0 selects 1 << 29 (512 MiB) */
     uint64_t refresh_capacity_bytes; /* cap on the refresh scratch of one refresh batch (the
-                                        d x d QR inputs and their scratch); 0 selects 48 GiB.
-                                        A matrix larger than the cap forms a batch alone. */
+                                        d x d QR inputs and their scratch); 0 selects the larger
+                                        of 4 GiB and the bytes of the copies of the bases and
+                                        the step scratch, which the refresh buffers overlay (so
+                                        the refresh adds no workspace beyond them). A matrix
+                                        larger than the cap forms a batch alone. */
     uint32_t flags;           /* OPT_FLAG_* bits; others must be 0 */
     int32_t ns_iters;         /* Newton-Schulz iterations of OPT_FLAG_MUON, >= 1 there; else ignored */
 } opt_hparams;
@@ -181,8 +184,11 @@ typedef struct {
 #define OPT_MAX_MATRICES 65536
 
 /* Bytes of device workspace a group over these matrices needs (host only).
- * The workspace holds the device-side work lists, copies of the bases and the
- * scratch of one micro-group (reused by every group in turn). The copies:
+ * The workspace holds the device-side work lists, then either the copies of
+ * the bases followed by the scratch of one micro-group (reused by every group
+ * in turn), or, during a refresh (and the drift check of opt_group_health),
+ * the buffers of one refresh batch, which overlay both: the total is the
+ * tables plus the larger of the two. The copies:
  * with fp32 rotations (no flag, or OPT_FLAG_ROTATED_MOMENTUM alone) U^T in
  * fp32, 4 m^2 bytes per matrix, so that U^T G and U^T M read rows of U^T,
  * and without flags, for a bf16 M with both sides multiples of 8, the three
@@ -190,10 +196,17 @@ typedef struct {
  * OPT_FLAG_FP32_MFMA);
  * with OPT_FLAG_BF16_ROTATION the bf16 bases described there. They are
  * rebuilt on the first step after a create, a refresh, refresh_basis,
- * reorthonormalize or set_step: a caller that writes U or V itself must call
- * opt_group_set_step afterwards. */
+ * reorthonormalize, health or set_step: a caller that writes U or V itself
+ * must call opt_group_set_step afterwards. */
 opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
                                     const opt_hparams* hp, uint64_t* bytes);
+
+/* The parts of that workspace (host only), in bytes: parts[0] the work
+ * lists, parts[1] the copies of the bases, parts[2] the step scratch,
+ * parts[3] the largest refresh batch's buffers. The workspace size is
+ * parts[0] + max(parts[1] + parts[2], parts[3]). `parts` has 4 entries. */
+opt_status opt_group_workspace_parts(const opt_matrix_desc* descs, int32_t count,
+                                     const opt_hparams* hp, uint64_t* parts);
 
 /* Validate, plan the micro-groups, lay out the workspace and upload the work
  * lists with an asynchronous copy on `stream`. `workspace` must be device
@@ -316,7 +329,9 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
  * that matter accumulate in fp32, and the ones left out are below 2^-23 of
  * each product. Same arguments as opt_gemm; the supported layouts are
  * (trans_a, trans_b, a_dtype, b_dtype) = (0, 0, F32, F32), (1, 0, F32, F32),
- * (0, 1, F32, F32) and (0, 0, F32, BF16); others return OPT_EUNSUPPORTED. */
+ * (0, 1, F32, F32), (0, 0, F32, BF16) and (0, 0, BF16, F32); with a bf16
+ * operand, which is its own high piece, three piece products. Others return
+ * OPT_EUNSUPPORTED. */
 opt_status opt_gemm_x6(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
                        float alpha, const void* A, int32_t a_dtype, int64_t lda,
                        const void* B, int32_t b_dtype, int64_t ldb,

@@ -216,6 +216,9 @@ struct opt_group_s {
     uint64_t ws_bytes = 0;
     Image img;
     uint64_t table_bytes = 0, scratch_bytes = 0;
+    // the largest refresh batch's buffers, which start where the copies of
+    // the bases start and overlay them and the scratch
+    uint64_t refresh_bytes_max = 0;
     // copies of the bases after the tables, before the scratch: bf16 U, U^T,
     // V, V^T (bf16-rotation variant) or fp32 U^T (fp32 rotations), their
     // conversion launch, and whether they match U, V
@@ -283,8 +286,11 @@ uint64_t capacity_of(const opt_hparams* hp) {
     return hp->capacity_bytes ? hp->capacity_bytes : (1ull << 29);
 }
 
-uint64_t refresh_capacity_of(const opt_hparams* hp) {
-    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : (48ull << 30);
+// The refresh cap: the caller's, else the larger of 4 GiB and `overlay`, the
+// bytes of the copies of the bases and the step's scratch, which a refresh
+// batch's buffers overlay (the copies are rebuilt after every refresh).
+uint64_t refresh_capacity_of(const opt_hparams* hp, uint64_t overlay) {
+    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : std::max(4ull << 30, (unsigned long long)overlay);
 }
 
 struct Span {
@@ -775,8 +781,9 @@ uint64_t refresh_bytes(int64_t m, int64_t n) {
 
 // Refresh batches: matrices in LPT order, next-fit under the refresh cap (a
 // matrix above the cap forms a batch of its own).
-std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vector<std::vector<int>>& plan) {
-    const uint64_t cap = refresh_capacity_of(&g->hp);
+std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vector<std::vector<int>>& plan,
+                                           uint64_t overlay) {
+    const uint64_t cap = refresh_capacity_of(&g->hp, overlay);
     std::vector<std::vector<int>> out;
     uint64_t used = 0;
     for (const std::vector<int>& members : plan)
@@ -812,6 +819,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
     g->rbatches.clear();
     g->img.bytes.clear();
     g->scratch_bytes = 0;
+    g->refresh_bytes_max = 0;
     const bool r16 = g->hp.flags & OPT_FLAG_BF16_ROTATION;
     // the tables depend on the flags, never on whether a pointer is set, so
     // that the size query (which reads no pointer) matches create
@@ -1181,7 +1189,12 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
 
     // the refresh's Gram products and QR block updates on bf16 MFMAs too
     const bool rx6 = !(g->hp.flags & OPT_FLAG_FP32_MFMA);
-    for (const std::vector<int>& members : muon ? std::vector<std::vector<int>>{} : plan_refresh(g, plan)) {
+    // A refresh batch's buffers start at the copies of the bases: a refresh
+    // makes the copies stale (they are rebuilt from the new U, V before any
+    // rotation reads them) and runs between the steps' use of the scratch.
+    char* const rscratch = region;
+    const uint64_t overlay = g->bases_bytes + g->scratch_bytes;
+    for (const std::vector<int>& members : muon ? std::vector<std::vector<int>>{} : plan_refresh(g, plan, overlay)) {
         RefreshBatch R;
         R.mats = members;
         uint64_t off = 0;
@@ -1214,16 +1227,16 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             const Mat& M = g->mats[mi];
             opt_matrix_desc x = M.d;
             const int64_t m = x.m, n = x.n, r = std::min(m, n);
-            float* B1U = (float*)(scratch + off); off += align_up(4ull * n * r);
-            float* B1V = (float*)(scratch + off); off += align_up(4ull * m * r);
-            float* ZU = (float*)(scratch + off); off += align_up(4ull * m * m);
-            float* ZV = (float*)(scratch + off); off += align_up(4ull * n * n);
+            float* B1U = (float*)(rscratch + off); off += align_up(4ull * n * r);
+            float* B1V = (float*)(rscratch + off); off += align_up(4ull * m * r);
+            float* ZU = (float*)(rscratch + off); off += align_up(4ull * m * m);
+            float* ZV = (float*)(rscratch + off); off += align_up(4ull * n * n);
             if (b16) {
                 // bases stored in 16 bits: the refresh works on fp32 copies in
                 // its scratch, widened from U, V before the first pass and
                 // rounded back into them after the last
-                float* XU = (float*)(scratch + off); off += align_up(4ull * m * m);
-                float* XV = (float*)(scratch + off); off += align_up(4ull * n * n);
+                float* XU = (float*)(rscratch + off); off += align_up(4ull * m * m);
+                float* XV = (float*)(rscratch + off); off += align_up(4ull * n * n);
                 for (int side = 0; side < 2; ++side) {
                     const int64_t nel = side ? n * n : m * m;
                     void* b = side ? (void*)x.V : (void*)x.U;
@@ -1239,9 +1252,9 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             if (gram16_eligible(M)) {
                 // bf16 M exactly, the fp32 operand as three exact bf16 pieces:
                 // every Gram product is three bf16 NT products accumulating in fp32
-                uint16_t* Mt = (uint16_t*)(scratch + off); off += align_up(2ull * n * m);
-                uint16_t* Up = (uint16_t*)(scratch + off); off += align_up(6ull * r * m);   // later B1V^T pieces
-                uint16_t* Vp = (uint16_t*)(scratch + off); off += align_up(6ull * r * n);   // later B1U^T pieces
+                uint16_t* Mt = (uint16_t*)(rscratch + off); off += align_up(2ull * n * m);
+                uint16_t* Up = (uint16_t*)(rscratch + off); off += align_up(6ull * r * m);   // later B1V^T pieces
+                uint16_t* Vp = (uint16_t*)(rscratch + off); off += align_up(6ull * r * n);   // later B1U^T pieces
                 const uint16_t* Mb = (const uint16_t*)x.M;
                 split(sj1, t1, x.M, true, n, m, n, Mt, 1);          // M^T (n x m)
                 split(sj1, t1, x.U, false, m, m, r, Up, 3);         // U[:, :r]^T pieces (r x m)
@@ -1282,7 +1295,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             j.X = js.X;
             j.d = (int32_t)js.d;
             j.np = panels((int)js.d);
-            off += qr_assign_scratch(j, scratch + off);
+            off += qr_assign_scratch(j, rscratch + off);
             jobs.push_back(j);
             R.qr.np.push_back(j.np);
             R.qr.d.push_back(j.d);
@@ -1361,7 +1374,7 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 R.ns.push_back(std::move(C));
             }
         }
-        g->scratch_bytes = std::max(g->scratch_bytes, R.ref_bytes);
+        g->refresh_bytes_max = std::max(g->refresh_bytes_max, R.ref_bytes);
         g->rbatches.push_back(std::move(R));
     }
     // state checks: every matrix, input order
@@ -1632,9 +1645,9 @@ opt_status opt_plan(const opt_matrix_desc* descs, int32_t count, const opt_hpara
     return OPT_OK;
 }
 
-opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
-                                    const opt_hparams* hp, uint64_t* bytes) {
-    if (!bytes) return fail(OPT_EINVAL, "bytes is NULL");
+opt_status opt_group_workspace_parts(const opt_matrix_desc* descs, int32_t count,
+                                     const opt_hparams* hp, uint64_t* parts) {
+    if (!parts) return fail(OPT_EINVAL, "parts is NULL");
     opt_status st = check_descs(descs, count, hp, false);
     if (st) return st;
     std::vector<int> ord;
@@ -1663,7 +1676,20 @@ opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
         tmp.mats.push_back(M);
     }
     build(&tmp, plan, (char*)(uintptr_t)kAlign);
-    *bytes = tmp.table_bytes + tmp.bases_bytes + tmp.scratch_bytes;
+    parts[0] = tmp.table_bytes;
+    parts[1] = tmp.bases_bytes;
+    parts[2] = tmp.scratch_bytes;
+    parts[3] = tmp.refresh_bytes_max;
+    return OPT_OK;
+}
+
+opt_status opt_group_workspace_size(const opt_matrix_desc* descs, int32_t count,
+                                    const opt_hparams* hp, uint64_t* bytes) {
+    if (!bytes) return fail(OPT_EINVAL, "bytes is NULL");
+    uint64_t parts[4];
+    const opt_status st = opt_group_workspace_parts(descs, count, hp, parts);
+    if (st) return st;
+    *bytes = parts[0] + std::max(parts[1] + parts[2], parts[3]);
     return OPT_OK;
 }
 
@@ -1945,6 +1971,9 @@ opt_status opt_group_health(opt_group_t g, opt_health* out, void* stream) {
     if ((e = launch_health_clear(dout, (int)g->mats.size(), s))) return hip_fail(e, "health launch");
     if ((e = launch_health_partials(segs, g->health_nseg, g->health_chunks, part, s))) return hip_fail(e, "health launch");
     if ((e = launch_health_final(segs, g->health_nseg, part, dout, s))) return hip_fail(e, "health launch");
+    // the drift's Gram products use the refresh buffers, which overlay the
+    // copies of the bases
+    g->copies_valid = false;
     for (const RefreshBatch& R : g->rbatches) {
         for (const std::vector<GemmLaunch>& stp : R.gram)
             if ((e = run_gemm(g, stp, 1.f, s))) return hip_fail(e, "Gram launch");

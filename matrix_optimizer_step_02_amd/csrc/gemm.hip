@@ -777,24 +777,21 @@ __device__ __forceinline__ void gemm_tile(const GemmProb& p, int tm, int tn, flo
 // memory row (k-major) is loaded four k rows at a time, one element per lane,
 // the lanes along the contiguous index. Rows past the operand, and k past K,
 // are loaded from clamped addresses and zeroed before the split. A bf16
-// operand (B only) is exact in its high piece: its plane is the loaded
-// value, and the three products with its zero pieces are skipped.
+// operand (A or B, not both) is exact in its high piece: its plane is the
+// loaded value, and the three products with its zero pieces are skipped; with
+// k contiguous it is loaded four k values (8 bytes) per lane.
 
 // The X6 products split each value once, at the fill (gemm_x6_kernel);
-// MATOPT_X6_REGISTER_SPLIT selects the in-register split of
-// gemm_grouped_kernel's X6 path instead.
-#ifdef MATOPT_X6_REGISTER_SPLIT
-constexpr bool kX6SplitAtFill = false;
-#else
-constexpr bool kX6SplitAtFill = true;
-#endif
+// MATOPT_X6_REGISTER_SPLIT (kX6SplitAtFill false) selects the in-register
+// split of gemm_grouped_kernel's X6 path instead.
 
-template <class C, bool BBF>
+template <class C, bool ABF, bool BBF>
 struct X6Lds {
     static constexpr int PA = C::BM * 32;   // bytes of one A piece plane
     static constexpr int PB = C::BN * 32;
+    static constexpr int NPA = ABF ? 1 : 3;
     static constexpr int NPB = BBF ? 1 : 3;
-    static constexpr int BUF = 3 * PA + NPB * PB;
+    static constexpr int BUF = NPA * PA + NPB * PB;
     static constexpr int BYTES = 2 * BUF;
 };
 
@@ -832,8 +829,23 @@ struct X6Fill {
                     else
                         v[i][e] = gptr((const float*)base)[(int64_t)ke * ld + rc];
                 }
+            } else if constexpr (BF) {
+                // four bf16 k values (8 bytes) per quad
+                if (vec) {
+                    const int last = (K - 1) & ~3;
+                    const u32x2 x = *gptr((const u32x2*)((const uint16_t*)base + (int64_t)rc * ld + (kq < last ? kq : last)));
+                    v[i][0] = __uint_as_float(x[0] << 16);
+                    v[i][1] = __uint_as_float(x[0] & 0xffff0000u);
+                    v[i][2] = __uint_as_float(x[1] << 16);
+                    v[i][3] = __uint_as_float(x[1] & 0xffff0000u);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int ke = kq + e < K ? kq + e : K - 1;
+                        v[i][e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)rc * ld + ke] << 16);
+                    }
+                }
             } else {
-                static_assert(!BF || KMAJ, "a bf16 operand is read k-major");
                 if (vec) {
                     const int last = (K - 1) & ~3;
                     const f32x4 x = *gptr((const f32x4*)((const float*)base + (int64_t)rc * ld + (kq < last ? kq : last)));
@@ -879,10 +891,19 @@ struct X6Fill {
     }
 };
 
-template <class C, bool AT, bool BT, bool BBF>
+// Slabs loaded into registers ahead of their LDS write: 1 (slab k + 2 is
+// loaded while slab k's MFMAs run) or 2 (slabs k + 2 and k + 3 in flight, two
+// register sets used alternately).
+#ifndef MATOPT_X6_PREFETCH
+#define MATOPT_X6_PREFETCH 1
+#endif
+static_assert(MATOPT_X6_PREFETCH == 1 || MATOPT_X6_PREFETCH == 2, "one or two slabs in registers");
+
+template <class C, bool AT, bool BT, bool ABF, bool BBF>
 __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, float alpha_scale, char* smem) {
-    using L = X6Lds<C, BBF>;
-    constexpr int TM = C::TM, TN = C::TN, NPB = L::NPB;
+    using L = X6Lds<C, ABF, BBF>;
+    constexpr int TM = C::TM, TN = C::TN, NPA = L::NPA, NPB = L::NPB;
+    static_assert(!(ABF && BBF), "a product of two bf16 operands needs no pieces");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave % C::WM, wn = wave / C::WM;
     const int m0 = tm * C::BM, n0 = tn * C::BN;
@@ -898,25 +919,32 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
     }
     // A: M x K (k contiguous) or stored K x M (k-major); B: stored K x N
     // (k-major) or N x K (k contiguous)
-    X6Fill<C::BM, AT, false, C::NT> fa;
-    X6Fill<C::BN, !BT, BBF, C::NT> fb;
-    auto load = [&](int k0) {
+    using FA = X6Fill<C::BM, AT, ABF, C::NT>;
+    using FB = X6Fill<C::BN, !BT, BBF, C::NT>;
+    FA fa0, fa1;
+    FB fb0, fb1;
+    auto load = [&](FA& fa, FB& fb, int k0) {
         fa.load(p.A, p.lda, m0, p.M, k0, p.K, avec);
         fb.load(p.B, p.ldb, n0, p.N, k0, p.K, bvec);
     };
-    auto put = [&](char* buf, int k0) {
+    auto put = [&](const FA& fa, const FB& fb, char* buf, int k0) {
         fa.put(buf, L::PA, m0, p.M, k0, p.K);
-        fb.put(buf + 3 * L::PA, L::PB, n0, p.N, k0, p.K);
+        fb.put(buf + NPA * L::PA, L::PB, n0, p.N, k0, p.K);
     };
-    load(0);
-    put(smem, 0);
-    load(16);   // past K: clamped addresses, zeroed at the put
+    // slabs past K are loaded from clamped addresses and zeroed at their put
+    load(fa0, fb0, 0);
+    put(fa0, fb0, smem, 0);
+    load(fa0, fb0, 16);
+    if constexpr (MATOPT_X6_PREFETCH == 2) load(fa1, fb1, 32);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; ++kt) {
+    // one slab: its MFMAs from LDS buffer kt % 2; after the first row block,
+    // slab kt + 1 from registers (fa, fb) into the other buffer and the load
+    // of slab kt + 1 + MATOPT_X6_PREFETCH into the same registers
+    auto slab = [&](int kt, FA& fa, FB& fb) {
         const char* cur = smem + (kt & 1) * L::BUF;
         char* nxt = smem + ((kt + 1) & 1) * L::BUF;
-        const char* Bp = cur + 3 * L::PA;
+        const char* Bp = cur + NPA * L::PA;
         bf16x8 b[TN][NPB];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -924,19 +952,19 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
 #pragma unroll
             for (int q = 0; q < NPB; ++q) b[j][q] = *(const bf16x8*)(Bp + q * L::PB + off);
         }
-        bf16x8 a[3];
+        bf16x8 a[NPA];
         {
             const int off = x6_off(wm * 32 * TM + l32, h);
 #pragma unroll
-            for (int q = 0; q < 3; ++q) a[q] = *(const bf16x8*)(cur + q * L::PA + off);
+            for (int q = 0; q < NPA; ++q) a[q] = *(const bf16x8*)(cur + q * L::PA + off);
         }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            bf16x8 an[3];
+            bf16x8 an[NPA];
             if (i + 1 < TM) {
                 const int off = x6_off(wm * 32 * TM + (i + 1) * 32 + l32, h);
 #pragma unroll
-                for (int q = 0; q < 3; ++q) an[q] = *(const bf16x8*)(cur + q * L::PA + off);
+                for (int q = 0; q < NPA; ++q) an[q] = *(const bf16x8*)(cur + q * L::PA + off);
             }
             __builtin_amdgcn_sched_barrier(0);
             // smallest piece products first; consecutive MFMAs go to
@@ -946,6 +974,13 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
                 for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[j][0], acc.v[i][j], 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[j][0], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][0], acc.v[i][j], 0, 0, 0);
+            } else if constexpr (ABF) {
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][2], acc.v[i][j], 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][1], acc.v[i][j], 0, 0, 0);
 #pragma unroll
                 for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][0], acc.v[i][j], 0, 0, 0);
             } else {
@@ -965,17 +1000,24 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
             __builtin_amdgcn_sched_barrier(0);
             if (i == 0) {
                 // the next slab's pieces into the other buffer (read by every
-                // wavefront before the previous barrier), then the loads of the
-                // slab after it (past K: clamped, zeroed at their put)
-                put(nxt, (kt + 1) * 16);
-                load((kt + 2) * 16);
+                // wavefront before the previous barrier), then the next load
+                put(fa, fb, nxt, (kt + 1) * 16);
+                load(fa, fb, (kt + 1 + MATOPT_X6_PREFETCH) * 16);
             }
             if (i + 1 < TM) {
 #pragma unroll
-                for (int q = 0; q < 3; ++q) a[q] = an[q];
+                for (int q = 0; q < NPA; ++q) a[q] = an[q];
             }
         }
         __syncthreads();
+    };
+    if constexpr (MATOPT_X6_PREFETCH == 2) {
+        for (int kt = 0; kt < nk; kt += 2) {
+            slab(kt, fa0, fb0);
+            if (kt + 1 < nk) slab(kt + 1, fa1, fb1);
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) slab(kt, fa0, fb0);
     }
     epilogue_blocks<C>(p, m0, n0, wm, wn, lane, acc, p.alpha * alpha_scale, p.beta);
 }
@@ -1099,9 +1141,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 }
 
 // The X6 products: same problem tables and tiles as gemm_grouped_kernel.
-template <class C, bool AT, bool BT, bool BBF>
+template <class C, bool AT, bool BT, bool ABF, bool BBF>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm_x6_kernel(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) char smem[X6Lds<C, BBF>::BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[X6Lds<C, ABF, BBF>::BYTES];
     const int bid = xcd_remap(blockIdx.x, args.total_tiles);
     GemmProb p;
     int t = bid;
@@ -1118,18 +1160,19 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     int tm, tn;
     raster(t, p.tiles_m, p.tiles_n, tm, tn);
-    gemm_tile_x6<C, AT, BT, BBF>(p, tm, tn, args.alpha_scale, smem);
+    gemm_tile_x6<C, AT, BT, ABF, BBF>(p, tm, tn, args.alpha_scale, smem);
 }
 
 template <bool AT, bool BT, bool ABF, bool BBF, bool X6 = false>
 hipError_t launch(int cfg, const GemmArgs& a, hipStream_t s) {
     if (a.total_tiles <= 0) return hipSuccess;
     if constexpr (X6 && kX6SplitAtFill) {
-        static_assert(!ABF, "the X6 products take an fp32 A");
         if (cfg == 1)
-            gemm_x6_kernel<LargeCfg, AT, BT, BBF><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
+            gemm_x6_kernel<LargeCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
         else
-            gemm_x6_kernel<SmallCfg, AT, BT, BBF><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+            gemm_x6_kernel<SmallCfg, AT, BT, ABF, BBF><<<dim3(a.total_tiles), dim3(SmallCfg::NT), 0, s>>>(a);
+    } else if constexpr (X6 && ABF) {
+        return hipErrorInvalidValue;   // the in-register split takes an fp32 A
     } else {
         if (cfg == 1)
             gemm_grouped_kernel<LargeCfg, AT, BT, ABF, BBF, X6><<<dim3(a.total_tiles), dim3(LargeCfg::NT), 0, s>>>(a);
@@ -1202,6 +1245,7 @@ static hipError_t dispatch(int variant, int cfg, const GemmArgs& a, hipStream_t 
         case GV_X6 | 1: return launch<true, false, false, false, true>(cfg, a, s);
         case GV_X6 | 2: return launch<false, true, false, false, true>(cfg, a, s);
         case GV_X6 | 8: return launch<false, false, false, true, true>(cfg, a, s);
+        case GV_X6 | 4: return launch<false, false, true, false, true>(cfg, a, s);
         default: return hipErrorInvalidValue;
     }
 }

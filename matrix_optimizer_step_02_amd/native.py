@@ -32,7 +32,7 @@ EXPORTED = (
     "opt_group_set_timing", "opt_group_read_timing", "opt_group_destroy", "opt_last_error",
     "opt_gemm", "opt_gemm_x6", "opt_gemm_bf16", "opt_orthonormalize_workspace_size", "opt_orthonormalize",
     "opt_partition_dp", "opt_plan_host_ranks", "opt_group_health", "opt_group_reorthonormalize",
-    "opt_orthonormalize_static", "opt_group_read_group_timing",
+    "opt_orthonormalize_static", "opt_group_read_group_timing", "opt_group_workspace_parts",
 )
 
 
@@ -83,6 +83,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
     D, H = C.POINTER(opt_matrix_desc), C.POINTER(opt_hparams)
     sig = {
         "opt_group_workspace_size": ([D, i32, H, C.POINTER(u64)], i32),
+        "opt_group_workspace_parts": ([D, i32, H, C.POINTER(u64)], i32),
         "opt_group_create": ([D, i32, H, vp, u64, vp, C.POINTER(vp)], i32),
         "opt_group_step": ([vp, vp], i32),
         "opt_group_refresh_basis": ([vp, i32, vp], i32),
@@ -135,6 +136,15 @@ def opt_group_workspace_size(descs, hp: opt_hparams) -> int:
     out = C.c_uint64(0)
     _check(load().opt_group_workspace_size(arr, n, C.byref(hp), C.byref(out)))
     return out.value
+
+
+def opt_group_workspace_parts(descs, hp: opt_hparams) -> dict:
+    """The workspace's parts in bytes: work lists, copies of the bases, step
+    scratch and the largest refresh batch (which overlays the two before)."""
+    arr, n = _descs(descs)
+    out = (C.c_uint64 * 4)()
+    _check(load().opt_group_workspace_parts(arr, n, C.byref(hp), out))
+    return dict(zip(("tables", "copies", "scratch", "refresh"), (int(x) for x in out)))
 
 
 def opt_group_create(descs, hp: opt_hparams, workspace_ptr: int, workspace_bytes: int,

@@ -141,44 +141,72 @@ def test_muon_flag_checks(N):
     assert need < 1 << 20
 
 
+def _parts(N, d, h):
+    p = N.opt_group_workspace_parts(d, h)
+    assert N.opt_group_workspace_size(d, h) == p["tables"] + max(p["copies"] + p["scratch"], p["refresh"])
+    return p
+
+
 def test_workspace_holds_the_copies_of_the_bases(N):
     """The fp32 rotations keep an fp32 U^T (4 m^2 bytes, 256-byte aligned)
     per matrix; the bf16 variant instead keeps bf16 U, U^T, V, V^T (rows
     padded to multiples of 8 elements) and a larger scratch; Muon keeps
     neither. The carried rotated momentum adds the work lists of its two
-    kinds of step (its m~ is caller-owned)."""
+    kinds of step (its m~ is caller-owned). The size is the tables plus the
+    larger of (copies + scratch) and the largest refresh batch."""
     shapes = [(130, 67), (64, 64), (24, 40)]
     d = descs(N, shapes)
-    base = N.opt_group_workspace_size(d, hp(N))
-    var = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
-    rm = N.opt_group_workspace_size(d, hp(N, flags=N.OPT_FLAG_ROTATED_MOMENTUM))
+    base = _parts(N, d, hp(N))
+    var = _parts(N, d, hp(N, flags=N.OPT_FLAG_BF16_ROTATION))
+    rm = _parts(N, d, hp(N, flags=N.OPT_FLAG_ROTATED_MOMENTUM))
+    mu = _parts(N, d, hp(N, flags=N.OPT_FLAG_MUON, ns_iters=2))
     r8 = lambda x: (x + 7) // 8 * 8
     a256 = lambda x: (x + 255) // 256 * 256
     ut = sum(a256(4 * m * m) for m, _ in shapes)
-    bases = sum(2 * 2 * m * r8(m) + 2 * 2 * n * r8(n) for m, n in shapes)
-    assert base > ut and base < rm < base + 64 * 1024     # the carried momentum adds only work lists
-    assert var >= base - ut + bases
-    assert var < base - ut + bases + 64 * 1024 + sum(4 * m * n for m, n in shapes)
+    bases = sum(a256(2 * m * r8(m)) * 2 + a256(2 * n * r8(n)) * 2 for m, n in shapes)
+    assert base["copies"] == ut and rm["copies"] == ut
+    assert var["copies"] == bases
+    assert mu["copies"] == 0 and mu["refresh"] == 0
+    assert base["scratch"] >= sum(16 * m * n for m, n in shapes[:1])
+    assert var["scratch"] > base["scratch"]
+    assert rm["scratch"] == base["scratch"] and base["tables"] < rm["tables"] < base["tables"] + 64 * 1024
+    # the refresh buffers do not depend on how the step rotates
+    assert base["refresh"] == rm["refresh"] == var["refresh"] > 0
+
+
+def test_refresh_buffers_overlay_the_copies(N):
+    """The default refresh cap is the larger of 4 GiB and the copies plus the
+    scratch, so a refresh batch never makes the workspace larger than that
+    unless one matrix alone needs more; an explicit cap splits the batches
+    (a matrix above it forms a batch alone)."""
+    shapes = [(4096, 4096), (4096, 1024), (1024, 4096), (2048, 2048)]
+    d = descs(N, shapes, dtype=N.OPT_BF16)
+    p = _parts(N, d, hp(N))
+    assert p["refresh"] <= max(4 << 30, p["copies"] + p["scratch"])
+    one = _parts(N, d, hp(N, refresh_capacity_bytes=1))
+    assert one["refresh"] < p["refresh"]
+    assert (one["tables"], one["copies"], one["scratch"]) != (0, 0, 0)
+    assert one["copies"] == p["copies"] and one["scratch"] == p["scratch"]
 
 
 def test_workspace_holds_the_pieces_of_the_momentum_bases(N):
     """A bf16 M with both sides multiples of 8 gets the three bf16 pieces of
     U^T (m > n) or V^T (m <= n), 6 d^2 bytes (256-byte aligned), beside the
-    fp32 U^T copy (and a few work-list entries); fp32 M, ragged sides, and
-    the flag that keeps the rotations on fp32 MFMAs add nothing."""
+    fp32 U^T copy; fp32 M, ragged sides, and the flag that keeps the
+    rotations on fp32 MFMAs add nothing."""
     shapes = [(200, 72), (72, 264), (136, 136), (130, 67), (8, 8)]
     a256 = lambda x: (x + 255) // 256 * 256
     bf = descs(N, shapes, dtype=N.OPT_BF16)
-    pieced = N.opt_group_workspace_size(bf, hp(N))
-    plain = N.opt_group_workspace_size(bf, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
+    pieced = _parts(N, bf, hp(N))
+    plain = _parts(N, bf, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
     f32 = descs(N, shapes)
     pieces = sum(a256(6 * max(m, n) ** 2) for m, n in shapes if m % 8 == 0 and n % 8 == 0)
-    assert 0 <= pieced - plain - pieces < 16 * 1024    # plus the work lists of the new launches
-    assert N.opt_group_workspace_size(f32, hp(N)) == \
-        N.opt_group_workspace_size(f32, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
+    assert pieced["copies"] - plain["copies"] == pieces
+    assert 0 <= pieced["tables"] - plain["tables"] < 16 * 1024    # the work lists of the new launches
+    assert N.opt_group_workspace_parts(f32, hp(N)) == N.opt_group_workspace_parts(f32, hp(N, flags=N.OPT_FLAG_FP32_MFMA))
     for other in (N.OPT_FLAG_ROTATED_MOMENTUM, N.OPT_FLAG_BF16_ROTATION):
-        assert N.opt_group_workspace_size(bf, hp(N, flags=other)) == \
-            N.opt_group_workspace_size(bf, hp(N, flags=other | N.OPT_FLAG_FP32_MFMA))
+        assert N.opt_group_workspace_parts(bf, hp(N, flags=other)) == \
+            N.opt_group_workspace_parts(bf, hp(N, flags=other | N.OPT_FLAG_FP32_MFMA))
 
 
 def test_rejects_bad_shapes_and_dtypes(N):
