@@ -171,11 +171,12 @@ typedef struct {
     int32_t power_iters;      /* orthogonal-iteration passes per refresh, >= 1 */
     uint64_t capacity_bytes;  /* micro-group cap on sum(4 m n); 0 selects 1 << 29 (512 MiB) */
     uint64_t refresh_capacity_bytes; /* cap on the refresh scratch of one refresh batch (the
-                                        d x d QR inputs and their scratch); 0 selects the larger
-                                        of 4 GiB and the bytes of the copies of the bases and
-                                        the step scratch, which the refresh buffers overlay (so
-                                        the refresh adds no workspace beyond them). A matrix
-                                        larger than the cap forms a batch alone. */
+                                        d x d QR inputs and their scratch); 0 selects the
+                                        largest of 4 GiB, the bytes of the copies of the bases
+                                        and the step scratch (which the refresh buffers
+                                        overlay) and the bytes of the group's tensors (W, G, M,
+                                        v, U, V, Mt). A matrix larger than the cap forms a
+                                        batch alone. */
     uint32_t flags;           /* OPT_FLAG_* bits; others must be 0 */
     int32_t ns_iters;         /* Newton-Schulz iterations of OPT_FLAG_MUON, >= 1 there; else ignored */
 } opt_hparams;

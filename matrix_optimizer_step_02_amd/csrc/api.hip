@@ -286,11 +286,29 @@ uint64_t capacity_of(const opt_hparams* hp) {
     return hp->capacity_bytes ? hp->capacity_bytes : (1ull << 29);
 }
 
-// The refresh cap: the caller's, else the larger of 4 GiB and `overlay`, the
+// The refresh cap: the caller's, else the largest of 4 GiB, `overlay` (the
 // bytes of the copies of the bases and the step's scratch, which a refresh
-// batch's buffers overlay (the copies are rebuilt after every refresh).
-uint64_t refresh_capacity_of(const opt_hparams* hp, uint64_t overlay) {
-    return hp->refresh_capacity_bytes ? hp->refresh_capacity_bytes : std::max(4ull << 30, (unsigned long long)overlay);
+// batch's buffers overlay: the copies are rebuilt after every refresh) and
+// `state` (the bytes of the caller's tensors), so that by default the
+// workspace is no larger than the larger of the state it serves and the
+// copies and scratch of a step, unless one matrix's refresh alone is.
+uint64_t refresh_capacity_of(const opt_hparams* hp, uint64_t overlay, uint64_t state) {
+    if (hp->refresh_capacity_bytes) return hp->refresh_capacity_bytes;
+    return std::max<uint64_t>(std::max<uint64_t>(4ull << 30, overlay), state);
+}
+
+// Bytes of the caller-owned tensors of a group: W, G, v (fp32), M, U, V, and
+// Mt with the carried rotated momentum.
+uint64_t state_bytes(const opt_group_s* g) {
+    uint64_t b = 0;
+    const bool b16 = g->hp.flags & OPT_FLAG_BF16_BASES, muon = g->hp.flags & OPT_FLAG_MUON;
+    const bool rmf = g->hp.flags & OPT_FLAG_ROTATED_MOMENTUM;
+    for (const Mat& M : g->mats) {
+        const uint64_t m = (uint64_t)M.d.m, n = (uint64_t)M.d.n, mn = m * n;
+        b += mn * (8 + (muon ? 0 : 4) + (M.bf16 ? 2 : 4) + (rmf ? 4 : 0));
+        if (!muon) b += (b16 ? 2 : 4) * (m * m + n * n);
+    }
+    return b;
 }
 
 struct Span {
@@ -783,7 +801,7 @@ uint64_t refresh_bytes(int64_t m, int64_t n) {
 // matrix above the cap forms a batch of its own).
 std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vector<std::vector<int>>& plan,
                                            uint64_t overlay) {
-    const uint64_t cap = refresh_capacity_of(&g->hp, overlay);
+    const uint64_t cap = refresh_capacity_of(&g->hp, overlay, state_bytes(g));
     std::vector<std::vector<int>> out;
     uint64_t used = 0;
     for (const std::vector<int>& members : plan)

@@ -799,11 +799,21 @@ __device__ __forceinline__ int x6_off(int r, int half) { return r * 32 + 16 * (h
 
 // One operand's slab in registers: R rows of 16 k values as quads of four k
 // values, Q quads per thread.
+//
+// Addresses: at the start of a tile each quad's byte offset from the
+// operand's slab-0 origin is computed once (its row clamped into the
+// operand), 32-bit since an operand of the step is at most 2^30 bytes (a
+// larger one takes the clamped path throughout). A slab whose 16 k values
+// all lie inside K then loads from the slab's origin, a uniform address,
+// plus those offsets; only a last, partial slab recomputes clamped
+// addresses.
 template <int R, bool KMAJ, bool BF, int NT>
 struct X6Fill {
     static constexpr int Q = R * 4 / NT;
+    static constexpr int ES = BF ? 2 : 4;   // element bytes
     static_assert(Q * NT == R * 4, "tile rows not divisible among the threads");
     float v[Q][4];
+    uint32_t off[Q];
 
     // quad i of this thread: row r (0..R-1) of the tile, quad q (0..3) of the slab
     __device__ __forceinline__ static void pos(int i, int& r, int& q) {
@@ -812,8 +822,61 @@ struct X6Fill {
         else      { r = f >> 2; q = f & 3; }
     }
 
-    // base: the operand; rows_v: valid rows (m or n), K; ld: leading dimension
-    __device__ __forceinline__ void load(const void* base, int64_t ld, int r0, int rows_v, int k0, int K, bool vec) {
+    __device__ __forceinline__ void init(int64_t ld, int r0, int rows_v) {
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            int r, q;
+            pos(i, r, q);
+            const int row = r0 + r;
+            const int rc = row < rows_v ? row : rows_v - 1;
+            off[i] = KMAJ ? (uint32_t)(((int64_t)(4 * q) * ld + rc) * ES) : (uint32_t)(((int64_t)rc * ld + 4 * q) * ES);
+        }
+    }
+
+    // A slab inside K: origin = the operand's element (k0, row 0) (k-major)
+    // or (row 0, k0); `vec`: rows of 16-byte (fp32) / 8-byte (bf16) aligned
+    // quads.
+    __device__ __forceinline__ void load_inner(const char* origin, int64_t ld, bool vec) {
+        const gmem<const char> o = gptr(origin);
+#pragma unroll
+        for (int i = 0; i < Q; ++i) {
+            if (KMAJ) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const gmem<const char> pe = o + (int64_t)e * ld * ES;
+                    if constexpr (BF)
+                        v[i][e] = __uint_as_float((uint32_t)*(const gmem<const uint16_t>)(pe + off[i]) << 16);
+                    else
+                        v[i][e] = *(const gmem<const float>)(pe + off[i]);
+                }
+            } else if (vec) {
+                if constexpr (BF) {
+                    const u32x2 x = *(const gmem<const u32x2>)(o + off[i]);
+                    v[i][0] = __uint_as_float(x[0] << 16);
+                    v[i][1] = __uint_as_float(x[0] & 0xffff0000u);
+                    v[i][2] = __uint_as_float(x[1] << 16);
+                    v[i][3] = __uint_as_float(x[1] & 0xffff0000u);
+                } else {
+                    const f32x4 x = *(const gmem<const f32x4>)(o + off[i]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[i][e] = x[e];
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (BF)
+                        v[i][e] = __uint_as_float((uint32_t)*(const gmem<const uint16_t>)(o + off[i] + e * ES) << 16);
+                    else
+                        v[i][e] = *(const gmem<const float>)(o + off[i] + e * ES);
+                }
+            }
+        }
+    }
+
+    // Any slab, addresses clamped into the operand. base: the operand;
+    // rows_v: valid rows (m or n), K; ld: leading dimension.
+    __device__ __forceinline__ void load_clamped(const void* base, int64_t ld, int r0, int rows_v, int k0, int K,
+                                                 bool vec) {
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
             int r, q;
@@ -862,17 +925,23 @@ struct X6Fill {
         }
     }
 
-    // Zero what lies outside the operand, split, and write the planes
-    // (planes p at `lds` + p * plane_bytes).
-    __device__ __forceinline__ void put(char* lds, int plane_bytes, int r0, int rows_v, int k0, int K) const {
+    // Split and write the planes (plane p at `lds` + p * plane_bytes); with
+    // `mask`, first zero what lies outside the operand (rows past rows_v, k
+    // past K), which the clamped loads read as copies of the last row or k.
+    __device__ __forceinline__ void put(char* lds, int plane_bytes, bool mask, int r0, int rows_v, int k0,
+                                        int K) const {
 #pragma unroll
         for (int i = 0; i < Q; ++i) {
             int r, q;
             pos(i, r, q);
-            const bool row_ok = r0 + r < rows_v;
             float x[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = (row_ok && k0 + 4 * q + e < K) ? v[i][e] : 0.f;
+            for (int e = 0; e < 4; ++e) x[e] = v[i][e];
+            if (mask) {
+                const bool row_ok = r0 + r < rows_v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = (row_ok && k0 + 4 * q + e < K) ? x[e] : 0.f;
+            }
             const int off = x6_off(r, q >> 1) + 8 * (q & 1);
             if constexpr (BF) {
                 // exact bf16 values: the high halves of the widened words
@@ -923,13 +992,34 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
     using FB = X6Fill<C::BN, !BT, BBF, C::NT>;
     FA fa0, fa1;
     FB fb0, fb1;
+    // the fast path: both operands' bytes addressable with 32-bit offsets
+    const int64_t a_span = (int64_t)(AT ? p.K : p.M) * p.lda * FA::ES;
+    const int64_t b_span = (int64_t)(BT ? p.N : p.K) * p.ldb * FB::ES;
+    const bool offs = a_span < (int64_t(1) << 32) && b_span < (int64_t(1) << 32);
+    if (offs) {
+        fa0.init(p.lda, m0, p.M);
+        fb0.init(p.ldb, n0, p.N);
+        if constexpr (MATOPT_X6_PREFETCH == 2) {
+#pragma unroll
+            for (int i = 0; i < FA::Q; ++i) fa1.off[i] = fa0.off[i];
+#pragma unroll
+            for (int i = 0; i < FB::Q; ++i) fb1.off[i] = fb0.off[i];
+        }
+    }
+    const bool rows_partial = m0 + C::BM > p.M || n0 + C::BN > p.N;
     auto load = [&](FA& fa, FB& fb, int k0) {
-        fa.load(p.A, p.lda, m0, p.M, k0, p.K, avec);
-        fb.load(p.B, p.ldb, n0, p.N, k0, p.K, bvec);
+        if (offs && k0 + 16 <= p.K) {
+            fa.load_inner((const char*)p.A + (int64_t)k0 * (AT ? p.lda : 1) * FA::ES, p.lda, avec);
+            fb.load_inner((const char*)p.B + (int64_t)k0 * (BT ? 1 : p.ldb) * FB::ES, p.ldb, bvec);
+        } else {
+            fa.load_clamped(p.A, p.lda, m0, p.M, k0, p.K, avec);
+            fb.load_clamped(p.B, p.ldb, n0, p.N, k0, p.K, bvec);
+        }
     };
     auto put = [&](const FA& fa, const FB& fb, char* buf, int k0) {
-        fa.put(buf, L::PA, m0, p.M, k0, p.K);
-        fb.put(buf + NPA * L::PA, L::PB, n0, p.N, k0, p.K);
+        const bool mask = rows_partial || k0 + 16 > p.K;
+        fa.put(buf, L::PA, mask, m0, p.M, k0, p.K);
+        fb.put(buf + NPA * L::PA, L::PB, mask, n0, p.N, k0, p.K);
     };
     // slabs past K are loaded from clamped addresses and zeroed at their put
     load(fa0, fb0, 0);

@@ -1,8 +1,10 @@
 """Determinism and checkpoint/resume of the whole step on the device.
 
-Every reduction in the library runs in a fixed order (no atomics in any
-product or QR kernel), so two runs over the same inputs must end in bitwise
-equal state. All state is caller-owned apart from the step counter, so a run
+Every reduction in the library runs in a fixed order (no atomic
+accumulation: the tall-panel QR kernel uses atomics only for its grid
+barrier and to pass partial sums between workgroups, which it adds in a fixed
+slice order), so two runs over the same inputs must end in bitwise equal
+state. All state is caller-owned apart from the step counter, so a run
 that is checkpointed at t = 5 (W, M, v, U, V copied out and the group
 destroyed), restored into a new group and told t = 5 (opt_group_set_step)
 must continue bitwise as the uninterrupted run does, through the refresh at
