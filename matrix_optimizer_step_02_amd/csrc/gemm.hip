@@ -1017,7 +1017,9 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
         }
     };
     auto put = [&](const FA& fa, const FB& fb, char* buf, int k0) {
-        const bool mask = rows_partial || k0 + 16 > p.K;
+        // interior slabs skip the zeroing, except with a bf16 operand, where
+        // the branch made the compiler keep more values live and spill
+        const bool mask = ABF || BBF || rows_partial || k0 + 16 > p.K;
         fa.put(buf, L::PA, mask, m0, p.M, k0, p.K);
         fb.put(buf + NPA * L::PA, L::PB, mask, n0, p.N, k0, p.K);
     };
