@@ -131,6 +131,7 @@ struct PanelCtx {
     int64_t ld;
     int L;        // rows of the panel
     int jb;       // columns of the panel
+    bool vec;     // ld % 4 == 0 and Z 16-byte aligned: groups of 4 columns from a multiple of 4 are 16-byte aligned
 };
 
 // Reflector entry Y[i][c] (panel-relative): 0 above the diagonal, 1 on it.
@@ -138,6 +139,36 @@ __device__ __forceinline__ float yval(const PanelCtx& c, int i, int col) {
     if (i < col) return 0.f;
     if (i == col) return 1.f;
     return c.A[(int64_t)i * c.ld + col];
+}
+
+// Row i's entries at panel columns col0 .. col0 + N - 1 (N a multiple of 4,
+// col0 a multiple of 4, all inside the panel, c.vec): N / 4 16-byte loads.
+// A thread owns whole rows, so its N values are contiguous; N separate
+// 4-byte loads would make every wavefront instruction touch 64 cache lines
+// for 4 bytes each.
+template <int N>
+__device__ __forceinline__ void load_row(const PanelCtx& c, int i, int col0, float (&x)[N]) {
+    const gmem<const f32x4> p = (const gmem<const f32x4>)(c.A + (int64_t)i * c.ld + col0);
+#pragma unroll
+    for (int g = 0; g < N / 4; ++g) {
+        const f32x4 v = p[g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[4 * g + e] = v[e];
+    }
+}
+
+// Reflector entries Y[i][y0 + l], l < N (as yval), for a block of N
+// columns inside the panel.
+template <int N>
+__device__ __forceinline__ void load_y(const PanelCtx& c, int i, int y0, float (&y)[N]) {
+    if (c.vec) {
+        load_row<N>(c, i, y0, y);
+#pragma unroll
+        for (int l = 0; l < N; ++l) y[l] = (i < y0 + l) ? 0.f : (i == y0 + l) ? 1.f : y[l];
+    } else {
+#pragma unroll
+        for (int l = 0; l < N; ++l) y[l] = yval(c, i, y0 + l);
+    }
 }
 
 template <int R, int SB>
@@ -251,6 +282,8 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
     c.A = gptr(Jb.Z + (int64_t)k * c.ld + k);
     c.L = Jb.d - k;
     c.jb = min(PB, Jb.d - k);
+    c.vec = (Jb.d % 4) == 0 && ((uintptr_t)Jb.Z & 15u) == 0;
+    static_assert(SB % 4 == 0, "sub-panels of whole 16-byte groups");
     const int tid = threadIdx.x;
     for (int e = tid; e < PB * (PB + 1); e += PT) (&sh.Tq[0][0])[e] = 0.f;
     int slot = 0;
@@ -259,17 +292,30 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
     for (int s = 0; s * SB < c.jb; ++s) {
         sp.c0 = s * SB;
         sp.sbw = min(SB, c.jb - sp.c0);
+        const bool full = c.vec && sp.sbw == SB;   // whole 16-byte groups inside the panel
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const int i = tid + PT * r;
+            if (full) {
+                if (i < c.L) load_row<SB>(c, i, sp.c0, sp.a[r]);
+                else {
 #pragma unroll
-            for (int q = 0; q < SB; ++q)
-                sp.a[r][q] = (i < c.L && q < sp.sbw) ? c.A[(int64_t)i * c.ld + sp.c0 + q] : 0.f;
+                    for (int q = 0; q < SB; ++q) sp.a[r][q] = 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < SB; ++q)
+                    sp.a[r][q] = (i < c.L && q < sp.sbw) ? c.A[(int64_t)i * c.ld + sp.c0 + q] : 0.f;
+            }
         }
         // left-looking: apply the earlier sub-panels' reflector blocks in order
+        // (with few rows per thread the block's reflector rows stay in
+        // registers between its two passes instead of being loaded twice)
+        constexpr bool kCacheY = R * SB <= 32;
         for (int qb = 0; qb < s; ++qb) {
             const int y0 = qb * SB;
             float part[SB * SB];
+            float yc[kCacheY ? R : 1][SB];
 #pragma unroll
             for (int e = 0; e < SB * SB; ++e) part[e] = 0.f;
 #pragma unroll
@@ -277,8 +323,11 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
                 const int i = tid + PT * r;
                 if (i < c.L && i >= y0) {
                     float y[SB];
+                    load_y<SB>(c, i, y0, y);
+                    if constexpr (kCacheY) {
 #pragma unroll
-                    for (int l = 0; l < SB; ++l) y[l] = yval(c, i, y0 + l);
+                        for (int l = 0; l < SB; ++l) yc[r][l] = y[l];
+                    }
 #pragma unroll
                     for (int l = 0; l < SB; ++l)
 #pragma unroll
@@ -301,8 +350,12 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
                 const int i = tid + PT * r;
                 if (i < c.L && i >= y0) {
                     float y[SB];
+                    if constexpr (kCacheY) {
 #pragma unroll
-                    for (int l = 0; l < SB; ++l) y[l] = yval(c, i, y0 + l);
+                        for (int l = 0; l < SB; ++l) y[l] = yc[r][l];
+                    } else {
+                        load_y<SB>(c, i, y0, y);
+                    }
 #pragma unroll
                     for (int q = 0; q < SB; ++q) {
                         float acc = 0.f;
@@ -333,9 +386,16 @@ __global__ __launch_bounds__(PT) void qr_panel_kernel(const QrJob* __restrict__ 
         for (int r = 0; r < R; ++r) {
             const int i = tid + PT * r;
             if (i < c.L) {
+                if (full) {
+                    const gmem<f32x4> o = (gmem<f32x4>)(c.A + (int64_t)i * c.ld + sp.c0);
 #pragma unroll
-                for (int q = 0; q < SB; ++q)
-                    if (q < sp.sbw) c.A[(int64_t)i * c.ld + sp.c0 + q] = sp.a[r][q];
+                    for (int g = 0; g < SB / 4; ++g)
+                        o[g] = (f32x4){sp.a[r][4 * g], sp.a[r][4 * g + 1], sp.a[r][4 * g + 2], sp.a[r][4 * g + 3]};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < SB; ++q)
+                        if (q < sp.sbw) c.A[(int64_t)i * c.ld + sp.c0 + q] = sp.a[r][q];
+                }
             }
         }
         __syncthreads();   // stored reflectors visible to the next sub-panel's loads; T_q complete
@@ -499,7 +559,7 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
 
 // W2[:, j] = T^T (sum_s W_s[:, j]).
 __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, QrClasses C, int p) {
-    __shared__ float Ts[PB][PB + 1];
+    __shared__ __attribute__((aligned(16))) float Ts[PB][PB];
     int job, local;
     if (!qr_locate(C, QG_REDUCE, p, blockIdx.x, job, local)) return;
     const QrJob Jb = jobs[job];
@@ -521,14 +581,21 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
 #pragma unroll
         for (int c = 0; c < PB; ++c) w[c] += part[(int64_t)c * d];
     }
-    // c stays a rolled loop: unrolled, the compiler hoists all PB*PB LDS reads
-    // of T ahead of the products and spills.
+    // Four output rows c at a time: every thread reads the same T entries
+    // (an LDS broadcast), four of them per 16-byte read. The c loop stays
+    // rolled: unrolled, the compiler hoists all the LDS reads of T ahead of
+    // the products and spills.
 #pragma unroll 1
-    for (int c = 0; c < PB; ++c) {
-        float acc = 0.f;
+    for (int c = 0; c < PB; c += 4) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int l = 0; l < PB; ++l) acc += Ts[l][c] * w[l];
-        gptr(Jb.W2)[(int64_t)c * d + j] = acc;
+        for (int l = 0; l < PB; ++l) {
+            const f32x4 t = *(const f32x4*)&Ts[l][c];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += t[e] * w[l];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gptr(Jb.W2)[(int64_t)(c + e) * d + j] = acc[e];
     }
 }
 
