@@ -53,7 +53,7 @@ inline bool gemm_x6_available(int variant) {
 
 // Two tile configurations of the grouped GEMM (rotations, Gram products,
 // opt_gemm): 128x128 outputs per workgroup of 2x2 wavefronts (64x64 each),
-// and 256x128 per workgroup of 2x2 wavefronts (128x64 each), which reuses
+// and 256x256 per workgroup of 2x4 wavefronts (128x64 each), which reuses
 // every staged operand more but needs many tiles to fill the GPU. A launch
 // takes the large tiles when it has at least kGemmLargeMinTiles of them.
 struct GemmTileCfg {
@@ -61,7 +61,7 @@ struct GemmTileCfg {
 };
 #ifndef MATOPT_LARGE_BM
 #define MATOPT_LARGE_BM 256
-#define MATOPT_LARGE_BN 128
+#define MATOPT_LARGE_BN 256
 #endif
 constexpr GemmTileCfg kGemmCfgs[2] = {{128, 128}, {MATOPT_LARGE_BM, MATOPT_LARGE_BN}};
 constexpr int kGemmLargeMinTiles = 512;

@@ -87,13 +87,14 @@ struct Cfg {
 };
 
 // Configurations of the grouped launches (rotations, Gram products, opt_gemm).
-// The large tile: 256 x 128 outputs per workgroup of 2 x 2 wavefronts (128 x
-// 64 each) with 16-deep slabs: 48 KiB of LDS and at most 256 registers per
-// lane, so two workgroups share a CU and one's barrier or fill wait is
-// covered by the other's MFMAs (measured 1 % faster on the rotation phases
-// than 256 x 256 tiles of 8 wavefronts with 32-deep slabs, one per CU).
+// The large tile: 256 x 256 outputs per workgroup of 2 x 4 wavefronts (128 x
+// 64 each) with 16-deep slabs, two wavefronts per SIMD. With the fp32
+// products on bf16 MFMAs (96 KiB of LDS, one workgroup per CU) each operand
+// value that a workgroup loads and splits feeds 256 outputs instead of 128 or
+// 256 on a 256 x 128 tile of 4 wavefronts: 7 % less time on the rotation
+// phases (the fill's loads and split per MFMA drop by a quarter).
 #ifndef MATOPT_LARGE_CFG
-#define MATOPT_LARGE_CFG 2, 2, 4, 2, 16
+#define MATOPT_LARGE_CFG 2, 4, 4, 2, 16
 #endif
 using SmallCfg = Cfg<2, 2, 2, 2>;
 using LargeCfg = Cfg<MATOPT_LARGE_CFG>;
@@ -797,10 +798,17 @@ struct X6Lds {
 
 __device__ __forceinline__ int x6_off(int r, int half) { return r * 32 + 16 * (half ^ ((r >> 3) & 1)); }
 
-// One operand's slab in registers: R rows of 16 k values as quads of four k
-// values, Q quads per thread.
+// One operand's slab in registers: R rows of 16 k values as halves of eight
+// k values, H halves per thread. A thread's half of a row is one 16-byte
+// write per piece plane (the half's slot in LDS, x6_off(r, h)). An operand
+// whose k index is the memory row (k-major) gives consecutive lanes
+// consecutive rows, so that each of its eight loads is coalesced across the
+// wavefront; the 16-byte writes then go to rows 32 bytes apart, which with
+// the half swizzle cover all banks once per 16 lanes (8-byte writes at that
+// stride had four-way bank conflicts). A k-contiguous operand gives each row
+// to two consecutive lanes (16 or 32 contiguous bytes per lane).
 //
-// Addresses: at the start of a tile each quad's byte offset from the
+// Addresses: at the start of a tile each half's byte offset from the
 // operand's slab-0 origin is computed once (its row clamped into the
 // operand), 32-bit since an operand of the step is at most 2^30 bytes (a
 // larger one takes the clamped path throughout). A slab whose 16 k values
@@ -809,40 +817,40 @@ __device__ __forceinline__ int x6_off(int r, int half) { return r * 32 + 16 * (h
 // addresses.
 template <int R, bool KMAJ, bool BF, int NT>
 struct X6Fill {
-    static constexpr int Q = R * 4 / NT;
+    static constexpr int H = R * 2 / NT;
     static constexpr int ES = BF ? 2 : 4;   // element bytes
-    static_assert(Q * NT == R * 4, "tile rows not divisible among the threads");
-    float v[Q][4];
-    uint32_t off[Q];
+    static_assert(H * NT == R * 2, "tile rows not divisible among the threads");
+    float v[H][8];
+    uint32_t off[H];
 
-    // quad i of this thread: row r (0..R-1) of the tile, quad q (0..3) of the slab
-    __device__ __forceinline__ static void pos(int i, int& r, int& q) {
+    // half i of this thread: row r (0..R-1) of the tile, half o (0, 1) of the slab
+    __device__ __forceinline__ static void pos(int i, int& r, int& o) {
         const int f = (int)threadIdx.x + NT * i;
-        if (KMAJ) { r = f % R; q = f / R; }
-        else      { r = f >> 2; q = f & 3; }
+        if (KMAJ) { r = f % R; o = f / R; }
+        else      { r = f >> 1; o = f & 1; }
     }
 
     __device__ __forceinline__ void init(int64_t ld, int r0, int rows_v) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-            int r, q;
-            pos(i, r, q);
+        for (int i = 0; i < H; ++i) {
+            int r, o;
+            pos(i, r, o);
             const int row = r0 + r;
             const int rc = row < rows_v ? row : rows_v - 1;
-            off[i] = KMAJ ? (uint32_t)(((int64_t)(4 * q) * ld + rc) * ES) : (uint32_t)(((int64_t)rc * ld + 4 * q) * ES);
+            off[i] = KMAJ ? (uint32_t)(((int64_t)(8 * o) * ld + rc) * ES) : (uint32_t)(((int64_t)rc * ld + 8 * o) * ES);
         }
     }
 
     // A slab inside K: origin = the operand's element (k0, row 0) (k-major)
-    // or (row 0, k0); `vec`: rows of 16-byte (fp32) / 8-byte (bf16) aligned
-    // quads.
+    // or (row 0, k0); `vec`: 16-byte (fp32) / 8-byte (bf16) aligned groups
+    // of four k values.
     __device__ __forceinline__ void load_inner(const char* origin, int64_t ld, bool vec) {
         const gmem<const char> o = gptr(origin);
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
+        for (int i = 0; i < H; ++i) {
             if (KMAJ) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < 8; ++e) {
                     const gmem<const char> pe = o + (int64_t)e * ld * ES;
                     if constexpr (BF)
                         v[i][e] = __uint_as_float((uint32_t)*(const gmem<const uint16_t>)(pe + off[i]) << 16);
@@ -850,20 +858,23 @@ struct X6Fill {
                         v[i][e] = *(const gmem<const float>)(pe + off[i]);
                 }
             } else if (vec) {
-                if constexpr (BF) {
-                    const u32x2 x = *(const gmem<const u32x2>)(o + off[i]);
-                    v[i][0] = __uint_as_float(x[0] << 16);
-                    v[i][1] = __uint_as_float(x[0] & 0xffff0000u);
-                    v[i][2] = __uint_as_float(x[1] << 16);
-                    v[i][3] = __uint_as_float(x[1] & 0xffff0000u);
-                } else {
-                    const f32x4 x = *(const gmem<const f32x4>)(o + off[i]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[i][e] = x[e];
+                for (int g = 0; g < 2; ++g) {
+                    if constexpr (BF) {
+                        const u32x2 x = *(const gmem<const u32x2>)(o + off[i] + 8 * g);
+                        v[i][4 * g + 0] = __uint_as_float(x[0] << 16);
+                        v[i][4 * g + 1] = __uint_as_float(x[0] & 0xffff0000u);
+                        v[i][4 * g + 2] = __uint_as_float(x[1] << 16);
+                        v[i][4 * g + 3] = __uint_as_float(x[1] & 0xffff0000u);
+                    } else {
+                        const f32x4 x = *(const gmem<const f32x4>)(o + off[i] + 16 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[i][4 * g + e] = x[e];
+                    }
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
+                for (int e = 0; e < 8; ++e) {
                     if constexpr (BF)
                         v[i][e] = __uint_as_float((uint32_t)*(const gmem<const uint16_t>)(o + off[i] + e * ES) << 16);
                     else
@@ -878,47 +889,45 @@ struct X6Fill {
     __device__ __forceinline__ void load_clamped(const void* base, int64_t ld, int r0, int rows_v, int k0, int K,
                                                  bool vec) {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-            int r, q;
-            pos(i, r, q);
-            const int row = r0 + r, kq = k0 + 4 * q;
+        for (int i = 0; i < H; ++i) {
+            int r, o;
+            pos(i, r, o);
+            const int row = r0 + r;
             const int rc = row < rows_v ? row : rows_v - 1;
-            if (KMAJ) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int ke = kq + e < K ? kq + e : K - 1;
-                    if constexpr (BF)
-                        v[i][e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)ke * ld + rc] << 16);
-                    else
-                        v[i][e] = gptr((const float*)base)[(int64_t)ke * ld + rc];
-                }
-            } else if constexpr (BF) {
-                // four bf16 k values (8 bytes) per quad
-                if (vec) {
-                    const int last = (K - 1) & ~3;
-                    const u32x2 x = *gptr((const u32x2*)((const uint16_t*)base + (int64_t)rc * ld + (kq < last ? kq : last)));
-                    v[i][0] = __uint_as_float(x[0] << 16);
-                    v[i][1] = __uint_as_float(x[0] & 0xffff0000u);
-                    v[i][2] = __uint_as_float(x[1] << 16);
-                    v[i][3] = __uint_as_float(x[1] & 0xffff0000u);
-                } else {
+            for (int g = 0; g < 2; ++g) {
+                const int kq = k0 + 8 * o + 4 * g;   // first k of this group of four
+                if (KMAJ) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int ke = kq + e < K ? kq + e : K - 1;
-                        v[i][e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)rc * ld + ke] << 16);
+                        if constexpr (BF)
+                            v[i][4 * g + e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)ke * ld + rc] << 16);
+                        else
+                            v[i][4 * g + e] = gptr((const float*)base)[(int64_t)ke * ld + rc];
                     }
-                }
-            } else {
-                if (vec) {
+                } else if (vec) {
                     const int last = (K - 1) & ~3;
-                    const f32x4 x = *gptr((const f32x4*)((const float*)base + (int64_t)rc * ld + (kq < last ? kq : last)));
+                    const int kc = kq < last ? kq : last;
+                    if constexpr (BF) {
+                        const u32x2 x = *gptr((const u32x2*)((const uint16_t*)base + (int64_t)rc * ld + kc));
+                        v[i][4 * g + 0] = __uint_as_float(x[0] << 16);
+                        v[i][4 * g + 1] = __uint_as_float(x[0] & 0xffff0000u);
+                        v[i][4 * g + 2] = __uint_as_float(x[1] << 16);
+                        v[i][4 * g + 3] = __uint_as_float(x[1] & 0xffff0000u);
+                    } else {
+                        const f32x4 x = *gptr((const f32x4*)((const float*)base + (int64_t)rc * ld + kc));
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) v[i][e] = x[e];
+                        for (int e = 0; e < 4; ++e) v[i][4 * g + e] = x[e];
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int ke = kq + e < K ? kq + e : K - 1;
-                        v[i][e] = gptr((const float*)base)[(int64_t)rc * ld + ke];
+                        if constexpr (BF)
+                            v[i][4 * g + e] = __uint_as_float((uint32_t)gptr((const uint16_t*)base)[(int64_t)rc * ld + ke] << 16);
+                        else
+                            v[i][4 * g + e] = gptr((const float*)base)[(int64_t)rc * ld + ke];
                     }
                 }
             }
@@ -931,30 +940,38 @@ struct X6Fill {
     __device__ __forceinline__ void put(char* lds, int plane_bytes, bool mask, int r0, int rows_v, int k0,
                                         int K) const {
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-            int r, q;
-            pos(i, r, q);
-            float x[4];
+        for (int i = 0; i < H; ++i) {
+            int r, o;
+            pos(i, r, o);
+            float x[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) x[e] = v[i][e];
+            for (int e = 0; e < 8; ++e) x[e] = v[i][e];
             if (mask) {
                 const bool row_ok = r0 + r < rows_v;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = (row_ok && k0 + 4 * q + e < K) ? x[e] : 0.f;
+                for (int e = 0; e < 8; ++e) x[e] = (row_ok && k0 + 8 * o + e < K) ? x[e] : 0.f;
             }
-            const int off = x6_off(r, q >> 1) + 8 * (q & 1);
+            const int off = x6_off(r, o);
             if constexpr (BF) {
                 // exact bf16 values: the high halves of the widened words
-                const uint32_t w0 = (__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xffff0000u);
-                const uint32_t w1 = (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xffff0000u);
-                *(u32x2*)(lds + off) = (u32x2){w0, w1};
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (__float_as_uint(x[2 * e]) >> 16) | (__float_as_uint(x[2 * e + 1]) & 0xffff0000u);
+                *(u32x4*)(lds + off) = w;
             } else {
-                uint32_t h0, m0, l0, h1, m1, l1;
-                split2(x[0], x[1], h0, m0, l0);
-                split2(x[2], x[3], h1, m1, l1);
-                *(u32x2*)(lds + off) = (u32x2){h0, h1};
-                *(u32x2*)(lds + plane_bytes + off) = (u32x2){m0, m1};
-                *(u32x2*)(lds + 2 * plane_bytes + off) = (u32x2){l0, l1};
+                u32x4 hi, mid, lo;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t h, m, l;
+                    split2(x[2 * e], x[2 * e + 1], h, m, l);
+                    hi[e] = h;
+                    mid[e] = m;
+                    lo[e] = l;
+                }
+                *(u32x4*)(lds + off) = hi;
+                *(u32x4*)(lds + plane_bytes + off) = mid;
+                *(u32x4*)(lds + 2 * plane_bytes + off) = lo;
             }
         }
     }
@@ -1001,9 +1018,9 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
         fb0.init(p.ldb, n0, p.N);
         if constexpr (MATOPT_X6_PREFETCH == 2) {
 #pragma unroll
-            for (int i = 0; i < FA::Q; ++i) fa1.off[i] = fa0.off[i];
+            for (int i = 0; i < FA::H; ++i) fa1.off[i] = fa0.off[i];
 #pragma unroll
-            for (int i = 0; i < FB::Q; ++i) fb1.off[i] = fb0.off[i];
+            for (int i = 0; i < FB::H; ++i) fb1.off[i] = fb0.off[i];
         }
     }
     const bool rows_partial = m0 + C::BM > p.M || n0 + C::BN > p.N;
