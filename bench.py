@@ -400,7 +400,8 @@ def main(argv=None):
         roofline = {
             "bound": "mfma", "achieved": achieved, "peak": mpeak, "unit": "TFLOP/s",
             "frac": achieved / mpeak if achieved else None, "traffic": None,
-            "kernel": "gemm_grouped_kernel (Newton-Schulz X^T X and X (X^T X)"
+            "kernel": ("gemm_grouped_kernel" if args.fp32_mfma else "gemm_x6_kernel")
+                      + " (Newton-Schulz X^T X and X (X^T X)"
                       + ("" if args.fp32_mfma else " on bf16 MFMAs, six piece products")
                       + "; the phase time includes the norm, scaling and combine kernels)",
             "launches": phases["ortho"][1], "avg_launch_ms": ms / max(phases["ortho"][1], 1),
@@ -425,9 +426,9 @@ def main(argv=None):
                 X6_FP32_EQUIV_TFLOPS if x6 else MI355X_FP32_MFMA_TFLOPS)
         kernel = ("gemm16_kernel (bf16 rotation phases: (X V)^T, U^T S^T, (u V^T)^T, W -= lr U P^T)"
                   if args.bf16_rotation else
-                  "gemm_grouped_kernel (fp32 rotation phases on bf16 MFMAs, six piece products: U^T G, "
+                  "gemm_x6_kernel (fp32 rotation phases on bf16 MFMAs, six piece products: U^T G, "
                   "(U^T G) V, the other product of M's chain, U u, W -= lr (.)V^T)" if "rot_pieced" in pf_all else
-                  ("gemm_grouped_kernel (rotation phases on bf16 MFMAs, six piece products: U^T[G|M], (.)V, "
+                  ("gemm_x6_kernel (rotation phases on bf16 MFMAs, six piece products: U^T[G|M], (.)V, "
                    "U u, W -= lr (.)V^T)" if x6 else
                    "gemm_grouped_kernel (rotation phases: U^T[G|M], (.)V, U u, W -= lr (.)V^T)"))
         roofline = {

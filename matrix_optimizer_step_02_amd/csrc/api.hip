@@ -427,8 +427,21 @@ int tiles_of(const std::vector<GemmProb>& probs, int cfg) {
     return t;
 }
 
-// Large tiles when the launch has enough of them to fill the GPU.
+// Large tiles when the launch has enough of them to fill the GPU, except for
+// launches whose products are all short in K (the QR's C -= Yb W2 with
+// K = 256): there a tile's epilogue (C read and written) is long against its
+// few slabs, and the small tile's three workgroups per CU overlap one's
+// epilogue with the others' MFMAs (a refresh of the Qwen3-1.7B set 779 ->
+// 755 ms; 0 turns this off).
+#ifndef MATOPT_SMALL_TILE_MAX_K
+#define MATOPT_SMALL_TILE_MAX_K 256
+#endif
 int choose_cfg(const std::vector<GemmProb>& probs) {
+    if (MATOPT_SMALL_TILE_MAX_K > 0) {
+        bool short_k = !probs.empty();
+        for (const GemmProb& q : probs) short_k = short_k && q.K <= MATOPT_SMALL_TILE_MAX_K;
+        if (short_k) return 0;
+    }
     return tiles_of(probs, 1) >= kGemmLargeMinTiles ? 1 : 0;
 }
 
