@@ -61,6 +61,7 @@ constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY blo
 constexpr int kQrPanelsPerBlock = MATOPT_QR_PANELS_PER_BLOCK;
 constexpr int kQrNB = kQrPB * kQrPanelsPerBlock;   // outer block width
 constexpr int kQrMaxSplits = 16;   // row splits of the in-block reflector-transpose products
+constexpr int kQrReduceCols = 64;  // columns per workgroup of the split reduction
 constexpr int kQrPanelThreads = 512;
 
 // One d x d orthonormalisation: Z (row stride d) is factorised in place, Q is
@@ -205,7 +206,7 @@ __host__ __device__ inline int qr_inblock_cols(int d, int p) {
 }
 
 // Blocks one job contributes to a per-panel launch: reflector-transpose
-// products (512 columns x one row split per block), their reduction (256
+// products (512 columns x one row split per block), their reduction (64
 // columns per block) and the in-block update (128 x 128 tiles).
 __host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p) {
     if (kind == QG_TALL) {
@@ -216,7 +217,7 @@ __host__ __device__ inline int qr_blocks_per_job(int kind, int d, int p) {
     if (ncols <= 0) return 0;
     const int L = d - p * kQrPB;
     if (kind == QG_DOTS) return ((ncols + 511) / 512) * qr_splits(L);
-    if (kind == QG_REDUCE) return (ncols + 255) / 256;
+    if (kind == QG_REDUCE) return (ncols + kQrReduceCols - 1) / kQrReduceCols;
     return ((L + kQrTile - 1) / kQrTile) * ((ncols + kQrTile - 1) / kQrTile);
 }
 

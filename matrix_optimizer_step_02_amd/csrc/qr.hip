@@ -507,32 +507,35 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // Four row pairs per iteration: all loads are issued before the MFMAs
-    // that consume them.
+    // Four row pairs per iteration; the next iteration's rows are loaded
+    // before this one's MFMAs, so the loads' latency overlaps them.
     constexpr int U = 4;
-    for (int i0 = r0; i0 < r1; i0 += 2 * U) {
-        float y[U][NB];
-        float x[U][4];
+    float y[U][NB], x[U][4], yn[U][NB], xn[U][4];
+    auto load = [&](int i0, float (&yy)[U][NB], float (&xx)[U][4]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = i0 + 2 * u + h;
 #pragma unroll
-            for (int a = 0; a < NB; ++a) y[u][a] = 0.f;
+            for (int a = 0; a < NB; ++a) yy[u][a] = 0.f;
 #pragma unroll
-            for (int b = 0; b < 4; ++b) x[u][b] = 0.f;
+            for (int b = 0; b < 4; ++b) xx[u][b] = 0.f;
             if (row < r1) {
 #pragma unroll
                 for (int a = 0; a < NB; ++a) {
                     const int yc = 32 * a + l32;
-                    if (yc < jb) y[u][a] = row < yc ? 0.f : (row == yc ? 1.f : Y[(int64_t)row * d + yc]);
+                    if (yc < jb) yy[u][a] = row < yc ? 0.f : (row == yc ? 1.f : Y[(int64_t)row * d + yc]);
                 }
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     const int col = j0 + 32 * b + l32;
-                    if (col < ncols) x[u][b] = C[(int64_t)row * d + col];
+                    if (col < ncols) xx[u][b] = C[(int64_t)row * d + col];
                 }
             }
         }
+    };
+    load(r0, y, x);
+    for (int i0 = r0; i0 < r1; i0 += 2 * U) {
+        if (i0 + 2 * U < r1) load(i0 + 2 * U, yn, xn);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -540,6 +543,13 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(y[u][a], x[u][b], acc[a][b], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int a = 0; a < NB; ++a) y[u][a] = yn[u][a];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) x[u][b] = xn[u][b];
+        }
     }
 
     gmem<float> part = gptr(Jb.part + (int64_t)s * PB * d);
@@ -557,9 +567,17 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
     }
 }
 
-// W2[:, j] = T^T (sum_s W_s[:, j]).
+// W2[:, j] = T^T (sum_s W_s[:, j]), 64 columns j per workgroup (kQrReduceCols):
+// the 256 threads first add up the split partials of the 64 x 64 block (16
+// sums each, loads coalesced along j) into LDS, then the thread of column j
+// in wavefront g forms outputs c = 16 g .. 16 g + 15, reading T rows as LDS
+// broadcasts. Spreading a job's columns over several workgroups this way
+// keeps the partials' loads from queueing on one CU.
 __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict__ jobs, QrClasses C, int p) {
+    constexpr int JC = kQrReduceCols;
+    static_assert(JC == 64 && PB == 64, "four wavefronts of 64 columns, 16 of the 64 rows each");
     __shared__ __attribute__((aligned(16))) float Ts[PB][PB];
+    __shared__ float Ws[PB][JC + 1];
     int job, local;
     if (!qr_locate(C, QG_REDUCE, p, blockIdx.x, job, local)) return;
     const QrJob Jb = jobs[job];
@@ -567,36 +585,40 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
     const int d = Jb.d;
     const int L = d - k;
     const int ncols = qr_inblock_cols(d, p);
+    const int tid = threadIdx.x, jj = tid & 63, g = tid >> 6;
+    const int j = local * JC + jj;
     gmem<const float> Tp = gptr((const float*)Jb.T + (int64_t)p * PB * PB);
-    for (int e = threadIdx.x; e < PB * PB; e += 256) Ts[e / PB][e % PB] = Tp[e];
-    __syncthreads();
-    const int j = local * 256 + threadIdx.x;
-    if (j >= ncols) return;
+    for (int e = tid; e < PB * PB; e += 256) Ts[e / PB][e % PB] = Tp[e];
     const int splits = qr_splits(L);
-    float w[PB];
+    float w[16];
 #pragma unroll
-    for (int c = 0; c < PB; ++c) w[c] = 0.f;
-    for (int s = 0; s < splits; ++s) {
-        gmem<const float> part = gptr((const float*)Jb.part + (int64_t)s * PB * d + j);
+    for (int c = 0; c < 16; ++c) w[c] = 0.f;
+    if (j < ncols) {
+        for (int s = 0; s < splits; ++s) {
+            gmem<const float> part = gptr((const float*)Jb.part + ((int64_t)s * PB + 16 * g) * d + j);
 #pragma unroll
-        for (int c = 0; c < PB; ++c) w[c] += part[(int64_t)c * d];
-    }
-    // Four output rows c at a time: every thread reads the same T entries
-    // (an LDS broadcast), four of them per 16-byte read. The c loop stays
-    // rolled: unrolled, the compiler hoists all the LDS reads of T ahead of
-    // the products and spills.
-#pragma unroll 1
-    for (int c = 0; c < PB; c += 4) {
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int l = 0; l < PB; ++l) {
-            const f32x4 t = *(const f32x4*)&Ts[l][c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += t[e] * w[l];
+            for (int c = 0; c < 16; ++c) w[c] += part[(int64_t)c * d];
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gptr(Jb.W2)[(int64_t)(c + e) * d + j] = acc[e];
     }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) Ws[16 * g + c][jj] = w[c];
+    __syncthreads();
+    if (j >= ncols) return;
+    float acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) acc[c] = 0.f;
+#pragma unroll 4
+    for (int l = 0; l < PB; ++l) {
+        const float x = Ws[l][jj];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 t = *(const f32x4*)&Ts[l][16 * g + 4 * q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * q + e] += t[e] * x;
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) gptr(Jb.W2)[(int64_t)(16 * g + c) * d + j] = acc[c];
 }
 
 __global__ __launch_bounds__(256) void qr_init_q_kernel(const QrJob* __restrict__ jobs) {
