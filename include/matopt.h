@@ -330,7 +330,8 @@ opt_status opt_gemm(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int6
  * that matter accumulate in fp32, and the ones left out are below 2^-23 of
  * each product. Same arguments as opt_gemm; the supported layouts are
  * (trans_a, trans_b, a_dtype, b_dtype) = (0, 0, F32, F32), (1, 0, F32, F32),
- * (0, 1, F32, F32), (0, 0, F32, BF16) and (0, 0, BF16, F32); with a bf16
+ * (0, 1, F32, F32), (0, 0, F32, BF16), (0, 0, BF16, F32) and
+ * (1, 0, BF16, F32); with a bf16
  * operand, which is its own high piece, three piece products. Others return
  * OPT_EUNSUPPORTED. */
 opt_status opt_gemm_x6(int32_t trans_a, int32_t trans_b, int64_t M, int64_t N, int64_t K,
@@ -363,7 +364,7 @@ opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc). The QR job record and scratch live in a
  * fixed device array inside the library, sized for one matrix of order
- * OPT_STATIC_MAX_DIM (about 34 MiB); every GPU the library runs on holds its
+ * OPT_STATIC_MAX_DIM (about 22 MiB); every GPU the library runs on holds its
  * own copy until the process ends. Same kernels and results as
  * opt_orthonormalize. d > OPT_STATIC_MAX_DIM returns OPT_EUNSUPPORTED; no
  * device memory is allocated or freed. The array keeps whatever the last call

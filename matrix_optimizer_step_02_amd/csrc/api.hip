@@ -172,12 +172,6 @@ struct NsChunk {
 struct RefreshBatch {
     std::vector<int> mats;
     std::vector<std::vector<GemmLaunch>> prod1, prod2;   // K-chunk steps, run in order
-    // Gram products of the matrices with bf16 M on bf16 MFMA: split jobs
-    // (M^T, and the three bf16 pieces of the fp32 operand, transposed), then
-    // one launch per piece accumulating into the fp32 product
-    uint64_t split1 = 0, split2 = 0;
-    int nsplit1 = 0, nsplit2 = 0, tiles1 = 0, tiles2 = 0;
-    std::vector<Gemm16Launch> p1_16, p2_16;
     CopyLaunch comp;
     QrBatch qr;
     uint64_t ref_bytes = 0;
@@ -647,8 +641,8 @@ size_t add_k_chunked16(std::vector<std::vector<Gemm16Prob>>& steps, size_t next,
 }
 
 // Rows of a basis per Newton-Schulz product launch: the product goes to the
-// QR job's `part` buffer, which holds kQrMaxSplits * kQrPB rows of d floats.
-constexpr int64_t kNsRows = (int64_t)kQrMaxSplits * kQrPB;
+// QR job's `part` buffer, which holds kNsRows rows of d floats.
+constexpr int64_t kNsRows = 256;
 
 // The K range [k0, k0 + kc) of a product, as a product of its own.
 PGemm k_slice(const PGemm& g, int64_t k0, int64_t kc, float beta) {
@@ -681,11 +675,14 @@ constexpr QrBytes qr_job_bytes(int64_t d) {
     QrBytes b{};
     b.Z = align_up(4ull * d * d);
     b.T = align_up(4ull * panels((int)d) * kQrPB * kQrPB);
-    // the in-block products' row splits, or the tall-panel path's sums, Gram
-    // blocks and barrier words (qr.hip), whichever is larger
+    // the in-block products' row splits (kQrMaxSplits x kQrPB rows of the
+    // at most kQrPartLd in-block columns), the tall-panel path's sums, Gram
+    // blocks and barrier words (qr.hip), or kNsRows rows of a Newton-Schulz
+    // product, whichever is largest
     const uint64_t gmax = (uint64_t)(d + kQrTallRows - 1) / kQrTallRows;
     const uint64_t tall = gmax * (2 * kQrPB + kQrPB * kQrPB) + 256;
-    b.part = align_up(4ull * std::max<uint64_t>((uint64_t)kQrMaxSplits * kQrPB * d, tall));
+    const uint64_t splits = (uint64_t)kQrMaxSplits * kQrPB * kQrPartLd;
+    b.part = align_up(4ull * std::max<uint64_t>(std::max<uint64_t>(splits, tall), (uint64_t)kNsRows * d));
     b.W2 = align_up(4ull * kQrPB * d);
     b.Yb = align_up(4ull * d * kQrNB);
     b.Wb = align_up(4ull * kQrNB * d);
@@ -790,20 +787,6 @@ QrSteps qr_block_steps(const std::vector<QrJob>& jobs) {
 
 // Refresh scratch of one matrix: Gram products B1U (n x r), B1V (m x r), the
 // QR inputs ZU (m x m), ZV (n x n) and the QR scratch of both orders.
-// Matrices whose Gram products run on bf16 MFMA: bf16 M that the bf16 GEMM
-// can read directly (rows of a multiple of 8 elements, 16-byte aligned).
-bool gram16_eligible(const Mat& M) {
-    return M.bf16 && M.d.m % 8 == 0 && M.d.n % 8 == 0 && aligned(M.d.M, 16);
-}
-
-// Extra refresh scratch of an eligible matrix: M^T (bf16, n x m) and the
-// three bf16 pieces of U_r^T (r x m) and of V_r^T (r x n), whose space the
-// pieces of B1V^T and B1U^T reuse.
-uint64_t gram16_bytes(int64_t m, int64_t n) {
-    const int64_t r = std::min(m, n);
-    return align_up(2ull * n * m) + align_up(6ull * r * m) + align_up(6ull * r * n);
-}
-
 uint64_t refresh_bytes(int64_t m, int64_t n) {
     const int64_t r = std::min(m, n);
     QrBytes bu = qr_job_bytes(m), bv = qr_job_bytes(n);
@@ -820,7 +803,7 @@ std::vector<std::vector<int>> plan_refresh(const opt_group_s* g, const std::vect
     for (const std::vector<int>& members : plan)
         for (int mi : members) {
             const int64_t m = g->mats[mi].d.m, n = g->mats[mi].d.n;
-            const uint64_t b = refresh_bytes(m, n) + (gram16_eligible(g->mats[mi]) ? gram16_bytes(m, n) : 0) +
+            const uint64_t b = refresh_bytes(m, n) +
                                ((g->hp.flags & OPT_FLAG_BF16_BASES) ? align_up(4ull * m * m) + align_up(4ull * n * n) : 0);
             if (out.empty() || (used + b > cap && !out.back().empty())) {
                 out.emplace_back();
@@ -1230,25 +1213,6 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
         R.mats = members;
         uint64_t off = 0;
         std::vector<PGemm> p1, p2;
-        std::vector<std::vector<Gemm16Prob>> q1, q2;
-        std::vector<SplitJob> sj1, sj2;
-        int t1 = 0, t2 = 0;
-        auto split = [](std::vector<SplitJob>& v, int& tiles, const void* src, bool src_bf16, int64_t ld_src,
-                        int64_t rows, int64_t cols, uint16_t* dst, int npieces) {
-            SplitJob j{};
-            j.src = src;
-            j.dst = dst;
-            j.ld_src = ld_src;
-            j.ld_dst = rows;
-            j.piece_stride = rows * cols;
-            j.rows = (int32_t)rows;
-            j.cols = (int32_t)cols;
-            j.npieces = npieces;
-            j.src_bf16 = src_bf16;
-            j.tile_begin = tiles;
-            tiles += (int)(((rows + 31) / 32) * ((cols + 31) / 32));
-            v.push_back(j);
-        };
         std::vector<CopyJob> comp;
         std::vector<CvtJob> widen, round16;
         int64_t widen_chunks = 0, round_chunks = 0;
@@ -1280,37 +1244,14 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
                 x.U = XU;
                 x.V = XV;
             }
-            if (gram16_eligible(M)) {
-                // bf16 M exactly, the fp32 operand as three exact bf16 pieces:
-                // every Gram product is three bf16 NT products accumulating in fp32
-                uint16_t* Mt = (uint16_t*)(rscratch + off); off += align_up(2ull * n * m);
-                uint16_t* Up = (uint16_t*)(rscratch + off); off += align_up(6ull * r * m);   // later B1V^T pieces
-                uint16_t* Vp = (uint16_t*)(rscratch + off); off += align_up(6ull * r * n);   // later B1U^T pieces
-                const uint16_t* Mb = (const uint16_t*)x.M;
-                split(sj1, t1, x.M, true, n, m, n, Mt, 1);          // M^T (n x m)
-                split(sj1, t1, x.U, false, m, m, r, Up, 3);         // U[:, :r]^T pieces (r x m)
-                split(sj1, t1, x.V, false, n, n, r, Vp, 3);         // V[:, :r]^T pieces (r x n)
-                split(sj2, t2, B1U, false, r, n, r, Vp, 3);         // B1U^T pieces (r x n)
-                split(sj2, t2, B1V, false, r, m, r, Up, 3);         // B1V^T pieces (r x m)
-                // pieces in order hi, mid, lo, each in K chunks, accumulating
-                size_t a = 0, b = 0, c = 0, d = 0;
-                for (int pc = 0; pc < 3; ++pc) {
-                    const float beta = pc ? 1.f : 0.f;
-                    a = add_k_chunked16(q1, a, g16(Mt, m, Up + pc * r * m, m, B1U, r, n, r, m, 1.f, beta, r));  // M^T U_r
-                    b = add_k_chunked16(q1, b, g16(Mb, n, Vp + pc * r * n, n, B1V, r, m, r, n, 1.f, beta, r));  // M V_r
-                    c = add_k_chunked16(q2, c, g16(Mb, n, Vp + pc * r * n, n, ZU, m, m, r, n, 1.f, beta, r));   // M B1U
-                    d = add_k_chunked16(q2, d, g16(Mt, m, Up + pc * r * m, m, ZV, n, n, r, m, 1.f, beta, r));   // M^T B1V
-                }
-            } else {
-                // B1U = M^T U[:, :r]   (n x r): A = M stored m x n read transposed
-                p1.push_back(mk(true, false, x.M, M.bf16, n, x.U, false, m, B1U, r, n, r, m, 1.f, 0.f));
-                // B1V = M V[:, :r]     (m x r)
-                p1.push_back(mk(false, false, x.M, M.bf16, n, x.V, false, n, B1V, r, m, r, n, 1.f, 0.f));
-                // ZU[:, :r] = M B1U     (m x r)
-                p2.push_back(mk(false, false, x.M, M.bf16, n, B1U, false, r, ZU, m, m, r, n, 1.f, 0.f));
-                // ZV[:, :r] = M^T B1V   (n x r)
-                p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
-            }
+            // B1U = M^T U[:, :r]   (n x r): A = M stored m x n read transposed
+            p1.push_back(mk(true, false, x.M, M.bf16, n, x.U, false, m, B1U, r, n, r, m, 1.f, 0.f));
+            // B1V = M V[:, :r]     (m x r)
+            p1.push_back(mk(false, false, x.M, M.bf16, n, x.V, false, n, B1V, r, m, r, n, 1.f, 0.f));
+            // ZU[:, :r] = M B1U     (m x r)
+            p2.push_back(mk(false, false, x.M, M.bf16, n, B1U, false, r, ZU, m, m, r, n, 1.f, 0.f));
+            // ZV[:, :r] = M^T B1V   (n x r)
+            p2.push_back(mk(true, false, x.M, M.bf16, n, B1V, false, r, ZV, n, n, r, m, 1.f, 0.f));
             if (r < m) comp.push_back({x.U, ZU, (int32_t)m, (int32_t)r});
             if (r < n) comp.push_back({x.V, ZV, (int32_t)n, (int32_t)r});
             jsrc.push_back({m, ZU, x.U, M.idx, 0});
@@ -1338,16 +1279,6 @@ void build(opt_group_s* g, const std::vector<std::vector<int>>& plan, char* regi
             for (const PGemm& x : p2) add_k_chunked(s2, x);
             for (const std::vector<PGemm>& st : s1) R.prod1.push_back(put_gemm(g->img, st, rx6));
             for (const std::vector<PGemm>& st : s2) R.prod2.push_back(put_gemm(g->img, st, rx6));
-            if (!sj1.empty()) {
-                R.nsplit1 = (int)sj1.size();
-                R.nsplit2 = (int)sj2.size();
-                R.tiles1 = t1;
-                R.tiles2 = t2;
-                R.split1 = g->img.put(sj1);
-                R.split2 = g->img.put(sj2);
-                for (const std::vector<Gemm16Prob>& st : q1) R.p1_16.push_back(put_gemm16(g->img, st, false));
-                for (const std::vector<Gemm16Prob>& st : q2) R.p2_16.push_back(put_gemm16(g->img, st, false));
-            }
         }
         R.nwiden = (int)widen.size();
         R.widen_chunks = widen_chunks;
@@ -1614,16 +1545,8 @@ hipError_t run_refresh(opt_group_s* g, const RefreshBatch& G, int power_iters, h
     hipError_t e;
     if (G.nwiden && (e = launch_cvt16(dptr<CvtJob>(g, G.widen), G.nwiden, G.widen_chunks, s))) return e;
     for (int it = 0; it < power_iters; ++it) {
-        if (G.nsplit1) {
-            if ((e = launch_split16(dptr<SplitJob>(g, G.split1), G.nsplit1, G.tiles1, s))) return e;
-            if ((e = run_gemm16(g, G.p1_16, 1.f, s))) return e;
-        }
         for (const std::vector<GemmLaunch>& st : G.prod1)
             if ((e = run_gemm(g, st, 1.f, s))) return e;
-        if (G.nsplit2) {
-            if ((e = launch_split16(dptr<SplitJob>(g, G.split2), G.nsplit2, G.tiles2, s))) return e;
-            if ((e = run_gemm16(g, G.p2_16, 1.f, s))) return e;
-        }
         for (const std::vector<GemmLaunch>& st : G.prod2)
             if ((e = run_gemm(g, st, 1.f, s))) return e;
         if ((e = launch_copy_cols(dptr<CopyJob>(g, G.comp.jobs), G.comp.n, G.comp.max_d, s))) return e;

@@ -39,8 +39,8 @@ inline int gemm_variant(bool at, bool bt, bool a_bf16, bool b_bf16) {
 // exact bf16 pieces and six piece products kept (fp32 accuracy; three when
 // one operand is bf16, which is its own high piece). Available for the
 // variants 0 (A M x K, B K x N), 1 (A stored K x M), 2 (B stored N x K),
-// 8 (B bf16) and 4 (A bf16; not with the in-register split that
-// MATOPT_X6_REGISTER_SPLIT selects).
+// 8 (B bf16), and 4 and 5 (A bf16, as stored or transposed; not with the
+// in-register split that MATOPT_X6_REGISTER_SPLIT selects).
 #ifdef MATOPT_X6_REGISTER_SPLIT
 constexpr bool kX6SplitAtFill = false;
 #else
@@ -48,7 +48,8 @@ constexpr bool kX6SplitAtFill = true;
 #endif
 constexpr int GV_X6 = 16;
 inline bool gemm_x6_available(int variant) {
-    return variant == 0 || variant == 1 || variant == 2 || variant == 8 || (kX6SplitAtFill && variant == 4);
+    return variant == 0 || variant == 1 || variant == 2 || variant == 8 ||
+           (kX6SplitAtFill && (variant == 4 || variant == 5));
 }
 
 // Two tile configurations of the grouped GEMM (rotations, Gram products,

@@ -1355,6 +1355,7 @@ static hipError_t dispatch(int variant, int cfg, const GemmArgs& a, hipStream_t 
         case GV_X6 | 2: return launch<false, true, false, false, true>(cfg, a, s);
         case GV_X6 | 8: return launch<false, false, false, true, true>(cfg, a, s);
         case GV_X6 | 4: return launch<false, false, true, false, true>(cfg, a, s);
+        case GV_X6 | 5: return launch<true, false, true, false, true>(cfg, a, s);
         default: return hipErrorInvalidValue;
     }
 }

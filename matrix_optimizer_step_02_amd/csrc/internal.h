@@ -60,13 +60,16 @@ constexpr int kQrPB = 64;          // panel width (reflectors per compact-WY blo
 #endif
 constexpr int kQrPanelsPerBlock = MATOPT_QR_PANELS_PER_BLOCK;
 constexpr int kQrNB = kQrPB * kQrPanelsPerBlock;   // outer block width
+constexpr int kQrPartLd = kQrNB;   // row stride of the split partials (in-block columns < kQrNB)
 constexpr int kQrMaxSplits = 16;   // row splits of the in-block reflector-transpose products
 constexpr int kQrReduceCols = 64;  // columns per workgroup of the split reduction
 constexpr int kQrPanelThreads = 512;
 
 // One d x d orthonormalisation: Z (row stride d) is factorised in place, Q is
 // formed in X. Scratch: T (np * PB * PB: the panels' compact-WY factors),
-// part (kQrMaxSplits * PB * d) and W2 (PB * d) for the in-block updates, and
+// part (the in-block products' split partials, kQrMaxSplits * PB rows of
+// kQrPartLd; also the tall-panel sums and a Newton-Schulz product's rows)
+// and W2 (PB * d) for the in-block updates, and
 // for the outer blocks Yb (d * NB: the block's reflectors as an explicit
 // unit-lower matrix, row stride NB), Wb and W2b (NB * d each, row stride d)
 // and Sb (nb * NB * NB: every block's reflector Gram matrix).

@@ -552,7 +552,9 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
         }
     }
 
-    gmem<float> part = gptr(Jb.part + (int64_t)s * PB * d);
+    // split s's partials: PB rows of kQrPartLd (the in-block columns) floats
+    static_assert(kQrPartLd >= kQrNB - PB, "the in-block columns fit in a partial row");
+    gmem<float> part = gptr(Jb.part + (int64_t)s * PB * kQrPartLd);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         const int j = j0 + 32 * b + l32;
@@ -562,7 +564,7 @@ __global__ __launch_bounds__(256) void qr_dots_kernel(const QrJob* __restrict__ 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int cc = 32 * a + 8 * (r >> 2) + 4 * h + (r & 3);
-                part[(int64_t)cc * d + j] = acc[a][b][r];
+                part[(int64_t)cc * kQrPartLd + j] = acc[a][b][r];
             }
     }
 }
@@ -595,9 +597,9 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
     for (int c = 0; c < 16; ++c) w[c] = 0.f;
     if (j < ncols) {
         for (int s = 0; s < splits; ++s) {
-            gmem<const float> part = gptr((const float*)Jb.part + ((int64_t)s * PB + 16 * g) * d + j);
+            gmem<const float> part = gptr((const float*)Jb.part + ((int64_t)s * PB + 16 * g) * kQrPartLd + j);
 #pragma unroll
-            for (int c = 0; c < 16; ++c) w[c] += part[(int64_t)c * d];
+            for (int c = 0; c < 16; ++c) w[c] += part[(int64_t)c * kQrPartLd];
         }
     }
 #pragma unroll

@@ -53,7 +53,8 @@ def _gemm_case(ta, tb, a_bf16, b_bf16, M, N, K, alpha=1.0, beta=0.0, seed=0, x6=
     return float(np.max(err / bound))
 
 
-@pytest.mark.parametrize("ta,tb,a_bf16,b_bf16", [(0, 0, 0, 0), (1, 0, 0, 0), (0, 1, 0, 0), (0, 0, 0, 1), (0, 0, 1, 0)])
+@pytest.mark.parametrize("ta,tb,a_bf16,b_bf16", [(0, 0, 0, 0), (1, 0, 0, 0), (0, 1, 0, 0), (0, 0, 0, 1), (0, 0, 1, 0),
+                                                  (1, 0, 1, 0)])
 def test_gemm_x6_variants(ta, tb, a_bf16, b_bf16):
     """fp32 products on bf16 MFMAs (three-piece split, six piece products):
     the fp32 dot-product bound holds element by element (the terms left out
