@@ -282,6 +282,36 @@ def cpu_baseline(wl, budget_s: float, muon_iters: int = 0):
     return out
 
 
+def time_orthonormalize(orders) -> int:
+    """One JSON line per order: opt_orthonormalize of a seeded Gaussian
+    d x d matrix, three runs (the first includes one-time set-up), with the
+    orthonormality of the result."""
+    import torch
+    import matrix_optimizer_step_02_amd as mo
+    N = mo.native
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    for d in orders:
+        g = torch.Generator(device="cuda").manual_seed(d)
+        Z0 = torch.randn(d, d, device="cuda", generator=g)
+        Q = torch.empty_like(Z0)
+        nb = N.opt_orthonormalize_workspace_size(d)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        times = []
+        for _ in range(3):
+            Z = Z0.clone()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            N.opt_orthonormalize(Z.data_ptr(), Q.data_ptr(), d, ws.data_ptr(), nb, mo.stream_ptr())
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        orth = float((Q.T @ Q - torch.eye(d, device="cuda")).abs().max())
+        print(json.dumps({"orthonormalize": d, "ms": times, "flops": (8.0 / 3.0) * d ** 3,
+                          "tflops": (8.0 / 3.0) * d ** 3 / (min(times) * 1e-3) / 1e12, "orth": orth}), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,7 +343,12 @@ def main(argv=None):
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the rotation-GEMM traffic summary from two rocprofv3 --pmc "
                          "counter_collection.csv files (FETCH_SIZE, WRITE_SIZE) and exit")
+    ap.add_argument("--orthonormalize", type=int, nargs="+", metavar="D",
+                    help="instead of the step: time opt_orthonormalize (the refresh's QR) on one "
+                         "seeded d x d Gaussian matrix per order D, three runs each, and exit")
     args = ap.parse_args(argv)
+    if args.orthonormalize:
+        return time_orthonormalize(args.orthonormalize)
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(*args.summarize_pmc, calib_mib=args.calibrate_copy_mib or 1024)))
         return 0

@@ -354,7 +354,8 @@ opt_status opt_gemm_bf16(int64_t M, int64_t N, int64_t K, float alpha, const voi
 
 /* Q = the positive-diagonal-R orthonormal factor of the d x d fp32 matrix Z
  * (row-major, stride d). Z is overwritten with the Householder factorisation
- * (R on and above the diagonal, reflectors below). Q must not overlap Z.
+ * (R on and above the diagonal, reflectors below). Q must not overlap Z. The
+ * block products run on bf16 MFMAs at fp32 accuracy, as in the refresh.
  * `workspace` is device memory of opt_orthonormalize_workspace_size(d) bytes. */
 opt_status opt_orthonormalize_workspace_size(int64_t d, uint64_t* bytes);
 opt_status opt_orthonormalize(float* Z, float* Q, int64_t d, void* workspace,

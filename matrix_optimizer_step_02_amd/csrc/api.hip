@@ -2191,7 +2191,8 @@ opt_status orthonormalize_in(float* Z, float* Q, int64_t d, char* w, hipStream_t
     hipLaunchKernelGGL(put_job_kernel, dim3(1), dim3(1), 0, s, (QrJob*)w, j);
     if ((e = hipGetLastError())) return hip_fail(e, "job upload");
     std::vector<int> np{j.np}, dd{(int)d};
-    // one job: every block step has one problem, passed by value
+    // one job: every block step has one problem, passed by value; the block
+    // products on bf16 MFMAs at fp32 accuracy, as in the step's refresh
     const QrSteps st = qr_block_steps({j});
     auto steps = [&](int b, bool qform) -> hipError_t {
         for (const std::vector<PGemm>& step : (qform ? st.qform : st.fact)[b])
@@ -2199,7 +2200,8 @@ opt_status orthonormalize_in(float* Z, float* Q, int64_t d, char* w, hipStream_t
                 GemmProb p1 = pg.p;
                 const int cfg = choose_cfg({p1});
                 set_tiles(p1, cfg);
-                if (hipError_t e2 = launch_gemm_single(pg.variant, cfg, p1, s)) return e2;
+                const int v = pg.variant | (gemm_x6_available(pg.variant) ? GV_X6 : 0);
+                if (hipError_t e2 = launch_gemm_single(v, cfg, p1, s)) return e2;
             }
         return hipSuccess;
     };
