@@ -291,8 +291,8 @@ def time_orthonormalize(orders) -> int:
     N = mo.native
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     for d in orders:
-        g = torch.Generator(device="cuda").manual_seed(d)
-        Z0 = torch.randn(d, d, device="cuda", generator=g)
+        g = torch.Generator().manual_seed(d)
+        Z0 = torch.randn(d, d, generator=g).to("cuda")
         Q = torch.empty_like(Z0)
         nb = N.opt_orthonormalize_workspace_size(d)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
