@@ -117,6 +117,47 @@ __device__ __forceinline__ void dma16(char* buf, const uint16_t* base, int64_t l
     }
 }
 
+// The same fill with the per-lane addresses computed once per tile: each
+// chunk's byte offset from the operand's slab-0 origin (row clamped into the
+// operand, 32-bit: the caller checks the operand's span) and whether its row
+// is inside the operand. A slab whose k values all lie inside K then loads
+// from origin + k0 (uniform) plus the offset, or the zero block for rows
+// past the operand.
+template <class C, int R>
+struct Dma16Offs {
+    static constexpr int RPC = 1024 / C::RB;
+    static constexpr int CPW = R / RPC / C::NW;
+    uint32_t off[CPW];
+    uint32_t rok;   // bit t: chunk t's row is inside the operand
+
+    __device__ __forceinline__ void init(int64_t ld, int rows, int r0) {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        rok = 0;
+#pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+            const int c = wave * CPW + t;
+            const int r = RPC * c + lane / C::CH;
+            const int kp = 8 * ((lane % C::CH) ^ swz16<C::BK>(r));
+            const int grow = r0 + r;
+            const int rc = grow < rows ? grow : rows - 1;
+            off[t] = (uint32_t)(((int64_t)rc * ld + kp) * 2);
+            rok |= (grow < rows ? 1u : 0u) << t;
+        }
+    }
+
+    __device__ __forceinline__ void fill(char* buf, const uint16_t* base, int k0) const {
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const char* origin = (const char*)(base + k0);
+#pragma unroll
+        for (int t = 0; t < CPW; ++t) {
+            const int c = wave * CPW + t;
+            const void* src = ((rok >> t) & 1u) ? (const void*)(origin + off[t]) : (const void*)g_gemm16_zero;
+            __builtin_amdgcn_global_load_lds((gsrc_ptr)src, (lds_ptr)(buf + c * 1024), 16, 0, 0);
+        }
+    }
+};
+
 // Fragments of k step s: lane l takes row (or column) l % 32 of each 32-block
 // and k values 16 s + 8 (l / 32) .. +7 of the slab.
 template <class C>
@@ -279,15 +320,31 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
     // Otherwise slab t covers k0 = t BK of the concatenated range: period q
     // at kk = k0 - q kper (kper is a multiple of the slab depth). Past the
     // last slab every load reads the zero block.
+    // per-tile fill addresses, when both operands' spans fit 32-bit offsets
+    Dma16Offs<C, C::BM> oa;
+    Dma16Offs<C, C::BN> ob;
+    const bool offs = (int64_t)p.M * p.lda * 2 < (int64_t(1) << 32) && (int64_t)p.N * p.ldb * 2 < (int64_t(1) << 32);
+    if (offs) {
+        oa.init(p.lda, p.M, m0);
+        ob.init(p.ldb, p.N, n0);
+    }
+    // slab of k values k0 .. k0 + BK - 1 of period q, inside K or not (kv = 0:
+    // past the last slab)
+    auto fill_a = [&](char* buf, int q, int kv, int k0) {
+        if (offs && kv > 0 && k0 + C::BK <= kv) oa.fill(buf, p.A + q * p.a_ps, k0);
+        else dma16<C, C::BM>(buf, p.A + q * p.a_ps, p.lda, p.M, kv, m0, k0);
+    };
+    auto fill_b = [&](char* buf, int q, int kv, int k0) {
+        if (offs && kv > 0 && k0 + C::BK <= kv) ob.fill(buf, p.B + q * p.b_ps, k0);
+        else dma16<C, C::BN>(buf, p.B + q * p.b_ps, p.ldb, p.N, kv, n0, k0);
+    };
     auto fill = [&](int b, int t) {
         if (inter) {
             const int ks = t / p.np, q = t - ks * p.np;
             const int k0 = ks * C::BK;
             const int kv = k0 < p.K ? p.K : 0;
-            if (p.a_ps != 0 || q == 0)
-                dma16<C, C::BM>(abuf(buf_a(t)), p.A + q * p.a_ps, p.lda, p.M, kv, m0, k0);
-            if (p.b_ps != 0 || q == 0)
-                dma16<C, C::BN>(bbuf(buf_b(t)), p.B + q * p.b_ps, p.ldb, p.N, kv, n0, k0);
+            if (p.a_ps != 0 || q == 0) fill_a(abuf(buf_a(t)), q, kv, k0);
+            if (p.b_ps != 0 || q == 0) fill_b(bbuf(buf_b(t)), q, kv, k0);
             return;
         }
         const int k0 = t * C::BK;
@@ -295,8 +352,8 @@ __device__ __forceinline__ void tile16(const Gemm16Prob& p, int tm, int tn, floa
         const int kk = k0 - q * p.kper;
         const int kv = q < p.np ? p.K : 0;
         q = min(q, p.np - 1);
-        dma16<C, C::BM>(abuf(b), p.A + q * p.a_ps, p.lda, p.M, kv, m0, kk);
-        dma16<C, C::BN>(bbuf(b), p.B + q * p.b_ps, p.ldb, p.N, kv, n0, kk);
+        fill_a(abuf(b), q, kv, kk);
+        fill_b(bbuf(b), q, kv, kk);
     };
     f32x16 acc[C::TM][C::TN];
 #pragma unroll
