@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <random>
+#include <algorithm>
 #include <vector>
 
 #include "matopt.h"
@@ -122,6 +123,10 @@ void plans_and_sizes() {
             uint64_t bytes = 0;
             expect(opt_group_workspace_size(d.data(), (int32_t)d.size(), &hf, &bytes) == OPT_OK && bytes > 0,
                    "workspace size");
+            uint64_t parts[4] = {};
+            expect(opt_group_workspace_parts(d.data(), (int32_t)d.size(), &hf, parts) == OPT_OK &&
+                       parts[0] + std::max(parts[1] + parts[2], parts[3]) == bytes,
+                   "workspace parts");
         }
     }
     // ragged shapes, every flag set

@@ -189,6 +189,23 @@ def test_refresh_buffers_overlay_the_copies(N):
     assert one["copies"] == p["copies"] and one["scratch"] == p["scratch"]
 
 
+def test_default_refresh_cap_keeps_the_qwen3_sets_in_one_batch(N):
+    """The default refresh cap (the largest of 4 GiB, the copies and scratch,
+    and the state) gives the Qwen3-1.7B set and the Qwen3-8B half one refresh
+    batch each (the same largest batch as an unbounded cap), with a
+    workspace below the state it serves."""
+    for key in ("qwen3_1p7b", "qwen3_8b_half"):
+        wl = workloads.get(key)
+        dt = N.OPT_BF16 if wl.m_dtype == "bf16" else N.OPT_F32
+        d = descs(N, [(s.m, s.n) for s in wl.matrices], dtype=dt)
+        default = _parts(N, d, hp(N, K=wl.K))
+        unbounded = _parts(N, d, hp(N, K=wl.K, refresh_capacity_bytes=1 << 50))
+        assert default["refresh"] == unbounded["refresh"]
+        state = sum(s.m * s.n * (12 + (2 if wl.m_dtype == "bf16" else 4)) + 4 * (s.m ** 2 + s.n ** 2)
+                    for s in wl.matrices)
+        assert N.opt_group_workspace_size(d, hp(N, K=wl.K)) <= state
+
+
 def test_workspace_holds_the_pieces_of_the_momentum_bases(N):
     """A bf16 M with both sides multiples of 8 gets the three bf16 pieces of
     U^T (m > n) or V^T (m <= n), 6 d^2 bytes (256-byte aligned), beside the
