@@ -1050,6 +1050,13 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
     // one slab: its MFMAs from LDS buffer kt % 2; after the first row block,
     // slab kt + 1 from registers (fa, fb) into the other buffer and the load
     // of slab kt + 1 + MATOPT_X6_PREFETCH into the same registers
+    // With both operands split, the two wavefronts that share a SIMD (w and
+    // w + 4 of 8) split and write the next slab at different row blocks, so
+    // that one's vector work meets the other's MFMAs instead of both leaving
+    // the matrix unit idle at once (they start each slab together, after its
+    // barrier). With one bf16 operand the split is half as long, and the
+    // common row block is faster.
+    const bool put_late = !ABF && !BBF && C::NT > 256 && (__builtin_amdgcn_readfirstlane(wave) >> 2) % 2 == 1;
     auto slab = [&](int kt, FA& fa, FB& fb) {
         const char* cur = smem + (kt & 1) * L::BUF;
         char* nxt = smem + ((kt + 1) & 1) * L::BUF;
@@ -1107,7 +1114,7 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
                 for (int j = 0; j < TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[j][0], acc.v[i][j], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            if (i == 0) {
+            if (put_late ? i == TM / 2 : i == 0) {
                 // the next slab's pieces into the other buffer (read by every
                 // wavefront before the previous barrier), then the next load
                 put(fa, fb, nxt, (kt + 1) * 16);
