@@ -631,29 +631,53 @@ __global__ __launch_bounds__(256) void qr_reduce_kernel(const QrJob* __restrict_
     for (int c = 0; c < 16; ++c) gptr(Jb.W2)[(int64_t)(16 * g + c) * d + j] = acc[c];
 }
 
+// The helper copies below move 16-byte groups of four consecutive columns
+// when a row's length and the base addresses allow it (else one float at a
+// time), in a grid-stride loop over each job's groups: the grid is sized for
+// the largest job, and smaller jobs' workgroups leave the loop early.
+
+__device__ __forceinline__ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// X = diag(sign Z_ii): the start of the backward accumulation of Q.
 __global__ __launch_bounds__(256) void qr_init_q_kernel(const QrJob* __restrict__ jobs) {
     const QrJob Jb = jobs[blockIdx.y];
     const int64_t d = Jb.d;
-    const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int64_t e = e0 + q;
-        if (e >= d * d) break;
-        const int64_t i = e / d, j = e - i * d;
-        float val = 0.f;
-        if (i == j) val = gptr(Jb.Z)[i * d + i] < 0.f ? -1.f : 1.f;
-        gptr(Jb.X)[e] = val;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const gmem<const float> Z = gptr((const float*)Jb.Z);
+    if (d % 4 == 0 && aligned16(Jb.X)) {
+        const gmem<f32x4> X = (gmem<f32x4>)Jb.X;
+        for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < d * d / 4; g += stride) {
+            const int64_t i = (4 * g) / d, j0 = 4 * g - i * d;
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (i >= j0 && i < j0 + 4) v[i - j0] = Z[i * d + i] < 0.f ? -1.f : 1.f;
+            X[g] = v;
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * d; e += stride) {
+            const int64_t i = e / d, j = e - i * d;
+            gptr(Jb.X)[e] = (i == j) ? (Z[i * d + i] < 0.f ? -1.f : 1.f) : 0.f;
+        }
     }
 }
 
+// Columns [c0, d) of src into dst (both d x d, row stride d).
 __global__ __launch_bounds__(256) void copy_cols_kernel(const CopyJob* __restrict__ jobs) {
     const CopyJob J = jobs[blockIdx.y];
     const int64_t d = J.d, w = J.d - J.c0;
     if (w <= 0) return;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= d * w) return;
-    const int64_t i = e / w, j = J.c0 + (e - i * w);
-    gptr(J.dst)[i * d + j] = gptr(J.src)[i * d + j];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if (d % 4 == 0 && J.c0 % 4 == 0 && aligned16(J.src) && aligned16(J.dst)) {
+        const int64_t gw = w / 4;   // groups per row
+        for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < d * gw; g += stride) {
+            const int64_t i = g / gw, j = J.c0 + 4 * (g - i * gw);
+            *(gmem<f32x4>)(J.dst + i * d + j) = *(const gmem<const f32x4>)(J.src + i * d + j);
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < d * w; e += stride) {
+            const int64_t i = e / w, j = J.c0 + (e - i * w);
+            gptr(J.dst)[i * d + j] = gptr(J.src)[i * d + j];
+        }
+    }
 }
 
 // Yb[i][c] = Y[kB + i][kB + c] of outer block b as a unit-lower matrix
@@ -664,16 +688,32 @@ __global__ __launch_bounds__(256) void qr_copy_block_kernel(const QrJob* __restr
     const int kB = b * kQrNB;
     const int64_t d = J.d, L = d - kB;
     if (L <= 0) return;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (e >= L * kQrNB) return;
-    const int64_t i = e / kQrNB;
-    const int c = (int)(e - i * kQrNB);
-    float v = 0.f;
-    if (kB + c < d) {
-        if (i == c) v = 1.f;
-        else if (i > c) v = gptr(J.Z)[(kB + i) * d + kB + c];
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const gmem<const float> Z = gptr((const float*)J.Z);
+    auto yv = [&](int64_t i, int c, float z) { return kB + c >= d ? 0.f : i == c ? 1.f : i > c ? z : 0.f; };
+    if (d % 4 == 0 && aligned16(J.Z) && aligned16(J.Yb)) {
+        constexpr int GR = kQrNB / 4;   // groups per row of Yb
+        const gmem<f32x4> Yb = (gmem<f32x4>)J.Yb;
+        for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < L * GR; g += stride) {
+            const int64_t i = g / GR;
+            const int c0 = 4 * (int)(g - i * GR);
+            // kB, c0 and d are multiples of 4: a group lies wholly inside the
+            // matrix's columns or wholly past them
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            if (kB + c0 < d && i > c0) z = *(const gmem<const f32x4>)(J.Z + (kB + i) * d + kB + c0);
+            f32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = yv(i, c0 + q, z[q]);
+            Yb[g] = v;
+        }
+    } else {
+        for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < L * kQrNB; e += stride) {
+            const int64_t i = e / kQrNB;
+            const int c = (int)(e - i * kQrNB);
+            const float z = (kB + c < d && i > c) ? Z[(kB + i) * d + kB + c] : 0.f;
+            gptr(J.Yb)[e] = yv(i, c, z);
+        }
     }
-    gptr(J.Yb)[e] = v;
 }
 
 // ---- tall panels: rows spread over many workgroups ---------------------
@@ -942,11 +982,17 @@ __global__ __launch_bounds__(256) void qr_tall_t_kernel(const QrJob* __restrict_
 
 }  // namespace
 
+// Workgroups per job of the helper copies for at most n elements: about four
+// 16-byte groups per thread.
+unsigned helper_blocks(int64_t n) {
+    const int64_t groups = (n + 3) / 4;
+    return (unsigned)std::max<int64_t>(1, (groups + 4 * 256 - 1) / (4 * 256));
+}
+
 hipError_t launch_qr_copy_block(const QrJob* jobs, int njobs, int b, int max_d, hipStream_t s) {
     const int64_t L = (int64_t)max_d - (int64_t)b * kQrNB;
     if (njobs <= 0 || L <= 0) return hipSuccess;
-    hipLaunchKernelGGL(qr_copy_block_kernel, dim3((unsigned)((L * kQrNB + 255) / 256), njobs), dim3(256), 0, s,
-                       jobs, b);
+    hipLaunchKernelGGL(qr_copy_block_kernel, dim3(helper_blocks(L * kQrNB), njobs), dim3(256), 0, s, jobs, b);
     return hipGetLastError();
 }
 
@@ -1023,16 +1069,14 @@ hipError_t launch_qr_reduce(const QrJob* jobs, const QrClasses& C, int p, hipStr
 hipError_t launch_qr_init_q(const QrJob* jobs, int njobs, int max_d, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     const int64_t n = (int64_t)max_d * max_d;
-    hipLaunchKernelGGL(qr_init_q_kernel, dim3((unsigned)((n + 1023) / 1024), njobs), dim3(256), 0, s,
-                       jobs);
+    hipLaunchKernelGGL(qr_init_q_kernel, dim3(helper_blocks(n), njobs), dim3(256), 0, s, jobs);
     return hipGetLastError();
 }
 
 hipError_t launch_copy_cols(const CopyJob* jobs, int njobs, int max_d, hipStream_t s) {
     if (njobs <= 0) return hipSuccess;
     const int64_t n = (int64_t)max_d * max_d;
-    hipLaunchKernelGGL(copy_cols_kernel, dim3((unsigned)((n + 255) / 256), njobs), dim3(256), 0, s,
-                       jobs);
+    hipLaunchKernelGGL(copy_cols_kernel, dim3(helper_blocks(n), njobs), dim3(256), 0, s, jobs);
     return hipGetLastError();
 }
 
