@@ -745,7 +745,15 @@ QrSteps qr_block_steps(const std::vector<QrJob>& jobs) {
             add_k_chunked(ws, mk(true, false, J.Yb, false, kQrNB, J.Yb, false, kQrNB, Sb, kQrNB, w, w, L, 1.f, 0.f));
             if (nc > 0)
                 add_k_chunked(ws, mk(true, false, J.Yb, false, kQrNB, Ct, false, d, J.Wb, d, w, nc, L, 1.f, 0.f));
-            add_k_chunked(qw, mk(true, false, J.Yb, false, kQrNB, Cx, false, d, J.Wb, d, w, L, L, 1.f, 0.f));
+            // In the Q formation X[kB:, kB:] is still diag(sign R) with zeros in
+            // its first w rows and columns (the later blocks, applied first,
+            // touch rows and columns from kB + w only): W's first w columns
+            // take only Yb's top w rows, the rest only the rows and columns
+            // past kB + w.
+            add_k_chunked(qw, mk(true, false, J.Yb, false, kQrNB, Cx, false, d, J.Wb, d, w, w, w, 1.f, 0.f));
+            if (nc > 0)
+                add_k_chunked(qw, mk(true, false, J.Yb + w * kQrNB, false, kQrNB, Cx + w * d + w, false, d, J.Wb + w,
+                                     d, w, nc, nc, 1.f, 0.f));
             for (int q = 0; q < npb; ++q) {
                 const int64_t r0 = (int64_t)q * kQrPB, jb = std::min<int64_t>(kQrPB, w - r0), r1 = r0 + jb;
                 const float* Tq = J.T + (int64_t)(b * P + q) * kQrPB * kQrPB;
