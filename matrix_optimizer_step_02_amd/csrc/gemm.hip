@@ -1047,9 +1047,9 @@ __device__ __forceinline__ void gemm_tile_x6(const GemmProb& p, int tm, int tn, 
     if constexpr (MATOPT_X6_PREFETCH == 2) load(fa1, fb1, 32);
     __syncthreads();
 
-    // one slab: its MFMAs from LDS buffer kt % 2; after the first row block,
-    // slab kt + 1 from registers (fa, fb) into the other buffer and the load
-    // of slab kt + 1 + MATOPT_X6_PREFETCH into the same registers
+    // one slab: its MFMAs from LDS buffer kt % 2; after one of its row
+    // blocks, slab kt + 1 from registers (fa, fb) into the other buffer and
+    // the load of slab kt + 1 + MATOPT_X6_PREFETCH into the same registers.
     // With both operands split, the two wavefronts that share a SIMD (w and
     // w + 4 of 8) split and write the next slab at different row blocks, so
     // that one's vector work meets the other's MFMAs instead of both leaving
